@@ -1,0 +1,80 @@
+"""The oracle's packed-record writer, pinned by unpacking every code from the layout rules.
+
+The unpacker here reads one bit pair / nibble at a time through np.unpackbits,
+a different route from the packer's vectorised shifts."""
+import numpy as np
+import pytest
+
+from oracle import loopkv_oracle as O
+from tests.test_oracle_pins import _row
+
+
+def _bits(arr_u8):
+    return np.unpackbits(np.asarray(arr_u8, dtype=np.uint8), bitorder="little")
+
+
+def _field(bits, pos, width):
+    return sum(int(bits[pos + i]) << i for i in range(width))
+
+
+def _unpack_token_major(buf, D, width):
+    bits = _bits(buf)
+    row = 16 * 0 + D * width  # bits per token row
+    return np.array([[_field(bits, t * D * width + d * width, width) for d in range(D)] for t in range(16)])
+
+
+def _unpack_channel_major_2bit(buf, D):
+    bits = _bits(buf)
+    return np.array([[_field(bits, 32 * d + 8 * (t % 4) + 2 * (t // 4), 2) for d in range(D)] for t in range(16)])
+
+
+def _unpack_channel_major_4bit(buf, D):
+    bits = _bits(buf)
+    out = np.zeros((16, D), dtype=np.int64)
+    for t in range(16):
+        w, tp = divmod(t, 8)
+        for d in range(D):
+            out[t, d] = _field(bits, 64 * d + 32 * w + 8 * (tp % 4) + 4 * (tp // 4), 4)
+    return out
+
+
+def _meta(buf):
+    w = np.asarray(buf, dtype=np.uint8).view("<u4")
+    s = (w & 0xFFFF).astype(np.uint16).view(np.float16).astype(np.float64)
+    z = (w >> 16).astype(np.uint16).view(np.float16).astype(np.float64)
+    return s, z
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("layout,bits", [(O.LAYOUT_PLANES, 4), (O.LAYOUT_PLANES, 2), (O.LAYOUT_KIVI4, 4)])
+def test_pack_roundtrip(D, layout, bits):
+    rng = np.random.default_rng(D + bits + layout)
+    q, K, V = _row(rng, 64, D, outliers=3)
+    qh = O.quantize_history(K, V, bits)
+    for j in range(4):
+        rec = O.pack_block(qh, j, layout)
+        kind = O.KIND_Q4 if bits == 4 else O.KIND_Q2
+        assert rec.size == O.record_bytes(D, kind, layout)
+        t0 = 16 * j
+        g, half = divmod(j, 2)
+        if layout == O.LAYOUT_KIVI4:
+            kc = _unpack_token_major(rec[:8 * D], D, 4)
+            vc = _unpack_channel_major_4bit(rec[8 * D:16 * D], D)
+            km, vm = rec[16 * D:18 * D], rec[18 * D:20 * D]
+        elif bits == 2:
+            kc = _unpack_token_major(rec[:4 * D], D, 2)
+            vc = _unpack_channel_major_2bit(rec[4 * D:8 * D], D)
+            km, vm = rec[8 * D:10 * D], rec[10 * D:12 * D]
+        else:
+            kc = 4 * _unpack_token_major(rec[:4 * D], D, 2) + _unpack_token_major(rec[12 * D:16 * D], D, 2)
+            vc = 4 * _unpack_channel_major_2bit(rec[4 * D:8 * D], D) + \
+                _unpack_channel_major_2bit(rec[16 * D:20 * D], D)
+            km, vm = rec[8 * D:10 * D], rec[10 * D:12 * D]
+        assert np.array_equal(kc, qh["kc"][t0:t0 + 16])
+        assert np.array_equal(vc, qh["vc"][t0:t0 + 16])
+        ks, kz = _meta(km)
+        chs = slice(half * D // 2, (half + 1) * D // 2)
+        assert np.array_equal(ks, qh["ks"][g, chs]) and np.array_equal(kz, qh["kz"][g, chs])
+        vs, vz = _meta(vm)
+        assert np.array_equal(vs.reshape(16, D // 32), qh["vs"][t0:t0 + 16])
+        assert np.array_equal(vz.reshape(16, D // 32), qh["vz"][t0:t0 + 16])

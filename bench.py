@@ -1,0 +1,317 @@
+"""Benchmark: loop-aware decode attention over the full 4-loop x 24-layer plan at 16K context.
+
+Workload (the long-context configuration): 96 cells (seeded 48 4-bit / 29 2-bit /
+19 reuse-final-loop plan), 16 heads x 128, batch 32, 16384-token context, paged
+16-token blocks with a shuffled block table, bf16 inputs, per-cell K/V scales
+log-uniform in [0.5, 4]. One step = a one-token append to every storing cell of
+every sequence (quantizing completed 32-token groups) followed by the
+whole-plan decode at tau = 0.01. Lengths start at 16384 - (warmup + steps) so
+the last step decodes exactly 16384 tokens.
+
+Prints one JSON line. ``value`` is the algorithmic HBM rate of the step (bytes
+the method must move / step time); ``roofline`` is the decode kernel's
+algorithmic bytes per launch over its mean duration (HIP events on the launch
+stream) against the 8 TB/s HBM peak; ``cpu_baseline`` times the fp64 oracle on a
+few sampled rows of the same workload on the host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(plan, lengths, H, D, sel_counts=None, layout_kivi=False, out_bytes=2, q_bytes=2):
+    """Bytes one whole-plan decode must move.
+
+    Per (cell, sequence, head) row with N tokens, n_q = 32 floor(N/32):
+      quantized prefix: 96 B/token (D=128: K_hi 32 + K_meta 16 + V_hi 32 + V_meta 16), plus
+      64 B (K_lo + V_lo) per selected token on a 4-bit target; KIVI-4 reads 160 B/token;
+      tail: 4*D B/token (bf16 K and V); query and output: D * dtype bytes each;
+      block table: 4 B per 16-token block; length: 4 B.
+    sel_counts[c][b][h] is the number of selected tokens (4-bit targets only).
+    """
+    import numpy as np
+    plan = np.asarray(plan).reshape(-1)
+    n_loops_layers = plan.size
+    per_tok_base = 96 * D // 128
+    per_tok_lo = 64 * D // 128
+    per_tok_kivi = 160 * D // 128
+    total = 0
+    n_layers = None
+    for c in range(n_loops_layers):
+        kind = plan[c]
+        for b, N in enumerate(lengths):
+            n_q = 32 * (N // 32)
+            row = (N - n_q) * 4 * D + D * q_bytes + D * out_bytes + 4 * ((N + 15) // 16) + 4
+            if layout_kivi:
+                row += n_q * per_tok_kivi
+                total += H * row
+                continue
+            row += n_q * per_tok_base
+            total += H * row
+            if sel_counts is not None:
+                total += per_tok_lo * int(sel_counts[c, b].sum())
+    return total
+
+
+def target_kinds(plan, n_loops, n_layers):
+    import numpy as np
+    p = np.asarray(plan).reshape(-1)
+    out = p.copy()
+    for c in range(p.size):
+        if p[c] == 2:
+            out[c] = p[(n_loops - 1) * n_layers + c % n_layers]
+    return out
+
+
+def append_bytes(n_storing, B, H, D, lengths_before):
+    """Bytes of a one-token append: bf16 K and V in, one tail slot out; a completed group
+    also reads its 31 tail tokens and writes two records."""
+    import numpy as np
+    tok = 2 * H * D * 2
+    total = n_storing * B * (tok + tok)
+    done = sum(1 for n in lengths_before if n % 32 == 31)
+    return total + n_storing * done * H * (31 * 2 * D * 2 + 2 * 20 * D)
+
+
+def sel_counts_from_mask(sm, n_q):
+    """Per-row selected counts from the u32 mask tensor [cells][B][H][words]."""
+    import numpy as np
+    w = sm.cpu().numpy().view(np.uint32)
+    bits = np.unpackbits(w.view(np.uint8), axis=-1, bitorder="little")
+    return bits.sum(axis=-1)
+
+
+def cpu_baseline(cfg, plan, tau, rows, log):
+    """Time the fp64 oracle (quantize + loop-aware decode of one row) on sampled rows."""
+    import numpy as np
+    from oracle import loopkv_oracle as O
+    from synth import recipes as R
+    from synth.philox import bf16_bits_to_f32
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([1] + [i.get("num_threads", 1) for i in threadpool_info()])
+    except Exception:
+        cores = 1
+    factors = R.factor_table(cfg)
+    sig = float(np.float32(1.0 / math.sqrt(cfg.head_dim)))
+    t_total = 0.0
+    bytes_total = 0
+    for (c, b, h) in rows:
+        st = O.storage_cell(plan.reshape(cfg.n_loops, cfg.n_layers), c)
+        kind = O.target_kind(plan.reshape(cfg.n_loops, cfg.n_layers), c)
+        N = cfg.lengths[b]
+        kb, vb = R.kv_row_bits(cfg, st, b, h, 0, N, factors)
+        K = bf16_bits_to_f32(kb).astype(np.float64)
+        V = bf16_bits_to_f32(vb).astype(np.float64)
+        q = R.q_values(cfg, c, 0, b, h).astype(np.float64)
+        t0 = time.perf_counter()
+        o, sel, _ = O.decode_row(q, K, V, kind, tau, sig)
+        t_total += time.perf_counter() - t0
+        n_q = 32 * (N // 32)
+        bytes_total += n_q * 96 + (N - n_q) * 512 + 512 + 4 * ((N + 15) // 16) + 4
+        if kind == 0:
+            bytes_total += 64 * int(sel.sum())
+    log(f"cpu oracle: {len(rows)} rows in {t_total:.2f}s")
+    return {"value": bytes_total / t_total / 1e9, "unit": "GB/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{len(rows)} (cell, seq, head) rows of the 16K-context plan (one 4-bit, one 2-bit, "
+                      f"one reuse cell per pair of rows), fp64 quantize + loop-aware decode per row; "
+                      f"{t_total:.2f} s measured, input generation excluded"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--tau", type=float, default=0.01)
+    ap.add_argument("--ctx", type=int, default=16384)
+    ap.add_argument("--batch", type=int, default=32)
+    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-kivi", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=4)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}). "
+              "Rows of the decode are independent; see the sharding notes for how it would split.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import quantized_kv_cache_loopkv_amd as lkv
+    from synth import recipes as R
+    from tests.harness import Workload
+
+    torch.cuda.set_device(0)
+    lkv.lib()
+    S = args.warmup + args.steps
+    cfg = R.make_config("C4")
+    cfg.batch = args.batch
+    cfg.lengths = [args.ctx - S] * args.batch
+    cfg.append_steps = S
+    plan = cfg.plan.reshape(-1)
+    H, D, C, B = cfg.n_heads, cfg.head_dim, cfg.n_cells, cfg.batch
+
+    t0 = time.time()
+    wl = Workload(cfg, gpu_synth=True, log=log)
+    log(f"workspace {wl.ws.numel() / 1e9:.2f} GB; filling {len(wl.storing_cells())} storing cells")
+    wl.fill()
+    log(f"filled in {time.time() - t0:.1f}s")
+    q = wl.q_all()
+    out = torch.empty((C, B, H, D), dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    inputs = [wl.append_inputs(s) for s in range(S)]   # drawn before the timed region
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(S)]
+    lengths_before = []
+    for s in range(S):
+        if s == args.warmup:
+            torch.cuda.synchronize()
+            t_wall0 = time.perf_counter()
+        lengths_before.append(wl.current_lengths(s))
+        e0, e1, e2 = ev[s]
+        e0.record(stream)
+        wl.append_step(s, inputs[s])
+        e1.record(stream)
+        wl.ctx.decode(q, wl.bt, wl.seq_lens, wl.max_len(s + 1), args.tau, out=out, out_dtype=torch.bfloat16)
+        e2.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall0
+    step_ms = [ev[s][0].elapsed_time(ev[s][2]) for s in range(args.warmup, S)]
+    dec_ms = [ev[s][1].elapsed_time(ev[s][2]) for s in range(args.warmup, S)]
+    app_ms = [ev[s][0].elapsed_time(ev[s][1]) for s in range(args.warmup, S)]
+    ms_per_step = t_wall * 1e3 / args.steps
+
+    # selected tokens at the final state (untimed), for the byte count
+    final_lens = wl.current_lengths(S)
+    _, sm = wl.ctx.decode(q, wl.bt, wl.seq_lens, max(final_lens), args.tau, out_dtype=torch.bfloat16,
+                          sel_mask=True)
+    torch.cuda.synchronize()
+    tk = target_kinds(plan, cfg.n_loops, cfg.n_layers)
+    counts = sel_counts_from_mask(sm, None)
+    counts[tk != 0] = 0
+    dec_bytes = algorithmic_bytes(plan, final_lens, H, D, counts)
+    n_storing = len(wl.storing_cells())
+    step_bytes = [algorithmic_bytes(plan, wl.current_lengths(s + 1), H, D, counts) +
+                  append_bytes(n_storing, B, H, D, lengths_before[s]) for s in range(args.warmup, S)]
+    value = float(np.mean(step_bytes)) / (ms_per_step * 1e-3) / 1e9
+    dec_mean_ms = float(np.mean(dec_ms))
+    achieved = dec_bytes / (dec_mean_ms * 1e-3) / 1e9
+    sel_frac = float(counts.sum()) / max(1, sum(int(H * B * (32 * (final_lens[0] // 32))) for c in range(C) if tk[c] == 0))
+    log(f"step {ms_per_step:.3f} ms (events {np.mean(step_ms):.3f}), decode {dec_mean_ms:.3f} ms, "
+        f"append {np.mean(app_ms):.3f} ms; decode {achieved:.0f} GB/s algorithmic; selected fraction {sel_frac:.2e}")
+
+    extra = {}
+    if not args.no_sweep:
+        sweep = {}
+        for tau in (0.0, 0.001, 0.01, 1.1):
+            _, smt = wl.ctx.decode(q, wl.bt, wl.seq_lens, max(final_lens), tau, out_dtype=torch.bfloat16,
+                                   sel_mask=True)
+            ct = sel_counts_from_mask(smt, None)
+            ct[tk != 0] = 0
+            bts = algorithmic_bytes(plan, final_lens, H, D, ct)
+            e_a, e_b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            wl.ctx.decode(q, wl.bt, wl.seq_lens, max(final_lens), tau, out=out, out_dtype=torch.bfloat16)
+            e_a.record(stream)
+            for _ in range(3):
+                wl.ctx.decode(q, wl.bt, wl.seq_lens, max(final_lens), tau, out=out, out_dtype=torch.bfloat16)
+            e_b.record(stream)
+            torch.cuda.synchronize()
+            ms = e_a.elapsed_time(e_b) / 3
+            sweep[str(tau)] = {"decode_ms": round(ms, 4), "algorithmic_GB": round(bts / 1e9, 3),
+                               "GBps": round(bts / (ms * 1e-3) / 1e9, 1), "selected": int(ct.sum())}
+            log(f"tau={tau}: {ms:.3f} ms, {bts / 1e9:.2f} GB, {bts / (ms * 1e-3) / 1e9:.0f} GB/s")
+        extra["tau_sweep"] = sweep
+    if not args.no_kivi:
+        kcfg = R.make_config("C4")
+        kcfg.batch = B
+        kcfg.lengths = list(final_lens)
+        kcfg.append_steps = 0
+        t1 = time.time()
+        kw = Workload(kcfg, layout=lkv.LAYOUT_KIVI4, gpu_synth=True, log=log)
+        kw.fill()
+        log(f"KIVI-4 cache filled in {time.time() - t1:.1f}s")
+        kb = algorithmic_bytes(plan, final_lens, H, D, layout_kivi=True)
+        kw.decode(q, args.tau, out_dtype=torch.bfloat16, sel_mask=False)
+        e_a, e_b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e_a.record(stream)
+        for _ in range(3):
+            kw.ctx.decode(q, kw.bt, kw.seq_lens, max(final_lens), args.tau, out=out, out_dtype=torch.bfloat16)
+        e_b.record(stream)
+        torch.cuda.synchronize()
+        kms = e_a.elapsed_time(e_b) / 3
+        extra["kivi4_same_kernel"] = {"decode_ms": round(kms, 4), "algorithmic_GB": round(kb / 1e9, 3),
+                                      "GBps": round(kb / (kms * 1e-3) / 1e9, 1),
+                                      "bytes_ratio_loopkv_over_kivi4": round(dec_bytes / kb, 4),
+                                      "time_ratio_loopkv_over_kivi4": round(dec_mean_ms / kms, 4)}
+        log(f"KIVI-4: {kms:.3f} ms, {kb / 1e9:.2f} GB, ratio bytes {dec_bytes / kb:.3f} time {dec_mean_ms / kms:.3f}")
+        del kw
+        torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu:
+        rows = []
+        kinds_seen = {}
+        for c in range(C):
+            k = int(plan[c])
+            if kinds_seen.get(k, 0) < max(1, args.cpu_rows // 3):
+                rows.append((c, (7 * c) % B, (3 * c) % H))
+                kinds_seen[k] = kinds_seen.get(k, 0) + 1
+            if len(rows) >= args.cpu_rows:
+                break
+        ccfg = R.make_config("C4")
+        ccfg.batch = B
+        ccfg.lengths = [args.ctx - S] * B     # the initial histories of the timed workload
+        ccfg.append_steps = S
+        cpu = cpu_baseline(ccfg, plan, args.tau, rows, log)
+
+    line = {
+        "metric": "achieved HBM GB/s (% of peak) + us per decode step, 4x24 plan, 16K ctx",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "us_per_decode_step": round(dec_mean_ms * 1e3, 1),
+        "pct_of_peak": round(100 * value / PEAK_HBM_GBS, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 in, fp32 accumulate, 2-bit/4-bit codes",
+        "data": "synthetic (seeded Philox normal draws, shapes of the pages' Ouro-1.4B 16K serving workload)",
+        "config": {"workload": "4 loops x 24 layers, 48 q4 / 29 q2 / 19 reuse, 16 heads x 128, batch 32, "
+                               f"context {args.ctx} (last step), 16-token blocks shuffled, tau {args.tau}, "
+                               "1-token append + whole-plan decode per step",
+                   "global_batch": B, "seq_len": args.ctx, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "kernel": "k_decode<128>", "bytes_per_launch": dec_bytes,
+                     "mean_launch_ms": round(dec_mean_ms, 4)},
+        "cpu_baseline": cpu,
+        "selected_fraction_q4_targets": sel_frac,
+        "append_ms": round(float(np.mean(app_ms)), 4),
+    }
+    line.update(extra)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

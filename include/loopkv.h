@@ -1,0 +1,165 @@
+/*
+ * loopkv.h — C ABI of the loop-aware mixed-precision KV cache and its decode attention.
+ *
+ * Method: "LoopKV: Loop-Aware KV Cache Compression for Serving Looped
+ * Transformers" (arXiv:2611.04137), Abstract. A looped transformer keeps a KV
+ * cache per (loop, layer) cell; each cell is stored as 4-bit, as 2-bit, or as
+ * a reuse of the final loop's KV of the same layer (abstract: the sentence on
+ * the one-time offline profile). While decoding, each loop reads the high 2
+ * bits of every 4-bit value and fetches the low bits only where its own
+ * attention weights require 4-bit precision (abstract: the sentence on
+ * decoding); values with low attention are read at 2 bits, never skipped
+ * (abstract: the sentence on skipping). KIVI-4, uniform 4-bit quantization,
+ * is the baseline run on the same kernel (abstract: the serving sentence).
+ *
+ * The abstract gives no formula; this library fixes:
+ *   - KIVI-style asymmetric groups of 32: K per channel over 32 consecutive
+ *     tokens, V per token over 32 consecutive channels. zero = f16(min),
+ *     scale = f16((max - min) / (2^b - 1)), code = clamp(rint((x - zero) /
+ *     scale), 0, 2^b - 1), all in float64 with a single round-to-nearest-even
+ *     to f16; scale 0 gives code 0.
+ *   - 4-bit codes are split into hi = code >> 2 and lo = code & 3 and stored
+ *     in separate planes. A value read from its high bits only is
+ *     zero + scale * (4*hi + 3/2).
+ *   - Selection: a token t of the quantized prefix is fetched at 4 bits when
+ *     its coarse softmax weight (scores from high bits, softmax over the whole
+ *     row) is >= tau. tau = 0 fetches every token, tau > 1 none.
+ *   - The last (len mod 32) tokens of a sequence are kept exact in bf16 (the
+ *     tail) and quantized by the append that completes their group.
+ *
+ * Storage (per storing cell, caller-allocated workspace):
+ *   pool  [num_blocks][n_heads][record]   record of one 16-token block, one head
+ *   tails [max_seqs][n_heads][2 (K,V)][32][head_dim] bf16
+ * Record layouts (D = head_dim, all words little-endian u32):
+ *   4-bit planes : [K_hi 4D | V_hi 4D | K_meta 2D | V_meta 2D | K_lo 4D | V_lo 4D]  = 20D bytes
+ *   2-bit        : [K2 4D   | V2 4D   | K_meta 2D | V_meta 2D]                      = 12D bytes
+ *   KIVI-4       : [K4 8D   | V4 8D   | K_meta 2D | V_meta 2D]                      = 20D bytes
+ *   K plane (2-bit): D/16 columns x 16 tokens of u32; word (w, t) holds channels
+ *     16w..16w+15 of token t, channel 16w+4k+p at bit 8k+2p.
+ *   K plane (4-bit): D/8 columns x 16 tokens; channel 8w+2k+n at bit 8k+4n.
+ *   V plane (2-bit): D words; word d holds channel d of the 16 tokens, token t at
+ *     bit 8*(t%4) + 2*(t/4).
+ *   V plane (4-bit): D x 2 words; word (d, j) holds tokens 8j..8j+7, token
+ *     t' = t-8j at bit 8*(t'%4) + 4*(t'/4).
+ *   Meta word: f16 scale in bits 0-15, f16 zero in bits 16-31. K_meta of group g
+ *     is split over its two blocks: logical block 2g holds channels 0..D/2-1,
+ *     block 2g+1 channels D/2..D-1. V_meta is [16 tokens][D/32].
+ *
+ * Paging: block_table[b * bt_stride + j] is the physical block of logical block
+ * j (tokens 16j..16j+15) of sequence b; the same id addresses every cell's pool.
+ *
+ * Ownership: the caller owns every device buffer (workspace, q, k, v, out,
+ * tables, masks). The library never allocates device memory and never
+ * synchronizes a stream. A context is not thread-safe; separate contexts are
+ * independent.
+ *
+ * Errors: every call validates its arguments on the host before enqueuing
+ * anything; on error nothing is enqueued and loopkv_last_error() describes it.
+ * Kernel faults surface at the caller's next synchronization.
+ */
+#ifndef LOOPKV_H
+#define LOOPKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LOOPKV_OK = 0,
+  LOOPKV_ERR_INVALID_ARG = 1, /* null / out-of-range argument, bad dtype, tau < 0 or NaN, sm_scale <= 0 */
+  LOOPKV_ERR_PLAN = 2,        /* no plan loaded, kind > 2, reuse cell in the final loop, bad cell index */
+  LOOPKV_ERR_WORKSPACE = 3,   /* workspace not bound, too small, or not 256-byte aligned */
+  LOOPKV_ERR_CAPACITY = 4,    /* bt_stride * 16 < max_len, max_len above the supported maximum */
+  LOOPKV_ERR_UNSUPPORTED = 5, /* head_dim not 64/128, group != 32, block != 16, too many cells */
+  LOOPKV_ERR_HIP = 6          /* HIP runtime / launch failure */
+} loopkv_status;
+
+typedef enum { LOOPKV_CELL_Q4 = 0, LOOPKV_CELL_Q2 = 1, LOOPKV_CELL_SHARE = 2 } loopkv_cell_kind;
+typedef enum { LOOPKV_F32 = 0, LOOPKV_BF16 = 1 } loopkv_dtype;
+typedef enum { LOOPKV_LAYOUT_PLANES = 0, LOOPKV_LAYOUT_KIVI4 = 1 } loopkv_layout;
+
+/* Largest supported max_len of one decode call (coarse scores of a row live in LDS). */
+#define LOOPKV_MAX_LEN 32768
+/* Largest n_loops * n_layers. */
+#define LOOPKV_MAX_CELLS 128
+
+typedef struct {
+  int32_t n_loops, n_layers; /* cells = n_loops * n_layers, row-major [loop][layer] */
+  int32_t n_heads;           /* KV heads = query heads (MHA) */
+  int32_t head_dim;          /* 64 or 128 */
+  int32_t group_size;        /* must be 32 */
+  int32_t block_tokens;      /* must be 16 */
+  int32_t num_blocks;        /* physical blocks in each storing cell's pool */
+  int32_t max_seqs;          /* sequence slots (tail buffers) */
+  int32_t layout;            /* loopkv_layout; KIVI4 requires an all-4-bit plan */
+} loopkv_config;
+
+typedef struct loopkv_ctx loopkv_ctx;
+
+/* Validate cfg and create a context (host memory only). */
+loopkv_status loopkv_create(const loopkv_config* cfg, loopkv_ctx** out);
+void loopkv_destroy(loopkv_ctx* ctx);
+
+/* Load the plan: host array kinds[n_loops * n_layers] of loopkv_cell_kind, row-major
+ * [loop][layer]. A reuse cell (SHARE) of layer l reads cell (n_loops-1, l); the final
+ * loop may not be SHARE. With the KIVI4 layout every cell must be Q4. Resets any
+ * bound workspace. */
+loopkv_status loopkv_plan(loopkv_ctx* ctx, const uint8_t* kinds);
+
+/* Bytes of workspace the loaded plan needs (pools + tails of the storing cells). */
+loopkv_status loopkv_workspace_bytes(const loopkv_ctx* ctx, size_t* bytes);
+
+/* Bind caller-owned device memory (>= loopkv_workspace_bytes, 256-byte aligned).
+ * The library does not clear it: a fresh cache is valid for any sequence whose
+ * seq_lens entry starts at 0. */
+loopkv_status loopkv_bind_workspace(loopkv_ctx* ctx, void* dev, size_t bytes);
+
+/* Where a cell's storage lives inside the workspace (for inspection and tests):
+ * byte offsets of its pool and tails and its record size; a SHARE cell reports the
+ * final-loop cell it reads. */
+loopkv_status loopkv_cell_storage(const loopkv_ctx* ctx, int32_t loop, int32_t layer,
+                                  size_t* pool_offset, size_t* tail_offset,
+                                  size_t* record_bytes, int32_t* storage_cell);
+
+/* Append n_new tokens to every sequence of one cell ((loop, layer)) or of every
+ * storing cell ((-1, -1)). k, v: device [cells][n_seqs][n_new][H][D] (whole plan,
+ * cells = n_loops*n_layers, SHARE entries ignored) or [n_seqs][n_new][H][D]; F32 input
+ * is rounded to bf16 (nearest even). seq_slots: device [n_seqs] tail slot of each
+ * sequence or NULL for slot = b. block_table: device [n_seqs][bt_stride]; blocks 2g and
+ * 2g+1 must be mapped before the append that completes group g. seq_lens: device
+ * [n_seqs], length before the append (read only; the caller advances it). Completed
+ * 32-token groups are quantized into the pool; the rest goes to the tail. Appending to
+ * a SHARE cell is a no-op. */
+loopkv_status loopkv_append(loopkv_ctx* ctx, hipStream_t stream, int32_t loop, int32_t layer,
+                            const void* k, const void* v, int32_t kv_dtype,
+                            int32_t n_seqs, int32_t n_new, const int32_t* seq_slots,
+                            const int32_t* block_table, int32_t bt_stride,
+                            const int32_t* seq_lens);
+
+/* Loop-aware decode attention of one cell ((loop, layer)) or of the whole plan ((-1, -1)).
+ * q: device [cells][n_seqs][H][D] (whole plan) or [n_seqs][H][D], dtype q_dtype.
+ * seq_lens: device lengths (tail included); max_len: host upper bound of them
+ * (<= LOOPKV_MAX_LEN, <= 16 * bt_stride). Rows whose length exceeds max_len get NaN
+ * output. tau >= 0: selection threshold on the coarse softmax; sm_scale > 0.
+ * out: device [cells][n_seqs][H][D] (or [n_seqs][H][D]) of out_dtype, accumulated in fp32.
+ * sel_mask: NULL or device [cells][n_seqs][H][ceil(max_len/32)] u32; bit t%32 of word
+ * t/32 is set iff token t was fetched at 4 bits (all quantized tokens for KIVI4 and
+ * tau = 0; none for 2-bit targets). */
+loopkv_status loopkv_decode_attn(loopkv_ctx* ctx, hipStream_t stream, int32_t loop, int32_t layer,
+                                 const void* q, int32_t q_dtype, int32_t n_seqs,
+                                 const int32_t* seq_slots, const int32_t* block_table,
+                                 int32_t bt_stride, const int32_t* seq_lens, int32_t max_len,
+                                 float tau, float sm_scale, void* out, int32_t out_dtype,
+                                 uint32_t* sel_mask);
+
+/* Thread-local description of the last error on this thread ("" after success). */
+const char* loopkv_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LOOPKV_H */

@@ -239,12 +239,16 @@ def attention_reference(q, Kt, Vt, sm_scale):
 # ---------------------------------------------------------------------------
 # Packed record layout (bit-exact contract with the library)
 # ---------------------------------------------------------------------------
-def _pack_2bit_token_major(c):
-    """[16][D] codes -> 16*D/4 bytes; channel d of token t at byte t*D/4 + d//4, bits 2*(d%4)."""
+def _pack_2bit_k(c):
+    """[16][D] codes -> D/16 columns x 16 tokens of little-endian u32 (column-major).
+
+    Word (w, t) holds channels 16w..16w+15 of token t: channel 16w + 4k + p at
+    bit 8k + 2p. Words are ordered w-major, so a column's 16 tokens are contiguous."""
     T, D = c.shape
-    c = c.astype(np.uint8).reshape(T, D // 4, 4)
-    b = c[..., 0] | (c[..., 1] << 2) | (c[..., 2] << 4) | (c[..., 3] << 6)
-    return b.reshape(-1).astype(np.uint8)
+    cw = c.astype(np.uint64).reshape(T, D // 16, 4, 4)            # [t][w][k][p]
+    shifts = (8 * np.arange(4)[:, None] + 2 * np.arange(4)[None, :]).astype(np.uint64)
+    words = (cw << shifts).sum(axis=(2, 3))                        # [t][w]
+    return words.T.reshape(-1).astype("<u4").view(np.uint8)
 
 
 def _pack_2bit_channel_major(c):
@@ -256,11 +260,14 @@ def _pack_2bit_channel_major(c):
     return words.astype("<u4").view(np.uint8)
 
 
-def _pack_4bit_token_major(c):
-    """[16][D] codes -> 16*D/2 bytes; channel d of token t at byte t*D/2 + d//2, bits 4*(d%2)."""
+def _pack_4bit_k(c):
+    """[16][D] codes -> D/8 columns x 16 tokens of u32 (column-major); word (w, t) holds
+    channels 8w..8w+7 of token t: channel 8w + 2k + n at bit 8k + 4n."""
     T, D = c.shape
-    c = c.astype(np.uint8).reshape(T, D // 2, 2)
-    return (c[..., 0] | (c[..., 1] << 4)).reshape(-1).astype(np.uint8)
+    cw = c.astype(np.uint64).reshape(T, D // 8, 4, 2)             # [t][w][k][n]
+    shifts = (8 * np.arange(4)[:, None] + 4 * np.arange(2)[None, :]).astype(np.uint64)
+    words = (cw << shifts).sum(axis=(2, 3))
+    return words.T.reshape(-1).astype("<u4").view(np.uint8)
 
 
 def _pack_4bit_channel_major(c):
@@ -293,7 +300,8 @@ def pack_block(qh, j, layout=LAYOUT_PLANES):
     4-bit, planes layout: [K_hi | V_hi | K_meta | V_meta | K_lo | V_lo]
     2-bit:                [K2   | V2   | K_meta | V_meta]
     4-bit, KIVI-4 layout: [K4   | V4   | K_meta | V_meta]
-    K planes are token-major, V planes channel-major (see the helpers above).
+    K planes are column-major (16-channel columns of the 16 tokens), V planes
+    channel-major (see the helpers above).
     K_meta of group g = j // 2 is split over its two blocks: block 2g holds
     channels 0..D/2-1, block 2g+1 channels D/2..D-1. V_meta is [16 tokens][D/32].
     """
@@ -307,12 +315,12 @@ def pack_block(qh, j, layout=LAYOUT_PLANES):
     kmeta = _meta_words(qh["ks"][g, ch], qh["kz"][g, ch])
     vmeta = _meta_words(qh["vs"][t0:t0 + BLOCK].reshape(-1), qh["vz"][t0:t0 + BLOCK].reshape(-1))
     if layout == LAYOUT_KIVI4:
-        parts = [_pack_4bit_token_major(kc), _pack_4bit_channel_major(vc), kmeta, vmeta]
+        parts = [_pack_4bit_k(kc), _pack_4bit_channel_major(vc), kmeta, vmeta]
     elif qh["bits"] == 2:
-        parts = [_pack_2bit_token_major(kc), _pack_2bit_channel_major(vc), kmeta, vmeta]
+        parts = [_pack_2bit_k(kc), _pack_2bit_channel_major(vc), kmeta, vmeta]
     else:
-        parts = [_pack_2bit_token_major(kc >> 2), _pack_2bit_channel_major(vc >> 2), kmeta, vmeta,
-                 _pack_2bit_token_major(kc & 3), _pack_2bit_channel_major(vc & 3)]
+        parts = [_pack_2bit_k(kc >> 2), _pack_2bit_channel_major(vc >> 2), kmeta, vmeta,
+                 _pack_2bit_k(kc & 3), _pack_2bit_channel_major(vc & 3)]
     return np.concatenate(parts)
 
 

@@ -1,0 +1,254 @@
+// Append and group quantization of the per-(loop, layer) KV cache (gfx950).
+//
+// Source: "LoopKV: Loop-Aware KV Cache Compression for Serving Looped
+// Transformers" (arXiv:2611.04137), Abstract — every cell is stored as 4-bit
+// (KIVI-4 style) or 2-bit, and decoding reads the high 2 bits of each 4-bit
+// value apart from its low bits, so 4-bit codes are split into a high and a
+// low 2-bit plane here.
+//
+// Quantizer (KIVI-style asymmetric groups of 32): K per channel over 32
+// consecutive tokens, V per token over 32 consecutive channels;
+// zero = f16(min), scale = f16((max - min) / (2^b - 1)),
+// code = clamp(rint((x - zero) / scale), 0, 2^b - 1), scale 0 -> code 0.
+// All of it in float64 with one round-to-nearest-even to f16, so codes and
+// meta are reproducible bit for bit. Built with -ffp-contract=off.
+//
+// Two kernels per append, on the caller's stream:
+//   k_quantize_groups  one workgroup per (group slot, head, cell x sequence):
+//                      gathers the 32 tokens of a group completed by this append
+//                      (old tail + new input), quantizes, writes the records of
+//                      its two 16-token blocks through the block table;
+//   k_write_tail       copies the new tokens of the last, incomplete group into
+//                      the tail (after the first kernel has read the old tail).
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+#include <stdint.h>
+#include "layout.h"
+
+namespace lkv {
+
+// float64 -> float16 bits, round to nearest even, one rounding.
+__device__ inline uint32_t f64_to_f16_bits(double x) {
+  uint64_t b = (uint64_t)__double_as_longlong(x);
+  uint32_t sign = (uint32_t)(b >> 48) & 0x8000u;
+  int ex = (int)((b >> 52) & 0x7ff);
+  uint64_t man = b & 0xFFFFFFFFFFFFFull;
+  if (ex == 0x7ff) return sign | 0x7c00u | (man ? 0x200u : 0u);
+  if (ex == 0) return sign;                       // below 2^-1022: rounds to zero
+  int e = ex - 1023;
+  if (e > 15) return sign | 0x7c00u;
+  uint64_t m = man | (1ull << 52);
+  int s = (e >= -14) ? 42 : (28 - e);             // bits dropped to reach the f16 ulp
+  if (s > 60) return sign;
+  uint64_t q = m >> s;
+  uint64_t rem = m & ((1ull << s) - 1);
+  uint64_t half = 1ull << (s - 1);
+  if (rem > half || (rem == half && (q & 1))) q++;
+  uint32_t bits = (e >= -14) ? (uint32_t)(((e + 15) << 10) + (int)q - 1024) : (uint32_t)q;
+  if (bits >= 0x7c00u) bits = 0x7c00u;
+  return sign | bits;
+}
+
+__device__ inline double f16_bits_to_f64(uint32_t h) {
+  return (double)__half2float(__ushort_as_half((unsigned short)h));
+}
+
+__device__ inline float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+__device__ inline uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);   // NaN stays NaN
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// Quantize n values read through get(i) with M = 2^bits - 1 levels.
+template <typename Get>
+__device__ inline void quantize_group(Get get, int M, uint8_t* codes, int stride, uint32_t* meta) {
+  double mn = get(0), mx = mn;
+  for (int i = 1; i < kGroup; ++i) {
+    double x = get(i);
+    mn = fmin(mn, x);
+    mx = fmax(mx, x);
+  }
+  uint32_t zb = f64_to_f16_bits(mn);
+  uint32_t sb = f64_to_f16_bits((mx - mn) / (double)M);
+  double z = f16_bits_to_f64(zb);
+  double s = f16_bits_to_f64(sb);
+  for (int i = 0; i < kGroup; ++i) {
+    int c = 0;
+    if (s != 0.0) {
+      double r = rint((get(i) - z) / s);
+      r = fmin(fmax(r, 0.0), (double)M);
+      c = (int)r;
+    }
+    codes[i * stride] = (uint8_t)c;
+  }
+  *meta = sb | (zb << 16);
+}
+
+template <int D>
+__global__ void __launch_bounds__(256) k_quantize_groups(AppendArgs a) {
+  const int b = blockIdx.z % a.n_seqs;
+  const int ci = blockIdx.z / a.n_seqs;
+  const int h = blockIdx.y;
+  const AppendCell cell = a.cells[ci];
+  const int L0 = a.seq_lens[b];
+  const int g = L0 / kGroup + (int)blockIdx.x;
+  if ((g + 1) * kGroup > L0 + a.n_new) return;
+  const int slot = a.seq_slots ? a.seq_slots[b] : b;
+  const int tid = threadIdx.x;
+
+  __shared__ float kx[kGroup][D];
+  __shared__ float vx[kGroup][D];
+  __shared__ uint8_t kc[kGroup][D];
+  __shared__ uint8_t vc[kGroup][D];
+  __shared__ uint32_t kmeta[D];
+  __shared__ uint32_t vmeta[kGroup][D / kGroup];
+
+  const uint16_t* tail = reinterpret_cast<const uint16_t*>(a.ws + cell.tail_off) +
+                         ((size_t)slot * a.n_heads + h) * tail_elems(D);
+  for (int idx = tid; idx < kGroup * D; idx += blockDim.x) {
+    const int i = idx / D, d = idx % D;
+    const int p = g * kGroup + i;
+    float kf, vf;
+    if (p < L0) {
+      kf = bf16_to_f32(tail[(0 * kGroup + (p % kGroup)) * D + d]);
+      vf = bf16_to_f32(tail[(1 * kGroup + (p % kGroup)) * D + d]);
+    } else {
+      const size_t e = ((((size_t)cell.in_cell * a.n_seqs + b) * a.n_new + (p - L0)) * a.n_heads + h) * D + d;
+      if (a.kv_bf16) {
+        kf = bf16_to_f32(reinterpret_cast<const uint16_t*>(a.k)[e]);
+        vf = bf16_to_f32(reinterpret_cast<const uint16_t*>(a.v)[e]);
+      } else {
+        kf = bf16_to_f32(f32_to_bf16_rne(reinterpret_cast<const float*>(a.k)[e]));
+        vf = bf16_to_f32(f32_to_bf16_rne(reinterpret_cast<const float*>(a.v)[e]));
+      }
+    }
+    kx[i][d] = kf;
+    vx[i][d] = vf;
+  }
+  __syncthreads();
+
+  const int M = (cell.kind == KIND_Q2) ? 3 : 15;
+  // K: one group per channel over the 32 tokens.
+  for (int d = tid; d < D; d += blockDim.x)
+    quantize_group([&](int i) { return (double)kx[i][d]; }, M, &kc[0][d], D, &kmeta[d]);
+  // V: one group per token over each run of 32 channels.
+  for (int task = tid; task < kGroup * (D / kGroup); task += blockDim.x) {
+    const int i = task / (D / kGroup), e = task % (D / kGroup);
+    quantize_group([&](int j) { return (double)vx[i][e * kGroup + j]; }, M, &vc[i][e * kGroup], 1, &vmeta[i][e]);
+  }
+  __syncthreads();
+
+  const int rec = record_bytes(cell.kind, D);
+  for (int half = 0; half < 2; ++half) {
+    const int j = 2 * g + half;
+    const int phys = a.block_table[(size_t)b * a.bt_stride + j];
+    uint32_t* r = reinterpret_cast<uint32_t*>(a.ws + cell.pool_off + ((size_t)phys * a.n_heads + h) * rec);
+    const int t0 = half * kBlock;
+    if (cell.kind == KIND_KIVI4) {
+      // K4: D/8 columns x 16 tokens; V4: D channels x 2 words.
+      for (int idx = tid; idx < (D / 8) * kBlock; idx += blockDim.x) {
+        const int w = idx / kBlock, t = idx % kBlock;
+        uint32_t word = 0;
+        for (int c = 0; c < 8; ++c) word |= (uint32_t)kc[t0 + t][8 * w + c] << (4 * c);
+        r[idx] = word;
+      }
+      for (int idx = tid; idx < D * 2; idx += blockDim.x) {
+        const int d = idx / 2, jj = idx % 2;
+        uint32_t word = 0;
+        for (int tp = 0; tp < 8; ++tp) word |= (uint32_t)vc[t0 + 8 * jj + tp][d] << (8 * (tp % 4) + 4 * (tp / 4));
+        r[off_v_kivi(D) / 4 + idx] = word;
+      }
+      for (int c = tid; c < D / 2; c += blockDim.x) r[off_kmeta_kivi(D) / 4 + c] = kmeta[half * (D / 2) + c];
+      for (int idx = tid; idx < kBlock * (D / kGroup); idx += blockDim.x)
+        r[off_vmeta_kivi(D) / 4 + idx] = vmeta[t0 + idx / (D / kGroup)][idx % (D / kGroup)];
+    } else {
+      const bool q4 = cell.kind == KIND_Q4;
+      // K planes: D/16 columns x 16 tokens.
+      for (int idx = tid; idx < (D / 16) * kBlock; idx += blockDim.x) {
+        const int w = idx / kBlock, t = idx % kBlock;
+        uint32_t hi = 0, lo = 0;
+        for (int c = 0; c < 16; ++c) {
+          const uint32_t code = kc[t0 + t][16 * w + c];
+          if (q4) {
+            hi |= (code >> 2) << (2 * c);
+            lo |= (code & 3u) << (2 * c);
+          } else {
+            hi |= code << (2 * c);
+          }
+        }
+        r[idx] = hi;
+        if (q4) r[off_klo(D) / 4 + idx] = lo;
+      }
+      // V planes: one word per channel, token t at bit 8*(t%4) + 2*(t/4).
+      for (int d = tid; d < D; d += blockDim.x) {
+        uint32_t hi = 0, lo = 0;
+        for (int t = 0; t < kBlock; ++t) {
+          const uint32_t code = vc[t0 + t][d];
+          const int sh = 8 * (t % 4) + 2 * (t / 4);
+          if (q4) {
+            hi |= (code >> 2) << sh;
+            lo |= (code & 3u) << sh;
+          } else {
+            hi |= code << sh;
+          }
+        }
+        r[off_v_planes(D) / 4 + d] = hi;
+        if (q4) r[off_vlo(D) / 4 + d] = lo;
+      }
+      for (int c = tid; c < D / 2; c += blockDim.x) r[off_kmeta_planes(D) / 4 + c] = kmeta[half * (D / 2) + c];
+      for (int idx = tid; idx < kBlock * (D / kGroup); idx += blockDim.x)
+        r[off_vmeta_planes(D) / 4 + idx] = vmeta[t0 + idx / (D / kGroup)][idx % (D / kGroup)];
+    }
+  }
+}
+
+template <int D>
+__global__ void __launch_bounds__(256) k_write_tail(AppendArgs a) {
+  const int b = blockIdx.z % a.n_seqs;
+  const int ci = blockIdx.z / a.n_seqs;
+  const int h = blockIdx.y;
+  const AppendCell cell = a.cells[ci];
+  const int L0 = a.seq_lens[b];
+  const int end = L0 + a.n_new;
+  const int first = max(L0, (end / kGroup) * kGroup);   // first position that stays in the tail
+  const int cnt = end - first;
+  if (cnt <= 0) return;
+  const int slot = a.seq_slots ? a.seq_slots[b] : b;
+  uint16_t* tail = reinterpret_cast<uint16_t*>(a.ws + cell.tail_off) + ((size_t)slot * a.n_heads + h) * tail_elems(D);
+  for (int idx = threadIdx.x; idx < cnt * D; idx += blockDim.x) {
+    const int i = idx / D, d = idx % D;
+    const int p = first + i;
+    const size_t e = ((((size_t)cell.in_cell * a.n_seqs + b) * a.n_new + (p - L0)) * a.n_heads + h) * D + d;
+    uint16_t kb, vb;
+    if (a.kv_bf16) {
+      kb = reinterpret_cast<const uint16_t*>(a.k)[e];
+      vb = reinterpret_cast<const uint16_t*>(a.v)[e];
+    } else {
+      kb = f32_to_bf16_rne(reinterpret_cast<const float*>(a.k)[e]);
+      vb = f32_to_bf16_rne(reinterpret_cast<const float*>(a.v)[e]);
+    }
+    tail[(0 * kGroup + (p % kGroup)) * D + d] = kb;
+    tail[(1 * kGroup + (p % kGroup)) * D + d] = vb;
+  }
+}
+
+// Host launcher: quantize completed groups, then update tails (same stream).
+hipError_t launch_append(const AppendArgs& a, int head_dim, hipStream_t stream) {
+  if (a.n_cells == 0 || a.n_seqs == 0 || a.n_new == 0) return hipSuccess;
+  const int slots = a.n_new / kGroup + 1;   // groups one append can complete
+  dim3 grid_q(slots, a.n_heads, a.n_cells * a.n_seqs);
+  dim3 grid_t(1, a.n_heads, a.n_cells * a.n_seqs);
+  if (head_dim == 128) {
+    hipLaunchKernelGGL(k_quantize_groups<128>, grid_q, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(k_write_tail<128>, grid_t, dim3(256), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL(k_quantize_groups<64>, grid_q, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(k_write_tail<64>, grid_t, dim3(256), 0, stream, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace lkv

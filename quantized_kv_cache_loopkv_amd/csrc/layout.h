@@ -1,0 +1,80 @@
+// Record layout, kinds and launch descriptors shared by the host runtime and the kernels.
+//
+// Storage follows "LoopKV: Loop-Aware KV Cache Compression for Serving Looped
+// Transformers" (arXiv:2611.04137), Abstract: each (loop, layer) cell is 4-bit
+// (high and low 2-bit planes kept apart so a loop can read only the high
+// bits), 2-bit, or a reuse of the final loop's KV. Byte layouts are spelled
+// out in include/loopkv.h.
+#pragma once
+#include <stdint.h>
+
+namespace lkv {
+
+constexpr int kGroup = 32;      // tokens per K group / channels per V group
+constexpr int kBlock = 16;      // tokens per paged block
+constexpr int kMaxCells = 128;
+constexpr int kMaxLen = 32768;
+
+// Kinds as the kernels see them (the storage a row reads).
+enum : int32_t { KIND_Q4 = 0, KIND_Q2 = 1, KIND_SHARE = 2, KIND_KIVI4 = 3 };
+
+// Byte offsets inside one record, for head dim D.
+__host__ __device__ constexpr int off_k(int) { return 0; }
+__host__ __device__ constexpr int off_v_planes(int D) { return 4 * D; }
+__host__ __device__ constexpr int off_kmeta_planes(int D) { return 8 * D; }
+__host__ __device__ constexpr int off_vmeta_planes(int D) { return 10 * D; }
+__host__ __device__ constexpr int off_klo(int D) { return 12 * D; }
+__host__ __device__ constexpr int off_vlo(int D) { return 16 * D; }
+__host__ __device__ constexpr int off_v_kivi(int D) { return 8 * D; }
+__host__ __device__ constexpr int off_kmeta_kivi(int D) { return 16 * D; }
+__host__ __device__ constexpr int off_vmeta_kivi(int D) { return 18 * D; }
+
+__host__ __device__ constexpr int record_bytes(int kind, int D) {
+  return kind == KIND_Q2 ? 12 * D : 20 * D;
+}
+// Tail of one (cell, slot, head): [2 (K, V)][32][D] bf16.
+__host__ __device__ constexpr int tail_elems(int D) { return 2 * kGroup * D; }
+
+// Per storing cell, for the append kernels.
+struct AppendCell {
+  uint64_t pool_off;   // byte offset of the cell's pool in the workspace
+  uint64_t tail_off;   // byte offset of the cell's tails
+  int32_t in_cell;     // index of the cell in the k/v input
+  int32_t kind;        // KIND_Q4 / KIND_Q2 / KIND_KIVI4
+};
+
+struct AppendArgs {
+  uint8_t* ws;
+  const void* k;
+  const void* v;
+  const int32_t* seq_slots;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  int32_t kv_bf16;
+  int32_t n_seqs, n_new, n_heads, bt_stride, n_cells;
+  AppendCell cells[kMaxCells];
+};
+
+// Per decoded cell, for the decode kernel.
+struct DecodeCell {
+  uint64_t pool_off;   // pool of the storage cell
+  uint64_t tail_off;   // tails of the storage cell
+  int32_t kind;        // kind of the storage cell (KIND_Q4 / KIND_Q2 / KIND_KIVI4)
+  int32_t pad;
+};
+
+struct DecodeArgs {
+  const uint8_t* ws;
+  const void* q;
+  void* out;
+  uint32_t* sel_mask;
+  const int32_t* seq_slots;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  int32_t q_bf16, out_bf16;
+  int32_t n_seqs, n_heads, bt_stride, max_len, sel_words, n_cells;
+  float tau, sm_scale;
+  DecodeCell cells[kMaxCells];
+};
+
+}  // namespace lkv

@@ -1,0 +1,287 @@
+// Host runtime of the C ABI declared in include/loopkv.h: plan validation,
+// workspace carving, argument checks and kernel launches. Nothing here touches
+// the GPU except the launches themselves, so every validation path runs (and is
+// tested) on a machine without a GPU.
+//
+// Plan semantics follow "LoopKV: Loop-Aware KV Cache Compression for Serving
+// Looped Transformers" (arXiv:2611.04137), Abstract: a cell is 4-bit, 2-bit or
+// a reuse of the final loop's KV of its layer.
+#include <hip/hip_runtime.h>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "loopkv.h"
+#include "layout.h"
+
+namespace lkv {
+hipError_t launch_append(const AppendArgs& a, int head_dim, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs& a, int head_dim, hipStream_t stream);
+size_t decode_lds_bytes(int max_len, int head_dim);
+}  // namespace lkv
+
+struct loopkv_ctx {
+  loopkv_config cfg;
+  bool has_plan = false;
+  std::vector<uint8_t> kinds;     // per cell, loopkv_cell_kind
+  std::vector<int> storage;       // per cell: cell whose cache it reads
+  std::vector<size_t> pool_off;   // per cell (valid for storing cells)
+  std::vector<size_t> tail_off;
+  size_t ws_need = 0;
+  uint8_t* ws = nullptr;
+  size_t ws_bytes = 0;
+};
+
+namespace {
+thread_local std::string g_err;
+
+loopkv_status fail(loopkv_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+loopkv_status fail(loopkv_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+loopkv_status ok() {
+  g_err.clear();
+  return LOOPKV_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+int n_cells(const loopkv_ctx* c) { return c->cfg.n_loops * c->cfg.n_layers; }
+
+int device_kind(const loopkv_ctx* c, int storage_cell) {
+  if (c->cfg.layout == LOOPKV_LAYOUT_KIVI4) return lkv::KIND_KIVI4;
+  return c->kinds[storage_cell] == LOOPKV_CELL_Q2 ? lkv::KIND_Q2 : lkv::KIND_Q4;
+}
+
+// Resolve (loop, layer) to a list of cells: (-1, -1) = all cells.
+loopkv_status resolve_cells(const loopkv_ctx* c, int loop, int layer, int* first, int* count) {
+  if (loop == -1 && layer == -1) {
+    *first = 0;
+    *count = n_cells(c);
+    return LOOPKV_OK;
+  }
+  if (loop < 0 || loop >= c->cfg.n_loops || layer < 0 || layer >= c->cfg.n_layers)
+    return fail(LOOPKV_ERR_PLAN, "cell (%d, %d) out of range for %d loops x %d layers", loop, layer,
+                c->cfg.n_loops, c->cfg.n_layers);
+  *first = loop * c->cfg.n_layers + layer;
+  *count = 1;
+  return LOOPKV_OK;
+}
+
+loopkv_status check_ready(const loopkv_ctx* c) {
+  if (!c) return fail(LOOPKV_ERR_INVALID_ARG, "null context");
+  if (!c->has_plan) return fail(LOOPKV_ERR_PLAN, "no plan loaded");
+  if (!c->ws) return fail(LOOPKV_ERR_WORKSPACE, "no workspace bound");
+  return LOOPKV_OK;
+}
+}  // namespace
+
+extern "C" {
+
+const char* loopkv_last_error(void) { return g_err.c_str(); }
+
+loopkv_status loopkv_create(const loopkv_config* cfg, loopkv_ctx** out) {
+  if (!cfg || !out) return fail(LOOPKV_ERR_INVALID_ARG, "null argument");
+  *out = nullptr;
+  if (cfg->n_loops < 1 || cfg->n_layers < 1 || cfg->n_heads < 1 || cfg->num_blocks < 1 || cfg->max_seqs < 1)
+    return fail(LOOPKV_ERR_INVALID_ARG, "n_loops, n_layers, n_heads, num_blocks and max_seqs must be >= 1");
+  if (cfg->head_dim != 64 && cfg->head_dim != 128)
+    return fail(LOOPKV_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)", cfg->head_dim);
+  if (cfg->group_size != lkv::kGroup) return fail(LOOPKV_ERR_UNSUPPORTED, "group_size must be 32");
+  if (cfg->block_tokens != lkv::kBlock) return fail(LOOPKV_ERR_UNSUPPORTED, "block_tokens must be 16");
+  if ((long long)cfg->n_loops * cfg->n_layers > lkv::kMaxCells)
+    return fail(LOOPKV_ERR_UNSUPPORTED, "at most %d cells", lkv::kMaxCells);
+  if (cfg->layout != LOOPKV_LAYOUT_PLANES && cfg->layout != LOOPKV_LAYOUT_KIVI4)
+    return fail(LOOPKV_ERR_INVALID_ARG, "unknown layout %d", cfg->layout);
+  loopkv_ctx* c = new loopkv_ctx();
+  c->cfg = *cfg;
+  *out = c;
+  return ok();
+}
+
+void loopkv_destroy(loopkv_ctx* ctx) { delete ctx; }
+
+loopkv_status loopkv_plan(loopkv_ctx* c, const uint8_t* kinds) {
+  if (!c || !kinds) return fail(LOOPKV_ERR_INVALID_ARG, "null argument");
+  const int n = n_cells(c);
+  const int L = c->cfg.n_loops, NL = c->cfg.n_layers;
+  for (int i = 0; i < n; ++i) {
+    if (kinds[i] > LOOPKV_CELL_SHARE) return fail(LOOPKV_ERR_PLAN, "cell %d: kind %u > 2", i, kinds[i]);
+    if (kinds[i] == LOOPKV_CELL_SHARE && i / NL == L - 1)
+      return fail(LOOPKV_ERR_PLAN, "cell %d: the final loop cannot reuse its own KV", i);
+    if (c->cfg.layout == LOOPKV_LAYOUT_KIVI4 && kinds[i] != LOOPKV_CELL_Q4)
+      return fail(LOOPKV_ERR_PLAN, "KIVI-4 layout needs an all-4-bit plan (cell %d)", i);
+  }
+  c->kinds.assign(kinds, kinds + n);
+  c->storage.resize(n);
+  c->pool_off.assign(n, 0);
+  c->tail_off.assign(n, 0);
+  const int D = c->cfg.head_dim, H = c->cfg.n_heads;
+  size_t off = 0;
+  for (int i = 0; i < n; ++i) {
+    c->storage[i] = kinds[i] == LOOPKV_CELL_SHARE ? (L - 1) * NL + i % NL : i;
+    if (kinds[i] == LOOPKV_CELL_SHARE) continue;
+    c->pool_off[i] = off;
+    off = align256(off + (size_t)c->cfg.num_blocks * H * lkv::record_bytes(device_kind(c, i), D));
+  }
+  for (int i = 0; i < n; ++i) {
+    if (kinds[i] == LOOPKV_CELL_SHARE) continue;
+    c->tail_off[i] = off;
+    off = align256(off + (size_t)c->cfg.max_seqs * H * lkv::tail_elems(D) * 2);
+  }
+  for (int i = 0; i < n; ++i) {
+    if (kinds[i] != LOOPKV_CELL_SHARE) continue;
+    c->pool_off[i] = c->pool_off[c->storage[i]];
+    c->tail_off[i] = c->tail_off[c->storage[i]];
+  }
+  c->ws_need = off;
+  c->has_plan = true;
+  c->ws = nullptr;
+  c->ws_bytes = 0;
+  return ok();
+}
+
+loopkv_status loopkv_workspace_bytes(const loopkv_ctx* c, size_t* bytes) {
+  if (!c || !bytes) return fail(LOOPKV_ERR_INVALID_ARG, "null argument");
+  if (!c->has_plan) return fail(LOOPKV_ERR_PLAN, "no plan loaded");
+  *bytes = c->ws_need;
+  return ok();
+}
+
+loopkv_status loopkv_bind_workspace(loopkv_ctx* c, void* dev, size_t bytes) {
+  if (!c || !dev) return fail(LOOPKV_ERR_INVALID_ARG, "null argument");
+  if (!c->has_plan) return fail(LOOPKV_ERR_PLAN, "no plan loaded");
+  if (((uintptr_t)dev & 255u) != 0) return fail(LOOPKV_ERR_WORKSPACE, "workspace not 256-byte aligned");
+  if (bytes < c->ws_need)
+    return fail(LOOPKV_ERR_WORKSPACE, "workspace of %zu bytes, plan needs %zu", bytes, c->ws_need);
+  c->ws = static_cast<uint8_t*>(dev);
+  c->ws_bytes = bytes;
+  return ok();
+}
+
+loopkv_status loopkv_cell_storage(const loopkv_ctx* c, int32_t loop, int32_t layer, size_t* pool_offset,
+                                  size_t* tail_offset, size_t* record_bytes, int32_t* storage_cell) {
+  if (!c) return fail(LOOPKV_ERR_INVALID_ARG, "null context");
+  if (!c->has_plan) return fail(LOOPKV_ERR_PLAN, "no plan loaded");
+  if (loop < 0 || layer < 0) return fail(LOOPKV_ERR_PLAN, "cell (%d, %d) out of range", loop, layer);
+  int first, count;
+  loopkv_status s = resolve_cells(c, loop, layer, &first, &count);
+  if (s != LOOPKV_OK) return s;
+  const int st = c->storage[first];
+  if (pool_offset) *pool_offset = c->pool_off[st];
+  if (tail_offset) *tail_offset = c->tail_off[st];
+  if (record_bytes) *record_bytes = lkv::record_bytes(device_kind(c, st), c->cfg.head_dim);
+  if (storage_cell) *storage_cell = st;
+  return ok();
+}
+
+loopkv_status loopkv_append(loopkv_ctx* c, hipStream_t stream, int32_t loop, int32_t layer, const void* k,
+                            const void* v, int32_t kv_dtype, int32_t n_seqs, int32_t n_new,
+                            const int32_t* seq_slots, const int32_t* block_table, int32_t bt_stride,
+                            const int32_t* seq_lens) {
+  loopkv_status s = check_ready(c);
+  if (s != LOOPKV_OK) return s;
+  int first, count;
+  s = resolve_cells(c, loop, layer, &first, &count);
+  if (s != LOOPKV_OK) return s;
+  if (kv_dtype != LOOPKV_F32 && kv_dtype != LOOPKV_BF16) return fail(LOOPKV_ERR_INVALID_ARG, "bad kv dtype %d", kv_dtype);
+  if (n_seqs < 0 || n_new < 0) return fail(LOOPKV_ERR_INVALID_ARG, "n_seqs and n_new must be >= 0");
+  if (!seq_slots && n_seqs > c->cfg.max_seqs)
+    return fail(LOOPKV_ERR_CAPACITY, "n_seqs %d > max_seqs %d with identity slots", n_seqs, c->cfg.max_seqs);
+  if (n_seqs == 0 || n_new == 0) return ok();
+  if (!k || !v || !block_table || !seq_lens) return fail(LOOPKV_ERR_INVALID_ARG, "null device pointer");
+  if (bt_stride < 1) return fail(LOOPKV_ERR_INVALID_ARG, "bt_stride must be >= 1");
+  lkv::AppendArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.ws = c->ws;
+  a.k = k;
+  a.v = v;
+  a.seq_slots = seq_slots;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.kv_bf16 = kv_dtype == LOOPKV_BF16;
+  a.n_seqs = n_seqs;
+  a.n_new = n_new;
+  a.n_heads = c->cfg.n_heads;
+  a.bt_stride = bt_stride;
+  int nc = 0;
+  for (int i = first; i < first + count; ++i) {
+    if (c->kinds[i] == LOOPKV_CELL_SHARE) continue;
+    a.cells[nc].pool_off = c->pool_off[i];
+    a.cells[nc].tail_off = c->tail_off[i];
+    a.cells[nc].in_cell = count == 1 ? 0 : i;
+    a.cells[nc].kind = device_kind(c, i);
+    ++nc;
+  }
+  a.n_cells = nc;
+  if (nc == 0) return ok();
+  hipError_t e = lkv::launch_append(a, c->cfg.head_dim, stream);
+  if (e != hipSuccess) return fail(LOOPKV_ERR_HIP, "append launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+loopkv_status loopkv_decode_attn(loopkv_ctx* c, hipStream_t stream, int32_t loop, int32_t layer, const void* q,
+                                 int32_t q_dtype, int32_t n_seqs, const int32_t* seq_slots,
+                                 const int32_t* block_table, int32_t bt_stride, const int32_t* seq_lens,
+                                 int32_t max_len, float tau, float sm_scale, void* out, int32_t out_dtype,
+                                 uint32_t* sel_mask) {
+  loopkv_status s = check_ready(c);
+  if (s != LOOPKV_OK) return s;
+  int first, count;
+  s = resolve_cells(c, loop, layer, &first, &count);
+  if (s != LOOPKV_OK) return s;
+  if (q_dtype != LOOPKV_F32 && q_dtype != LOOPKV_BF16) return fail(LOOPKV_ERR_INVALID_ARG, "bad q dtype %d", q_dtype);
+  if (out_dtype != LOOPKV_F32 && out_dtype != LOOPKV_BF16)
+    return fail(LOOPKV_ERR_INVALID_ARG, "bad out dtype %d", out_dtype);
+  if (!(tau >= 0.f)) return fail(LOOPKV_ERR_INVALID_ARG, "tau must be >= 0 (got %g)", (double)tau);
+  if (!(sm_scale > 0.f) || !std::isfinite(sm_scale))
+    return fail(LOOPKV_ERR_INVALID_ARG, "sm_scale must be finite and > 0 (got %g)", (double)sm_scale);
+  if (n_seqs < 0) return fail(LOOPKV_ERR_INVALID_ARG, "n_seqs must be >= 0");
+  if (!seq_slots && n_seqs > c->cfg.max_seqs)
+    return fail(LOOPKV_ERR_CAPACITY, "n_seqs %d > max_seqs %d with identity slots", n_seqs, c->cfg.max_seqs);
+  if (max_len < 0 || max_len > LOOPKV_MAX_LEN)
+    return fail(LOOPKV_ERR_CAPACITY, "max_len %d outside [0, %d]", max_len, LOOPKV_MAX_LEN);
+  if (bt_stride < 1 || (long long)bt_stride * lkv::kBlock < max_len)
+    return fail(LOOPKV_ERR_CAPACITY, "bt_stride %d too small for max_len %d", bt_stride, max_len);
+  if (n_seqs == 0) return ok();
+  if (!q || !out || !block_table || !seq_lens) return fail(LOOPKV_ERR_INVALID_ARG, "null device pointer");
+  lkv::DecodeArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.ws = c->ws;
+  a.q = q;
+  a.out = out;
+  a.sel_mask = sel_mask;
+  a.seq_slots = seq_slots;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.q_bf16 = q_dtype == LOOPKV_BF16;
+  a.out_bf16 = out_dtype == LOOPKV_BF16;
+  a.n_seqs = n_seqs;
+  a.n_heads = c->cfg.n_heads;
+  a.bt_stride = bt_stride;
+  a.max_len = max_len;
+  a.sel_words = (max_len + 31) / 32;
+  a.n_cells = count;
+  a.tau = tau;
+  a.sm_scale = sm_scale;
+  for (int i = 0; i < count; ++i) {
+    const int st = c->storage[first + i];
+    a.cells[i].pool_off = c->pool_off[st];
+    a.cells[i].tail_off = c->tail_off[st];
+    a.cells[i].kind = device_kind(c, st);
+  }
+  hipError_t e = lkv::launch_decode(a, c->cfg.head_dim, stream);
+  if (e != hipSuccess) return fail(LOOPKV_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // extern "C"

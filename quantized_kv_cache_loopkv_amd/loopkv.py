@@ -1,0 +1,213 @@
+"""Thin ctypes binding of libloopkv.so (include/loopkv.h).
+
+Argument marshalling only: every step of append and decode runs in the HIP
+kernels of the library. torch supplies device memory (tensors) and the stream
+(``torch.cuda.current_stream()``). If the library is missing this module raises;
+there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Sequence
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libloopkv.so")
+
+OK, ERR_INVALID_ARG, ERR_PLAN, ERR_WORKSPACE, ERR_CAPACITY, ERR_UNSUPPORTED, ERR_HIP = range(7)
+CELL_Q4, CELL_Q2, CELL_SHARE = 0, 1, 2
+F32, BF16 = 0, 1
+LAYOUT_PLANES, LAYOUT_KIVI4 = 0, 1
+MAX_LEN = 32768
+MAX_CELLS = 128
+
+EXPORTED = ["loopkv_create", "loopkv_destroy", "loopkv_plan", "loopkv_workspace_bytes",
+            "loopkv_bind_workspace", "loopkv_cell_storage", "loopkv_append", "loopkv_decode_attn",
+            "loopkv_last_error"]
+
+
+class LoopKVError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"loopkv status {status}: {msg}")
+        self.status = status
+
+
+class _Config(ctypes.Structure):
+    _fields_ = [("n_loops", ctypes.c_int32), ("n_layers", ctypes.c_int32), ("n_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("group_size", ctypes.c_int32), ("block_tokens", ctypes.c_int32),
+                ("num_blocks", ctypes.c_int32), ("max_seqs", ctypes.c_int32), ("layout", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libloopkv.so (after torch, so both share torch's HIP runtime)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build()")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float
+    L.loopkv_create.argtypes = [ctypes.POINTER(_Config), ctypes.POINTER(vp)]
+    L.loopkv_destroy.argtypes = [vp]
+    L.loopkv_destroy.restype = None
+    L.loopkv_plan.argtypes = [vp, ctypes.POINTER(ctypes.c_uint8)]
+    L.loopkv_workspace_bytes.argtypes = [vp, ctypes.POINTER(ctypes.c_size_t)]
+    L.loopkv_bind_workspace.argtypes = [vp, vp, ctypes.c_size_t]
+    L.loopkv_cell_storage.argtypes = [vp, i32, i32, ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_size_t),
+                                      ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(i32)]
+    L.loopkv_append.argtypes = [vp, vp, i32, i32, vp, vp, i32, i32, i32, vp, vp, i32, vp]
+    L.loopkv_decode_attn.argtypes = [vp, vp, i32, i32, vp, i32, i32, vp, vp, i32, vp, i32, f32, f32, vp, i32, vp]
+    L.loopkv_last_error.restype = ctypes.c_char_p
+    L.loopkv_last_error.argtypes = []
+    for name in ["loopkv_create", "loopkv_plan", "loopkv_workspace_bytes", "loopkv_bind_workspace",
+                 "loopkv_cell_storage", "loopkv_append", "loopkv_decode_attn"]:
+        getattr(L, name).restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def _check(status: int):
+    if status != OK:
+        raise LoopKVError(status, lib().loopkv_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+def _dev_i32(t: Optional[torch.Tensor], name: str, numel: Optional[int] = None):
+    if t is None:
+        return None
+    if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous int32 CUDA tensor")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{name} has {t.numel()} elements, needs {numel}")
+    return t
+
+
+class Context:
+    """One LoopKV cache: config, plan, caller-owned workspace."""
+
+    def __init__(self, n_loops: int, n_layers: int, n_heads: int, head_dim: int, num_blocks: int,
+                 max_seqs: int, layout: int = LAYOUT_PLANES):
+        self.cfg = _Config(n_loops, n_layers, n_heads, head_dim, 32, 16, num_blocks, max_seqs, layout)
+        h = ctypes.c_void_p()
+        _check(lib().loopkv_create(ctypes.byref(self.cfg), ctypes.byref(h)))
+        self._h = h
+        self.workspace = None
+        self.kinds = None
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value and _lib is not None:
+            _lib.loopkv_destroy(h)
+            self._h = None
+
+    @property
+    def n_cells(self) -> int:
+        return self.cfg.n_loops * self.cfg.n_layers
+
+    def plan(self, kinds: Sequence[int]):
+        arr = (ctypes.c_uint8 * self.n_cells)(*[int(k) for k in list(kinds)])
+        if len(list(kinds)) != self.n_cells:
+            raise ValueError(f"plan needs {self.n_cells} kinds")
+        _check(lib().loopkv_plan(self._h, arr))
+        self.kinds = [int(k) for k in kinds]
+        self.workspace = None
+
+    def workspace_bytes(self) -> int:
+        n = ctypes.c_size_t()
+        _check(lib().loopkv_workspace_bytes(self._h, ctypes.byref(n)))
+        return n.value
+
+    def bind(self, ws: torch.Tensor):
+        if not ws.is_cuda:
+            raise ValueError("workspace must be a CUDA tensor")
+        _check(lib().loopkv_bind_workspace(self._h, _ptr(ws), ws.numel() * ws.element_size()))
+        self.workspace = ws
+
+    def cell_storage(self, loop: int, layer: int) -> dict:
+        p, t, r = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+        s = ctypes.c_int32()
+        _check(lib().loopkv_cell_storage(self._h, loop, layer, ctypes.byref(p), ctypes.byref(t), ctypes.byref(r),
+                                         ctypes.byref(s)))
+        return {"pool_offset": p.value, "tail_offset": t.value, "record_bytes": r.value, "storage_cell": s.value}
+
+    def _cell(self, cell):
+        if cell is None:
+            return -1, -1
+        return int(cell[0]), int(cell[1])
+
+    def append(self, k: torch.Tensor, v: torch.Tensor, block_table: torch.Tensor, seq_lens: torch.Tensor,
+               cell=None, seq_slots: Optional[torch.Tensor] = None):
+        """k, v: [cells][n_seqs][n_new][H][D] (cell=None) or [n_seqs][n_new][H][D]."""
+        loop, layer = self._cell(cell)
+        if k.shape != v.shape or not k.is_contiguous() or not v.is_contiguous() or k.dtype != v.dtype:
+            raise ValueError("k and v must be contiguous tensors of one shape and dtype")
+        if cell is None:
+            if k.dim() != 5 or k.shape[0] != self.n_cells:
+                raise ValueError("whole-plan append needs k of shape [cells][n_seqs][n_new][H][D]")
+            n_seqs, n_new = k.shape[1], k.shape[2]
+        else:
+            if k.dim() != 4:
+                raise ValueError("single-cell append needs k of shape [n_seqs][n_new][H][D]")
+            n_seqs, n_new = k.shape[0], k.shape[1]
+        if k.shape[-2:] != (self.cfg.n_heads, self.cfg.head_dim):
+            raise ValueError("k trailing dims must be [H][D]")
+        bt = _dev_i32(block_table, "block_table", n_seqs)
+        _dev_i32(seq_lens, "seq_lens", n_seqs)
+        _dev_i32(seq_slots, "seq_slots", n_seqs)
+        bt_stride = bt.shape[-1] if bt.dim() == 2 else bt.numel()
+        _check(lib().loopkv_append(self._h, _stream(), loop, layer, _ptr(k), _ptr(v), _dtype_code(k), n_seqs, n_new,
+                                   _ptr(seq_slots), _ptr(bt), bt_stride, _ptr(seq_lens)))
+
+    def decode(self, q: torch.Tensor, block_table: torch.Tensor, seq_lens: torch.Tensor, max_len: int,
+               tau: float, sm_scale: Optional[float] = None, cell=None, out_dtype=torch.float32,
+               out: Optional[torch.Tensor] = None, sel_mask=False, seq_slots: Optional[torch.Tensor] = None):
+        """q: [cells][n_seqs][H][D] (cell=None) or [n_seqs][H][D]. Returns out (and sel_mask if asked)."""
+        loop, layer = self._cell(cell)
+        if not q.is_contiguous():
+            raise ValueError("q must be contiguous")
+        n_seqs = q.shape[1] if cell is None else q.shape[0]
+        if (cell is None and (q.dim() != 4 or q.shape[0] != self.n_cells)) or (cell is not None and q.dim() != 3):
+            raise ValueError("q has the wrong rank for this call")
+        D = self.cfg.head_dim
+        if sm_scale is None:
+            sm_scale = 1.0 / math.sqrt(D)
+        if out is None:
+            out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+        if out.shape != q.shape or not out.is_contiguous():
+            raise ValueError("out must be contiguous with q's shape")
+        sm = None
+        if sel_mask is True:
+            sm = torch.zeros((*q.shape[:-1], (max_len + 31) // 32), dtype=torch.int32, device=q.device)
+        elif isinstance(sel_mask, torch.Tensor):
+            sm = sel_mask
+        bt = _dev_i32(block_table, "block_table", n_seqs)
+        _dev_i32(seq_lens, "seq_lens", n_seqs)
+        _dev_i32(seq_slots, "seq_slots", n_seqs)
+        bt_stride = bt.shape[-1] if bt.dim() == 2 else bt.numel()
+        _check(lib().loopkv_decode_attn(self._h, _stream(), loop, layer, _ptr(q), _dtype_code(q), n_seqs,
+                                        _ptr(seq_slots), _ptr(bt), bt_stride, _ptr(seq_lens), int(max_len),
+                                        float(tau), float(sm_scale), _ptr(out), _dtype_code(out), _ptr(sm)))
+        if sm is not None:
+            return out, sm
+        return out

@@ -1,0 +1,99 @@
+// GPU side of the seeded input generator (no step of the attention method here).
+//
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as easy
+// as 1, 2, 3", SC'11) and the Irwin-Hall(12) normal draw defined in
+// synth/philox.py: element i of stream s evaluates Philox at counters
+// (i lo, i hi, s, 0) and (i lo, i hi, s, 1) under key (seed lo, seed hi); the
+// first twelve 16-bit halves h_j give z = (sum h_j - 393210) / 65536 exactly;
+// a scaled value is bf16_rne(z * f) with one float32 multiply.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+__device__ inline void philox(uint32_t c[4], uint32_t k0, uint32_t k1) {
+  for (int r = 0; r < 10; ++r) {
+    if (r) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c[0];
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c[2];
+    const uint32_t hi0 = (uint32_t)(p0 >> 32), lo0 = (uint32_t)p0;
+    const uint32_t hi1 = (uint32_t)(p1 >> 32), lo1 = (uint32_t)p1;
+    const uint32_t n0 = hi1 ^ c[1] ^ k0, n2 = hi0 ^ c[3] ^ k1;
+    c[0] = n0;
+    c[1] = lo1;
+    c[2] = n2;
+    c[3] = lo0;
+  }
+}
+
+__device__ inline float normal12(uint64_t seed, uint32_t stream, uint64_t i) {
+  uint32_t a[4] = {(uint32_t)i, (uint32_t)(i >> 32), stream, 0u};
+  uint32_t b[4] = {(uint32_t)i, (uint32_t)(i >> 32), stream, 1u};
+  philox(a, (uint32_t)seed, (uint32_t)(seed >> 32));
+  philox(b, (uint32_t)seed, (uint32_t)(seed >> 32));
+  int32_t s = 0;
+  for (int j = 0; j < 4; ++j) s += (int32_t)(a[j] & 0xffffu) + (int32_t)(a[j] >> 16);
+  for (int j = 0; j < 2; ++j) s += (int32_t)(b[j] & 0xffffu) + (int32_t)(b[j] >> 16);
+  return (float)(s - 393210) / 65536.0f;
+}
+
+__device__ inline uint16_t bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// out[((b * n_tok + i) * H + h) * D + d] for token t = t0 (or t0s[b]) + i, element
+// index ((b * T + t) * H + h) * D + d, factor factors[h * D + d].
+__global__ void k_kv(uint64_t seed, uint32_t stream, int B, int n_tok, int t0, const int32_t* t0s, int T, int H,
+                     int D, const float* factors, uint16_t* out) {
+  const size_t n = (size_t)B * n_tok * H * D;
+  for (size_t o = (size_t)blockIdx.x * blockDim.x + threadIdx.x; o < n; o += (size_t)gridDim.x * blockDim.x) {
+    const int d = (int)(o % D);
+    const int h = (int)((o / D) % H);
+    const int i = (int)((o / ((size_t)D * H)) % n_tok);
+    const int b = (int)(o / ((size_t)D * H * n_tok));
+    const int t = (t0s ? t0s[b] : t0) + i;
+    const uint64_t idx = (((uint64_t)b * T + t) * H + h) * D + d;
+    const float z = normal12(seed, stream, idx);
+    out[o] = bf16_rne(__fmul_rn(z, factors[h * D + d]));
+  }
+}
+
+__global__ void k_normal(uint64_t seed, uint32_t stream, uint64_t offset, size_t n, int as_bf16, void* out) {
+  for (size_t o = (size_t)blockIdx.x * blockDim.x + threadIdx.x; o < n; o += (size_t)gridDim.x * blockDim.x) {
+    const float z = normal12(seed, stream, offset + o);
+    if (as_bf16) reinterpret_cast<uint16_t*>(out)[o] = bf16_rne(z);
+    else reinterpret_cast<float*>(out)[o] = z;
+  }
+}
+
+unsigned grid_for(size_t n) {
+  size_t g = (n + 255) / 256;
+  if (g > 65536) g = 65536;
+  if (g == 0) g = 1;
+  return (unsigned)g;
+}
+}  // namespace
+
+extern "C" {
+
+// K or V values of one cell as bf16 bits, in the append input layout [B][n_tok][H][D].
+int synth_kv_bf16(hipStream_t s, uint64_t seed, uint32_t stream, int B, int n_tok, int t0, const int32_t* t0s,
+                  int T, int H, int D, const float* factors, uint16_t* out) {
+  const size_t n = (size_t)B * n_tok * H * D;
+  if (n == 0) return 0;
+  hipLaunchKernelGGL(k_kv, dim3(grid_for(n)), dim3(256), 0, s, seed, stream, B, n_tok, t0, t0s, T, H, D, factors, out);
+  return (int)hipGetLastError();
+}
+
+// n consecutive draws starting at element offset, as bf16 bits or float32.
+int synth_normal(hipStream_t s, uint64_t seed, uint32_t stream, uint64_t offset, size_t n, int as_bf16, void* out) {
+  if (n == 0) return 0;
+  hipLaunchKernelGGL(k_normal, dim3(grid_for(n)), dim3(256), 0, s, seed, stream, offset, n, as_bf16, out);
+  return (int)hipGetLastError();
+}
+}

@@ -1,0 +1,56 @@
+"""ctypes binding of synth/libloopkv_synth.so: the seeded generator drawn directly in HBM.
+
+Produces the same bits as ``synth.philox`` (the tests check it) so that caches
+too large for host memory can be built on the GPU.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libloopkv_synth.so")
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        vp = ctypes.c_void_p
+        L.synth_kv_bf16.argtypes = [vp, ctypes.c_uint64, ctypes.c_uint32, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp,
+                                    ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp]
+        L.synth_kv_bf16.restype = ctypes.c_int
+        L.synth_normal.argtypes = [vp, ctypes.c_uint64, ctypes.c_uint32, ctypes.c_uint64, ctypes.c_size_t, ctypes.c_int, vp]
+        L.synth_normal.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _s():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def kv_bf16(seed: int, stream: int, B: int, n_tok: int, t0: int, T: int, H: int, D: int,
+            factors: torch.Tensor, out: torch.Tensor, t0s: torch.Tensor = None):
+    """Fill out (bf16 [B][n_tok][H][D]) with stream values of tokens t0 + i (or t0s[b] + i)."""
+    assert out.dtype == torch.bfloat16 and out.is_contiguous() and out.numel() == B * n_tok * H * D
+    assert factors.dtype == torch.float32 and factors.is_cuda and factors.numel() == H * D
+    r = lib().synth_kv_bf16(_s(), seed, stream, B, n_tok, t0, None if t0s is None else ctypes.c_void_p(t0s.data_ptr()),
+                            T, H, D, ctypes.c_void_p(factors.data_ptr()), ctypes.c_void_p(out.data_ptr()))
+    if r != 0:
+        raise RuntimeError(f"synth_kv_bf16 failed: {r}")
+    return out
+
+
+def normal(seed: int, stream: int, offset: int, out: torch.Tensor):
+    """Fill out (bf16 or float32, contiguous) with draws offset .. offset + numel - 1."""
+    assert out.is_contiguous() and out.dtype in (torch.bfloat16, torch.float32)
+    r = lib().synth_normal(_s(), seed, stream, offset, out.numel(), int(out.dtype == torch.bfloat16),
+                           ctypes.c_void_p(out.data_ptr()))
+    if r != 0:
+        raise RuntimeError(f"synth_normal failed: {r}")
+    return out

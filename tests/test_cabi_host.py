@@ -1,0 +1,190 @@
+"""Host-side checks of the C ABI (no GPU needed): exported symbols, validation and error codes.
+
+Every call here fails validation (or touches no device memory), so nothing is
+ever enqueued on a GPU.
+"""
+import ctypes
+import math
+import os
+import re
+
+import numpy as np
+import pytest
+
+import quantized_kv_cache_loopkv_amd as lkv
+from quantized_kv_cache_loopkv_amd import loopkv as B
+from synth import recipes as R
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE_DEV = 0x7f0000000000   # 256-byte aligned, never dereferenced on the host
+
+
+def _declared(header):
+    text = open(os.path.join(ROOT, "include", header)).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(loopkv_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared("loopkv.h")
+    assert set(names) == set(B.EXPORTED)
+    L = lkv.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    # and the exported dynamic symbols are plain C names
+    syms = os.popen(f"nm -D --defined-only {B.LIB_PATH}").read()
+    for n in names:
+        assert re.search(rf"\bT {n}\b", syms), n
+
+
+def test_synth_library_exports():
+    from synth import gpu as G
+    L = G.lib()
+    assert hasattr(L, "synth_kv_bf16") and hasattr(L, "synth_normal")
+
+
+def _cfg(**kw):
+    base = dict(n_loops=4, n_layers=24, n_heads=16, head_dim=128, group_size=32, block_tokens=16,
+                num_blocks=64, max_seqs=4, layout=0)
+    base.update(kw)
+    return B._Config(*[base[k] for k, _ in B._Config._fields_])
+
+
+def _create(**kw):
+    h = ctypes.c_void_p()
+    s = lkv.lib().loopkv_create(ctypes.byref(_cfg(**kw)), ctypes.byref(h))
+    return s, h
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=96), B.ERR_UNSUPPORTED), (dict(head_dim=256), B.ERR_UNSUPPORTED),
+    (dict(group_size=64), B.ERR_UNSUPPORTED), (dict(block_tokens=32), B.ERR_UNSUPPORTED),
+    (dict(n_loops=0), B.ERR_INVALID_ARG), (dict(n_heads=0), B.ERR_INVALID_ARG),
+    (dict(num_blocks=0), B.ERR_INVALID_ARG), (dict(max_seqs=0), B.ERR_INVALID_ARG),
+    (dict(n_loops=6, n_layers=24), B.ERR_UNSUPPORTED), (dict(layout=5), B.ERR_INVALID_ARG),
+])
+def test_create_rejects(kw, status):
+    s, h = _create(**kw)
+    assert s == status and not h.value
+    assert lkv.lib().loopkv_last_error().decode()
+
+
+def test_plan_rules_and_workspace_sizes():
+    ctx = lkv.Context(4, 24, 16, 128, 1024, 32)
+    with pytest.raises(lkv.LoopKVError) as e:
+        ctx.workspace_bytes()
+    assert e.value.status == B.ERR_PLAN
+    bad = [0] * 96
+    bad[80] = 2          # reuse cell in the final loop
+    with pytest.raises(lkv.LoopKVError) as e:
+        ctx.plan(bad)
+    assert e.value.status == B.ERR_PLAN
+    bad = [0] * 96
+    bad[3] = 3
+    with pytest.raises(lkv.LoopKVError):
+        ctx.plan(bad)
+    plan = R.random_plan(4, 24, 0).reshape(-1).tolist()
+    ctx.plan(plan)
+    assert lkv.lib().loopkv_last_error().decode() == ""
+    pools = 0
+    for c in range(96):
+        st = ctx.cell_storage(*divmod(c, 24))
+        if plan[c] == 2:
+            assert st["storage_cell"] == 72 + c % 24
+        else:
+            assert st["storage_cell"] == c
+            assert st["pool_offset"] % 256 == 0 and st["tail_offset"] % 256 == 0
+            pools += 1024 * 16 * st["record_bytes"]
+    kctx = lkv.Context(4, 24, 16, 128, 1024, 32, layout=lkv.LAYOUT_KIVI4)
+    with pytest.raises(lkv.LoopKVError):
+        kctx.plan(plan)                      # KIVI-4 needs all 4-bit
+    kctx.plan([0] * 96)
+    kpools = 96 * 1024 * 16 * 2560
+    assert abs(pools / kpools - 0.68125) < 1e-12
+    tails = 77 * 32 * 16 * 2 * 32 * 128 * 2
+    assert ctx.workspace_bytes() == pools + tails
+    assert kctx.workspace_bytes() == kpools + 96 * 32 * 16 * 2 * 32 * 128 * 2
+
+
+def _ready_ctx(layout=0):
+    ctx = lkv.Context(2, 3, 2, 64, 16, 2, layout=layout)
+    ctx.plan([0, 1, 2, 0, 0, 1] if layout == 0 else [0] * 6)
+    L = lkv.lib()
+    need = ctx.workspace_bytes()
+    assert L.loopkv_bind_workspace(ctx._h, ctypes.c_void_p(FAKE_DEV + 8), need) == B.ERR_WORKSPACE
+    assert L.loopkv_bind_workspace(ctx._h, ctypes.c_void_p(FAKE_DEV), need - 1) == B.ERR_WORKSPACE
+    assert L.loopkv_bind_workspace(ctx._h, ctypes.c_void_p(FAKE_DEV), need) == B.OK
+    return ctx
+
+
+def _decode(ctx, **kw):
+    a = dict(loop=-1, layer=-1, q=FAKE_DEV, q_dtype=1, n_seqs=2, slots=None, bt=FAKE_DEV, bt_stride=4,
+             lens=FAKE_DEV, max_len=64, tau=0.01, sm=0.125, out=FAKE_DEV, out_dtype=0, mask=None)
+    a.update(kw)
+    vp = ctypes.c_void_p
+    return lkv.lib().loopkv_decode_attn(ctx._h, None, a["loop"], a["layer"], vp(a["q"]), a["q_dtype"], a["n_seqs"],
+                                        vp(a["slots"]), vp(a["bt"]), a["bt_stride"], vp(a["lens"]), a["max_len"],
+                                        ctypes.c_float(a["tau"]), ctypes.c_float(a["sm"]), vp(a["out"]),
+                                        a["out_dtype"], vp(a["mask"]))
+
+
+def _append(ctx, **kw):
+    a = dict(loop=-1, layer=-1, k=FAKE_DEV, v=FAKE_DEV, dt=1, n_seqs=2, n_new=1, slots=None, bt=FAKE_DEV,
+             bt_stride=4, lens=FAKE_DEV)
+    a.update(kw)
+    vp = ctypes.c_void_p
+    return lkv.lib().loopkv_append(ctx._h, None, a["loop"], a["layer"], vp(a["k"]), vp(a["v"]), a["dt"], a["n_seqs"],
+                                   a["n_new"], vp(a["slots"]), vp(a["bt"]), a["bt_stride"], vp(a["lens"]))
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(tau=-0.1), B.ERR_INVALID_ARG), (dict(tau=math.nan), B.ERR_INVALID_ARG),
+    (dict(sm=0.0), B.ERR_INVALID_ARG), (dict(sm=math.inf), B.ERR_INVALID_ARG),
+    (dict(q_dtype=2), B.ERR_INVALID_ARG), (dict(out_dtype=-1), B.ERR_INVALID_ARG),
+    (dict(max_len=32769, bt_stride=4096), B.ERR_CAPACITY), (dict(max_len=65), B.ERR_CAPACITY),
+    (dict(max_len=-1), B.ERR_CAPACITY), (dict(bt_stride=0), B.ERR_CAPACITY),
+    (dict(loop=2, layer=0), B.ERR_PLAN), (dict(loop=0, layer=3), B.ERR_PLAN), (dict(loop=-1, layer=0), B.ERR_PLAN),
+    (dict(n_seqs=3), B.ERR_CAPACITY), (dict(n_seqs=-1), B.ERR_INVALID_ARG),
+    (dict(q=0), B.ERR_INVALID_ARG), (dict(out=0), B.ERR_INVALID_ARG), (dict(bt=0), B.ERR_INVALID_ARG),
+    (dict(lens=0), B.ERR_INVALID_ARG),
+])
+def test_decode_validation(kw, status):
+    ctx = _ready_ctx()
+    assert _decode(ctx, **kw) == status
+    assert lkv.lib().loopkv_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dt=3), B.ERR_INVALID_ARG), (dict(n_new=-1), B.ERR_INVALID_ARG), (dict(n_seqs=3), B.ERR_CAPACITY),
+    (dict(loop=5, layer=0), B.ERR_PLAN), (dict(k=0), B.ERR_INVALID_ARG), (dict(bt=0), B.ERR_INVALID_ARG),
+    (dict(lens=0), B.ERR_INVALID_ARG), (dict(bt_stride=0), B.ERR_INVALID_ARG),
+])
+def test_append_validation(kw, status):
+    ctx = _ready_ctx()
+    assert _append(ctx, **kw) == status
+
+
+def test_noop_calls_enqueue_nothing():
+    ctx = _ready_ctx()
+    assert _append(ctx, n_new=0) == B.OK             # nothing to append
+    assert _append(ctx, loop=0, layer=2) == B.OK     # reuse cell: append is a no-op
+    assert _decode(ctx, n_seqs=0) == B.OK
+    assert lkv.lib().loopkv_last_error().decode() == ""
+
+
+def test_unready_context():
+    ctx = lkv.Context(1, 1, 2, 64, 16, 2)
+    assert _decode(ctx) == B.ERR_PLAN
+    ctx.plan([0])
+    assert _decode(ctx) == B.ERR_WORKSPACE
+    assert _append(ctx) == B.ERR_WORKSPACE
+    ctx.plan([1])                                    # re-planning unbinds the workspace
+    assert _decode(ctx) == B.ERR_WORKSPACE
+
+
+def test_single_hip_runtime_loaded():
+    import torch  # noqa: F401
+    lkv.lib()
+    maps = open("/proc/self/maps").read()
+    paths = {l.split()[-1] for l in maps.splitlines() if "libamdhip64" in l}
+    assert len(paths) == 1, paths

@@ -17,10 +17,16 @@ def _field(bits, pos, width):
     return sum(int(bits[pos + i]) << i for i in range(width))
 
 
-def _unpack_token_major(buf, D, width):
+def _unpack_k(buf, D, width):
+    """Column-major K plane: column w of 32/width channels, 16 tokens of 32 bits each."""
     bits = _bits(buf)
-    row = 16 * 0 + D * width  # bits per token row
-    return np.array([[_field(bits, t * D * width + d * width, width) for d in range(D)] for t in range(16)])
+    per_col = 32 // width
+    out = np.zeros((16, D), dtype=np.int64)
+    for t in range(16):
+        for d in range(D):
+            w, r = divmod(d, per_col)
+            out[t, d] = _field(bits, 32 * (16 * w + t) + width * r, width)
+    return out
 
 
 def _unpack_channel_major_2bit(buf, D):
@@ -58,15 +64,15 @@ def test_pack_roundtrip(D, layout, bits):
         t0 = 16 * j
         g, half = divmod(j, 2)
         if layout == O.LAYOUT_KIVI4:
-            kc = _unpack_token_major(rec[:8 * D], D, 4)
+            kc = _unpack_k(rec[:8 * D], D, 4)
             vc = _unpack_channel_major_4bit(rec[8 * D:16 * D], D)
             km, vm = rec[16 * D:18 * D], rec[18 * D:20 * D]
         elif bits == 2:
-            kc = _unpack_token_major(rec[:4 * D], D, 2)
+            kc = _unpack_k(rec[:4 * D], D, 2)
             vc = _unpack_channel_major_2bit(rec[4 * D:8 * D], D)
             km, vm = rec[8 * D:10 * D], rec[10 * D:12 * D]
         else:
-            kc = 4 * _unpack_token_major(rec[:4 * D], D, 2) + _unpack_token_major(rec[12 * D:16 * D], D, 2)
+            kc = 4 * _unpack_k(rec[:4 * D], D, 2) + _unpack_k(rec[12 * D:16 * D], D, 2)
             vc = 4 * _unpack_channel_major_2bit(rec[4 * D:8 * D], D) + \
                 _unpack_channel_major_2bit(rec[16 * D:20 * D], D)
             km, vm = rec[8 * D:10 * D], rec[10 * D:12 * D]

@@ -31,9 +31,11 @@
  *   pool  [num_blocks][n_heads][record]   record of one 16-token block, one head
  *   tails [max_seqs][n_heads][2 (K,V)][32][head_dim] bf16
  * Record layouts (D = head_dim, all words little-endian u32):
- *   4-bit planes : [K_hi 4D | V_hi 4D | K_meta 2D | V_meta 2D | K_lo 4D | V_lo 4D]  = 20D bytes
- *   2-bit        : [K2 4D   | V2 4D   | K_meta 2D | V_meta 2D]                      = 12D bytes
- *   KIVI-4       : [K4 8D   | V4 8D   | K_meta 2D | V_meta 2D]                      = 20D bytes
+ *   4-bit planes : [K_hi 4D | K_meta 2D | V_hi 4D | V_meta 2D | K_lo 4D | V_lo 4D]  = 20D bytes
+ *   2-bit        : [K2 4D   | K_meta 2D | V2 4D   | V_meta 2D]                      = 12D bytes
+ *   KIVI-4       : [K4 8D   | K_meta 2D | V4 8D   | V_meta 2D]                      = 20D bytes
+ *   (the bytes a decode reads for every token — high K part, then high V part — are
+ *   each contiguous; the low planes follow and are read only where selected)
  *   K plane (2-bit): D/16 columns x 16 tokens of u32; word (w, t) holds channels
  *     16w..16w+15 of token t, channel 16w+4k+p at bit 8k+2p.
  *   K plane (4-bit): D/8 columns x 16 tokens; channel 8w+2k+n at bit 8k+4n.

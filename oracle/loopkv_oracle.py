@@ -297,9 +297,9 @@ def record_bytes(head_dim, kind, layout):
 def pack_block(qh, j, layout=LAYOUT_PLANES):
     """Bytes of the record of logical block j (tokens 16j..16j+15, all quantized).
 
-    4-bit, planes layout: [K_hi | V_hi | K_meta | V_meta | K_lo | V_lo]
-    2-bit:                [K2   | V2   | K_meta | V_meta]
-    4-bit, KIVI-4 layout: [K4   | V4   | K_meta | V_meta]
+    4-bit, planes layout: [K_hi | K_meta | V_hi | V_meta | K_lo | V_lo]
+    2-bit:                [K2   | K_meta | V2   | V_meta]
+    4-bit, KIVI-4 layout: [K4   | K_meta | V4   | V_meta]
     K planes are column-major (16-channel columns of the 16 tokens), V planes
     channel-major (see the helpers above).
     K_meta of group g = j // 2 is split over its two blocks: block 2g holds
@@ -315,11 +315,11 @@ def pack_block(qh, j, layout=LAYOUT_PLANES):
     kmeta = _meta_words(qh["ks"][g, ch], qh["kz"][g, ch])
     vmeta = _meta_words(qh["vs"][t0:t0 + BLOCK].reshape(-1), qh["vz"][t0:t0 + BLOCK].reshape(-1))
     if layout == LAYOUT_KIVI4:
-        parts = [_pack_4bit_k(kc), _pack_4bit_channel_major(vc), kmeta, vmeta]
+        parts = [_pack_4bit_k(kc), kmeta, _pack_4bit_channel_major(vc), vmeta]
     elif qh["bits"] == 2:
-        parts = [_pack_2bit_k(kc), _pack_2bit_channel_major(vc), kmeta, vmeta]
+        parts = [_pack_2bit_k(kc), kmeta, _pack_2bit_channel_major(vc), vmeta]
     else:
-        parts = [_pack_2bit_k(kc >> 2), _pack_2bit_channel_major(vc >> 2), kmeta, vmeta,
+        parts = [_pack_2bit_k(kc >> 2), kmeta, _pack_2bit_channel_major(vc >> 2), vmeta,
                  _pack_2bit_k(kc & 3), _pack_2bit_channel_major(vc & 3)]
     return np.concatenate(parts)
 

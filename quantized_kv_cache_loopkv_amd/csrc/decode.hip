@@ -7,19 +7,21 @@
 // at low precision rather than skipped; a reuse cell reads the final loop's KV;
 // KIVI-4 (uniform 4-bit) runs on the same kernel as the baseline.
 //
-// One workgroup (4 wave64s) owns one row (cell, sequence, head). The path is
-// HBM-bound with a VALU co-limit, so no MFMA: 2-bit codes are widened with
-// in-place byte masks and v_cvt_f32_ubyteN, and every per-group / per-token
-// scale is folded into the coefficient that multiplies the code.
+// One workgroup (8 wave64s) owns one row (cell, sequence, head); a whole plan is
+// one launch of cells x sequences x heads workgroups. The path is HBM-bound with
+// a VALU co-limit, so no MFMA: 2-bit codes are widened with in-place byte masks
+// and v_cvt_f32_ubyteN, every per-group / per-token scale is folded into the
+// coefficient that multiplies the code, and every wave keeps the loads of its
+// next step in flight while it computes the current one.
 //
 //   K pass   coarse scores s_t = sigma q . (z + s (4 hi + 3/2)) from the high plane
-//            (4-bit target), full scores for tau = 0 and KIVI-4, 2-bit scores for a
+//            (4-bit target); full scores for tau = 0 and KIVI-4; 2-bit scores for a
 //            2-bit target; the tail (last len mod 32 tokens) is exact bf16. Scores
 //            stay in LDS (4 bytes per token).
 //   stats    m = max s, l = sum exp(s - m) over the whole row.
 //   select   token t of the quantized prefix is selected when exp(s_t - m)/l >= tau;
 //            a ballot per 64 tokens gives one 32-bit mask per 32-token group.
-//   refine   only groups with a selected token: gather their low K plane and add
+//   refine   only groups with a selected token: read their low K plane and add
 //            sigma q . s (lo - 3/2) to the selected scores.
 //   V pass   weights w_t = exp(s_t - m') with the final max m'; values
 //            z + s (4 hi + lo) for selected tokens (low V plane read only for blocks
@@ -32,9 +34,9 @@
 
 namespace lkv {
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kWaveScratch = 512;   // floats of per-wave LDS scratch
+constexpr int kWaveScratch = 256;   // floats of per-wave LDS scratch
 
 enum : int { MODE_COARSE = 0, MODE_DENSE = 1, MODE_Q2 = 2, MODE_KIVI = 3 };
 
@@ -44,10 +46,22 @@ __device__ inline void wave_sync_lds() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-__device__ inline float wave_sum(float v) {
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+template <int CTRL>
+__device__ inline float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+// Sum over aligned groups of N lanes: quad swaps, then half-row and row mirrors, then shuffles.
+template <int N>
+__device__ inline float group_sum(float v) {
+  if (N >= 2) v += dpp<0xB1>(v);    // quad_perm [1,0,3,2]
+  if (N >= 4) v += dpp<0x4E>(v);    // quad_perm [2,3,0,1]
+  if (N >= 8) v += dpp<0x141>(v);   // row_half_mirror
+  if (N >= 16) v += dpp<0x140>(v);  // row_mirror
+  if (N >= 32) v += __shfl_xor(v, 16);
+  if (N >= 64) v += __shfl_xor(v, 32);
   return v;
 }
+__device__ inline float wave_sum(float v) { return group_sum<64>(v); }
 __device__ inline float wave_max(float v) {
   for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
   return v;
@@ -58,8 +72,18 @@ __device__ inline float f16hi(uint32_t w) { return __half2float(__ushort_as_half
 __device__ inline float bf16f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 __device__ inline float ubyte(uint32_t x, int k) { return (float)((x >> (8 * k)) & 0xffu); }
 
-// Sixteen 2-bit codes of one word; cf[4p + k] multiplies the code at byte k, bits 2p.
-__device__ inline float dot16_2bit(uint32_t x, const float* cf, float acc) {
+// Sixteen 2-bit codes of one word. K order: cf[4k + p] for the code at byte k, bits 2p.
+__device__ inline float dot16_k(uint32_t x, const float* cf, float acc) {
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const uint32_t m = x & (0x03030303u << (2 * p));
+#pragma unroll
+    for (int k = 0; k < 4; ++k) acc = fmaf(cf[4 * k + p], ubyte(m, k), acc);
+  }
+  return acc;
+}
+// V order: cf[4p + k] (token 4p + k of the block).
+__device__ inline float dot16_v(uint32_t x, const float* cf, float acc) {
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
     const uint32_t m = x & (0x03030303u << (2 * p));
@@ -68,8 +92,18 @@ __device__ inline float dot16_2bit(uint32_t x, const float* cf, float acc) {
   }
   return acc;
 }
-// Eight 4-bit codes of one word; cf[4n + k] multiplies the code at byte k, nibble n.
-__device__ inline float dot8_4bit(uint32_t x, const float* cf, float acc) {
+// Eight 4-bit codes of one word. K order: cf[2k + n] for the nibble n of byte k.
+__device__ inline float dot8_k4(uint32_t x, const float* cf, float acc) {
+#pragma unroll
+  for (int n = 0; n < 2; ++n) {
+    const uint32_t m = x & (0x0F0F0F0Fu << (4 * n));
+#pragma unroll
+    for (int k = 0; k < 4; ++k) acc = fmaf(cf[2 * k + n], ubyte(m, k), acc);
+  }
+  return acc;
+}
+// V order: cf[4n + k] (token 4n + k of the word's 8 tokens).
+__device__ inline float dot8_v4(uint32_t x, const float* cf, float acc) {
 #pragma unroll
   for (int n = 0; n < 2; ++n) {
     const uint32_t m = x & (0x0F0F0F0Fu << (4 * n));
@@ -79,122 +113,145 @@ __device__ inline float dot8_4bit(uint32_t x, const float* cf, float acc) {
   return acc;
 }
 
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+// Streaming loads (the cache bytes are read once per decode).
+__device__ inline uint4 ld_stream4(const void* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ inline uint4 ld_stream2(const void* p) {
+  const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+  return make_uint4(v.x, v.y, 0u, 0u);
+}
+
+__device__ inline uint32_t w4(const uint4& v, int i) { return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w; }
+
 struct Row {
   const uint8_t* pool;     // pool base of the storage cell
-  const int32_t* bt;       // block table row of the sequence
+  const int32_t* btl;      // block table row of the sequence (in LDS)
   const uint16_t* tail;    // tail of (slot, head): [2][32][D] bf16
   int H, h, rec, N, n_q, n_groups;
   __device__ inline const uint8_t* rec_ptr(int j) const {
-    return pool + ((size_t)bt[j] * H + h) * (size_t)rec;
+    return pool + ((size_t)btl[j] * H + h) * (size_t)rec;
   }
 };
 
 // ----------------------------------------------------------------------------- K pass
 // Lane mapping per wave step: GPS groups, each covered by LPG = 4*COLS lanes
-// (2 blocks x 2 token octets x COLS columns of UNIT channels). A lane reads 8
-// consecutive words of its column (8 tokens) and keeps 8 partial scores, which
-// are summed over the COLS column lanes with xor shuffles.
+// (2 blocks x 2 token octets x COLS columns of UNIT channels). A lane reads the 8
+// words of its column for 8 consecutive tokens and keeps 8 partial scores, which
+// are summed over the COLS column lanes with DPP. Coefficients of a group are
+// built by the LPG lanes of the group (CPL channels each) and passed through LDS.
 template <int D, int MODE, bool REFINE>
-__device__ void k_pass(const Row& r, const float* qs, float* scores, const uint32_t* selm,
-                       float* wscr, int lane, int w, float& mloc) {
-  constexpr bool KIVI = MODE == MODE_KIVI;
-  constexpr int UNIT = KIVI ? 8 : 16;
-  constexpr int COLS = D / UNIT;
-  constexpr int LPG = 4 * COLS;
-  constexpr int GPS = 64 / LPG;
-  constexpr int CPL = UNIT / 4;
-  constexpr int KMETA = KIVI ? off_kmeta_kivi(D) : off_kmeta_planes(D);
-  const int gsub = lane / LPG;
-  const int rl = lane % LPG;
-  const int blk = rl / (2 * COLS), oct = (rl / COLS) & 1, col = rl % COLS;
-  float* coef = wscr;             // [GPS][D]
-  float* coefl = wscr + GPS * D;  // [GPS][D]
+struct KPass {
+  static constexpr bool KIVI = MODE == MODE_KIVI;
+  static constexpr bool DENSE = MODE == MODE_DENSE && !REFINE;
+  static constexpr int UNIT = KIVI ? 8 : 16;
+  static constexpr int COLS = D / UNIT;
+  static constexpr int LPG = 4 * COLS;
+  static constexpr int GPS = 64 / LPG;
+  static constexpr int CPL = UNIT / 4;
+  static constexpr int KMETA = KIVI ? off_kmeta_kivi(D) : off_kmeta_planes(D);
+  static constexpr int CODE_OFF = REFINE ? off_klo(D) : 0;
 
-  for (int it = 0;; ++it) {
-    const int gbase = (it * kWaves + w) * GPS;
-    if (gbase >= r.n_groups) break;
-    if (REFINE) {
-      bool any = false;
-#pragma unroll
-      for (int gs = 0; gs < GPS; ++gs) any |= (gbase + gs < r.n_groups) && selm[gbase + gs] != 0u;
-      if (!any) continue;
+  struct Buf {
+    uint4 meta, c0, c1, l0, l1;
+    bool vm, vc;
+  };
+
+  __device__ static inline void load(const Row& r, const uint32_t* selm, int s, int lane, int w, Buf& b) {
+    const int gbase = (s * kWaves + w) * GPS;
+    const int idx = lane * CPL;
+    const int gm = gbase + idx / D, ch = idx % D;
+    b.vm = gm < r.n_groups && (!REFINE || selm[gm] != 0u);
+    if (b.vm) {
+      const uint8_t* p = r.rec_ptr(2 * gm + (ch >= D / 2)) + KMETA + 4 * (ch % (D / 2));
+      b.meta = CPL == 4 ? ld_stream4(p) : ld_stream2(p);
     }
-    // Per-(group, channel) coefficients, each lane CPL channels of one group.
+    const int rl = lane % LPG;
+    const int blk = rl / (2 * COLS), oct = (rl / COLS) & 1, col = rl % COLS;
+    const int gc = gbase + lane / LPG;
+    b.vc = gc < r.n_groups && (!REFINE || selm[gc] != 0u);
+    if (b.vc) {
+      const uint8_t* rb = r.rec_ptr(2 * gc + blk);
+      const uint8_t* kp = rb + CODE_OFF + (col * kBlock + oct * 8) * 4;
+      b.c0 = ld_stream4(kp);
+      b.c1 = ld_stream4(kp + 16);
+      if (DENSE) {
+        const uint8_t* lp = rb + off_klo(D) + (col * kBlock + oct * 8) * 4;
+        b.l0 = ld_stream4(lp);
+        b.l1 = ld_stream4(lp + 16);
+      }
+    }
+  }
+
+  __device__ static inline void compute(const Row& r, const float* qs, float* scores, const uint32_t* selm,
+                                        float* coef, int s, int lane, int w, const Buf& b, float& mloc) {
+    const int gbase = (s * kWaves + w) * GPS;
+    const int idx = lane * CPL;
+    const int gsm = idx / D, ch0 = idx % D;
+    // coefficients of CPL consecutive channels; stored [column][byte k][bit pair p]
     float cst = 0.f;
+    if (b.vm) {
+      float cv[CPL];
 #pragma unroll
-    for (int rr = 0; rr < CPL; ++rr) {
-      const int idx = lane * CPL + rr;
-      const int gs = idx / D, ch = idx % D;
-      const int g = gbase + gs;
-      if (g < r.n_groups) {
-        const uint32_t mw = *reinterpret_cast<const uint32_t*>(
-            r.rec_ptr(2 * g + (ch >= D / 2)) + KMETA + 4 * (ch % (D / 2)));
-        const float s = f16lo(mw), z = f16hi(mw), qv = qs[ch];
-        int pos;
-        float pre;
-        if (KIVI) {
-          const int n = ch & 1;
-          pos = (ch / 8) * 8 + n * 4 + ((ch >> 1) & 3);
-          pre = n ? (1.f / 16.f) : 1.f;
-        } else {
-          const int p = ch & 3;
-          pos = (ch / 16) * 16 + p * 4 + ((ch >> 2) & 3);
-          pre = p == 0 ? 1.f : p == 1 ? 0.25f : p == 2 ? 0.0625f : 0.015625f;
-        }
-        const float qsv = qv * s;
+      for (int rr = 0; rr < CPL; ++rr) {
+        const uint32_t mw = w4(b.meta, rr);
+        const int ch = ch0 + rr;
+        const float sc = f16lo(mw), z = f16hi(mw), qv = qs[ch];
+        const float qsv = qv * sc;
+        const float pre = KIVI ? (rr ? 1.f / 16.f : 1.f)
+                               : (rr == 0 ? 1.f : rr == 1 ? 0.25f : rr == 2 ? 0.0625f : 0.015625f);
         if (REFINE) {
-          coefl[gs * D + pos] = qsv * pre;
+          cv[rr] = qsv * pre;
           cst = fmaf(-1.5f, qsv, cst);
-        } else if (MODE == MODE_COARSE) {
-          coef[gs * D + pos] = 4.f * qsv * pre;
-          cst += qv * fmaf(1.5f, s, z);
-        } else if (MODE == MODE_DENSE) {
-          coef[gs * D + pos] = 4.f * qsv * pre;
-          coefl[gs * D + pos] = qsv * pre;
-          cst = fmaf(qv, z, cst);
+        } else if (MODE == MODE_COARSE || MODE == MODE_DENSE) {
+          cv[rr] = 4.f * qsv * pre;
+          cst += (MODE == MODE_COARSE) ? qv * fmaf(1.5f, sc, z) : qv * z;
         } else {
-          coef[gs * D + pos] = qsv * pre;
+          cv[rr] = qsv * pre;
           cst = fmaf(qv, z, cst);
         }
       }
+      float* dst = coef + gsm * D + ch0;   // CPL consecutive floats
+      if (CPL == 4) *reinterpret_cast<float4*>(dst) = make_float4(cv[0], cv[1], cv[2], cv[3]);
+      else *reinterpret_cast<float2*>(dst) = make_float2(cv[0], cv[CPL - 1]);
     }
-#pragma unroll
-    for (int off = 1; off < LPG; off <<= 1) cst += __shfl_xor(cst, off);
+    cst = group_sum<LPG>(cst);
     wave_sync_lds();
 
-    const int g = gbase + gsub;
-    const bool active = g < r.n_groups && (!REFINE || selm[g] != 0u);
-    if (active) {
-      const uint8_t* rb = r.rec_ptr(2 * g + blk);
-      const int woff = (col * kBlock + oct * 8) * 4;
-      float part[8];
+    const int gsub = lane / LPG;
+    const int rl = lane % LPG;
+    const int blk = rl / (2 * COLS), oct = (rl / COLS) & 1, col = rl % COLS;
+    float part[8], partl[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) part[j] = 0.f;
-      if (!REFINE) {
-        const uint4* kp = reinterpret_cast<const uint4*>(rb + woff);
-        const uint4 x0 = kp[0], x1 = kp[1];
-        const uint32_t xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-        float cf[UNIT];
+    for (int j = 0; j < 8; ++j) part[j] = partl[j] = 0.f;
+    if (b.vc) {
+      float cf[UNIT];
+      const float4* cp = reinterpret_cast<const float4*>(coef + gsub * D + col * UNIT);
 #pragma unroll
-        for (int u = 0; u < UNIT; ++u) cf[u] = coef[gsub * D + col * UNIT + u];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) part[j] = KIVI ? dot8_4bit(xs[j], cf, 0.f) : dot16_2bit(xs[j], cf, 0.f);
-      }
-      if (REFINE || MODE == MODE_DENSE) {
-        const uint4* lp = reinterpret_cast<const uint4*>(rb + off_klo(D) + woff);
-        const uint4 y0 = lp[0], y1 = lp[1];
-        const uint32_t ys[8] = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};
-        float cl[16];
-#pragma unroll
-        for (int u = 0; u < 16; ++u) cl[u] = coefl[gsub * D + col * 16 + u];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) part[j] = dot16_2bit(ys[j], cl, part[j]);
+      for (int u = 0; u < UNIT / 4; ++u) {
+        const float4 t = cp[u];
+        cf[4 * u] = t.x;
+        cf[4 * u + 1] = t.y;
+        cf[4 * u + 2] = t.z;
+        cf[4 * u + 3] = t.w;
       }
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-#pragma unroll
-        for (int off = 1; off < COLS; off <<= 1) part[j] += __shfl_xor(part[j], off);
+        const uint32_t x = j < 4 ? w4(b.c0, j) : w4(b.c1, j - 4);
+        part[j] = KIVI ? dot8_k4(x, cf, 0.f) : dot16_k(x, cf, 0.f);
+        if (DENSE) partl[j] = dot16_k(j < 4 ? w4(b.l0, j) : w4(b.l1, j - 4), cf, 0.f);
       }
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (DENSE) part[j] = fmaf(0.25f, partl[j], part[j]);
+      part[j] = group_sum<COLS>(part[j]);
+    }
+    if (b.vc) {
+      const int g = gbase + gsub;
       const uint32_t gm = REFINE ? selm[g] : 0u;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -217,133 +274,179 @@ __device__ void k_pass(const Row& r, const float* qs, float* scores, const uint3
     }
     wave_sync_lds();
   }
-}
+
+  __device__ static void run(const Row& r, const float* qs, float* scores, const uint32_t* selm, float* coef,
+                             int lane, int w, float& mloc) {
+    const int steps = (r.n_groups + kWaves * GPS - 1) / (kWaves * GPS);
+    Buf cur, nxt;
+    load(r, selm, 0, lane, w, cur);
+    for (int s = 0; s < steps; ++s) {
+      if (s + 1 < steps) load(r, selm, s + 1, lane, w, nxt);
+      if (!REFINE || __any(cur.vm))
+        compute(r, qs, scores, selm, coef, s, lane, w, cur, mloc);
+      cur = nxt;
+    }
+  }
+};
 
 // ----------------------------------------------------------------------------- V pass
-// Lane mapping per wave step: BPS blocks, each covered by LPB lanes of VCH
-// channels. First every lane folds weight, scale and bucket offset of a few
-// (token, channel group) pairs into LDS coefficients; then each lane reads the
-// V words of its channels (16 tokens per word) and accumulates.
+// Lane mapping per wave step: 4 blocks (64 tokens). Lane t of the step first folds
+// weight, scale and bucket offset of its token into LDS coefficients (one per
+// 32-channel group); then lane (block, chunk) reads the V words of its D/16
+// channels (16 tokens per word) and accumulates.
 template <int D, int MODE, bool SPARSE>
-__device__ void v_pass(const Row& r, const float* scores, const uint32_t* selm, float* wscr,
-                       int lane, int w, float mfin, float* acc, float& accz, float& lsum) {
-  constexpr bool KIVI = MODE == MODE_KIVI;
-  constexpr int VCH = KIVI ? 4 : 8;
-  constexpr int LPB = D / VCH;
-  constexpr int BPS = 64 / LPB;
-  constexpr int NE = D / kGroup;
-  constexpr int ITEMS = kBlock * BPS * NE / 64;
-  constexpr int VOFF = KIVI ? off_v_kivi(D) : off_v_planes(D);
-  constexpr int VMETA = KIVI ? off_vmeta_kivi(D) : off_vmeta_planes(D);
-  const int vblk = lane / LPB, chunk = lane % LPB;
-  const int e_lane = (chunk * VCH) / kGroup;
-  float* coefv = wscr;                    // [BPS][NE][16]
-  float* coefvl = wscr + BPS * NE * 16;   // [BPS][NE][16]
-  const int nb = r.n_q / kBlock;
+struct VPass {
+  static constexpr bool KIVI = MODE == MODE_KIVI;
+  static constexpr int VCH = D / 16;            // channels per lane
+  static constexpr int NE = D / kGroup;         // channel groups
+  static constexpr int WPL = KIVI ? 2 * VCH : VCH;  // V words per lane
+  static constexpr int NV4 = WPL / 4;           // uint4 loads per lane
+  static constexpr int VOFF = KIVI ? off_v_kivi(D) : off_v_planes(D);
+  static constexpr int VMETA = KIVI ? off_vmeta_kivi(D) : off_vmeta_planes(D);
+  static constexpr bool DENSE = MODE == MODE_DENSE;
 
-  for (int it = 0;; ++it) {
-    const int jbase = (it * kWaves + w) * BPS;
-    if (jbase >= nb) break;
+  struct Buf {
+    uint4 meta;
+    uint4 c[NV4];
+    uint4 l[DENSE ? NV4 : 1];
+    bool v;
+  };
+
+  __device__ static inline void load(const Row& r, int s, int lane, int w, Buf& b) {
+    const int nb = r.n_q / kBlock;
+    const int j = (s * kWaves + w) * 4 + lane / 16;
+    b.v = j < nb;
+    if (!b.v) return;
+    const uint8_t* rb = r.rec_ptr(j);
+    const int t16 = lane % 16, chunk = lane % 16;
+    const uint8_t* mp = rb + VMETA + 4 * NE * t16;
+    b.meta = NE == 4 ? ld_stream4(mp) : ld_stream2(mp);
+    const uint8_t* vp = rb + VOFF + chunk * WPL * 4;
 #pragma unroll
-    for (int q = 0; q < ITEMS; ++q) {
-      const int idx = lane + 64 * q;
-      const int e = idx % NE, tt = idx / NE;
-      const int jb = tt / kBlock, t16 = tt % kBlock;
-      const int j = jbase + jb;
-      float ahi = 0.f, alo = 0.f;
-      if (j < nb) {
-        const int t = j * kBlock + t16;
-        const float wgt = __expf(scores[t] - mfin);
-        const uint32_t mw = *reinterpret_cast<const uint32_t*>(r.rec_ptr(j) + VMETA + 4 * (t16 * NE + e));
-        const float s = f16lo(mw), z = f16hi(mw);
-        const float ws = wgt * s;
-        if (KIVI) {
-          ahi = ws * (((t16 & 7) >> 2) ? (1.f / 16.f) : 1.f);
-          accz = fmaf(wgt, z, accz);
-        } else {
-          const int p = t16 >> 2;
-          const float pre = p == 0 ? 1.f : p == 1 ? 0.25f : p == 2 ? 0.0625f : 0.015625f;
-          if (MODE == MODE_Q2) {
-            ahi = ws * pre;
-            accz = fmaf(wgt, z, accz);
-          } else {
-            ahi = 4.f * ws * pre;
-            bool sel = MODE == MODE_DENSE;
-            if (SPARSE) sel = (selm[t >> 5] >> (t & 31)) & 1u;
-            if (sel) {
-              alo = ws * pre;
-              accz = fmaf(wgt, z, accz);
-            } else {
-              accz = fmaf(wgt, fmaf(1.5f, s, z), accz);
-            }
-          }
-        }
-        if (e == 0) lsum += wgt;
+    for (int i = 0; i < NV4; ++i) b.c[i] = ld_stream4(vp + 16 * i);
+    if (DENSE) {
+      const uint8_t* lp = rb + off_vlo(D) + chunk * WPL * 4;
+#pragma unroll
+      for (int i = 0; i < NV4; ++i) b.l[i] = ld_stream4(lp + 16 * i);
+    }
+  }
+
+  __device__ static inline void compute(const Row& r, const float* scores, const uint32_t* selm, float* coefv,
+                                        int s, int lane, int w, float mfin, const Buf& b, float* acc,
+                                        float* accl, float* accz, float& lsum) {
+    const int jb = lane / 16, t16 = lane % 16;
+    const int j = (s * kWaves + w) * 4 + jb;
+    if (b.v) {
+      const int t = j * kBlock + t16;
+      const float wgt = __expf(scores[t] - mfin);
+      bool sel = DENSE;
+      if (SPARSE) sel = (selm[t >> 5] >> (t & 31)) & 1u;
+      float pre;
+      if (KIVI) pre = ((t16 & 7) >> 2) ? (1.f / 16.f) : 1.f;
+      else {
+        const int p = t16 >> 2;
+        pre = p == 0 ? 1.f : p == 1 ? 0.25f : p == 2 ? 0.0625f : 0.015625f;
       }
-      coefv[(jb * NE + e) * 16 + t16] = ahi;
-      coefvl[(jb * NE + e) * 16 + t16] = alo;
+      const float mult = (MODE == MODE_Q2 || KIVI) ? 1.f : 4.f;
+#pragma unroll
+      for (int e = 0; e < NE; ++e) {
+        const uint32_t mw = w4(b.meta, e);
+        const float sc = f16lo(mw), z = f16hi(mw);
+        const float ws = wgt * sc;
+        coefv[(jb * NE + e) * 16 + t16] = mult * ws * pre;
+        const bool mid = (MODE == MODE_COARSE) && !sel;
+        accz[e] = fmaf(wgt, mid ? fmaf(1.5f, sc, z) : z, accz[e]);
+      }
+      lsum += wgt;
     }
     wave_sync_lds();
-
-    const int j = jbase + vblk;
-    if (j < nb) {
-      const uint8_t* rb = r.rec_ptr(j);
+    if (b.v) {
+      const int chunk = lane % 16;
+      const int e_lane = (chunk * VCH) / kGroup;
       float cf[16];
+      const float4* cp = reinterpret_cast<const float4*>(coefv + (jb * NE + e_lane) * 16);
 #pragma unroll
-      for (int u = 0; u < 16; ++u) cf[u] = coefv[(vblk * NE + e_lane) * 16 + u];
+      for (int u = 0; u < 4; ++u) {
+        const float4 tq = cp[u];
+        cf[4 * u] = tq.x;
+        cf[4 * u + 1] = tq.y;
+        cf[4 * u + 2] = tq.z;
+        cf[4 * u + 3] = tq.w;
+      }
       if (KIVI) {
-        const uint4* vp = reinterpret_cast<const uint4*>(rb + VOFF + chunk * VCH * 8);
-        const uint4 x0 = vp[0], x1 = vp[1];
-        const uint32_t xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
 #pragma unroll
         for (int c = 0; c < VCH; ++c) {
 #pragma unroll
-          for (int jj = 0; jj < 2; ++jj) acc[c] = dot8_4bit(xs[2 * c + jj], cf + 8 * jj, acc[c]);
+          for (int jj = 0; jj < 2; ++jj) acc[c] = dot8_v4(w4(b.c[(2 * c + jj) / 4], (2 * c + jj) % 4), cf + 8 * jj, acc[c]);
         }
       } else {
-        const uint4* vp = reinterpret_cast<const uint4*>(rb + VOFF + chunk * VCH * 4);
-        const uint4 x0 = vp[0], x1 = vp[1];
-        const uint32_t xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
 #pragma unroll
-        for (int c = 0; c < VCH; ++c) acc[c] = dot16_2bit(xs[c], cf, acc[c]);
-        bool need_lo = MODE == MODE_DENSE;
-        if (SPARSE) need_lo = ((selm[j >> 1] >> (16 * (j & 1))) & 0xffffu) != 0u;
-        if (MODE != MODE_Q2 && need_lo) {
-          float cl[16];
+        for (int c = 0; c < VCH; ++c) acc[c] = dot16_v(w4(b.c[c / 4], c % 4), cf, acc[c]);
+        if (DENSE) {
 #pragma unroll
-          for (int u = 0; u < 16; ++u) cl[u] = coefvl[(vblk * NE + e_lane) * 16 + u];
-          const uint4* lp = reinterpret_cast<const uint4*>(rb + off_vlo(D) + chunk * VCH * 4);
-          const uint4 y0 = lp[0], y1 = lp[1];
-          const uint32_t ys[8] = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};
+          for (int c = 0; c < VCH; ++c) accl[c] = dot16_v(w4(b.l[c / 4], c % 4), cf, accl[c]);
+        }
+        if (SPARSE) {
+          const uint32_t bm = (selm[j >> 1] >> (16 * (j & 1))) & 0xffffu;
+          if (bm) {
+            uint32_t m32 = 0;
 #pragma unroll
-          for (int c = 0; c < VCH; ++c) acc[c] = dot16_2bit(ys[c], cl, acc[c]);
+            for (int tt = 0; tt < 16; ++tt)
+              if ((bm >> tt) & 1u) m32 |= 3u << (8 * (tt & 3) + 2 * (tt >> 2));
+            const uint4* lp = reinterpret_cast<const uint4*>(r.rec_ptr(j) + off_vlo(D) + chunk * VCH * 4);
+            uint4 lw[NV4];
+#pragma unroll
+            for (int i = 0; i < NV4; ++i) lw[i] = lp[i];
+#pragma unroll
+            for (int c = 0; c < VCH; ++c) accl[c] = dot16_v(w4(lw[c / 4], c % 4) & m32, cf, accl[c]);
+          }
         }
       }
     }
     wave_sync_lds();
   }
-}
 
-// KIVI-4 V words use the 4-bit coefficient order (token t' of 16, scaled by 16^-n).
-// dot8_4bit consumes cf[4n + k] for the word's tokens 8jj + 4n + k, which is cf + 8jj.
+  __device__ static void run(const Row& r, const float* scores, const uint32_t* selm, float* coefv, int lane,
+                             int w, float mfin, float* acc, float* accl, float* accz, float& lsum) {
+    const int nb = r.n_q / kBlock;
+    const int steps = (nb + kWaves * 4 - 1) / (kWaves * 4);
+    Buf cur, nxt;
+    load(r, 0, lane, w, cur);
+    for (int s = 0; s < steps; ++s) {
+      if (s + 1 < steps) load(r, s + 1, lane, w, nxt);
+      compute(r, scores, selm, coefv, s, lane, w, mfin, cur, acc, accl, accz, lsum);
+      cur = nxt;
+    }
+  }
+};
+
+struct Smem {
+  float* scores;    // [lpad]; after the V pass: [kThreads][VCH] partials, then [kWaves][D] tail partials
+  uint32_t* selm;   // [lpad / 32]
+  int32_t* btl;     // [lpad / 16]
+  float* qs;        // [D]
+  float* wscr;      // [kWaves][kWaveScratch]
+  float* misc;      // [64 + kWaves * 4]
+};
 
 template <int D, int MODE, bool SPARSE>
-__device__ void row_body(const DecodeArgs& a, const Row& r, float* scores, uint32_t* selm, float* qs,
-                         float* wscr_all, float* tred, float* misc, size_t orow, int ci, int b, int h) {
+__device__ void row_body(const DecodeArgs& a, const Row& r, const Smem& sm, size_t orow) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  float* wscr = wscr_all + w * kWaveScratch;
+  float* coef = sm.wscr + w * kWaveScratch;
+  float* scores = sm.scores;
+  uint32_t* selm = sm.selm;
+  float* misc = sm.misc;
   constexpr int NE = D / kGroup;
-  constexpr int VCH = (MODE == MODE_KIVI) ? 4 : 8;
-  constexpr int LPB = D / VCH;
+  constexpr int VCH = D / 16;
 
   // ---- K pass (coarse / dense / 2-bit / KIVI-4 scores)
   float mloc = -INFINITY;
-  k_pass<D, MODE, false>(r, qs, scores, selm, wscr, lane, w, mloc);
+  KPass<D, MODE, false>::run(r, sm.qs, scores, selm, coef, lane, w, mloc);
   // tail: exact scores
   for (int t = r.n_q + w; t < r.N; t += kWaves) {
     const uint16_t* kt = r.tail + (size_t)(t % kGroup) * D;
     float p = 0.f;
-    for (int d = lane; d < D; d += 64) p = fmaf(qs[d], bf16f(kt[d]), p);
+    for (int d = lane; d < D; d += 64) p = fmaf(sm.qs[d], bf16f(kt[d]), p);
     p = wave_sum(p);
     if (lane == 0) {
       scores[t] = p;
@@ -353,14 +456,16 @@ __device__ void row_body(const DecodeArgs& a, const Row& r, float* scores, uint3
   mloc = wave_max(mloc);
   if (lane == 0) misc[w] = mloc;
   __syncthreads();
-  const float m = fmaxf(fmaxf(misc[0], misc[1]), fmaxf(misc[2], misc[3]));
+  float m = misc[0];
+  for (int i = 1; i < kWaves; ++i) m = fmaxf(m, misc[i]);
   // ---- row sum of the coarse softmax
   float ls = 0.f;
   for (int t = tid; t < r.N; t += kThreads) ls += __expf(scores[t] - m);
   ls = wave_sum(ls);
-  if (lane == 0) misc[4 + w] = ls;
+  if (lane == 0) misc[8 + w] = ls;
   __syncthreads();
-  const float l = (misc[4] + misc[5]) + (misc[6] + misc[7]);
+  float l = 0.f;
+  for (int i = 0; i < kWaves; ++i) l += misc[8 + i];
 
   // ---- selection masks (one u32 per 32-token group)
   if (SPARSE) {
@@ -379,27 +484,29 @@ __device__ void row_body(const DecodeArgs& a, const Row& r, float* scores, uint3
   }
   __syncthreads();
   if (a.sel_mask) {
-    uint32_t* sm = a.sel_mask + orow * (size_t)a.sel_words;
-    for (int g = tid; g < a.sel_words; g += kThreads) sm[g] = g < r.n_groups ? selm[g] : 0u;
+    uint32_t* smo = a.sel_mask + orow * (size_t)a.sel_words;
+    for (int g = tid; g < a.sel_words; g += kThreads) smo[g] = g < r.n_groups ? selm[g] : 0u;
   }
 
   // ---- refinement of the selected scores
   float mfin = m;
   if (SPARSE) {
     float mref = -INFINITY;
-    k_pass<D, MODE_COARSE, true>(r, qs, scores, selm, wscr, lane, w, mref);
+    KPass<D, MODE_COARSE, true>::run(r, sm.qs, scores, selm, coef, lane, w, mref);
     mref = wave_max(mref);
-    if (lane == 0) misc[8 + w] = mref;
+    if (lane == 0) misc[16 + w] = mref;
     __syncthreads();
-    mfin = fmaxf(m, fmaxf(fmaxf(misc[8], misc[9]), fmaxf(misc[10], misc[11])));
+    for (int i = 0; i < kWaves; ++i) mfin = fmaxf(mfin, misc[16 + i]);
   }
 
   // ---- V pass
-  float acc[VCH];
+  float acc[VCH], accl[VCH], accz[NE];
 #pragma unroll
-  for (int c = 0; c < VCH; ++c) acc[c] = 0.f;
-  float accz = 0.f, lsum = 0.f;
-  v_pass<D, MODE, SPARSE>(r, scores, selm, wscr, lane, w, mfin, acc, accz, lsum);
+  for (int c = 0; c < VCH; ++c) acc[c] = accl[c] = 0.f;
+#pragma unroll
+  for (int e = 0; e < NE; ++e) accz[e] = 0.f;
+  float lsum = 0.f;
+  VPass<D, MODE, SPARSE>::run(r, scores, selm, coef, lane, w, mfin, acc, accl, accz, lsum);
   // tail values, exact
   float tacc[D / 64];
 #pragma unroll
@@ -411,29 +518,31 @@ __device__ void row_body(const DecodeArgs& a, const Row& r, float* scores, uint3
     for (int i = 0; i < D / 64; ++i) tacc[i] = fmaf(wgt, bf16f(vt[lane + 64 * i]), tacc[i]);
     if (lane == 0) lsum += wgt;
   }
-  __syncthreads();   // all waves are done with their scratch
-  float* red = wscr_all;   // [kWaves * 64][VCH]
+  __syncthreads();   // scores are dead from here on: reuse them for partials
+  float* red = scores;                         // [kThreads][VCH]
+  float* tred = scores + kThreads * VCH;       // [kWaves][D]
 #pragma unroll
-  for (int c = 0; c < VCH; ++c) red[tid * VCH + c] = acc[c];
+  for (int c = 0; c < VCH; ++c) red[tid * VCH + c] = fmaf(0.25f, accl[c], acc[c]);
 #pragma unroll
   for (int i = 0; i < D / 64; ++i) tred[w * D + lane + 64 * i] = tacc[i];
-  float* zred = misc + 16;   // [kThreads]
-  zred[tid] = accz;
   lsum = wave_sum(lsum);
-  if (lane == 0) misc[12 + w] = lsum;
-  __syncthreads();
-  if (tid < NE) {
-    float zs = 0.f;
-    for (int i = tid; i < kThreads; i += NE) zs += zred[i];
-    misc[16 + kThreads + tid] = zs;
+#pragma unroll
+  for (int e = 0; e < NE; ++e) accz[e] = wave_sum(accz[e]);
+  if (lane == 0) {
+    misc[24 + w] = lsum;
+#pragma unroll
+    for (int e = 0; e < NE; ++e) misc[32 + w * 4 + e] = accz[e];
   }
   __syncthreads();
-  const float L = (misc[12] + misc[13]) + (misc[14] + misc[15]);
+  float L = 0.f;
+  for (int i = 0; i < kWaves; ++i) L += misc[24 + i];
   for (int d = tid; d < D; d += kThreads) {
     const int chunk = d / VCH, c = d % VCH;
-    float o = misc[16 + kThreads + d / kGroup];
+    float o = 0.f;
     for (int ww = 0; ww < kWaves; ++ww) {
-      for (int vb = 0; vb < 64 / LPB; ++vb) o += red[(ww * 64 + vb * LPB + chunk) * VCH + c];
+      o += misc[32 + ww * 4 + d / kGroup];
+#pragma unroll
+      for (int vb = 0; vb < 4; ++vb) o += red[(ww * 64 + vb * 16 + chunk) * VCH + c];
       o += tred[ww * D + d];
     }
     o = o / L;
@@ -447,9 +556,15 @@ __device__ void row_body(const DecodeArgs& a, const Row& r, float* scores, uint3
   }
 }
 
+__host__ __device__ inline size_t lds_lpad(int max_len) { return ((size_t)max_len + 63) / 64 * 64; }
+__host__ __device__ inline size_t lds_region_a(int max_len, int D) {
+  const size_t need = (size_t)kThreads * (D / 16) + (size_t)kWaves * D;
+  const size_t lp = lds_lpad(max_len);
+  return lp > need ? lp : need;
+}
 __host__ __device__ inline size_t decode_lds_floats(int max_len, int D) {
-  const size_t lpad = ((size_t)max_len + 63) / 64 * 64;
-  return lpad + lpad / 32 + D + (size_t)kWaves * kWaveScratch + (size_t)kWaves * D + 16 + kThreads + 16;
+  const size_t lp = lds_lpad(max_len);
+  return lds_region_a(max_len, D) + lp / 32 + lp / 16 + 16 + D + (size_t)kWaves * kWaveScratch + 64 + kWaves * 4;
 }
 
 template <int D>
@@ -464,13 +579,14 @@ __global__ void __launch_bounds__(kThreads) k_decode(DecodeArgs a) {
   const size_t orow = ((size_t)ci * a.n_seqs + b) * a.n_heads + h;
   const int N = a.seq_lens[b];
 
-  const size_t lpad = ((size_t)a.max_len + 63) / 64 * 64;
-  float* scores = smem;
-  uint32_t* selm = reinterpret_cast<uint32_t*>(smem + lpad);
-  float* qs = smem + lpad + lpad / 32;
-  float* wscr = qs + D;
-  float* tred = wscr + kWaves * kWaveScratch;
-  float* misc = tred + kWaves * D;
+  const size_t lp = lds_lpad(a.max_len);
+  Smem sm;
+  sm.scores = smem;
+  sm.selm = reinterpret_cast<uint32_t*>(smem + lds_region_a(a.max_len, D));
+  sm.btl = reinterpret_cast<int32_t*>(sm.selm + lp / 32);
+  sm.qs = reinterpret_cast<float*>(sm.btl + lp / 16 + 16);
+  sm.wscr = sm.qs + D;
+  sm.misc = sm.wscr + kWaves * kWaveScratch;
 
   if (N <= 0 || N > a.max_len) {
     const float v = N == 0 ? 0.f : __builtin_nanf("");
@@ -485,7 +601,7 @@ __global__ void __launch_bounds__(kThreads) k_decode(DecodeArgs a) {
 
   Row r;
   r.pool = a.ws + cell.pool_off;
-  r.bt = a.block_table + (size_t)b * a.bt_stride;
+  r.btl = sm.btl;
   const int slot = a.seq_slots ? a.seq_slots[b] : b;
   r.tail = reinterpret_cast<const uint16_t*>(a.ws + cell.tail_off) + ((size_t)slot * a.n_heads + h) * tail_elems(D);
   r.H = a.n_heads;
@@ -495,24 +611,27 @@ __global__ void __launch_bounds__(kThreads) k_decode(DecodeArgs a) {
   r.n_q = (N / kGroup) * kGroup;
   r.n_groups = N / kGroup;
 
-  // sigma * q in LDS
+  // block table row and sigma * q into LDS
+  const int32_t* bt = a.block_table + (size_t)b * a.bt_stride;
+  const int nbq = r.n_q / kBlock;
+  for (int j = tid; j < nbq; j += kThreads) sm.btl[j] = bt[j];
   for (int d = tid; d < D; d += kThreads) {
     const size_t qi = orow * D + d;
     const float qv = a.q_bf16 ? bf16f(reinterpret_cast<const uint16_t*>(a.q)[qi]) : reinterpret_cast<const float*>(a.q)[qi];
-    qs[d] = a.sm_scale * qv;
+    sm.qs[d] = a.sm_scale * qv;
   }
   __syncthreads();
 
   if (cell.kind == KIND_KIVI4) {
-    row_body<D, MODE_KIVI, false>(a, r, scores, selm, qs, wscr, tred, misc, orow, ci, b, h);
+    row_body<D, MODE_KIVI, false>(a, r, sm, orow);
   } else if (cell.kind == KIND_Q2) {
-    row_body<D, MODE_Q2, false>(a, r, scores, selm, qs, wscr, tred, misc, orow, ci, b, h);
+    row_body<D, MODE_Q2, false>(a, r, sm, orow);
   } else if (a.tau <= 0.f) {
-    row_body<D, MODE_DENSE, false>(a, r, scores, selm, qs, wscr, tred, misc, orow, ci, b, h);
+    row_body<D, MODE_DENSE, false>(a, r, sm, orow);
   } else if (a.tau > 1.f) {
-    row_body<D, MODE_COARSE, false>(a, r, scores, selm, qs, wscr, tred, misc, orow, ci, b, h);
+    row_body<D, MODE_COARSE, false>(a, r, sm, orow);
   } else {
-    row_body<D, MODE_COARSE, true>(a, r, scores, selm, qs, wscr, tred, misc, orow, ci, b, h);
+    row_body<D, MODE_COARSE, true>(a, r, sm, orow);
   }
 }
 
@@ -525,13 +644,13 @@ hipError_t launch_decode(const DecodeArgs& a, int head_dim, hipStream_t stream) 
   static bool attr_set[2] = {false, false};
   if (head_dim == 128) {
     if (!attr_set[1]) {
-      hipFuncSetAttribute((const void*)k_decode<128>, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+      (void)hipFuncSetAttribute((const void*)k_decode<128>, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
       attr_set[1] = true;
     }
     hipLaunchKernelGGL(k_decode<128>, dim3((unsigned)rows), dim3(kThreads), lds, stream, a);
   } else {
     if (!attr_set[0]) {
-      hipFuncSetAttribute((const void*)k_decode<64>, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+      (void)hipFuncSetAttribute((const void*)k_decode<64>, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
       attr_set[0] = true;
     }
     hipLaunchKernelGGL(k_decode<64>, dim3((unsigned)rows), dim3(kThreads), lds, stream, a);

@@ -20,13 +20,13 @@ enum : int32_t { KIND_Q4 = 0, KIND_Q2 = 1, KIND_SHARE = 2, KIND_KIVI4 = 3 };
 
 // Byte offsets inside one record, for head dim D.
 __host__ __device__ constexpr int off_k(int) { return 0; }
-__host__ __device__ constexpr int off_v_planes(int D) { return 4 * D; }
-__host__ __device__ constexpr int off_kmeta_planes(int D) { return 8 * D; }
+__host__ __device__ constexpr int off_kmeta_planes(int D) { return 4 * D; }
+__host__ __device__ constexpr int off_v_planes(int D) { return 6 * D; }
 __host__ __device__ constexpr int off_vmeta_planes(int D) { return 10 * D; }
 __host__ __device__ constexpr int off_klo(int D) { return 12 * D; }
 __host__ __device__ constexpr int off_vlo(int D) { return 16 * D; }
-__host__ __device__ constexpr int off_v_kivi(int D) { return 8 * D; }
-__host__ __device__ constexpr int off_kmeta_kivi(int D) { return 16 * D; }
+__host__ __device__ constexpr int off_kmeta_kivi(int D) { return 8 * D; }
+__host__ __device__ constexpr int off_v_kivi(int D) { return 10 * D; }
 __host__ __device__ constexpr int off_vmeta_kivi(int D) { return 18 * D; }
 
 __host__ __device__ constexpr int record_bytes(int kind, int D) {

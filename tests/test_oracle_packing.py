@@ -65,17 +65,19 @@ def test_pack_roundtrip(D, layout, bits):
         g, half = divmod(j, 2)
         if layout == O.LAYOUT_KIVI4:
             kc = _unpack_k(rec[:8 * D], D, 4)
-            vc = _unpack_channel_major_4bit(rec[8 * D:16 * D], D)
-            km, vm = rec[16 * D:18 * D], rec[18 * D:20 * D]
+            km = rec[8 * D:10 * D]
+            vc = _unpack_channel_major_4bit(rec[10 * D:18 * D], D)
+            vm = rec[18 * D:20 * D]
         elif bits == 2:
             kc = _unpack_k(rec[:4 * D], D, 2)
-            vc = _unpack_channel_major_2bit(rec[4 * D:8 * D], D)
-            km, vm = rec[8 * D:10 * D], rec[10 * D:12 * D]
+            km = rec[4 * D:6 * D]
+            vc = _unpack_channel_major_2bit(rec[6 * D:10 * D], D)
+            vm = rec[10 * D:12 * D]
         else:
             kc = 4 * _unpack_k(rec[:4 * D], D, 2) + _unpack_k(rec[12 * D:16 * D], D, 2)
-            vc = 4 * _unpack_channel_major_2bit(rec[4 * D:8 * D], D) + \
+            vc = 4 * _unpack_channel_major_2bit(rec[6 * D:10 * D], D) + \
                 _unpack_channel_major_2bit(rec[16 * D:20 * D], D)
-            km, vm = rec[8 * D:10 * D], rec[10 * D:12 * D]
+            km, vm = rec[4 * D:6 * D], rec[10 * D:12 * D]
         assert np.array_equal(kc, qh["kc"][t0:t0 + 16])
         assert np.array_equal(vc, qh["vc"][t0:t0 + 16])
         ks, kz = _meta(km)

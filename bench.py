@@ -145,7 +145,21 @@ def main():
     ap.add_argument("--no-kivi", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=4)
+    ap.add_argument("--table", choices=["shuffled", "identity"], default="shuffled",
+                    help="block table of the workload (the configuration uses a shuffled one)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a device-to-device copy of 4 GiB three times (counter calibration)")
     args = ap.parse_args()
+    if args.calibrate_copy:
+        import torch
+        n = 4 << 30
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 3}))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}). "
               "Rows of the decode are independent; see the sharding notes for how it would split.", file=sys.stderr)
@@ -164,6 +178,7 @@ def main():
     cfg.batch = args.batch
     cfg.lengths = [args.ctx - S] * args.batch
     cfg.append_steps = S
+    cfg.shuffled = args.table == "shuffled"
     plan = cfg.plan.reshape(-1)
     H, D, C, B = cfg.n_heads, cfg.head_dim, cfg.n_cells, cfg.batch
 
@@ -303,7 +318,7 @@ def main():
                    "global_batch": B, "seq_len": args.ctx, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
-                     "kernel": "k_decode<128>", "bytes_per_launch": dec_bytes,
+                     "kernel": "k_decode<128, tau regime>", "bytes_per_launch": dec_bytes,
                      "mean_launch_ms": round(dec_mean_ms, 4)},
         "cpu_baseline": cpu,
         "selected_fraction_q4_targets": sel_frac,

@@ -43,9 +43,12 @@
  *     bit 8*(t%4) + 2*(t/4).
  *   V plane (4-bit): D x 2 words; word (d, j) holds tokens 8j..8j+7, token
  *     t' = t-8j at bit 8*(t'%4) + 4*(t'/4).
- *   Meta word: f16 scale in bits 0-15, f16 zero in bits 16-31. K_meta of group g
- *     is split over its two blocks: logical block 2g holds channels 0..D/2-1,
- *     block 2g+1 channels D/2..D-1. V_meta is [16 tokens][D/32].
+ *   Meta word: f16 scale in bits 0-15, f16 zero in bits 16-31.
+ *   K_meta of group g: one word per channel, permuted inside each K column so that a
+ *     column's words follow its bit layout — 2-bit: position 16w+4p+k holds channel
+ *     16w+4k+p; 4-bit: position 8w+4n+k holds channel 8w+2k+n — and split over the
+ *     group's two blocks: logical block 2g holds positions 0..D/2-1, 2g+1 the rest.
+ *   V_meta: [D/32 channel groups][16 tokens].
  *
  * Paging: block_table[b * bt_stride + j] is the physical block of logical block
  * j (tokens 16j..16j+15) of sequence b; the same id addresses every cell's pool.

@@ -287,6 +287,22 @@ def _meta_words(s, z):
     return w.astype("<u4").view(np.uint8)
 
 
+def k_meta_order(D, bits):
+    """Channel stored at each K-meta position, inside every K column.
+
+    2-bit planes: position 16w + 4p + k holds channel 16w + 4k + p (the channel at
+    byte k, bit pair p of column word w). KIVI-4: position 8w + 4n + k holds channel
+    8w + 2k + n (byte k, nibble n)."""
+    pos = np.arange(D)
+    if bits == 2:
+        w, r = divmod(pos, 16)
+        p, k = divmod(r, 4)
+        return 16 * w + 4 * k + p
+    w, r = divmod(pos, 8)
+    n, k = divmod(r, 4)
+    return 8 * w + 2 * k + n
+
+
 def record_bytes(head_dim, kind, layout):
     D = head_dim
     if layout == LAYOUT_KIVI4:
@@ -302,8 +318,10 @@ def pack_block(qh, j, layout=LAYOUT_PLANES):
     4-bit, KIVI-4 layout: [K4   | K_meta | V4   | V_meta]
     K planes are column-major (16-channel columns of the 16 tokens), V planes
     channel-major (see the helpers above).
-    K_meta of group g = j // 2 is split over its two blocks: block 2g holds
-    channels 0..D/2-1, block 2g+1 channels D/2..D-1. V_meta is [16 tokens][D/32].
+    K_meta of group g = j // 2 holds one word per channel in the order of
+    k_meta_order (a permutation inside each K column), split over the group's
+    two blocks: block 2g holds positions 0..D/2-1, block 2g+1 the rest. V_meta is
+    [D/32 channel groups][16 tokens].
     """
     t0 = BLOCK * j
     assert t0 + BLOCK <= qh["n_q"]
@@ -311,9 +329,10 @@ def pack_block(qh, j, layout=LAYOUT_PLANES):
     vc = qh["vc"][t0:t0 + BLOCK]
     D = kc.shape[1]
     g, half = divmod(j, 2)
-    ch = slice(half * D // 2, (half + 1) * D // 2)
+    order = k_meta_order(D, 4 if layout == LAYOUT_KIVI4 else 2)
+    ch = order[half * D // 2:(half + 1) * D // 2]
     kmeta = _meta_words(qh["ks"][g, ch], qh["kz"][g, ch])
-    vmeta = _meta_words(qh["vs"][t0:t0 + BLOCK].reshape(-1), qh["vz"][t0:t0 + BLOCK].reshape(-1))
+    vmeta = _meta_words(qh["vs"][t0:t0 + BLOCK].T.reshape(-1), qh["vz"][t0:t0 + BLOCK].T.reshape(-1))
     if layout == LAYOUT_KIVI4:
         parts = [_pack_4bit_k(kc), kmeta, _pack_4bit_channel_major(vc), vmeta]
     elif qh["bits"] == 2:

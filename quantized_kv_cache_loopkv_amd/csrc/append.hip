@@ -87,6 +87,11 @@ __device__ inline void quantize_group(Get get, int M, uint8_t* codes, int stride
   *meta = sb | (zb << 16);
 }
 
+// Channel stored at K-meta position i: the words of a K column follow the column's
+// bit layout (2-bit: byte k, bit pair p; 4-bit: byte k, nibble n).
+__device__ inline int kmeta_channel2(int i) { return (i & ~15) + 4 * (i & 3) + ((i >> 2) & 3); }
+__device__ inline int kmeta_channel4(int i) { return (i & ~7) + 2 * (i & 3) + ((i >> 2) & 1); }
+
 template <int D>
 __global__ void __launch_bounds__(256) k_quantize_groups(AppendArgs a) {
   const int b = blockIdx.z % a.n_seqs;
@@ -161,9 +166,9 @@ __global__ void __launch_bounds__(256) k_quantize_groups(AppendArgs a) {
         for (int tp = 0; tp < 8; ++tp) word |= (uint32_t)vc[t0 + 8 * jj + tp][d] << (8 * (tp % 4) + 4 * (tp / 4));
         r[off_v_kivi(D) / 4 + idx] = word;
       }
-      for (int c = tid; c < D / 2; c += blockDim.x) r[off_kmeta_kivi(D) / 4 + c] = kmeta[half * (D / 2) + c];
+      for (int c = tid; c < D / 2; c += blockDim.x) r[off_kmeta_kivi(D) / 4 + c] = kmeta[kmeta_channel4(half * (D / 2) + c)];
       for (int idx = tid; idx < kBlock * (D / kGroup); idx += blockDim.x)
-        r[off_vmeta_kivi(D) / 4 + idx] = vmeta[t0 + idx / (D / kGroup)][idx % (D / kGroup)];
+        r[off_vmeta_kivi(D) / 4 + idx] = vmeta[t0 + idx % kBlock][idx / kBlock];
     } else {
       const bool q4 = cell.kind == KIND_Q4;
       // K planes: D/16 columns x 16 tokens.
@@ -198,9 +203,9 @@ __global__ void __launch_bounds__(256) k_quantize_groups(AppendArgs a) {
         r[off_v_planes(D) / 4 + d] = hi;
         if (q4) r[off_vlo(D) / 4 + d] = lo;
       }
-      for (int c = tid; c < D / 2; c += blockDim.x) r[off_kmeta_planes(D) / 4 + c] = kmeta[half * (D / 2) + c];
+      for (int c = tid; c < D / 2; c += blockDim.x) r[off_kmeta_planes(D) / 4 + c] = kmeta[kmeta_channel2(half * (D / 2) + c)];
       for (int idx = tid; idx < kBlock * (D / kGroup); idx += blockDim.x)
-        r[off_vmeta_planes(D) / 4 + idx] = vmeta[t0 + idx / (D / kGroup)][idx % (D / kGroup)];
+        r[off_vmeta_planes(D) / 4 + idx] = vmeta[t0 + idx % kBlock][idx / kBlock];
     }
   }
 }

@@ -71,46 +71,70 @@ __device__ inline float f16lo(uint32_t w) { return __half2float(__ushort_as_half
 __device__ inline float f16hi(uint32_t w) { return __half2float(__ushort_as_half((unsigned short)(w >> 16))); }
 __device__ inline float bf16f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 __device__ inline float ubyte(uint32_t x, int k) { return (float)((x >> (8 * k)) & 0xffu); }
+// Byte masks the optimizer cannot see through (a scalar move it may hoist and reuse):
+// with a visible constant it merges the mask with the byte extraction into 2-bit
+// field extracts and loses v_cvt_f32_ubyte1..3 (one extra VALU op per code).
+template <uint32_t C>
+__device__ inline uint32_t smask() {
+  uint32_t m;
+  asm("s_mov_b32 %0, %1" : "=s"(m) : "i"(C));
+  return m;
+}
+template <int P>
+__device__ inline uint32_t mask2() { return smask<(0x03030303u << (2 * P))>(); }
+template <int N>
+__device__ inline uint32_t mask4() { return smask<(0x0F0F0F0Fu << (4 * N))>(); }
 
 // Sixteen 2-bit codes of one word. K order: cf[4k + p] for the code at byte k, bits 2p.
-__device__ inline float dot16_k(uint32_t x, const float* cf, float acc) {
+template <int P>
+__device__ inline float dot4_k(uint32_t x, const float* cf, float acc) {
+  const uint32_t m = x & mask2<P>();
 #pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const uint32_t m = x & (0x03030303u << (2 * p));
-#pragma unroll
-    for (int k = 0; k < 4; ++k) acc = fmaf(cf[4 * k + p], ubyte(m, k), acc);
-  }
+  for (int k = 0; k < 4; ++k) acc = fmaf(cf[4 * k + P], ubyte(m, k), acc);
   return acc;
+}
+__device__ inline float dot16_k(uint32_t x, const float* cf, float acc) {
+  acc = dot4_k<0>(x, cf, acc);
+  acc = dot4_k<1>(x, cf, acc);
+  acc = dot4_k<2>(x, cf, acc);
+  return dot4_k<3>(x, cf, acc);
 }
 // V order: cf[4p + k] (token 4p + k of the block).
-__device__ inline float dot16_v(uint32_t x, const float* cf, float acc) {
+template <int P>
+__device__ inline float dot4_v(uint32_t x, const float* cf, float acc) {
+  const uint32_t m = x & mask2<P>();
 #pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const uint32_t m = x & (0x03030303u << (2 * p));
-#pragma unroll
-    for (int k = 0; k < 4; ++k) acc = fmaf(cf[4 * p + k], ubyte(m, k), acc);
-  }
+  for (int k = 0; k < 4; ++k) acc = fmaf(cf[4 * P + k], ubyte(m, k), acc);
   return acc;
 }
-// Eight 4-bit codes of one word. K order: cf[2k + n] for the nibble n of byte k.
-__device__ inline float dot8_k4(uint32_t x, const float* cf, float acc) {
+__device__ inline float dot16_v(uint32_t x, const float* cf, float acc) {
+  acc = dot4_v<0>(x, cf, acc);
+  acc = dot4_v<1>(x, cf, acc);
+  acc = dot4_v<2>(x, cf, acc);
+  return dot4_v<3>(x, cf, acc);
+}
+// Eight 4-bit codes of one word. K order (the K-meta position order): cf[4n + k] for
+// nibble n of byte k.
+template <int N>
+__device__ inline float dot4_k4(uint32_t x, const float* cf, float acc) {
+  const uint32_t m = x & mask4<N>();
 #pragma unroll
-  for (int n = 0; n < 2; ++n) {
-    const uint32_t m = x & (0x0F0F0F0Fu << (4 * n));
-#pragma unroll
-    for (int k = 0; k < 4; ++k) acc = fmaf(cf[2 * k + n], ubyte(m, k), acc);
-  }
+  for (int k = 0; k < 4; ++k) acc = fmaf(cf[4 * N + k], ubyte(m, k), acc);
   return acc;
+}
+__device__ inline float dot8_k4(uint32_t x, const float* cf, float acc) {
+  return dot4_k4<1>(x, cf, dot4_k4<0>(x, cf, acc));
 }
 // V order: cf[4n + k] (token 4n + k of the word's 8 tokens).
-__device__ inline float dot8_v4(uint32_t x, const float* cf, float acc) {
+template <int N>
+__device__ inline float dot4_v4(uint32_t x, const float* cf, float acc) {
+  const uint32_t m = x & mask4<N>();
 #pragma unroll
-  for (int n = 0; n < 2; ++n) {
-    const uint32_t m = x & (0x0F0F0F0Fu << (4 * n));
-#pragma unroll
-    for (int k = 0; k < 4; ++k) acc = fmaf(cf[4 * n + k], ubyte(m, k), acc);
-  }
+  for (int k = 0; k < 4; ++k) acc = fmaf(cf[4 * N + k], ubyte(m, k), acc);
   return acc;
+}
+__device__ inline float dot8_v4(uint32_t x, const float* cf, float acc) {
+  return dot4_v4<1>(x, cf, dot4_v4<0>(x, cf, acc));
 }
 
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
@@ -125,31 +149,60 @@ __device__ inline uint4 ld_stream2(const void* p) {
   return make_uint4(v.x, v.y, 0u, 0u);
 }
 
+__device__ inline int sdot4(uint32_t a, uint32_t b, int c) { return __builtin_amdgcn_sdot4((int)a, (int)b, c, false); }
+__device__ inline uint32_t udot4(uint32_t a, uint32_t b, uint32_t c) { return __builtin_amdgcn_udot4(a, b, c, false); }
+// Byte j of each of four words, packed (byte k of the result from word k).
+__device__ inline uint32_t gather_byte(uint32_t v0, uint32_t v1, uint32_t v2, uint32_t v3, int j) {
+  const uint32_t sel = (uint32_t)j | ((uint32_t)(4 + j) << 8) | 0x0c0c0000u;
+  const uint32_t t01 = __builtin_amdgcn_perm(v1, v0, sel);
+  const uint32_t t23 = __builtin_amdgcn_perm(v3, v2, sel);
+  return __builtin_amdgcn_perm(t23, t01, 0x05040100u);
+}
+// Fixed-point scale for values of magnitude below vmax: 2^(22 - e) with vmax < 2^e, so
+// rint(v * scale) fits 23 bits; returns the scale and its inverse.
+__device__ inline void fixed_scale(float vmax, float& scl, float& inv) {
+  int e = __builtin_amdgcn_frexp_expf(vmax);
+  e = e < -100 ? -100 : e;
+  scl = __builtin_amdgcn_ldexpf(1.f, 22 - e);
+  inv = __builtin_amdgcn_ldexpf(1.f, e - 22);
+}
+template <int N>
+__device__ inline float group_max(float v) {
+  for (int off = 1; off < N; off <<= 1) v = fmaxf(v, __shfl_xor(v, off));
+  return v;
+}
+
 __device__ inline uint32_t w4(const uint4& v, int i) { return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w; }
 
 struct Row {
   const uint8_t* pool;     // pool base of the storage cell
-  const int32_t* btl;      // block table row of the sequence (in LDS)
+  const uint32_t* boff;    // per logical block: record offset in 256-byte units (in LDS)
   const uint16_t* tail;    // tail of (slot, head): [2][32][D] bf16
-  int H, h, rec, N, n_q, n_groups;
-  __device__ inline const uint8_t* rec_ptr(int j) const {
-    return pool + ((size_t)btl[j] * H + h) * (size_t)rec;
-  }
+  int N, n_q, n_groups;
+  __device__ inline const uint8_t* rec_ptr(int j) const { return pool + ((uint64_t)boff[j] << 8); }
 };
 
 // ----------------------------------------------------------------------------- K pass
-// Lane mapping per wave step: GPS groups, each covered by LPG = 4*COLS lanes
-// (2 blocks x 2 token octets x COLS columns of UNIT channels). A lane reads the 8
-// words of its column for 8 consecutive tokens and keeps 8 partial scores, which
-// are summed over the COLS column lanes with DPP. Coefficients of a group are
-// built by the LPG lanes of the group (CPL channels each) and passed through LDS.
+// Lane mapping per wave step: GPS groups, each covered by LPG lanes = 2 blocks x 4
+// token quads x CPG column pairs (a column is one 32-bit word of UNIT channels). A
+// lane reads 4 consecutive tokens of two adjacent columns (two 16-byte loads) and
+// keeps 4 partial scores, summed over the CPG column-pair lanes with quad DPP. The
+// coefficients of a group are built by its LPG lanes (CPL consecutive K-meta
+// positions each) and passed through LDS.
+//
+// 2-bit planes use integer dot products: the group's coefficients become 23-bit
+// fixed point (scale 2^(22-e) from the group maximum) split into three signed byte
+// limbs; v_dot4_i32_i8 multiplies the four codes at one bit pair of a word's bytes by
+// four limbs, and the limb sums are recombined exactly in one register
+// ((l2 << 8) + l1) << 8 + l0. KIVI-4 words (4-bit codes) stay on the fp32 path.
 template <int D, int MODE, bool REFINE>
 struct KPass {
   static constexpr bool KIVI = MODE == MODE_KIVI;
   static constexpr bool DENSE = MODE == MODE_DENSE && !REFINE;
   static constexpr int UNIT = KIVI ? 8 : 16;
   static constexpr int COLS = D / UNIT;
-  static constexpr int LPG = 4 * COLS;
+  static constexpr int CPG = COLS / 2;
+  static constexpr int LPG = 8 * CPG;
   static constexpr int GPS = 64 / LPG;
   static constexpr int CPL = UNIT / 4;
   static constexpr int KMETA = KIVI ? off_kmeta_kivi(D) : off_kmeta_planes(D);
@@ -160,112 +213,169 @@ struct KPass {
     bool vm, vc;
   };
 
+  __device__ static inline void lane_role(int lane, int& blk, int& quad, int& cp) {
+    const int rl = lane % LPG;
+    blk = rl / (4 * CPG);
+    quad = (rl / CPG) % 4;
+    cp = rl % CPG;
+  }
+
   __device__ static inline void load(const Row& r, const uint32_t* selm, int s, int lane, int w, Buf& b) {
     const int gbase = (s * kWaves + w) * GPS;
     const int idx = lane * CPL;
-    const int gm = gbase + idx / D, ch = idx % D;
+    const int gm = gbase + idx / D, pos = idx % D;
     b.vm = gm < r.n_groups && (!REFINE || selm[gm] != 0u);
     if (b.vm) {
-      const uint8_t* p = r.rec_ptr(2 * gm + (ch >= D / 2)) + KMETA + 4 * (ch % (D / 2));
+      const uint8_t* p = r.rec_ptr(2 * gm + (pos >= D / 2)) + KMETA + 4 * (pos % (D / 2));
       b.meta = CPL == 4 ? ld_stream4(p) : ld_stream2(p);
     }
-    const int rl = lane % LPG;
-    const int blk = rl / (2 * COLS), oct = (rl / COLS) & 1, col = rl % COLS;
+    int blk, quad, cp;
+    lane_role(lane, blk, quad, cp);
     const int gc = gbase + lane / LPG;
     b.vc = gc < r.n_groups && (!REFINE || selm[gc] != 0u);
     if (b.vc) {
-      const uint8_t* rb = r.rec_ptr(2 * gc + blk);
-      const uint8_t* kp = rb + CODE_OFF + (col * kBlock + oct * 8) * 4;
-      b.c0 = ld_stream4(kp);
-      b.c1 = ld_stream4(kp + 16);
+      const uint8_t* kp = r.rec_ptr(2 * gc + blk) + CODE_OFF + (2 * cp * kBlock + 4 * quad) * 4;
+      b.c0 = ld_stream4(kp);                 // column 2cp, tokens 4quad..4quad+3
+      b.c1 = ld_stream4(kp + kBlock * 4);    // column 2cp+1
       if (DENSE) {
-        const uint8_t* lp = rb + off_klo(D) + (col * kBlock + oct * 8) * 4;
-        b.l0 = ld_stream4(lp);
-        b.l1 = ld_stream4(lp + 16);
+        b.l0 = ld_stream4(kp + off_klo(D));
+        b.l1 = ld_stream4(kp + off_klo(D) + kBlock * 4);
       }
     }
   }
 
+  // Coefficient of the channel at one K-meta position and its share of the constant term.
+  __device__ static inline float coef_of(uint32_t mw, float qv, float pre, float& cst) {
+    const float sc = f16lo(mw), z = f16hi(mw);
+    const float qsv = qv * sc;
+    if (REFINE) {
+      cst = fmaf(-1.5f, qsv, cst);           // sigma q . s (lo - 3/2)
+      return qsv * pre;
+    } else if (MODE == MODE_COARSE) {
+      cst += qv * fmaf(1.5f, sc, z);         // sigma q . (z + s (4 hi + 3/2))
+      return 4.f * qsv * pre;
+    } else {
+      cst = fmaf(qv, z, cst);                // sigma q . (z + s c), c 2-bit / 4-bit
+      return qsv * pre;
+    }
+  }
+
+  // Exact sum over one word's 16 channels of limb-coded coefficient x 2-bit (or 4-bit) code,
+  // accumulated into a (three limb passes, Horner in one register).
+  __device__ static inline int word_dot(const uint32_t* L, uint32_t x, uint32_t y, int limb, int a) {
+#pragma unroll
+    for (int pp = 0; pp < 4; ++pp) {
+      uint32_t m = (x >> (2 * pp)) & 0x03030303u;
+      if (DENSE) m = (m << 2) | ((y >> (2 * pp)) & 0x03030303u);   // 4-bit code 4 hi + lo
+      a = sdot4(L[3 * pp + limb], m, a);
+    }
+    return a;
+  }
+
   __device__ static inline void compute(const Row& r, const float* qs, float* scores, const uint32_t* selm,
-                                        float* coef, int s, int lane, int w, const Buf& b, float& mloc) {
+                                        float* scratch, int s, int lane, int w, const Buf& b, float& mloc) {
     const int gbase = (s * kWaves + w) * GPS;
     const int idx = lane * CPL;
-    const int gsm = idx / D, ch0 = idx % D;
-    // coefficients of CPL consecutive channels; stored [column][byte k][bit pair p]
-    float cst = 0.f;
-    if (b.vm) {
-      float cv[CPL];
+    const int gsm = idx / D, pos0 = idx % D;
+    const int gsub = lane / LPG;
+    int blk, quad, cp;
+    lane_role(lane, blk, quad, cp);
+    float part[4] = {0.f, 0.f, 0.f, 0.f};
+    float cst = 0.f, inv = 1.f;
+
+    if constexpr (KIVI) {
+      // positions 8w + 4n + k hold channel 8w + 2k + n; this lane: n fixed, k and k+1
+      float* coef = scratch;   // [GPS][D] in position order
+      if (b.vm) {
+        const int cw = pos0 / 8, r8 = pos0 % 8, n = r8 / 4, k0 = r8 % 4;
+        const float pre = n ? 1.f / 16.f : 1.f;
+        const float c0 = coef_of(b.meta.x, qs[8 * cw + 2 * k0 + n], pre, cst);
+        const float c1 = coef_of(b.meta.y, qs[8 * cw + 2 * (k0 + 1) + n], pre, cst);
+        *reinterpret_cast<float2*>(coef + gsm * D + pos0) = make_float2(c0, c1);
+      }
+      cst = group_sum<LPG>(cst);
+      wave_sync_lds();
+      if (b.vc) {
+        float cf[2 * UNIT];
+        const float4* cq = reinterpret_cast<const float4*>(coef + gsub * D + 2 * cp * UNIT);
 #pragma unroll
-      for (int rr = 0; rr < CPL; ++rr) {
-        const uint32_t mw = w4(b.meta, rr);
-        const int ch = ch0 + rr;
-        const float sc = f16lo(mw), z = f16hi(mw), qv = qs[ch];
-        const float qsv = qv * sc;
-        const float pre = KIVI ? (rr ? 1.f / 16.f : 1.f)
-                               : (rr == 0 ? 1.f : rr == 1 ? 0.25f : rr == 2 ? 0.0625f : 0.015625f);
-        if (REFINE) {
-          cv[rr] = qsv * pre;
-          cst = fmaf(-1.5f, qsv, cst);
-        } else if (MODE == MODE_COARSE || MODE == MODE_DENSE) {
-          cv[rr] = 4.f * qsv * pre;
-          cst += (MODE == MODE_COARSE) ? qv * fmaf(1.5f, sc, z) : qv * z;
-        } else {
-          cv[rr] = qsv * pre;
-          cst = fmaf(qv, z, cst);
+        for (int u = 0; u < UNIT / 2; ++u) {
+          const float4 t = cq[u];
+          cf[4 * u] = t.x;
+          cf[4 * u + 1] = t.y;
+          cf[4 * u + 2] = t.z;
+          cf[4 * u + 3] = t.w;
+        }
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+          part[tt] = dot8_k4(w4(b.c1, tt), cf + UNIT, dot8_k4(w4(b.c0, tt), cf, 0.f));
+      }
+    } else {
+      // positions 16w + 4p + k hold channel 16w + 4k + p; this lane: column w, bit pair p, k = 0..3
+      uint32_t* qlimb = reinterpret_cast<uint32_t*>(scratch);   // [GPS][COLS][4 p][3 limbs]
+      const int cw = pos0 / 16, p = (pos0 >> 2) & 3;
+      float f[4] = {0.f, 0.f, 0.f, 0.f};
+      if (b.vm) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) f[k] = coef_of(w4(b.meta, k), qs[16 * cw + 4 * k + p], 1.f, cst);
+      }
+      float fm = fmaxf(fmaxf(fabsf(f[0]), fabsf(f[1])), fmaxf(fabsf(f[2]), fabsf(f[3])));
+      fm = group_max<LPG>(fm);
+      float scl;
+      fixed_scale(fm, scl, inv);
+      if (b.vm) {
+        uint32_t qb[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) qb[k] = (uint32_t)(__float2int_rn(f[k] * scl) + 0x808080);
+        uint32_t* dst = qlimb + ((gsm * COLS + cw) * 4 + p) * 3;
+#pragma unroll
+        for (int j = 0; j < 3; ++j) dst[j] = gather_byte(qb[0], qb[1], qb[2], qb[3], j) ^ 0x80808080u;
+      }
+      cst = group_sum<LPG>(cst);
+      wave_sync_lds();
+      if (b.vc) {
+        uint32_t L[24];   // limbs of columns 2cp and 2cp+1: [col][p][limb]
+        const uint4* lq = reinterpret_cast<const uint4*>(qlimb + (gsub * COLS + 2 * cp) * 12);
+#pragma unroll
+        for (int u = 0; u < 6; ++u) {
+          const uint4 t = lq[u];
+          L[4 * u] = t.x;
+          L[4 * u + 1] = t.y;
+          L[4 * u + 2] = t.z;
+          L[4 * u + 3] = t.w;
+        }
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+          const uint32_t x0 = w4(b.c0, tt), x1 = w4(b.c1, tt);
+          const uint32_t y0 = DENSE ? w4(b.l0, tt) : 0u, y1 = DENSE ? w4(b.l1, tt) : 0u;
+          int a = word_dot(L, x0, y0, 2, 0);
+          a = word_dot(L + 12, x1, y1, 2, a);
+          a = word_dot(L, x0, y0, 1, a << 8);
+          a = word_dot(L + 12, x1, y1, 1, a);
+          a = word_dot(L, x0, y0, 0, a << 8);
+          a = word_dot(L + 12, x1, y1, 0, a);
+          part[tt] = (float)a;
         }
       }
-      float* dst = coef + gsm * D + ch0;   // CPL consecutive floats
-      if (CPL == 4) *reinterpret_cast<float4*>(dst) = make_float4(cv[0], cv[1], cv[2], cv[3]);
-      else *reinterpret_cast<float2*>(dst) = make_float2(cv[0], cv[CPL - 1]);
-    }
-    cst = group_sum<LPG>(cst);
-    wave_sync_lds();
-
-    const int gsub = lane / LPG;
-    const int rl = lane % LPG;
-    const int blk = rl / (2 * COLS), oct = (rl / COLS) & 1, col = rl % COLS;
-    float part[8], partl[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) part[j] = partl[j] = 0.f;
-    if (b.vc) {
-      float cf[UNIT];
-      const float4* cp = reinterpret_cast<const float4*>(coef + gsub * D + col * UNIT);
-#pragma unroll
-      for (int u = 0; u < UNIT / 4; ++u) {
-        const float4 t = cp[u];
-        cf[4 * u] = t.x;
-        cf[4 * u + 1] = t.y;
-        cf[4 * u + 2] = t.z;
-        cf[4 * u + 3] = t.w;
-      }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const uint32_t x = j < 4 ? w4(b.c0, j) : w4(b.c1, j - 4);
-        part[j] = KIVI ? dot8_k4(x, cf, 0.f) : dot16_k(x, cf, 0.f);
-        if (DENSE) partl[j] = dot16_k(j < 4 ? w4(b.l0, j) : w4(b.l1, j - 4), cf, 0.f);
-      }
     }
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if (DENSE) part[j] = fmaf(0.25f, partl[j], part[j]);
-      part[j] = group_sum<COLS>(part[j]);
-    }
+    for (int tt = 0; tt < 4; ++tt) part[tt] = inv * group_sum<CPG>(part[tt]);
     if (b.vc) {
       const int g = gbase + gsub;
       const uint32_t gm = REFINE ? selm[g] : 0u;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        if ((j % COLS) == col) {
-          const int tt = blk * kBlock + oct * 8 + j;
-          const int t = g * kGroup + tt;
+      for (int tt = 0; tt < 4; ++tt) {
+        if ((tt % CPG) == cp) {
+          const int ti = blk * kBlock + quad * 4 + tt;
+          const int t = g * kGroup + ti;
           if (REFINE) {
-            if ((gm >> tt) & 1u) {
-              const float sc = scores[t] + cst + part[j];
+            if ((gm >> ti) & 1u) {
+              const float sc = scores[t] + cst + part[tt];
               scores[t] = sc;
               mloc = fmaxf(mloc, sc);
             }
           } else {
-            const float sc = cst + part[j];
+            const float sc = cst + part[tt];
             scores[t] = sc;
             mloc = fmaxf(mloc, sc);
           }
@@ -275,52 +385,68 @@ struct KPass {
     wave_sync_lds();
   }
 
-  __device__ static void run(const Row& r, const float* qs, float* scores, const uint32_t* selm, float* coef,
+  __device__ static void run(const Row& r, const float* qs, float* scores, const uint32_t* selm, float* scratch,
                              int lane, int w, float& mloc) {
     const int steps = (r.n_groups + kWaves * GPS - 1) / (kWaves * GPS);
-    Buf cur, nxt;
-    load(r, selm, 0, lane, w, cur);
-    for (int s = 0; s < steps; ++s) {
-      if (s + 1 < steps) load(r, selm, s + 1, lane, w, nxt);
-      if (!REFINE || __any(cur.vm))
-        compute(r, qs, scores, selm, coef, s, lane, w, cur, mloc);
-      cur = nxt;
+    // three buffers in rotation: the loads of steps s+1 and s+2 are in flight while step s computes
+    Buf b0, b1, b2;
+    load(r, selm, 0, lane, w, b0);
+    if (1 < steps) load(r, selm, 1, lane, w, b1);
+    for (int s = 0; s < steps; s += 3) {
+      if (s + 2 < steps) load(r, selm, s + 2, lane, w, b2);
+      if (!REFINE || __any(b0.vm)) compute(r, qs, scores, selm, scratch, s, lane, w, b0, mloc);
+      if (s + 1 >= steps) break;
+      if (s + 3 < steps) load(r, selm, s + 3, lane, w, b0);
+      if (!REFINE || __any(b1.vm)) compute(r, qs, scores, selm, scratch, s + 1, lane, w, b1, mloc);
+      if (s + 2 >= steps) break;
+      if (s + 4 < steps) load(r, selm, s + 4, lane, w, b1);
+      if (!REFINE || __any(b2.vm)) compute(r, qs, scores, selm, scratch, s + 2, lane, w, b2, mloc);
     }
   }
 };
 
 // ----------------------------------------------------------------------------- V pass
-// Lane mapping per wave step: 4 blocks (64 tokens). Lane t of the step first folds
-// weight, scale and bucket offset of its token into LDS coefficients (one per
-// 32-channel group); then lane (block, chunk) reads the V words of its D/16
-// channels (16 tokens per word) and accumulates.
+// Lane mapping per wave step: 4 blocks (64 tokens).
+//   weights: lane (block jb, bit pair p, channel group e) folds weight, scale and
+//            bucket offset of the four tokens 4p..4p+3 of its block and group;
+//   values:  lane (block, chunk) reads the V words of D/16 channels (16 tokens per
+//            word) and accumulates.
+// 2-bit planes use integer dot products: the weights w_t * s_t of a (block, group)
+// become 23-bit fixed point split into three unsigned byte limbs, v_dot4_u32_u8
+// multiplies them with four tokens' codes of a channel, and each block's exact
+// integer sum is scaled back into the fp32 accumulator. A 4-bit target uses the code
+// 4*hi + lo, with lo = 0 for tokens whose low bits were not fetched (their bucket
+// midpoint sits in the per-token constant term). KIVI-4 stays on the fp32 path.
 template <int D, int MODE, bool SPARSE>
 struct VPass {
   static constexpr bool KIVI = MODE == MODE_KIVI;
-  static constexpr int VCH = D / 16;            // channels per lane
-  static constexpr int NE = D / kGroup;         // channel groups
+  static constexpr bool DENSE = MODE == MODE_DENSE;
+  static constexpr int VCH = D / 16;                // channels per lane
+  static constexpr int NE = D / kGroup;             // channel groups
   static constexpr int WPL = KIVI ? 2 * VCH : VCH;  // V words per lane
-  static constexpr int NV4 = WPL / 4;           // uint4 loads per lane
+  static constexpr int NV4 = WPL / 4;               // uint4 loads per lane
   static constexpr int VOFF = KIVI ? off_v_kivi(D) : off_v_planes(D);
   static constexpr int VMETA = KIVI ? off_vmeta_kivi(D) : off_vmeta_planes(D);
-  static constexpr bool DENSE = MODE == MODE_DENSE;
+  static constexpr int COOP = 16 * NE;              // lanes with a weights role
 
   struct Buf {
     uint4 meta;
     uint4 c[NV4];
     uint4 l[DENSE ? NV4 : 1];
-    bool v;
+    bool v, vm;
   };
 
   __device__ static inline void load(const Row& r, int s, int lane, int w, Buf& b) {
     const int nb = r.n_q / kBlock;
-    const int j = (s * kWaves + w) * 4 + lane / 16;
+    const int base = (s * kWaves + w) * 4;
+    const int jm = base + lane / (4 * NE), p = (lane / NE) % 4, e = lane % NE;
+    b.vm = lane < COOP && jm < nb;
+    if (b.vm) b.meta = ld_stream4(r.rec_ptr(jm) + VMETA + 4 * (e * kBlock + 4 * p));
+    const int j = base + lane / 16;
     b.v = j < nb;
     if (!b.v) return;
     const uint8_t* rb = r.rec_ptr(j);
-    const int t16 = lane % 16, chunk = lane % 16;
-    const uint8_t* mp = rb + VMETA + 4 * NE * t16;
-    b.meta = NE == 4 ? ld_stream4(mp) : ld_stream2(mp);
+    const int chunk = lane % 16;
     const uint8_t* vp = rb + VOFF + chunk * WPL * 4;
 #pragma unroll
     for (int i = 0; i < NV4; ++i) b.c[i] = ld_stream4(vp + 16 * i);
@@ -331,91 +457,158 @@ struct VPass {
     }
   }
 
-  __device__ static inline void compute(const Row& r, const float* scores, const uint32_t* selm, float* coefv,
-                                        int s, int lane, int w, float mfin, const Buf& b, float* acc,
-                                        float* accl, float* accz, float& lsum) {
-    const int jb = lane / 16, t16 = lane % 16;
-    const int j = (s * kWaves + w) * 4 + jb;
-    if (b.v) {
-      const int t = j * kBlock + t16;
-      const float wgt = __expf(scores[t] - mfin);
-      bool sel = DENSE;
-      if (SPARSE) sel = (selm[t >> 5] >> (t & 31)) & 1u;
-      float pre;
-      if (KIVI) pre = ((t16 & 7) >> 2) ? (1.f / 16.f) : 1.f;
-      else {
-        const int p = t16 >> 2;
-        pre = p == 0 ? 1.f : p == 1 ? 0.25f : p == 2 ? 0.0625f : 0.015625f;
-      }
-      const float mult = (MODE == MODE_Q2 || KIVI) ? 1.f : 4.f;
+  __device__ static inline void compute(const Row& r, const float* weights, const uint32_t* selm, float* scratch,
+                                        int s, int lane, int w, const Buf& b, float* acc, float& accz) {
+    const int base = (s * kWaves + w) * 4;
+    const int jbm = lane / (4 * NE), p = (lane / NE) % 4, e = lane % NE;
+    float a[4] = {0.f, 0.f, 0.f, 0.f};
+    if (b.vm) {
+      const int t0 = (base + jbm) * kBlock + 4 * p;
+      const float4 w4v = *reinterpret_cast<const float4*>(weights + t0);
+      const float wv[4] = {w4v.x, w4v.y, w4v.z, w4v.w};
+      uint32_t sel = DENSE ? 0xFu : 0u;
+      if (SPARSE) sel = (selm[t0 >> 5] >> (t0 & 31)) & 0xFu;
+      // KIVI-4 tokens 4p..4p+3 sit in nibble p % 2 of their word: fold 16^-n here
+      const float pre = KIVI && (p & 1) ? (1.f / 16.f) : 1.f;
 #pragma unroll
-      for (int e = 0; e < NE; ++e) {
-        const uint32_t mw = w4(b.meta, e);
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t mw = w4(b.meta, k);
         const float sc = f16lo(mw), z = f16hi(mw);
-        const float ws = wgt * sc;
-        coefv[(jb * NE + e) * 16 + t16] = mult * ws * pre;
-        const bool mid = (MODE == MODE_COARSE) && !sel;
-        accz[e] = fmaf(wgt, mid ? fmaf(1.5f, sc, z) : z, accz[e]);
+        a[k] = wv[k] * sc * pre;
+        const bool mid = (MODE == MODE_COARSE) && !((sel >> k) & 1u);
+        accz = fmaf(wv[k], mid ? fmaf(1.5f, sc, z) : z, accz);
       }
-      lsum += wgt;
     }
-    wave_sync_lds();
-    if (b.v) {
-      const int chunk = lane % 16;
-      const int e_lane = (chunk * VCH) / kGroup;
-      float cf[16];
-      const float4* cp = reinterpret_cast<const float4*>(coefv + (jb * NE + e_lane) * 16);
+    const int chunk = lane % 16, jb = lane / 16;
+    const int e_lane = (chunk * VCH) / kGroup;
+    const int j = base + jb;
+    if constexpr (KIVI) {
+      float* coefv = scratch;   // [4][NE][16]
+      if (b.vm) *reinterpret_cast<float4*>(coefv + (jbm * NE + e) * 16 + 4 * p) = make_float4(a[0], a[1], a[2], a[3]);
+      wave_sync_lds();
+      if (b.v) {
+        float cf[16];
+        const float4* cp = reinterpret_cast<const float4*>(coefv + (jb * NE + e_lane) * 16);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const float4 tq = cp[u];
-        cf[4 * u] = tq.x;
-        cf[4 * u + 1] = tq.y;
-        cf[4 * u + 2] = tq.z;
-        cf[4 * u + 3] = tq.w;
-      }
-      if (KIVI) {
+        for (int u = 0; u < 4; ++u) {
+          const float4 tq = cp[u];
+          cf[4 * u] = tq.x;
+          cf[4 * u + 1] = tq.y;
+          cf[4 * u + 2] = tq.z;
+          cf[4 * u + 3] = tq.w;
+        }
 #pragma unroll
         for (int c = 0; c < VCH; ++c) {
 #pragma unroll
-          for (int jj = 0; jj < 2; ++jj) acc[c] = dot8_v4(w4(b.c[(2 * c + jj) / 4], (2 * c + jj) % 4), cf + 8 * jj, acc[c]);
+          for (int jj = 0; jj < 2; ++jj)
+            acc[c] = dot8_v4(w4(b.c[(2 * c + jj) / 4], (2 * c + jj) % 4), cf + 8 * jj, acc[c]);
         }
-      } else {
+      }
+    } else {
+      uint32_t* vlimb = reinterpret_cast<uint32_t*>(scratch);   // [4][NE][4 p][3]
+      float* vinv = scratch + 4 * NE * 12;                      // [4][NE]
+      float am = fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3]));
+      am = fmaxf(am, __shfl_xor(am, NE));
+      am = fmaxf(am, __shfl_xor(am, 2 * NE));
+      float scl, inv;
+      fixed_scale(am, scl, inv);
+      if (b.vm) {
+        uint32_t qb[4];
 #pragma unroll
-        for (int c = 0; c < VCH; ++c) acc[c] = dot16_v(w4(b.c[c / 4], c % 4), cf, acc[c]);
-        if (DENSE) {
+        for (int k = 0; k < 4; ++k) qb[k] = (uint32_t)__float2uint_rn(a[k] * scl);
+        uint32_t* dst = vlimb + ((jbm * NE + e) * 4 + p) * 3;
 #pragma unroll
-          for (int c = 0; c < VCH; ++c) accl[c] = dot16_v(w4(b.l[c / 4], c % 4), cf, accl[c]);
+        for (int jj = 0; jj < 3; ++jj) dst[jj] = gather_byte(qb[0], qb[1], qb[2], qb[3], jj);
+        if (p == 0) vinv[jbm * NE + e] = inv;
+      }
+      wave_sync_lds();
+      if (b.v) {
+        uint32_t L[12];
+        const uint4* lp = reinterpret_cast<const uint4*>(vlimb + (jb * NE + e_lane) * 12);
+#pragma unroll
+        for (int u = 0; u < 3; ++u) {
+          const uint4 t = lp[u];
+          L[4 * u] = t.x;
+          L[4 * u + 1] = t.y;
+          L[4 * u + 2] = t.z;
+          L[4 * u + 3] = t.w;
         }
+        float binv = vinv[jb * NE + e_lane];
+        const float hscale = 4.f * binv;   // high bits only: code 4 hi
+        bool need_lo = DENSE;
+        uint32_t m32 = 0xffffffffu;
+        uint4 lw[NV4];
         if (SPARSE) {
           const uint32_t bm = (selm[j >> 1] >> (16 * (j & 1))) & 0xffffu;
-          if (bm) {
-            uint32_t m32 = 0;
+          need_lo = bm != 0u;
+          if (need_lo) {
+            m32 = 0;
 #pragma unroll
             for (int tt = 0; tt < 16; ++tt)
               if ((bm >> tt) & 1u) m32 |= 3u << (8 * (tt & 3) + 2 * (tt >> 2));
-            const uint4* lp = reinterpret_cast<const uint4*>(r.rec_ptr(j) + off_vlo(D) + chunk * VCH * 4);
-            uint4 lw[NV4];
+            const uint8_t* lq = r.rec_ptr(j) + off_vlo(D) + chunk * VCH * 4;
 #pragma unroll
-            for (int i = 0; i < NV4; ++i) lw[i] = lp[i];
-#pragma unroll
-            for (int c = 0; c < VCH; ++c) accl[c] = dot16_v(w4(lw[c / 4], c % 4) & m32, cf, accl[c]);
+            for (int i = 0; i < NV4; ++i) lw[i] = *reinterpret_cast<const uint4*>(lq + 16 * i);
           }
+        }
+        if (DENSE) {
+#pragma unroll
+          for (int i = 0; i < NV4; ++i) lw[i] = b.l[i];
+        }
+#pragma unroll
+        for (int c = 0; c < VCH; ++c) {
+          const uint32_t x = w4(b.c[c / 4], c % 4);
+          uint32_t a0 = 0, a1 = 0, a2 = 0;
+          if (MODE == MODE_Q2 || !(DENSE || SPARSE)) {
+            // 2-bit codes, or a 4-bit target read at high bits only (code 4 hi: the 4 is in hscale)
+#pragma unroll
+            for (int pp = 0; pp < 4; ++pp) {
+              const uint32_t m = (x >> (2 * pp)) & 0x03030303u;
+              a0 = udot4(L[3 * pp], m, a0);
+              a1 = udot4(L[3 * pp + 1], m, a1);
+              a2 = udot4(L[3 * pp + 2], m, a2);
+            }
+          } else if (need_lo) {
+            const uint32_t y = w4(lw[c / 4], c % 4) & m32;
+#pragma unroll
+            for (int pp = 0; pp < 4; ++pp) {
+              const uint32_t m = (((x >> (2 * pp)) & 0x03030303u) << 2) | ((y >> (2 * pp)) & 0x03030303u);
+              a0 = udot4(L[3 * pp], m, a0);
+              a1 = udot4(L[3 * pp + 1], m, a1);
+              a2 = udot4(L[3 * pp + 2], m, a2);
+            }
+          } else {
+#pragma unroll
+            for (int pp = 0; pp < 4; ++pp) {
+              const uint32_t m = (x >> (2 * pp)) & 0x03030303u;
+              a0 = udot4(L[3 * pp], m, a0);
+              a1 = udot4(L[3 * pp + 1], m, a1);
+              a2 = udot4(L[3 * pp + 2], m, a2);
+            }
+          }
+          acc[c] = fmaf(need_lo || MODE == MODE_Q2 ? binv : hscale, (float)((a2 << 16) + (a1 << 8) + a0), acc[c]);
         }
       }
     }
     wave_sync_lds();
   }
 
-  __device__ static void run(const Row& r, const float* scores, const uint32_t* selm, float* coefv, int lane,
-                             int w, float mfin, float* acc, float* accl, float* accz, float& lsum) {
+  __device__ static void run(const Row& r, const float* weights, const uint32_t* selm, float* scratch, int lane,
+                             int w, float* acc, float& accz) {
     const int nb = r.n_q / kBlock;
     const int steps = (nb + kWaves * 4 - 1) / (kWaves * 4);
-    Buf cur, nxt;
-    load(r, 0, lane, w, cur);
-    for (int s = 0; s < steps; ++s) {
-      if (s + 1 < steps) load(r, s + 1, lane, w, nxt);
-      compute(r, scores, selm, coefv, s, lane, w, mfin, cur, acc, accl, accz, lsum);
-      cur = nxt;
+    Buf b0, b1, b2;
+    load(r, 0, lane, w, b0);
+    if (1 < steps) load(r, 1, lane, w, b1);
+    for (int s = 0; s < steps; s += 3) {
+      if (s + 2 < steps) load(r, s + 2, lane, w, b2);
+      compute(r, weights, selm, scratch, s, lane, w, b0, acc, accz);
+      if (s + 1 >= steps) break;
+      if (s + 3 < steps) load(r, s + 3, lane, w, b0);
+      compute(r, weights, selm, scratch, s + 1, lane, w, b1, acc, accz);
+      if (s + 2 >= steps) break;
+      if (s + 4 < steps) load(r, s + 4, lane, w, b1);
+      compute(r, weights, selm, scratch, s + 2, lane, w, b2, acc, accz);
     }
   }
 };
@@ -423,7 +616,7 @@ struct VPass {
 struct Smem {
   float* scores;    // [lpad]; after the V pass: [kThreads][VCH] partials, then [kWaves][D] tail partials
   uint32_t* selm;   // [lpad / 32]
-  int32_t* btl;     // [lpad / 16]
+  uint32_t* boff;   // [lpad / 16] record offset of each logical block, 256-byte units
   float* qs;        // [D]
   float* wscr;      // [kWaves][kWaveScratch]
   float* misc;      // [64 + kWaves * 4]
@@ -500,38 +693,45 @@ __device__ void row_body(const DecodeArgs& a, const Row& r, const Smem& sm, size
   }
 
   // ---- V pass
-  float acc[VCH], accl[VCH], accz[NE];
-#pragma unroll
-  for (int c = 0; c < VCH; ++c) acc[c] = accl[c] = 0.f;
-#pragma unroll
-  for (int e = 0; e < NE; ++e) accz[e] = 0.f;
+  // softmax weights w_t = exp(s_t - m') replace the scores in LDS
   float lsum = 0.f;
-  VPass<D, MODE, SPARSE>::run(r, scores, selm, coef, lane, w, mfin, acc, accl, accz, lsum);
+  for (int t = tid; t < r.N; t += kThreads) {
+    const float wgt = __expf(scores[t] - mfin);
+    scores[t] = wgt;
+    lsum += wgt;
+  }
+  __syncthreads();
+  const float* weights = scores;
+  float acc[VCH];
+#pragma unroll
+  for (int c = 0; c < VCH; ++c) acc[c] = 0.f;
+  float accz = 0.f;   // constant terms of channel group lane % NE
+  VPass<D, MODE, SPARSE>::run(r, weights, selm, coef, lane, w, acc, accz);
   // tail values, exact
   float tacc[D / 64];
 #pragma unroll
   for (int i = 0; i < D / 64; ++i) tacc[i] = 0.f;
   for (int t = r.n_q + w; t < r.N; t += kWaves) {
-    const float wgt = __expf(scores[t] - mfin);
+    const float wgt = weights[t];
     const uint16_t* vt = r.tail + (size_t)(kGroup + t % kGroup) * D;
 #pragma unroll
     for (int i = 0; i < D / 64; ++i) tacc[i] = fmaf(wgt, bf16f(vt[lane + 64 * i]), tacc[i]);
-    if (lane == 0) lsum += wgt;
   }
   __syncthreads();   // scores are dead from here on: reuse them for partials
   float* red = scores;                         // [kThreads][VCH]
   float* tred = scores + kThreads * VCH;       // [kWaves][D]
 #pragma unroll
-  for (int c = 0; c < VCH; ++c) red[tid * VCH + c] = fmaf(0.25f, accl[c], acc[c]);
+  for (int c = 0; c < VCH; ++c) red[tid * VCH + c] = acc[c];
 #pragma unroll
   for (int i = 0; i < D / 64; ++i) tred[w * D + lane + 64 * i] = tacc[i];
   lsum = wave_sum(lsum);
+  float zs[NE];
 #pragma unroll
-  for (int e = 0; e < NE; ++e) accz[e] = wave_sum(accz[e]);
+  for (int e = 0; e < NE; ++e) zs[e] = wave_sum((lane % NE) == e ? accz : 0.f);
   if (lane == 0) {
     misc[24 + w] = lsum;
 #pragma unroll
-    for (int e = 0; e < NE; ++e) misc[32 + w * 4 + e] = accz[e];
+    for (int e = 0; e < NE; ++e) misc[32 + w * 4 + e] = zs[e];
   }
   __syncthreads();
   float L = 0.f;
@@ -556,19 +756,26 @@ __device__ void row_body(const DecodeArgs& a, const Row& r, const Smem& sm, size
   }
 }
 
+__host__ __device__ inline size_t pad4(size_t n) { return (n + 3) / 4 * 4; }   // keep 16-byte alignment
 __host__ __device__ inline size_t lds_lpad(int max_len) { return ((size_t)max_len + 63) / 64 * 64; }
 __host__ __device__ inline size_t lds_region_a(int max_len, int D) {
   const size_t need = (size_t)kThreads * (D / 16) + (size_t)kWaves * D;
   const size_t lp = lds_lpad(max_len);
-  return lp > need ? lp : need;
+  return pad4(lp > need ? lp : need);
 }
 __host__ __device__ inline size_t decode_lds_floats(int max_len, int D) {
   const size_t lp = lds_lpad(max_len);
-  return lds_region_a(max_len, D) + lp / 32 + lp / 16 + 16 + D + (size_t)kWaves * kWaveScratch + 64 + kWaves * 4;
+  return lds_region_a(max_len, D) + pad4(lp / 32) + pad4(lp / 16 + 16) + D + (size_t)kWaves * kWaveScratch + 64 +
+         kWaves * 4;
 }
 
-template <int D>
-__global__ void __launch_bounds__(kThreads) k_decode(DecodeArgs a) {
+// One kernel per selection regime of the launch (tau = 0, tau > 1, 0 < tau <= 1, or the
+// KIVI-4 layout), so each variant gets its own register allocation; rows of 2-bit cells
+// run the 2-bit path inside every planes variant.
+enum : int { VAR_KIVI = 0, VAR_DENSE = 1, VAR_COARSE = 2, VAR_SPARSE = 3 };
+
+template <int D, int VAR>
+__global__ void __launch_bounds__(kThreads, 4) k_decode(DecodeArgs a) {
   extern __shared__ float smem[];
   const int row = blockIdx.x;
   const int h = row % a.n_heads;
@@ -583,8 +790,8 @@ __global__ void __launch_bounds__(kThreads) k_decode(DecodeArgs a) {
   Smem sm;
   sm.scores = smem;
   sm.selm = reinterpret_cast<uint32_t*>(smem + lds_region_a(a.max_len, D));
-  sm.btl = reinterpret_cast<int32_t*>(sm.selm + lp / 32);
-  sm.qs = reinterpret_cast<float*>(sm.btl + lp / 16 + 16);
+  sm.boff = sm.selm + pad4(lp / 32);
+  sm.qs = reinterpret_cast<float*>(sm.boff + pad4(lp / 16 + 16));
   sm.wscr = sm.qs + D;
   sm.misc = sm.wscr + kWaves * kWaveScratch;
 
@@ -601,12 +808,9 @@ __global__ void __launch_bounds__(kThreads) k_decode(DecodeArgs a) {
 
   Row r;
   r.pool = a.ws + cell.pool_off;
-  r.btl = sm.btl;
+  r.boff = sm.boff;
   const int slot = a.seq_slots ? a.seq_slots[b] : b;
   r.tail = reinterpret_cast<const uint16_t*>(a.ws + cell.tail_off) + ((size_t)slot * a.n_heads + h) * tail_elems(D);
-  r.H = a.n_heads;
-  r.h = h;
-  r.rec = record_bytes(cell.kind, D);
   r.N = N;
   r.n_q = (N / kGroup) * kGroup;
   r.n_groups = N / kGroup;
@@ -614,7 +818,8 @@ __global__ void __launch_bounds__(kThreads) k_decode(DecodeArgs a) {
   // block table row and sigma * q into LDS
   const int32_t* bt = a.block_table + (size_t)b * a.bt_stride;
   const int nbq = r.n_q / kBlock;
-  for (int j = tid; j < nbq; j += kThreads) sm.btl[j] = bt[j];
+  const uint32_t rec256 = (uint32_t)(record_bytes(cell.kind, D) / 256);
+  for (int j = tid; j < nbq; j += kThreads) sm.boff[j] = ((uint32_t)bt[j] * (uint32_t)a.n_heads + (uint32_t)h) * rec256;
   for (int d = tid; d < D; d += kThreads) {
     const size_t qi = orow * D + d;
     const float qv = a.q_bf16 ? bf16f(reinterpret_cast<const uint16_t*>(a.q)[qi]) : reinterpret_cast<const float*>(a.q)[qi];
@@ -622,39 +827,42 @@ __global__ void __launch_bounds__(kThreads) k_decode(DecodeArgs a) {
   }
   __syncthreads();
 
-  if (cell.kind == KIND_KIVI4) {
+  if constexpr (VAR == VAR_KIVI) {
     row_body<D, MODE_KIVI, false>(a, r, sm, orow);
-  } else if (cell.kind == KIND_Q2) {
-    row_body<D, MODE_Q2, false>(a, r, sm, orow);
-  } else if (a.tau <= 0.f) {
-    row_body<D, MODE_DENSE, false>(a, r, sm, orow);
-  } else if (a.tau > 1.f) {
-    row_body<D, MODE_COARSE, false>(a, r, sm, orow);
   } else {
-    row_body<D, MODE_COARSE, true>(a, r, sm, orow);
+    if (cell.kind == KIND_Q2) row_body<D, MODE_Q2, false>(a, r, sm, orow);
+    else if (VAR == VAR_DENSE) row_body<D, MODE_DENSE, false>(a, r, sm, orow);
+    else if (VAR == VAR_COARSE) row_body<D, MODE_COARSE, false>(a, r, sm, orow);
+    else row_body<D, MODE_COARSE, true>(a, r, sm, orow);
   }
 }
 
 size_t decode_lds_bytes(int max_len, int head_dim) { return decode_lds_floats(max_len, head_dim) * 4; }
 
+template <int D, int VAR>
+static void launch_variant(const DecodeArgs& a, size_t rows, size_t lds, hipStream_t stream) {
+  static bool attr_set = false;
+  if (!attr_set) {
+    (void)hipFuncSetAttribute((const void*)k_decode<D, VAR>, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    attr_set = true;
+  }
+  hipLaunchKernelGGL((k_decode<D, VAR>), dim3((unsigned)rows), dim3(kThreads), lds, stream, a);
+}
+
+template <int D>
+static void launch_d(const DecodeArgs& a, size_t rows, size_t lds, hipStream_t stream) {
+  if (a.cells[0].kind == KIND_KIVI4) launch_variant<D, VAR_KIVI>(a, rows, lds, stream);
+  else if (a.tau <= 0.f) launch_variant<D, VAR_DENSE>(a, rows, lds, stream);
+  else if (a.tau > 1.f) launch_variant<D, VAR_COARSE>(a, rows, lds, stream);
+  else launch_variant<D, VAR_SPARSE>(a, rows, lds, stream);
+}
+
 hipError_t launch_decode(const DecodeArgs& a, int head_dim, hipStream_t stream) {
   const size_t rows = (size_t)a.n_cells * a.n_seqs * a.n_heads;
   if (rows == 0) return hipSuccess;
   const size_t lds = decode_lds_bytes(a.max_len, head_dim);
-  static bool attr_set[2] = {false, false};
-  if (head_dim == 128) {
-    if (!attr_set[1]) {
-      (void)hipFuncSetAttribute((const void*)k_decode<128>, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-      attr_set[1] = true;
-    }
-    hipLaunchKernelGGL(k_decode<128>, dim3((unsigned)rows), dim3(kThreads), lds, stream, a);
-  } else {
-    if (!attr_set[0]) {
-      (void)hipFuncSetAttribute((const void*)k_decode<64>, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-      attr_set[0] = true;
-    }
-    hipLaunchKernelGGL(k_decode<64>, dim3((unsigned)rows), dim3(kThreads), lds, stream, a);
-  }
+  if (head_dim == 128) launch_d<128>(a, rows, lds, stream);
+  else launch_d<64>(a, rows, lds, stream);
   return hipGetLastError();
 }
 

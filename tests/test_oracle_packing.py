@@ -81,8 +81,16 @@ def test_pack_roundtrip(D, layout, bits):
         assert np.array_equal(kc, qh["kc"][t0:t0 + 16])
         assert np.array_equal(vc, qh["vc"][t0:t0 + 16])
         ks, kz = _meta(km)
-        chs = slice(half * D // 2, (half + 1) * D // 2)
-        assert np.array_equal(ks, qh["ks"][g, chs]) and np.array_equal(kz, qh["kz"][g, chs])
+        # position -> channel inside a K column: 2-bit word byte k / bit pair p, or byte k / nibble n
+        for i in range(D // 2):
+            pos = half * D // 2 + i
+            if layout == O.LAYOUT_KIVI4:
+                w, r = divmod(pos, 8)
+                chn = 8 * w + 2 * (r % 4) + r // 4
+            else:
+                w, r = divmod(pos, 16)
+                chn = 16 * w + 4 * (r % 4) + r // 4
+            assert ks[i] == qh["ks"][g, chn] and kz[i] == qh["kz"][g, chn]
         vs, vz = _meta(vm)
-        assert np.array_equal(vs.reshape(16, D // 32), qh["vs"][t0:t0 + 16])
-        assert np.array_equal(vz.reshape(16, D // 32), qh["vz"][t0:t0 + 16])
+        assert np.array_equal(vs.reshape(D // 32, 16).T, qh["vs"][t0:t0 + 16])
+        assert np.array_equal(vz.reshape(D // 32, 16).T, qh["vz"][t0:t0 + 16])

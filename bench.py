@@ -28,6 +28,30 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
+COUNTERS = os.path.join(ROOT, "profiles", "k_decode_c4_tau0.01_counters.json")
+KERNEL_SOURCES = ["quantized_kv_cache_loopkv_amd/csrc/decode.hip", "quantized_kv_cache_loopkv_amd/csrc/layout.h"]
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def counter_traffic():
+    """HBM bytes per decode launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary
+    (copy-calibrated), or None when the decode kernel's source has changed since."""
+    try:
+        with open(COUNTERS) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if d.get("source_sha256") != kernel_source_hash():
+        return None
+    return d.get("traffic_bytes_per_launch")
 
 
 def log(*a):
@@ -96,8 +120,11 @@ def sel_counts_from_mask(sm, n_q):
     return bits.sum(axis=-1)
 
 
-def cpu_baseline(cfg, plan, tau, rows, log):
-    """Time the fp64 oracle (quantize + loop-aware decode of one row) on sampled rows."""
+def cpu_baseline(cfg, plan, tau, rows, log, min_seconds=10.0, max_evals=400):
+    """Time the fp64 oracle (quantize + loop-aware decode of one row) on sampled rows.
+
+    The distinct rows' inputs are drawn first (untimed); the oracle then evaluates the
+    rows round-robin until about ``min_seconds`` of CPU time has accumulated."""
     import numpy as np
     from oracle import loopkv_oracle as O
     from synth import recipes as R
@@ -109,8 +136,7 @@ def cpu_baseline(cfg, plan, tau, rows, log):
         cores = 1
     factors = R.factor_table(cfg)
     sig = float(np.float32(1.0 / math.sqrt(cfg.head_dim)))
-    t_total = 0.0
-    bytes_total = 0
+    inputs = []
     for (c, b, h) in rows:
         st = O.storage_cell(plan.reshape(cfg.n_loops, cfg.n_layers), c)
         kind = O.target_kind(plan.reshape(cfg.n_loops, cfg.n_layers), c)
@@ -119,6 +145,12 @@ def cpu_baseline(cfg, plan, tau, rows, log):
         K = bf16_bits_to_f32(kb).astype(np.float64)
         V = bf16_bits_to_f32(vb).astype(np.float64)
         q = R.q_values(cfg, c, 0, b, h).astype(np.float64)
+        inputs.append((q, K, V, kind, N))
+    t_total = 0.0
+    bytes_total = 0
+    evals = 0
+    while evals < max_evals and (t_total < min_seconds or evals < len(inputs)):
+        q, K, V, kind, N = inputs[evals % len(inputs)]
         t0 = time.perf_counter()
         o, sel, _ = O.decode_row(q, K, V, kind, tau, sig)
         t_total += time.perf_counter() - t0
@@ -126,11 +158,13 @@ def cpu_baseline(cfg, plan, tau, rows, log):
         bytes_total += n_q * 96 + (N - n_q) * 512 + 512 + 4 * ((N + 15) // 16) + 4
         if kind == 0:
             bytes_total += 64 * int(sel.sum())
-    log(f"cpu oracle: {len(rows)} rows in {t_total:.2f}s")
+        evals += 1
+    log(f"cpu oracle: {evals} row evaluations ({len(inputs)} distinct rows) in {t_total:.2f}s")
     return {"value": bytes_total / t_total / 1e9, "unit": "GB/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{len(rows)} (cell, seq, head) rows of the 16K-context plan (one 4-bit, one 2-bit, "
-                      f"one reuse cell per pair of rows), fp64 quantize + loop-aware decode per row; "
-                      f"{t_total:.2f} s measured, input generation excluded"}
+            "sample": f"{len(inputs)} distinct (cell, seq, head) rows of the 16K-context plan (4-bit, 2-bit and "
+                      f"reuse cells), evaluated round-robin {evals} times: fp64 quantize + loop-aware decode "
+                      f"per row, {t_total:.2f} s measured, input generation excluded; value = the rows' "
+                      f"algorithmic bytes / oracle time"}
 
 
 def main():
@@ -144,7 +178,7 @@ def main():
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-kivi", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=4)
+    ap.add_argument("--cpu-rows", type=int, default=6)
     ap.add_argument("--table", choices=["shuffled", "identity"], default="shuffled",
                     help="block table of the workload (the configuration uses a shuffled one)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -317,7 +351,7 @@ def main():
                                "1-token append + whole-plan decode per step",
                    "global_batch": B, "seq_len": args.ctx, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": counter_traffic(),
                      "kernel": "k_decode<128, tau regime>", "bytes_per_launch": dec_bytes,
                      "mean_launch_ms": round(dec_mean_ms, 4)},
         "cpu_baseline": cpu,

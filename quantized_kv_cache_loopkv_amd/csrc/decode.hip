@@ -166,10 +166,31 @@ __device__ inline void fixed_scale(float vmax, float& scl, float& inv) {
   scl = __builtin_amdgcn_ldexpf(1.f, 22 - e);
   inv = __builtin_amdgcn_ldexpf(1.f, e - 22);
 }
+// Max over aligned groups of N lanes (same lane pattern as group_sum).
 template <int N>
 __device__ inline float group_max(float v) {
-  for (int off = 1; off < N; off <<= 1) v = fmaxf(v, __shfl_xor(v, off));
+  if (N >= 2) v = fmaxf(v, dpp<0xB1>(v));
+  if (N >= 4) v = fmaxf(v, dpp<0x4E>(v));
+  if (N >= 8) v = fmaxf(v, dpp<0x141>(v));
+  if (N >= 16) v = fmaxf(v, dpp<0x140>(v));
+  if (N >= 32) v = fmaxf(v, __shfl_xor(v, 16));
+  if (N >= 64) v = fmaxf(v, __shfl_xor(v, 32));
   return v;
+}
+
+// Codes at bit pair p of every byte of two words, each as four bytes: one 64-bit shift
+// serves both words (bits pulled in from the upper word land above bit 25 and are
+// masked off).
+__device__ inline void bitpairs2(uint32_t x0, uint32_t x1, uint32_t* m0, uint32_t* m1) {
+  const uint64_t X = ((uint64_t)x1 << 32) | x0;
+  m0[0] = x0 & 0x03030303u;
+  m1[0] = x1 & 0x03030303u;
+#pragma unroll
+  for (int p = 1; p < 4; ++p) {
+    const uint64_t Y = X >> (2 * p);
+    m0[p] = (uint32_t)Y & 0x03030303u;
+    m1[p] = (uint32_t)(Y >> 32) & 0x03030303u;
+  }
 }
 
 __device__ inline uint32_t w4(const uint4& v, int i) { return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w; }
@@ -260,15 +281,11 @@ struct KPass {
     }
   }
 
-  // Exact sum over one word's 16 channels of limb-coded coefficient x 2-bit (or 4-bit) code,
-  // accumulated into a (three limb passes, Horner in one register).
-  __device__ static inline int word_dot(const uint32_t* L, uint32_t x, uint32_t y, int limb, int a) {
+  // One limb's contribution of a word's 16 channels: codes m[p] (four channels at bit pair p)
+  // times the limb bytes of those channels, accumulated into a.
+  __device__ static inline int word_dot(const uint32_t* L, const uint32_t* m, int limb, int a) {
 #pragma unroll
-    for (int pp = 0; pp < 4; ++pp) {
-      uint32_t m = (x >> (2 * pp)) & 0x03030303u;
-      if (DENSE) m = (m << 2) | ((y >> (2 * pp)) & 0x03030303u);   // 4-bit code 4 hi + lo
-      a = sdot4(L[3 * pp + limb], m, a);
-    }
+    for (int pp = 0; pp < 4; ++pp) a = sdot4(L[3 * pp + limb], m[pp], a);
     return a;
   }
 
@@ -346,14 +363,23 @@ struct KPass {
         }
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) {
-          const uint32_t x0 = w4(b.c0, tt), x1 = w4(b.c1, tt);
-          const uint32_t y0 = DENSE ? w4(b.l0, tt) : 0u, y1 = DENSE ? w4(b.l1, tt) : 0u;
-          int a = word_dot(L, x0, y0, 2, 0);
-          a = word_dot(L + 12, x1, y1, 2, a);
-          a = word_dot(L, x0, y0, 1, a << 8);
-          a = word_dot(L + 12, x1, y1, 1, a);
-          a = word_dot(L, x0, y0, 0, a << 8);
-          a = word_dot(L + 12, x1, y1, 0, a);
+          uint32_t m0[4], m1[4];
+          bitpairs2(w4(b.c0, tt), w4(b.c1, tt), m0, m1);
+          if (DENSE) {   // 4-bit codes 4 hi + lo
+            uint32_t n0[4], n1[4];
+            bitpairs2(w4(b.l0, tt), w4(b.l1, tt), n0, n1);
+#pragma unroll
+            for (int pp = 0; pp < 4; ++pp) {
+              m0[pp] = (m0[pp] << 2) | n0[pp];
+              m1[pp] = (m1[pp] << 2) | n1[pp];
+            }
+          }
+          int a = word_dot(L, m0, 2, 0);
+          a = word_dot(L + 12, m1, 2, a);
+          a = word_dot(L, m0, 1, a << 8);
+          a = word_dot(L + 12, m1, 1, a);
+          a = word_dot(L, m0, 0, a << 8);
+          a = word_dot(L + 12, m1, 0, a);
           part[tt] = (float)a;
         }
       }
@@ -508,8 +534,14 @@ struct VPass {
       uint32_t* vlimb = reinterpret_cast<uint32_t*>(scratch);   // [4][NE][4 p][3]
       float* vinv = scratch + 4 * NE * 12;                      // [4][NE]
       float am = fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3]));
-      am = fmaxf(am, __shfl_xor(am, NE));
-      am = fmaxf(am, __shfl_xor(am, 2 * NE));
+      // max over the 4 bit-pair lanes of (block, group): lanes e + NE*p inside a 16-lane row
+      if (NE == 4) {
+        am = fmaxf(am, dpp<0x124>(am));   // row_ror:4
+        am = fmaxf(am, dpp<0x128>(am));   // row_ror:8
+      } else {
+        am = fmaxf(am, __shfl_xor(am, NE));
+        am = fmaxf(am, __shfl_xor(am, 2 * NE));
+      }
       float scl, inv;
       fixed_scale(am, scl, inv);
       if (b.vm) {
@@ -555,38 +587,33 @@ struct VPass {
 #pragma unroll
           for (int i = 0; i < NV4; ++i) lw[i] = b.l[i];
         }
+        const bool lo_path = (DENSE || SPARSE) && MODE != MODE_Q2 && need_lo;
+        const float cscale = lo_path || MODE == MODE_Q2 ? binv : hscale;
 #pragma unroll
-        for (int c = 0; c < VCH; ++c) {
-          const uint32_t x = w4(b.c[c / 4], c % 4);
-          uint32_t a0 = 0, a1 = 0, a2 = 0;
-          if (MODE == MODE_Q2 || !(DENSE || SPARSE)) {
-            // 2-bit codes, or a 4-bit target read at high bits only (code 4 hi: the 4 is in hscale)
+        for (int c = 0; c < VCH; c += 2) {
+          uint32_t mc[2][4];
+          bitpairs2(w4(b.c[c / 4], c % 4), w4(b.c[c / 4], c % 4 + 1), mc[0], mc[1]);
+          if (lo_path) {   // 4-bit code 4 hi + lo, lo only for fetched tokens
+            uint32_t nc[2][4];
+            bitpairs2(w4(lw[c / 4], c % 4) & m32, w4(lw[c / 4], c % 4 + 1) & m32, nc[0], nc[1]);
 #pragma unroll
-            for (int pp = 0; pp < 4; ++pp) {
-              const uint32_t m = (x >> (2 * pp)) & 0x03030303u;
-              a0 = udot4(L[3 * pp], m, a0);
-              a1 = udot4(L[3 * pp + 1], m, a1);
-              a2 = udot4(L[3 * pp + 2], m, a2);
-            }
-          } else if (need_lo) {
-            const uint32_t y = w4(lw[c / 4], c % 4) & m32;
+            for (int i = 0; i < 2; ++i)
 #pragma unroll
-            for (int pp = 0; pp < 4; ++pp) {
-              const uint32_t m = (((x >> (2 * pp)) & 0x03030303u) << 2) | ((y >> (2 * pp)) & 0x03030303u);
-              a0 = udot4(L[3 * pp], m, a0);
-              a1 = udot4(L[3 * pp + 1], m, a1);
-              a2 = udot4(L[3 * pp + 2], m, a2);
-            }
-          } else {
-#pragma unroll
-            for (int pp = 0; pp < 4; ++pp) {
-              const uint32_t m = (x >> (2 * pp)) & 0x03030303u;
-              a0 = udot4(L[3 * pp], m, a0);
-              a1 = udot4(L[3 * pp + 1], m, a1);
-              a2 = udot4(L[3 * pp + 2], m, a2);
-            }
+              for (int pp = 0; pp < 4; ++pp) mc[i][pp] = (mc[i][pp] << 2) | nc[i][pp];
           }
-          acc[c] = fmaf(need_lo || MODE == MODE_Q2 ? binv : hscale, (float)((a2 << 16) + (a1 << 8) + a0), acc[c]);
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            uint32_t a = 0;
+#pragma unroll
+            for (int pp = 0; pp < 4; ++pp) a = udot4(L[3 * pp + 2], mc[i][pp], a);
+            a <<= 8;
+#pragma unroll
+            for (int pp = 0; pp < 4; ++pp) a = udot4(L[3 * pp + 1], mc[i][pp], a);
+            a <<= 8;
+#pragma unroll
+            for (int pp = 0; pp < 4; ++pp) a = udot4(L[3 * pp], mc[i][pp], a);
+            acc[c + i] = fmaf(cscale, (float)a, acc[c + i]);
+          }
         }
       }
     }

@@ -314,6 +314,13 @@ def main():
         del kw
         torch.cuda.empty_cache()
 
+    try:
+        from synth import gpu as G
+        extra["read_ceiling"] = G.read_ceiling()
+        log(f"read ceiling: {extra['read_ceiling']}")
+    except Exception as e:  # the probe is context only
+        log(f"read ceiling probe failed: {e}")
+
     cpu = None
     if not args.no_cpu:
         rows = []

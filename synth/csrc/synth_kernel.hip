@@ -71,6 +71,49 @@ __global__ void k_normal(uint64_t seed, uint32_t stream, uint64_t offset, size_t
   }
 }
 
+// Read-bandwidth probes (no method arithmetic): stream a buffer, or read chunk_bytes at
+// the starts of records taken in the order of a permutation (the decode's access shape).
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+__global__ void k_stream_read(const u32x4_t* p, size_t n16, unsigned* out) {
+  u32x4_t acc = {0u, 0u, 0u, 0u};
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    const u32x4_t a = __builtin_nontemporal_load(p + i);
+    const u32x4_t b = __builtin_nontemporal_load(p + i + stride);
+    const u32x4_t c = __builtin_nontemporal_load(p + i + 2 * stride);
+    const u32x4_t d = __builtin_nontemporal_load(p + i + 3 * stride);
+    acc ^= a ^ b ^ c ^ d;
+  }
+  for (; i < n16; i += stride) acc ^= __builtin_nontemporal_load(p + i);
+  out[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = acc.x ^ acc.y ^ acc.z ^ acc.w;
+}
+
+// Each wave reads whole chunks: wave k of the grid takes chunks k, k + waves, ...; chunk c
+// starts at order[c] * record_bytes.
+__global__ void k_chunk_read(const unsigned char* base, const unsigned* order, int n_chunks, int record_bytes,
+                             int chunk_bytes, unsigned* out) {
+  const int lane = threadIdx.x & 63;
+  const int wave = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  const int waves = (gridDim.x * blockDim.x) >> 6;
+  const int per = chunk_bytes / 16;
+  u32x4_t acc = {0u, 0u, 0u, 0u};
+  for (int c = wave; c < n_chunks; c += 4 * waves) {
+    u32x4_t v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int cc = c + u * waves;
+      v[u] = (u32x4_t){0u, 0u, 0u, 0u};
+      if (cc < n_chunks && lane < per)
+        v[u] = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4_t*>(base + (size_t)order[cc] * record_bytes) + lane);
+    }
+    acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+  }
+  out[blockIdx.x * blockDim.x + threadIdx.x] = acc.x ^ acc.y ^ acc.z ^ acc.w;
+}
+
 unsigned grid_for(size_t n) {
   size_t g = (n + 255) / 256;
   if (g > 65536) g = 65536;
@@ -87,6 +130,20 @@ int synth_kv_bf16(hipStream_t s, uint64_t seed, uint32_t stream, int B, int n_to
   const size_t n = (size_t)B * n_tok * H * D;
   if (n == 0) return 0;
   hipLaunchKernelGGL(k_kv, dim3(grid_for(n)), dim3(256), 0, s, seed, stream, B, n_tok, t0, t0s, T, H, D, factors, out);
+  return (int)hipGetLastError();
+}
+
+// Streaming read of n16 16-byte words; out: one word per thread of a grid of 256-thread blocks.
+int synth_stream_read(hipStream_t s, const void* p, size_t n16, int blocks, unsigned* out) {
+  hipLaunchKernelGGL(k_stream_read, dim3(blocks), dim3(256), 0, s, (const u32x4_t*)p, n16, out);
+  return (int)hipGetLastError();
+}
+
+// Chunk reads at permuted record starts (see k_chunk_read).
+int synth_chunk_read(hipStream_t s, const void* base, const unsigned* order, int n_chunks, int record_bytes,
+                     int chunk_bytes, int blocks, unsigned* out) {
+  hipLaunchKernelGGL(k_chunk_read, dim3(blocks), dim3(256), 0, s, (const unsigned char*)base, order, n_chunks,
+                     record_bytes, chunk_bytes, out);
   return (int)hipGetLastError();
 }
 

@@ -26,6 +26,10 @@ def lib():
         L.synth_kv_bf16.restype = ctypes.c_int
         L.synth_normal.argtypes = [vp, ctypes.c_uint64, ctypes.c_uint32, ctypes.c_uint64, ctypes.c_size_t, ctypes.c_int, vp]
         L.synth_normal.restype = ctypes.c_int
+        L.synth_stream_read.argtypes = [vp, vp, ctypes.c_size_t, ctypes.c_int, vp]
+        L.synth_stream_read.restype = ctypes.c_int
+        L.synth_chunk_read.argtypes = [vp, vp, vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp]
+        L.synth_chunk_read.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -54,3 +58,38 @@ def normal(seed: int, stream: int, offset: int, out: torch.Tensor):
     if r != 0:
         raise RuntimeError(f"synth_normal failed: {r}")
     return out
+
+
+def read_ceiling(n_bytes: int = 16 << 30, record_bytes: int = 2560, chunk_bytes: int = 768, reps: int = 3) -> dict:
+    """Practical HBM read rates on this device: a plain streaming read of ``n_bytes``, and
+    ``chunk_bytes`` reads at the starts of ``record_bytes`` records in a seeded random order
+    (the shape of the decode's per-block reads). Returns GB/s for both."""
+    buf = torch.empty(n_bytes, dtype=torch.uint8, device="cuda")
+    buf.fill_(1)
+    blocks = 256 * 32
+    out = torch.empty(blocks * 256, dtype=torch.int32, device="cuda")
+    L = lib()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    L.synth_stream_read(_s(), ctypes.c_void_p(buf.data_ptr()), n_bytes // 16, blocks, ctypes.c_void_p(out.data_ptr()))
+    ev0.record()
+    for _ in range(reps):
+        L.synth_stream_read(_s(), ctypes.c_void_p(buf.data_ptr()), n_bytes // 16, blocks, ctypes.c_void_p(out.data_ptr()))
+    ev1.record()
+    torch.cuda.synchronize()
+    stream_gbs = reps * n_bytes / (ev0.elapsed_time(ev1) * 1e-3) / 1e9
+    n_chunks = n_bytes // record_bytes
+    g = torch.Generator(device="cpu").manual_seed(0)
+    order = torch.randperm(n_chunks, generator=g).to(torch.int32).cuda()
+    L.synth_chunk_read(_s(), ctypes.c_void_p(buf.data_ptr()), ctypes.c_void_p(order.data_ptr()), n_chunks, record_bytes,
+                       chunk_bytes, blocks, ctypes.c_void_p(out.data_ptr()))
+    ev0.record()
+    for _ in range(reps):
+        L.synth_chunk_read(_s(), ctypes.c_void_p(buf.data_ptr()), ctypes.c_void_p(order.data_ptr()), n_chunks,
+                           record_bytes, chunk_bytes, blocks, ctypes.c_void_p(out.data_ptr()))
+    ev1.record()
+    torch.cuda.synchronize()
+    chunk_gbs = reps * n_chunks * chunk_bytes / (ev0.elapsed_time(ev1) * 1e-3) / 1e9
+    del buf
+    torch.cuda.empty_cache()
+    return {"stream_read_GBps": round(stream_gbs, 1), "record_chunk_read_GBps": round(chunk_gbs, 1),
+            "chunk_bytes": chunk_bytes, "record_bytes": record_bytes, "buffer_GB": n_bytes / 1e9}

@@ -151,20 +151,34 @@ __device__ inline uint4 ld_stream2(const void* p) {
 
 __device__ inline int sdot4(uint32_t a, uint32_t b, int c) { return __builtin_amdgcn_sdot4((int)a, (int)b, c, false); }
 __device__ inline uint32_t udot4(uint32_t a, uint32_t b, uint32_t c) { return __builtin_amdgcn_udot4(a, b, c, false); }
-// Byte j of each of four words, packed (byte k of the result from word k).
-__device__ inline uint32_t gather_byte(uint32_t v0, uint32_t v1, uint32_t v2, uint32_t v3, int j) {
-  const uint32_t sel = (uint32_t)j | ((uint32_t)(4 + j) << 8) | 0x0c0c0000u;
-  const uint32_t t01 = __builtin_amdgcn_perm(v1, v0, sel);
-  const uint32_t t23 = __builtin_amdgcn_perm(v3, v2, sel);
-  return __builtin_amdgcn_perm(t23, t01, 0x05040100u);
+// Bytes 0..2 of four words, transposed: limb j holds byte j of word k in its byte k.
+__device__ inline void transpose3(const uint32_t* u, uint32_t* limb) {
+  const uint32_t a = __builtin_amdgcn_perm(u[1], u[0], 0x05010400u);   // u0.b0 u1.b0 u0.b1 u1.b1
+  const uint32_t b = __builtin_amdgcn_perm(u[3], u[2], 0x05010400u);   // u2.b0 u3.b0 u2.b1 u3.b1
+  const uint32_t c = __builtin_amdgcn_perm(u[1], u[0], 0x07030602u);   // u0.b2 u1.b2 u0.b3 u1.b3
+  const uint32_t d = __builtin_amdgcn_perm(u[3], u[2], 0x07030602u);
+  limb[0] = __builtin_amdgcn_perm(b, a, 0x05040100u);
+  limb[1] = __builtin_amdgcn_perm(b, a, 0x07060302u);
+  limb[2] = __builtin_amdgcn_perm(d, c, 0x05040100u);
 }
-// Fixed-point scale for values of magnitude below vmax: 2^(22 - e) with vmax < 2^e, so
-// rint(v * scale) fits 23 bits; returns the scale and its inverse.
-__device__ inline void fixed_scale(float vmax, float& scl, float& inv) {
-  int e = __builtin_amdgcn_frexp_expf(vmax);
-  e = e < -100 ? -100 : e;
-  scl = __builtin_amdgcn_ldexpf(1.f, 22 - e);
-  inv = __builtin_amdgcn_ldexpf(1.f, e - 22);
+// Bytes 0..1 of four words, transposed.
+__device__ inline void transpose2(const uint32_t* u, uint32_t* limb) {
+  const uint32_t a = __builtin_amdgcn_perm(u[1], u[0], 0x05010400u);
+  const uint32_t b = __builtin_amdgcn_perm(u[3], u[2], 0x05010400u);
+  limb[0] = __builtin_amdgcn_perm(b, a, 0x05040100u);
+  limb[1] = __builtin_amdgcn_perm(b, a, 0x07060302u);
+}
+// Binary exponent e with |v| < 2^e for the largest magnitude v of a set (frexp), kept
+// above -100 so that 2^(bits - e) stays finite for tiny or zero sets.
+__device__ inline int set_exponent(float vmax) {
+  const int e = __builtin_amdgcn_frexp_expf(vmax);
+  return e < -100 ? -100 : e;
+}
+// Signed 22-bit fixed point with byte-limb bias: for |v| < 2^21, returns v + 0x808080
+// (three biased bytes). The add of 1.5 * 2^23 rounds v to the nearest integer (ties to
+// even) inside the fma and leaves it in the low mantissa bits.
+__device__ inline uint32_t biased_fixed22(float c, float scl) {
+  return __float_as_uint(fmaf(c, scl, 12582912.0f)) - (0x4B400000u - 0x808080u);
 }
 // Max over aligned groups of N lanes (same lane pattern as group_sum).
 template <int N>
@@ -176,6 +190,20 @@ __device__ inline float group_max(float v) {
   if (N >= 32) v = fmaxf(v, __shfl_xor(v, 16));
   if (N >= 64) v = fmaxf(v, __shfl_xor(v, 32));
   return v;
+}
+
+// Max over aligned groups of N lanes of non-negative floats, compared as unsigned bit
+// patterns (same order for values >= 0; fuses into DPP max instructions).
+template <int N>
+__device__ inline float group_max_nonneg(float x) {
+  uint32_t v = __float_as_uint(x);
+  if (N >= 2) v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));
+  if (N >= 4) v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));
+  if (N >= 8) v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));
+  if (N >= 16) v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));
+  if (N >= 32) v = max(v, (uint32_t)__shfl_xor((int)v, 16));
+  if (N >= 64) v = max(v, (uint32_t)__shfl_xor((int)v, 32));
+  return __uint_as_float(v);
 }
 
 // Codes at bit pair p of every byte of two words, each as four bytes: one 64-bit shift
@@ -289,8 +317,9 @@ struct KPass {
     return a;
   }
 
-  __device__ static inline void compute(const Row& r, const float* qs, float* scores, const uint32_t* selm,
-                                        float* scratch, int s, int lane, int w, const Buf& b, float& mloc) {
+  __device__ static inline void compute(const Row& r, const float* qs, const float* qreg, float* scores,
+                                        const uint32_t* selm, float* scratch, int s, int lane, int w, const Buf& b,
+                                        float& mloc) {
     const int gbase = (s * kWaves + w) * GPS;
     const int idx = lane * CPL;
     const int gsm = idx / D, pos0 = idx % D;
@@ -329,24 +358,39 @@ struct KPass {
       }
     } else {
       // positions 16w + 4p + k hold channel 16w + 4k + p; this lane: column w, bit pair p, k = 0..3
+      // (sigma q of those channels arrives hoisted in qreg)
       uint32_t* qlimb = reinterpret_cast<uint32_t*>(scratch);   // [GPS][COLS][4 p][3 limbs]
       const int cw = pos0 / 16, p = (pos0 >> 2) & 3;
       float f[4] = {0.f, 0.f, 0.f, 0.f};
       if (b.vm) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) f[k] = coef_of(w4(b.meta, k), qs[16 * cw + 4 * k + p], 1.f, cst);
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t mw = w4(b.meta, k);
+          f[k] = qreg[k] * f16lo(mw);                         // sigma q s
+          if (REFINE) {
+            cst = fmaf(-1.5f, f[k], cst);                     // sigma q s (lo - 3/2)
+          } else if (MODE == MODE_COARSE) {
+            cst = fmaf(qreg[k], f16hi(mw), cst);              // sigma q (z + s (4 hi + 3/2))
+            cst = fmaf(1.5f, f[k], cst);
+          } else {
+            cst = fmaf(qreg[k], f16hi(mw), cst);              // sigma q (z + s c)
+          }
+        }
       }
       float fm = fmaxf(fmaxf(fabsf(f[0]), fabsf(f[1])), fmaxf(fabsf(f[2]), fabsf(f[3])));
-      fm = group_max<LPG>(fm);
-      float scl;
-      fixed_scale(fm, scl, inv);
+      fm = group_max_nonneg<LPG>(fm);
+      const int ex = set_exponent(fm);
+      const float scl = __builtin_amdgcn_ldexpf(1.f, 21 - ex);
+      // high-plane-only codes carry weight 4 (code 4 hi): folded into the inverse scale
+      inv = __builtin_amdgcn_ldexpf(MODE == MODE_COARSE && !REFINE ? 4.f : 1.f, ex - 21);
       if (b.vm) {
-        uint32_t qb[4];
+        uint32_t u[4], limb[3];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) qb[k] = (uint32_t)(__float2int_rn(f[k] * scl) + 0x808080);
+        for (int k = 0; k < 4; ++k) u[k] = biased_fixed22(f[k], scl);
+        transpose3(u, limb);
         uint32_t* dst = qlimb + ((gsm * COLS + cw) * 4 + p) * 3;
 #pragma unroll
-        for (int j = 0; j < 3; ++j) dst[j] = gather_byte(qb[0], qb[1], qb[2], qb[3], j) ^ 0x80808080u;
+        for (int j = 0; j < 3; ++j) dst[j] = limb[j] ^ 0x80808080u;   // biased byte -> signed digit
       }
       cst = group_sum<LPG>(cst);
       wave_sync_lds();
@@ -384,26 +428,62 @@ struct KPass {
         }
       }
     }
+    if constexpr (KIVI) {
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) part[tt] = inv * group_sum<CPG>(part[tt]);
-    if (b.vc) {
-      const int g = gbase + gsub;
-      const uint32_t gm = REFINE ? selm[g] : 0u;
+      for (int tt = 0; tt < 4; ++tt) part[tt] = group_sum<CPG>(part[tt]);
+      if (b.vc) {
+        const int g = gbase + gsub;
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
-        if ((tt % CPG) == cp) {
-          const int ti = blk * kBlock + quad * 4 + tt;
-          const int t = g * kGroup + ti;
-          if (REFINE) {
-            if ((gm >> ti) & 1u) {
-              const float sc = scores[t] + cst + part[tt];
-              scores[t] = sc;
-              mloc = fmaxf(mloc, sc);
-            }
-          } else {
+        for (int tt = 0; tt < 4; ++tt) {
+          if ((tt % CPG) == cp) {
+            const int t = g * kGroup + blk * kBlock + quad * 4 + tt;
             const float sc = cst + part[tt];
             scores[t] = sc;
             mloc = fmaxf(mloc, sc);
+          }
+        }
+      }
+    } else {
+      // The CPG column-pair lanes of a token quad are consecutive: reduce-scatter their
+      // four partial scores so that lane cp ends with token cp (CPG = 4) or tokens cp and
+      // cp + 2 (CPG = 2).
+      const bool odd = cp & 1;
+      float k0 = odd ? part[1] : part[0], k1 = odd ? part[3] : part[2];
+      const float s0 = odd ? part[0] : part[1], s1 = odd ? part[2] : part[3];
+      k0 += dpp<0xB1>(s0);   // quad_perm [1,0,3,2]
+      k1 += dpp<0xB1>(s1);
+      float mine[2];
+      int nmine;
+      if (CPG == 4) {
+        const bool hi = cp & 2;
+        const float keep = hi ? k1 : k0, send = hi ? k0 : k1;
+        mine[0] = keep + dpp<0x4E>(send);   // quad_perm [2,3,0,1]
+        mine[1] = 0.f;
+        nmine = 1;
+      } else {
+        mine[0] = k0;
+        mine[1] = k1;
+        nmine = 2;
+      }
+      if (b.vc) {
+        const int g = gbase + gsub;
+        const uint32_t gm = REFINE ? selm[g] : 0u;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          if (i < nmine) {
+            const int ti = blk * kBlock + quad * 4 + (CPG == 4 ? cp : cp + 2 * i);
+            const int t = g * kGroup + ti;
+            if (REFINE) {
+              if ((gm >> ti) & 1u) {
+                const float sc = scores[t] + fmaf(inv, mine[i], cst);
+                scores[t] = sc;
+                mloc = fmaxf(mloc, sc);
+              }
+            } else {
+              const float sc = fmaf(inv, mine[i], cst);
+              scores[t] = sc;
+              mloc = fmaxf(mloc, sc);
+            }
           }
         }
       }
@@ -414,19 +494,26 @@ struct KPass {
   __device__ static void run(const Row& r, const float* qs, float* scores, const uint32_t* selm, float* scratch,
                              int lane, int w, float& mloc) {
     const int steps = (r.n_groups + kWaves * GPS - 1) / (kWaves * GPS);
+    // sigma q of the four channels whose coefficients this lane builds (fixed for the row)
+    float qreg[4];
+    {
+      const int pos0 = (lane * CPL) % D, cw = pos0 / 16, p = (pos0 >> 2) & 3;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) qreg[k] = KIVI ? 0.f : qs[16 * cw + 4 * k + p];
+    }
     // three buffers in rotation: the loads of steps s+1 and s+2 are in flight while step s computes
     Buf b0, b1, b2;
     load(r, selm, 0, lane, w, b0);
     if (1 < steps) load(r, selm, 1, lane, w, b1);
     for (int s = 0; s < steps; s += 3) {
       if (s + 2 < steps) load(r, selm, s + 2, lane, w, b2);
-      if (!REFINE || __any(b0.vm)) compute(r, qs, scores, selm, scratch, s, lane, w, b0, mloc);
+      if (!REFINE || __any(b0.vm)) compute(r, qs, qreg, scores, selm, scratch, s, lane, w, b0, mloc);
       if (s + 1 >= steps) break;
       if (s + 3 < steps) load(r, selm, s + 3, lane, w, b0);
-      if (!REFINE || __any(b1.vm)) compute(r, qs, scores, selm, scratch, s + 1, lane, w, b1, mloc);
+      if (!REFINE || __any(b1.vm)) compute(r, qs, qreg, scores, selm, scratch, s + 1, lane, w, b1, mloc);
       if (s + 2 >= steps) break;
       if (s + 4 < steps) load(r, selm, s + 4, lane, w, b1);
-      if (!REFINE || __any(b2.vm)) compute(r, qs, scores, selm, scratch, s + 2, lane, w, b2, mloc);
+      if (!REFINE || __any(b2.vm)) compute(r, qs, qreg, scores, selm, scratch, s + 2, lane, w, b2, mloc);
     }
   }
 };
@@ -531,34 +618,42 @@ struct VPass {
         }
       }
     } else {
-      uint32_t* vlimb = reinterpret_cast<uint32_t*>(scratch);   // [4][NE][4 p][3]
-      float* vinv = scratch + 4 * NE * 12;                      // [4][NE]
+      uint32_t* vlimb = reinterpret_cast<uint32_t*>(scratch);   // [4][NE][4 p][2]
+      float* vinv = scratch + 4 * NE * 8;                       // [4][NE]
       float am = fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3]));
       // max over the 4 bit-pair lanes of (block, group): lanes e + NE*p inside a 16-lane row
-      if (NE == 4) {
-        am = fmaxf(am, dpp<0x124>(am));   // row_ror:4
-        am = fmaxf(am, dpp<0x128>(am));   // row_ror:8
-      } else {
-        am = fmaxf(am, __shfl_xor(am, NE));
-        am = fmaxf(am, __shfl_xor(am, 2 * NE));
+      // (non-negative: compared as unsigned bit patterns)
+      {
+        uint32_t v = __float_as_uint(am);
+        if (NE == 4) {
+          v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x124, 0xF, 0xF, false));   // row_ror:4
+          v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xF, 0xF, false));   // row_ror:8
+        } else {
+          v = max(v, (uint32_t)__shfl_xor((int)v, NE));
+          v = max(v, (uint32_t)__shfl_xor((int)v, 2 * NE));
+        }
+        am = __uint_as_float(v);
       }
-      float scl, inv;
-      fixed_scale(am, scl, inv);
+      // unsigned 16-bit fixed point (weights are >= 0), rounded to nearest inside the fma
+      // with 2^23 added; the scale 2^(16-e) (1 - 2^-17) keeps the rounded value <= 65535
+      const int ex = set_exponent(am);
+      const float scl = __builtin_amdgcn_ldexpf(1.f - 0x1p-17f, 16 - ex);
       if (b.vm) {
-        uint32_t qb[4];
+        uint32_t qb[4], limb[2];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) qb[k] = (uint32_t)__float2uint_rn(a[k] * scl);
-        uint32_t* dst = vlimb + ((jbm * NE + e) * 4 + p) * 3;
-#pragma unroll
-        for (int jj = 0; jj < 3; ++jj) dst[jj] = gather_byte(qb[0], qb[1], qb[2], qb[3], jj);
-        if (p == 0) vinv[jbm * NE + e] = inv;
+        for (int k = 0; k < 4; ++k) qb[k] = __float_as_uint(fmaf(a[k], scl, 8388608.0f)) - 0x4B000000u;
+        transpose2(qb, limb);
+        uint32_t* dst = vlimb + ((jbm * NE + e) * 4 + p) * 2;
+        dst[0] = limb[0];
+        dst[1] = limb[1];
+        if (p == 0) vinv[jbm * NE + e] = __builtin_amdgcn_ldexpf(1.f + 0x1p-17f, ex - 16);   // 1 / scl
       }
       wave_sync_lds();
       if (b.v) {
-        uint32_t L[12];
-        const uint4* lp = reinterpret_cast<const uint4*>(vlimb + (jb * NE + e_lane) * 12);
+        uint32_t L[8];
+        const uint4* lp = reinterpret_cast<const uint4*>(vlimb + (jb * NE + e_lane) * 8);
 #pragma unroll
-        for (int u = 0; u < 3; ++u) {
+        for (int u = 0; u < 2; ++u) {
           const uint4 t = lp[u];
           L[4 * u] = t.x;
           L[4 * u + 1] = t.y;
@@ -605,13 +700,10 @@ struct VPass {
           for (int i = 0; i < 2; ++i) {
             uint32_t a = 0;
 #pragma unroll
-            for (int pp = 0; pp < 4; ++pp) a = udot4(L[3 * pp + 2], mc[i][pp], a);
+            for (int pp = 0; pp < 4; ++pp) a = udot4(L[2 * pp + 1], mc[i][pp], a);
             a <<= 8;
 #pragma unroll
-            for (int pp = 0; pp < 4; ++pp) a = udot4(L[3 * pp + 1], mc[i][pp], a);
-            a <<= 8;
-#pragma unroll
-            for (int pp = 0; pp < 4; ++pp) a = udot4(L[3 * pp], mc[i][pp], a);
+            for (int pp = 0; pp < 4; ++pp) a = udot4(L[2 * pp], mc[i][pp], a);
             acc[c + i] = fmaf(cscale, (float)a, acc[c + i]);
           }
         }

@@ -9,23 +9,28 @@
 //
 // One workgroup (8 wave64s) owns one row (cell, sequence, head); a whole plan is
 // one launch of cells x sequences x heads workgroups. The path is HBM-bound with
-// a VALU co-limit, so no MFMA: 2-bit codes are widened with in-place byte masks
-// and v_cvt_f32_ubyteN, every per-group / per-token scale is folded into the
-// coefficient that multiplies the code, and every wave keeps the loads of its
-// next step in flight while it computes the current one.
+// a VALU co-limit, so no MFMA: codes are widened with byte masks and multiplied by
+// fixed-point coefficients with v_dot4 integer dot products.
 //
-//   K pass   coarse scores s_t = sigma q . (z + s (4 hi + 3/2)) from the high plane
-//            (4-bit target); full scores for tau = 0 and KIVI-4; 2-bit scores for a
-//            2-bit target; the tail (last len mod 32 tokens) is exact bf16. Scores
-//            stay in LDS (4 bytes per token).
-//   stats    m = max s, l = sum exp(s - m) over the whole row.
-//   select   token t of the quantized prefix is selected when exp(s_t - m)/l >= tau;
-//            a ballot per 64 tokens gives one 32-bit mask per 32-token group.
-//   refine   only groups with a selected token: read their low K plane and add
-//            sigma q . s (lo - 3/2) to the selected scores.
-//   V pass   weights w_t = exp(s_t - m') with the final max m'; values
-//            z + s (4 hi + lo) for selected tokens (low V plane read only for blocks
-//            holding one), z + s (4 hi + 3/2) otherwise, exact on the tail.
+// Single streaming pass (split-K online softmax): each wave walks its share of the
+// row in steps of 32 or 64 tokens. A step reads, for every 16-token block it covers,
+// the K and V parts of the record that every token needs (one contiguous span of the
+// record), and computes
+//   K   scores s_t = sigma q . (z + s c) from the codes it read (4-bit target: high
+//       plane, c = 4 hi + 3/2; 2-bit target: c; tau = 0 or KIVI-4: the 4-bit code);
+//       the scores stay in LDS;
+//   max the wave's running maximum m; on a new maximum its accumulators are rescaled;
+//   V   weights w_t = exp(s_t - m) times the codes, accumulated per channel.
+// The last (len mod 32) tokens are exact bf16 and join the same online softmax.
+//
+// Selection (0 < tau <= 1, 4-bit target): after the pass the row's coarse maximum M
+// and sum L are known; token t of the quantized prefix is selected when
+// exp(s_t - M) / L >= tau. The groups holding a selected token are gathered (a ballot
+// over the per-group masks); their low K plane refines the selected scores, and the
+// selected tokens' contributions are corrected in place:
+//   w' (z + s (4 hi + lo)) - w (z + s (4 hi + 3/2)),  w, w' = exp(coarse, refined - m).
+// If the removed coarse weight exceeds 1024 times what the row keeps, the subtraction
+// could lose precision; the row's V is then recomputed from the final scores.
 #include <hip/hip_runtime.h>
 #include <hip/hip_fp16.h>
 #include <stdint.h>
@@ -34,12 +39,17 @@
 
 namespace lkv {
 
-constexpr int kWaves = 8;
+#ifndef LKV_WAVES
+#define LKV_WAVES 8
+#endif
+constexpr int kWaves = LKV_WAVES;           // waves per workgroup (one row)
 constexpr int kThreads = 64 * kWaves;
-constexpr int kWaveScratch = 256;   // floats of per-wave LDS scratch
+constexpr int kWavesPerSimd = kWaves / 2;   // two workgroups per CU (LDS-bound)
+constexpr int kWaveScratch = 256;   // words of per-wave LDS scratch
 
 enum : int { MODE_COARSE = 0, MODE_DENSE = 1, MODE_Q2 = 2, MODE_KIVI = 3 };
 
+// ----------------------------------------------------------------------------- helpers
 __device__ inline void wave_sync_lds() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
@@ -50,92 +60,80 @@ template <int CTRL>
 __device__ inline float dpp(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
 }
-// Sum over aligned groups of N lanes: quad swaps, then half-row and row mirrors, then shuffles.
+template <int CTRL>
+__device__ inline uint32_t dpp_u(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+// Cross-row exchanges without LDS (gfx950 permlane swaps): with both operands equal,
+// permlane16_swap returns rows (0,0,2,2) and (1,1,3,3); permlane32_swap returns rows
+// (0,1,0,1) and (2,3,2,3). Combining the pair reduces over row pairs / wave halves, with
+// the same operand order in every lane.
+__device__ inline float add_rows2(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ inline float add_halves(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ inline uint32_t max_rows2(uint32_t v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return max((uint32_t)r[0], (uint32_t)r[1]);
+}
+__device__ inline uint32_t max_halves(uint32_t v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return max((uint32_t)r[0], (uint32_t)r[1]);
+}
+
+// Sum over aligned groups of N lanes: quad swaps, half-row and row mirrors, then row pairs
+// and wave halves. Every lane of a group ends with the same value.
 template <int N>
 __device__ inline float group_sum(float v) {
   if (N >= 2) v += dpp<0xB1>(v);    // quad_perm [1,0,3,2]
   if (N >= 4) v += dpp<0x4E>(v);    // quad_perm [2,3,0,1]
   if (N >= 8) v += dpp<0x141>(v);   // row_half_mirror
   if (N >= 16) v += dpp<0x140>(v);  // row_mirror
-  if (N >= 32) v += __shfl_xor(v, 16);
-  if (N >= 64) v += __shfl_xor(v, 32);
+  if (N >= 32) v = add_rows2(v);
+  if (N >= 64) v = add_halves(v);
   return v;
 }
 __device__ inline float wave_sum(float v) { return group_sum<64>(v); }
-__device__ inline float wave_max(float v) {
-  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
-  return v;
+__device__ inline float uniform(float v) {
+  return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v)));
+}
+
+// Max over aligned groups of N lanes of non-negative floats, compared as unsigned bit
+// patterns (same order for values >= 0; fuses into DPP max instructions).
+template <int N>
+__device__ inline float group_max_nonneg(float x) {
+  uint32_t v = __float_as_uint(x);
+  if (N >= 2) v = max(v, dpp_u<0xB1>(v));
+  if (N >= 4) v = max(v, dpp_u<0x4E>(v));
+  if (N >= 8) v = max(v, dpp_u<0x141>(v));
+  if (N >= 16) v = max(v, dpp_u<0x140>(v));
+  if (N >= 32) v = max_rows2(v);
+  if (N >= 64) v = max_halves(v);
+  return __uint_as_float(v);
+}
+// Wave-uniform max of floats of any sign: order-preserving unsigned keys, row maxima by
+// DPP, then the four row maxima read into scalars.
+__device__ inline float wave_max(float x) {
+  const uint32_t u = __float_as_uint(x);
+  uint32_t k = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  k = max(k, dpp_u<0xB1>(k));
+  k = max(k, dpp_u<0x4E>(k));
+  k = max(k, dpp_u<0x141>(k));
+  k = max(k, dpp_u<0x140>(k));
+  const uint32_t m01 = max((uint32_t)__builtin_amdgcn_readlane((int)k, 0), (uint32_t)__builtin_amdgcn_readlane((int)k, 16));
+  const uint32_t m23 = max((uint32_t)__builtin_amdgcn_readlane((int)k, 32), (uint32_t)__builtin_amdgcn_readlane((int)k, 48));
+  const uint32_t m = max(m01, m23);
+  return __uint_as_float((m & 0x80000000u) ? (m & 0x7fffffffu) : ~m);
 }
 
 __device__ inline float f16lo(uint32_t w) { return __half2float(__ushort_as_half((unsigned short)(w & 0xffffu))); }
 __device__ inline float f16hi(uint32_t w) { return __half2float(__ushort_as_half((unsigned short)(w >> 16))); }
 __device__ inline float bf16f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
-__device__ inline float ubyte(uint32_t x, int k) { return (float)((x >> (8 * k)) & 0xffu); }
-// Byte masks the optimizer cannot see through (a scalar move it may hoist and reuse):
-// with a visible constant it merges the mask with the byte extraction into 2-bit
-// field extracts and loses v_cvt_f32_ubyte1..3 (one extra VALU op per code).
-template <uint32_t C>
-__device__ inline uint32_t smask() {
-  uint32_t m;
-  asm("s_mov_b32 %0, %1" : "=s"(m) : "i"(C));
-  return m;
-}
-template <int P>
-__device__ inline uint32_t mask2() { return smask<(0x03030303u << (2 * P))>(); }
-template <int N>
-__device__ inline uint32_t mask4() { return smask<(0x0F0F0F0Fu << (4 * N))>(); }
-
-// Sixteen 2-bit codes of one word. K order: cf[4k + p] for the code at byte k, bits 2p.
-template <int P>
-__device__ inline float dot4_k(uint32_t x, const float* cf, float acc) {
-  const uint32_t m = x & mask2<P>();
-#pragma unroll
-  for (int k = 0; k < 4; ++k) acc = fmaf(cf[4 * k + P], ubyte(m, k), acc);
-  return acc;
-}
-__device__ inline float dot16_k(uint32_t x, const float* cf, float acc) {
-  acc = dot4_k<0>(x, cf, acc);
-  acc = dot4_k<1>(x, cf, acc);
-  acc = dot4_k<2>(x, cf, acc);
-  return dot4_k<3>(x, cf, acc);
-}
-// V order: cf[4p + k] (token 4p + k of the block).
-template <int P>
-__device__ inline float dot4_v(uint32_t x, const float* cf, float acc) {
-  const uint32_t m = x & mask2<P>();
-#pragma unroll
-  for (int k = 0; k < 4; ++k) acc = fmaf(cf[4 * P + k], ubyte(m, k), acc);
-  return acc;
-}
-__device__ inline float dot16_v(uint32_t x, const float* cf, float acc) {
-  acc = dot4_v<0>(x, cf, acc);
-  acc = dot4_v<1>(x, cf, acc);
-  acc = dot4_v<2>(x, cf, acc);
-  return dot4_v<3>(x, cf, acc);
-}
-// Eight 4-bit codes of one word. K order (the K-meta position order): cf[4n + k] for
-// nibble n of byte k.
-template <int N>
-__device__ inline float dot4_k4(uint32_t x, const float* cf, float acc) {
-  const uint32_t m = x & mask4<N>();
-#pragma unroll
-  for (int k = 0; k < 4; ++k) acc = fmaf(cf[4 * N + k], ubyte(m, k), acc);
-  return acc;
-}
-__device__ inline float dot8_k4(uint32_t x, const float* cf, float acc) {
-  return dot4_k4<1>(x, cf, dot4_k4<0>(x, cf, acc));
-}
-// V order: cf[4n + k] (token 4n + k of the word's 8 tokens).
-template <int N>
-__device__ inline float dot4_v4(uint32_t x, const float* cf, float acc) {
-  const uint32_t m = x & mask4<N>();
-#pragma unroll
-  for (int k = 0; k < 4; ++k) acc = fmaf(cf[4 * N + k], ubyte(m, k), acc);
-  return acc;
-}
-__device__ inline float dot8_v4(uint32_t x, const float* cf, float acc) {
-  return dot4_v4<1>(x, cf, dot4_v4<0>(x, cf, acc));
-}
+__device__ inline uint32_t w4(const uint4& v, int i) { return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w; }
 
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
@@ -148,9 +146,17 @@ __device__ inline uint4 ld_stream2(const void* p) {
   const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
   return make_uint4(v.x, v.y, 0u, 0u);
 }
+__device__ inline uint4 ld_stream1(const void* p) {
+  return make_uint4(__builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p)), 0u, 0u, 0u);
+}
+template <int N>
+__device__ inline uint4 ld_words(const void* p) {
+  return N == 4 ? ld_stream4(p) : N == 2 ? ld_stream2(p) : ld_stream1(p);
+}
 
 __device__ inline int sdot4(uint32_t a, uint32_t b, int c) { return __builtin_amdgcn_sdot4((int)a, (int)b, c, false); }
 __device__ inline uint32_t udot4(uint32_t a, uint32_t b, uint32_t c) { return __builtin_amdgcn_udot4(a, b, c, false); }
+
 // Bytes 0..2 of four words, transposed: limb j holds byte j of word k in its byte k.
 __device__ inline void transpose3(const uint32_t* u, uint32_t* limb) {
   const uint32_t a = __builtin_amdgcn_perm(u[1], u[0], 0x05010400u);   // u0.b0 u1.b0 u0.b1 u1.b1
@@ -180,48 +186,11 @@ __device__ inline int set_exponent(float vmax) {
 __device__ inline uint32_t biased_fixed22(float c, float scl) {
   return __float_as_uint(fmaf(c, scl, 12582912.0f)) - (0x4B400000u - 0x808080u);
 }
-// Max over aligned groups of N lanes (same lane pattern as group_sum).
-template <int N>
-__device__ inline float group_max(float v) {
-  if (N >= 2) v = fmaxf(v, dpp<0xB1>(v));
-  if (N >= 4) v = fmaxf(v, dpp<0x4E>(v));
-  if (N >= 8) v = fmaxf(v, dpp<0x141>(v));
-  if (N >= 16) v = fmaxf(v, dpp<0x140>(v));
-  if (N >= 32) v = fmaxf(v, __shfl_xor(v, 16));
-  if (N >= 64) v = fmaxf(v, __shfl_xor(v, 32));
-  return v;
+// Unsigned 16-bit fixed point of a >= 0 with scale scl (a * scl <= 65535.5): rounded to
+// nearest inside the fma with 2^23 added.
+__device__ inline uint32_t fixed16(float a, float scl) {
+  return __float_as_uint(fmaf(a, scl, 8388608.0f)) - 0x4B000000u;
 }
-
-// Max over aligned groups of N lanes of non-negative floats, compared as unsigned bit
-// patterns (same order for values >= 0; fuses into DPP max instructions).
-template <int N>
-__device__ inline float group_max_nonneg(float x) {
-  uint32_t v = __float_as_uint(x);
-  if (N >= 2) v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));
-  if (N >= 4) v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));
-  if (N >= 8) v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));
-  if (N >= 16) v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));
-  if (N >= 32) v = max(v, (uint32_t)__shfl_xor((int)v, 16));
-  if (N >= 64) v = max(v, (uint32_t)__shfl_xor((int)v, 32));
-  return __uint_as_float(v);
-}
-
-// Codes at bit pair p of every byte of two words, each as four bytes: one 64-bit shift
-// serves both words (bits pulled in from the upper word land above bit 25 and are
-// masked off).
-__device__ inline void bitpairs2(uint32_t x0, uint32_t x1, uint32_t* m0, uint32_t* m1) {
-  const uint64_t X = ((uint64_t)x1 << 32) | x0;
-  m0[0] = x0 & 0x03030303u;
-  m1[0] = x1 & 0x03030303u;
-#pragma unroll
-  for (int p = 1; p < 4; ++p) {
-    const uint64_t Y = X >> (2 * p);
-    m0[p] = (uint32_t)Y & 0x03030303u;
-    m1[p] = (uint32_t)(Y >> 32) & 0x03030303u;
-  }
-}
-
-__device__ inline uint32_t w4(const uint4& v, int i) { return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w; }
 
 struct Row {
   const uint8_t* pool;     // pool base of the storage cell
@@ -231,640 +200,784 @@ struct Row {
   __device__ inline const uint8_t* rec_ptr(int j) const { return pool + ((uint64_t)boff[j] << 8); }
 };
 
-// ----------------------------------------------------------------------------- K pass
-// Lane mapping per wave step: GPS groups, each covered by LPG lanes = 2 blocks x 4
-// token quads x CPG column pairs (a column is one 32-bit word of UNIT channels). A
-// lane reads 4 consecutive tokens of two adjacent columns (two 16-byte loads) and
-// keeps 4 partial scores, summed over the CPG column-pair lanes with quad DPP. The
-// coefficients of a group are built by its LPG lanes (CPL consecutive K-meta
-// positions each) and passed through LDS.
-//
-// 2-bit planes use integer dot products: the group's coefficients become 23-bit
-// fixed point (scale 2^(22-e) from the group maximum) split into three signed byte
-// limbs; v_dot4_i32_i8 multiplies the four codes at one bit pair of a word's bytes by
-// four limbs, and the limb sums are recombined exactly in one register
-// ((l2 << 8) + l1) << 8 + l0. KIVI-4 words (4-bit codes) stay on the fp32 path.
-template <int D, int MODE, bool REFINE>
-struct KPass {
+// Per-wave state of the online softmax. acc: this lane's V channels; accz: constant
+// (zero-point / bucket-midpoint) terms of channel group lane % NE on the weight lanes;
+// lsum: weights of the tokens this lane owns (tail tokens: lane 0); m: the reference.
+template <int VCH>
+struct Acc {
+  float acc[VCH];
+  float accz, lsum, m;
+  __device__ inline void zero() {
+#pragma unroll
+    for (int c = 0; c < VCH; ++c) acc[c] = 0.f;
+    accz = lsum = 0.f;
+    m = -INFINITY;
+  }
+  // Move the reference up to mnew (wave-uniform, mnew > m); returns the factor applied.
+  __device__ inline float raise(float mnew) {
+    const float f = __expf(m - mnew);
+#pragma unroll
+    for (int c = 0; c < VCH; ++c) acc[c] *= f;
+    accz *= f;
+    lsum *= f;
+    m = mnew;
+    return f;
+  }
+};
+
+// ----------------------------------------------------------------------------- step geometry
+// A step covers TPS tokens: 64, or 32 for 4-bit codes at D = 128, so that every lane reads
+// 32 bytes of K codes and 32 bytes of V codes (16 for 2-bit codes at D = 64).
+template <int D, int MODE>
+struct Geo {
   static constexpr bool KIVI = MODE == MODE_KIVI;
-  static constexpr bool DENSE = MODE == MODE_DENSE && !REFINE;
+  static constexpr bool DENSE = MODE == MODE_DENSE;
+  static constexpr int TPS = (KIVI || DENSE) && D == 128 ? 32 : 64;
+  static constexpr int GPS = TPS / kGroup;      // groups per step
+  static constexpr int BPS = TPS / kBlock;      // blocks per step
+  // K: a group is covered by LPG lanes = 2 blocks x 4 token quads x CPG column lanes;
+  // a column is one 32-bit word of UNIT channels, NC columns per lane.
   static constexpr int UNIT = KIVI ? 8 : 16;
   static constexpr int COLS = D / UNIT;
-  static constexpr int CPG = COLS / 2;
-  static constexpr int LPG = 8 * CPG;
-  static constexpr int GPS = 64 / LPG;
-  static constexpr int CPL = UNIT / 4;
+  static constexpr int LPG = 64 / GPS;
+  static constexpr int CPG = LPG / 8;
+  static constexpr int NC = COLS / CPG;
+  static constexpr int CPL = GPS * D / 64;      // K-meta positions per lane
+  static constexpr int SPC = KIVI ? 2 : 4;      // limb sets (4 channels each) per column
   static constexpr int KMETA = KIVI ? off_kmeta_kivi(D) : off_kmeta_planes(D);
+  // V: LPB lanes per block, VCH channels per lane; weight lanes (block, bit pair, group).
+  static constexpr int LPB = 64 / BPS;
+  static constexpr int VCH = D / LPB;
+  static constexpr int NE = D / kGroup;
+  static constexpr int COOP = BPS * 4 * NE;
+  static constexpr int VW = KIVI ? 2 * VCH : VCH;   // code words per lane (high plane or KIVI-4)
+  static constexpr int NV4 = VW / 4;
+  static constexpr int VOFF = KIVI ? off_v_kivi(D) : off_v_planes(D);
+  static constexpr int VMETA = KIVI ? off_vmeta_kivi(D) : off_vmeta_planes(D);
+  // Token t_loc of a step is owned by lane t_loc and a weight lane's four tokens are its own
+  // quad: the weights reach the weight lanes by quad broadcasts (D = 128, 2-bit codes).
+  static constexpr bool QUAD_W = CPG == 4 && LPG == 32 && NE == 4;
+  // per-wave scratch (words): K limbs at 0; step weights at 0 once the K limbs are
+  // consumed; V limbs and their inverse scales from 64.
+  static constexpr int S_W = 0, S_VL = 64, S_VI = 64 + BPS * NE * 8;
+  static_assert(NC >= 1 && VW % 4 == 0 && COOP <= 64, "geometry");
+  static_assert(GPS * (D / 4) * 3 <= kWaveScratch && S_VI + BPS * NE <= kWaveScratch && TPS <= S_VL, "scratch");
+};
+
+// ----------------------------------------------------------------------------- K step
+// Coefficients: the lanes of a group build the fixed-point coefficients of its D channels
+// (CPL consecutive K-meta positions each; four consecutive positions form one limb set:
+// the four channels a code word holds at one bit pair or nibble). They become 22-bit fixed
+// point (scale 2^(21-e) from the group maximum) in three signed byte limbs; v_dot4_i32_i8
+// multiplies four codes by four limbs and the limb sums recombine exactly in one register,
+// ((l2 << 8) + l1) << 8 + l0. REFINE reads the low plane of a 4-bit cell with coefficients
+// sigma q s and the constant -3/2 sigma q . s (from the bucket midpoint to lo).
+template <int D, int MODE, bool REFINE>
+struct KStep {
+  using G = Geo<D, MODE>;
   static constexpr int CODE_OFF = REFINE ? off_klo(D) : 0;
 
   struct Buf {
-    uint4 meta, c0, c1, l0, l1;
-    bool vm, vc;
+    uint4 meta, c[G::NC], l[G::DENSE ? G::NC : 1];
   };
 
-  __device__ static inline void lane_role(int lane, int& blk, int& quad, int& cp) {
-    const int rl = lane % LPG;
-    blk = rl / (4 * CPG);
-    quad = (rl / CPG) % 4;
-    cp = rl % CPG;
+  __device__ static inline void role(int lane, int& gsub, int& blk, int& quad, int& cp) {
+    const int rl = lane % G::LPG;
+    gsub = lane / G::LPG;
+    blk = rl / (4 * G::CPG);
+    quad = (rl / G::CPG) % 4;
+    cp = rl % G::CPG;
   }
 
-  __device__ static inline void load(const Row& r, const uint32_t* selm, int s, int lane, int w, Buf& b) {
-    const int gbase = (s * kWaves + w) * GPS;
-    const int idx = lane * CPL;
-    const int gm = gbase + idx / D, pos = idx % D;
-    b.vm = gm < r.n_groups && (!REFINE || selm[gm] != 0u);
-    if (b.vm) {
-      const uint8_t* p = r.rec_ptr(2 * gm + (pos >= D / 2)) + KMETA + 4 * (pos % (D / 2));
-      b.meta = CPL == 4 ? ld_stream4(p) : ld_stream2(p);
-    }
-    int blk, quad, cp;
-    lane_role(lane, blk, quad, cp);
-    const int gc = gbase + lane / LPG;
-    b.vc = gc < r.n_groups && (!REFINE || selm[gc] != 0u);
-    if (b.vc) {
-      const uint8_t* kp = r.rec_ptr(2 * gc + blk) + CODE_OFF + (2 * cp * kBlock + 4 * quad) * 4;
-      b.c0 = ld_stream4(kp);                 // column 2cp, tokens 4quad..4quad+3
-      b.c1 = ld_stream4(kp + kBlock * 4);    // column 2cp+1
-      if (DENSE) {
-        b.l0 = ld_stream4(kp + off_klo(D));
-        b.l1 = ld_stream4(kp + off_klo(D) + kBlock * 4);
-      }
+  // groups: the group read by each of the step's GPS slots (an empty slot repeats a valid
+  // group of the step, so every load is in bounds and the kernel needs no per-lane branch).
+  __device__ static inline void load(const Row& r, const int* groups, int lane, Buf& b) {
+    int gsub, blk, quad, cp;
+    role(lane, gsub, blk, quad, cp);
+    const int g = groups[gsub];
+    const int pos0 = (lane % G::LPG) * G::CPL;
+    b.meta = ld_words<G::CPL>(r.rec_ptr(2 * g + (pos0 >= D / 2)) + G::KMETA + 4 * (pos0 % (D / 2)));
+    const uint8_t* kp = r.rec_ptr(2 * g + blk) + CODE_OFF + ((cp * G::NC) * kBlock + 4 * quad) * 4;
+#pragma unroll
+    for (int i = 0; i < G::NC; ++i) b.c[i] = ld_stream4(kp + i * kBlock * 4);
+    if (G::DENSE) {
+#pragma unroll
+      for (int i = 0; i < G::NC; ++i) b.l[i] = ld_stream4(kp + off_klo(D) + i * kBlock * 4);
     }
   }
 
-  // Coefficient of the channel at one K-meta position and its share of the constant term.
-  __device__ static inline float coef_of(uint32_t mw, float qv, float pre, float& cst) {
-    const float sc = f16lo(mw), z = f16hi(mw);
-    const float qsv = qv * sc;
-    if (REFINE) {
-      cst = fmaf(-1.5f, qsv, cst);           // sigma q . s (lo - 3/2)
-      return qsv * pre;
-    } else if (MODE == MODE_COARSE) {
-      cst += qv * fmaf(1.5f, sc, z);         // sigma q . (z + s (4 hi + 3/2))
-      return 4.f * qsv * pre;
+  // sigma q of the channels at this lane's K-meta positions (fixed for the row).
+  __device__ static inline void qregs(const float* qs, int lane, float* qreg) {
+    const int pos0 = (lane % G::LPG) * G::CPL;
+#pragma unroll
+    for (int k = 0; k < G::CPL; ++k) {
+      const int pos = pos0 + k;
+      // 2-bit: position 16w + 4p + k holds channel 16w + 4k + p; 4-bit: 8w + 4n + k holds 8w + 2k + n
+      const int ch = G::KIVI ? 8 * (pos / 8) + 2 * (pos % 4) + (pos / 4) % 2
+                             : 16 * (pos / 16) + 4 * (pos % 4) + (pos / 4) % 4;
+      qreg[k] = qs[ch];
+    }
+  }
+
+  // Masked words of one code word (and its low-plane word for DENSE): the four codes of
+  // one limb set each, one code per byte.
+  __device__ static inline void masked(uint32_t x, uint32_t y, uint32_t* m) {
+    if constexpr (G::KIVI) {
+      m[0] = x & 0x0F0F0F0Fu;
+      m[1] = (x >> 4) & 0x0F0F0F0Fu;
     } else {
-      cst = fmaf(qv, z, cst);                // sigma q . (z + s c), c 2-bit / 4-bit
-      return qsv * pre;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        m[p] = (x >> (2 * p)) & 0x03030303u;
+        if (G::DENSE) m[p] = (m[p] << 2) | ((y >> (2 * p)) & 0x03030303u);
+      }
     }
   }
 
-  // One limb's contribution of a word's 16 channels: codes m[p] (four channels at bit pair p)
-  // times the limb bytes of those channels, accumulated into a.
-  __device__ static inline int word_dot(const uint32_t* L, const uint32_t* m, int limb, int a) {
+  // The step's scores. Every token t_loc of the step has one owner lane (own), which
+  // receives sigma q . k_t (REFINE: the correction to it).
+  __device__ static inline float compute(const float* qreg, uint32_t* klimb, int lane, const Buf& b, bool& own,
+                                         int& t_loc) {
+    int gsub, blk, quad, cp;
+    role(lane, gsub, blk, quad, cp);
+    const int pos0 = (lane % G::LPG) * G::CPL;
+    float f[G::CPL];
+    float cst = 0.f;
 #pragma unroll
-    for (int pp = 0; pp < 4; ++pp) a = sdot4(L[3 * pp + limb], m[pp], a);
-    return a;
-  }
-
-  __device__ static inline void compute(const Row& r, const float* qs, const float* qreg, float* scores,
-                                        const uint32_t* selm, float* scratch, int s, int lane, int w, const Buf& b,
-                                        float& mloc) {
-    const int gbase = (s * kWaves + w) * GPS;
-    const int idx = lane * CPL;
-    const int gsm = idx / D, pos0 = idx % D;
-    const int gsub = lane / LPG;
-    int blk, quad, cp;
-    lane_role(lane, blk, quad, cp);
-    float part[4] = {0.f, 0.f, 0.f, 0.f};
-    float cst = 0.f, inv = 1.f;
-
-    if constexpr (KIVI) {
-      // positions 8w + 4n + k hold channel 8w + 2k + n; this lane: n fixed, k and k+1
-      float* coef = scratch;   // [GPS][D] in position order
-      if (b.vm) {
-        const int cw = pos0 / 8, r8 = pos0 % 8, n = r8 / 4, k0 = r8 % 4;
-        const float pre = n ? 1.f / 16.f : 1.f;
-        const float c0 = coef_of(b.meta.x, qs[8 * cw + 2 * k0 + n], pre, cst);
-        const float c1 = coef_of(b.meta.y, qs[8 * cw + 2 * (k0 + 1) + n], pre, cst);
-        *reinterpret_cast<float2*>(coef + gsm * D + pos0) = make_float2(c0, c1);
+    for (int k = 0; k < G::CPL; ++k) {
+      const uint32_t mw = w4(b.meta, k);
+      f[k] = fmaf(qreg[k], f16lo(mw), -0.f);               // sigma q s
+      if (REFINE) {
+        cst = fmaf(-1.5f, f[k], cst);                     // sigma q s (lo - 3/2)
+      } else if (MODE == MODE_COARSE) {
+        cst = fmaf(qreg[k], f16hi(mw), cst);              // sigma q (z + s (4 hi + 3/2))
+        cst = fmaf(1.5f, f[k], cst);
+      } else {
+        cst = fmaf(qreg[k], f16hi(mw), cst);              // sigma q (z + s c)
       }
-      cst = group_sum<LPG>(cst);
-      wave_sync_lds();
-      if (b.vc) {
-        float cf[2 * UNIT];
-        const float4* cq = reinterpret_cast<const float4*>(coef + gsub * D + 2 * cp * UNIT);
+    }
+    float fm = fabsf(f[0]);
 #pragma unroll
-        for (int u = 0; u < UNIT / 2; ++u) {
-          const float4 t = cq[u];
-          cf[4 * u] = t.x;
-          cf[4 * u + 1] = t.y;
-          cf[4 * u + 2] = t.z;
-          cf[4 * u + 3] = t.w;
+    for (int k = 1; k < G::CPL; ++k) fm = fmaxf(fm, fabsf(f[k]));
+    // group max of |f| and group sum of the constant, interleaved
+    {
+      uint32_t v = __float_as_uint(fm);
+      v = max(v, dpp_u<0xB1>(v));
+      cst += dpp<0xB1>(cst);
+      v = max(v, dpp_u<0x4E>(v));
+      cst += dpp<0x4E>(cst);
+      v = max(v, dpp_u<0x141>(v));
+      cst += dpp<0x141>(cst);
+      v = max(v, dpp_u<0x140>(v));
+      cst += dpp<0x140>(cst);
+      v = max_rows2(v);
+      cst = add_rows2(cst);
+      if (G::LPG == 64) {
+        v = max_halves(v);
+        cst = add_halves(cst);
+      }
+      fm = __uint_as_float(v);
+    }
+    static_assert(G::LPG >= 32, "group lanes");
+    const int ex = set_exponent(fm);
+    const float scl = __builtin_amdgcn_ldexpf(1.f, 21 - ex);
+    // high-plane-only codes carry weight 4 (code 4 hi): folded into the inverse scale
+    const float inv = __builtin_amdgcn_ldexpf(MODE == MODE_COARSE && !REFINE ? 4.f : 1.f, ex - 21);
+    uint32_t mine[G::CPL];
+#pragma unroll
+    for (int k = 0; k < G::CPL; ++k) mine[k] = biased_fixed22(f[k], scl);
+    // the four values of this lane's limb set (held by 4 / CPL consecutive lanes)
+    uint32_t u[4];
+    if constexpr (G::CPL == 4) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) u[k] = mine[k];
+    } else if constexpr (G::CPL == 2) {
+      const uint32_t o0 = dpp_u<0xB1>(mine[0]), o1 = dpp_u<0xB1>(mine[1]);
+      const bool odd = lane & 1;
+      u[0] = odd ? o0 : mine[0];
+      u[1] = odd ? o1 : mine[1];
+      u[2] = odd ? mine[0] : o0;
+      u[3] = odd ? mine[1] : o1;
+    } else {
+      u[0] = dpp_u<0x00>(mine[0]);   // quad_perm [0,0,0,0]
+      u[1] = dpp_u<0x55>(mine[0]);   // quad_perm [1,1,1,1]
+      u[2] = dpp_u<0xAA>(mine[0]);
+      u[3] = dpp_u<0xFF>(mine[0]);
+    }
+    if ((lane % (4 / G::CPL)) == 0) {
+      uint32_t limb[3];
+      transpose3(u, limb);
+      uint32_t* dst = klimb + (gsub * (D / 4) + pos0 / 4) * 3;
+#pragma unroll
+      for (int j = 0; j < 3; ++j) dst[j] = limb[j] ^ 0x80808080u;   // biased byte -> signed digit
+    }
+    wave_sync_lds();
+    // Limbs of this lane's NC columns (SPC sets x 3 words each); the four tokens' chains run
+    // interleaved, limb 2 first. With registers to spare (2 waves per SIMD) one chain per
+    // token covers all columns; otherwise one column at a time, each recombined exactly.
+    constexpr bool ONE_CHAIN = kWavesPerSimd <= 2;
+    constexpr int NCC = ONE_CHAIN ? G::NC : 1;   // columns per chain
+    constexpr int CW = NCC * G::SPC * 3;
+    int acc4[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int i0 = 0; i0 < G::NC; i0 += NCC) {
+      uint32_t L[CW];
+      const uint32_t* src = klimb + (gsub * (D / 4) + (cp * G::NC + i0) * G::SPC) * 3;
+      if constexpr (CW % 4 == 0) {
+#pragma unroll
+        for (int u4 = 0; u4 < CW / 4; ++u4) {
+          const uint4 t = reinterpret_cast<const uint4*>(src)[u4];
+          L[4 * u4] = t.x;
+          L[4 * u4 + 1] = t.y;
+          L[4 * u4 + 2] = t.z;
+          L[4 * u4 + 3] = t.w;
+        }
+      } else {
+#pragma unroll
+        for (int u2 = 0; u2 < CW / 2; ++u2) {
+          const uint2 t = reinterpret_cast<const uint2*>(src)[u2];
+          L[2 * u2] = t.x;
+          L[2 * u2 + 1] = t.y;
+        }
+      }
+      uint32_t m[4][NCC][G::SPC];
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int i = 0; i < NCC; ++i)
+          masked(w4(b.c[i0 + i], tt), G::DENSE ? w4(b.l[i0 + i], tt) : 0u, m[tt][i]);
+      int a[4] = {0, 0, 0, 0};
+#pragma unroll
+      for (int j = 2; j >= 0; --j) {
+        if (j < 2) {
+#pragma unroll
+          for (int tt = 0; tt < 4; ++tt) a[tt] <<= 8;
         }
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt)
-          part[tt] = dot8_k4(w4(b.c1, tt), cf + UNIT, dot8_k4(w4(b.c0, tt), cf, 0.f));
+#pragma unroll
+          for (int i = 0; i < NCC; ++i)
+#pragma unroll
+            for (int s = 0; s < G::SPC; ++s) a[tt] = sdot4(L[(i * G::SPC + s) * 3 + j], m[tt][i][s], a[tt]);
       }
-    } else {
-      // positions 16w + 4p + k hold channel 16w + 4k + p; this lane: column w, bit pair p, k = 0..3
-      // (sigma q of those channels arrives hoisted in qreg)
-      uint32_t* qlimb = reinterpret_cast<uint32_t*>(scratch);   // [GPS][COLS][4 p][3 limbs]
-      const int cw = pos0 / 16, p = (pos0 >> 2) & 3;
-      float f[4] = {0.f, 0.f, 0.f, 0.f};
-      if (b.vm) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const uint32_t mw = w4(b.meta, k);
-          f[k] = qreg[k] * f16lo(mw);                         // sigma q s
-          if (REFINE) {
-            cst = fmaf(-1.5f, f[k], cst);                     // sigma q s (lo - 3/2)
-          } else if (MODE == MODE_COARSE) {
-            cst = fmaf(qreg[k], f16hi(mw), cst);              // sigma q (z + s (4 hi + 3/2))
-            cst = fmaf(1.5f, f[k], cst);
-          } else {
-            cst = fmaf(qreg[k], f16hi(mw), cst);              // sigma q (z + s c)
-          }
-        }
-      }
-      float fm = fmaxf(fmaxf(fabsf(f[0]), fabsf(f[1])), fmaxf(fabsf(f[2]), fabsf(f[3])));
-      fm = group_max_nonneg<LPG>(fm);
-      const int ex = set_exponent(fm);
-      const float scl = __builtin_amdgcn_ldexpf(1.f, 21 - ex);
-      // high-plane-only codes carry weight 4 (code 4 hi): folded into the inverse scale
-      inv = __builtin_amdgcn_ldexpf(MODE == MODE_COARSE && !REFINE ? 4.f : 1.f, ex - 21);
-      if (b.vm) {
-        uint32_t u[4], limb[3];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) u[k] = biased_fixed22(f[k], scl);
-        transpose3(u, limb);
-        uint32_t* dst = qlimb + ((gsm * COLS + cw) * 4 + p) * 3;
-#pragma unroll
-        for (int j = 0; j < 3; ++j) dst[j] = limb[j] ^ 0x80808080u;   // biased byte -> signed digit
-      }
-      cst = group_sum<LPG>(cst);
-      wave_sync_lds();
-      if (b.vc) {
-        uint32_t L[24];   // limbs of columns 2cp and 2cp+1: [col][p][limb]
-        const uint4* lq = reinterpret_cast<const uint4*>(qlimb + (gsub * COLS + 2 * cp) * 12);
-#pragma unroll
-        for (int u = 0; u < 6; ++u) {
-          const uint4 t = lq[u];
-          L[4 * u] = t.x;
-          L[4 * u + 1] = t.y;
-          L[4 * u + 2] = t.z;
-          L[4 * u + 3] = t.w;
-        }
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-          uint32_t m0[4], m1[4];
-          bitpairs2(w4(b.c0, tt), w4(b.c1, tt), m0, m1);
-          if (DENSE) {   // 4-bit codes 4 hi + lo
-            uint32_t n0[4], n1[4];
-            bitpairs2(w4(b.l0, tt), w4(b.l1, tt), n0, n1);
-#pragma unroll
-            for (int pp = 0; pp < 4; ++pp) {
-              m0[pp] = (m0[pp] << 2) | n0[pp];
-              m1[pp] = (m1[pp] << 2) | n1[pp];
-            }
-          }
-          int a = word_dot(L, m0, 2, 0);
-          a = word_dot(L + 12, m1, 2, a);
-          a = word_dot(L, m0, 1, a << 8);
-          a = word_dot(L + 12, m1, 1, a);
-          a = word_dot(L, m0, 0, a << 8);
-          a = word_dot(L + 12, m1, 0, a);
-          part[tt] = (float)a;
-        }
-      }
+      for (int tt = 0; tt < 4; ++tt) acc4[tt] = i0 == 0 ? a[tt] : acc4[tt] + a[tt];
     }
-    if constexpr (KIVI) {
+    float part[4];
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt) part[tt] = group_sum<CPG>(part[tt]);
-      if (b.vc) {
-        const int g = gbase + gsub;
+    for (int tt = 0; tt < 4; ++tt) part[tt] = (float)acc4[tt];
+    // Reduce-scatter over the CPG column lanes of a token quad (consecutive lanes): the lane
+    // with in-quad index q ends with token q (CPG = 8: pairs i, 7 - i first; lanes 0..3 own).
+    if (G::CPG == 8) {
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-          if ((tt % CPG) == cp) {
-            const int t = g * kGroup + blk * kBlock + quad * 4 + tt;
-            const float sc = cst + part[tt];
-            scores[t] = sc;
-            mloc = fmaxf(mloc, sc);
-          }
-        }
-      }
-    } else {
-      // The CPG column-pair lanes of a token quad are consecutive: reduce-scatter their
-      // four partial scores so that lane cp ends with token cp (CPG = 4) or tokens cp and
-      // cp + 2 (CPG = 2).
-      const bool odd = cp & 1;
-      float k0 = odd ? part[1] : part[0], k1 = odd ? part[3] : part[2];
-      const float s0 = odd ? part[0] : part[1], s1 = odd ? part[2] : part[3];
-      k0 += dpp<0xB1>(s0);   // quad_perm [1,0,3,2]
-      k1 += dpp<0xB1>(s1);
-      float mine[2];
-      int nmine;
-      if (CPG == 4) {
-        const bool hi = cp & 2;
-        const float keep = hi ? k1 : k0, send = hi ? k0 : k1;
-        mine[0] = keep + dpp<0x4E>(send);   // quad_perm [2,3,0,1]
-        mine[1] = 0.f;
-        nmine = 1;
-      } else {
-        mine[0] = k0;
-        mine[1] = k1;
-        nmine = 2;
-      }
-      if (b.vc) {
-        const int g = gbase + gsub;
-        const uint32_t gm = REFINE ? selm[g] : 0u;
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          if (i < nmine) {
-            const int ti = blk * kBlock + quad * 4 + (CPG == 4 ? cp : cp + 2 * i);
-            const int t = g * kGroup + ti;
-            if (REFINE) {
-              if ((gm >> ti) & 1u) {
-                const float sc = scores[t] + fmaf(inv, mine[i], cst);
-                scores[t] = sc;
-                mloc = fmaxf(mloc, sc);
-              }
-            } else {
-              const float sc = fmaf(inv, mine[i], cst);
-              scores[t] = sc;
-              mloc = fmaxf(mloc, sc);
-            }
-          }
-        }
-      }
+      for (int tt = 0; tt < 4; ++tt) part[tt] += dpp<0x141>(part[tt]);   // row_half_mirror
     }
-    wave_sync_lds();
-  }
-
-  __device__ static void run(const Row& r, const float* qs, float* scores, const uint32_t* selm, float* scratch,
-                             int lane, int w, float& mloc) {
-    const int steps = (r.n_groups + kWaves * GPS - 1) / (kWaves * GPS);
-    // sigma q of the four channels whose coefficients this lane builds (fixed for the row)
-    float qreg[4];
-    {
-      const int pos0 = (lane * CPL) % D, cw = pos0 / 16, p = (pos0 >> 2) & 3;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) qreg[k] = KIVI ? 0.f : qs[16 * cw + 4 * k + p];
-    }
-    // three buffers in rotation: the loads of steps s+1 and s+2 are in flight while step s computes
-    Buf b0, b1, b2;
-    load(r, selm, 0, lane, w, b0);
-    if (1 < steps) load(r, selm, 1, lane, w, b1);
-    for (int s = 0; s < steps; s += 3) {
-      if (s + 2 < steps) load(r, selm, s + 2, lane, w, b2);
-      if (!REFINE || __any(b0.vm)) compute(r, qs, qreg, scores, selm, scratch, s, lane, w, b0, mloc);
-      if (s + 1 >= steps) break;
-      if (s + 3 < steps) load(r, selm, s + 3, lane, w, b0);
-      if (!REFINE || __any(b1.vm)) compute(r, qs, qreg, scores, selm, scratch, s + 1, lane, w, b1, mloc);
-      if (s + 2 >= steps) break;
-      if (s + 4 < steps) load(r, selm, s + 4, lane, w, b1);
-      if (!REFINE || __any(b2.vm)) compute(r, qs, qreg, scores, selm, scratch, s + 2, lane, w, b2, mloc);
-    }
+    const bool odd = cp & 1, hi = cp & 2;
+    float k0 = odd ? part[1] : part[0], k1 = odd ? part[3] : part[2];
+    const float s0 = odd ? part[0] : part[1], s1 = odd ? part[2] : part[3];
+    k0 += dpp<0xB1>(s0);   // quad_perm [1,0,3,2]
+    k1 += dpp<0xB1>(s1);
+    const float keep = hi ? k1 : k0, send = hi ? k0 : k1;
+    const float sum = keep + dpp<0x4E>(send);   // quad_perm [2,3,0,1]
+    own = G::CPG == 4 || cp < 4;
+    t_loc = gsub * kGroup + blk * kBlock + quad * 4 + (cp & 3);
+    return fmaf(inv, sum, cst);
   }
 };
 
-// ----------------------------------------------------------------------------- V pass
-// Lane mapping per wave step: 4 blocks (64 tokens).
-//   weights: lane (block jb, bit pair p, channel group e) folds weight, scale and
-//            bucket offset of the four tokens 4p..4p+3 of its block and group;
-//   values:  lane (block, chunk) reads the V words of D/16 channels (16 tokens per
-//            word) and accumulates.
-// 2-bit planes use integer dot products: the weights w_t * s_t of a (block, group)
-// become 23-bit fixed point split into three unsigned byte limbs, v_dot4_u32_u8
-// multiplies them with four tokens' codes of a channel, and each block's exact
-// integer sum is scaled back into the fp32 accumulator. A 4-bit target uses the code
-// 4*hi + lo, with lo = 0 for tokens whose low bits were not fetched (their bucket
-// midpoint sits in the per-token constant term). KIVI-4 stays on the fp32 path.
-template <int D, int MODE, bool SPARSE>
-struct VPass {
-  static constexpr bool KIVI = MODE == MODE_KIVI;
-  static constexpr bool DENSE = MODE == MODE_DENSE;
-  static constexpr int VCH = D / 16;                // channels per lane
-  static constexpr int NE = D / kGroup;             // channel groups
-  static constexpr int WPL = KIVI ? 2 * VCH : VCH;  // V words per lane
-  static constexpr int NV4 = WPL / 4;               // uint4 loads per lane
-  static constexpr int VOFF = KIVI ? off_v_kivi(D) : off_v_planes(D);
-  static constexpr int VMETA = KIVI ? off_vmeta_kivi(D) : off_vmeta_planes(D);
-  static constexpr int COOP = 16 * NE;              // lanes with a weights role
+// ----------------------------------------------------------------------------- V step
+// Weight lanes (block jbm, bit pair p, channel group e) fold weight and scale of the four
+// tokens 4p..4p+3 of their block and group into 16-bit fixed point (scale from the max over
+// the block and group) in two unsigned byte limbs; value lanes (block, chunk of VCH
+// channels) multiply them with four tokens' codes of a channel with v_dot4_u32_u8 and
+// scale each block's exact integer sum into the fp32 accumulator. Constant terms (w z, plus
+// w s 3/2 for a high-plane-only read) go to accz on the weight lanes.
+template <int D, int MODE>
+struct VStep {
+  using G = Geo<D, MODE>;
 
   struct Buf {
-    uint4 meta;
-    uint4 c[NV4];
-    uint4 l[DENSE ? NV4 : 1];
-    bool v, vm;
+    uint4 meta, c[G::NV4], l[G::DENSE ? G::NV4 : 1];
   };
 
-  __device__ static inline void load(const Row& r, int s, int lane, int w, Buf& b) {
-    const int nb = r.n_q / kBlock;
-    const int base = (s * kWaves + w) * 4;
-    const int jm = base + lane / (4 * NE), p = (lane / NE) % 4, e = lane % NE;
-    b.vm = lane < COOP && jm < nb;
-    if (b.vm) b.meta = ld_stream4(r.rec_ptr(jm) + VMETA + 4 * (e * kBlock + 4 * p));
-    const int j = base + lane / 16;
-    b.v = j < nb;
-    if (!b.v) return;
+  // Blocks past the row's end repeat the step's first block (in bounds; their weights are 0).
+  __device__ static inline void load(const Row& r, int jbase, int nb, int lane, Buf& b) {
+    int jm = jbase + lane / (4 * G::NE);
+    const int p = (lane / G::NE) % 4, e = lane % G::NE;
+    jm = jm < nb ? jm : jbase;
+    if (lane < G::COOP) b.meta = ld_stream4(r.rec_ptr(jm) + G::VMETA + 4 * (e * kBlock + 4 * p));
+    int j = jbase + lane / G::LPB;
+    j = j < nb ? j : jbase;
+    const int chunk = lane % G::LPB;
     const uint8_t* rb = r.rec_ptr(j);
-    const int chunk = lane % 16;
-    const uint8_t* vp = rb + VOFF + chunk * WPL * 4;
 #pragma unroll
-    for (int i = 0; i < NV4; ++i) b.c[i] = ld_stream4(vp + 16 * i);
-    if (DENSE) {
-      const uint8_t* lp = rb + off_vlo(D) + chunk * WPL * 4;
+    for (int i = 0; i < G::NV4; ++i) b.c[i] = ld_stream4(rb + G::VOFF + chunk * G::VW * 4 + 16 * i);
+    if (G::DENSE) {
 #pragma unroll
-      for (int i = 0; i < NV4; ++i) b.l[i] = ld_stream4(lp + 16 * i);
+      for (int i = 0; i < G::NV4; ++i) b.l[i] = ld_stream4(rb + off_vlo(D) + chunk * G::VCH * 4 + 16 * i);
     }
   }
 
-  __device__ static inline void compute(const Row& r, const float* weights, const uint32_t* selm, float* scratch,
-                                        int s, int lane, int w, const Buf& b, float* acc, float& accz) {
-    const int base = (s * kWaves + w) * 4;
-    const int jbm = lane / (4 * NE), p = (lane / NE) % 4, e = lane % NE;
+  // wgt: this lane's own token weight (QUAD_W) or the step's weights in LDS (wts).
+  template <class A>
+  __device__ static inline void compute(float wgt, const float* wts, float* scratch, int lane, const Buf& b, A& st) {
+    const int jbm = lane / (4 * G::NE), p = (lane / G::NE) % 4, e = lane % G::NE;
+    uint32_t* vlimb = reinterpret_cast<uint32_t*>(scratch + G::S_VL);   // [BPS][NE][4 p][2]
+    float* vinv = scratch + G::S_VI;                                     // [BPS][NE]
     float a[4] = {0.f, 0.f, 0.f, 0.f};
-    if (b.vm) {
-      const int t0 = (base + jbm) * kBlock + 4 * p;
-      const float4 w4v = *reinterpret_cast<const float4*>(weights + t0);
-      const float wv[4] = {w4v.x, w4v.y, w4v.z, w4v.w};
-      uint32_t sel = DENSE ? 0xFu : 0u;
-      if (SPARSE) sel = (selm[t0 >> 5] >> (t0 & 31)) & 0xFu;
-      // KIVI-4 tokens 4p..4p+3 sit in nibble p % 2 of their word: fold 16^-n here
-      const float pre = KIVI && (p & 1) ? (1.f / 16.f) : 1.f;
+    const bool coop = lane < G::COOP;
+    if (coop) {
+      float wv[4];
+      if constexpr (G::QUAD_W) {
+        wv[0] = dpp<0x00>(wgt);   // quad_perm [0,0,0,0]
+        wv[1] = dpp<0x55>(wgt);
+        wv[2] = dpp<0xAA>(wgt);
+        wv[3] = dpp<0xFF>(wgt);
+      } else {
+        const float4 w4v = *reinterpret_cast<const float4*>(wts + jbm * kBlock + 4 * p);
+        wv[0] = w4v.x;
+        wv[1] = w4v.y;
+        wv[2] = w4v.z;
+        wv[3] = w4v.w;
+      }
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const uint32_t mw = w4(b.meta, k);
-        const float sc = f16lo(mw), z = f16hi(mw);
-        a[k] = wv[k] * sc * pre;
-        const bool mid = (MODE == MODE_COARSE) && !((sel >> k) & 1u);
-        accz = fmaf(wv[k], mid ? fmaf(1.5f, sc, z) : z, accz);
+        a[k] = fmaf(wv[k], f16lo(mw), -0.f);
+        st.accz = fmaf(wv[k], f16hi(mw), st.accz);
+        if (MODE == MODE_COARSE) st.accz = fmaf(1.5f, a[k], st.accz);   // bucket midpoint
       }
     }
-    const int chunk = lane % 16, jb = lane / 16;
-    const int e_lane = (chunk * VCH) / kGroup;
-    const int j = base + jb;
-    if constexpr (KIVI) {
-      float* coefv = scratch;   // [4][NE][16]
-      if (b.vm) *reinterpret_cast<float4*>(coefv + (jbm * NE + e) * 16 + 4 * p) = make_float4(a[0], a[1], a[2], a[3]);
-      wave_sync_lds();
-      if (b.v) {
-        float cf[16];
-        const float4* cp = reinterpret_cast<const float4*>(coefv + (jb * NE + e_lane) * 16);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const float4 tq = cp[u];
-          cf[4 * u] = tq.x;
-          cf[4 * u + 1] = tq.y;
-          cf[4 * u + 2] = tq.z;
-          cf[4 * u + 3] = tq.w;
-        }
-#pragma unroll
-        for (int c = 0; c < VCH; ++c) {
-#pragma unroll
-          for (int jj = 0; jj < 2; ++jj)
-            acc[c] = dot8_v4(w4(b.c[(2 * c + jj) / 4], (2 * c + jj) % 4), cf + 8 * jj, acc[c]);
-        }
+    float am = fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3]));
+    {   // max over the 4 bit-pair lanes of (block, group) (non-negative: unsigned compare)
+      uint32_t v = __float_as_uint(am);
+      if (G::NE == 4) {   // lanes e + 4p of a 16-lane row
+        v = max(v, dpp_u<0x124>(v));   // row_ror:4
+        v = max(v, dpp_u<0x128>(v));   // row_ror:8
+      } else {
+        v = max(v, (uint32_t)__shfl_xor((int)v, G::NE));
+        v = max(v, (uint32_t)__shfl_xor((int)v, 2 * G::NE));
       }
-    } else {
-      uint32_t* vlimb = reinterpret_cast<uint32_t*>(scratch);   // [4][NE][4 p][2]
-      float* vinv = scratch + 4 * NE * 8;                       // [4][NE]
-      float am = fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3]));
-      // max over the 4 bit-pair lanes of (block, group): lanes e + NE*p inside a 16-lane row
-      // (non-negative: compared as unsigned bit patterns)
-      {
-        uint32_t v = __float_as_uint(am);
-        if (NE == 4) {
-          v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x124, 0xF, 0xF, false));   // row_ror:4
-          v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xF, 0xF, false));   // row_ror:8
-        } else {
-          v = max(v, (uint32_t)__shfl_xor((int)v, NE));
-          v = max(v, (uint32_t)__shfl_xor((int)v, 2 * NE));
-        }
-        am = __uint_as_float(v);
-      }
-      // unsigned 16-bit fixed point (weights are >= 0), rounded to nearest inside the fma
-      // with 2^23 added; the scale 2^(16-e) (1 - 2^-17) keeps the rounded value <= 65535
-      const int ex = set_exponent(am);
-      const float scl = __builtin_amdgcn_ldexpf(1.f - 0x1p-17f, 16 - ex);
-      if (b.vm) {
-        uint32_t qb[4], limb[2];
+      am = __uint_as_float(v);
+    }
+    // scale 2^(16-e) (1 - 2^-17) keeps the rounded value <= 65535
+    const int ex = set_exponent(am);
+    const float scl = __builtin_amdgcn_ldexpf(1.f - 0x1p-17f, 16 - ex);
+    if (coop) {
+      uint32_t qb[4], limb[2];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) qb[k] = __float_as_uint(fmaf(a[k], scl, 8388608.0f)) - 0x4B000000u;
-        transpose2(qb, limb);
-        uint32_t* dst = vlimb + ((jbm * NE + e) * 4 + p) * 2;
-        dst[0] = limb[0];
-        dst[1] = limb[1];
-        if (p == 0) vinv[jbm * NE + e] = __builtin_amdgcn_ldexpf(1.f + 0x1p-17f, ex - 16);   // 1 / scl
-      }
-      wave_sync_lds();
-      if (b.v) {
-        uint32_t L[8];
-        const uint4* lp = reinterpret_cast<const uint4*>(vlimb + (jb * NE + e_lane) * 8);
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const uint4 t = lp[u];
-          L[4 * u] = t.x;
-          L[4 * u + 1] = t.y;
-          L[4 * u + 2] = t.z;
-          L[4 * u + 3] = t.w;
-        }
-        float binv = vinv[jb * NE + e_lane];
-        const float hscale = 4.f * binv;   // high bits only: code 4 hi
-        bool need_lo = DENSE;
-        uint32_t m32 = 0xffffffffu;
-        uint4 lw[NV4];
-        if (SPARSE) {
-          const uint32_t bm = (selm[j >> 1] >> (16 * (j & 1))) & 0xffffu;
-          need_lo = bm != 0u;
-          if (need_lo) {
-            m32 = 0;
-#pragma unroll
-            for (int tt = 0; tt < 16; ++tt)
-              if ((bm >> tt) & 1u) m32 |= 3u << (8 * (tt & 3) + 2 * (tt >> 2));
-            const uint8_t* lq = r.rec_ptr(j) + off_vlo(D) + chunk * VCH * 4;
-#pragma unroll
-            for (int i = 0; i < NV4; ++i) lw[i] = *reinterpret_cast<const uint4*>(lq + 16 * i);
-          }
-        }
-        if (DENSE) {
-#pragma unroll
-          for (int i = 0; i < NV4; ++i) lw[i] = b.l[i];
-        }
-        const bool lo_path = (DENSE || SPARSE) && MODE != MODE_Q2 && need_lo;
-        const float cscale = lo_path || MODE == MODE_Q2 ? binv : hscale;
-#pragma unroll
-        for (int c = 0; c < VCH; c += 2) {
-          uint32_t mc[2][4];
-          bitpairs2(w4(b.c[c / 4], c % 4), w4(b.c[c / 4], c % 4 + 1), mc[0], mc[1]);
-          if (lo_path) {   // 4-bit code 4 hi + lo, lo only for fetched tokens
-            uint32_t nc[2][4];
-            bitpairs2(w4(lw[c / 4], c % 4) & m32, w4(lw[c / 4], c % 4 + 1) & m32, nc[0], nc[1]);
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-              for (int pp = 0; pp < 4; ++pp) mc[i][pp] = (mc[i][pp] << 2) | nc[i][pp];
-          }
-#pragma unroll
-          for (int i = 0; i < 2; ++i) {
-            uint32_t a = 0;
-#pragma unroll
-            for (int pp = 0; pp < 4; ++pp) a = udot4(L[2 * pp + 1], mc[i][pp], a);
-            a <<= 8;
-#pragma unroll
-            for (int pp = 0; pp < 4; ++pp) a = udot4(L[2 * pp], mc[i][pp], a);
-            acc[c + i] = fmaf(cscale, (float)a, acc[c + i]);
-          }
-        }
-      }
+      for (int k = 0; k < 4; ++k) qb[k] = fixed16(a[k], scl);
+      transpose2(qb, limb);
+      uint32_t* dst = vlimb + ((jbm * G::NE + e) * 4 + p) * 2;
+      dst[0] = limb[0];
+      dst[1] = limb[1];
+      if (p == 0) vinv[jbm * G::NE + e] = __builtin_amdgcn_ldexpf(1.f + 0x1p-17f, ex - 16);   // 1 / scl
     }
     wave_sync_lds();
-  }
-
-  __device__ static void run(const Row& r, const float* weights, const uint32_t* selm, float* scratch, int lane,
-                             int w, float* acc, float& accz) {
-    const int nb = r.n_q / kBlock;
-    const int steps = (nb + kWaves * 4 - 1) / (kWaves * 4);
-    Buf b0, b1, b2;
-    load(r, 0, lane, w, b0);
-    if (1 < steps) load(r, 1, lane, w, b1);
-    for (int s = 0; s < steps; s += 3) {
-      if (s + 2 < steps) load(r, s + 2, lane, w, b2);
-      compute(r, weights, selm, scratch, s, lane, w, b0, acc, accz);
-      if (s + 1 >= steps) break;
-      if (s + 3 < steps) load(r, s + 3, lane, w, b0);
-      compute(r, weights, selm, scratch, s + 1, lane, w, b1, acc, accz);
-      if (s + 2 >= steps) break;
-      if (s + 4 < steps) load(r, s + 4, lane, w, b1);
-      compute(r, weights, selm, scratch, s + 2, lane, w, b2, acc, accz);
+    const int jb = lane / G::LPB, chunk = lane % G::LPB;
+    const int e_lane = chunk * G::VCH / kGroup;
+    uint32_t L[8];
+    const uint4* lp = reinterpret_cast<const uint4*>(vlimb + (jb * G::NE + e_lane) * 8);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const uint4 t = lp[u];
+      L[4 * u] = t.x;
+      L[4 * u + 1] = t.y;
+      L[4 * u + 2] = t.z;
+      L[4 * u + 3] = t.w;
+    }
+    const float binv = vinv[jb * G::NE + e_lane];
+    const float cscale = MODE == MODE_COARSE ? 4.f * binv : binv;   // high plane only: code 4 hi
+    // two channels at a time, their chains interleaved
+#pragma unroll
+    for (int c = 0; c < G::VCH; c += 2) {
+      uint32_t m[2][4];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        if constexpr (G::KIVI) {   // word (d, j): token 8j + 4n + k at nibble n of byte k
+#pragma unroll
+          for (int jj = 0; jj < 2; ++jj) {
+            const int wi = 2 * (c + i) + jj;
+            const uint32_t x = w4(b.c[wi / 4], wi % 4);
+            m[i][2 * jj] = x & 0x0F0F0F0Fu;
+            m[i][2 * jj + 1] = (x >> 4) & 0x0F0F0F0Fu;
+          }
+        } else {   // word d: token 4p + k at bits 8k + 2p
+          const uint32_t x = w4(b.c[(c + i) / 4], (c + i) % 4);
+#pragma unroll
+          for (int pp = 0; pp < 4; ++pp) {
+            m[i][pp] = (x >> (2 * pp)) & 0x03030303u;
+            if (G::DENSE) m[i][pp] = (m[i][pp] << 2) | ((w4(b.l[(c + i) / 4], (c + i) % 4) >> (2 * pp)) & 0x03030303u);
+          }
+        }
+      }
+      uint32_t s0 = 0, s1 = 0;
+#pragma unroll
+      for (int pp = 0; pp < 4; ++pp) {
+        s0 = udot4(L[2 * pp + 1], m[0][pp], s0);
+        s1 = udot4(L[2 * pp + 1], m[1][pp], s1);
+      }
+      s0 <<= 8;
+      s1 <<= 8;
+#pragma unroll
+      for (int pp = 0; pp < 4; ++pp) {
+        s0 = udot4(L[2 * pp], m[0][pp], s0);
+        s1 = udot4(L[2 * pp], m[1][pp], s1);
+      }
+      st.acc[c] = fmaf(cscale, (float)s0, st.acc[c]);
+      st.acc[c + 1] = fmaf(cscale, (float)s1, st.acc[c + 1]);
     }
   }
 };
 
+// ----------------------------------------------------------------------------- exact V pass
+// Recomputes a 4-bit row's V sum from final weights held in LDS (selected tokens at 4
+// bits, the rest at the bucket midpoint) in the value-lane layout of the coarse step
+// (4 blocks per 64 lanes, D/16 channels per lane), constants included. Runs only when a
+// correction would cancel most of the row's weight.
+template <int D>
+__device__ void exact_v_pass(const Row& r, const float* weights, const uint32_t* selm, int lane, int w,
+                             float* acc) {
+  constexpr int VCH = D / 16;
+  const int nb = r.n_q / kBlock;
+  const int jb = lane / 16, chunk = lane % 16, e = chunk * VCH / kGroup;
+  for (int j = w * 4 + jb; j < nb; j += 4 * kWaves) {
+    const uint8_t* rb = r.rec_ptr(j);
+    uint32_t hw[VCH], lw[VCH];
+#pragma unroll
+    for (int c = 0; c < VCH; ++c) {
+      hw[c] = reinterpret_cast<const uint32_t*>(rb + off_v_planes(D))[chunk * VCH + c];
+      lw[c] = reinterpret_cast<const uint32_t*>(rb + off_vlo(D))[chunk * VCH + c];
+    }
+    const uint32_t bm = (selm[j >> 1] >> (16 * (j & 1))) & 0xffffu;
+    for (int tt = 0; tt < kBlock; ++tt) {
+      const float wt = weights[j * kBlock + tt];
+      const uint32_t mw = reinterpret_cast<const uint32_t*>(rb + off_vmeta_planes(D))[e * kBlock + tt];
+      const float s = f16lo(mw), z = f16hi(mw);
+      const bool sel = (bm >> tt) & 1u;
+      const int sh = 8 * (tt % 4) + 2 * (tt / 4);
+#pragma unroll
+      for (int c = 0; c < VCH; ++c) {
+        const float code = 4.f * (float)((hw[c] >> sh) & 3u) + (sel ? (float)((lw[c] >> sh) & 3u) : 1.5f);
+        acc[c] = fmaf(wt, fmaf(s, code, z), acc[c]);
+      }
+    }
+  }
+}
+
 struct Smem {
-  float* scores;    // [lpad]; after the V pass: [kThreads][VCH] partials, then [kWaves][D] tail partials
+  float* scores;    // [lpad]; at the end: [kThreads][VCH] partials, then [kWaves][D] tail partials
   uint32_t* selm;   // [lpad / 32]
   uint32_t* boff;   // [lpad / 16] record offset of each logical block, 256-byte units
   float* qs;        // [D]
   float* wscr;      // [kWaves][kWaveScratch]
-  float* misc;      // [64 + kWaves * 4]
+  float* misc;      // [96]
 };
 
+// ----------------------------------------------------------------------------- row body
 template <int D, int MODE, bool SPARSE>
 __device__ void row_body(const DecodeArgs& a, const Row& r, const Smem& sm, size_t orow) {
+  using G = Geo<D, MODE>;
+  using KS = KStep<D, MODE, false>;
+  using VS = VStep<D, MODE>;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  float* coef = sm.wscr + w * kWaveScratch;
+  float* scr = sm.wscr + w * kWaveScratch;
+  uint32_t* klimb = reinterpret_cast<uint32_t*>(scr);
   float* scores = sm.scores;
   uint32_t* selm = sm.selm;
   float* misc = sm.misc;
-  constexpr int NE = D / kGroup;
-  constexpr int VCH = D / 16;
+  constexpr int NE = G::NE;
+  constexpr int VCH = G::VCH;
 
-  // ---- K pass (coarse / dense / 2-bit / KIVI-4 scores)
-  float mloc = -INFINITY;
-  KPass<D, MODE, false>::run(r, sm.qs, scores, selm, coef, lane, w, mloc);
-  // tail: exact scores
+  Acc<VCH> st;
+  st.zero();
+  float qreg[G::CPL];
+  KS::qregs(sm.qs, lane, qreg);
+
+  // ---- single streaming pass: K scores, online softmax, V accumulation; wave w takes the
+  // steps (chunks of TPS tokens) w, w + 8, ...; the loads of the next step are in flight
+  // while a step computes
+  const int nb = r.n_q / kBlock;
+  const int n_chunks = (r.n_q + G::TPS - 1) / G::TPS;
+  const int steps = (n_chunks + kWaves - 1) / kWaves;
+  typename KS::Buf kb0, kb1;
+  typename VS::Buf vb0, vb1;
+  // K loads of step s + 1 are issued as step s starts, its V loads once step s's K part is
+  // done: each load has about one step of lead while at most three buffers are live.
+  auto issue_k = [&](int s, typename KS::Buf& kb) {
+    const int c = s * kWaves + w;
+    if (c >= n_chunks) return;   // no chunk for this wave (uniform)
+    int groups[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int g = c * G::GPS + i;
+      groups[i] = (i < G::GPS && g < r.n_groups) ? g : c * G::GPS;
+    }
+    KS::load(r, groups, lane, kb);
+  };
+  auto issue_v = [&](int s, typename VS::Buf& vb) {
+    const int c = s * kWaves + w;
+    if (c >= n_chunks) return;
+    VS::load(r, c * G::BPS, nb, lane, vb);
+  };
+  auto step_k = [&](int s, const typename KS::Buf& kb) -> float {
+    const int c = s * kWaves + w;
+    if (c >= n_chunks) return 0.f;
+    bool own;
+    int t_loc;
+    const float sc0 = KS::compute(qreg, klimb, lane, kb, own, t_loc);
+    const bool valid = own && c * G::GPS + t_loc / kGroup < r.n_groups;
+    const float sc = valid ? sc0 : -INFINITY;
+    if (valid) scores[c * G::TPS + t_loc] = sc;
+    if (__any(sc > st.m)) st.raise(wave_max(sc));   // a new running maximum (rare once warm)
+    const float wgt = valid ? __expf(sc - st.m) : 0.f;
+    st.lsum += wgt;
+    if constexpr (!G::QUAD_W) {
+      wave_sync_lds();   // the K limbs are read before the weights overwrite them
+      if (own) scr[G::S_W + t_loc] = wgt;
+    }
+    wave_sync_lds();
+    return wgt;
+  };
+  auto step_v = [&](int s, const typename VS::Buf& vb, float wgt) {
+    const int c = s * kWaves + w;
+    if (c >= n_chunks) return;
+    VS::compute(wgt, scr + G::S_W, scr, lane, vb, st);
+    wave_sync_lds();
+  };
+  if (steps > 0) {
+    issue_k(0, kb0);
+    issue_v(0, vb0);
+  }
+  for (int s = 0; s < steps; s += 2) {
+    if (s + 1 < steps) issue_k(s + 1, kb1);
+    float wgt = step_k(s, kb0);
+    if (s + 1 < steps) issue_v(s + 1, vb1);
+    step_v(s, vb0, wgt);
+    if (s + 1 >= steps) break;
+    if (s + 2 < steps) issue_k(s + 2, kb0);
+    wgt = step_k(s + 1, kb1);
+    if (s + 2 < steps) issue_v(s + 2, vb0);
+    step_v(s + 1, vb1, wgt);
+  }
+  // ---- tail (exact bf16): tokens n_q + w, n_q + w + 8, ...; tacc: channels lane + 64 i
+  float tacc[D / 64];
+#pragma unroll
+  for (int i = 0; i < D / 64; ++i) tacc[i] = 0.f;
   for (int t = r.n_q + w; t < r.N; t += kWaves) {
     const uint16_t* kt = r.tail + (size_t)(t % kGroup) * D;
     float p = 0.f;
-    for (int d = lane; d < D; d += 64) p = fmaf(sm.qs[d], bf16f(kt[d]), p);
-    p = wave_sum(p);
-    if (lane == 0) {
-      scores[t] = p;
-      mloc = fmaxf(mloc, p);
+#pragma unroll
+    for (int i = 0; i < D / 64; ++i) p = fmaf(sm.qs[lane + 64 * i], bf16f(kt[lane + 64 * i]), p);
+    p = uniform(wave_sum(p));
+    if (lane == 0) scores[t] = p;
+    if (p > st.m) {
+      const float f = st.raise(p);
+#pragma unroll
+      for (int i = 0; i < D / 64; ++i) tacc[i] *= f;
     }
+    const float wgt = __expf(p - st.m);
+    if (lane == 0) st.lsum += wgt;
+    const uint16_t* vt = r.tail + (size_t)(kGroup + t % kGroup) * D;
+#pragma unroll
+    for (int i = 0; i < D / 64; ++i) tacc[i] = fmaf(wgt, bf16f(vt[lane + 64 * i]), tacc[i]);
   }
-  mloc = wave_max(mloc);
-  if (lane == 0) misc[w] = mloc;
-  __syncthreads();
-  float m = misc[0];
-  for (int i = 1; i < kWaves; ++i) m = fmaxf(m, misc[i]);
-  // ---- row sum of the coarse softmax
-  float ls = 0.f;
-  for (int t = tid; t < r.N; t += kThreads) ls += __expf(scores[t] - m);
-  ls = wave_sum(ls);
-  if (lane == 0) misc[8 + w] = ls;
-  __syncthreads();
-  float l = 0.f;
-  for (int i = 0; i < kWaves; ++i) l += misc[8 + i];
 
-  // ---- selection masks (one u32 per 32-token group)
-  if (SPARSE) {
+  // ---- selection (4-bit target, 0 < tau <= 1) and corrections
+  if constexpr (SPARSE) {
+    const float lw = wave_sum(st.lsum);
+    if (lane == 0) {
+      misc[w] = st.m;
+      misc[8 + w] = lw;
+    }
+    __syncthreads();
+    float M = misc[0];
+    for (int i = 1; i < kWaves; ++i) M = fmaxf(M, misc[i]);
+    float L = 0.f;
+    for (int i = 0; i < kWaves; ++i)
+      if (misc[i] > -INFINITY) L += misc[8 + i] * __expf(misc[i] - M);
+    if (st.m > -INFINITY) {
+      const float f = st.raise(M);
+#pragma unroll
+      for (int i = 0; i < D / 64; ++i) tacc[i] *= f;
+    }
+    st.m = M;   // every wave now shares the reference M
+    float removed = 0.f;   // coarse weight taken out by the corrections
     for (int base = 0; base < r.n_q; base += kThreads) {
       const int t = base + tid;
       bool pred = false;
-      if (t < r.n_q) pred = __expf(scores[t] - m) / l >= a.tau;
+      if (t < r.n_q) pred = __expf(scores[t] - M) / L >= a.tau;
       const unsigned long long bal = __ballot(pred);
       const int g0 = (base + 64 * w) / kGroup;
       if (lane == 0 && g0 < r.n_groups) selm[g0] = (uint32_t)bal;
       if (lane == 0 && g0 + 1 < r.n_groups) selm[g0 + 1] = (uint32_t)(bal >> 32);
     }
-  } else {
-    const uint32_t fill = (MODE == MODE_DENSE || MODE == MODE_KIVI) ? 0xffffffffu : 0u;
-    for (int g = tid; g < r.n_groups; g += kThreads) selm[g] = fill;
-  }
-  __syncthreads();
-  if (a.sel_mask) {
-    uint32_t* smo = a.sel_mask + orow * (size_t)a.sel_words;
-    for (int g = tid; g < a.sel_words; g += kThreads) smo[g] = g < r.n_groups ? selm[g] : 0u;
-  }
-
-  // ---- refinement of the selected scores
-  float mfin = m;
-  if (SPARSE) {
-    float mref = -INFINITY;
-    KPass<D, MODE_COARSE, true>::run(r, sm.qs, scores, selm, coef, lane, w, mref);
-    mref = wave_max(mref);
-    if (lane == 0) misc[16 + w] = mref;
     __syncthreads();
-    for (int i = 0; i < kWaves; ++i) mfin = fmaxf(mfin, misc[16 + i]);
+    if (a.sel_mask) {
+      uint32_t* smo = a.sel_mask + orow * (size_t)a.sel_words;
+      for (int g = tid; g < a.sel_words; g += kThreads) smo[g] = g < r.n_groups ? selm[g] : 0u;
+    }
+    // Gather: wave w takes the 64-group spans w, w + 8, ... and corrects their selected
+    // groups two at a time.
+    using KR = KStep<D, MODE_COARSE, true>;
+    using GC = Geo<D, MODE_COARSE>;
+    float* wfix = scr;   // [2][64]: refined and coarse weights of the pair's selected tokens
+    for (int g64 = 64 * w; g64 < r.n_groups; g64 += 64 * kWaves) {
+      const int gi = g64 + lane;
+      unsigned long long pend = __ballot(gi < r.n_groups && selm[gi < r.n_groups ? gi : 0] != 0u);
+      while (pend) {
+        int groups[2];
+        groups[0] = g64 + __builtin_ctzll(pend);
+        pend &= pend - 1;
+        groups[1] = pend ? g64 + __builtin_ctzll(pend) : -1;
+        if (pend) pend &= pend - 1;
+        typename KR::Buf kb;
+        const int lg[2] = {groups[0], groups[1] >= 0 ? groups[1] : groups[0]};
+        KR::load(r, lg, lane, kb);
+        bool own;
+        int t_loc;
+        const float delta = KR::compute(qreg, klimb, lane, kb, own, t_loc);
+        const int ti = t_loc % kGroup;
+        const int g = groups[t_loc / kGroup];
+        const bool sel = own && g >= 0 && ((selm[g < 0 ? 0 : g] >> ti) & 1u);
+        const int t = g * kGroup + ti;
+        const float s_hat = sel ? scores[t] : 0.f;
+        const float s_ref = s_hat + delta;
+        if (sel) scores[t] = s_ref;
+        const float sref = sel ? s_ref : -INFINITY;
+        if (__any(sref > st.m)) {
+          const float f = st.raise(wave_max(sref));
+          removed *= f;
+#pragma unroll
+          for (int i = 0; i < D / 64; ++i) tacc[i] *= f;
+        }
+        const float wf = sel ? __expf(s_ref - st.m) : 0.f;
+        const float wc = sel ? __expf(s_hat - st.m) : 0.f;
+        st.lsum += wf - wc;
+        removed += wc;
+        wave_sync_lds();
+        if (own) {
+          wfix[t_loc] = wf;
+          wfix[64 + t_loc] = wc;
+        }
+        wave_sync_lds();
+        // corrections of the selected tokens' values, in the value-lane layout of the step
+        const int jb = lane / GC::LPB, chunk = lane % GC::LPB;
+        const int gv = groups[jb / 2];
+        const uint32_t bm = gv >= 0 ? (selm[gv] >> (16 * (jb % 2))) & 0xffffu : 0u;
+        if (bm) {
+          const uint8_t* rb = r.rec_ptr(2 * gv + jb % 2);
+          const int e = chunk * GC::VCH / kGroup;
+          uint32_t hw[GC::VCH], lw[GC::VCH];
+#pragma unroll
+          for (int c = 0; c < GC::VCH; ++c) {
+            hw[c] = reinterpret_cast<const uint32_t*>(rb + off_v_planes(D))[chunk * GC::VCH + c];
+            lw[c] = reinterpret_cast<const uint32_t*>(rb + off_vlo(D))[chunk * GC::VCH + c];
+          }
+          for (int tt = 0; tt < kBlock; ++tt) {
+            if (!((bm >> tt) & 1u)) continue;
+            const uint32_t mw = reinterpret_cast<const uint32_t*>(rb + off_vmeta_planes(D))[e * kBlock + tt];
+            const float s = f16lo(mw), z = f16hi(mw);
+            const float f1 = wfix[jb * kBlock + tt], f0 = wfix[64 + jb * kBlock + tt];
+            // w' (z + s (4 hi + lo)) - w (z + s (4 hi + 3/2)) = A hi + B lo + C
+            const float A = 4.f * s * (f1 - f0), B = s * f1, C = (f1 - f0) * z - 1.5f * s * f0;
+            const int sh = 8 * (tt % 4) + 2 * (tt / 4);
+#pragma unroll
+            for (int c = 0; c < GC::VCH; ++c)
+              st.acc[c] += fmaf(A, (float)((hw[c] >> sh) & 3u), fmaf(B, (float)((lw[c] >> sh) & 3u), C));
+          }
+        }
+        wave_sync_lds();
+      }
+    }
+    // Cancellation check over the row.
+    const float lw2 = wave_sum(st.lsum), rw = wave_sum(removed);
+    __syncthreads();
+    if (lane == 0) {
+      misc[w] = st.m;
+      misc[8 + w] = lw2;
+      misc[16 + w] = rw;
+    }
+    __syncthreads();
+    float Ms = misc[0];
+    for (int i = 1; i < kWaves; ++i) Ms = fmaxf(Ms, misc[i]);
+    float Lp = 0.f, Rm = 0.f;
+    for (int i = 0; i < kWaves; ++i) {
+      const float f = __expf(misc[i] - Ms);
+      Lp += misc[8 + i] * f;
+      Rm += misc[16 + i] * f;
+    }
+    if (Rm > 1024.f * Lp) {   // recompute the row's V from the final scores
+      __syncthreads();
+      float ls = 0.f;
+      for (int t = tid; t < r.N; t += kThreads) {
+        const float wgt = __expf(scores[t] - Ms);
+        scores[t] = wgt;
+        ls += wgt;
+      }
+      __syncthreads();
+      st.zero();
+      st.m = Ms;
+      st.lsum = ls;
+      exact_v_pass<D>(r, scores, selm, lane, w, st.acc);
+#pragma unroll
+      for (int i = 0; i < D / 64; ++i) tacc[i] = 0.f;
+      for (int t = r.n_q + w; t < r.N; t += kWaves) {
+        const uint16_t* vt = r.tail + (size_t)(kGroup + t % kGroup) * D;
+#pragma unroll
+        for (int i = 0; i < D / 64; ++i) tacc[i] = fmaf(scores[t], bf16f(vt[lane + 64 * i]), tacc[i]);
+      }
+    }
+  } else {
+    if (a.sel_mask) {
+      const uint32_t fill = (MODE == MODE_DENSE || MODE == MODE_KIVI) ? 0xffffffffu : 0u;
+      uint32_t* smo = a.sel_mask + orow * (size_t)a.sel_words;
+      for (int g = tid; g < a.sel_words; g += kThreads) smo[g] = g < r.n_groups ? fill : 0u;
+    }
   }
 
-  // ---- V pass
-  // softmax weights w_t = exp(s_t - m') replace the scores in LDS
-  float lsum = 0.f;
-  for (int t = tid; t < r.N; t += kThreads) {
-    const float wgt = __expf(scores[t] - mfin);
-    scores[t] = wgt;
-    lsum += wgt;
-  }
-  __syncthreads();
-  const float* weights = scores;
-  float acc[VCH];
-#pragma unroll
-  for (int c = 0; c < VCH; ++c) acc[c] = 0.f;
-  float accz = 0.f;   // constant terms of channel group lane % NE
-  VPass<D, MODE, SPARSE>::run(r, weights, selm, coef, lane, w, acc, accz);
-  // tail values, exact
-  float tacc[D / 64];
-#pragma unroll
-  for (int i = 0; i < D / 64; ++i) tacc[i] = 0.f;
-  for (int t = r.n_q + w; t < r.N; t += kWaves) {
-    const float wgt = weights[t];
-    const uint16_t* vt = r.tail + (size_t)(kGroup + t % kGroup) * D;
-#pragma unroll
-    for (int i = 0; i < D / 64; ++i) tacc[i] = fmaf(wgt, bf16f(vt[lane + 64 * i]), tacc[i]);
-  }
-  __syncthreads();   // scores are dead from here on: reuse them for partials
-  float* red = scores;                         // [kThreads][VCH]
-  float* tred = scores + kThreads * VCH;       // [kWaves][D]
-#pragma unroll
-  for (int c = 0; c < VCH; ++c) red[tid * VCH + c] = acc[c];
-#pragma unroll
-  for (int i = 0; i < D / 64; ++i) tred[w * D + lane + 64 * i] = tacc[i];
-  lsum = wave_sum(lsum);
+  // ---- merge the waves (the exact pass writes in the value-lane layout of the coarse
+  // step, which is this mode's layout whenever it runs)
+  const float lsum = wave_sum(st.lsum);
   float zs[NE];
 #pragma unroll
-  for (int e = 0; e < NE; ++e) zs[e] = wave_sum((lane % NE) == e ? accz : 0.f);
+  for (int e = 0; e < NE; ++e) zs[e] = wave_sum((lane % NE) == e && lane < G::COOP ? st.accz : 0.f);
+  __syncthreads();   // scores are dead from here on: reuse them for partials
   if (lane == 0) {
-    misc[24 + w] = lsum;
+    misc[w] = st.m;
+    misc[8 + w] = lsum;
 #pragma unroll
     for (int e = 0; e < NE; ++e) misc[32 + w * 4 + e] = zs[e];
   }
   __syncthreads();
-  float L = 0.f;
-  for (int i = 0; i < kWaves; ++i) L += misc[24 + i];
+  float M = misc[0];
+  for (int i = 1; i < kWaves; ++i) M = fmaxf(M, misc[i]);
+  const float fw = st.m > -INFINITY ? __expf(st.m - M) : 0.f;
+  float* red = scores;                         // [kThreads][VCH]
+  float* tred = scores + kThreads * VCH;       // [kWaves][D]
+#pragma unroll
+  for (int c = 0; c < VCH; ++c) red[tid * VCH + c] = st.acc[c] * fw;
+#pragma unroll
+  for (int i = 0; i < D / 64; ++i) tred[w * D + lane + 64 * i] = tacc[i] * fw;
+  __syncthreads();
+  float fws[kWaves];
+  float Lt = 0.f;
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) {
+    fws[i] = misc[i] > -INFINITY ? __expf(misc[i] - M) : 0.f;
+    Lt += misc[8 + i] * fws[i];
+  }
   for (int d = tid; d < D; d += kThreads) {
     const int chunk = d / VCH, c = d % VCH;
     float o = 0.f;
-    for (int ww = 0; ww < kWaves; ++ww) {
-      o += misc[32 + ww * 4 + d / kGroup];
 #pragma unroll
-      for (int vb = 0; vb < 4; ++vb) o += red[(ww * 64 + vb * 16 + chunk) * VCH + c];
+    for (int ww = 0; ww < kWaves; ++ww) {
+      o += misc[32 + ww * 4 + d / kGroup] * fws[ww];
+#pragma unroll
+      for (int vb = 0; vb < G::BPS; ++vb) o += red[(ww * 64 + vb * G::LPB + chunk) * VCH + c];
       o += tred[ww * D + d];
     }
-    o = o / L;
+    o = o / Lt;
     if (a.out_bf16) {
       uint32_t u = __float_as_uint(o);
       u += 0x7fffu + ((u >> 16) & 1u);
@@ -884,8 +997,7 @@ __host__ __device__ inline size_t lds_region_a(int max_len, int D) {
 }
 __host__ __device__ inline size_t decode_lds_floats(int max_len, int D) {
   const size_t lp = lds_lpad(max_len);
-  return lds_region_a(max_len, D) + pad4(lp / 32) + pad4(lp / 16 + 16) + D + (size_t)kWaves * kWaveScratch + 64 +
-         kWaves * 4;
+  return lds_region_a(max_len, D) + pad4(lp / 32) + pad4(lp / 16 + 16) + D + (size_t)kWaves * kWaveScratch + 96;
 }
 
 // One kernel per selection regime of the launch (tau = 0, tau > 1, 0 < tau <= 1, or the
@@ -894,7 +1006,7 @@ __host__ __device__ inline size_t decode_lds_floats(int max_len, int D) {
 enum : int { VAR_KIVI = 0, VAR_DENSE = 1, VAR_COARSE = 2, VAR_SPARSE = 3 };
 
 template <int D, int VAR>
-__global__ void __launch_bounds__(kThreads, 4) k_decode(DecodeArgs a) {
+__global__ void __launch_bounds__(kThreads, kWavesPerSimd) k_decode(DecodeArgs a) {
   extern __shared__ float smem[];
   const int row = blockIdx.x;
   const int h = row % a.n_heads;

@@ -132,6 +132,13 @@ __device__ inline float wave_max(float x) {
 
 __device__ inline float f16lo(uint32_t w) { return __half2float(__ushort_as_half((unsigned short)(w & 0xffffu))); }
 __device__ inline float f16hi(uint32_t w) { return __half2float(__ushort_as_half((unsigned short)(w >> 16))); }
+// a * (f16 in the low half of w), rounded once (v_fma_mix; the compiler otherwise converts
+// and multiplies in two instructions).
+__device__ inline float mul_f16lo(float a, uint32_t w) {
+  float r;
+  asm("v_fma_mix_f32 %0, %1, %2, 0 op_sel_hi:[0,1,0]" : "=v"(r) : "v"(a), "v"(w));
+  return r;
+}
 __device__ inline float bf16f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 __device__ inline uint32_t w4(const uint4& v, int i) { return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w; }
 
@@ -152,6 +159,19 @@ __device__ inline uint4 ld_stream1(const void* p) {
 template <int N>
 __device__ inline uint4 ld_words(const void* p) {
   return N == 4 ? ld_stream4(p) : N == 2 ? ld_stream2(p) : ld_stream1(p);
+}
+
+template <int N>
+__device__ inline uint4 ld_words_lds(const float* p) {
+  if constexpr (N == 4) {
+    const float4 v = *reinterpret_cast<const float4*>(p);
+    return make_uint4(__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z), __float_as_uint(v.w));
+  } else if constexpr (N == 2) {
+    const float2 v = *reinterpret_cast<const float2*>(p);
+    return make_uint4(__float_as_uint(v.x), __float_as_uint(v.y), 0u, 0u);
+  } else {
+    return make_uint4(__float_as_uint(p[0]), 0u, 0u, 0u);
+  }
 }
 
 __device__ inline int sdot4(uint32_t a, uint32_t b, int c) { return __builtin_amdgcn_sdot4((int)a, (int)b, c, false); }
@@ -306,16 +326,14 @@ struct KStep {
     }
   }
 
-  // sigma q of the channels at this lane's K-meta positions (fixed for the row).
-  __device__ static inline void qregs(const float* qs, int lane, float* qreg) {
-    const int pos0 = (lane % G::LPG) * G::CPL;
-#pragma unroll
-    for (int k = 0; k < G::CPL; ++k) {
-      const int pos = pos0 + k;
-      // 2-bit: position 16w + 4p + k holds channel 16w + 4k + p; 4-bit: 8w + 4n + k holds 8w + 2k + n
+  // sigma q in K-meta position order (2-bit: position 16w + 4p + k holds channel 16w + 4k + p;
+  // 4-bit: 8w + 4n + k holds 8w + 2k + n), written once per row so that a lane reads the q
+  // of its positions with one LDS load per step instead of holding them in registers.
+  __device__ static inline void fill_qperm(const float* qs, float* qperm) {
+    for (int pos = threadIdx.x; pos < D; pos += kThreads) {
       const int ch = G::KIVI ? 8 * (pos / 8) + 2 * (pos % 4) + (pos / 4) % 2
                              : 16 * (pos / 16) + 4 * (pos % 4) + (pos / 4) % 4;
-      qreg[k] = qs[ch];
+      qperm[pos] = qs[ch];
     }
   }
 
@@ -336,17 +354,23 @@ struct KStep {
 
   // The step's scores. Every token t_loc of the step has one owner lane (own), which
   // receives sigma q . k_t (REFINE: the correction to it).
-  __device__ static inline float compute(const float* qreg, uint32_t* klimb, int lane, const Buf& b, bool& own,
+  __device__ static inline float compute(const float* qperm, uint32_t* klimb, int lane, const Buf& b, bool& own,
                                          int& t_loc) {
     int gsub, blk, quad, cp;
     role(lane, gsub, blk, quad, cp);
     const int pos0 = (lane % G::LPG) * G::CPL;
+    float qreg[G::CPL];
+    {
+      const uint4 qv = ld_words_lds<G::CPL>(qperm + pos0);
+#pragma unroll
+      for (int k = 0; k < G::CPL; ++k) qreg[k] = __uint_as_float(w4(qv, k));
+    }
     float f[G::CPL];
     float cst = 0.f;
 #pragma unroll
     for (int k = 0; k < G::CPL; ++k) {
       const uint32_t mw = w4(b.meta, k);
-      f[k] = fmaf(qreg[k], f16lo(mw), -0.f);               // sigma q s
+      f[k] = mul_f16lo(qreg[k], mw);                       // sigma q s
       if (REFINE) {
         cst = fmaf(-1.5f, f[k], cst);                     // sigma q s (lo - 3/2)
       } else if (MODE == MODE_COARSE) {
@@ -543,7 +567,7 @@ struct VStep {
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const uint32_t mw = w4(b.meta, k);
-        a[k] = fmaf(wv[k], f16lo(mw), -0.f);
+        a[k] = mul_f16lo(wv[k], mw);
         st.accz = fmaf(wv[k], f16hi(mw), st.accz);
         if (MODE == MODE_COARSE) st.accz = fmaf(1.5f, a[k], st.accz);   // bucket midpoint
       }
@@ -670,6 +694,7 @@ struct Smem {
   uint32_t* selm;   // [lpad / 32]
   uint32_t* boff;   // [lpad / 16] record offset of each logical block, 256-byte units
   float* qs;        // [D]
+  float* qperm;     // [D] sigma q in K-meta position order
   float* wscr;      // [kWaves][kWaveScratch]
   float* misc;      // [96]
 };
@@ -691,8 +716,8 @@ __device__ void row_body(const DecodeArgs& a, const Row& r, const Smem& sm, size
 
   Acc<VCH> st;
   st.zero();
-  float qreg[G::CPL];
-  KS::qregs(sm.qs, lane, qreg);
+  KS::fill_qperm(sm.qs, sm.qperm);
+  __syncthreads();
 
   // ---- single streaming pass: K scores, online softmax, V accumulation; wave w takes the
   // steps (chunks of TPS tokens) w, w + 8, ...; the loads of the next step are in flight
@@ -725,7 +750,7 @@ __device__ void row_body(const DecodeArgs& a, const Row& r, const Smem& sm, size
     if (c >= n_chunks) return 0.f;
     bool own;
     int t_loc;
-    const float sc0 = KS::compute(qreg, klimb, lane, kb, own, t_loc);
+    const float sc0 = KS::compute(sm.qperm, klimb, lane, kb, own, t_loc);
     const bool valid = own && c * G::GPS + t_loc / kGroup < r.n_groups;
     const float sc = valid ? sc0 : -INFINITY;
     if (valid) scores[c * G::TPS + t_loc] = sc;
@@ -836,7 +861,7 @@ __device__ void row_body(const DecodeArgs& a, const Row& r, const Smem& sm, size
         KR::load(r, lg, lane, kb);
         bool own;
         int t_loc;
-        const float delta = KR::compute(qreg, klimb, lane, kb, own, t_loc);
+        const float delta = KR::compute(sm.qperm, klimb, lane, kb, own, t_loc);
         const int ti = t_loc % kGroup;
         const int g = groups[t_loc / kGroup];
         const bool sel = own && g >= 0 && ((selm[g < 0 ? 0 : g] >> ti) & 1u);
@@ -997,7 +1022,7 @@ __host__ __device__ inline size_t lds_region_a(int max_len, int D) {
 }
 __host__ __device__ inline size_t decode_lds_floats(int max_len, int D) {
   const size_t lp = lds_lpad(max_len);
-  return lds_region_a(max_len, D) + pad4(lp / 32) + pad4(lp / 16 + 16) + D + (size_t)kWaves * kWaveScratch + 96;
+  return lds_region_a(max_len, D) + pad4(lp / 32) + pad4(lp / 16 + 16) + 2 * D + (size_t)kWaves * kWaveScratch + 96;
 }
 
 // One kernel per selection regime of the launch (tau = 0, tau > 1, 0 < tau <= 1, or the
@@ -1023,7 +1048,8 @@ __global__ void __launch_bounds__(kThreads, kWavesPerSimd) k_decode(DecodeArgs a
   sm.selm = reinterpret_cast<uint32_t*>(smem + lds_region_a(a.max_len, D));
   sm.boff = sm.selm + pad4(lp / 32);
   sm.qs = reinterpret_cast<float*>(sm.boff + pad4(lp / 16 + 16));
-  sm.wscr = sm.qs + D;
+  sm.qperm = sm.qs + D;
+  sm.wscr = sm.qperm + D;
   sm.misc = sm.wscr + kWaves * kWaveScratch;
 
   if (N <= 0 || N > a.max_len) {

@@ -90,8 +90,8 @@ __global__ void k_stream_read(const u32x4_t* p, size_t n16, unsigned* out) {
   out[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = acc.x ^ acc.y ^ acc.z ^ acc.w;
 }
 
-// Each wave reads whole chunks: wave k of the grid takes chunks k, k + waves, ...; chunk c
-// starts at order[c] * record_bytes.
+// Each wave reads whole chunks (up to 4096 bytes): wave k of the grid takes chunks k,
+// k + waves, ...; chunk c starts at order[c] * record_bytes.
 __global__ void k_chunk_read(const unsigned char* base, const unsigned* order, int n_chunks, int record_bytes,
                              int chunk_bytes, unsigned* out) {
   const int lane = threadIdx.x & 63;
@@ -100,16 +100,21 @@ __global__ void k_chunk_read(const unsigned char* base, const unsigned* order, i
   const int per = chunk_bytes / 16;
   u32x4_t acc = {0u, 0u, 0u, 0u};
   for (int c = wave; c < n_chunks; c += 4 * waves) {
-    u32x4_t v[4];
+    u32x4_t v[4][4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int cc = c + u * waves;
-      v[u] = (u32x4_t){0u, 0u, 0u, 0u};
-      if (cc < n_chunks && lane < per)
-        v[u] = __builtin_nontemporal_load(
-            reinterpret_cast<const u32x4_t*>(base + (size_t)order[cc] * record_bytes) + lane);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = lane + 64 * r;
+        v[u][r] = (u32x4_t){0u, 0u, 0u, 0u};
+        if (cc < n_chunks && i < per)
+          v[u][r] = __builtin_nontemporal_load(
+              reinterpret_cast<const u32x4_t*>(base + (size_t)order[cc] * record_bytes) + i);
+      }
     }
-    acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
   }
   out[blockIdx.x * blockDim.x + threadIdx.x] = acc.x ^ acc.y ^ acc.z ^ acc.w;
 }
@@ -139,7 +144,7 @@ int synth_stream_read(hipStream_t s, const void* p, size_t n16, int blocks, unsi
   return (int)hipGetLastError();
 }
 
-// Chunk reads at permuted record starts (see k_chunk_read).
+// Chunk reads (chunk_bytes <= 4096, a multiple of 16) at permuted record starts (see k_chunk_read).
 int synth_chunk_read(hipStream_t s, const void* base, const unsigned* order, int n_chunks, int record_bytes,
                      int chunk_bytes, int blocks, unsigned* out) {
   hipLaunchKernelGGL(k_chunk_read, dim3(blocks), dim3(256), 0, s, (const unsigned char*)base, order, n_chunks,

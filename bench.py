@@ -316,7 +316,7 @@ def main():
 
     try:
         from synth import gpu as G
-        extra["read_ceiling"] = G.read_ceiling()
+        extra["read_ceiling"] = G.read_ceiling(chunk_bytes=1536)   # the K and V spans of one 4-bit record
         log(f"read ceiling: {extra['read_ceiling']}")
     except Exception as e:  # the probe is context only
         log(f"read ceiling probe failed: {e}")
@@ -351,7 +351,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16 in, fp32 accumulate, 2-bit/4-bit codes",
+        "dtype": "i8 dot products into i32, f32 softmax and accumulators (bf16 q/K/V in, bf16 out)",
         "data": "synthetic (seeded Philox normal draws, shapes of the pages' Ouro-1.4B 16K serving workload)",
         "config": {"workload": "4 loops x 24 layers, 48 q4 / 29 q2 / 19 reuse, 16 heads x 128, batch 32, "
                                f"context {args.ctx} (last step), 16-token blocks shuffled, tau {args.tau}, "

@@ -56,13 +56,16 @@ __device__ inline void wave_sync_lds() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// DPP lane moves. Every pattern used here (quad permutes, row mirrors, row rotates) reads a
+// valid lane, so the old value is never kept: mov_dpp leaves it undefined and the move
+// fuses into the consuming ALU op without initializing a destination first.
 template <int CTRL>
 __device__ inline float dpp(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
 }
 template <int CTRL>
 __device__ inline uint32_t dpp_u(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, true);
 }
 // Cross-row exchanges without LDS (gfx950 permlane swaps): with both operands equal,
 // permlane16_swap returns rows (0,0,2,2) and (1,1,3,3); permlane32_swap returns rows
@@ -200,16 +203,19 @@ __device__ inline int set_exponent(float vmax) {
   const int e = __builtin_amdgcn_frexp_expf(vmax);
   return e < -100 ? -100 : e;
 }
-// Signed 22-bit fixed point with byte-limb bias: for |v| < 2^21, returns v + 0x808080
-// (three biased bytes). The add of 1.5 * 2^23 rounds v to the nearest integer (ties to
-// even) inside the fma and leaves it in the low mantissa bits.
+// Signed 22-bit fixed point split into three signed byte digits: for |v| < 2^21 returns
+// w = v + 0x8080 (two's complement), so v = (b0 - 128) + 256 (b1 - 128) + 65536 b2 with b2
+// the signed top byte of w; bytes 0 and 1 become signed digits by flipping their top bit.
+// The add of 1.5 * 2^23 rounds v to the nearest integer (ties to even) inside the fma and
+// leaves it in the low mantissa bits.
 __device__ inline uint32_t biased_fixed22(float c, float scl) {
-  return __float_as_uint(fmaf(c, scl, 12582912.0f)) - (0x4B400000u - 0x808080u);
+  return __float_as_uint(fmaf(c, scl, 12582912.0f)) - (0x4B400000u - 0x8080u);
 }
-// Unsigned 16-bit fixed point of a >= 0 with scale scl (a * scl <= 65535.5): rounded to
-// nearest inside the fma with 2^23 added.
-__device__ inline uint32_t fixed16(float a, float scl) {
-  return __float_as_uint(fmaf(a, scl, 8388608.0f)) - 0x4B000000u;
+// Unsigned 16-bit fixed point of a >= 0 with scale scl (a * scl <= 65535.5), rounded to
+// nearest inside the fma with 2^23 added: bytes 0 and 1 of the returned bit pattern are the
+// value (the exponent bits above are never read).
+__device__ inline uint32_t fixed16_lo(float a, float scl) {
+  return __float_as_uint(fmaf(a, scl, 8388608.0f));
 }
 
 struct Row {
@@ -433,7 +439,8 @@ struct KStep {
       transpose3(u, limb);
       uint32_t* dst = klimb + (gsub * (D / 4) + pos0 / 4) * 3;
 #pragma unroll
-      for (int j = 0; j < 3; ++j) dst[j] = limb[j] ^ 0x80808080u;   // biased byte -> signed digit
+      for (int j = 0; j < 2; ++j) dst[j] = limb[j] ^ 0x80808080u;   // biased byte -> signed digit
+      dst[2] = limb[2];
     }
     wave_sync_lds();
     // Limbs of this lane's NC columns (SPC sets x 3 words each); the four tokens' chains run
@@ -572,9 +579,10 @@ struct VStep {
         if (MODE == MODE_COARSE) st.accz = fmaf(1.5f, a[k], st.accz);   // bucket midpoint
       }
     }
-    float am = fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3]));
-    {   // max over the 4 bit-pair lanes of (block, group) (non-negative: unsigned compare)
-      uint32_t v = __float_as_uint(am);
+    float am;
+    {   // max over the 4 tokens and the 4 bit-pair lanes of (block, group) (non-negative:
+        // unsigned compare of the bit patterns)
+      uint32_t v = max(max(__float_as_uint(a[0]), __float_as_uint(a[1])), max(__float_as_uint(a[2]), __float_as_uint(a[3])));
       if (G::NE == 4) {   // lanes e + 4p of a 16-lane row
         v = max(v, dpp_u<0x124>(v));   // row_ror:4
         v = max(v, dpp_u<0x128>(v));   // row_ror:8
@@ -590,7 +598,7 @@ struct VStep {
     if (coop) {
       uint32_t qb[4], limb[2];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) qb[k] = fixed16(a[k], scl);
+      for (int k = 0; k < 4; ++k) qb[k] = fixed16_lo(a[k], scl);
       transpose2(qb, limb);
       uint32_t* dst = vlimb + ((jbm * G::NE + e) * 4 + p) * 2;
       dst[0] = limb[0];
@@ -828,10 +836,12 @@ __device__ void row_body(const DecodeArgs& a, const Row& r, const Smem& sm, size
     }
     st.m = M;   // every wave now shares the reference M
     float removed = 0.f;   // coarse weight taken out by the corrections
+    // exp(s - M) / L >= tau  <=>  s >= M + ln(tau L): one compare per token
+    const float thr = M + logf(a.tau * L);
     for (int base = 0; base < r.n_q; base += kThreads) {
       const int t = base + tid;
       bool pred = false;
-      if (t < r.n_q) pred = __expf(scores[t] - M) / L >= a.tau;
+      if (t < r.n_q) pred = scores[t] >= thr;
       const unsigned long long bal = __ballot(pred);
       const int g0 = (base + 64 * w) / kGroup;
       if (lane == 0 && g0 < r.n_groups) selm[g0] = (uint32_t)bal;

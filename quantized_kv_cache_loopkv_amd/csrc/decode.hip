@@ -869,6 +869,24 @@ __device__ void row_body(const DecodeArgs& a, const Row& r, const Smem& sm, size
         typename KR::Buf kb;
         const int lg[2] = {groups[0], groups[1] >= 0 ? groups[1] : groups[0]};
         KR::load(r, lg, lane, kb);
+        // the V words the corrections need are loaded together with the K low plane (one
+        // memory round trip): value-lane layout of the step, blocks holding a selected token
+        const int jb = lane / GC::LPB, chunk = lane % GC::LPB;
+        const int gv = groups[jb / 2];
+        const uint32_t bm = gv >= 0 ? (selm[gv] >> (16 * (jb % 2))) & 0xffffu : 0u;
+        const int ev = chunk * GC::VCH / kGroup;
+        uint4 hw4[GC::VCH / 4], lw4[GC::VCH / 4], mv4[4];
+        if (bm) {
+          const uint8_t* rb = r.rec_ptr(2 * gv + jb % 2);
+#pragma unroll
+          for (int i = 0; i < GC::VCH / 4; ++i) {
+            hw4[i] = *reinterpret_cast<const uint4*>(rb + off_v_planes(D) + 4 * (chunk * GC::VCH + 4 * i));
+            lw4[i] = *reinterpret_cast<const uint4*>(rb + off_vlo(D) + 4 * (chunk * GC::VCH + 4 * i));
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            mv4[i] = *reinterpret_cast<const uint4*>(rb + off_vmeta_planes(D) + 4 * (ev * kBlock + 4 * i));
+        }
         bool own;
         int t_loc;
         const float delta = KR::compute(sm.qperm, klimb, lane, kb, own, t_loc);
@@ -896,30 +914,21 @@ __device__ void row_body(const DecodeArgs& a, const Row& r, const Smem& sm, size
           wfix[64 + t_loc] = wc;
         }
         wave_sync_lds();
-        // corrections of the selected tokens' values, in the value-lane layout of the step
-        const int jb = lane / GC::LPB, chunk = lane % GC::LPB;
-        const int gv = groups[jb / 2];
-        const uint32_t bm = gv >= 0 ? (selm[gv] >> (16 * (jb % 2))) & 0xffffu : 0u;
+        // corrections of the selected tokens' values
         if (bm) {
-          const uint8_t* rb = r.rec_ptr(2 * gv + jb % 2);
-          const int e = chunk * GC::VCH / kGroup;
-          uint32_t hw[GC::VCH], lw[GC::VCH];
-#pragma unroll
-          for (int c = 0; c < GC::VCH; ++c) {
-            hw[c] = reinterpret_cast<const uint32_t*>(rb + off_v_planes(D))[chunk * GC::VCH + c];
-            lw[c] = reinterpret_cast<const uint32_t*>(rb + off_vlo(D))[chunk * GC::VCH + c];
-          }
           for (int tt = 0; tt < kBlock; ++tt) {
             if (!((bm >> tt) & 1u)) continue;
-            const uint32_t mw = reinterpret_cast<const uint32_t*>(rb + off_vmeta_planes(D))[e * kBlock + tt];
+            const uint32_t mw = w4(mv4[tt / 4], tt % 4);
             const float s = f16lo(mw), z = f16hi(mw);
             const float f1 = wfix[jb * kBlock + tt], f0 = wfix[64 + jb * kBlock + tt];
             // w' (z + s (4 hi + lo)) - w (z + s (4 hi + 3/2)) = A hi + B lo + C
             const float A = 4.f * s * (f1 - f0), B = s * f1, C = (f1 - f0) * z - 1.5f * s * f0;
             const int sh = 8 * (tt % 4) + 2 * (tt / 4);
 #pragma unroll
-            for (int c = 0; c < GC::VCH; ++c)
-              st.acc[c] += fmaf(A, (float)((hw[c] >> sh) & 3u), fmaf(B, (float)((lw[c] >> sh) & 3u), C));
+            for (int c = 0; c < GC::VCH; ++c) {
+              const uint32_t hwc = w4(hw4[c / 4], c % 4), lwc = w4(lw4[c / 4], c % 4);
+              st.acc[c] += fmaf(A, (float)((hwc >> sh) & 3u), fmaf(B, (float)((lwc >> sh) & 3u), C));
+            }
           }
         }
         wave_sync_lds();

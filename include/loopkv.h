@@ -89,6 +89,7 @@ typedef enum { LOOPKV_LAYOUT_PLANES = 0, LOOPKV_LAYOUT_KIVI4 = 1 } loopkv_layout
 
 /* Largest supported max_len of one decode call (coarse scores of a row live in LDS). */
 #define LOOPKV_MAX_LEN 32768
+#define LOOPKV_MAX_SPLIT 64   /* workgroups per row of a split decode */
 /* Largest n_loops * n_layers. */
 #define LOOPKV_MAX_CELLS 128
 
@@ -160,6 +161,35 @@ loopkv_status loopkv_decode_attn(loopkv_ctx* ctx, hipStream_t stream, int32_t lo
                                  int32_t bt_stride, const int32_t* seq_lens, int32_t max_len,
                                  float tau, float sm_scale, void* out, int32_t out_dtype,
                                  uint32_t* sel_mask);
+
+/* Scratch bytes a split decode of this (loop, layer) ((-1, -1): whole plan) needs for
+ * n_seqs sequences, max_len and n_split (1..LOOPKV_MAX_SPLIT): per row, n_split partials
+ * of (2 + head_dim) floats and one line of ceil(max_len/64)*64 coarse scores. */
+loopkv_status loopkv_split_scratch_bytes(const loopkv_ctx* ctx, int32_t loop, int32_t layer,
+                                         int32_t n_seqs, int32_t max_len, int32_t n_split,
+                                         size_t* bytes);
+
+/* The same decode as loopkv_decode_attn (same arguments, same results up to the order of
+ * fp32 additions), with each row's tokens split over n_split workgroups, for calls with
+ * few rows (one cell at a small batch), where one workgroup per row leaves most of the
+ * GPU idle. The split follows the split-K online softmax of the decode: every workgroup
+ * streams a range of the row's tokens and leaves a partial (max, weight, values); a
+ * second launch on the same stream merges the partials, selects the tokens whose coarse
+ * weight over the whole row reaches tau (the row-global softmax of the Abstract's
+ * decoding sentence), fetches their low bits and writes the row.
+ * scratch: caller-owned device memory of >= loopkv_split_scratch_bytes bytes, 16-byte
+ * aligned; its contents are overwritten and need no initialization. Calls that share a
+ * scratch buffer must be ordered (one stream). Errors as for loopkv_decode_attn, plus
+ * LOOPKV_ERR_INVALID_ARG for n_split outside [1, LOOPKV_MAX_SPLIT] and
+ * LOOPKV_ERR_WORKSPACE for a missing, misaligned or short scratch. */
+loopkv_status loopkv_decode_attn_split(loopkv_ctx* ctx, hipStream_t stream, int32_t loop,
+                                       int32_t layer, const void* q, int32_t q_dtype,
+                                       int32_t n_seqs, const int32_t* seq_slots,
+                                       const int32_t* block_table, int32_t bt_stride,
+                                       const int32_t* seq_lens, int32_t max_len, float tau,
+                                       float sm_scale, void* out, int32_t out_dtype,
+                                       uint32_t* sel_mask, int32_t n_split, void* scratch,
+                                       size_t scratch_bytes);
 
 /* Thread-local description of the last error on this thread ("" after success). */
 const char* loopkv_last_error(void);

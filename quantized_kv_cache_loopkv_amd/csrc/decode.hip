@@ -708,15 +708,30 @@ struct Smem {
 };
 
 // ----------------------------------------------------------------------------- row body
-template <int D, int MODE, bool SPARSE>
-__device__ void row_body(const DecodeArgs& a, const Row& r, const Smem& sm, size_t orow) {
+// Phases: PH_ROW runs a whole row in one workgroup. A split decode runs PH_PART on each of
+// n_split workgroups of a row (a range of its chunks; the last one also takes the tail) and
+// writes a partial (m, l, o) plus, when the row selects, its coarse scores; PH_FINISH then
+// merges the partials of the row, selects, corrects the selected tokens and writes the row.
+enum : int { PH_ROW = 0, PH_PART = 1, PH_FINISH = 2 };
+
+// Chunk range [cb, ce) of split `split` over a row of n_chunks chunks: equal shares rounded
+// up to a multiple of the waves of a workgroup, so every wave gets the same step count.
+__device__ inline void split_range(int n_chunks, int n_split, int split, int& cb, int& ce) {
+  const int per = ((n_chunks + n_split - 1) / n_split + kWaves - 1) / kWaves * kWaves;
+  cb = min(n_chunks, split * per);
+  ce = min(n_chunks, cb + per);
+}
+
+template <int D, int MODE, bool SPARSE, int PH>
+__device__ void row_body(const DecodeArgs& a, const Row& r, const Smem& sm, size_t orow, int split) {
   using G = Geo<D, MODE>;
   using KS = KStep<D, MODE, false>;
   using VS = VStep<D, MODE>;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   float* scr = sm.wscr + w * kWaveScratch;
   uint32_t* klimb = reinterpret_cast<uint32_t*>(scr);
-  float* scores = sm.scores;
+  // coarse scores: LDS for a whole row, the row's scratch line for a split one
+  float* scores = (SPARSE && PH != PH_ROW) ? a.part_scores + orow * (size_t)a.split_row_stride : sm.scores;
   uint32_t* selm = sm.selm;
   float* misc = sm.misc;
   constexpr int NE = G::NE;
@@ -731,14 +746,16 @@ __device__ void row_body(const DecodeArgs& a, const Row& r, const Smem& sm, size
   // steps (chunks of TPS tokens) w, w + 8, ...; the loads of the next step are in flight
   // while a step computes
   const int nb = r.n_q / kBlock;
-  const int n_chunks = (r.n_q + G::TPS - 1) / G::TPS;
-  const int steps = (n_chunks + kWaves - 1) / kWaves;
+  int cb = 0, n_chunks = (r.n_q + G::TPS - 1) / G::TPS;   // this workgroup's chunks: [cb, n_chunks)
+  if constexpr (PH == PH_PART) split_range(n_chunks, a.n_split, split, cb, n_chunks);
+  if constexpr (PH == PH_FINISH) n_chunks = 0;
+  const int steps = (n_chunks - cb + kWaves - 1) / kWaves;
   typename KS::Buf kb0, kb1;
   typename VS::Buf vb0, vb1;
   // K loads of step s + 1 are issued as step s starts, its V loads once step s's K part is
   // done: each load has about one step of lead while at most three buffers are live.
   auto issue_k = [&](int s, typename KS::Buf& kb) {
-    const int c = s * kWaves + w;
+    const int c = cb + s * kWaves + w;
     if (c >= n_chunks) return;   // no chunk for this wave (uniform)
     int groups[2];
 #pragma unroll
@@ -749,12 +766,12 @@ __device__ void row_body(const DecodeArgs& a, const Row& r, const Smem& sm, size
     KS::load(r, groups, lane, kb);
   };
   auto issue_v = [&](int s, typename VS::Buf& vb) {
-    const int c = s * kWaves + w;
+    const int c = cb + s * kWaves + w;
     if (c >= n_chunks) return;
     VS::load(r, c * G::BPS, nb, lane, vb);
   };
   auto step_k = [&](int s, const typename KS::Buf& kb) -> float {
-    const int c = s * kWaves + w;
+    const int c = cb + s * kWaves + w;
     if (c >= n_chunks) return 0.f;
     bool own;
     int t_loc;
@@ -773,7 +790,7 @@ __device__ void row_body(const DecodeArgs& a, const Row& r, const Smem& sm, size
     return wgt;
   };
   auto step_v = [&](int s, const typename VS::Buf& vb, float wgt) {
-    const int c = s * kWaves + w;
+    const int c = cb + s * kWaves + w;
     if (c >= n_chunks) return;
     VS::compute(wgt, scr + G::S_W, scr, lane, vb, st);
     wave_sync_lds();
@@ -797,7 +814,8 @@ __device__ void row_body(const DecodeArgs& a, const Row& r, const Smem& sm, size
   float tacc[D / 64];
 #pragma unroll
   for (int i = 0; i < D / 64; ++i) tacc[i] = 0.f;
-  for (int t = r.n_q + w; t < r.N; t += kWaves) {
+  const bool has_tail = PH == PH_ROW || (PH == PH_PART && split == a.n_split - 1);
+  for (int t = r.n_q + w; has_tail && t < r.N; t += kWaves) {
     const uint16_t* kt = r.tail + (size_t)(t % kGroup) * D;
     float p = 0.f;
 #pragma unroll
@@ -817,18 +835,28 @@ __device__ void row_body(const DecodeArgs& a, const Row& r, const Smem& sm, size
   }
 
   // ---- selection (4-bit target, 0 < tau <= 1) and corrections
-  if constexpr (SPARSE) {
-    const float lw = wave_sum(st.lsum);
-    if (lane == 0) {
-      misc[w] = st.m;
-      misc[8 + w] = lw;
+  bool use_parts = true;   // PH_FINISH: the partials hold the row's streamed part
+  if constexpr (SPARSE && PH != PH_PART) {
+    float M = -INFINITY, L = 0.f;   // the row's coarse maximum and weight
+    if constexpr (PH == PH_FINISH) {
+      const float* pp = a.part + orow * (size_t)a.n_split * (2 + D);
+      for (int i = 0; i < a.n_split; ++i) M = fmaxf(M, pp[(size_t)i * (2 + D)]);
+      for (int i = 0; i < a.n_split; ++i) {
+        const float mi = pp[(size_t)i * (2 + D)];
+        if (mi > -INFINITY) L += pp[(size_t)i * (2 + D) + 1] * __expf(mi - M);
+      }
+    } else {
+      const float lw = wave_sum(st.lsum);
+      if (lane == 0) {
+        misc[w] = st.m;
+        misc[8 + w] = lw;
+      }
+      __syncthreads();
+      M = misc[0];
+      for (int i = 1; i < kWaves; ++i) M = fmaxf(M, misc[i]);
+      for (int i = 0; i < kWaves; ++i)
+        if (misc[i] > -INFINITY) L += misc[8 + i] * __expf(misc[i] - M);
     }
-    __syncthreads();
-    float M = misc[0];
-    for (int i = 1; i < kWaves; ++i) M = fmaxf(M, misc[i]);
-    float L = 0.f;
-    for (int i = 0; i < kWaves; ++i)
-      if (misc[i] > -INFINITY) L += misc[8 + i] * __expf(misc[i] - M);
     if (st.m > -INFINITY) {
       const float f = st.raise(M);
 #pragma unroll
@@ -951,7 +979,9 @@ __device__ void row_body(const DecodeArgs& a, const Row& r, const Smem& sm, size
       Lp += misc[8 + i] * f;
       Rm += misc[16 + i] * f;
     }
+    if (PH == PH_FINISH) Lp += L * __expf(M - Ms);   // the streamed part's coarse weight
     if (Rm > 1024.f * Lp) {   // recompute the row's V from the final scores
+      use_parts = false;
       __syncthreads();
       float ls = 0.f;
       for (int t = tid; t < r.N; t += kThreads) {
@@ -972,7 +1002,7 @@ __device__ void row_body(const DecodeArgs& a, const Row& r, const Smem& sm, size
         for (int i = 0; i < D / 64; ++i) tacc[i] = fmaf(scores[t], bf16f(vt[lane + 64 * i]), tacc[i]);
       }
     }
-  } else {
+  } else if constexpr (PH != PH_PART) {
     if (a.sel_mask) {
       const uint32_t fill = (MODE == MODE_DENSE || MODE == MODE_KIVI) ? 0xffffffffu : 0u;
       uint32_t* smo = a.sel_mask + orow * (size_t)a.sel_words;
@@ -996,9 +1026,16 @@ __device__ void row_body(const DecodeArgs& a, const Row& r, const Smem& sm, size
   __syncthreads();
   float M = misc[0];
   for (int i = 1; i < kWaves; ++i) M = fmaxf(M, misc[i]);
+  const float* parts = nullptr;   // PH_FINISH: the row's partials, unless the exact pass replaced them
+  if constexpr (PH == PH_FINISH) {
+    if (use_parts) {
+      parts = a.part + orow * (size_t)a.n_split * (2 + D);
+      for (int i = 0; i < a.n_split; ++i) M = fmaxf(M, parts[(size_t)i * (2 + D)]);
+    }
+  }
   const float fw = st.m > -INFINITY ? __expf(st.m - M) : 0.f;
-  float* red = scores;                         // [kThreads][VCH]
-  float* tred = scores + kThreads * VCH;       // [kWaves][D]
+  float* red = sm.scores;                      // [kThreads][VCH]
+  float* tred = sm.scores + kThreads * VCH;    // [kWaves][D]
 #pragma unroll
   for (int c = 0; c < VCH; ++c) red[tid * VCH + c] = st.acc[c] * fw;
 #pragma unroll
@@ -1011,6 +1048,11 @@ __device__ void row_body(const DecodeArgs& a, const Row& r, const Smem& sm, size
     fws[i] = misc[i] > -INFINITY ? __expf(misc[i] - M) : 0.f;
     Lt += misc[8 + i] * fws[i];
   }
+  if (parts)
+    for (int i = 0; i < a.n_split; ++i) {
+      const float mi = parts[(size_t)i * (2 + D)];
+      if (mi > -INFINITY) Lt += parts[(size_t)i * (2 + D) + 1] * __expf(mi - M);
+    }
   for (int d = tid; d < D; d += kThreads) {
     const int chunk = d / VCH, c = d % VCH;
     float o = 0.f;
@@ -1020,6 +1062,20 @@ __device__ void row_body(const DecodeArgs& a, const Row& r, const Smem& sm, size
 #pragma unroll
       for (int vb = 0; vb < G::BPS; ++vb) o += red[(ww * 64 + vb * G::LPB + chunk) * VCH + c];
       o += tred[ww * D + d];
+    }
+    if (parts)
+      for (int i = 0; i < a.n_split; ++i) {
+        const float mi = parts[(size_t)i * (2 + D)];
+        if (mi > -INFINITY) o = fmaf(parts[(size_t)i * (2 + D) + 2 + d], __expf(mi - M), o);
+      }
+    if constexpr (PH == PH_PART) {   // unnormalized, relative to M
+      float* pp = a.part + (orow * (size_t)a.n_split + split) * (2 + D);
+      if (d == 0) {
+        pp[0] = M;
+        pp[1] = Lt;
+      }
+      pp[2 + d] = o;
+      continue;
     }
     o = o / Lt;
     if (a.out_bf16) {
@@ -1049,10 +1105,12 @@ __host__ __device__ inline size_t decode_lds_floats(int max_len, int D) {
 // run the 2-bit path inside every planes variant.
 enum : int { VAR_KIVI = 0, VAR_DENSE = 1, VAR_COARSE = 2, VAR_SPARSE = 3 };
 
-template <int D, int VAR>
+template <int D, int VAR, int PH>
 __global__ void __launch_bounds__(kThreads, kWavesPerSimd) k_decode(DecodeArgs a) {
   extern __shared__ float smem[];
-  const int row = blockIdx.x;
+  // PH_PART: workgroup (row, split), the splits of a row adjacent
+  const int row = PH == PH_PART ? blockIdx.x / a.n_split : blockIdx.x;
+  const int split = PH == PH_PART ? blockIdx.x % a.n_split : 0;
   const int h = row % a.n_heads;
   const int b = (row / a.n_heads) % a.n_seqs;
   const int ci = row / (a.n_heads * a.n_seqs);
@@ -1072,6 +1130,7 @@ __global__ void __launch_bounds__(kThreads, kWavesPerSimd) k_decode(DecodeArgs a
   sm.misc = sm.wscr + kWaves * kWaveScratch;
 
   if (N <= 0 || N > a.max_len) {
+    if (PH == PH_PART) return;   // the finishing launch writes the row
     const float v = N == 0 ? 0.f : __builtin_nanf("");
     for (int d = tid; d < D; d += kThreads) {
       if (a.out_bf16) reinterpret_cast<uint16_t*>(a.out)[orow * D + d] = N == 0 ? 0 : 0x7fc0;
@@ -1104,25 +1163,36 @@ __global__ void __launch_bounds__(kThreads, kWavesPerSimd) k_decode(DecodeArgs a
   __syncthreads();
 
   if constexpr (VAR == VAR_KIVI) {
-    row_body<D, MODE_KIVI, false>(a, r, sm, orow);
+    row_body<D, MODE_KIVI, false, PH>(a, r, sm, orow, split);
   } else {
-    if (cell.kind == KIND_Q2) row_body<D, MODE_Q2, false>(a, r, sm, orow);
-    else if (VAR == VAR_DENSE) row_body<D, MODE_DENSE, false>(a, r, sm, orow);
-    else if (VAR == VAR_COARSE) row_body<D, MODE_COARSE, false>(a, r, sm, orow);
-    else row_body<D, MODE_COARSE, true>(a, r, sm, orow);
+    if (cell.kind == KIND_Q2) row_body<D, MODE_Q2, false, PH>(a, r, sm, orow, split);
+    else if (VAR == VAR_DENSE) row_body<D, MODE_DENSE, false, PH>(a, r, sm, orow, split);
+    else if (VAR == VAR_COARSE) row_body<D, MODE_COARSE, false, PH>(a, r, sm, orow, split);
+    else row_body<D, MODE_COARSE, true, PH>(a, r, sm, orow, split);
   }
 }
 
 size_t decode_lds_bytes(int max_len, int head_dim) { return decode_lds_floats(max_len, head_dim) * 4; }
 
-template <int D, int VAR>
-static void launch_variant(const DecodeArgs& a, size_t rows, size_t lds, hipStream_t stream) {
+template <int D, int VAR, int PH>
+static void launch_phase(const DecodeArgs& a, size_t grid, size_t lds, hipStream_t stream) {
   static bool attr_set = false;
   if (!attr_set) {
-    (void)hipFuncSetAttribute((const void*)k_decode<D, VAR>, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    (void)hipFuncSetAttribute((const void*)k_decode<D, VAR, PH>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              160 * 1024);
     attr_set = true;
   }
-  hipLaunchKernelGGL((k_decode<D, VAR>), dim3((unsigned)rows), dim3(kThreads), lds, stream, a);
+  hipLaunchKernelGGL((k_decode<D, VAR, PH>), dim3((unsigned)grid), dim3(kThreads), lds, stream, a);
+}
+
+template <int D, int VAR>
+static void launch_variant(const DecodeArgs& a, size_t rows, size_t lds, hipStream_t stream) {
+  if (a.n_split < 1) {
+    launch_phase<D, VAR, PH_ROW>(a, rows, lds, stream);
+  } else {   // stream order: every partial is written before the finishing launch reads it
+    launch_phase<D, VAR, PH_PART>(a, rows * (size_t)a.n_split, lds, stream);
+    launch_phase<D, VAR, PH_FINISH>(a, rows, lds, stream);
+  }
 }
 
 template <int D>

@@ -74,7 +74,19 @@ struct DecodeArgs {
   int32_t q_bf16, out_bf16;
   int32_t n_seqs, n_heads, bt_stride, max_len, sel_words, n_cells;
   float tau, sm_scale;
+  // Split of each row's tokens over n_split workgroups (n_split 0: one workgroup per row).
+  // part: [rows][n_split][2 + D] floats (m, l, unnormalized o relative to m);
+  // part_scores: [rows][split_row_stride] coarse scores (4-bit targets, 0 < tau <= 1).
+  int32_t n_split, split_row_stride;
+  float* part;
+  float* part_scores;
   DecodeCell cells[kMaxCells];
 };
+
+// Scratch of a split decode, in floats: partials, then one score row per decoded row.
+__host__ __device__ inline size_t split_row_stride(int max_len) { return ((size_t)max_len + 63) / 64 * 64; }
+__host__ __device__ inline size_t split_scratch_floats(size_t rows, int n_split, int max_len, int D) {
+  return rows * (size_t)n_split * (size_t)(2 + D) + rows * split_row_stride(max_len);
+}
 
 }  // namespace lkv

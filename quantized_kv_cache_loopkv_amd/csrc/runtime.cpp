@@ -229,11 +229,15 @@ loopkv_status loopkv_append(loopkv_ctx* c, hipStream_t stream, int32_t loop, int
   return ok();
 }
 
-loopkv_status loopkv_decode_attn(loopkv_ctx* c, hipStream_t stream, int32_t loop, int32_t layer, const void* q,
-                                 int32_t q_dtype, int32_t n_seqs, const int32_t* seq_slots,
-                                 const int32_t* block_table, int32_t bt_stride, const int32_t* seq_lens,
-                                 int32_t max_len, float tau, float sm_scale, void* out, int32_t out_dtype,
-                                 uint32_t* sel_mask) {
+}  // extern "C"
+
+namespace {
+// Shared by the one-workgroup-per-row decode (n_split 0) and the split decode.
+loopkv_status decode_common(loopkv_ctx* c, hipStream_t stream, int32_t loop, int32_t layer, const void* q,
+                            int32_t q_dtype, int32_t n_seqs, const int32_t* seq_slots, const int32_t* block_table,
+                            int32_t bt_stride, const int32_t* seq_lens, int32_t max_len, float tau, float sm_scale,
+                            void* out, int32_t out_dtype, uint32_t* sel_mask, int32_t n_split, void* scratch,
+                            size_t scratch_bytes) {
   loopkv_status s = check_ready(c);
   if (s != LOOPKV_OK) return s;
   int first, count;
@@ -252,6 +256,16 @@ loopkv_status loopkv_decode_attn(loopkv_ctx* c, hipStream_t stream, int32_t loop
     return fail(LOOPKV_ERR_CAPACITY, "max_len %d outside [0, %d]", max_len, LOOPKV_MAX_LEN);
   if (bt_stride < 1 || (long long)bt_stride * lkv::kBlock < max_len)
     return fail(LOOPKV_ERR_CAPACITY, "bt_stride %d too small for max_len %d", bt_stride, max_len);
+  if (n_split != 0) {
+    if (n_split < 1 || n_split > LOOPKV_MAX_SPLIT)
+      return fail(LOOPKV_ERR_INVALID_ARG, "n_split %d outside [1, %d]", n_split, LOOPKV_MAX_SPLIT);
+    if (n_seqs > 0 && (!scratch || ((uintptr_t)scratch & 15u) != 0))
+      return fail(LOOPKV_ERR_WORKSPACE, "split scratch is null or not 16-byte aligned");
+    const size_t need = lkv::split_scratch_floats((size_t)count * n_seqs * c->cfg.n_heads, n_split, max_len,
+                                                  c->cfg.head_dim) * sizeof(float);
+    if (n_seqs > 0 && scratch_bytes < need)
+      return fail(LOOPKV_ERR_WORKSPACE, "split scratch of %zu bytes, this call needs %zu", scratch_bytes, need);
+  }
   if (n_seqs == 0) return ok();
   if (!q || !out || !block_table || !seq_lens) return fail(LOOPKV_ERR_INVALID_ARG, "null device pointer");
   lkv::DecodeArgs a;
@@ -273,6 +287,13 @@ loopkv_status loopkv_decode_attn(loopkv_ctx* c, hipStream_t stream, int32_t loop
   a.n_cells = count;
   a.tau = tau;
   a.sm_scale = sm_scale;
+  a.n_split = n_split;
+  if (n_split > 0) {
+    const size_t rows = (size_t)count * n_seqs * c->cfg.n_heads;
+    a.split_row_stride = (int32_t)lkv::split_row_stride(max_len);
+    a.part = static_cast<float*>(scratch);
+    a.part_scores = a.part + rows * (size_t)n_split * (2 + c->cfg.head_dim);
+  }
   for (int i = 0; i < count; ++i) {
     const int st = c->storage[first + i];
     a.cells[i].pool_off = c->pool_off[st];
@@ -282,6 +303,45 @@ loopkv_status loopkv_decode_attn(loopkv_ctx* c, hipStream_t stream, int32_t loop
   hipError_t e = lkv::launch_decode(a, c->cfg.head_dim, stream);
   if (e != hipSuccess) return fail(LOOPKV_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
   return ok();
+}
+}  // namespace
+
+extern "C" {
+
+loopkv_status loopkv_decode_attn(loopkv_ctx* c, hipStream_t stream, int32_t loop, int32_t layer, const void* q,
+                                 int32_t q_dtype, int32_t n_seqs, const int32_t* seq_slots,
+                                 const int32_t* block_table, int32_t bt_stride, const int32_t* seq_lens,
+                                 int32_t max_len, float tau, float sm_scale, void* out, int32_t out_dtype,
+                                 uint32_t* sel_mask) {
+  return decode_common(c, stream, loop, layer, q, q_dtype, n_seqs, seq_slots, block_table, bt_stride, seq_lens,
+                       max_len, tau, sm_scale, out, out_dtype, sel_mask, 0, nullptr, 0);
+}
+
+loopkv_status loopkv_split_scratch_bytes(const loopkv_ctx* c, int32_t loop, int32_t layer, int32_t n_seqs,
+                                         int32_t max_len, int32_t n_split, size_t* bytes) {
+  if (!c || !bytes) return fail(LOOPKV_ERR_INVALID_ARG, "null argument");
+  if (!c->has_plan) return fail(LOOPKV_ERR_PLAN, "no plan loaded");
+  int first, count;
+  loopkv_status s = resolve_cells(c, loop, layer, &first, &count);
+  if (s != LOOPKV_OK) return s;
+  if (n_seqs < 0) return fail(LOOPKV_ERR_INVALID_ARG, "n_seqs must be >= 0");
+  if (max_len < 0 || max_len > LOOPKV_MAX_LEN)
+    return fail(LOOPKV_ERR_CAPACITY, "max_len %d outside [0, %d]", max_len, LOOPKV_MAX_LEN);
+  if (n_split < 1 || n_split > LOOPKV_MAX_SPLIT)
+    return fail(LOOPKV_ERR_INVALID_ARG, "n_split %d outside [1, %d]", n_split, LOOPKV_MAX_SPLIT);
+  *bytes = lkv::split_scratch_floats((size_t)count * n_seqs * c->cfg.n_heads, n_split, max_len, c->cfg.head_dim) *
+           sizeof(float);
+  return ok();
+}
+
+loopkv_status loopkv_decode_attn_split(loopkv_ctx* c, hipStream_t stream, int32_t loop, int32_t layer,
+                                       const void* q, int32_t q_dtype, int32_t n_seqs, const int32_t* seq_slots,
+                                       const int32_t* block_table, int32_t bt_stride, const int32_t* seq_lens,
+                                       int32_t max_len, float tau, float sm_scale, void* out, int32_t out_dtype,
+                                       uint32_t* sel_mask, int32_t n_split, void* scratch, size_t scratch_bytes) {
+  if (n_split == 0) return fail(LOOPKV_ERR_INVALID_ARG, "n_split %d outside [1, %d]", n_split, LOOPKV_MAX_SPLIT);
+  return decode_common(c, stream, loop, layer, q, q_dtype, n_seqs, seq_slots, block_table, bt_stride, seq_lens,
+                       max_len, tau, sm_scale, out, out_dtype, sel_mask, n_split, scratch, scratch_bytes);
 }
 
 }  // extern "C"

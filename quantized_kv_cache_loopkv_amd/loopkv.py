@@ -23,10 +23,11 @@ F32, BF16 = 0, 1
 LAYOUT_PLANES, LAYOUT_KIVI4 = 0, 1
 MAX_LEN = 32768
 MAX_CELLS = 128
+MAX_SPLIT = 64
 
 EXPORTED = ["loopkv_create", "loopkv_destroy", "loopkv_plan", "loopkv_workspace_bytes",
             "loopkv_bind_workspace", "loopkv_cell_storage", "loopkv_append", "loopkv_decode_attn",
-            "loopkv_last_error"]
+            "loopkv_split_scratch_bytes", "loopkv_decode_attn_split", "loopkv_last_error"]
 
 
 class LoopKVError(RuntimeError):
@@ -63,10 +64,14 @@ def lib():
                                       ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(i32)]
     L.loopkv_append.argtypes = [vp, vp, i32, i32, vp, vp, i32, i32, i32, vp, vp, i32, vp]
     L.loopkv_decode_attn.argtypes = [vp, vp, i32, i32, vp, i32, i32, vp, vp, i32, vp, i32, f32, f32, vp, i32, vp]
+    L.loopkv_split_scratch_bytes.argtypes = [vp, i32, i32, i32, i32, i32, ctypes.POINTER(ctypes.c_size_t)]
+    L.loopkv_decode_attn_split.argtypes = [vp, vp, i32, i32, vp, i32, i32, vp, vp, i32, vp, i32, f32, f32, vp, i32,
+                                           vp, i32, vp, ctypes.c_size_t]
     L.loopkv_last_error.restype = ctypes.c_char_p
     L.loopkv_last_error.argtypes = []
     for name in ["loopkv_create", "loopkv_plan", "loopkv_workspace_bytes", "loopkv_bind_workspace",
-                 "loopkv_cell_storage", "loopkv_append", "loopkv_decode_attn"]:
+                 "loopkv_cell_storage", "loopkv_append", "loopkv_decode_attn", "loopkv_split_scratch_bytes",
+                 "loopkv_decode_attn_split"]:
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -179,10 +184,20 @@ class Context:
         _check(lib().loopkv_append(self._h, _stream(), loop, layer, _ptr(k), _ptr(v), _dtype_code(k), n_seqs, n_new,
                                    _ptr(seq_slots), _ptr(bt), bt_stride, _ptr(seq_lens)))
 
+    def split_scratch_bytes(self, n_seqs: int, max_len: int, n_split: int, cell=None) -> int:
+        loop, layer = self._cell(cell)
+        n = ctypes.c_size_t()
+        _check(lib().loopkv_split_scratch_bytes(self._h, loop, layer, int(n_seqs), int(max_len), int(n_split),
+                                                ctypes.byref(n)))
+        return n.value
+
     def decode(self, q: torch.Tensor, block_table: torch.Tensor, seq_lens: torch.Tensor, max_len: int,
                tau: float, sm_scale: Optional[float] = None, cell=None, out_dtype=torch.float32,
-               out: Optional[torch.Tensor] = None, sel_mask=False, seq_slots: Optional[torch.Tensor] = None):
-        """q: [cells][n_seqs][H][D] (cell=None) or [n_seqs][H][D]. Returns out (and sel_mask if asked)."""
+               out: Optional[torch.Tensor] = None, sel_mask=False, seq_slots: Optional[torch.Tensor] = None,
+               n_split: int = 0, scratch: Optional[torch.Tensor] = None):
+        """q: [cells][n_seqs][H][D] (cell=None) or [n_seqs][H][D]. Returns out (and sel_mask if asked).
+        n_split > 0 splits each row over that many workgroups (loopkv_decode_attn_split); scratch is
+        then a CUDA tensor of at least split_scratch_bytes() bytes (allocated here if None)."""
         loop, layer = self._cell(cell)
         if not q.is_contiguous():
             raise ValueError("q must be contiguous")
@@ -205,9 +220,21 @@ class Context:
         _dev_i32(seq_lens, "seq_lens", n_seqs)
         _dev_i32(seq_slots, "seq_slots", n_seqs)
         bt_stride = bt.shape[-1] if bt.dim() == 2 else bt.numel()
-        _check(lib().loopkv_decode_attn(self._h, _stream(), loop, layer, _ptr(q), _dtype_code(q), n_seqs,
-                                        _ptr(seq_slots), _ptr(bt), bt_stride, _ptr(seq_lens), int(max_len),
-                                        float(tau), float(sm_scale), _ptr(out), _dtype_code(out), _ptr(sm)))
+        if n_split:
+            if scratch is None:
+                scratch = torch.empty(self.split_scratch_bytes(n_seqs, max_len, n_split, cell), dtype=torch.uint8,
+                                      device=q.device)
+            if not scratch.is_cuda or not scratch.is_contiguous():
+                raise ValueError("scratch must be a contiguous CUDA tensor")
+            _check(lib().loopkv_decode_attn_split(self._h, _stream(), loop, layer, _ptr(q), _dtype_code(q), n_seqs,
+                                                  _ptr(seq_slots), _ptr(bt), bt_stride, _ptr(seq_lens), int(max_len),
+                                                  float(tau), float(sm_scale), _ptr(out), _dtype_code(out), _ptr(sm),
+                                                  int(n_split), _ptr(scratch),
+                                                  scratch.numel() * scratch.element_size()))
+        else:
+            _check(lib().loopkv_decode_attn(self._h, _stream(), loop, layer, _ptr(q), _dtype_code(q), n_seqs,
+                                            _ptr(seq_slots), _ptr(bt), bt_stride, _ptr(seq_lens), int(max_len),
+                                            float(tau), float(sm_scale), _ptr(out), _dtype_code(out), _ptr(sm)))
         if sm is not None:
             return out, sm
         return out

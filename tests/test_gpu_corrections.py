@@ -40,8 +40,9 @@ def _bf16(x):
     return torch.tensor(np.asarray(x, dtype=np.float32)).to(torch.bfloat16)
 
 
-def _decode_one(K, V, q, tau):
-    """Append K, V ([N][D] bf16 tensors, one head) to a fresh one-cell 4-bit cache and decode q."""
+def _decode_one(K, V, q, tau, n_split=0):
+    """Append K, V ([N][D] bf16 tensors, one head) to a fresh one-cell 4-bit cache and decode q
+    (n_split > 0: the split decode)."""
     N, D = K.shape
     nb = N // 16 + 2
     ctx = lkv.Context(1, 1, 1, D, nb, 1)
@@ -54,14 +55,14 @@ def _decode_one(K, V, q, tau):
                cell=(0, 0))
     lens = torch.full((1,), N, dtype=torch.int32, device="cuda")
     qd = torch.tensor(np.asarray(q, dtype=np.float32)).view(1, 1, D).cuda()
-    out, sm = ctx.decode(qd, bt, lens, N, tau, cell=(0, 0), sel_mask=True)
+    out, sm = ctx.decode(qd, bt, lens, N, tau, cell=(0, 0), sel_mask=True, n_split=n_split)
     torch.cuda.synchronize()
     return out.view(D).cpu().numpy(), sm.view(-1).cpu().numpy()
 
 
-def _check(K, V, q, tau, label):
+def _check(K, V, q, tau, label, n_split=0):
     N, D = K.shape
-    o_gpu, sm = _decode_one(K, V, q, tau)
+    o_gpu, sm = _decode_one(K, V, q, tau, n_split)
     Kd, Vd = K.float().numpy().astype(np.float64), V.float().numpy().astype(np.float64)
     sig = float(np.float32(1.0 / math.sqrt(D)))
     o_ref, sel_ref, phat = O.decode_row(np.asarray(q, np.float64), Kd, Vd, O.KIND_Q4, tau, sig)

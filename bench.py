@@ -13,6 +13,11 @@ the method must move / step time); ``roofline`` is the decode kernel's
 algorithmic bytes per launch over its mean duration (HIP events on the launch
 stream) against the 8 TB/s HBM peak; ``cpu_baseline`` times the fp64 oracle on a
 few sampled rows of the same workload on the host.
+
+Extra fields: the tau sweep, the KIVI-4 layout on the same kernel, a read-ceiling probe, and
+the per-(loop, layer) serving order under a graph (each cell appends its token and decodes in
+turn, as a looped model calls it): at batch 32 beside the whole-plan step, and at batch 1 with
+the split decode (each row over n_split workgroups) against one workgroup per row.
 """
 from __future__ import annotations
 
@@ -28,6 +33,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
+SERVING_WARM, SERVING_REPS = 2, 5     # graph replays of the per-(loop, layer) legs
+SERVING_SPLITS = (0, 8, 16, 32)       # workgroups per row tried at batch 1
 COUNTERS = os.path.join(ROOT, "profiles", "k_decode_c4_tau0.01_counters.json")
 KERNEL_SOURCES = ["quantized_kv_cache_loopkv_amd/csrc/decode.hip", "quantized_kv_cache_loopkv_amd/csrc/layout.h"]
 
@@ -167,6 +174,47 @@ def cpu_baseline(cfg, plan, tau, rows, log, min_seconds=10.0, max_evals=400):
                       f"algorithmic bytes / oracle time"}
 
 
+def serving_graph(wl, q, tau, first_step, n_rep, n_split, log, warm=2):
+    """Per-(loop, layer) serving order (each cell: append the new token, decode the cell) captured
+    once in a graph and replayed; returns the mean and per-replay ms. Appends n_rep + warm tokens."""
+    import torch
+    cfg = wl.cfg
+    C, B, H, D = cfg.n_cells, cfg.batch, cfg.n_heads, cfg.head_dim
+    max_len = cfg.max_len
+    stream = torch.cuda.current_stream()
+    K0, V0, before, _ = wl.append_inputs(first_step)
+    sK, sV = K0.clone(), V0.clone()
+    lb = before.clone()
+    la = lb + 1
+    out = torch.empty((C, B, H, D), dtype=torch.bfloat16, device="cuda")
+    scratch = None
+    if n_split:
+        scratch = torch.empty(wl.ctx.split_scratch_bytes(B, max_len, n_split, cell=(0, 0)), dtype=torch.uint8,
+                              device="cuda")
+    # one read-only decode first: one-time launch attributes are set outside the capture
+    wl.ctx.decode(q[0], wl.bt, la, max_len, tau, cell=(0, 0), out=out[0], n_split=n_split, scratch=scratch)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        wl.serving_step(sK, sV, q, lb, la, max_len, tau, out, n_split=n_split, scratch=scratch)
+    torch.cuda.synchronize()
+    ms = []
+    for k in range(warm + n_rep):
+        if k > 0:
+            K, V, _, _ = wl.append_inputs(first_step + k)
+            sK.copy_(K)
+            sV.copy_(V)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        if k >= warm:
+            ms.append(e0.elapsed_time(e1))
+    del g
+    return float(sum(ms) / len(ms)), ms
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -178,6 +226,8 @@ def main():
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-kivi", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-serving", action="store_true",
+                    help="skip the per-(loop, layer) graph legs (batch 32 and batch 1)")
     ap.add_argument("--cpu-rows", type=int, default=6)
     ap.add_argument("--table", choices=["shuffled", "identity"], default="shuffled",
                     help="block table of the workload (the configuration uses a shuffled one)")
@@ -208,10 +258,11 @@ def main():
     torch.cuda.set_device(0)
     lkv.lib()
     S = args.warmup + args.steps
+    GS = 0 if args.no_serving else SERVING_WARM + SERVING_REPS   # tokens the serving leg appends
     cfg = R.make_config("C4")
     cfg.batch = args.batch
     cfg.lengths = [args.ctx - S] * args.batch
-    cfg.append_steps = S
+    cfg.append_steps = S + GS
     cfg.shuffled = args.table == "shuffled"
     plan = cfg.plan.reshape(-1)
     H, D, C, B = cfg.n_heads, cfg.head_dim, cfg.n_cells, cfg.batch
@@ -288,6 +339,33 @@ def main():
                                "GBps": round(bts / (ms * 1e-3) / 1e9, 1), "selected": int(ct.sum())}
             log(f"tau={tau}: {ms:.3f} ms, {bts / 1e9:.2f} GB, {bts / (ms * 1e-3) / 1e9:.0f} GB/s")
         extra["tau_sweep"] = sweep
+    if not args.no_serving:
+        # the same cache in the order a looped model calls it (96 cells one by one), under a graph
+        ms, per = serving_graph(wl, q, args.tau, S, SERVING_REPS, 0, log, warm=SERVING_WARM)
+        extra["per_cell_graph"] = {
+            "batch": B, "context": f"{args.ctx}..{args.ctx + GS}", "ms_per_step": round(ms, 4),
+            "whole_plan_ms_per_step": round(float(np.mean(step_ms)), 4),
+            "ratio_to_whole_plan": round(ms / float(np.mean(step_ms)), 4),
+            "launches_per_step": 2 * n_storing + C + 2}
+        log(f"per-cell graph, batch {B}: {ms:.3f} ms per step vs whole plan {np.mean(step_ms):.3f} ms")
+        # one sequence: the per-cell launches hold 16 rows each, so the split decode fills the GPU
+        scfg = R.make_config("C4")
+        scfg.batch = 1
+        scfg.lengths = [args.ctx]
+        scfg.append_steps = len(SERVING_SPLITS) * (SERVING_WARM + SERVING_REPS)
+        sw = Workload(scfg, gpu_synth=True, log=log)
+        sw.fill()
+        sq = sw.q_all()
+        small = {"batch": 1, "context": args.ctx}
+        first = 0
+        for ns in SERVING_SPLITS:
+            ms1, _ = serving_graph(sw, sq, args.tau, first, SERVING_REPS, ns, log, warm=SERVING_WARM)
+            first += SERVING_WARM + SERVING_REPS
+            small[f"ms_per_step_split{ns}"] = round(ms1, 4)
+            log(f"per-cell graph, batch 1, n_split {ns}: {ms1:.3f} ms per step")
+        extra["per_cell_graph_batch1"] = small
+        del sw
+        torch.cuda.empty_cache()
     if not args.no_kivi:
         kcfg = R.make_config("C4")
         kcfg.batch = B
@@ -335,7 +413,7 @@ def main():
         ccfg = R.make_config("C4")
         ccfg.batch = B
         ccfg.lengths = [args.ctx - S] * B     # the initial histories of the timed workload
-        ccfg.append_steps = S
+        ccfg.append_steps = S + GS
         cpu = cpu_baseline(ccfg, plan, args.tau, rows, log)
 
     line = {

@@ -163,8 +163,9 @@ loopkv_status loopkv_decode_attn(loopkv_ctx* ctx, hipStream_t stream, int32_t lo
                                  uint32_t* sel_mask);
 
 /* Scratch bytes a split decode of this (loop, layer) ((-1, -1): whole plan) needs for
- * n_seqs sequences, max_len and n_split (1..LOOPKV_MAX_SPLIT): per row, n_split partials
- * of (2 + head_dim) floats and one line of ceil(max_len/64)*64 coarse scores. */
+ * n_seqs sequences, max_len and n_split (1..LOOPKV_MAX_SPLIT): n_split partials of
+ * (2 + head_dim) floats per row (the region rounded up to 64 floats), then one line of
+ * ceil(max_len/64)*64 coarse scores per row. */
 loopkv_status loopkv_split_scratch_bytes(const loopkv_ctx* ctx, int32_t loop, int32_t layer,
                                          int32_t n_seqs, int32_t max_len, int32_t n_split,
                                          size_t* bytes);

@@ -13,11 +13,17 @@
 // All of it in float64 with one round-to-nearest-even to f16, so codes and
 // meta are reproducible bit for bit. Built with -ffp-contract=off.
 //
-// Two kernels per append, on the caller's stream:
-//   k_quantize_groups  one workgroup per (group slot, head, cell x sequence):
+// Appends of fewer than 32 tokens per sequence (decode time) take one kernel:
+//   k_quantize_groups<D, true>  one workgroup per (head, cell x sequence): reads the
+//                      old tail of the group this append completes (if any) into LDS,
+//                      writes the new tokens that stay in the tail once every read of
+//                      the old tail is done, then quantizes the completed group and
+//                      writes the records of its two 16-token blocks through the
+//                      block table.
+// Longer appends (a prefill) take two, on the caller's stream:
+//   k_quantize_groups<D, false> one workgroup per (group slot, head, cell x sequence):
 //                      gathers the 32 tokens of a group completed by this append
-//                      (old tail + new input), quantizes, writes the records of
-//                      its two 16-token blocks through the block table;
+//                      (old tail + new input), quantizes, writes its records;
 //   k_write_tail       copies the new tokens of the last, incomplete group into
 //                      the tail (after the first kernel has read the old tail).
 #include <hip/hip_runtime.h>
@@ -92,7 +98,35 @@ __device__ inline void quantize_group(Get get, int M, uint8_t* codes, int stride
 __device__ inline int kmeta_channel2(int i) { return (i & ~15) + 4 * (i & 3) + ((i >> 2) & 3); }
 __device__ inline int kmeta_channel4(int i) { return (i & ~7) + 2 * (i & 3) + ((i >> 2) & 1); }
 
+// The new tokens of (cell ci, sequence b, head h) that stay in the tail (those after the
+// last group the append completes), rounded from f32 if needed.
 template <int D>
+__device__ void write_tail_tokens(const AppendArgs& a, const AppendCell& cell, int b, int h, int L0) {
+  const int end = L0 + a.n_new;
+  const int first = max(L0, (end / kGroup) * kGroup);   // first position that stays in the tail
+  const int cnt = end - first;
+  if (cnt <= 0) return;
+  const int slot = a.seq_slots ? a.seq_slots[b] : b;
+  uint16_t* tail = reinterpret_cast<uint16_t*>(a.ws + cell.tail_off) + ((size_t)slot * a.n_heads + h) * tail_elems(D);
+  for (int idx = threadIdx.x; idx < cnt * D; idx += blockDim.x) {
+    const int i = idx / D, d = idx % D;
+    const int p = first + i;
+    const size_t e = ((((size_t)cell.in_cell * a.n_seqs + b) * a.n_new + (p - L0)) * a.n_heads + h) * D + d;
+    uint16_t kb, vb;
+    if (a.kv_bf16) {
+      kb = reinterpret_cast<const uint16_t*>(a.k)[e];
+      vb = reinterpret_cast<const uint16_t*>(a.v)[e];
+    } else {
+      kb = f32_to_bf16_rne(reinterpret_cast<const float*>(a.k)[e]);
+      vb = f32_to_bf16_rne(reinterpret_cast<const float*>(a.v)[e]);
+    }
+    tail[(0 * kGroup + (p % kGroup)) * D + d] = kb;
+    tail[(1 * kGroup + (p % kGroup)) * D + d] = vb;
+  }
+}
+
+// WITH_TAIL: the one-kernel append of fewer than 32 tokens (grid x = 1).
+template <int D, bool WITH_TAIL>
 __global__ void __launch_bounds__(256) k_quantize_groups(AppendArgs a) {
   const int b = blockIdx.z % a.n_seqs;
   const int ci = blockIdx.z / a.n_seqs;
@@ -100,7 +134,8 @@ __global__ void __launch_bounds__(256) k_quantize_groups(AppendArgs a) {
   const AppendCell cell = a.cells[ci];
   const int L0 = a.seq_lens[b];
   const int g = L0 / kGroup + (int)blockIdx.x;
-  if ((g + 1) * kGroup > L0 + a.n_new) return;
+  const bool complete = (g + 1) * kGroup <= L0 + a.n_new;   // uniform over the workgroup
+  if (!WITH_TAIL && !complete) return;
   const int slot = a.seq_slots ? a.seq_slots[b] : b;
   const int tid = threadIdx.x;
 
@@ -113,7 +148,7 @@ __global__ void __launch_bounds__(256) k_quantize_groups(AppendArgs a) {
 
   const uint16_t* tail = reinterpret_cast<const uint16_t*>(a.ws + cell.tail_off) +
                          ((size_t)slot * a.n_heads + h) * tail_elems(D);
-  for (int idx = tid; idx < kGroup * D; idx += blockDim.x) {
+  for (int idx = tid; complete && idx < kGroup * D; idx += blockDim.x) {
     const int i = idx / D, d = idx % D;
     const int p = g * kGroup + i;
     float kf, vf;
@@ -134,6 +169,10 @@ __global__ void __launch_bounds__(256) k_quantize_groups(AppendArgs a) {
     vx[i][d] = vf;
   }
   __syncthreads();
+  if constexpr (WITH_TAIL) {   // every read of the old tail is done (barrier above)
+    write_tail_tokens<D>(a, cell, b, h, L0);
+    if (!complete) return;
+  }
 
   const int M = (cell.kind == KIND_Q2) ? 3 : 15;
   // K: one group per channel over the 32 tokens.
@@ -214,45 +253,27 @@ template <int D>
 __global__ void __launch_bounds__(256) k_write_tail(AppendArgs a) {
   const int b = blockIdx.z % a.n_seqs;
   const int ci = blockIdx.z / a.n_seqs;
-  const int h = blockIdx.y;
-  const AppendCell cell = a.cells[ci];
-  const int L0 = a.seq_lens[b];
-  const int end = L0 + a.n_new;
-  const int first = max(L0, (end / kGroup) * kGroup);   // first position that stays in the tail
-  const int cnt = end - first;
-  if (cnt <= 0) return;
-  const int slot = a.seq_slots ? a.seq_slots[b] : b;
-  uint16_t* tail = reinterpret_cast<uint16_t*>(a.ws + cell.tail_off) + ((size_t)slot * a.n_heads + h) * tail_elems(D);
-  for (int idx = threadIdx.x; idx < cnt * D; idx += blockDim.x) {
-    const int i = idx / D, d = idx % D;
-    const int p = first + i;
-    const size_t e = ((((size_t)cell.in_cell * a.n_seqs + b) * a.n_new + (p - L0)) * a.n_heads + h) * D + d;
-    uint16_t kb, vb;
-    if (a.kv_bf16) {
-      kb = reinterpret_cast<const uint16_t*>(a.k)[e];
-      vb = reinterpret_cast<const uint16_t*>(a.v)[e];
-    } else {
-      kb = f32_to_bf16_rne(reinterpret_cast<const float*>(a.k)[e]);
-      vb = f32_to_bf16_rne(reinterpret_cast<const float*>(a.v)[e]);
-    }
-    tail[(0 * kGroup + (p % kGroup)) * D + d] = kb;
-    tail[(1 * kGroup + (p % kGroup)) * D + d] = vb;
+  write_tail_tokens<D>(a, a.cells[ci], b, blockIdx.y, a.seq_lens[b]);
+}
+
+template <int D>
+static void launch_d(const AppendArgs& a, hipStream_t stream) {
+  if (a.n_new < kGroup) {   // at most one group per (sequence, head) completes: one kernel
+    hipLaunchKernelGGL((k_quantize_groups<D, true>), dim3(1, a.n_heads, a.n_cells * a.n_seqs), dim3(256), 0, stream,
+                       a);
+    return;
   }
+  const int slots = a.n_new / kGroup + 1;   // groups one append can complete
+  hipLaunchKernelGGL((k_quantize_groups<D, false>), dim3(slots, a.n_heads, a.n_cells * a.n_seqs), dim3(256), 0,
+                     stream, a);
+  hipLaunchKernelGGL(k_write_tail<D>, dim3(1, a.n_heads, a.n_cells * a.n_seqs), dim3(256), 0, stream, a);
 }
 
 // Host launcher: quantize completed groups, then update tails (same stream).
 hipError_t launch_append(const AppendArgs& a, int head_dim, hipStream_t stream) {
   if (a.n_cells == 0 || a.n_seqs == 0 || a.n_new == 0) return hipSuccess;
-  const int slots = a.n_new / kGroup + 1;   // groups one append can complete
-  dim3 grid_q(slots, a.n_heads, a.n_cells * a.n_seqs);
-  dim3 grid_t(1, a.n_heads, a.n_cells * a.n_seqs);
-  if (head_dim == 128) {
-    hipLaunchKernelGGL(k_quantize_groups<128>, grid_q, dim3(256), 0, stream, a);
-    hipLaunchKernelGGL(k_write_tail<128>, grid_t, dim3(256), 0, stream, a);
-  } else {
-    hipLaunchKernelGGL(k_quantize_groups<64>, grid_q, dim3(256), 0, stream, a);
-    hipLaunchKernelGGL(k_write_tail<64>, grid_t, dim3(256), 0, stream, a);
-  }
+  if (head_dim == 128) launch_d<128>(a, stream);
+  else launch_d<64>(a, stream);
   return hipGetLastError();
 }
 

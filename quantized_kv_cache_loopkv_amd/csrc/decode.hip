@@ -730,8 +730,9 @@ __device__ void row_body(const DecodeArgs& a, const Row& r, const Smem& sm, size
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   float* scr = sm.wscr + w * kWaveScratch;
   uint32_t* klimb = reinterpret_cast<uint32_t*>(scr);
-  // coarse scores: LDS for a whole row, the row's scratch line for a split one
-  float* scores = (SPARSE && PH != PH_ROW) ? a.part_scores + orow * (size_t)a.split_row_stride : sm.scores;
+  // coarse scores: LDS, except the partial launches of a split row, which leave them in the
+  // row's scratch line for the finishing launch to copy back into LDS
+  float* scores = (SPARSE && PH == PH_PART) ? a.part_scores + orow * (size_t)a.split_row_stride : sm.scores;
   uint32_t* selm = sm.selm;
   float* misc = sm.misc;
   constexpr int NE = G::NE;
@@ -740,6 +741,13 @@ __device__ void row_body(const DecodeArgs& a, const Row& r, const Smem& sm, size
   Acc<VCH> st;
   st.zero();
   KS::fill_qperm(sm.qs, sm.qperm);
+  // PH_FINISH: lane i of every wave holds partial i's (m, l) (n_split <= 64)
+  const float* parts = PH == PH_FINISH ? a.part + orow * (size_t)a.n_split * (2 + D) : nullptr;
+  float part_m = -INFINITY, part_l = 0.f;
+  if (PH == PH_FINISH && lane < a.n_split) {
+    part_m = parts[(size_t)lane * (2 + D)];
+    part_l = parts[(size_t)lane * (2 + D) + 1];
+  }
   __syncthreads();
 
   // ---- single streaming pass: K scores, online softmax, V accumulation; wave w takes the
@@ -839,12 +847,24 @@ __device__ void row_body(const DecodeArgs& a, const Row& r, const Smem& sm, size
   if constexpr (SPARSE && PH != PH_PART) {
     float M = -INFINITY, L = 0.f;   // the row's coarse maximum and weight
     if constexpr (PH == PH_FINISH) {
-      const float* pp = a.part + orow * (size_t)a.n_split * (2 + D);
-      for (int i = 0; i < a.n_split; ++i) M = fmaxf(M, pp[(size_t)i * (2 + D)]);
-      for (int i = 0; i < a.n_split; ++i) {
-        const float mi = pp[(size_t)i * (2 + D)];
-        if (mi > -INFINITY) L += pp[(size_t)i * (2 + D) + 1] * __expf(mi - M);
+      // the row's coarse scores (tail included) from its scratch line into LDS: eight
+      // independent 16-byte loads per thread in flight at once
+      const float4* g4 = reinterpret_cast<const float4*>(a.part_scores + orow * (size_t)a.split_row_stride);
+      float4* l4 = reinterpret_cast<float4*>(scores);
+      const int n4 = (r.N + 3) / 4;   // within the line: its stride is a multiple of 64 floats
+      for (int base = 0; base < n4; base += 8 * kThreads) {
+        float4 v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] = g4[min(base + k * kThreads + tid, n4 - 1)];   // N >= 1
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int i = base + k * kThreads + tid;
+          if (i < n4) l4[i] = v[k];
+        }
       }
+      M = wave_max(part_m);
+      L = wave_sum(part_m > -INFINITY ? part_l * __expf(part_m - M) : 0.f);
+      __syncthreads();   // the scores are in LDS
     } else {
       const float lw = wave_sum(st.lsum);
       if (lane == 0) {
@@ -1026,13 +1046,10 @@ __device__ void row_body(const DecodeArgs& a, const Row& r, const Smem& sm, size
   __syncthreads();
   float M = misc[0];
   for (int i = 1; i < kWaves; ++i) M = fmaxf(M, misc[i]);
-  const float* parts = nullptr;   // PH_FINISH: the row's partials, unless the exact pass replaced them
-  if constexpr (PH == PH_FINISH) {
-    if (use_parts) {
-      parts = a.part + orow * (size_t)a.n_split * (2 + D);
-      for (int i = 0; i < a.n_split; ++i) M = fmaxf(M, parts[(size_t)i * (2 + D)]);
-    }
-  }
+  // PH_FINISH: the row's partials join the merge, unless the exact pass replaced them
+  const bool with_parts = PH == PH_FINISH && use_parts;
+  if (with_parts) M = fmaxf(M, wave_max(part_m));
+  const float part_f = with_parts && part_m > -INFINITY ? __expf(part_m - M) : 0.f;   // lane i: partial i
   const float fw = st.m > -INFINITY ? __expf(st.m - M) : 0.f;
   float* red = sm.scores;                      // [kThreads][VCH]
   float* tred = sm.scores + kThreads * VCH;    // [kWaves][D]
@@ -1048,11 +1065,7 @@ __device__ void row_body(const DecodeArgs& a, const Row& r, const Smem& sm, size
     fws[i] = misc[i] > -INFINITY ? __expf(misc[i] - M) : 0.f;
     Lt += misc[8 + i] * fws[i];
   }
-  if (parts)
-    for (int i = 0; i < a.n_split; ++i) {
-      const float mi = parts[(size_t)i * (2 + D)];
-      if (mi > -INFINITY) Lt += parts[(size_t)i * (2 + D) + 1] * __expf(mi - M);
-    }
+  if (with_parts) Lt += wave_sum(part_l * part_f);
   for (int d = tid; d < D; d += kThreads) {
     const int chunk = d / VCH, c = d % VCH;
     float o = 0.f;
@@ -1063,11 +1076,19 @@ __device__ void row_body(const DecodeArgs& a, const Row& r, const Smem& sm, size
       for (int vb = 0; vb < G::BPS; ++vb) o += red[(ww * 64 + vb * G::LPB + chunk) * VCH + c];
       o += tred[ww * D + d];
     }
-    if (parts)
-      for (int i = 0; i < a.n_split; ++i) {
-        const float mi = parts[(size_t)i * (2 + D)];
-        if (mi > -INFINITY) o = fmaf(parts[(size_t)i * (2 + D) + 2 + d], __expf(mi - M), o);
+    if (with_parts) {   // the partials' values, all loads in flight together
+      const float* pv = parts + 2 + d;
+      float ps[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      for (int i0 = 0; i0 < a.n_split; i0 += 8) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int i = i0 + k;
+          const float fi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(part_f), i & 63));
+          if (i < a.n_split) ps[k] = fmaf(pv[(size_t)i * (2 + D)], fi, ps[k]);
+        }
       }
+      o += ((ps[0] + ps[1]) + (ps[2] + ps[3])) + ((ps[4] + ps[5]) + (ps[6] + ps[7]));
+    }
     if constexpr (PH == PH_PART) {   // unnormalized, relative to M
       float* pp = a.part + (orow * (size_t)a.n_split + split) * (2 + D);
       if (d == 0) {

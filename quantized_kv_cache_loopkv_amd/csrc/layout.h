@@ -83,10 +83,15 @@ struct DecodeArgs {
   DecodeCell cells[kMaxCells];
 };
 
-// Scratch of a split decode, in floats: partials, then one score row per decoded row.
+// Scratch of a split decode, in floats: partials (padded to 64 floats), then one score line
+// per decoded row (lines of a multiple of 64 floats, so every line is 256-byte aligned
+// relative to the scratch base).
 __host__ __device__ inline size_t split_row_stride(int max_len) { return ((size_t)max_len + 63) / 64 * 64; }
+__host__ __device__ inline size_t split_part_floats(size_t rows, int n_split, int D) {
+  return (rows * (size_t)n_split * (size_t)(2 + D) + 63) / 64 * 64;
+}
 __host__ __device__ inline size_t split_scratch_floats(size_t rows, int n_split, int max_len, int D) {
-  return rows * (size_t)n_split * (size_t)(2 + D) + rows * split_row_stride(max_len);
+  return split_part_floats(rows, n_split, D) + rows * split_row_stride(max_len);
 }
 
 }  // namespace lkv

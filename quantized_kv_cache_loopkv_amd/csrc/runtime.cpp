@@ -292,7 +292,7 @@ loopkv_status decode_common(loopkv_ctx* c, hipStream_t stream, int32_t loop, int
     const size_t rows = (size_t)count * n_seqs * c->cfg.n_heads;
     a.split_row_stride = (int32_t)lkv::split_row_stride(max_len);
     a.part = static_cast<float*>(scratch);
-    a.part_scores = a.part + rows * (size_t)n_split * (2 + c->cfg.head_dim);
+    a.part_scores = a.part + lkv::split_part_floats(rows, n_split, c->cfg.head_dim);
   }
   for (int i = 0; i < count; ++i) {
     const int st = c->storage[first + i];

@@ -182,6 +182,25 @@ class Workload:
         return self.ctx.decode(qq, self.bt, self.seq_lens, self.max_len(step), tau, cell=cell,
                                out_dtype=out_dtype, sel_mask=sel_mask)
 
+    def serving_step(self, K, V, q, lens_before, lens_after, max_len, tau, out, sm=None, n_split=0, scratch=None):
+        """One decode step in the order a looped model runs it: for each (loop, layer) cell in turn,
+        append the new token's K, V (storing cells; K, V: [cells][B][1][H][D]) and decode that cell
+        with its query. A reuse cell reads the final loop's cache as it stands, which does not hold
+        the current token yet (the final loop runs later in the step), so it decodes over
+        lens_before tokens; every other cell over lens_after. Advances both length tensors in
+        place, so the step can be captured in a graph and replayed."""
+        cfg = self.cfg
+        for c in range(cfg.n_cells):
+            cell = divmod(c, cfg.n_layers)
+            share = self.plan[c] == R.SHARE
+            if not share:
+                self.ctx.append(K[c], V[c], self.bt, lens_before, cell=cell)
+            self.ctx.decode(q[c], self.bt, lens_before if share else lens_after, max_len, tau, cell=cell,
+                            out=out[c], sel_mask=sm[c] if sm is not None else False, n_split=n_split,
+                            scratch=scratch)
+        lens_before.add_(1)
+        lens_after.add_(1)
+
     # ------------------------------------------------------------------ inspection
     def record(self, cell: int, b: int, h: int, j: int) -> np.ndarray:
         loop, layer = self.cell_ll(cell)

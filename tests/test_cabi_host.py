@@ -208,7 +208,8 @@ def test_split_scratch_bytes():
     for cell, cells in ((None, cfg.n_loops * cfg.n_layers), ((1, 2), 1)):
         for n_seqs, max_len, n_split in ((2, 64, 4), (3, 100, 1), (1, 16384, 64), (0, 64, 2)):
             rows = cells * n_seqs * cfg.n_heads
-            want = 4 * (rows * n_split * (2 + cfg.head_dim) + rows * ((max_len + 63) // 64 * 64))
+            parts = (rows * n_split * (2 + cfg.head_dim) + 63) // 64 * 64
+            want = 4 * (parts + rows * ((max_len + 63) // 64 * 64))
             assert ctx.split_scratch_bytes(n_seqs, max_len, n_split, cell) == want
     n = ctypes.c_size_t()
     L = lkv.lib()

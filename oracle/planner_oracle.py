@@ -20,8 +20,9 @@ Readings taken where the abstract is silent:
   sum at most the storage budget; cells of the final loop cannot reuse;
 * the planner returns a feasible plan of least total reads (None if there is none).
 
-This is that definition written out: every one of the 3^k (at most 2^(final-loop
-cells) fewer) kind assignments is enumerated and the least-reads feasible one kept.
+This is that definition written out: every kind assignment (3 kinds per cell, 2 in the
+final loop) is enumerated, its sums taken, the infeasible ones dropped and the least-reads
+one kept.
 Ties in reads are broken by least damage, then least storage, then the smallest
 assignment in lexicographic order over cells (kind codes 0 = 4-bit, 1 = 2-bit,
 2 = reuse); callers compare the objective, not the tie-break.
@@ -61,14 +62,20 @@ def plan_search_brute(n_loops: int, n_layers: int, damage, reads, storage, damag
     n = n_loops * n_layers
     if n > 13:
         raise ValueError("brute force is for at most 13 cells")
-    best = None
-    best_key = None
-    for kinds in itertools.product(*allowed_kinds(n_loops, n_layers)):
-        d, r, s = plan_cost(kinds, damage, reads, storage)
-        if d > damage_budget or s > storage_budget:
-            continue
-        key = (r, d, s, kinds)
-        if best_key is None or key < best_key:
-            best_key = key
-            best = (tuple(kinds), d, r, s)
-    return best
+    damage = np.asarray(damage, np.float64)
+    reads = np.asarray(reads, np.float64)
+    storage = np.asarray(storage, np.int64)
+    # every assignment, one per row
+    plans = np.array(list(itertools.product(*allowed_kinds(n_loops, n_layers))), dtype=np.int64)
+    cells = np.arange(n)
+    d = damage[cells, plans].sum(axis=1)
+    r = reads[cells, plans].sum(axis=1)
+    s = storage[cells, plans].sum(axis=1)
+    ok = (d <= damage_budget) & (s <= storage_budget)
+    if not ok.any():
+        return None
+    plans, d, r, s = plans[ok], d[ok], r[ok], s[ok]
+    # least reads, then least damage, then least storage, then the lexicographically first plan
+    order = np.lexsort(tuple(plans[:, c] for c in range(n - 1, -1, -1)) + (s, d, r))
+    i = order[0]
+    return tuple(int(k) for k in plans[i]), float(d[i]), float(r[i]), int(s[i])

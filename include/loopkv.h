@@ -92,6 +92,7 @@ typedef enum { LOOPKV_LAYOUT_PLANES = 0, LOOPKV_LAYOUT_KIVI4 = 1 } loopkv_layout
 #define LOOPKV_MAX_SPLIT 64   /* workgroups per row of a split decode */
 /* Largest n_loops * n_layers. */
 #define LOOPKV_MAX_CELLS 128
+#define LOOPKV_MAX_PLAN_CELLS 4096   /* cells of one plan search */
 
 typedef struct {
   int32_t n_loops, n_layers; /* cells = n_loops * n_layers, row-major [loop][layer] */
@@ -191,6 +192,32 @@ loopkv_status loopkv_decode_attn_split(loopkv_ctx* ctx, hipStream_t stream, int3
                                        float sm_scale, void* out, int32_t out_dtype,
                                        uint32_t* sel_mask, int32_t n_split, void* scratch,
                                        size_t scratch_bytes);
+
+/* Costs of one cell for the planner, indexed by loopkv_cell_kind (Q4, Q2, SHARE): the
+ * predicted damage of storing the cell that way (damages of cells add up: the additive
+ * model of the Abstract's sentence on measurements on Ouro), the bytes (or any one unit) the
+ * cell reads per decode step, and its storage in integer units. */
+typedef struct {
+  double damage[3];
+  double reads[3];
+  int64_t storage[3];
+} loopkv_cell_cost;
+
+/* The planner (Abstract, sentence on the planner): choose a kind for each of the
+ * n_loops * n_layers cells (costs row-major [loop][layer]) that minimizes the total reads
+ * subject to total damage <= damage_budget (may be +inf) and total storage <=
+ * storage_budget, cells of the final loop never SHARE. Exact (dynamic programming over
+ * non-dominated partial plans; host only, no GPU). kinds_out: host [cells] loopkv_cell_kind,
+ * ready for loopkv_plan; the plan's sums go to damage_out / reads_out / storage_out
+ * (each nullable). Among plans of equal least reads the one returned is unspecified but
+ * fixed for a given table. Errors: LOOPKV_ERR_INVALID_ARG (null costs or kinds_out, cell
+ * count outside [1, LOOPKV_MAX_PLAN_CELLS], a NaN, infinite or negative cost, a negative
+ * or NaN budget), LOOPKV_ERR_PLAN (no plan meets the budgets; kinds_out untouched),
+ * LOOPKV_ERR_UNSUPPORTED (the search outgrows its state limit, 2^22 partial plans). */
+loopkv_status loopkv_plan_search(int32_t n_loops, int32_t n_layers, const loopkv_cell_cost* costs,
+                                 double damage_budget, int64_t storage_budget,
+                                 uint8_t* kinds_out, double* damage_out, double* reads_out,
+                                 int64_t* storage_out);
 
 /* Thread-local description of the last error on this thread ("" after success). */
 const char* loopkv_last_error(void);

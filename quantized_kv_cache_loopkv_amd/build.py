@@ -48,7 +48,7 @@ def build_loopkv(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     hipcc = _hipcc()
     objs = []
-    units = [("runtime.cpp", []), ("append.hip", ["-ffp-contract=off"]), ("decode.hip", [])]
+    units = [("runtime.cpp", []), ("planner.cpp", []), ("append.hip", ["-ffp-contract=off"]), ("decode.hip", [])]
     for src, extra in units:
         obj = os.path.join(BUILD, src.replace(".", "_") + ".o")
         lang = ["-x", "hip"]

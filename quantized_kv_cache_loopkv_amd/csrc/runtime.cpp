@@ -85,6 +85,11 @@ loopkv_status check_ready(const loopkv_ctx* c) {
 }
 }  // namespace
 
+namespace lkv {   // error reporting for the planner (planner.cpp)
+loopkv_status planner_fail(loopkv_status s, const char* msg) { return fail(s, "%s", msg); }
+loopkv_status planner_ok() { return ok(); }
+}  // namespace lkv
+
 extern "C" {
 
 const char* loopkv_last_error(void) { return g_err.c_str(); }

@@ -27,7 +27,7 @@ MAX_SPLIT = 64
 
 EXPORTED = ["loopkv_create", "loopkv_destroy", "loopkv_plan", "loopkv_workspace_bytes",
             "loopkv_bind_workspace", "loopkv_cell_storage", "loopkv_append", "loopkv_decode_attn",
-            "loopkv_split_scratch_bytes", "loopkv_decode_attn_split", "loopkv_last_error"]
+            "loopkv_split_scratch_bytes", "loopkv_decode_attn_split", "loopkv_plan_search", "loopkv_last_error"]
 
 
 class LoopKVError(RuntimeError):
@@ -40,6 +40,10 @@ class _Config(ctypes.Structure):
     _fields_ = [("n_loops", ctypes.c_int32), ("n_layers", ctypes.c_int32), ("n_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("group_size", ctypes.c_int32), ("block_tokens", ctypes.c_int32),
                 ("num_blocks", ctypes.c_int32), ("max_seqs", ctypes.c_int32), ("layout", ctypes.c_int32)]
+
+
+class _CellCost(ctypes.Structure):
+    _fields_ = [("damage", ctypes.c_double * 3), ("reads", ctypes.c_double * 3), ("storage", ctypes.c_int64 * 3)]
 
 
 _lib = None
@@ -67,11 +71,14 @@ def lib():
     L.loopkv_split_scratch_bytes.argtypes = [vp, i32, i32, i32, i32, i32, ctypes.POINTER(ctypes.c_size_t)]
     L.loopkv_decode_attn_split.argtypes = [vp, vp, i32, i32, vp, i32, i32, vp, vp, i32, vp, i32, f32, f32, vp, i32,
                                            vp, i32, vp, ctypes.c_size_t]
+    L.loopkv_plan_search.argtypes = [i32, i32, ctypes.POINTER(_CellCost), ctypes.c_double, ctypes.c_int64,
+                                     ctypes.POINTER(ctypes.c_uint8), ctypes.POINTER(ctypes.c_double),
+                                     ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
     L.loopkv_last_error.restype = ctypes.c_char_p
     L.loopkv_last_error.argtypes = []
     for name in ["loopkv_create", "loopkv_plan", "loopkv_workspace_bytes", "loopkv_bind_workspace",
                  "loopkv_cell_storage", "loopkv_append", "loopkv_decode_attn", "loopkv_split_scratch_bytes",
-                 "loopkv_decode_attn_split"]:
+                 "loopkv_decode_attn_split", "loopkv_plan_search"]:
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -106,6 +113,25 @@ def _dev_i32(t: Optional[torch.Tensor], name: str, numel: Optional[int] = None):
     if numel is not None and t.numel() < numel:
         raise ValueError(f"{name} has {t.numel()} elements, needs {numel}")
     return t
+
+
+def plan_search(n_loops: int, n_layers: int, damage, reads, storage, damage_budget: float, storage_budget: int):
+    """Least-reads kinds ([n_loops * n_layers] list of CELL_*) under the damage and storage budgets
+    (loopkv_plan_search). damage, reads: [cells][3] floats; storage: [cells][3] ints (kind order
+    Q4, Q2, SHARE). Returns (kinds, damage, reads, storage); raises LoopKVError (status ERR_PLAN)
+    when no plan meets the budgets."""
+    n = n_loops * n_layers
+    arr = (_CellCost * n)()
+    for c in range(n):
+        for k in range(3):
+            arr[c].damage[k] = float(damage[c][k])
+            arr[c].reads[k] = float(reads[c][k])
+            arr[c].storage[k] = int(storage[c][k])
+    kinds = (ctypes.c_uint8 * n)()
+    d, r, st = ctypes.c_double(), ctypes.c_double(), ctypes.c_int64()
+    _check(lib().loopkv_plan_search(n_loops, n_layers, arr, float(damage_budget), int(storage_budget), kinds,
+                                    ctypes.byref(d), ctypes.byref(r), ctypes.byref(st)))
+    return [int(k) for k in kinds], d.value, r.value, st.value
 
 
 class Context:

@@ -175,7 +175,7 @@ def softmax_weights(scores):
     return e / np.sum(e)
 
 
-def decode_row(q, K, V, kind, tau, sm_scale, qh=None, sel_override=None):
+def decode_row(q, K, V, kind, tau, sm_scale, qh=None, sel_override=None, skip=False):
     """One decode-attention row of the loop-aware method.
 
     q: [D] query; K, V: [N][D] history (bf16 values as float64); kind: 0 for a
@@ -191,6 +191,12 @@ def decode_row(q, K, V, kind, tau, sm_scale, qh=None, sel_override=None):
          (read at 2 bits, never skipped), exact on the tail;
       6. o = softmax(refined scores) . values.
     2-bit target: one pass over x_2bit K and V, no selection.
+
+    skip=True is the rejected alternative of the abstract's sentence on skipping (the
+    ablation, not the method): steps 1-4 as above, but the unselected quantized tokens are
+    dropped instead of read at 2 bits, so the softmax runs over the selected tokens and the
+    tail only (reading: a skipped token leaves the attention entirely, as in sparse
+    attention); if nothing is kept, o = 0. 4-bit targets only.
     """
     q = np.asarray(q, dtype=np.float64)
     K = np.asarray(K, dtype=np.float64)
@@ -225,6 +231,14 @@ def decode_row(q, K, V, kind, tau, sm_scale, qh=None, sel_override=None):
     v_vals = np.concatenate([dequant_hi(qh, "v"), V[n_q:]])
     v4 = dequant_full(qh, "v")
     v_vals[:n_q][sel] = v4[sel]
+    if skip:
+        if kind != KIND_Q4:
+            raise ValueError("skipping applies to 4-bit targets")
+        keep = np.concatenate([sel, np.ones(N - n_q, dtype=bool)])
+        if not keep.any():
+            return np.zeros(D), sel, phat
+        w = softmax_weights(scores[keep])
+        return w @ v_vals[keep], sel, phat
     w = softmax_weights(scores)
     return w @ v_vals, sel, phat
 

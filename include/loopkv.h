@@ -193,6 +193,22 @@ loopkv_status loopkv_decode_attn_split(loopkv_ctx* ctx, hipStream_t stream, int3
                                        uint32_t* sel_mask, int32_t n_split, void* scratch,
                                        size_t scratch_bytes);
 
+/* The token-skipping ablation (the alternative the Abstract's sentence on skipping rejects;
+ * not the method): arguments, selection and sel_mask as loopkv_decode_attn, but a 4-bit
+ * target's unselected quantized tokens are dropped instead of read at 2 bits: their values
+ * are never read and the softmax runs over the selected tokens (at 4 bits) and the exact
+ * tail; a row that keeps nothing gets 0. tau = 0 keeps every token (the decode of
+ * loopkv_decode_attn at tau = 0); tau > 1 keeps the tail only. 2-bit targets decode as in
+ * loopkv_decode_attn. Errors as loopkv_decode_attn, plus LOOPKV_ERR_UNSUPPORTED with the
+ * KIVI4 layout. */
+loopkv_status loopkv_decode_attn_skip(loopkv_ctx* ctx, hipStream_t stream, int32_t loop,
+                                      int32_t layer, const void* q, int32_t q_dtype,
+                                      int32_t n_seqs, const int32_t* seq_slots,
+                                      const int32_t* block_table, int32_t bt_stride,
+                                      const int32_t* seq_lens, int32_t max_len, float tau,
+                                      float sm_scale, void* out, int32_t out_dtype,
+                                      uint32_t* sel_mask);
+
 /* Costs of one cell for the planner, indexed by loopkv_cell_kind (Q4, Q2, SHARE): the
  * predicted damage of storing the cell that way (damages of cells add up: the additive
  * model of the Abstract's sentence on measurements on Ouro), the bytes (or any one unit) the

@@ -722,7 +722,10 @@ __device__ inline void split_range(int n_chunks, int n_split, int split, int& cb
   ce = min(n_chunks, cb + per);
 }
 
-template <int D, int MODE, bool SPARSE, int PH>
+// SKIP (with SPARSE, PH_ROW): the token-skipping ablation. The same coarse pass and
+// selection, but the values are not streamed and the unselected quantized tokens leave the
+// attention: the softmax runs over the selected tokens (at 4 bits) and the tail only.
+template <int D, int MODE, bool SPARSE, int PH, bool SKIP = false>
 __device__ void row_body(const DecodeArgs& a, const Row& r, const Smem& sm, size_t orow, int split) {
   using G = Geo<D, MODE>;
   using KS = KStep<D, MODE, false>;
@@ -774,6 +777,7 @@ __device__ void row_body(const DecodeArgs& a, const Row& r, const Smem& sm, size
     KS::load(r, groups, lane, kb);
   };
   auto issue_v = [&](int s, typename VS::Buf& vb) {
+    if constexpr (SKIP) return;
     const int c = cb + s * kWaves + w;
     if (c >= n_chunks) return;
     VS::load(r, c * G::BPS, nb, lane, vb);
@@ -798,6 +802,7 @@ __device__ void row_body(const DecodeArgs& a, const Row& r, const Smem& sm, size
     return wgt;
   };
   auto step_v = [&](int s, const typename VS::Buf& vb, float wgt) {
+    if constexpr (SKIP) return;
     const int c = cb + s * kWaves + w;
     if (c >= n_chunks) return;
     VS::compute(wgt, scr + G::S_W, scr, lane, vb, st);
@@ -823,6 +828,7 @@ __device__ void row_body(const DecodeArgs& a, const Row& r, const Smem& sm, size
 #pragma unroll
   for (int i = 0; i < D / 64; ++i) tacc[i] = 0.f;
   const bool has_tail = PH == PH_ROW || (PH == PH_PART && split == a.n_split - 1);
+  float tl = 0.f;   // SKIP: the tail's weight (lane 0)
   for (int t = r.n_q + w; has_tail && t < r.N; t += kWaves) {
     const uint16_t* kt = r.tail + (size_t)(t % kGroup) * D;
     float p = 0.f;
@@ -834,9 +840,12 @@ __device__ void row_body(const DecodeArgs& a, const Row& r, const Smem& sm, size
       const float f = st.raise(p);
 #pragma unroll
       for (int i = 0; i < D / 64; ++i) tacc[i] *= f;
+      if constexpr (SKIP) tl *= f;
     }
     const float wgt = __expf(p - st.m);
     if (lane == 0) st.lsum += wgt;
+    if constexpr (SKIP)
+      if (lane == 0) tl += wgt;
     const uint16_t* vt = r.tail + (size_t)(kGroup + t % kGroup) * D;
 #pragma unroll
     for (int i = 0; i < D / 64; ++i) tacc[i] = fmaf(wgt, bf16f(vt[lane + 64 * i]), tacc[i]);
@@ -881,8 +890,10 @@ __device__ void row_body(const DecodeArgs& a, const Row& r, const Smem& sm, size
       const float f = st.raise(M);
 #pragma unroll
       for (int i = 0; i < D / 64; ++i) tacc[i] *= f;
+      if constexpr (SKIP) tl *= f;
     }
     st.m = M;   // every wave now shares the reference M
+    if constexpr (SKIP) st.lsum = tl;   // the quantized tokens' coarse weights served the selection only
     float removed = 0.f;   // coarse weight taken out by the corrections
     // exp(s - M) / L >= tau  <=>  s >= M + ln(tau L): one compare per token
     const float thr = M + logf(a.tau * L);
@@ -953,7 +964,7 @@ __device__ void row_body(const DecodeArgs& a, const Row& r, const Smem& sm, size
           for (int i = 0; i < D / 64; ++i) tacc[i] *= f;
         }
         const float wf = sel ? __expf(s_ref - st.m) : 0.f;
-        const float wc = sel ? __expf(s_hat - st.m) : 0.f;
+        const float wc = (sel && !SKIP) ? __expf(s_hat - st.m) : 0.f;   // SKIP: nothing to take out
         st.lsum += wf - wc;
         removed += wc;
         wave_sync_lds();
@@ -1098,7 +1109,8 @@ __device__ void row_body(const DecodeArgs& a, const Row& r, const Smem& sm, size
       pp[2 + d] = o;
       continue;
     }
-    o = o / Lt;
+    if constexpr (SKIP) o = Lt > 0.f ? o / Lt : 0.f;   // nothing kept: 0
+    else o = o / Lt;
     if (a.out_bf16) {
       uint32_t u = __float_as_uint(o);
       u += 0x7fffu + ((u >> 16) & 1u);
@@ -1124,7 +1136,7 @@ __host__ __device__ inline size_t decode_lds_floats(int max_len, int D) {
 // One kernel per selection regime of the launch (tau = 0, tau > 1, 0 < tau <= 1, or the
 // KIVI-4 layout), so each variant gets its own register allocation; rows of 2-bit cells
 // run the 2-bit path inside every planes variant.
-enum : int { VAR_KIVI = 0, VAR_DENSE = 1, VAR_COARSE = 2, VAR_SPARSE = 3 };
+enum : int { VAR_KIVI = 0, VAR_DENSE = 1, VAR_COARSE = 2, VAR_SPARSE = 3, VAR_SKIP = 4 };
 
 template <int D, int VAR, int PH>
 __global__ void __launch_bounds__(kThreads, kWavesPerSimd) k_decode(DecodeArgs a) {
@@ -1189,6 +1201,7 @@ __global__ void __launch_bounds__(kThreads, kWavesPerSimd) k_decode(DecodeArgs a
     if (cell.kind == KIND_Q2) row_body<D, MODE_Q2, false, PH>(a, r, sm, orow, split);
     else if (VAR == VAR_DENSE) row_body<D, MODE_DENSE, false, PH>(a, r, sm, orow, split);
     else if (VAR == VAR_COARSE) row_body<D, MODE_COARSE, false, PH>(a, r, sm, orow, split);
+    else if (VAR == VAR_SKIP) row_body<D, MODE_COARSE, true, PH, true>(a, r, sm, orow, split);
     else row_body<D, MODE_COARSE, true, PH>(a, r, sm, orow, split);
   }
 }
@@ -1208,7 +1221,9 @@ static void launch_phase(const DecodeArgs& a, size_t grid, size_t lds, hipStream
 
 template <int D, int VAR>
 static void launch_variant(const DecodeArgs& a, size_t rows, size_t lds, hipStream_t stream) {
-  if (a.n_split < 1) {
+  if constexpr (VAR == VAR_SKIP) {   // one workgroup per row only (the host refuses a split)
+    launch_phase<D, VAR, PH_ROW>(a, rows, lds, stream);
+  } else if (a.n_split < 1) {
     launch_phase<D, VAR, PH_ROW>(a, rows, lds, stream);
   } else {   // stream order: every partial is written before the finishing launch reads it
     launch_phase<D, VAR, PH_PART>(a, rows * (size_t)a.n_split, lds, stream);
@@ -1219,7 +1234,8 @@ static void launch_variant(const DecodeArgs& a, size_t rows, size_t lds, hipStre
 template <int D>
 static void launch_d(const DecodeArgs& a, size_t rows, size_t lds, hipStream_t stream) {
   if (a.cells[0].kind == KIND_KIVI4) launch_variant<D, VAR_KIVI>(a, rows, lds, stream);
-  else if (a.tau <= 0.f) launch_variant<D, VAR_DENSE>(a, rows, lds, stream);
+  else if (a.tau <= 0.f) launch_variant<D, VAR_DENSE>(a, rows, lds, stream);   // everything kept
+  else if (a.skip) launch_variant<D, VAR_SKIP>(a, rows, lds, stream);
   else if (a.tau > 1.f) launch_variant<D, VAR_COARSE>(a, rows, lds, stream);
   else launch_variant<D, VAR_SPARSE>(a, rows, lds, stream);
 }

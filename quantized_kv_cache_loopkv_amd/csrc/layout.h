@@ -78,6 +78,7 @@ struct DecodeArgs {
   // part: [rows][n_split][2 + D] floats (m, l, unnormalized o relative to m);
   // part_scores: [rows][split_row_stride] coarse scores (4-bit targets, 0 < tau <= 1).
   int32_t n_split, split_row_stride;
+  int32_t skip;   // token-skipping ablation: unselected quantized tokens leave the attention
   float* part;
   float* part_scores;
   DecodeCell cells[kMaxCells];

@@ -242,7 +242,7 @@ loopkv_status decode_common(loopkv_ctx* c, hipStream_t stream, int32_t loop, int
                             int32_t q_dtype, int32_t n_seqs, const int32_t* seq_slots, const int32_t* block_table,
                             int32_t bt_stride, const int32_t* seq_lens, int32_t max_len, float tau, float sm_scale,
                             void* out, int32_t out_dtype, uint32_t* sel_mask, int32_t n_split, void* scratch,
-                            size_t scratch_bytes) {
+                            size_t scratch_bytes, bool skip) {
   loopkv_status s = check_ready(c);
   if (s != LOOPKV_OK) return s;
   int first, count;
@@ -261,6 +261,9 @@ loopkv_status decode_common(loopkv_ctx* c, hipStream_t stream, int32_t loop, int
     return fail(LOOPKV_ERR_CAPACITY, "max_len %d outside [0, %d]", max_len, LOOPKV_MAX_LEN);
   if (bt_stride < 1 || (long long)bt_stride * lkv::kBlock < max_len)
     return fail(LOOPKV_ERR_CAPACITY, "bt_stride %d too small for max_len %d", bt_stride, max_len);
+  if (skip && c->cfg.layout == LOOPKV_LAYOUT_KIVI4)
+    return fail(LOOPKV_ERR_UNSUPPORTED, "token skipping needs the planes layout");
+  if (skip && n_split != 0) return fail(LOOPKV_ERR_INVALID_ARG, "token skipping runs one workgroup per row");
   if (n_split != 0) {
     if (n_split < 1 || n_split > LOOPKV_MAX_SPLIT)
       return fail(LOOPKV_ERR_INVALID_ARG, "n_split %d outside [1, %d]", n_split, LOOPKV_MAX_SPLIT);
@@ -293,6 +296,7 @@ loopkv_status decode_common(loopkv_ctx* c, hipStream_t stream, int32_t loop, int
   a.tau = tau;
   a.sm_scale = sm_scale;
   a.n_split = n_split;
+  a.skip = skip ? 1 : 0;
   if (n_split > 0) {
     const size_t rows = (size_t)count * n_seqs * c->cfg.n_heads;
     a.split_row_stride = (int32_t)lkv::split_row_stride(max_len);
@@ -319,7 +323,16 @@ loopkv_status loopkv_decode_attn(loopkv_ctx* c, hipStream_t stream, int32_t loop
                                  int32_t max_len, float tau, float sm_scale, void* out, int32_t out_dtype,
                                  uint32_t* sel_mask) {
   return decode_common(c, stream, loop, layer, q, q_dtype, n_seqs, seq_slots, block_table, bt_stride, seq_lens,
-                       max_len, tau, sm_scale, out, out_dtype, sel_mask, 0, nullptr, 0);
+                       max_len, tau, sm_scale, out, out_dtype, sel_mask, 0, nullptr, 0, false);
+}
+
+loopkv_status loopkv_decode_attn_skip(loopkv_ctx* c, hipStream_t stream, int32_t loop, int32_t layer, const void* q,
+                                      int32_t q_dtype, int32_t n_seqs, const int32_t* seq_slots,
+                                      const int32_t* block_table, int32_t bt_stride, const int32_t* seq_lens,
+                                      int32_t max_len, float tau, float sm_scale, void* out, int32_t out_dtype,
+                                      uint32_t* sel_mask) {
+  return decode_common(c, stream, loop, layer, q, q_dtype, n_seqs, seq_slots, block_table, bt_stride, seq_lens,
+                       max_len, tau, sm_scale, out, out_dtype, sel_mask, 0, nullptr, 0, true);
 }
 
 loopkv_status loopkv_split_scratch_bytes(const loopkv_ctx* c, int32_t loop, int32_t layer, int32_t n_seqs,
@@ -346,7 +359,7 @@ loopkv_status loopkv_decode_attn_split(loopkv_ctx* c, hipStream_t stream, int32_
                                        uint32_t* sel_mask, int32_t n_split, void* scratch, size_t scratch_bytes) {
   if (n_split == 0) return fail(LOOPKV_ERR_INVALID_ARG, "n_split %d outside [1, %d]", n_split, LOOPKV_MAX_SPLIT);
   return decode_common(c, stream, loop, layer, q, q_dtype, n_seqs, seq_slots, block_table, bt_stride, seq_lens,
-                       max_len, tau, sm_scale, out, out_dtype, sel_mask, n_split, scratch, scratch_bytes);
+                       max_len, tau, sm_scale, out, out_dtype, sel_mask, n_split, scratch, scratch_bytes, false);
 }
 
 }  // extern "C"

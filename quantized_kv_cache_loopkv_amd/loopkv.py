@@ -27,7 +27,8 @@ MAX_SPLIT = 64
 
 EXPORTED = ["loopkv_create", "loopkv_destroy", "loopkv_plan", "loopkv_workspace_bytes",
             "loopkv_bind_workspace", "loopkv_cell_storage", "loopkv_append", "loopkv_decode_attn",
-            "loopkv_split_scratch_bytes", "loopkv_decode_attn_split", "loopkv_plan_search", "loopkv_last_error"]
+            "loopkv_split_scratch_bytes", "loopkv_decode_attn_split", "loopkv_decode_attn_skip", "loopkv_plan_search",
+            "loopkv_last_error"]
 
 
 class LoopKVError(RuntimeError):
@@ -68,6 +69,7 @@ def lib():
                                       ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(i32)]
     L.loopkv_append.argtypes = [vp, vp, i32, i32, vp, vp, i32, i32, i32, vp, vp, i32, vp]
     L.loopkv_decode_attn.argtypes = [vp, vp, i32, i32, vp, i32, i32, vp, vp, i32, vp, i32, f32, f32, vp, i32, vp]
+    L.loopkv_decode_attn_skip.argtypes = [vp, vp, i32, i32, vp, i32, i32, vp, vp, i32, vp, i32, f32, f32, vp, i32, vp]
     L.loopkv_split_scratch_bytes.argtypes = [vp, i32, i32, i32, i32, i32, ctypes.POINTER(ctypes.c_size_t)]
     L.loopkv_decode_attn_split.argtypes = [vp, vp, i32, i32, vp, i32, i32, vp, vp, i32, vp, i32, f32, f32, vp, i32,
                                            vp, i32, vp, ctypes.c_size_t]
@@ -78,7 +80,7 @@ def lib():
     L.loopkv_last_error.argtypes = []
     for name in ["loopkv_create", "loopkv_plan", "loopkv_workspace_bytes", "loopkv_bind_workspace",
                  "loopkv_cell_storage", "loopkv_append", "loopkv_decode_attn", "loopkv_split_scratch_bytes",
-                 "loopkv_decode_attn_split", "loopkv_plan_search"]:
+                 "loopkv_decode_attn_split", "loopkv_decode_attn_skip", "loopkv_plan_search"]:
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -220,10 +222,11 @@ class Context:
     def decode(self, q: torch.Tensor, block_table: torch.Tensor, seq_lens: torch.Tensor, max_len: int,
                tau: float, sm_scale: Optional[float] = None, cell=None, out_dtype=torch.float32,
                out: Optional[torch.Tensor] = None, sel_mask=False, seq_slots: Optional[torch.Tensor] = None,
-               n_split: int = 0, scratch: Optional[torch.Tensor] = None):
+               n_split: int = 0, scratch: Optional[torch.Tensor] = None, skip: bool = False):
         """q: [cells][n_seqs][H][D] (cell=None) or [n_seqs][H][D]. Returns out (and sel_mask if asked).
         n_split > 0 splits each row over that many workgroups (loopkv_decode_attn_split); scratch is
-        then a CUDA tensor of at least split_scratch_bytes() bytes (allocated here if None)."""
+        then a CUDA tensor of at least split_scratch_bytes() bytes (allocated here if None).
+        skip=True runs the token-skipping ablation (loopkv_decode_attn_skip), not the method."""
         loop, layer = self._cell(cell)
         if not q.is_contiguous():
             raise ValueError("q must be contiguous")
@@ -246,7 +249,13 @@ class Context:
         _dev_i32(seq_lens, "seq_lens", n_seqs)
         _dev_i32(seq_slots, "seq_slots", n_seqs)
         bt_stride = bt.shape[-1] if bt.dim() == 2 else bt.numel()
-        if n_split:
+        if skip:
+            if n_split:
+                raise ValueError("the token-skipping ablation runs one workgroup per row (n_split=0)")
+            _check(lib().loopkv_decode_attn_skip(self._h, _stream(), loop, layer, _ptr(q), _dtype_code(q), n_seqs,
+                                                 _ptr(seq_slots), _ptr(bt), bt_stride, _ptr(seq_lens), int(max_len),
+                                                 float(tau), float(sm_scale), _ptr(out), _dtype_code(out), _ptr(sm)))
+        elif n_split:
             if scratch is None:
                 scratch = torch.empty(self.split_scratch_bytes(n_seqs, max_len, n_split, cell), dtype=torch.uint8,
                                       device=q.device)

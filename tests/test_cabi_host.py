@@ -242,3 +242,20 @@ def test_split_scratch_exact_size_passes_validation_of_size():
     assert _decode_split(ctx, scratch_bytes=need - 1) == B.ERR_WORKSPACE
     assert _decode_split(ctx, scratch_bytes=need, q=0) == B.ERR_INVALID_ARG
     assert _decode_split(ctx, n_seqs=0, scratch=0, scratch_bytes=0) == B.OK
+
+
+def test_skip_decode_validation():
+    """The token-skipping ablation shares the decode's checks and refuses the KIVI-4 layout."""
+    vp = ctypes.c_void_p
+    for layout, want in ((0, B.OK), (1, B.ERR_UNSUPPORTED)):
+        ctx = _ready_ctx(layout)
+        # n_seqs = 0: validation only, nothing enqueued
+        s = lkv.lib().loopkv_decode_attn_skip(ctx._h, None, -1, -1, vp(FAKE_DEV), 1, 0, None, vp(FAKE_DEV), 4,
+                                              vp(FAKE_DEV), 64, ctypes.c_float(0.01), ctypes.c_float(0.125),
+                                              vp(FAKE_DEV), 0, None)
+        assert s == want
+    ctx = _ready_ctx(0)
+    s = lkv.lib().loopkv_decode_attn_skip(ctx._h, None, -1, -1, vp(FAKE_DEV), 1, 2, None, vp(FAKE_DEV), 4,
+                                          vp(FAKE_DEV), 64, ctypes.c_float(-1.0), ctypes.c_float(0.125),
+                                          vp(FAKE_DEV), 0, None)
+    assert s == B.ERR_INVALID_ARG

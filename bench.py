@@ -14,7 +14,8 @@ algorithmic bytes per launch over its mean duration (HIP events on the launch
 stream) against the 8 TB/s HBM peak; ``cpu_baseline`` times the fp64 oracle on a
 few sampled rows of the same workload on the host.
 
-Extra fields: the tau sweep, the KIVI-4 layout on the same kernel, a read-ceiling probe, and
+Extra fields: the tau sweep, the token-skipping ablation (unselected tokens dropped instead of
+read at 2 bits), the KIVI-4 layout on the same kernel, a read-ceiling probe, and
 the per-(loop, layer) serving order under a graph (each cell appends its token and decodes in
 turn, as a looped model calls it): at batch 32 beside the whole-plan step, and at batch 1 with
 the split decode (each row over n_split workgroups) against one workgroup per row.
@@ -96,6 +97,24 @@ def algorithmic_bytes(plan, lengths, H, D, sel_counts=None, layout_kivi=False, o
             total += H * row
             if sel_counts is not None:
                 total += per_tok_lo * int(sel_counts[c, b].sum())
+    return total
+
+
+def algorithmic_bytes_skip(tk, lengths, H, D, sel_counts, out_bytes=2, q_bytes=2):
+    """Bytes of the token-skipping ablation's whole-plan decode: rows with a 4-bit target read
+    48 B/token (D=128: K_hi 32 + K_meta 16) plus 112 B per selected token (K_lo 32 + V_hi 32 +
+    V_lo 32 + V_meta 16); 2-bit targets, tails, q, output and block table as in the method."""
+    import numpy as np
+    tk = np.asarray(tk).reshape(-1)
+    total = 0
+    for c in range(tk.size):
+        for b, N in enumerate(lengths):
+            n_q = 32 * (N // 32)
+            row = (N - n_q) * 4 * D + D * q_bytes + D * out_bytes + 4 * ((N + 15) // 16) + 4
+            row += n_q * (48 if tk[c] == 0 else 96) * D // 128
+            total += H * row
+            if tk[c] == 0:
+                total += (112 * D // 128) * int(sel_counts[c, b].sum())
     return total
 
 
@@ -339,6 +358,25 @@ def main():
                                "GBps": round(bts / (ms * 1e-3) / 1e9, 1), "selected": int(ct.sum())}
             log(f"tau={tau}: {ms:.3f} ms, {bts / 1e9:.2f} GB, {bts / (ms * 1e-3) / 1e9:.0f} GB/s")
         extra["tau_sweep"] = sweep
+        # the ablation the pages reject: drop the unselected tokens instead of reading them at 2 bits
+        _, sms = wl.ctx.decode(q, wl.bt, wl.seq_lens, max(final_lens), args.tau, out_dtype=torch.bfloat16,
+                               sel_mask=True, skip=True)
+        cs = sel_counts_from_mask(sms, None)
+        cs[tk != 0] = 0
+        sb = algorithmic_bytes_skip(tk, final_lens, H, D, cs)
+        e_a, e_b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e_a.record(stream)
+        for _ in range(3):
+            wl.ctx.decode(q, wl.bt, wl.seq_lens, max(final_lens), args.tau, out=out, out_dtype=torch.bfloat16,
+                          skip=True)
+        e_b.record(stream)
+        torch.cuda.synchronize()
+        sms_ms = e_a.elapsed_time(e_b) / 3
+        extra["skip_ablation"] = {"decode_ms": round(sms_ms, 4), "algorithmic_GB": round(sb / 1e9, 3),
+                                  "GBps": round(sb / (sms_ms * 1e-3) / 1e9, 1),
+                                  "bytes_ratio_to_method": round(sb / dec_bytes, 4),
+                                  "time_ratio_to_method": round(sms_ms / dec_mean_ms, 4)}
+        log(f"skip ablation: {sms_ms:.3f} ms, {sb / 1e9:.2f} GB ({sb / dec_bytes:.3f} of the method's bytes)")
     if not args.no_serving:
         # the same cache in the order a looped model calls it (96 cells one by one), under a graph
         ms, per = serving_graph(wl, q, args.tau, S, SERVING_REPS, 0, log, warm=SERVING_WARM)

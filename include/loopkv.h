@@ -100,7 +100,8 @@ typedef struct {
   int32_t head_dim;          /* 64 or 128 */
   int32_t group_size;        /* must be 32 */
   int32_t block_tokens;      /* must be 16 */
-  int32_t num_blocks;        /* physical blocks in each storing cell's pool */
+  int32_t num_blocks;        /* physical blocks in each storing cell's pool; a pool
+                                (num_blocks x n_heads x 20*head_dim bytes) stays below 4 GiB */
   int32_t max_seqs;          /* sequence slots (tail buffers) */
   int32_t layout;            /* loopkv_layout; KIVI4 requires an all-4-bit plan */
 } loopkv_config;

@@ -223,7 +223,10 @@ struct Row {
   const uint32_t* boff;    // per logical block: record offset in 256-byte units (in LDS)
   const uint16_t* tail;    // tail of (slot, head): [2][32][D] bf16
   int N, n_q, n_groups;
-  __device__ inline const uint8_t* rec_ptr(int j) const { return pool + ((uint64_t)boff[j] << 8); }
+  // Byte `off` of logical block j's record: the pool is under 4 GiB (checked at create), so
+  // the offset is 32-bit and the load takes the uniform pool base plus a 32-bit lane offset.
+  __device__ inline const uint8_t* at(int j, uint32_t off) const { return pool + ((boff[j] << 8) + off); }
+  __device__ inline const uint8_t* rec_ptr(int j) const { return at(j, 0u); }
 };
 
 // Per-wave state of the online softmax. acc: this lane's V channels; accz: constant
@@ -322,8 +325,8 @@ struct KStep {
     role(lane, gsub, blk, quad, cp);
     const int g = groups[gsub];
     const int pos0 = (lane % G::LPG) * G::CPL;
-    b.meta = ld_words<G::CPL>(r.rec_ptr(2 * g + (pos0 >= D / 2)) + G::KMETA + 4 * (pos0 % (D / 2)));
-    const uint8_t* kp = r.rec_ptr(2 * g + blk) + CODE_OFF + ((cp * G::NC) * kBlock + 4 * quad) * 4;
+    b.meta = ld_words<G::CPL>(r.at(2 * g + (pos0 >= D / 2), G::KMETA + 4 * (pos0 % (D / 2))));
+    const uint8_t* kp = r.at(2 * g + blk, CODE_OFF + ((cp * G::NC) * kBlock + 4 * quad) * 4);
 #pragma unroll
     for (int i = 0; i < G::NC; ++i) b.c[i] = ld_stream4(kp + i * kBlock * 4);
     if (G::DENSE) {
@@ -344,11 +347,19 @@ struct KStep {
   }
 
   // Masked words of one code word (and its low-plane word for DENSE): the four codes of
-  // one limb set each, one code per byte.
+  // one limb set each, one code per byte. 2-bit planes: bit pairs 1 and 3 are taken in place
+  // (4 c, no shift) and their coefficients stay at scale 1 while those of pairs 0 and 2 are
+  // made 4x, so every product carries the same factor 4 (five operations per word).
   __device__ static inline void masked(uint32_t x, uint32_t y, uint32_t* m) {
     if constexpr (G::KIVI) {
       m[0] = x & 0x0F0F0F0Fu;
       m[1] = (x >> 4) & 0x0F0F0F0Fu;
+    } else if constexpr (!G::DENSE) {
+      const uint32_t x4 = x >> 4;
+      m[0] = x & 0x03030303u;
+      m[1] = x & 0x0C0C0C0Cu;
+      m[2] = x4 & 0x03030303u;
+      m[3] = x4 & 0x0C0C0C0Cu;
     } else {
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
@@ -410,9 +421,14 @@ struct KStep {
     }
     static_assert(G::LPG >= 32, "group lanes");
     const int ex = set_exponent(fm);
-    const float scl = __builtin_amdgcn_ldexpf(1.f, 21 - ex);
+    // 2-bit planes (see masked): positions of bit pairs 0 and 2 get 4x coefficients (below
+    // 2^22), those of pairs 1 and 3 scale 1 (below 2^20), every product then holds 4 v c;
+    // a lane's positions share one bit pair. Other layouts: below 2^21, factor 1.
+    constexpr bool X4 = !G::KIVI && !G::DENSE;
+    const bool even_pair = ((pos0 % 16) / 4) % 2 == 0;
+    const float scl = __builtin_amdgcn_ldexpf(X4 && even_pair ? 4.f : 1.f, (X4 ? 20 : 21) - ex);
     // high-plane-only codes carry weight 4 (code 4 hi): folded into the inverse scale
-    const float inv = __builtin_amdgcn_ldexpf(MODE == MODE_COARSE && !REFINE ? 4.f : 1.f, ex - 21);
+    const float inv = __builtin_amdgcn_ldexpf(MODE == MODE_COARSE && !REFINE ? 4.f : 1.f, ex - (X4 ? 22 : 21));
     uint32_t mine[G::CPL];
 #pragma unroll
     for (int k = 0; k < G::CPL; ++k) mine[k] = biased_fixed22(f[k], scl);
@@ -536,16 +552,17 @@ struct VStep {
     int jm = jbase + lane / (4 * G::NE);
     const int p = (lane / G::NE) % 4, e = lane % G::NE;
     jm = jm < nb ? jm : jbase;
-    if (lane < G::COOP) b.meta = ld_stream4(r.rec_ptr(jm) + G::VMETA + 4 * (e * kBlock + 4 * p));
+    if (lane < G::COOP) b.meta = ld_stream4(r.at(jm, G::VMETA + 4 * (e * kBlock + 4 * p)));
     int j = jbase + lane / G::LPB;
     j = j < nb ? j : jbase;
     const int chunk = lane % G::LPB;
-    const uint8_t* rb = r.rec_ptr(j);
+    const uint8_t* rb = r.at(j, G::VOFF + chunk * G::VW * 4);
 #pragma unroll
-    for (int i = 0; i < G::NV4; ++i) b.c[i] = ld_stream4(rb + G::VOFF + chunk * G::VW * 4 + 16 * i);
+    for (int i = 0; i < G::NV4; ++i) b.c[i] = ld_stream4(rb + 16 * i);
     if (G::DENSE) {
+      const uint8_t* rl = r.at(j, off_vlo(D) + chunk * G::VCH * 4);
 #pragma unroll
-      for (int i = 0; i < G::NV4; ++i) b.l[i] = ld_stream4(rb + off_vlo(D) + chunk * G::VCH * 4 + 16 * i);
+      for (int i = 0; i < G::NV4; ++i) b.l[i] = ld_stream4(rl + 16 * i);
     }
   }
 

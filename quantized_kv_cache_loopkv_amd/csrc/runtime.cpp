@@ -103,6 +103,9 @@ loopkv_status loopkv_create(const loopkv_config* cfg, loopkv_ctx** out) {
     return fail(LOOPKV_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)", cfg->head_dim);
   if (cfg->group_size != lkv::kGroup) return fail(LOOPKV_ERR_UNSUPPORTED, "group_size must be 32");
   if (cfg->block_tokens != lkv::kBlock) return fail(LOOPKV_ERR_UNSUPPORTED, "block_tokens must be 16");
+  if ((uint64_t)cfg->num_blocks * (uint64_t)cfg->n_heads * lkv::record_bytes(lkv::KIND_Q4, cfg->head_dim) > 0xFFFFFFFFull)
+    return fail(LOOPKV_ERR_UNSUPPORTED, "a cell's pool (num_blocks x n_heads x %d-byte records) must stay below 4 GiB",
+                lkv::record_bytes(lkv::KIND_Q4, cfg->head_dim));
   if ((long long)cfg->n_loops * cfg->n_layers > lkv::kMaxCells)
     return fail(LOOPKV_ERR_UNSUPPORTED, "at most %d cells", lkv::kMaxCells);
   if (cfg->layout != LOOPKV_LAYOUT_PLANES && cfg->layout != LOOPKV_LAYOUT_KIVI4)

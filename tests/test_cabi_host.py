@@ -62,11 +62,19 @@ def _create(**kw):
     (dict(n_loops=0), B.ERR_INVALID_ARG), (dict(n_heads=0), B.ERR_INVALID_ARG),
     (dict(num_blocks=0), B.ERR_INVALID_ARG), (dict(max_seqs=0), B.ERR_INVALID_ARG),
     (dict(n_loops=6, n_layers=24), B.ERR_UNSUPPORTED), (dict(layout=5), B.ERR_INVALID_ARG),
+    # a cell's pool must stay below 4 GiB: 104858 x 16 x 2560 B > 2^32 - 1
+    (dict(num_blocks=104858), B.ERR_UNSUPPORTED),
 ])
 def test_create_rejects(kw, status):
     s, h = _create(**kw)
     assert s == status and not h.value
     assert lkv.lib().loopkv_last_error().decode()
+
+
+def test_create_accepts_pool_just_under_4gib():
+    s, h = _create(num_blocks=104857)   # 104857 x 16 x 2560 B = 2^32 - 2560
+    assert s == B.OK and h.value
+    lkv.lib().loopkv_destroy(h)
 
 
 def test_plan_rules_and_workspace_sizes():

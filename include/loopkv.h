@@ -96,14 +96,16 @@ typedef enum { LOOPKV_LAYOUT_PLANES = 0, LOOPKV_LAYOUT_KIVI4 = 1 } loopkv_layout
 
 typedef struct {
   int32_t n_loops, n_layers; /* cells = n_loops * n_layers, row-major [loop][layer] */
-  int32_t n_heads;           /* KV heads = query heads (MHA) */
+  int32_t n_heads;           /* query heads */
   int32_t head_dim;          /* 64 or 128 */
   int32_t group_size;        /* must be 32 */
   int32_t block_tokens;      /* must be 16 */
   int32_t num_blocks;        /* physical blocks in each storing cell's pool; a pool
-                                (num_blocks x n_heads x 20*head_dim bytes) stays below 4 GiB */
+                                (num_blocks x KV heads x 20*head_dim bytes) stays below 4 GiB */
   int32_t max_seqs;          /* sequence slots (tail buffers) */
   int32_t layout;            /* loopkv_layout; KIVI4 requires an all-4-bit plan */
+  int32_t n_kv_heads;        /* KV heads (0: = n_heads, MHA); divides n_heads. Query head h
+                                reads KV head h / (n_heads / n_kv_heads) (grouped queries) */
 } loopkv_config;
 
 typedef struct loopkv_ctx loopkv_ctx;

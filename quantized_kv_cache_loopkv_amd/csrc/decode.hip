@@ -1158,10 +1158,23 @@ enum : int { VAR_KIVI = 0, VAR_DENSE = 1, VAR_COARSE = 2, VAR_SPARSE = 3, VAR_SK
 template <int D, int VAR, int PH>
 __global__ void __launch_bounds__(kThreads, kWavesPerSimd) k_decode(DecodeArgs a) {
   extern __shared__ float smem[];
-  // PH_PART: workgroup (row, split), the splits of a row adjacent
-  const int row = PH == PH_PART ? blockIdx.x / a.n_split : blockIdx.x;
+  // Rows are (cell, sequence, query head). PH_PART: workgroup (row, split), the splits of a
+  // row adjacent. PH_ROW with grouped queries (G query heads per KV head): workgroups are
+  // dispatched round-robin over the 8 XCDs, so the G rows of one KV head take the block
+  // indices 8 apart (same XCD, same L2, dispatched together) and stream the same records.
+  const int G = a.n_heads / a.n_kv_heads;
+  int row;
+  if (PH == PH_ROW && G > 1) {
+    const int span = 8 * G, q = blockIdx.x / span, rem = blockIdx.x % span;
+    const int gi = 8 * q + rem % 8;   // (cell, sequence, KV head)
+    if (gi >= a.n_cells * a.n_seqs * a.n_kv_heads) return;   // grid padding
+    row = (gi / a.n_kv_heads) * a.n_heads + (gi % a.n_kv_heads) * G + rem / 8;
+  } else {
+    row = PH == PH_PART ? blockIdx.x / a.n_split : blockIdx.x;
+  }
   const int split = PH == PH_PART ? blockIdx.x % a.n_split : 0;
   const int h = row % a.n_heads;
+  const int kh = h / G;   // the KV head this query head reads
   const int b = (row / a.n_heads) % a.n_seqs;
   const int ci = row / (a.n_heads * a.n_seqs);
   const DecodeCell cell = a.cells[ci];
@@ -1195,7 +1208,7 @@ __global__ void __launch_bounds__(kThreads, kWavesPerSimd) k_decode(DecodeArgs a
   r.pool = a.ws + cell.pool_off;
   r.boff = sm.boff;
   const int slot = a.seq_slots ? a.seq_slots[b] : b;
-  r.tail = reinterpret_cast<const uint16_t*>(a.ws + cell.tail_off) + ((size_t)slot * a.n_heads + h) * tail_elems(D);
+  r.tail = reinterpret_cast<const uint16_t*>(a.ws + cell.tail_off) + ((size_t)slot * a.n_kv_heads + kh) * tail_elems(D);
   r.N = N;
   r.n_q = (N / kGroup) * kGroup;
   r.n_groups = N / kGroup;
@@ -1204,7 +1217,7 @@ __global__ void __launch_bounds__(kThreads, kWavesPerSimd) k_decode(DecodeArgs a
   const int32_t* bt = a.block_table + (size_t)b * a.bt_stride;
   const int nbq = r.n_q / kBlock;
   const uint32_t rec256 = (uint32_t)(record_bytes(cell.kind, D) / 256);
-  for (int j = tid; j < nbq; j += kThreads) sm.boff[j] = ((uint32_t)bt[j] * (uint32_t)a.n_heads + (uint32_t)h) * rec256;
+  for (int j = tid; j < nbq; j += kThreads) sm.boff[j] = ((uint32_t)bt[j] * (uint32_t)a.n_kv_heads + (uint32_t)kh) * rec256;
   for (int d = tid; d < D; d += kThreads) {
     const size_t qi = orow * D + d;
     const float qv = a.q_bf16 ? bf16f(reinterpret_cast<const uint16_t*>(a.q)[qi]) : reinterpret_cast<const float*>(a.q)[qi];
@@ -1236,12 +1249,21 @@ static void launch_phase(const DecodeArgs& a, size_t grid, size_t lds, hipStream
   hipLaunchKernelGGL((k_decode<D, VAR, PH>), dim3((unsigned)grid), dim3(kThreads), lds, stream, a);
 }
 
+// Grid of a one-workgroup-per-row launch: with grouped queries the rows of 8 KV heads form
+// one span of 8 G block indices (see k_decode), padded to whole spans.
+static size_t row_grid(const DecodeArgs& a, size_t rows) {
+  const int G = a.n_heads / a.n_kv_heads;
+  if (G == 1) return rows;
+  const size_t groups = rows / G;
+  return (groups + 7) / 8 * 8 * (size_t)G;
+}
+
 template <int D, int VAR>
 static void launch_variant(const DecodeArgs& a, size_t rows, size_t lds, hipStream_t stream) {
   if constexpr (VAR == VAR_SKIP) {   // one workgroup per row only (the host refuses a split)
-    launch_phase<D, VAR, PH_ROW>(a, rows, lds, stream);
+    launch_phase<D, VAR, PH_ROW>(a, row_grid(a, rows), lds, stream);
   } else if (a.n_split < 1) {
-    launch_phase<D, VAR, PH_ROW>(a, rows, lds, stream);
+    launch_phase<D, VAR, PH_ROW>(a, row_grid(a, rows), lds, stream);
   } else {   // stream order: every partial is written before the finishing launch reads it
     launch_phase<D, VAR, PH_PART>(a, rows * (size_t)a.n_split, lds, stream);
     launch_phase<D, VAR, PH_FINISH>(a, rows, lds, stream);

@@ -73,6 +73,7 @@ struct DecodeArgs {
   const int32_t* seq_lens;
   int32_t q_bf16, out_bf16;
   int32_t n_seqs, n_heads, bt_stride, max_len, sel_words, n_cells;
+  int32_t n_kv_heads;   // divides n_heads; query head h reads KV head h / (n_heads / n_kv_heads)
   float tau, sm_scale;
   // Split of each row's tokens over n_split workgroups (n_split 0: one workgroup per row).
   // part: [rows][n_split][2 + D] floats (m, l, unnormalized o relative to m);

@@ -25,6 +25,7 @@ size_t decode_lds_bytes(int max_len, int head_dim);
 
 struct loopkv_ctx {
   loopkv_config cfg;
+  int kvh = 0;                    // KV heads (cfg.n_kv_heads, or n_heads when 0)
   bool has_plan = false;
   std::vector<uint8_t> kinds;     // per cell, loopkv_cell_kind
   std::vector<int> storage;       // per cell: cell whose cache it reads
@@ -99,12 +100,15 @@ loopkv_status loopkv_create(const loopkv_config* cfg, loopkv_ctx** out) {
   *out = nullptr;
   if (cfg->n_loops < 1 || cfg->n_layers < 1 || cfg->n_heads < 1 || cfg->num_blocks < 1 || cfg->max_seqs < 1)
     return fail(LOOPKV_ERR_INVALID_ARG, "n_loops, n_layers, n_heads, num_blocks and max_seqs must be >= 1");
+  if (cfg->n_kv_heads < 0 || (cfg->n_kv_heads > 0 && cfg->n_heads % cfg->n_kv_heads != 0))
+    return fail(LOOPKV_ERR_INVALID_ARG, "n_kv_heads %d must be 0 or divide n_heads %d", cfg->n_kv_heads, cfg->n_heads);
+  const int kvh = cfg->n_kv_heads ? cfg->n_kv_heads : cfg->n_heads;
   if (cfg->head_dim != 64 && cfg->head_dim != 128)
     return fail(LOOPKV_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)", cfg->head_dim);
   if (cfg->group_size != lkv::kGroup) return fail(LOOPKV_ERR_UNSUPPORTED, "group_size must be 32");
   if (cfg->block_tokens != lkv::kBlock) return fail(LOOPKV_ERR_UNSUPPORTED, "block_tokens must be 16");
-  if ((uint64_t)cfg->num_blocks * (uint64_t)cfg->n_heads * lkv::record_bytes(lkv::KIND_Q4, cfg->head_dim) > 0xFFFFFFFFull)
-    return fail(LOOPKV_ERR_UNSUPPORTED, "a cell's pool (num_blocks x n_heads x %d-byte records) must stay below 4 GiB",
+  if ((uint64_t)cfg->num_blocks * (uint64_t)kvh * lkv::record_bytes(lkv::KIND_Q4, cfg->head_dim) > 0xFFFFFFFFull)
+    return fail(LOOPKV_ERR_UNSUPPORTED, "a cell's pool (num_blocks x KV heads x %d-byte records) must stay below 4 GiB",
                 lkv::record_bytes(lkv::KIND_Q4, cfg->head_dim));
   if ((long long)cfg->n_loops * cfg->n_layers > lkv::kMaxCells)
     return fail(LOOPKV_ERR_UNSUPPORTED, "at most %d cells", lkv::kMaxCells);
@@ -112,6 +116,7 @@ loopkv_status loopkv_create(const loopkv_config* cfg, loopkv_ctx** out) {
     return fail(LOOPKV_ERR_INVALID_ARG, "unknown layout %d", cfg->layout);
   loopkv_ctx* c = new loopkv_ctx();
   c->cfg = *cfg;
+  c->kvh = kvh;
   *out = c;
   return ok();
 }
@@ -133,7 +138,7 @@ loopkv_status loopkv_plan(loopkv_ctx* c, const uint8_t* kinds) {
   c->storage.resize(n);
   c->pool_off.assign(n, 0);
   c->tail_off.assign(n, 0);
-  const int D = c->cfg.head_dim, H = c->cfg.n_heads;
+  const int D = c->cfg.head_dim, H = c->kvh;   // records and tails per KV head
   size_t off = 0;
   for (int i = 0; i < n; ++i) {
     c->storage[i] = kinds[i] == LOOPKV_CELL_SHARE ? (L - 1) * NL + i % NL : i;
@@ -219,7 +224,7 @@ loopkv_status loopkv_append(loopkv_ctx* c, hipStream_t stream, int32_t loop, int
   a.kv_bf16 = kv_dtype == LOOPKV_BF16;
   a.n_seqs = n_seqs;
   a.n_new = n_new;
-  a.n_heads = c->cfg.n_heads;
+  a.n_heads = c->kvh;   // the append's inputs hold the KV heads
   a.bt_stride = bt_stride;
   int nc = 0;
   for (int i = first; i < first + count; ++i) {
@@ -292,6 +297,7 @@ loopkv_status decode_common(loopkv_ctx* c, hipStream_t stream, int32_t loop, int
   a.out_bf16 = out_dtype == LOOPKV_BF16;
   a.n_seqs = n_seqs;
   a.n_heads = c->cfg.n_heads;
+  a.n_kv_heads = c->kvh;
   a.bt_stride = bt_stride;
   a.max_len = max_len;
   a.sel_words = (max_len + 31) / 32;

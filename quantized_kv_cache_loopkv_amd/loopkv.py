@@ -40,7 +40,8 @@ class LoopKVError(RuntimeError):
 class _Config(ctypes.Structure):
     _fields_ = [("n_loops", ctypes.c_int32), ("n_layers", ctypes.c_int32), ("n_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("group_size", ctypes.c_int32), ("block_tokens", ctypes.c_int32),
-                ("num_blocks", ctypes.c_int32), ("max_seqs", ctypes.c_int32), ("layout", ctypes.c_int32)]
+                ("num_blocks", ctypes.c_int32), ("max_seqs", ctypes.c_int32), ("layout", ctypes.c_int32),
+                ("n_kv_heads", ctypes.c_int32)]
 
 
 class _CellCost(ctypes.Structure):
@@ -140,8 +141,10 @@ class Context:
     """One LoopKV cache: config, plan, caller-owned workspace."""
 
     def __init__(self, n_loops: int, n_layers: int, n_heads: int, head_dim: int, num_blocks: int,
-                 max_seqs: int, layout: int = LAYOUT_PLANES):
-        self.cfg = _Config(n_loops, n_layers, n_heads, head_dim, 32, 16, num_blocks, max_seqs, layout)
+                 max_seqs: int, layout: int = LAYOUT_PLANES, n_kv_heads: int = 0):
+        """n_kv_heads: KV heads (0: one per query head); query head h reads KV head
+        h // (n_heads // n_kv_heads)."""
+        self.cfg = _Config(n_loops, n_layers, n_heads, head_dim, 32, 16, num_blocks, max_seqs, layout, n_kv_heads)
         h = ctypes.c_void_p()
         _check(lib().loopkv_create(ctypes.byref(self.cfg), ctypes.byref(h)))
         self._h = h
@@ -153,6 +156,10 @@ class Context:
         if h is not None and h.value and _lib is not None:
             _lib.loopkv_destroy(h)
             self._h = None
+
+    @property
+    def kv_heads(self) -> int:
+        return self.cfg.n_kv_heads or self.cfg.n_heads
 
     @property
     def n_cells(self) -> int:
@@ -203,8 +210,8 @@ class Context:
             if k.dim() != 4:
                 raise ValueError("single-cell append needs k of shape [n_seqs][n_new][H][D]")
             n_seqs, n_new = k.shape[0], k.shape[1]
-        if k.shape[-2:] != (self.cfg.n_heads, self.cfg.head_dim):
-            raise ValueError("k trailing dims must be [H][D]")
+        if k.shape[-2:] != (self.kv_heads, self.cfg.head_dim):
+            raise ValueError("k trailing dims must be [KV heads][D]")
         bt = _dev_i32(block_table, "block_table", n_seqs)
         _dev_i32(seq_lens, "seq_lens", n_seqs)
         _dev_i32(seq_slots, "seq_slots", n_seqs)
@@ -233,6 +240,8 @@ class Context:
         n_seqs = q.shape[1] if cell is None else q.shape[0]
         if (cell is None and (q.dim() != 4 or q.shape[0] != self.n_cells)) or (cell is not None and q.dim() != 3):
             raise ValueError("q has the wrong rank for this call")
+        if q.shape[-2:] != (self.cfg.n_heads, self.cfg.head_dim):
+            raise ValueError("q trailing dims must be [query heads][D]")
         D = self.cfg.head_dim
         if sm_scale is None:
             sm_scale = 1.0 / math.sqrt(D)

@@ -47,6 +47,11 @@ class Config:
     append_steps: int = 0         # decode steps, each preceded by a 1-token append
     seed: int = 0
     plan: Optional[np.ndarray] = field(default=None, repr=False)
+    n_kv_heads: int = 0           # 0: one KV head per query head
+
+    @property
+    def kv_heads(self) -> int:
+        return self.n_kv_heads or self.n_heads
 
     @property
     def n_cells(self) -> int:
@@ -120,11 +125,13 @@ def make_config(name: str, seed: int = 0) -> Config:
 def small_config(name: str, n_loops: int, n_layers: int, n_heads: int, head_dim: int,
                  lengths: List[int], taus: List[float], plan=None, seed: int = 0,
                  outlier_count: int = 0, outlier_mult: float = 1.0, cell_scales: bool = False,
-                 shuffled: bool = False, q_fp32: bool = False, append_steps: int = 0) -> Config:
+                 shuffled: bool = False, q_fp32: bool = False, append_steps: int = 0,
+                 n_kv_heads: int = 0) -> Config:
     """A reduced configuration with the same generators, for tests that the oracle finishes quickly."""
     cfg = Config(name, n_loops, n_layers, n_heads, head_dim, len(lengths), list(lengths), list(taus),
                  q_fp32=q_fp32, outlier_count=outlier_count, outlier_mult=outlier_mult,
-                 cell_scales=cell_scales, shuffled=shuffled, append_steps=append_steps, seed=seed)
+                 cell_scales=cell_scales, shuffled=shuffled, append_steps=append_steps, seed=seed,
+                 n_kv_heads=n_kv_heads)
     if plan is None:
         plan = np.zeros((n_loops, n_layers), dtype=np.uint8) if n_loops * n_layers == 1 \
             else random_plan(n_loops, n_layers, seed)
@@ -133,8 +140,8 @@ def small_config(name: str, n_loops: int, n_layers: int, n_heads: int, head_dim:
 
 
 def factor_table(cfg: Config) -> np.ndarray:
-    """float32 [cells][2 (K, V)][H][D]: outlier multiplier times the cell's scale."""
-    C, H, D = cfg.n_cells, cfg.n_heads, cfg.head_dim
+    """float32 [cells][2 (K, V)][KV heads][D]: outlier multiplier times the cell's scale."""
+    C, H, D = cfg.n_cells, cfg.kv_heads, cfg.head_dim
     f = np.ones((C, 2, H, D), dtype=np.float64)
     if cfg.cell_scales:
         rng = np.random.default_rng([cfg.seed, 2])
@@ -173,7 +180,7 @@ def num_blocks(cfg: Config) -> int:
 
 
 def kv_index(cfg: Config, b, t, h, d):
-    T, H, D = cfg.token_stride, cfg.n_heads, cfg.head_dim
+    T, H, D = cfg.token_stride, cfg.kv_heads, cfg.head_dim
     b = np.asarray(b, dtype=np.uint64)
     t = np.asarray(t, dtype=np.uint64)
     h = np.asarray(h, dtype=np.uint64)
@@ -182,7 +189,7 @@ def kv_index(cfg: Config, b, t, h, d):
 
 
 def kv_row_bits(cfg: Config, cell: int, b: int, h: int, t0: int, t1: int, factors=None):
-    """bf16 bits of K and V, each [t1-t0][D], for one (cell, sequence, head)."""
+    """bf16 bits of K and V, each [t1-t0][D], for one (cell, sequence, KV head)."""
     if factors is None:
         factors = factor_table(cfg)
     D = cfg.head_dim
@@ -195,10 +202,10 @@ def kv_row_bits(cfg: Config, cell: int, b: int, h: int, t0: int, t1: int, factor
 
 
 def kv_tensor_bits(cfg: Config, cell: int, t0: int, t1: int, factors=None):
-    """bf16 bits of K and V, each [B][t1-t0][H][D], for one cell (append input layout)."""
+    """bf16 bits of K and V, each [B][t1-t0][KV heads][D], for one cell (append input layout)."""
     if factors is None:
         factors = factor_table(cfg)
-    B, H, D = cfg.batch, cfg.n_heads, cfg.head_dim
+    B, H, D = cfg.batch, cfg.kv_heads, cfg.head_dim
     b = np.arange(B, dtype=np.uint64)[:, None, None, None]
     t = np.arange(t0, t1, dtype=np.uint64)[None, :, None, None]
     h = np.arange(H, dtype=np.uint64)[None, None, :, None]

@@ -37,7 +37,8 @@ class Workload:
             plan = np.zeros_like(plan)
         self.plan = plan
         self.nb = R.num_blocks(cfg)
-        self.ctx = lkv.Context(cfg.n_loops, cfg.n_layers, cfg.n_heads, cfg.head_dim, self.nb, cfg.batch, layout)
+        self.ctx = lkv.Context(cfg.n_loops, cfg.n_layers, cfg.n_heads, cfg.head_dim, self.nb, cfg.batch, layout,
+                               n_kv_heads=cfg.n_kv_heads)
         self.ctx.plan(plan.tolist())
         self.ws = torch.empty(self.ctx.workspace_bytes(), dtype=torch.uint8, device=device)
         self.ctx.bind(self.ws)
@@ -46,7 +47,7 @@ class Workload:
         self.lengths = np.array(cfg.lengths, dtype=np.int64)
         self.seq_lens = torch.zeros(cfg.batch, dtype=torch.int32, device=device)
         self.factors = R.factor_table(cfg)
-        big = cfg.batch * max(cfg.lengths) * cfg.n_heads * cfg.head_dim > (1 << 24)
+        big = cfg.batch * max(cfg.lengths) * cfg.kv_heads * cfg.head_dim > (1 << 24)
         self.gpu_synth = big if gpu_synth is None else gpu_synth
         self.factors_dev = torch.from_numpy(self.factors).to(device) if self.gpu_synth else None
 
@@ -64,11 +65,11 @@ class Workload:
             from synth import gpu as G
             B = cfg.batch if seqs is None else len(seqs)
             assert seqs is None, "GPU draw covers every sequence"
-            K = torch.empty((B, n, cfg.n_heads, cfg.head_dim), dtype=torch.bfloat16, device=self.device)
+            K = torch.empty((B, n, cfg.kv_heads, cfg.head_dim), dtype=torch.bfloat16, device=self.device)
             V = torch.empty_like(K)
-            G.kv_bf16(cfg.seed, 4 * cell + R.STREAM_K, B, n, t0, cfg.token_stride, cfg.n_heads, cfg.head_dim,
+            G.kv_bf16(cfg.seed, 4 * cell + R.STREAM_K, B, n, t0, cfg.token_stride, cfg.kv_heads, cfg.head_dim,
                       self.factors_dev[cell, 0].contiguous(), K)
-            G.kv_bf16(cfg.seed, 4 * cell + R.STREAM_V, B, n, t0, cfg.token_stride, cfg.n_heads, cfg.head_dim,
+            G.kv_bf16(cfg.seed, 4 * cell + R.STREAM_V, B, n, t0, cfg.token_stride, cfg.kv_heads, cfg.head_dim,
                       self.factors_dev[cell, 1].contiguous(), V)
             return K, V
         kb, vb = R.kv_tensor_bits(cfg, cell, t0, t0 + n, self.factors)
@@ -79,13 +80,13 @@ class Workload:
     def kv_seq_gpu(self, cell, b, t0, n):
         from synth import gpu as G
         cfg = self.cfg
-        K = torch.empty((1, n, cfg.n_heads, cfg.head_dim), dtype=torch.bfloat16, device=self.device)
+        K = torch.empty((1, n, cfg.kv_heads, cfg.head_dim), dtype=torch.bfloat16, device=self.device)
         V = torch.empty_like(K)
         t0s = torch.tensor([t0], dtype=torch.int32, device=self.device)
         # draw with the sequence index b: use a one-sequence view whose element index uses b
-        G.kv_bf16(cfg.seed, 4 * cell + R.STREAM_K, 1, n, 0, cfg.token_stride, cfg.n_heads, cfg.head_dim,
+        G.kv_bf16(cfg.seed, 4 * cell + R.STREAM_K, 1, n, 0, cfg.token_stride, cfg.kv_heads, cfg.head_dim,
                   self.factors_dev[cell, 0].contiguous(), K, t0s=t0s + b * cfg.token_stride)
-        G.kv_bf16(cfg.seed, 4 * cell + R.STREAM_V, 1, n, 0, cfg.token_stride, cfg.n_heads, cfg.head_dim,
+        G.kv_bf16(cfg.seed, 4 * cell + R.STREAM_V, 1, n, 0, cfg.token_stride, cfg.kv_heads, cfg.head_dim,
                   self.factors_dev[cell, 1].contiguous(), V, t0s=t0s + b * cfg.token_stride)
         return K, V
 
@@ -124,9 +125,9 @@ class Workload:
 
     def append_inputs(self, step: int):
         """Inputs of the one-token append before decode step ``step``: bf16 K, V
-        [cells][B][1][H][D] (token lengths[b] + step of each sequence), lengths before and after."""
+        [cells][B][1][KV heads][D] (token lengths[b] + step of each sequence), lengths before and after."""
         cfg = self.cfg
-        C, B, H, D = cfg.n_cells, cfg.batch, cfg.n_heads, cfg.head_dim
+        C, B, H, D = cfg.n_cells, cfg.batch, cfg.kv_heads, cfg.head_dim
         K = torch.zeros((C, B, 1, H, D), dtype=torch.bfloat16, device=self.device)
         V = torch.zeros_like(K)
         pos = torch.tensor([n + step for n in cfg.lengths], dtype=torch.int32, device=self.device)
@@ -207,7 +208,7 @@ class Workload:
         st = self.ctx.cell_storage(loop, layer)
         rb = st["record_bytes"]
         phys = int(self.bt_np[b, j])
-        off = st["pool_offset"] + (phys * self.cfg.n_heads + h) * rb
+        off = st["pool_offset"] + (phys * self.cfg.kv_heads + h) * rb
         return self.ws[off:off + rb].cpu().numpy()
 
     def tail(self, cell: int, b: int, h: int) -> np.ndarray:
@@ -216,11 +217,17 @@ class Workload:
         st = self.ctx.cell_storage(loop, layer)
         D = self.cfg.head_dim
         n = 2 * 32 * D * 2
-        off = st["tail_offset"] + (b * self.cfg.n_heads + h) * n
+        off = st["tail_offset"] + (b * self.cfg.kv_heads + h) * n
         return self.ws[off:off + n].cpu().numpy().view(np.uint16).reshape(2, 32, D)
 
 
+def kv_head(cfg: R.Config, h: int) -> int:
+    """The KV head query head h reads (grouped queries: h // (query heads per KV head))."""
+    return h // (cfg.n_heads // cfg.kv_heads)
+
+
 def oracle_row_inputs(cfg: R.Config, cell_store: int, b: int, h: int, n_tokens: int, factors=None):
+    """History (bf16 bits and float64 values of K and V) of KV head h of a storage cell."""
     kb, vb = R.kv_row_bits(cfg, cell_store, b, h, 0, n_tokens, factors)
     K = bf16_bits_to_f32(kb).astype(np.float64)
     V = bf16_bits_to_f32(vb).astype(np.float64)

@@ -45,7 +45,7 @@ def test_synth_library_exports():
 
 def _cfg(**kw):
     base = dict(n_loops=4, n_layers=24, n_heads=16, head_dim=128, group_size=32, block_tokens=16,
-                num_blocks=64, max_seqs=4, layout=0)
+                num_blocks=64, max_seqs=4, layout=0, n_kv_heads=0)
     base.update(kw)
     return B._Config(*[base[k] for k, _ in B._Config._fields_])
 
@@ -64,6 +64,8 @@ def _create(**kw):
     (dict(n_loops=6, n_layers=24), B.ERR_UNSUPPORTED), (dict(layout=5), B.ERR_INVALID_ARG),
     # a cell's pool must stay below 4 GiB: 104858 x 16 x 2560 B > 2^32 - 1
     (dict(num_blocks=104858), B.ERR_UNSUPPORTED),
+    (dict(n_kv_heads=3), B.ERR_INVALID_ARG), (dict(n_kv_heads=-1), B.ERR_INVALID_ARG),
+    (dict(n_kv_heads=32), B.ERR_INVALID_ARG),
 ])
 def test_create_rejects(kw, status):
     s, h = _create(**kw)
@@ -267,3 +269,20 @@ def test_skip_decode_validation():
                                           vp(FAKE_DEV), 64, ctypes.c_float(-1.0), ctypes.c_float(0.125),
                                           vp(FAKE_DEV), 0, None)
     assert s == B.ERR_INVALID_ARG
+
+
+def test_grouped_query_workspace_and_shapes():
+    """KV heads size the pools and tails; a pool is capped by KV heads, not query heads."""
+    mha = lkv.Context(2, 2, 16, 128, 64, 4)
+    gqa = lkv.Context(2, 2, 16, 128, 64, 4, n_kv_heads=4)
+    for c in (mha, gqa):
+        c.plan([0, 1, 0, 0])
+    per_head = 64 * 2560 * 3 + 64 * 1536 + 4 * 2 * 32 * 128 * 2 * 4   # 3 Q4 + 1 Q2 pools, 4 tails
+    assert mha.workspace_bytes() == 16 * per_head
+    assert gqa.workspace_bytes() == 4 * per_head
+    assert gqa.kv_heads == 4 and mha.kv_heads == 16
+    s, h = _create(num_blocks=104857 * 4, n_kv_heads=4)   # 4 KV heads: the pool stays under 4 GiB
+    assert s == B.OK
+    lkv.lib().loopkv_destroy(h)
+    s, h = _create(num_blocks=104857 * 4)                 # the same blocks with 16 KV heads do not
+    assert s == B.ERR_UNSUPPORTED

@@ -18,7 +18,7 @@ import quantized_kv_cache_loopkv_amd as lkv
 from oracle import loopkv_oracle as O
 from synth import recipes as R
 from synth.philox import f32_to_bf16_bits
-from tests.harness import Workload, oracle_row_inputs
+from tests.harness import Workload, kv_head, oracle_row_inputs
 from tests.test_gpu_parity import check_row
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
@@ -45,7 +45,7 @@ def _check_records(wl, cell, b, h, n_tokens, blocks):
     cfg = wl.cfg
     st = O.storage_cell(cfg.plan, cell)
     bits = 2 if cfg.plan.reshape(-1)[st] == R.Q2 else 4
-    _, _, K, V = oracle_row_inputs(cfg, st, b, h, n_tokens, wl.factors)
+    _, _, K, V = oracle_row_inputs(cfg, st, b, kv_head(cfg, h), n_tokens, wl.factors)
     qh = O.quantize_history(K, V, bits)
     for j in blocks:
         if 16 * (j + 1) <= qh["n_q"]:

@@ -16,7 +16,7 @@ import quantized_kv_cache_loopkv_amd as lkv
 from oracle import loopkv_oracle as O
 from synth import recipes as R
 from synth.philox import f32_to_bf16_bits
-from tests.harness import Workload, oracle_row_inputs, rel_err, sel_bits_from_mask
+from tests.harness import Workload, kv_head, oracle_row_inputs, rel_err, sel_bits_from_mask
 
 pytestmark = pytest.mark.gpu
 
@@ -36,7 +36,7 @@ def check_row(wl: Workload, out, sm, q, cell, b, h, tau, n_tokens, label=""):
     kind = O.target_kind(wl.plan.reshape(cfg.n_loops, cfg.n_layers), cell)
     if wl.layout == lkv.LAYOUT_KIVI4:
         kind = "kivi4"
-    _, _, K, V = oracle_row_inputs(cfg, st, b, h, n_tokens, wl.factors)
+    _, _, K, V = oracle_row_inputs(cfg, st, b, kv_head(cfg, h), n_tokens, wl.factors)
     qv = q[cell, b, h].float().cpu().numpy().astype(np.float64)
     sig = np.float32(1.0 / math.sqrt(cfg.head_dim))
     o_ref, sel_ref, phat = O.decode_row(qv, K, V, kind, tau, float(sig))

@@ -19,7 +19,7 @@ import torch
 import quantized_kv_cache_loopkv_amd as lkv
 from oracle import loopkv_oracle as O
 from synth import recipes as R
-from tests.harness import Workload, oracle_row_inputs, rel_err, sel_bits_from_mask
+from tests.harness import Workload, kv_head, oracle_row_inputs, rel_err, sel_bits_from_mask
 from tests.test_gpu_parity import TIE, TOL
 
 pytestmark = pytest.mark.gpu
@@ -35,7 +35,7 @@ def _check_skip_row(wl, out, sm, q, cell, b, h, tau, n_tokens, label):
     plan = wl.plan.reshape(cfg.n_loops, cfg.n_layers)
     st = O.storage_cell(plan, cell)
     kind = O.target_kind(plan, cell)
-    _, _, K, V = oracle_row_inputs(cfg, st, b, h, n_tokens, wl.factors)
+    _, _, K, V = oracle_row_inputs(cfg, st, b, kv_head(cfg, h), n_tokens, wl.factors)
     qv = q[cell, b, h].float().cpu().numpy().astype(np.float64)
     sig = float(np.float32(1.0 / math.sqrt(cfg.head_dim)))
     skip = kind == O.KIND_Q4

@@ -97,7 +97,7 @@ typedef enum { LOOPKV_LAYOUT_PLANES = 0, LOOPKV_LAYOUT_KIVI4 = 1 } loopkv_layout
 typedef struct {
   int32_t n_loops, n_layers; /* cells = n_loops * n_layers, row-major [loop][layer] */
   int32_t n_heads;           /* query heads */
-  int32_t head_dim;          /* 64 or 128 */
+  int32_t head_dim;          /* 64, 128 or 256 */
   int32_t group_size;        /* must be 32 */
   int32_t block_tokens;      /* must be 16 */
   int32_t num_blocks;        /* physical blocks in each storing cell's pool; a pool

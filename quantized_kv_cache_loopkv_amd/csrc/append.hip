@@ -139,8 +139,8 @@ __global__ void __launch_bounds__(256) k_quantize_groups(AppendArgs a) {
   const int slot = a.seq_slots ? a.seq_slots[b] : b;
   const int tid = threadIdx.x;
 
-  __shared__ float kx[kGroup][D];
-  __shared__ float vx[kGroup][D];
+  __shared__ uint16_t kx[kGroup][D];   // bf16 bits of the group's 32 tokens (exact values)
+  __shared__ uint16_t vx[kGroup][D];
   __shared__ uint8_t kc[kGroup][D];
   __shared__ uint8_t vc[kGroup][D];
   __shared__ uint32_t kmeta[D];
@@ -151,22 +151,22 @@ __global__ void __launch_bounds__(256) k_quantize_groups(AppendArgs a) {
   for (int idx = tid; complete && idx < kGroup * D; idx += blockDim.x) {
     const int i = idx / D, d = idx % D;
     const int p = g * kGroup + i;
-    float kf, vf;
+    uint16_t kb, vb;
     if (p < L0) {
-      kf = bf16_to_f32(tail[(0 * kGroup + (p % kGroup)) * D + d]);
-      vf = bf16_to_f32(tail[(1 * kGroup + (p % kGroup)) * D + d]);
+      kb = tail[(0 * kGroup + (p % kGroup)) * D + d];
+      vb = tail[(1 * kGroup + (p % kGroup)) * D + d];
     } else {
       const size_t e = ((((size_t)cell.in_cell * a.n_seqs + b) * a.n_new + (p - L0)) * a.n_heads + h) * D + d;
       if (a.kv_bf16) {
-        kf = bf16_to_f32(reinterpret_cast<const uint16_t*>(a.k)[e]);
-        vf = bf16_to_f32(reinterpret_cast<const uint16_t*>(a.v)[e]);
+        kb = reinterpret_cast<const uint16_t*>(a.k)[e];
+        vb = reinterpret_cast<const uint16_t*>(a.v)[e];
       } else {
-        kf = bf16_to_f32(f32_to_bf16_rne(reinterpret_cast<const float*>(a.k)[e]));
-        vf = bf16_to_f32(f32_to_bf16_rne(reinterpret_cast<const float*>(a.v)[e]));
+        kb = f32_to_bf16_rne(reinterpret_cast<const float*>(a.k)[e]);
+        vb = f32_to_bf16_rne(reinterpret_cast<const float*>(a.v)[e]);
       }
     }
-    kx[i][d] = kf;
-    vx[i][d] = vf;
+    kx[i][d] = kb;
+    vx[i][d] = vb;
   }
   __syncthreads();
   if constexpr (WITH_TAIL) {   // every read of the old tail is done (barrier above)
@@ -177,11 +177,12 @@ __global__ void __launch_bounds__(256) k_quantize_groups(AppendArgs a) {
   const int M = (cell.kind == KIND_Q2) ? 3 : 15;
   // K: one group per channel over the 32 tokens.
   for (int d = tid; d < D; d += blockDim.x)
-    quantize_group([&](int i) { return (double)kx[i][d]; }, M, &kc[0][d], D, &kmeta[d]);
+    quantize_group([&](int i) { return (double)bf16_to_f32(kx[i][d]); }, M, &kc[0][d], D, &kmeta[d]);
   // V: one group per token over each run of 32 channels.
   for (int task = tid; task < kGroup * (D / kGroup); task += blockDim.x) {
     const int i = task / (D / kGroup), e = task % (D / kGroup);
-    quantize_group([&](int j) { return (double)vx[i][e * kGroup + j]; }, M, &vc[i][e * kGroup], 1, &vmeta[i][e]);
+    quantize_group([&](int j) { return (double)bf16_to_f32(vx[i][e * kGroup + j]); }, M, &vc[i][e * kGroup], 1,
+                   &vmeta[i][e]);
   }
   __syncthreads();
 
@@ -273,6 +274,7 @@ static void launch_d(const AppendArgs& a, hipStream_t stream) {
 hipError_t launch_append(const AppendArgs& a, int head_dim, hipStream_t stream) {
   if (a.n_cells == 0 || a.n_seqs == 0 || a.n_new == 0) return hipSuccess;
   if (head_dim == 128) launch_d<128>(a, stream);
+  else if (head_dim == 256) launch_d<256>(a, stream);
   else launch_d<64>(a, stream);
   return hipGetLastError();
 }

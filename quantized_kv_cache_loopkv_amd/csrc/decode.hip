@@ -255,13 +255,13 @@ struct Acc {
 };
 
 // ----------------------------------------------------------------------------- step geometry
-// A step covers TPS tokens: 64, or 32 for 4-bit codes at D = 128, so that every lane reads
-// 32 bytes of K codes and 32 bytes of V codes (16 for 2-bit codes at D = 64).
+// A step covers TPS tokens: 64, or 32 for 4-bit codes at D = 128 and for D = 256, so that
+// every lane reads 32 bytes of K codes and 32 bytes of V codes (16 for 2-bit codes at D = 64).
 template <int D, int MODE>
 struct Geo {
   static constexpr bool KIVI = MODE == MODE_KIVI;
   static constexpr bool DENSE = MODE == MODE_DENSE;
-  static constexpr int TPS = (KIVI || DENSE) && D == 128 ? 32 : 64;
+  static constexpr int TPS = (D == 256 || ((KIVI || DENSE) && D == 128)) ? 32 : 64;
   static constexpr int GPS = TPS / kGroup;      // groups per step
   static constexpr int BPS = TPS / kBlock;      // blocks per step
   // K: a group is covered by LPG lanes = 2 blocks x 4 token quads x CPG column lanes;
@@ -687,10 +687,11 @@ struct VStep {
 template <int D>
 __device__ void exact_v_pass(const Row& r, const float* weights, const uint32_t* selm, int lane, int w,
                              float* acc) {
-  constexpr int VCH = D / 16;
+  using GC = Geo<D, MODE_COARSE>;
+  constexpr int VCH = GC::VCH;
   const int nb = r.n_q / kBlock;
-  const int jb = lane / 16, chunk = lane % 16, e = chunk * VCH / kGroup;
-  for (int j = w * 4 + jb; j < nb; j += 4 * kWaves) {
+  const int jb = lane / GC::LPB, chunk = lane % GC::LPB, e = chunk * VCH / kGroup;
+  for (int j = w * GC::BPS + jb; j < nb; j += GC::BPS * kWaves) {
     const uint8_t* rb = r.rec_ptr(j);
     uint32_t hw[VCH], lw[VCH];
 #pragma unroll
@@ -721,7 +722,7 @@ struct Smem {
   float* qs;        // [D]
   float* qperm;     // [D] sigma q in K-meta position order
   float* wscr;      // [kWaves][kWaveScratch]
-  float* misc;      // [96]
+  float* misc;      // [96]: per wave m, l, removed weight (0..23), constant terms [kWaves][NE] (32..)
 };
 
 // ----------------------------------------------------------------------------- row body
@@ -757,6 +758,7 @@ __device__ void row_body(const DecodeArgs& a, const Row& r, const Smem& sm, size
   float* misc = sm.misc;
   constexpr int NE = G::NE;
   constexpr int VCH = G::VCH;
+  static_assert(32 + kWaves * NE <= 96, "constant terms of every wave fit the exchange words");
 
   Acc<VCH> st;
   st.zero();
@@ -929,19 +931,21 @@ __device__ void row_body(const DecodeArgs& a, const Row& r, const Smem& sm, size
       for (int g = tid; g < a.sel_words; g += kThreads) smo[g] = g < r.n_groups ? selm[g] : 0u;
     }
     // Gather: wave w takes the 64-group spans w, w + 8, ... and corrects their selected
-    // groups two at a time.
+    // groups as many at a time as a coarse step holds (two; one at D = 256).
     using KR = KStep<D, MODE_COARSE, true>;
     using GC = Geo<D, MODE_COARSE>;
-    float* wfix = scr;   // [2][64]: refined and coarse weights of the pair's selected tokens
+    float* wfix = scr;   // [2][64]: refined and coarse weights of the step's selected tokens
     for (int g64 = 64 * w; g64 < r.n_groups; g64 += 64 * kWaves) {
       const int gi = g64 + lane;
       unsigned long long pend = __ballot(gi < r.n_groups && selm[gi < r.n_groups ? gi : 0] != 0u);
       while (pend) {
-        int groups[2];
+        int groups[2] = {-1, -1};
         groups[0] = g64 + __builtin_ctzll(pend);
         pend &= pend - 1;
-        groups[1] = pend ? g64 + __builtin_ctzll(pend) : -1;
-        if (pend) pend &= pend - 1;
+        if constexpr (GC::GPS == 2) {
+          groups[1] = pend ? g64 + __builtin_ctzll(pend) : -1;
+          if (pend) pend &= pend - 1;
+        }
         typename KR::Buf kb;
         const int lg[2] = {groups[0], groups[1] >= 0 ? groups[1] : groups[0]};
         KR::load(r, lg, lane, kb);
@@ -1069,7 +1073,7 @@ __device__ void row_body(const DecodeArgs& a, const Row& r, const Smem& sm, size
     misc[w] = st.m;
     misc[8 + w] = lsum;
 #pragma unroll
-    for (int e = 0; e < NE; ++e) misc[32 + w * 4 + e] = zs[e];
+    for (int e = 0; e < NE; ++e) misc[32 + w * NE + e] = zs[e];   // NE <= 8: within the 96 words
   }
   __syncthreads();
   float M = misc[0];
@@ -1099,7 +1103,7 @@ __device__ void row_body(const DecodeArgs& a, const Row& r, const Smem& sm, size
     float o = 0.f;
 #pragma unroll
     for (int ww = 0; ww < kWaves; ++ww) {
-      o += misc[32 + ww * 4 + d / kGroup] * fws[ww];
+      o += misc[32 + ww * NE + d / kGroup] * fws[ww];
 #pragma unroll
       for (int vb = 0; vb < G::BPS; ++vb) o += red[(ww * 64 + vb * G::LPB + chunk) * VCH + c];
       o += tred[ww * D + d];
@@ -1284,6 +1288,7 @@ hipError_t launch_decode(const DecodeArgs& a, int head_dim, hipStream_t stream) 
   if (rows == 0) return hipSuccess;
   const size_t lds = decode_lds_bytes(a.max_len, head_dim);
   if (head_dim == 128) launch_d<128>(a, rows, lds, stream);
+  else if (head_dim == 256) launch_d<256>(a, rows, lds, stream);
   else launch_d<64>(a, rows, lds, stream);
   return hipGetLastError();
 }

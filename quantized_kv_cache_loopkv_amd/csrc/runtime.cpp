@@ -103,8 +103,8 @@ loopkv_status loopkv_create(const loopkv_config* cfg, loopkv_ctx** out) {
   if (cfg->n_kv_heads < 0 || (cfg->n_kv_heads > 0 && cfg->n_heads % cfg->n_kv_heads != 0))
     return fail(LOOPKV_ERR_INVALID_ARG, "n_kv_heads %d must be 0 or divide n_heads %d", cfg->n_kv_heads, cfg->n_heads);
   const int kvh = cfg->n_kv_heads ? cfg->n_kv_heads : cfg->n_heads;
-  if (cfg->head_dim != 64 && cfg->head_dim != 128)
-    return fail(LOOPKV_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)", cfg->head_dim);
+  if (cfg->head_dim != 64 && cfg->head_dim != 128 && cfg->head_dim != 256)
+    return fail(LOOPKV_ERR_UNSUPPORTED, "head_dim %d not supported (64, 128 or 256)", cfg->head_dim);
   if (cfg->group_size != lkv::kGroup) return fail(LOOPKV_ERR_UNSUPPORTED, "group_size must be 32");
   if (cfg->block_tokens != lkv::kBlock) return fail(LOOPKV_ERR_UNSUPPORTED, "block_tokens must be 16");
   if ((uint64_t)cfg->num_blocks * (uint64_t)kvh * lkv::record_bytes(lkv::KIND_Q4, cfg->head_dim) > 0xFFFFFFFFull)

@@ -57,7 +57,7 @@ def _create(**kw):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(head_dim=96), B.ERR_UNSUPPORTED), (dict(head_dim=256), B.ERR_UNSUPPORTED),
+    (dict(head_dim=96), B.ERR_UNSUPPORTED), (dict(head_dim=512), B.ERR_UNSUPPORTED),
     (dict(group_size=64), B.ERR_UNSUPPORTED), (dict(block_tokens=32), B.ERR_UNSUPPORTED),
     (dict(n_loops=0), B.ERR_INVALID_ARG), (dict(n_heads=0), B.ERR_INVALID_ARG),
     (dict(num_blocks=0), B.ERR_INVALID_ARG), (dict(max_seqs=0), B.ERR_INVALID_ARG),

@@ -87,8 +87,8 @@ def _winner_row(D, N, mode, seed):
     K = np.zeros((N, D), np.float32)
     K[:32] = -A
     if mode == "drop":
-        for h in range(D // 32):   # tokens 1.. hold the maximum of 32 channels each
-            K[1 + h, 32 * h:32 * (h + 1)] = A
+        for h in range(D // 32):   # tokens 8.. hold the maximum of 32 channels each
+            K[8 + h, 32 * h:32 * (h + 1)] = A
         K[5] = -A + 12.0 * (2.0 * A / 15.0)
     else:
         K[5] = A
@@ -97,7 +97,7 @@ def _winner_row(D, N, mode, seed):
     return _bf16(K), _bf16(V), np.ones(D, np.float32)
 
 
-@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("D", [64, 128, 256])
 @pytest.mark.parametrize("mode", ["drop", "rise"])
 def test_gpu_correction_of_coarse_winner(D, mode):
     _need_gpu()
@@ -108,7 +108,7 @@ def test_gpu_correction_of_coarse_winner(D, mode):
     print(f"{mode} D={D}: rel err {err:.2e}, selected {n_sel}", flush=True)
 
 
-@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("D", [64, 128, 256])
 def test_gpu_many_selected_groups(D):
     _need_gpu()
     rng = np.random.default_rng(5 + D)

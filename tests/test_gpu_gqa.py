@@ -23,7 +23,7 @@ def _need_gpu():
         pytest.skip("no GPU")
 
 
-@pytest.mark.parametrize("H,Hkv,D", [(8, 2, 128), (4, 1, 64), (6, 3, 128)])
+@pytest.mark.parametrize("H,Hkv,D", [(8, 2, 128), (4, 1, 64), (6, 3, 128), (4, 2, 256)])
 def test_gpu_gqa_rows(H, Hkv, D):
     _need_gpu()
     lengths = [33, 640, 1000]   # 3 sequences: KV-head groups not a multiple of 8 (grid padding)

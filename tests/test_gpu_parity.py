@@ -78,7 +78,7 @@ def test_gpu_synth_matches_host():
 
 # --------------------------------------------------------------------------- quantize + pack
 @pytest.mark.parametrize("layout,plan", [(lkv.LAYOUT_PLANES, [0]), (lkv.LAYOUT_PLANES, [1]), (lkv.LAYOUT_KIVI4, [0])])
-@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("D", [64, 128, 256])
 def test_gpu_records_bit_exact(layout, plan, D):
     _need_gpu()
     lengths = [1, 31, 32, 33, 100, 257]
@@ -167,7 +167,7 @@ def test_gpu_decode_c1():
 
 
 @pytest.mark.parametrize("tau", [0.0, 0.001, 0.01, 0.2, 1.1])
-@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("D", [64, 128, 256])
 def test_gpu_decode_ragged_tau_sweep(tau, D):
     _need_gpu()
     lengths = [1, 2, 31, 32, 33, 95, 96, 97, 640, 1000, 2049]
@@ -212,7 +212,7 @@ def test_gpu_decode_whole_plan_small():
             assert torch.equal(out2[c], out2[6 + c % 3]) and torch.equal(sm2[c], sm2[6 + c % 3])
 
 
-@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("D", [64, 128, 256])
 def test_gpu_kivi4_equals_planes_tau0(D):
     """P12: the KIVI-4 layout matches the planes layout at tau = 0 (same codes, same selection)."""
     _need_gpu()

@@ -58,7 +58,7 @@ def _check_skip_row(wl, out, sm, q, cell, b, h, tau, n_tokens, label):
 
 
 @pytest.mark.parametrize("tau", [0.0, 0.003, 0.02, 1.5])
-@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("D", [64, 128, 256])
 def test_gpu_skip_rows(tau, D):
     _need_gpu()
     lengths = [1, 31, 32, 33, 96, 640, 1000, 2049]

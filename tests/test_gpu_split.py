@@ -34,7 +34,7 @@ def _split(wl, q, tau, n_split, cell=None, out_dtype=torch.float32, max_len=None
 
 
 @pytest.mark.parametrize("tau", [0.0, 0.001, 0.01, 1.1])
-@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("D", [64, 128, 256])
 def test_gpu_split_ragged(tau, D):
     _need_gpu()
     lengths = [1, 31, 32, 33, 97, 640, 1000, 2049]

@@ -744,7 +744,7 @@ __device__ inline void split_range(int n_chunks, int n_split, int split, int& cb
 // selection, but the values are not streamed and the unselected quantized tokens leave the
 // attention: the softmax runs over the selected tokens (at 4 bits) and the tail only.
 template <int D, int MODE, bool SPARSE, int PH, bool SKIP = false>
-__device__ void row_body(const DecodeArgs& a, const Row& r, const Smem& sm, size_t orow, int split) {
+__device__ __forceinline__ void row_body(const DecodeArgs& a, const Row& r, const Smem& sm, size_t orow, int split) {
   using G = Geo<D, MODE>;
   using KS = KStep<D, MODE, false>;
   using VS = VStep<D, MODE>;
@@ -880,15 +880,20 @@ __device__ void row_body(const DecodeArgs& a, const Row& r, const Smem& sm, size
       const float4* g4 = reinterpret_cast<const float4*>(a.part_scores + orow * (size_t)a.split_row_stride);
       float4* l4 = reinterpret_cast<float4*>(scores);
       const int n4 = (r.N + 3) / 4;   // within the line: its stride is a multiple of 64 floats
-      for (int base = 0; base < n4; base += 8 * kThreads) {
-        float4 v[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) v[k] = g4[min(base + k * kThreads + tid, n4 - 1)];   // N >= 1
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const int i = base + k * kThreads + tid;
-          if (i < n4) l4[i] = v[k];
-        }
+      for (int base = tid; base < n4; base += 8 * kThreads) {
+        // eight named registers (an array here can end up in scratch memory); N >= 1
+        const float4 v0 = g4[min(base + 0 * kThreads, n4 - 1)], v1 = g4[min(base + 1 * kThreads, n4 - 1)];
+        const float4 v2 = g4[min(base + 2 * kThreads, n4 - 1)], v3 = g4[min(base + 3 * kThreads, n4 - 1)];
+        const float4 v4 = g4[min(base + 4 * kThreads, n4 - 1)], v5 = g4[min(base + 5 * kThreads, n4 - 1)];
+        const float4 v6 = g4[min(base + 6 * kThreads, n4 - 1)], v7 = g4[min(base + 7 * kThreads, n4 - 1)];
+        if (base + 0 * kThreads < n4) l4[base + 0 * kThreads] = v0;
+        if (base + 1 * kThreads < n4) l4[base + 1 * kThreads] = v1;
+        if (base + 2 * kThreads < n4) l4[base + 2 * kThreads] = v2;
+        if (base + 3 * kThreads < n4) l4[base + 3 * kThreads] = v3;
+        if (base + 4 * kThreads < n4) l4[base + 4 * kThreads] = v4;
+        if (base + 5 * kThreads < n4) l4[base + 5 * kThreads] = v5;
+        if (base + 6 * kThreads < n4) l4[base + 6 * kThreads] = v6;
+        if (base + 7 * kThreads < n4) l4[base + 7 * kThreads] = v7;
       }
       M = wave_max(part_m);
       L = wave_sum(part_m > -INFINITY ? part_l * __expf(part_m - M) : 0.f);

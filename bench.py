@@ -186,7 +186,16 @@ def cpu_baseline(cfg, plan, tau, rows, log, min_seconds=10.0, max_evals=400):
             bytes_total += 64 * int(sel.sum())
         evals += 1
     log(f"cpu oracle: {evals} row evaluations ({len(inputs)} distinct rows) in {t_total:.2f}s")
+    cpu_model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu_model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {"value": bytes_total / t_total / 1e9, "unit": "GB/s", "cores": int(cores), "kind": "oracle",
+            "host_cpus": os.cpu_count(), "cpu_model": cpu_model,
             "sample": f"{len(inputs)} distinct (cell, seq, head) rows of the 16K-context plan (4-bit, 2-bit and "
                       f"reuse cells), evaluated round-robin {evals} times: fp64 quantize + loop-aware decode "
                       f"per row, {t_total:.2f} s measured, input generation excluded; value = the rows' "

@@ -29,8 +29,11 @@
 // over the per-group masks); their low K plane refines the selected scores, and the
 // selected tokens' contributions are corrected in place:
 //   w' (z + s (4 hi + lo)) - w (z + s (4 hi + 3/2)),  w, w' = exp(coarse, refined - m).
-// If the removed coarse weight exceeds 1024 times what the row keeps, the subtraction
-// could lose precision; the row's V is then recomputed from the final scores.
+// Token weights enter the value sums as 16-bit fixed point against the largest weight of
+// their 16-token block, so a selected token that dominated its block and then loses most of
+// its weight leaves its neighbours' rounding (up to 2^-16 of its coarse weight each) in the
+// sum; relative to the output that error grows with removed / kept weight. Past 8 the row's
+// V is recomputed from the final scores.
 #include <hip/hip_runtime.h>
 #include <hip/hip_fp16.h>
 #include <stdint.h>
@@ -1037,7 +1040,7 @@ __device__ __forceinline__ void row_body(const DecodeArgs& a, const Row& r, cons
       Rm += misc[16 + i] * f;
     }
     if (PH == PH_FINISH) Lp += L * __expf(M - Ms);   // the streamed part's coarse weight
-    if (Rm > 1024.f * Lp) {   // recompute the row's V from the final scores
+    if (Rm > 8.f * Lp) {   // recompute the row's V from the final scores
       use_parts = false;
       __syncthreads();
       float ls = 0.f;

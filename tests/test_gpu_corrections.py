@@ -119,3 +119,43 @@ def test_gpu_many_selected_groups(D):
     for tau in (1e-4, 1e-3):
         err, n_sel = _check(K, V, q, tau, f"many D={D} tau={tau}")
         print(f"many D={D} tau={tau}: rel err {err:.2e}, selected {n_sel}", flush=True)
+
+
+# Generator rows (seed, head dim, sequence, head, query gain, tau) whose selected coarse winner
+# loses most of its weight to its low bits: the removed coarse weight is tens to hundreds of
+# times the weight the row keeps. The values sum carries each weight at 16 bits against the
+# largest weight of its 16-token block, so the winner's neighbours are rounded coarsely; these
+# rows put that rounding, amplified by removed / kept, above the tolerance unless the row's
+# values are recomputed from the final scores.
+_PEAKED = [(25, 128, 0, 0, 5.0, 0.05), (38, 64, 0, 1, 5.0, 0.05), (27, 64, 0, 3, 5.0, 0.05),
+           (18, 64, 0, 1, 3.0, 0.05), (29, 256, 0, 2, 5.0, 0.05)]
+
+
+def _removed_over_kept(q, K, V, tau, sig):
+    """Coarse weight of the selected tokens over the final weight of the row (oracle values)."""
+    qh = O.quantize_history(K, V, 4)
+    n_q = qh["n_q"]
+    coarse = sig * (np.concatenate([O.dequant_hi(qh, "k"), K[n_q:]]) @ q)
+    _, sel, _ = O.decode_row(q, K, V, O.KIND_Q4, tau, sig, qh=qh)
+    refined = coarse.copy()
+    refined[:n_q][sel] = sig * (O.dequant_full(qh, "k")[sel] @ q)
+    m = coarse.max()
+    return np.exp(coarse[:n_q][sel] - m).sum() / np.exp(refined - m).sum()
+
+
+@pytest.mark.parametrize("n_split", [0, 3])
+@pytest.mark.parametrize("row", _PEAKED)
+def test_gpu_peaked_rows(row, n_split):
+    _need_gpu()
+    from synth import recipes as R
+    from tests.harness import oracle_row_inputs
+    seed, D, b, h, gain, tau = row
+    cfg = R.small_config("peak", 1, 1, 4, D, [700, 1300], [tau], outlier_count=3, outlier_mult=10.0, seed=seed)
+    N = cfg.lengths[b]
+    _, _, K, V = oracle_row_inputs(cfg, 0, b, h, N, R.factor_table(cfg))
+    q = (R.q_values(cfg, 0, 0, b, h) * gain).astype(np.float32)
+    ratio = _removed_over_kept(q.astype(np.float64), K, V, tau, float(np.float32(1.0 / math.sqrt(D))))
+    assert 20 < ratio < 1024, ratio
+    err, n_sel = _check(_bf16(K), _bf16(V), q, tau, f"peaked {row} split={n_split}", n_split=n_split)
+    print(f"peaked {row} split={n_split}: removed/kept {ratio:.0f}, rel err {err:.2e}, selected {n_sel}",
+          flush=True)

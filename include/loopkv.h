@@ -28,8 +28,8 @@
  *     tail) and quantized by the append that completes their group.
  *
  * Storage (per storing cell, caller-allocated workspace):
- *   pool  [num_blocks][n_heads][record]   record of one 16-token block, one head
- *   tails [max_seqs][n_heads][2 (K,V)][32][head_dim] bf16
+ *   pool  [num_blocks * block_tokens/16][KV heads][record]   record of 16 tokens, one KV head
+ *   tails [max_seqs][KV heads][2 (K,V)][32][head_dim] bf16
  * Record layouts (D = head_dim, all words little-endian u32):
  *   4-bit planes : [K_hi 4D | K_meta 2D | V_hi 4D | V_meta 2D | K_lo 4D | V_lo 4D]  = 20D bytes
  *   2-bit        : [K2 4D   | K_meta 2D | V2 4D   | V_meta 2D]                      = 12D bytes
@@ -50,8 +50,10 @@
  *     group's two blocks: logical block 2g holds positions 0..D/2-1, 2g+1 the rest.
  *   V_meta: [D/32 channel groups][16 tokens].
  *
- * Paging: block_table[b * bt_stride + j] is the physical block of logical block
- * j (tokens 16j..16j+15) of sequence b; the same id addresses every cell's pool.
+ * Paging: block_table[b * bt_stride + p] is the physical page of logical page p
+ * (tokens block_tokens*p .. block_tokens*(p+1)-1) of sequence b; the same id addresses
+ * every cell's pool. A page of 16 tokens is one record slot; a page of 32 tokens is the
+ * two consecutive slots 2*id and 2*id+1, holding its first and second 16 tokens.
  *
  * Ownership: the caller owns every device buffer (workspace, q, k, v, out,
  * tables, masks). The library never allocates device memory and never
@@ -78,8 +80,8 @@ typedef enum {
   LOOPKV_ERR_INVALID_ARG = 1, /* null / out-of-range argument, bad dtype, tau < 0 or NaN, sm_scale <= 0 */
   LOOPKV_ERR_PLAN = 2,        /* no plan loaded, kind > 2, reuse cell in the final loop, bad cell index */
   LOOPKV_ERR_WORKSPACE = 3,   /* workspace not bound, too small, or not 256-byte aligned */
-  LOOPKV_ERR_CAPACITY = 4,    /* bt_stride * 16 < max_len, max_len above the supported maximum */
-  LOOPKV_ERR_UNSUPPORTED = 5, /* head_dim not 64/128, group != 32, block != 16, too many cells */
+  LOOPKV_ERR_CAPACITY = 4,    /* bt_stride * block_tokens < max_len, max_len above the supported maximum */
+  LOOPKV_ERR_UNSUPPORTED = 5, /* head_dim not 64/128/256, group != 32, block not 16/32, too many cells */
   LOOPKV_ERR_HIP = 6          /* HIP runtime / launch failure */
 } loopkv_status;
 
@@ -99,9 +101,9 @@ typedef struct {
   int32_t n_heads;           /* query heads */
   int32_t head_dim;          /* 64, 128 or 256 */
   int32_t group_size;        /* must be 32 */
-  int32_t block_tokens;      /* must be 16 */
-  int32_t num_blocks;        /* physical blocks in each storing cell's pool; a pool
-                                (num_blocks x KV heads x 20*head_dim bytes) stays below 4 GiB */
+  int32_t block_tokens;      /* tokens per page of the block table: 16 or 32 */
+  int32_t num_blocks;        /* physical pages in each storing cell's pool; a pool (num_blocks x
+                                block_tokens/16 x KV heads x 20*head_dim bytes) stays below 4 GiB */
   int32_t max_seqs;          /* sequence slots (tail buffers) */
   int32_t layout;            /* loopkv_layout; KIVI4 requires an all-4-bit plan */
   int32_t n_kv_heads;        /* KV heads (0: = n_heads, MHA); divides n_heads. Query head h
@@ -139,8 +141,9 @@ loopkv_status loopkv_cell_storage(const loopkv_ctx* ctx, int32_t loop, int32_t l
  * storing cell ((-1, -1)). k, v: device [cells][n_seqs][n_new][H][D] (whole plan,
  * cells = n_loops*n_layers, SHARE entries ignored) or [n_seqs][n_new][H][D]; F32 input
  * is rounded to bf16 (nearest even). seq_slots: device [n_seqs] tail slot of each
- * sequence or NULL for slot = b. block_table: device [n_seqs][bt_stride]; blocks 2g and
- * 2g+1 must be mapped before the append that completes group g. seq_lens: device
+ * sequence or NULL for slot = b. block_table: device [n_seqs][bt_stride]; the page(s) of
+ * tokens 32g..32g+31 (pages 2g and 2g+1 of 16 tokens, page g of 32) must be mapped before
+ * the append that completes group g. seq_lens: device
  * [n_seqs], length before the append (read only; the caller advances it). Completed
  * 32-token groups are quantized into the pool; the rest goes to the tail. Appending to
  * a SHARE cell is a no-op. */
@@ -153,7 +156,7 @@ loopkv_status loopkv_append(loopkv_ctx* ctx, hipStream_t stream, int32_t loop, i
 /* Loop-aware decode attention of one cell ((loop, layer)) or of the whole plan ((-1, -1)).
  * q: device [cells][n_seqs][H][D] (whole plan) or [n_seqs][H][D], dtype q_dtype.
  * seq_lens: device lengths (tail included); max_len: host upper bound of them
- * (<= LOOPKV_MAX_LEN, <= 16 * bt_stride). Rows whose length exceeds max_len get NaN
+ * (<= LOOPKV_MAX_LEN, <= block_tokens * bt_stride). Rows whose length exceeds max_len get NaN
  * output. tau >= 0: selection threshold on the coarse softmax; sm_scale > 0.
  * out: device [cells][n_seqs][H][D] (or [n_seqs][H][D]) of out_dtype, accumulated in fp32.
  * sel_mask: NULL or device [cells][n_seqs][H][ceil(max_len/32)] u32; bit t%32 of word

@@ -189,7 +189,7 @@ __global__ void __launch_bounds__(256) k_quantize_groups(AppendArgs a) {
   const int rec = record_bytes(cell.kind, D);
   for (int half = 0; half < 2; ++half) {
     const int j = 2 * g + half;
-    const int phys = a.block_table[(size_t)b * a.bt_stride + j];
+    const uint32_t phys = record_slot(a.block_table + (size_t)b * a.bt_stride, j, a.bt_shift);
     uint32_t* r = reinterpret_cast<uint32_t*>(a.ws + cell.pool_off + ((size_t)phys * a.n_heads + h) * rec);
     const int t0 = half * kBlock;
     if (cell.kind == KIND_KIVI4) {

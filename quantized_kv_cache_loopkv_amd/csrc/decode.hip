@@ -1229,7 +1229,8 @@ __global__ void __launch_bounds__(kThreads, kWavesPerSimd) k_decode(DecodeArgs a
   const int32_t* bt = a.block_table + (size_t)b * a.bt_stride;
   const int nbq = r.n_q / kBlock;
   const uint32_t rec256 = (uint32_t)(record_bytes(cell.kind, D) / 256);
-  for (int j = tid; j < nbq; j += kThreads) sm.boff[j] = ((uint32_t)bt[j] * (uint32_t)a.n_kv_heads + (uint32_t)kh) * rec256;
+  for (int j = tid; j < nbq; j += kThreads)
+    sm.boff[j] = (record_slot(bt, j, a.bt_shift) * (uint32_t)a.n_kv_heads + (uint32_t)kh) * rec256;
   for (int d = tid; d < D; d += kThreads) {
     const size_t qi = orow * D + d;
     const float qv = a.q_bf16 ? bf16f(reinterpret_cast<const uint16_t*>(a.q)[qi]) : reinterpret_cast<const float*>(a.q)[qi];

@@ -11,7 +11,7 @@
 namespace lkv {
 
 constexpr int kGroup = 32;      // tokens per K group / channels per V group
-constexpr int kBlock = 16;      // tokens per paged block
+constexpr int kBlock = 16;      // tokens per record (a page of the block table holds 1 or 2)
 constexpr int kMaxCells = 128;
 constexpr int kMaxLen = 32768;
 
@@ -34,6 +34,12 @@ __host__ __device__ constexpr int record_bytes(int kind, int D) {
 }
 // Tail of one (cell, slot, head): [2 (K, V)][32][D] bf16.
 __host__ __device__ constexpr int tail_elems(int D) { return 2 * kGroup * D; }
+// Pool index of 16-token record j of a sequence whose block-table row is bt: pages of
+// 2^shift records are consecutive record slots, so record j sits in slot
+// (bt[j >> shift] << shift) + (j mod 2^shift).
+__host__ __device__ inline uint32_t record_slot(const int32_t* bt, int j, int shift) {
+  return ((uint32_t)bt[j >> shift] << shift) + (uint32_t)(j & ((1 << shift) - 1));
+}
 
 // Per storing cell, for the append kernels.
 struct AppendCell {
@@ -52,6 +58,7 @@ struct AppendArgs {
   const int32_t* seq_lens;
   int32_t kv_bf16;
   int32_t n_seqs, n_new, n_heads, bt_stride, n_cells;
+  int32_t bt_shift;     // log2(records per page): 16-token record j lives in page j >> bt_shift
   AppendCell cells[kMaxCells];
 };
 
@@ -74,6 +81,7 @@ struct DecodeArgs {
   int32_t q_bf16, out_bf16;
   int32_t n_seqs, n_heads, bt_stride, max_len, sel_words, n_cells;
   int32_t n_kv_heads;   // divides n_heads; query head h reads KV head h / (n_heads / n_kv_heads)
+  int32_t bt_shift;     // log2(records per page): 16-token record j lives in page j >> bt_shift
   float tau, sm_scale;
   // Split of each row's tokens over n_split workgroups (n_split 0: one workgroup per row).
   // part: [rows][n_split][2 + D] floats (m, l, unnormalized o relative to m);

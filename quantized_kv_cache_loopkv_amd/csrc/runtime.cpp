@@ -106,9 +106,12 @@ loopkv_status loopkv_create(const loopkv_config* cfg, loopkv_ctx** out) {
   if (cfg->head_dim != 64 && cfg->head_dim != 128 && cfg->head_dim != 256)
     return fail(LOOPKV_ERR_UNSUPPORTED, "head_dim %d not supported (64, 128 or 256)", cfg->head_dim);
   if (cfg->group_size != lkv::kGroup) return fail(LOOPKV_ERR_UNSUPPORTED, "group_size must be 32");
-  if (cfg->block_tokens != lkv::kBlock) return fail(LOOPKV_ERR_UNSUPPORTED, "block_tokens must be 16");
-  if ((uint64_t)cfg->num_blocks * (uint64_t)kvh * lkv::record_bytes(lkv::KIND_Q4, cfg->head_dim) > 0xFFFFFFFFull)
-    return fail(LOOPKV_ERR_UNSUPPORTED, "a cell's pool (num_blocks x KV heads x %d-byte records) must stay below 4 GiB",
+  if (cfg->block_tokens != 16 && cfg->block_tokens != 32)
+    return fail(LOOPKV_ERR_UNSUPPORTED, "block_tokens %d not supported (16 or 32)", cfg->block_tokens);
+  const uint64_t recs = (uint64_t)cfg->num_blocks * (uint64_t)(cfg->block_tokens / lkv::kBlock);
+  if (recs * (uint64_t)kvh * lkv::record_bytes(lkv::KIND_Q4, cfg->head_dim) > 0xFFFFFFFFull)
+    return fail(LOOPKV_ERR_UNSUPPORTED,
+                "a cell's pool (num_blocks x block_tokens/16 x KV heads x %d-byte records) must stay below 4 GiB",
                 lkv::record_bytes(lkv::KIND_Q4, cfg->head_dim));
   if ((long long)cfg->n_loops * cfg->n_layers > lkv::kMaxCells)
     return fail(LOOPKV_ERR_UNSUPPORTED, "at most %d cells", lkv::kMaxCells);
@@ -144,7 +147,8 @@ loopkv_status loopkv_plan(loopkv_ctx* c, const uint8_t* kinds) {
     c->storage[i] = kinds[i] == LOOPKV_CELL_SHARE ? (L - 1) * NL + i % NL : i;
     if (kinds[i] == LOOPKV_CELL_SHARE) continue;
     c->pool_off[i] = off;
-    off = align256(off + (size_t)c->cfg.num_blocks * H * lkv::record_bytes(device_kind(c, i), D));
+    off = align256(off + (size_t)c->cfg.num_blocks * (c->cfg.block_tokens / lkv::kBlock) * H *
+                             lkv::record_bytes(device_kind(c, i), D));
   }
   for (int i = 0; i < n; ++i) {
     if (kinds[i] == LOOPKV_CELL_SHARE) continue;
@@ -226,6 +230,7 @@ loopkv_status loopkv_append(loopkv_ctx* c, hipStream_t stream, int32_t loop, int
   a.n_new = n_new;
   a.n_heads = c->kvh;   // the append's inputs hold the KV heads
   a.bt_stride = bt_stride;
+  a.bt_shift = c->cfg.block_tokens == 32 ? 1 : 0;
   int nc = 0;
   for (int i = first; i < first + count; ++i) {
     if (c->kinds[i] == LOOPKV_CELL_SHARE) continue;
@@ -267,7 +272,7 @@ loopkv_status decode_common(loopkv_ctx* c, hipStream_t stream, int32_t loop, int
     return fail(LOOPKV_ERR_CAPACITY, "n_seqs %d > max_seqs %d with identity slots", n_seqs, c->cfg.max_seqs);
   if (max_len < 0 || max_len > LOOPKV_MAX_LEN)
     return fail(LOOPKV_ERR_CAPACITY, "max_len %d outside [0, %d]", max_len, LOOPKV_MAX_LEN);
-  if (bt_stride < 1 || (long long)bt_stride * lkv::kBlock < max_len)
+  if (bt_stride < 1 || (long long)bt_stride * c->cfg.block_tokens < max_len)
     return fail(LOOPKV_ERR_CAPACITY, "bt_stride %d too small for max_len %d", bt_stride, max_len);
   if (skip && c->cfg.layout == LOOPKV_LAYOUT_KIVI4)
     return fail(LOOPKV_ERR_UNSUPPORTED, "token skipping needs the planes layout");
@@ -299,6 +304,7 @@ loopkv_status decode_common(loopkv_ctx* c, hipStream_t stream, int32_t loop, int
   a.n_heads = c->cfg.n_heads;
   a.n_kv_heads = c->kvh;
   a.bt_stride = bt_stride;
+  a.bt_shift = c->cfg.block_tokens == 32 ? 1 : 0;
   a.max_len = max_len;
   a.sel_words = (max_len + 31) / 32;
   a.n_cells = count;

@@ -141,10 +141,12 @@ class Context:
     """One LoopKV cache: config, plan, caller-owned workspace."""
 
     def __init__(self, n_loops: int, n_layers: int, n_heads: int, head_dim: int, num_blocks: int,
-                 max_seqs: int, layout: int = LAYOUT_PLANES, n_kv_heads: int = 0):
+                 max_seqs: int, layout: int = LAYOUT_PLANES, n_kv_heads: int = 0, block_tokens: int = 16):
         """n_kv_heads: KV heads (0: one per query head); query head h reads KV head
-        h // (n_heads // n_kv_heads)."""
-        self.cfg = _Config(n_loops, n_layers, n_heads, head_dim, 32, 16, num_blocks, max_seqs, layout, n_kv_heads)
+        h // (n_heads // n_kv_heads). block_tokens: tokens per page of the block table (16 or
+        32); num_blocks counts pages."""
+        self.cfg = _Config(n_loops, n_layers, n_heads, head_dim, 32, block_tokens, num_blocks, max_seqs, layout,
+                           n_kv_heads)
         h = ctypes.c_void_p()
         _check(lib().loopkv_create(ctypes.byref(self.cfg), ctypes.byref(h)))
         self._h = h

@@ -48,6 +48,7 @@ class Config:
     seed: int = 0
     plan: Optional[np.ndarray] = field(default=None, repr=False)
     n_kv_heads: int = 0           # 0: one KV head per query head
+    block_tokens: int = 16        # tokens per page of the block table (16 or 32)
 
     @property
     def kv_heads(self) -> int:
@@ -67,7 +68,7 @@ class Config:
 
     @property
     def bt_stride(self) -> int:
-        return (self.max_len + 15) // 16
+        return (self.max_len + self.block_tokens - 1) // self.block_tokens
 
 
 def random_plan(n_loops: int, n_layers: int, seed: int, frac=(0.5, 0.3, 0.2)) -> np.ndarray:
@@ -126,12 +127,12 @@ def small_config(name: str, n_loops: int, n_layers: int, n_heads: int, head_dim:
                  lengths: List[int], taus: List[float], plan=None, seed: int = 0,
                  outlier_count: int = 0, outlier_mult: float = 1.0, cell_scales: bool = False,
                  shuffled: bool = False, q_fp32: bool = False, append_steps: int = 0,
-                 n_kv_heads: int = 0) -> Config:
+                 n_kv_heads: int = 0, block_tokens: int = 16) -> Config:
     """A reduced configuration with the same generators, for tests that the oracle finishes quickly."""
     cfg = Config(name, n_loops, n_layers, n_heads, head_dim, len(lengths), list(lengths), list(taus),
                  q_fp32=q_fp32, outlier_count=outlier_count, outlier_mult=outlier_mult,
                  cell_scales=cell_scales, shuffled=shuffled, append_steps=append_steps, seed=seed,
-                 n_kv_heads=n_kv_heads)
+                 n_kv_heads=n_kv_heads, block_tokens=block_tokens)
     if plan is None:
         plan = np.zeros((n_loops, n_layers), dtype=np.uint8) if n_loops * n_layers == 1 \
             else random_plan(n_loops, n_layers, seed)
@@ -158,11 +159,13 @@ def factor_table(cfg: Config) -> np.ndarray:
 
 
 def block_table(cfg: Config) -> np.ndarray:
-    """int32 [B][bt_stride]: physical block id of each logical 16-token block (-1 if unused).
+    """int32 [B][bt_stride]: physical page of each logical page of cfg.block_tokens tokens
+    (-1 if unused).
 
-    Each sequence owns ceil(max length it reaches / 16) blocks; ids are handed out
-    in order (identity) or from a seeded permutation (shuffled)."""
-    need = [(n + cfg.append_steps + 15) // 16 for n in cfg.lengths]
+    Each sequence owns ceil(max length it reaches / block_tokens) pages; ids are handed
+    out in order (identity) or from a seeded permutation (shuffled)."""
+    P = cfg.block_tokens
+    need = [(n + cfg.append_steps + P - 1) // P for n in cfg.lengths]
     total = int(sum(need))
     ids = np.arange(total, dtype=np.int64)
     if cfg.shuffled:
@@ -176,7 +179,8 @@ def block_table(cfg: Config) -> np.ndarray:
 
 
 def num_blocks(cfg: Config) -> int:
-    return int(sum((n + cfg.append_steps + 15) // 16 for n in cfg.lengths))
+    P = cfg.block_tokens
+    return int(sum((n + cfg.append_steps + P - 1) // P for n in cfg.lengths))
 
 
 def kv_index(cfg: Config, b, t, h, d):

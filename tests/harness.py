@@ -38,7 +38,7 @@ class Workload:
         self.plan = plan
         self.nb = R.num_blocks(cfg)
         self.ctx = lkv.Context(cfg.n_loops, cfg.n_layers, cfg.n_heads, cfg.head_dim, self.nb, cfg.batch, layout,
-                               n_kv_heads=cfg.n_kv_heads)
+                               n_kv_heads=cfg.n_kv_heads, block_tokens=cfg.block_tokens)
         self.ctx.plan(plan.tolist())
         self.ws = torch.empty(self.ctx.workspace_bytes(), dtype=torch.uint8, device=device)
         self.ctx.bind(self.ws)
@@ -204,11 +204,14 @@ class Workload:
 
     # ------------------------------------------------------------------ inspection
     def record(self, cell: int, b: int, h: int, j: int) -> np.ndarray:
+        """Bytes of the record of 16-token block j of (cell, sequence b, KV head h): pages of
+        32 tokens hold two consecutive record slots."""
         loop, layer = self.cell_ll(cell)
         st = self.ctx.cell_storage(loop, layer)
         rb = st["record_bytes"]
-        phys = int(self.bt_np[b, j])
-        off = st["pool_offset"] + (phys * self.cfg.kv_heads + h) * rb
+        per = self.cfg.block_tokens // 16
+        slot = int(self.bt_np[b, j // per]) * per + j % per
+        off = st["pool_offset"] + (slot * self.cfg.kv_heads + h) * rb
         return self.ws[off:off + rb].cpu().numpy()
 
     def tail(self, cell: int, b: int, h: int) -> np.ndarray:

@@ -58,7 +58,10 @@ def _create(**kw):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(head_dim=96), B.ERR_UNSUPPORTED), (dict(head_dim=512), B.ERR_UNSUPPORTED),
-    (dict(group_size=64), B.ERR_UNSUPPORTED), (dict(block_tokens=32), B.ERR_UNSUPPORTED),
+    (dict(group_size=64), B.ERR_UNSUPPORTED), (dict(block_tokens=8), B.ERR_UNSUPPORTED),
+    (dict(block_tokens=64), B.ERR_UNSUPPORTED), (dict(block_tokens=0), B.ERR_UNSUPPORTED),
+    # 32-token pages: 52429 x 2 x 16 x 2560 B > 2^32 - 1
+    (dict(block_tokens=32, num_blocks=52429), B.ERR_UNSUPPORTED),
     (dict(n_loops=0), B.ERR_INVALID_ARG), (dict(n_heads=0), B.ERR_INVALID_ARG),
     (dict(num_blocks=0), B.ERR_INVALID_ARG), (dict(max_seqs=0), B.ERR_INVALID_ARG),
     (dict(n_loops=6, n_layers=24), B.ERR_UNSUPPORTED), (dict(layout=5), B.ERR_INVALID_ARG),
@@ -77,6 +80,33 @@ def test_create_accepts_pool_just_under_4gib():
     s, h = _create(num_blocks=104857)   # 104857 x 16 x 2560 B = 2^32 - 2560
     assert s == B.OK and h.value
     lkv.lib().loopkv_destroy(h)
+    s, h = _create(num_blocks=52428, block_tokens=32)   # 52428 x 2 x 16 x 2560 B = 2^32 - 65536
+    assert s == B.OK and h.value
+    lkv.lib().loopkv_destroy(h)
+
+
+def test_pages_of_32_tokens_hold_two_records():
+    """A pool of n 32-token pages is the size of a pool of 2n 16-token pages; tails do not
+    depend on the page size."""
+    a = lkv.Context(2, 3, 4, 128, 40, 3, block_tokens=32)
+    b = lkv.Context(2, 3, 4, 128, 80, 3)
+    for c in (a, b):
+        c.plan([0, 1, 2, 0, 0, 1])
+    assert a.workspace_bytes() == b.workspace_bytes()
+    for loop in range(2):
+        for layer in range(3):
+            assert a.cell_storage(loop, layer) == b.cell_storage(loop, layer)
+
+
+def test_decode_capacity_counts_page_tokens():
+    """bt_stride pages cover bt_stride * block_tokens tokens (n_seqs = 0: validation only)."""
+    L = lkv.lib()
+    for bt_tokens, want in ((16, B.ERR_CAPACITY), (32, B.OK)):
+        ctx = lkv.Context(2, 3, 2, 64, 16, 2, block_tokens=bt_tokens)
+        ctx.plan([0, 1, 2, 0, 0, 1])
+        assert L.loopkv_bind_workspace(ctx._h, ctypes.c_void_p(FAKE_DEV), ctx.workspace_bytes()) == B.OK
+        assert _decode(ctx, n_seqs=0, bt_stride=2, max_len=64) == want
+        assert _decode(ctx, n_seqs=0, bt_stride=2, max_len=65) == B.ERR_CAPACITY
 
 
 def test_plan_rules_and_workspace_sizes():

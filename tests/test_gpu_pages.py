@@ -1,0 +1,103 @@
+"""32-token pages of the block table on the GPU.
+
+A page of 32 tokens is two consecutive 16-token record slots (the record layout does not
+change), so a cache paged at 32 tokens must hold, record for record, the bytes of the same
+cache paged at 16, and every decode over it must give bit-identical outputs and selections.
+Checked on a mixed plan (4-bit, 2-bit and reuse cells) with grouped queries, shuffled page
+tables and ragged lengths: records and tails after the bulk fill, the one-workgroup, split and
+token-skipping decodes, and one-token appends at decode time that complete groups; plus rows
+against the fp64 oracle. Paging of the KV cache: "LoopKV: Loop-Aware KV Cache Compression for
+Serving Looped Transformers" (arXiv:2611.04137), Abstract (serving sentence).
+"""
+import numpy as np
+import pytest
+import torch
+
+from synth import recipes as R
+from tests.harness import Workload
+from tests.test_gpu_parity import check_row
+
+pytestmark = pytest.mark.gpu
+
+STEPS = 3
+LENGTHS = [95, 517, 1000]   # the first sequence completes a group during the steps
+
+
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _pair(D=128, H=4, Hkv=2):
+    plan = np.array([[0, 2], [1, 0]], dtype=np.uint8)
+    out = []
+    for bt in (16, 32):
+        cfg = R.small_config("pages", 2, 2, H, D, LENGTHS, [0.01], plan=plan, cell_scales=True, shuffled=True,
+                             n_kv_heads=Hkv, append_steps=STEPS, outlier_count=2, outlier_mult=8.0, block_tokens=bt)
+        wl = Workload(cfg, gpu_synth=False)
+        wl.fill()
+        out.append(wl)
+    torch.cuda.synchronize()
+    return out
+
+
+def _same_storage(w16, w32, lengths):
+    cfg = w16.cfg
+    for c in w16.storing_cells():
+        for b, N in enumerate(lengths):
+            for h in range(cfg.kv_heads):
+                for j in range(32 * (N // 32) // 16):
+                    assert np.array_equal(w16.record(c, b, h, j), w32.record(c, b, h, j)), (c, b, h, j)
+                r = N % 32   # tail rows past the length are not written
+                assert np.array_equal(w16.tail(c, b, h)[:, :r], w32.tail(c, b, h)[:, :r]), (c, b, h)
+
+
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_gpu_pages_of_32_equal_pages_of_16(D):
+    _need_gpu()
+    w16, w32 = _pair(D=D)
+    assert w32.bt.shape[1] * 2 >= w16.bt.shape[1]
+    _same_storage(w16, w32, LENGTHS)
+    q = w16.q_all() * 2
+    q = q.to(torch.bfloat16).float().to(q.dtype)
+    print(f"D={D}: storage equal", flush=True)
+    for tau in (0.0, 0.01, 1.1):
+        for n_split, skip in ((0, False), (3, False), (0, True)):
+            if skip and tau == 0.0:
+                continue
+            o16, s16 = w16.ctx.decode(q, w16.bt, w16.seq_lens, w16.max_len(), tau, sel_mask=True, n_split=n_split,
+                                      skip=skip)
+            o32, s32 = w32.ctx.decode(q, w32.bt, w32.seq_lens, w32.max_len(), tau, sel_mask=True, n_split=n_split,
+                                      skip=skip)
+            torch.cuda.synchronize()
+            assert torch.equal(o16, o32) and torch.equal(s16, s32), f"D={D} tau={tau} split={n_split} skip={skip}"
+    out, sm = w32.ctx.decode(q, w32.bt, w32.seq_lens, w32.max_len(), 0.01, sel_mask=True)
+    torch.cuda.synchronize()
+    for c in range(4):
+        for b, N in enumerate(LENGTHS):
+            for h in range(4):
+                check_row(w32, out, sm, q, c, b, h, 0.01, N, f"pages of 32, D={D} cell={c} b={b} h={h}")
+
+
+def test_gpu_pages_of_32_serving_appends():
+    """One-token appends at decode time (per-(loop, layer) order) write the same records."""
+    _need_gpu()
+    w16, w32 = _pair()
+    cfg = w16.cfg
+    C, B, H, D = cfg.n_cells, cfg.batch, cfg.n_heads, cfg.head_dim
+    max_len = max(LENGTHS) + STEPS
+    words = (max_len + 31) // 32
+    lens = [(torch.tensor(LENGTHS, dtype=torch.int32, device="cuda"),
+             torch.tensor(LENGTHS, dtype=torch.int32, device="cuda") + 1) for _ in range(2)]
+    for s in range(STEPS):
+        K, V, _, _ = w16.append_inputs(s)
+        q = w16.q_all(s)
+        res = []
+        for wl, (lb, la) in zip((w16, w32), lens):
+            out = torch.zeros((C, B, H, D), dtype=torch.float32, device="cuda")
+            sm = torch.zeros((C, B, H, words), dtype=torch.int32, device="cuda")
+            wl.serving_step(K, V, q, lb, la, max_len, 0.01, out, sm)
+            res.append((out, sm))
+        torch.cuda.synchronize()
+        assert torch.equal(res[0][0], res[1][0]) and torch.equal(res[0][1], res[1][1]), f"step {s}"
+    _same_storage(w16, w32, [n + STEPS for n in LENGTHS])

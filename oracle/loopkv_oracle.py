@@ -22,15 +22,16 @@ shape:
 The abstract gives no formula. Where it is silent this module takes these
 readings:
 
-* KIVI-style asymmetric groups of 32: K per channel over 32 consecutive
-  tokens, V per token over 32 consecutive channels; zero = f16(min),
+* KIVI-style asymmetric groups of 32 (64 as the wider option): K per channel
+  over 32 consecutive tokens, V per token over 32 consecutive channels; zero = f16(min),
   scale = f16((max - min) / (2^b - 1)), each a single round-to-nearest-even
   from float64; code = clamp(rint((x - zero) / scale), 0, 2^b - 1) with
   float64 subtraction and division and ties to even; scale 0 gives code 0;
 * a 4-bit code splits into hi = code >> 2 and lo = code & 3; a value whose
   low bits were not fetched is read at the bucket midpoint 4*hi + 3/2;
 * a 2-bit cell is its own 2-bit quantizer, not the high plane of a 4-bit one;
-* the last N mod 32 tokens of a history (the tail) stay exact in bf16;
+* the last N mod 32 tokens of a history (the tail; N mod 64 with groups of 64)
+  stay exact in bf16;
 * a token t < n_q is selected when its coarse softmax weight, taken over the
   whole row including the tail, is at least tau; a selected token uses its
   4-bit K and V, the others their high-bit values; the final softmax runs over
@@ -53,7 +54,8 @@ from __future__ import annotations
 
 import numpy as np
 
-GROUP = 32          # tokens per K group, channels per V group
+GROUP = 32          # tokens per K group, channels per V group (64 is the other supported size)
+GROUPS = (32, 64)
 BLOCK = 16          # tokens per paged block
 KIND_Q4, KIND_Q2, KIND_SHARE = 0, 1, 2
 LAYOUT_PLANES, LAYOUT_KIVI4 = 0, 1
@@ -102,28 +104,30 @@ def quantize_groups(x, bits):
     return q.astype(np.int64), scale, zero
 
 
-def quantize_history(K, V, bits):
-    """Quantize the complete 32-token groups of one (cell, sequence, head) history.
+def quantize_history(K, V, bits, group=GROUP):
+    """Quantize the complete groups of one (cell, sequence, head) history.
 
-    K, V: float64 [N][D]. Tokens t < n_q = 32 * floor(N / 32) are quantized:
-    K per channel over each 32-token group, V per token over each run of 32
-    channels. Returns a dict with
-      n_q, kc [n_q][D], ks/kz [n_q/32][D], vc [n_q][D], vs/vz [n_q][D/32].
+    K, V: float64 [N][D]; group G = 32 or 64 (D a multiple of G). Tokens
+    t < n_q = G * floor(N / G) are quantized: K per channel over each G-token
+    group, V per token over each run of G channels. Returns a dict with
+      n_q, bits, group, kc [n_q][D], ks/kz [n_q/G][D], vc [n_q][D], vs/vz [n_q][D/G].
     """
+    assert group in GROUPS
     K = np.asarray(K, dtype=np.float64)
     V = np.asarray(V, dtype=np.float64)
     N, D = K.shape
-    n_q = GROUP * (N // GROUP)
-    ng = n_q // GROUP
+    assert D % group == 0
+    n_q = group * (N // group)
+    ng = n_q // group
     # K: group over tokens, per channel -> move tokens to the last axis
-    kg = K[:n_q].reshape(ng, GROUP, D).transpose(0, 2, 1)          # [ng][D][32]
+    kg = K[:n_q].reshape(ng, group, D).transpose(0, 2, 1)          # [ng][D][G]
     kc, ks, kz = quantize_groups(kg, bits)
     kc = kc.transpose(0, 2, 1).reshape(n_q, D)
     # V: group over channels, per token
-    vg = V[:n_q].reshape(n_q, D // GROUP, GROUP)                      # [n_q][D/32][32]
+    vg = V[:n_q].reshape(n_q, D // group, group)                      # [n_q][D/G][G]
     vc, vs, vz = quantize_groups(vg, bits)
     vc = vc.reshape(n_q, D)
-    return {"n_q": n_q, "bits": bits, "kc": kc, "ks": ks, "kz": kz,
+    return {"n_q": n_q, "bits": bits, "group": group, "kc": kc, "ks": ks, "kz": kz,
             "vc": vc, "vs": vs, "vz": vz}
 
 
@@ -132,14 +136,14 @@ def quantize_history(K, V, bits):
 # ---------------------------------------------------------------------------
 def _k_meta_per_token(qh):
     n_q = qh["n_q"]
-    ks = np.repeat(qh["ks"], GROUP, axis=0)[:n_q]
-    kz = np.repeat(qh["kz"], GROUP, axis=0)[:n_q]
+    ks = np.repeat(qh["ks"], qh["group"], axis=0)[:n_q]
+    kz = np.repeat(qh["kz"], qh["group"], axis=0)[:n_q]
     return ks, kz
 
 
 def _v_meta_per_elem(qh):
-    vs = np.repeat(qh["vs"], GROUP, axis=1)
-    vz = np.repeat(qh["vz"], GROUP, axis=1)
+    vs = np.repeat(qh["vs"], qh["group"], axis=1)
+    vz = np.repeat(qh["vz"], qh["group"], axis=1)
     return vs, vz
 
 
@@ -175,7 +179,7 @@ def softmax_weights(scores):
     return e / np.sum(e)
 
 
-def decode_row(q, K, V, kind, tau, sm_scale, qh=None, sel_override=None, skip=False):
+def decode_row(q, K, V, kind, tau, sm_scale, qh=None, sel_override=None, skip=False, group=GROUP):
     """One decode-attention row of the loop-aware method.
 
     q: [D] query; K, V: [N][D] history (bf16 values as float64); kind: 0 for a
@@ -207,7 +211,7 @@ def decode_row(q, K, V, kind, tau, sm_scale, qh=None, sel_override=None, skip=Fa
         return np.zeros(D), np.zeros(0, dtype=bool), None
     bits = 2 if kind == KIND_Q2 else 4
     if qh is None:
-        qh = quantize_history(K, V, bits)
+        qh = quantize_history(K, V, bits, group)
     n_q = qh["n_q"]
 
     if kind == KIND_Q2:
@@ -317,11 +321,13 @@ def k_meta_order(D, bits):
     return 8 * w + 2 * k + n
 
 
-def record_bytes(head_dim, kind, layout):
+def record_bytes(head_dim, kind, layout, group=GROUP):
+    """Bytes of one 16-token record: codes (4-bit: 16D, 2-bit: 8D) plus K and V meta
+    (64 D / group bytes each), padded to a multiple of 256."""
     D = head_dim
-    if layout == LAYOUT_KIVI4:
-        return 20 * D
-    return 20 * D if kind == KIND_Q4 else 12 * D
+    codes = 8 * D if (layout == LAYOUT_PLANES and kind == KIND_Q2) else 16 * D
+    n = codes + 2 * (64 * D // group)
+    return (n + 255) // 256 * 256
 
 
 def pack_block(qh, j, layout=LAYOUT_PLANES):
@@ -332,19 +338,21 @@ def pack_block(qh, j, layout=LAYOUT_PLANES):
     4-bit, KIVI-4 layout: [K4   | K_meta | V4   | V_meta]
     K planes are column-major (16-channel columns of the 16 tokens), V planes
     channel-major (see the helpers above).
-    K_meta of group g = j // 2 holds one word per channel in the order of
-    k_meta_order (a permutation inside each K column), split over the group's
-    two blocks: block 2g holds positions 0..D/2-1, block 2g+1 the rest. V_meta is
-    [D/32 channel groups][16 tokens].
+    K_meta of group g = j // P (P = group / 16 blocks per group) holds one word per
+    channel in the order of k_meta_order (a permutation inside each K column),
+    split over the group's P blocks: block P g + i holds positions i D/P ..
+    (i+1) D/P - 1. V_meta is [D/group channel groups][16 tokens]. The returned bytes
+    stop before the record's padding (record_bytes rounds up to 256).
     """
     t0 = BLOCK * j
     assert t0 + BLOCK <= qh["n_q"]
     kc = qh["kc"][t0:t0 + BLOCK]
     vc = qh["vc"][t0:t0 + BLOCK]
     D = kc.shape[1]
-    g, half = divmod(j, 2)
+    per = qh["group"] // BLOCK
+    g, part = divmod(j, per)
     order = k_meta_order(D, 4 if layout == LAYOUT_KIVI4 else 2)
-    ch = order[half * D // 2:(half + 1) * D // 2]
+    ch = order[part * D // per:(part + 1) * D // per]
     kmeta = _meta_words(qh["ks"][g, ch], qh["kz"][g, ch])
     vmeta = _meta_words(qh["vs"][t0:t0 + BLOCK].T.reshape(-1), qh["vz"][t0:t0 + BLOCK].T.reshape(-1))
     if layout == LAYOUT_KIVI4:
@@ -357,11 +365,11 @@ def pack_block(qh, j, layout=LAYOUT_PLANES):
     return np.concatenate(parts)
 
 
-def tail_tokens(K_bits, V_bits):
-    """Tail of a history given as bf16 bit patterns [N][D]: the last N mod 32 tokens,
-    returned as (first position, K bits, V bits). Slot of position t is t mod 32."""
+def tail_tokens(K_bits, V_bits, group=GROUP):
+    """Tail of a history given as bf16 bit patterns [N][D]: the last N mod group tokens,
+    returned as (first position, K bits, V bits). Slot of position t is t mod group."""
     N = K_bits.shape[0]
-    n_q = GROUP * (N // GROUP)
+    n_q = group * (N // group)
     return n_q, K_bits[n_q:], V_bits[n_q:]
 
 

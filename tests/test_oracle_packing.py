@@ -51,39 +51,47 @@ def _meta(buf):
     return s, z
 
 
+@pytest.mark.parametrize("group", [32, 64])
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("layout,bits", [(O.LAYOUT_PLANES, 4), (O.LAYOUT_PLANES, 2), (O.LAYOUT_KIVI4, 4)])
-def test_pack_roundtrip(D, layout, bits):
-    rng = np.random.default_rng(D + bits + layout)
-    q, K, V = _row(rng, 64, D, outliers=3)
-    qh = O.quantize_history(K, V, bits)
-    for j in range(4):
+def test_pack_roundtrip(D, layout, bits, group):
+    rng = np.random.default_rng(D + bits + layout + group)
+    q, K, V = _row(rng, 128, D, outliers=3)
+    qh = O.quantize_history(K, V, bits, group)
+    M = 64 * D // group   # bytes of K meta, and of V meta, in one record
+    per = group // 16     # records per group
+    for j in range(8):
         rec = O.pack_block(qh, j, layout)
         kind = O.KIND_Q4 if bits == 4 else O.KIND_Q2
-        assert rec.size == O.record_bytes(D, kind, layout)
+        size = O.record_bytes(D, kind, layout, group)
+        assert size % 256 == 0 and rec.size <= size < rec.size + 256
         t0 = 16 * j
-        g, half = divmod(j, 2)
+        g, part = divmod(j, per)
         if layout == O.LAYOUT_KIVI4:
             kc = _unpack_k(rec[:8 * D], D, 4)
-            km = rec[8 * D:10 * D]
-            vc = _unpack_channel_major_4bit(rec[10 * D:18 * D], D)
-            vm = rec[18 * D:20 * D]
+            km = rec[8 * D:8 * D + M]
+            vc = _unpack_channel_major_4bit(rec[8 * D + M:16 * D + M], D)
+            vm = rec[16 * D + M:16 * D + 2 * M]
+            assert rec.size == 16 * D + 2 * M
         elif bits == 2:
             kc = _unpack_k(rec[:4 * D], D, 2)
-            km = rec[4 * D:6 * D]
-            vc = _unpack_channel_major_2bit(rec[6 * D:10 * D], D)
-            vm = rec[10 * D:12 * D]
+            km = rec[4 * D:4 * D + M]
+            vc = _unpack_channel_major_2bit(rec[4 * D + M:8 * D + M], D)
+            vm = rec[8 * D + M:8 * D + 2 * M]
+            assert rec.size == 8 * D + 2 * M
         else:
-            kc = 4 * _unpack_k(rec[:4 * D], D, 2) + _unpack_k(rec[12 * D:16 * D], D, 2)
-            vc = 4 * _unpack_channel_major_2bit(rec[6 * D:10 * D], D) + \
-                _unpack_channel_major_2bit(rec[16 * D:20 * D], D)
-            km, vm = rec[4 * D:6 * D], rec[10 * D:12 * D]
+            kc = 4 * _unpack_k(rec[:4 * D], D, 2) + _unpack_k(rec[8 * D + 2 * M:12 * D + 2 * M], D, 2)
+            vc = 4 * _unpack_channel_major_2bit(rec[4 * D + M:8 * D + M], D) + \
+                _unpack_channel_major_2bit(rec[12 * D + 2 * M:16 * D + 2 * M], D)
+            km, vm = rec[4 * D:4 * D + M], rec[8 * D + M:8 * D + 2 * M]
+            assert rec.size == 16 * D + 2 * M
         assert np.array_equal(kc, qh["kc"][t0:t0 + 16])
         assert np.array_equal(vc, qh["vc"][t0:t0 + 16])
         ks, kz = _meta(km)
+        assert ks.size == D // per
         # position -> channel inside a K column: 2-bit word byte k / bit pair p, or byte k / nibble n
-        for i in range(D // 2):
-            pos = half * D // 2 + i
+        for i in range(D // per):
+            pos = part * D // per + i
             if layout == O.LAYOUT_KIVI4:
                 w, r = divmod(pos, 8)
                 chn = 8 * w + 2 * (r % 4) + r // 4
@@ -92,5 +100,5 @@ def test_pack_roundtrip(D, layout, bits):
                 chn = 16 * w + 4 * (r % 4) + r // 4
             assert ks[i] == qh["ks"][g, chn] and kz[i] == qh["kz"][g, chn]
         vs, vz = _meta(vm)
-        assert np.array_equal(vs.reshape(D // 32, 16).T, qh["vs"][t0:t0 + 16])
-        assert np.array_equal(vz.reshape(D // 32, 16).T, qh["vz"][t0:t0 + 16])
+        assert np.array_equal(vs.reshape(D // group, 16).T, qh["vs"][t0:t0 + 16])
+        assert np.array_equal(vz.reshape(D // group, 16).T, qh["vz"][t0:t0 + 16])

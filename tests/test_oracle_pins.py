@@ -113,22 +113,28 @@ def test_quantizer_constant_group():
     assert s[0] == 0.0 and z[0] == 0.75 and np.all(c == 0)
 
 
-def test_history_grouping_axes():
-    """K groups run over 32 tokens of one channel; V groups over 32 channels of one token."""
+@pytest.mark.parametrize("G", [32, 64])
+def test_history_grouping_axes(G):
+    """K groups run over G tokens of one channel; V groups over G channels of one token."""
     rng = np.random.default_rng(3)
-    q, K, V = _row(rng, 70, 64)
-    qh = O.quantize_history(K, V, 4)
-    assert qh["n_q"] == 64
+    q, K, V = _row(rng, 2 * G + 6, 128)
+    qh = O.quantize_history(K, V, 4, G)
+    assert qh["n_q"] == 2 * G and qh["ks"].shape == (2, 128) and qh["vs"].shape == (2 * G, 128 // G)
     for g in range(2):
-        for d in (0, 17, 63):
-            c, s, z = O.quantize_groups(K[32 * g:32 * g + 32, d][None, :], 4)
-            assert np.array_equal(qh["kc"][32 * g:32 * g + 32, d], c[0])
+        for d in (0, 17, 63, 127):
+            c, s, z = O.quantize_groups(K[G * g:G * g + G, d][None, :], 4)
+            assert np.array_equal(qh["kc"][G * g:G * g + G, d], c[0])
             assert qh["ks"][g, d] == s[0] and qh["kz"][g, d] == z[0]
-    for t in (0, 31, 63):
-        for e in range(2):
-            c, s, z = O.quantize_groups(V[t, 32 * e:32 * e + 32][None, :], 4)
-            assert np.array_equal(qh["vc"][t, 32 * e:32 * e + 32], c[0])
+    for t in (0, 31, G - 1, 2 * G - 1):
+        for e in range(128 // G):
+            c, s, z = O.quantize_groups(V[t, G * e:G * e + G][None, :], 4)
+            assert np.array_equal(qh["vc"][t, G * e:G * e + G], c[0])
             assert qh["vs"][t, e] == s[0] and qh["vz"][t, e] == z[0]
+    # dequantized values carry their own group's scale and zero
+    full = O.dequant_full(qh, "k")
+    assert full[G + 5, 9] == qh["kz"][1, 9] + qh["ks"][1, 9] * qh["kc"][G + 5, 9]
+    full = O.dequant_full(qh, "v")
+    assert full[7, 127] == qh["vz"][7, 127 // G] + qh["vs"][7, 127 // G] * qh["vc"][7, 127]
 
 
 # ----------------------------------------------------------------- decode closed forms
@@ -146,25 +152,28 @@ def _hi_only(qh, K, V):
     return Kt, Vt
 
 
+@pytest.mark.parametrize("G", [32, 64])
 @pytest.mark.parametrize("N", [32, 100, 256, 1000])
-def test_p1_tau0_equals_full_4bit(N):
+def test_p1_tau0_equals_full_4bit(N, G):
     rng = np.random.default_rng(N)
     q, K, V = _row(rng, N, 64, outliers=4)
     sig = 1 / 8
-    o, sel, _ = O.decode_row(q, K, V, O.KIND_Q4, 0.0, sig)
-    qh = O.quantize_history(K, V, 4)
+    o, sel, _ = O.decode_row(q, K, V, O.KIND_Q4, 0.0, sig, group=G)
+    qh = O.quantize_history(K, V, 4, G)
+    assert sel.size == G * (N // G)
     ref = O.attention_reference(q, *_full4(qh, K, V), sig)
     assert sel.all()
     np.testing.assert_allclose(o, ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
 
 
+@pytest.mark.parametrize("G", [32, 64])
 @pytest.mark.parametrize("tau", [1.0000001, 1.1, 5.0])
-def test_p2_tau_above_one_equals_high_bits_only(tau):
+def test_p2_tau_above_one_equals_high_bits_only(tau, G):
     rng = np.random.default_rng(11)
     q, K, V = _row(rng, 300, 128, outliers=3, mult=10)
     sig = 128 ** -0.5
-    o, sel, _ = O.decode_row(q, K, V, O.KIND_Q4, tau, sig)
-    qh = O.quantize_history(K, V, 4)
+    o, sel, _ = O.decode_row(q, K, V, O.KIND_Q4, tau, sig, group=G)
+    qh = O.quantize_history(K, V, 4, G)
     ref = O.attention_reference(q, *_hi_only(qh, K, V), sig)
     assert not sel.any()
     np.testing.assert_allclose(o, ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
@@ -279,39 +288,45 @@ def test_p14_storage_ratio():
     kivi = 96 * O.record_bytes(D, O.KIND_Q4, O.LAYOUT_KIVI4)
     assert O.record_bytes(D, O.KIND_Q4, O.LAYOUT_PLANES) == 16 * 160
     assert O.record_bytes(D, O.KIND_Q2, O.LAYOUT_PLANES) == 16 * 96
+    # groups of 64 halve the meta: 144 and 80 bytes per token-head at D = 128
+    assert O.record_bytes(D, O.KIND_Q4, O.LAYOUT_PLANES, 64) == 16 * 144
+    assert O.record_bytes(D, O.KIND_Q2, O.LAYOUT_PLANES, 64) == 16 * 80
+    # D = 64 with groups of 64: 1152 and 640 bytes, padded to 256-byte multiples
+    assert O.record_bytes(64, O.KIND_Q4, O.LAYOUT_PLANES, 64) == 1280
+    assert O.record_bytes(64, O.KIND_Q2, O.LAYOUT_PLANES, 64) == 768
     assert abs(ours / kivi - (48 * 160 + 29 * 96) / (96 * 160)) < 1e-15
     assert abs(ours / kivi - 0.68125) < 1e-12
 
 
 # ----------------------------------------------------------------- P5 brute force
-@pytest.mark.parametrize("D", [32, 64])
-@pytest.mark.parametrize("N", [1, 31, 32, 33, 64, 65])
-def test_p5_tiny_rows_brute_force(D, N):
-    rng = np.random.default_rng(100 * D + N)
+@pytest.mark.parametrize("D,G,N", [(D, 32, N) for D in (32, 64) for N in (1, 31, 32, 33, 64, 65)] +
+                         [(64, 64, N) for N in (1, 63, 64, 65, 128, 129)])
+def test_p5_tiny_rows_brute_force(D, G, N):
+    rng = np.random.default_rng(100 * D + N + G)
     q, K, V = _row(rng, N, D, outliers=2 if D == 64 else 0)
     q = q * 2.5
     sig = D ** -0.5
     tau = 0.02
-    n_q = 32 * (N // 32)
-    # exact-rational quantization, independent of the oracle
+    n_q = G * (N // G)
+    # exact-rational quantization over groups of G, independent of the oracle
     Kq = K.copy()
     Khi = K.copy()
     Vq = V.copy()
     Vhi = V.copy()
-    for g in range(n_q // 32):
+    for g in range(n_q // G):
         for d in range(D):
-            codes, s, z, flagged = brute.quantize_exact(K[32 * g:32 * g + 32, d], 4)
+            codes, s, z, flagged = brute.quantize_exact(K[G * g:G * g + G, d], 4)
             assert not flagged
             for i, c in enumerate(codes):
-                Kq[32 * g + i, d] = float(z + c * s)
-                Khi[32 * g + i, d] = float(z + (4 * (c // 4) + Fraction(3, 2)) * s)
+                Kq[G * g + i, d] = float(z + c * s)
+                Khi[G * g + i, d] = float(z + (4 * (c // 4) + Fraction(3, 2)) * s)
     for t in range(n_q):
-        for e in range(D // 32):
-            codes, s, z, flagged = brute.quantize_exact(V[t, 32 * e:32 * e + 32], 4)
+        for e in range(D // G):
+            codes, s, z, flagged = brute.quantize_exact(V[t, G * e:G * e + G], 4)
             assert not flagged
             for i, c in enumerate(codes):
-                Vq[t, 32 * e + i] = float(z + c * s)
-                Vhi[t, 32 * e + i] = float(z + (4 * (c // 4) + Fraction(3, 2)) * s)
+                Vq[t, G * e + i] = float(z + c * s)
+                Vhi[t, G * e + i] = float(z + (4 * (c // 4) + Fraction(3, 2)) * s)
     # coarse softmax in 50 digits, selection, then final attention in 50 digits
     _, phat = brute.attention_mp(q, Khi, Vhi, sig)
     sel = [float(p) >= tau for p in phat[:n_q]]
@@ -320,7 +335,8 @@ def test_p5_tiny_rows_brute_force(D, N):
     Vf = np.array([Vq[t] if t < n_q and sel[t] else Vhi[t] for t in range(N)])
     ref, _ = brute.attention_mp(q, Kf, Vf, sig)
     ref = np.array([float(x) for x in ref])
-    o, osel, _ = O.decode_row(q, K, V, O.KIND_Q4, tau, sig)
+    o, osel, _ = O.decode_row(q, K, V, O.KIND_Q4, tau, sig, group=G)
+    assert osel.size == n_q
     for t in range(n_q):
         if not near[t]:
             assert osel[t] == sel[t]

@@ -66,12 +66,13 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def algorithmic_bytes(plan, lengths, H, D, sel_counts=None, layout_kivi=False, out_bytes=2, q_bytes=2):
+def algorithmic_bytes(plan, lengths, H, D, sel_counts=None, layout_kivi=False, out_bytes=2, q_bytes=2, group=32):
     """Bytes one whole-plan decode must move.
 
-    Per (cell, sequence, head) row with N tokens, n_q = 32 floor(N/32):
-      quantized prefix: 96 B/token (D=128: K_hi 32 + K_meta 16 + V_hi 32 + V_meta 16), plus
-      64 B (K_lo + V_lo) per selected token on a 4-bit target; KIVI-4 reads 160 B/token;
+    Per (cell, sequence, head) row with N tokens, n_q = G floor(N/G) (G = group):
+      quantized prefix: D/2 + 8D/G B/token (D=128, G=32: K_hi 32 + K_meta 16 + V_hi 32 +
+      V_meta 16 = 96; G=64: 80), plus D/2 B (K_lo + V_lo) per selected token on a 4-bit
+      target; KIVI-4 reads D + 8D/G B/token (160 at D=128, G=32);
       tail: 4*D B/token (bf16 K and V); query and output: D * dtype bytes each;
       block table: 4 B per 16-token block; length: 4 B.
     sel_counts[c][b][h] is the number of selected tokens (4-bit targets only).
@@ -79,15 +80,15 @@ def algorithmic_bytes(plan, lengths, H, D, sel_counts=None, layout_kivi=False, o
     import numpy as np
     plan = np.asarray(plan).reshape(-1)
     n_loops_layers = plan.size
-    per_tok_base = 96 * D // 128
-    per_tok_lo = 64 * D // 128
-    per_tok_kivi = 160 * D // 128
+    per_tok_base = D // 2 + 8 * D // group
+    per_tok_lo = D // 2
+    per_tok_kivi = D + 8 * D // group
     total = 0
     n_layers = None
     for c in range(n_loops_layers):
         kind = plan[c]
         for b, N in enumerate(lengths):
-            n_q = 32 * (N // 32)
+            n_q = group * (N // group)
             row = (N - n_q) * 4 * D + D * q_bytes + D * out_bytes + 4 * ((N + 15) // 16) + 4
             if layout_kivi:
                 row += n_q * per_tok_kivi
@@ -100,21 +101,22 @@ def algorithmic_bytes(plan, lengths, H, D, sel_counts=None, layout_kivi=False, o
     return total
 
 
-def algorithmic_bytes_skip(tk, lengths, H, D, sel_counts, out_bytes=2, q_bytes=2):
+def algorithmic_bytes_skip(tk, lengths, H, D, sel_counts, out_bytes=2, q_bytes=2, group=32):
     """Bytes of the token-skipping ablation's whole-plan decode: rows with a 4-bit target read
-    48 B/token (D=128: K_hi 32 + K_meta 16) plus 112 B per selected token (K_lo 32 + V_hi 32 +
-    V_lo 32 + V_meta 16); 2-bit targets, tails, q, output and block table as in the method."""
+    D/4 + 4D/G B/token (D=128, G=32: K_hi 32 + K_meta 16) plus 3D/4 + 4D/G per selected token
+    (K_lo 32 + V_hi 32 + V_lo 32 + V_meta 16); 2-bit targets, tails, q, output and block table
+    as in the method."""
     import numpy as np
     tk = np.asarray(tk).reshape(-1)
     total = 0
     for c in range(tk.size):
         for b, N in enumerate(lengths):
-            n_q = 32 * (N // 32)
+            n_q = group * (N // group)
             row = (N - n_q) * 4 * D + D * q_bytes + D * out_bytes + 4 * ((N + 15) // 16) + 4
-            row += n_q * (48 if tk[c] == 0 else 96) * D // 128
+            row += n_q * ((D // 4 + 4 * D // group) if tk[c] == 0 else (D // 2 + 8 * D // group))
             total += H * row
             if tk[c] == 0:
-                total += (112 * D // 128) * int(sel_counts[c, b].sum())
+                total += (3 * D // 4 + 4 * D // group) * int(sel_counts[c, b].sum())
     return total
 
 
@@ -128,14 +130,14 @@ def target_kinds(plan, n_loops, n_layers):
     return out
 
 
-def append_bytes(n_storing, B, H, D, lengths_before):
+def append_bytes(n_storing, B, H, D, lengths_before, group=32):
     """Bytes of a one-token append: bf16 K and V in, one tail slot out; a completed group
-    also reads its 31 tail tokens and writes two records."""
+    also reads its G - 1 tail tokens and writes its G / 16 4-bit records (G D + 8 D bytes)."""
     import numpy as np
     tok = 2 * H * D * 2
     total = n_storing * B * (tok + tok)
-    done = sum(1 for n in lengths_before if n % 32 == 31)
-    return total + n_storing * done * H * (31 * 2 * D * 2 + 2 * 20 * D)
+    done = sum(1 for n in lengths_before if n % group == group - 1)
+    return total + n_storing * done * H * ((group - 1) * 2 * D * 2 + group * D + 8 * D)
 
 
 def sel_counts_from_mask(sm, n_q):
@@ -178,12 +180,13 @@ def cpu_baseline(cfg, plan, tau, rows, log, min_seconds=10.0, max_evals=400):
     while evals < max_evals and (t_total < min_seconds or evals < len(inputs)):
         q, K, V, kind, N = inputs[evals % len(inputs)]
         t0 = time.perf_counter()
-        o, sel, _ = O.decode_row(q, K, V, kind, tau, sig)
+        o, sel, _ = O.decode_row(q, K, V, kind, tau, sig, group=cfg.group)
         t_total += time.perf_counter() - t0
-        n_q = 32 * (N // 32)
-        bytes_total += n_q * 96 + (N - n_q) * 512 + 512 + 4 * ((N + 15) // 16) + 4
+        D, G = cfg.head_dim, cfg.group
+        n_q = G * (N // G)
+        bytes_total += n_q * (D // 2 + 8 * D // G) + (N - n_q) * 4 * D + 4 * D + 4 * ((N + 15) // 16) + 4
         if kind == 0:
-            bytes_total += 64 * int(sel.sum())
+            bytes_total += D // 2 * int(sel.sum())
         evals += 1
     log(f"cpu oracle: {evals} row evaluations ({len(inputs)} distinct rows) in {t_total:.2f}s")
     cpu_model = "unknown"
@@ -257,6 +260,8 @@ def main():
     ap.add_argument("--no-serving", action="store_true",
                     help="skip the per-(loop, layer) graph legs (batch 32 and batch 1)")
     ap.add_argument("--cpu-rows", type=int, default=6)
+    ap.add_argument("--group", type=int, choices=[32, 64], default=32,
+                    help="quantization group (tokens per K group, channels per V group); the pages' is 32")
     ap.add_argument("--table", choices=["shuffled", "identity"], default="shuffled",
                     help="block table of the workload (the configuration uses a shuffled one)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -292,6 +297,7 @@ def main():
     cfg.lengths = [args.ctx - S] * args.batch
     cfg.append_steps = S + GS
     cfg.shuffled = args.table == "shuffled"
+    cfg.group = GQ = args.group
     plan = cfg.plan.reshape(-1)
     H, D, C, B = cfg.n_heads, cfg.head_dim, cfg.n_cells, cfg.batch
 
@@ -335,14 +341,14 @@ def main():
     tk = target_kinds(plan, cfg.n_loops, cfg.n_layers)
     counts = sel_counts_from_mask(sm, None)
     counts[tk != 0] = 0
-    dec_bytes = algorithmic_bytes(plan, final_lens, H, D, counts)
+    dec_bytes = algorithmic_bytes(plan, final_lens, H, D, counts, group=GQ)
     n_storing = len(wl.storing_cells())
-    step_bytes = [algorithmic_bytes(plan, wl.current_lengths(s + 1), H, D, counts) +
-                  append_bytes(n_storing, B, H, D, lengths_before[s]) for s in range(args.warmup, S)]
+    step_bytes = [algorithmic_bytes(plan, wl.current_lengths(s + 1), H, D, counts, group=GQ) +
+                  append_bytes(n_storing, B, H, D, lengths_before[s], group=GQ) for s in range(args.warmup, S)]
     value = float(np.mean(step_bytes)) / (ms_per_step * 1e-3) / 1e9
     dec_mean_ms = float(np.mean(dec_ms))
     achieved = dec_bytes / (dec_mean_ms * 1e-3) / 1e9
-    sel_frac = float(counts.sum()) / max(1, sum(int(H * B * (32 * (final_lens[0] // 32))) for c in range(C) if tk[c] == 0))
+    sel_frac = float(counts.sum()) / max(1, sum(int(H * B * (GQ * (final_lens[0] // GQ))) for c in range(C) if tk[c] == 0))
     log(f"step {ms_per_step:.3f} ms (events {np.mean(step_ms):.3f}), decode {dec_mean_ms:.3f} ms, "
         f"append {np.mean(app_ms):.3f} ms; decode {achieved:.0f} GB/s algorithmic; selected fraction {sel_frac:.2e}")
 
@@ -354,7 +360,7 @@ def main():
                                    sel_mask=True)
             ct = sel_counts_from_mask(smt, None)
             ct[tk != 0] = 0
-            bts = algorithmic_bytes(plan, final_lens, H, D, ct)
+            bts = algorithmic_bytes(plan, final_lens, H, D, ct, group=GQ)
             e_a, e_b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             wl.ctx.decode(q, wl.bt, wl.seq_lens, max(final_lens), tau, out=out, out_dtype=torch.bfloat16)
             e_a.record(stream)
@@ -372,7 +378,7 @@ def main():
                                sel_mask=True, skip=True)
         cs = sel_counts_from_mask(sms, None)
         cs[tk != 0] = 0
-        sb = algorithmic_bytes_skip(tk, final_lens, H, D, cs)
+        sb = algorithmic_bytes_skip(tk, final_lens, H, D, cs, group=GQ)
         e_a, e_b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e_a.record(stream)
         for _ in range(3):
@@ -400,6 +406,7 @@ def main():
         scfg.batch = 1
         scfg.lengths = [args.ctx]
         scfg.append_steps = len(SERVING_SPLITS) * (SERVING_WARM + SERVING_REPS)
+        scfg.group = GQ
         sw = Workload(scfg, gpu_synth=True, log=log)
         sw.fill()
         sq = sw.q_all()
@@ -417,12 +424,13 @@ def main():
         kcfg = R.make_config("C4")
         kcfg.batch = B
         kcfg.lengths = list(final_lens)
+        kcfg.group = GQ
         kcfg.append_steps = 0
         t1 = time.time()
         kw = Workload(kcfg, layout=lkv.LAYOUT_KIVI4, gpu_synth=True, log=log)
         kw.fill()
         log(f"KIVI-4 cache filled in {time.time() - t1:.1f}s")
-        kb = algorithmic_bytes(plan, final_lens, H, D, layout_kivi=True)
+        kb = algorithmic_bytes(plan, final_lens, H, D, layout_kivi=True, group=GQ)
         kw.decode(q, args.tau, out_dtype=torch.bfloat16, sel_mask=False)
         e_a, e_b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e_a.record(stream)
@@ -461,6 +469,7 @@ def main():
         ccfg.batch = B
         ccfg.lengths = [args.ctx - S] * B     # the initial histories of the timed workload
         ccfg.append_steps = S + GS
+        ccfg.group = GQ
         cpu = cpu_baseline(ccfg, plan, args.tau, rows, log)
 
     line = {
@@ -480,11 +489,13 @@ def main():
         "data": "synthetic (seeded Philox normal draws, shapes of the pages' Ouro-1.4B 16K serving workload)",
         "config": {"workload": "4 loops x 24 layers, 48 q4 / 29 q2 / 19 reuse, 16 heads x 128, batch 32, "
                                f"context {args.ctx} (last step), 16-token blocks shuffled, tau {args.tau}, "
-                               "1-token append + whole-plan decode per step",
+                               "1-token append + whole-plan decode per step"
+                               + ("" if GQ == 32 else f", quantization groups of {GQ}"),
                    "global_batch": B, "seq_len": args.ctx, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": counter_traffic(),
-                     "kernel": "k_decode<128, tau regime>", "bytes_per_launch": dec_bytes,
+                     "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": counter_traffic() if GQ == 32 else None,   # the counters cover groups of 32
+                     "kernel": f"k_decode<128, {GQ}, tau regime, PH_ROW>", "bytes_per_launch": dec_bytes,
                      "mean_launch_ms": round(dec_mean_ms, 4)},
         "cpu_baseline": cpu,
         "selected_fraction_q4_targets": sel_frac,

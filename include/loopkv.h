@@ -13,8 +13,8 @@
  * is the baseline run on the same kernel (abstract: the serving sentence).
  *
  * The abstract gives no formula; this library fixes:
- *   - KIVI-style asymmetric groups of 32: K per channel over 32 consecutive
- *     tokens, V per token over 32 consecutive channels. zero = f16(min),
+ *   - KIVI-style asymmetric groups of G = group_size (32, or 64): K per channel
+ *     over G consecutive tokens, V per token over G consecutive channels. zero = f16(min),
  *     scale = f16((max - min) / (2^b - 1)), code = clamp(rint((x - zero) /
  *     scale), 0, 2^b - 1), all in float64 with a single round-to-nearest-even
  *     to f16; scale 0 gives code 0.
@@ -24,16 +24,18 @@
  *   - Selection: a token t of the quantized prefix is fetched at 4 bits when
  *     its coarse softmax weight (scores from high bits, softmax over the whole
  *     row) is >= tau. tau = 0 fetches every token, tau > 1 none.
- *   - The last (len mod 32) tokens of a sequence are kept exact in bf16 (the
+ *   - The last (len mod G) tokens of a sequence are kept exact in bf16 (the
  *     tail) and quantized by the append that completes their group.
  *
  * Storage (per storing cell, caller-allocated workspace):
  *   pool  [num_blocks * block_tokens/16][KV heads][record]   record of 16 tokens, one KV head
- *   tails [max_seqs][KV heads][2 (K,V)][32][head_dim] bf16
- * Record layouts (D = head_dim, all words little-endian u32):
- *   4-bit planes : [K_hi 4D | K_meta 2D | V_hi 4D | V_meta 2D | K_lo 4D | V_lo 4D]  = 20D bytes
- *   2-bit        : [K2 4D   | K_meta 2D | V2 4D   | V_meta 2D]                      = 12D bytes
- *   KIVI-4       : [K4 8D   | K_meta 2D | V4 8D   | V_meta 2D]                      = 20D bytes
+ *   tails [max_seqs][KV heads][2 (K,V)][G][head_dim] bf16
+ * Record layouts (D = head_dim, M = 64D/G meta bytes: 2D for G = 32, D for G = 64; all
+ * words little-endian u32; each record padded to a multiple of 256 bytes, which only
+ * D = 64 with G = 64 needs):
+ *   4-bit planes : [K_hi 4D | K_meta M | V_hi 4D | V_meta M | K_lo 4D | V_lo 4D]  = 20D (G 32), 18D (G 64)
+ *   2-bit        : [K2 4D   | K_meta M | V2 4D   | V_meta M]                      = 12D (G 32), 10D (G 64)
+ *   KIVI-4       : [K4 8D   | K_meta M | V4 8D   | V_meta M]                      = 20D (G 32), 18D (G 64)
  *   (the bytes a decode reads for every token — high K part, then high V part — are
  *   each contiguous; the low planes follow and are read only where selected)
  *   K plane (2-bit): D/16 columns x 16 tokens of u32; word (w, t) holds channels
@@ -47,8 +49,8 @@
  *   K_meta of group g: one word per channel, permuted inside each K column so that a
  *     column's words follow its bit layout — 2-bit: position 16w+4p+k holds channel
  *     16w+4k+p; 4-bit: position 8w+4n+k holds channel 8w+2k+n — and split over the
- *     group's two blocks: logical block 2g holds positions 0..D/2-1, 2g+1 the rest.
- *   V_meta: [D/32 channel groups][16 tokens].
+ *     group's P = G/16 blocks: logical block P*g + i holds positions i*D/P .. (i+1)*D/P - 1.
+ *   V_meta: [D/G channel groups][16 tokens].
  *
  * Paging: block_table[b * bt_stride + p] is the physical page of logical page p
  * (tokens block_tokens*p .. block_tokens*(p+1)-1) of sequence b; the same id addresses
@@ -81,7 +83,7 @@ typedef enum {
   LOOPKV_ERR_PLAN = 2,        /* no plan loaded, kind > 2, reuse cell in the final loop, bad cell index */
   LOOPKV_ERR_WORKSPACE = 3,   /* workspace not bound, too small, or not 256-byte aligned */
   LOOPKV_ERR_CAPACITY = 4,    /* bt_stride * block_tokens < max_len, max_len above the supported maximum */
-  LOOPKV_ERR_UNSUPPORTED = 5, /* head_dim not 64/128/256, group != 32, block not 16/32, too many cells */
+  LOOPKV_ERR_UNSUPPORTED = 5, /* head_dim not 64/128/256, group not 32/64, block not 16/32, too many cells */
   LOOPKV_ERR_HIP = 6          /* HIP runtime / launch failure */
 } loopkv_status;
 
@@ -100,7 +102,7 @@ typedef struct {
   int32_t n_loops, n_layers; /* cells = n_loops * n_layers, row-major [loop][layer] */
   int32_t n_heads;           /* query heads */
   int32_t head_dim;          /* 64, 128 or 256 */
-  int32_t group_size;        /* must be 32 */
+  int32_t group_size;        /* quantization group G: 32 (the default reading) or 64 */
   int32_t block_tokens;      /* tokens per page of the block table: 16 or 32 */
   int32_t num_blocks;        /* physical pages in each storing cell's pool; a pool (num_blocks x
                                 block_tokens/16 x KV heads x 20*head_dim bytes) stays below 4 GiB */
@@ -141,11 +143,10 @@ loopkv_status loopkv_cell_storage(const loopkv_ctx* ctx, int32_t loop, int32_t l
  * storing cell ((-1, -1)). k, v: device [cells][n_seqs][n_new][H][D] (whole plan,
  * cells = n_loops*n_layers, SHARE entries ignored) or [n_seqs][n_new][H][D]; F32 input
  * is rounded to bf16 (nearest even). seq_slots: device [n_seqs] tail slot of each
- * sequence or NULL for slot = b. block_table: device [n_seqs][bt_stride]; the page(s) of
- * tokens 32g..32g+31 (pages 2g and 2g+1 of 16 tokens, page g of 32) must be mapped before
- * the append that completes group g. seq_lens: device
+ * sequence or NULL for slot = b. block_table: device [n_seqs][bt_stride]; the pages of
+ * tokens G*g .. G*g+G-1 must be mapped before the append that completes group g. seq_lens: device
  * [n_seqs], length before the append (read only; the caller advances it). Completed
- * 32-token groups are quantized into the pool; the rest goes to the tail. Appending to
+ * groups of G tokens are quantized into the pool; the rest goes to the tail. Appending to
  * a SHARE cell is a no-op. */
 loopkv_status loopkv_append(loopkv_ctx* ctx, hipStream_t stream, int32_t loop, int32_t layer,
                             const void* k, const void* v, int32_t kv_dtype,

@@ -21,12 +21,17 @@
 //       the scores stay in LDS;
 //   max the wave's running maximum m; on a new maximum its accumulators are rescaled;
 //   V   weights w_t = exp(s_t - m) times the codes, accumulated per channel.
-// The last (len mod 32) tokens are exact bf16 and join the same online softmax.
+// The last (len mod GS) tokens are exact bf16 and join the same online softmax.
+//
+// Quantization groups GS of 32 (the default) or 64 tokens / channels are a template
+// parameter; the kernel works in 32-token units either way (selection words, gathers,
+// step geometry), and a unit of a 64-group reads its group's meta: K meta from the
+// group's four records (a quarter each), V meta word e / 2 for 32-channel slice e.
 //
 // Selection (0 < tau <= 1, 4-bit target): after the pass the row's coarse maximum M
 // and sum L are known; token t of the quantized prefix is selected when
-// exp(s_t - M) / L >= tau. The groups holding a selected token are gathered (a ballot
-// over the per-group masks); their low K plane refines the selected scores, and the
+// exp(s_t - M) / L >= tau. The 32-token units holding a selected token are gathered (a
+// ballot over the per-unit masks); their low K plane refines the selected scores, and the
 // selected tokens' contributions are corrected in place:
 //   w' (z + s (4 hi + lo)) - w (z + s (4 hi + 3/2)),  w, w' = exp(coarse, refined - m).
 // Token weights enter the value sums as 16-bit fixed point against the largest weight of
@@ -260,12 +265,14 @@ struct Acc {
 // ----------------------------------------------------------------------------- step geometry
 // A step covers TPS tokens: 64, or 32 for 4-bit codes at D = 128 and for D = 256, so that
 // every lane reads 32 bytes of K codes and 32 bytes of V codes (16 for 2-bit codes at D = 64).
-template <int D, int MODE>
+template <int D, int MODE, int GS>
 struct Geo {
   static constexpr bool KIVI = MODE == MODE_KIVI;
   static constexpr bool DENSE = MODE == MODE_DENSE;
   static constexpr int TPS = (D == 256 || ((KIVI || DENSE) && D == 128)) ? 32 : 64;
-  static constexpr int GPS = TPS / kGroup;      // groups per step
+  static constexpr int GPS = TPS / kUnit;       // 32-token units per step
+  static constexpr int GU = GS / kUnit;         // units per quantization group (1 or 2)
+  static constexpr int GP = GS / kBlock;        // records per quantization group (2 or 4)
   static constexpr int BPS = TPS / kBlock;      // blocks per step
   // K: a group is covered by LPG lanes = 2 blocks x 4 token quads x CPG column lanes;
   // a column is one 32-bit word of UNIT channels, NC columns per lane.
@@ -280,12 +287,12 @@ struct Geo {
   // V: LPB lanes per block, VCH channels per lane; weight lanes (block, bit pair, group).
   static constexpr int LPB = 64 / BPS;
   static constexpr int VCH = D / LPB;
-  static constexpr int NE = D / kGroup;
+  static constexpr int NE = D / kUnit;           // 32-channel V slices per token (GU share a meta word)
   static constexpr int COOP = BPS * 4 * NE;
   static constexpr int VW = KIVI ? 2 * VCH : VCH;   // code words per lane (high plane or KIVI-4)
   static constexpr int NV4 = VW / 4;
-  static constexpr int VOFF = KIVI ? off_v_kivi(D) : off_v_planes(D);
-  static constexpr int VMETA = KIVI ? off_vmeta_kivi(D) : off_vmeta_planes(D);
+  static constexpr int VOFF = KIVI ? off_v_kivi(D, GS) : off_v_planes(D, GS);
+  static constexpr int VMETA = KIVI ? off_vmeta_kivi(D, GS) : off_vmeta_planes(D, GS);
   // Token t_loc of a step is owned by lane t_loc and a weight lane's four tokens are its own
   // quad: the weights reach the weight lanes by quad broadcasts (D = 128, 2-bit codes).
   static constexpr bool QUAD_W = CPG == 4 && LPG == 32 && NE == 4;
@@ -304,10 +311,10 @@ struct Geo {
 // multiplies four codes by four limbs and the limb sums recombine exactly in one register,
 // ((l2 << 8) + l1) << 8 + l0. REFINE reads the low plane of a 4-bit cell with coefficients
 // sigma q s and the constant -3/2 sigma q . s (from the bucket midpoint to lo).
-template <int D, int MODE, bool REFINE>
+template <int D, int MODE, bool REFINE, int GS>
 struct KStep {
-  using G = Geo<D, MODE>;
-  static constexpr int CODE_OFF = REFINE ? off_klo(D) : 0;
+  using G = Geo<D, MODE, GS>;
+  static constexpr int CODE_OFF = REFINE ? off_klo(D, GS) : 0;
 
   struct Buf {
     uint4 meta, c[G::NC], l[G::DENSE ? G::NC : 1];
@@ -328,13 +335,17 @@ struct KStep {
     role(lane, gsub, blk, quad, cp);
     const int g = groups[gsub];
     const int pos0 = (lane % G::LPG) * G::CPL;
-    b.meta = ld_words<G::CPL>(r.at(2 * g + (pos0 >= D / 2), G::KMETA + 4 * (pos0 % (D / 2))));
+    // K meta of the unit's group: its D / GP positions per record over the group's GP records
+    if constexpr (G::GU == 1)
+      b.meta = ld_words<G::CPL>(r.at(2 * g + (pos0 >= D / 2), G::KMETA + 4 * (pos0 % (D / 2))));
+    else
+      b.meta = ld_words<G::CPL>(r.at(G::GP * (g / G::GU) + pos0 / (D / G::GP), G::KMETA + 4 * (pos0 % (D / G::GP))));
     const uint8_t* kp = r.at(2 * g + blk, CODE_OFF + ((cp * G::NC) * kBlock + 4 * quad) * 4);
 #pragma unroll
     for (int i = 0; i < G::NC; ++i) b.c[i] = ld_stream4(kp + i * kBlock * 4);
     if (G::DENSE) {
 #pragma unroll
-      for (int i = 0; i < G::NC; ++i) b.l[i] = ld_stream4(kp + off_klo(D) + i * kBlock * 4);
+      for (int i = 0; i < G::NC; ++i) b.l[i] = ld_stream4(kp + off_klo(D, GS) + i * kBlock * 4);
     }
   }
 
@@ -530,7 +541,7 @@ struct KStep {
     const float keep = hi ? k1 : k0, send = hi ? k0 : k1;
     const float sum = keep + dpp<0x4E>(send);   // quad_perm [2,3,0,1]
     own = G::CPG == 4 || cp < 4;
-    t_loc = gsub * kGroup + blk * kBlock + quad * 4 + (cp & 3);
+    t_loc = gsub * kUnit + blk * kBlock + quad * 4 + (cp & 3);
     return fmaf(inv, sum, cst);
   }
 };
@@ -542,9 +553,9 @@ struct KStep {
 // channels) multiply them with four tokens' codes of a channel with v_dot4_u32_u8 and
 // scale each block's exact integer sum into the fp32 accumulator. Constant terms (w z, plus
 // w s 3/2 for a high-plane-only read) go to accz on the weight lanes.
-template <int D, int MODE>
+template <int D, int MODE, int GS>
 struct VStep {
-  using G = Geo<D, MODE>;
+  using G = Geo<D, MODE, GS>;
 
   struct Buf {
     uint4 meta, c[G::NV4], l[G::DENSE ? G::NV4 : 1];
@@ -555,7 +566,7 @@ struct VStep {
     int jm = jbase + lane / (4 * G::NE);
     const int p = (lane / G::NE) % 4, e = lane % G::NE;
     jm = jm < nb ? jm : jbase;
-    if (lane < G::COOP) b.meta = ld_stream4(r.at(jm, G::VMETA + 4 * (e * kBlock + 4 * p)));
+    if (lane < G::COOP) b.meta = ld_stream4(r.at(jm, G::VMETA + 4 * ((e / G::GU) * kBlock + 4 * p)));
     int j = jbase + lane / G::LPB;
     j = j < nb ? j : jbase;
     const int chunk = lane % G::LPB;
@@ -563,7 +574,7 @@ struct VStep {
 #pragma unroll
     for (int i = 0; i < G::NV4; ++i) b.c[i] = ld_stream4(rb + 16 * i);
     if (G::DENSE) {
-      const uint8_t* rl = r.at(j, off_vlo(D) + chunk * G::VCH * 4);
+      const uint8_t* rl = r.at(j, off_vlo(D, GS) + chunk * G::VCH * 4);
 #pragma unroll
       for (int i = 0; i < G::NV4; ++i) b.l[i] = ld_stream4(rl + 16 * i);
     }
@@ -627,7 +638,7 @@ struct VStep {
     }
     wave_sync_lds();
     const int jb = lane / G::LPB, chunk = lane % G::LPB;
-    const int e_lane = chunk * G::VCH / kGroup;
+    const int e_lane = chunk * G::VCH / kUnit;
     uint32_t L[8];
     const uint4* lp = reinterpret_cast<const uint4*>(vlimb + (jb * G::NE + e_lane) * 8);
 #pragma unroll
@@ -687,25 +698,25 @@ struct VStep {
 // bits, the rest at the bucket midpoint) in the value-lane layout of the coarse step
 // (4 blocks per 64 lanes, D/16 channels per lane), constants included. Runs only when a
 // correction would cancel most of the row's weight.
-template <int D>
+template <int D, int GS>
 __device__ void exact_v_pass(const Row& r, const float* weights, const uint32_t* selm, int lane, int w,
                              float* acc) {
-  using GC = Geo<D, MODE_COARSE>;
+  using GC = Geo<D, MODE_COARSE, GS>;
   constexpr int VCH = GC::VCH;
   const int nb = r.n_q / kBlock;
-  const int jb = lane / GC::LPB, chunk = lane % GC::LPB, e = chunk * VCH / kGroup;
+  const int jb = lane / GC::LPB, chunk = lane % GC::LPB, e = chunk * VCH / kUnit / GC::GU;   // meta group
   for (int j = w * GC::BPS + jb; j < nb; j += GC::BPS * kWaves) {
     const uint8_t* rb = r.rec_ptr(j);
     uint32_t hw[VCH], lw[VCH];
 #pragma unroll
     for (int c = 0; c < VCH; ++c) {
-      hw[c] = reinterpret_cast<const uint32_t*>(rb + off_v_planes(D))[chunk * VCH + c];
-      lw[c] = reinterpret_cast<const uint32_t*>(rb + off_vlo(D))[chunk * VCH + c];
+      hw[c] = reinterpret_cast<const uint32_t*>(rb + off_v_planes(D, GS))[chunk * VCH + c];
+      lw[c] = reinterpret_cast<const uint32_t*>(rb + off_vlo(D, GS))[chunk * VCH + c];
     }
     const uint32_t bm = (selm[j >> 1] >> (16 * (j & 1))) & 0xffffu;
     for (int tt = 0; tt < kBlock; ++tt) {
       const float wt = weights[j * kBlock + tt];
-      const uint32_t mw = reinterpret_cast<const uint32_t*>(rb + off_vmeta_planes(D))[e * kBlock + tt];
+      const uint32_t mw = reinterpret_cast<const uint32_t*>(rb + off_vmeta_planes(D, GS))[e * kBlock + tt];
       const float s = f16lo(mw), z = f16hi(mw);
       const bool sel = (bm >> tt) & 1u;
       const int sh = 8 * (tt % 4) + 2 * (tt / 4);
@@ -746,11 +757,11 @@ __device__ inline void split_range(int n_chunks, int n_split, int split, int& cb
 // SKIP (with SPARSE, PH_ROW): the token-skipping ablation. The same coarse pass and
 // selection, but the values are not streamed and the unselected quantized tokens leave the
 // attention: the softmax runs over the selected tokens (at 4 bits) and the tail only.
-template <int D, int MODE, bool SPARSE, int PH, bool SKIP = false>
+template <int D, int GS, int MODE, bool SPARSE, int PH, bool SKIP = false>
 __device__ __forceinline__ void row_body(const DecodeArgs& a, const Row& r, const Smem& sm, size_t orow, int split) {
-  using G = Geo<D, MODE>;
-  using KS = KStep<D, MODE, false>;
-  using VS = VStep<D, MODE>;
+  using G = Geo<D, MODE, GS>;
+  using KS = KStep<D, MODE, false, GS>;
+  using VS = VStep<D, MODE, GS>;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   float* scr = sm.wscr + w * kWaveScratch;
   uint32_t* klimb = reinterpret_cast<uint32_t*>(scr);
@@ -810,7 +821,7 @@ __device__ __forceinline__ void row_body(const DecodeArgs& a, const Row& r, cons
     bool own;
     int t_loc;
     const float sc0 = KS::compute(sm.qperm, klimb, lane, kb, own, t_loc);
-    const bool valid = own && c * G::GPS + t_loc / kGroup < r.n_groups;
+    const bool valid = own && c * G::GPS + t_loc / kUnit < r.n_groups;
     const float sc = valid ? sc0 : -INFINITY;
     if (valid) scores[c * G::TPS + t_loc] = sc;
     if (__any(sc > st.m)) st.raise(wave_max(sc));   // a new running maximum (rare once warm)
@@ -852,7 +863,7 @@ __device__ __forceinline__ void row_body(const DecodeArgs& a, const Row& r, cons
   const bool has_tail = PH == PH_ROW || (PH == PH_PART && split == a.n_split - 1);
   float tl = 0.f;   // SKIP: the tail's weight (lane 0)
   for (int t = r.n_q + w; has_tail && t < r.N; t += kWaves) {
-    const uint16_t* kt = r.tail + (size_t)(t % kGroup) * D;
+    const uint16_t* kt = r.tail + (size_t)(t % GS) * D;
     float p = 0.f;
 #pragma unroll
     for (int i = 0; i < D / 64; ++i) p = fmaf(sm.qs[lane + 64 * i], bf16f(kt[lane + 64 * i]), p);
@@ -868,7 +879,7 @@ __device__ __forceinline__ void row_body(const DecodeArgs& a, const Row& r, cons
     if (lane == 0) st.lsum += wgt;
     if constexpr (SKIP)
       if (lane == 0) tl += wgt;
-    const uint16_t* vt = r.tail + (size_t)(kGroup + t % kGroup) * D;
+    const uint16_t* vt = r.tail + (size_t)(GS + t % GS) * D;
 #pragma unroll
     for (int i = 0; i < D / 64; ++i) tacc[i] = fmaf(wgt, bf16f(vt[lane + 64 * i]), tacc[i]);
   }
@@ -929,7 +940,7 @@ __device__ __forceinline__ void row_body(const DecodeArgs& a, const Row& r, cons
       bool pred = false;
       if (t < r.n_q) pred = scores[t] >= thr;
       const unsigned long long bal = __ballot(pred);
-      const int g0 = (base + 64 * w) / kGroup;
+      const int g0 = (base + 64 * w) / kUnit;
       if (lane == 0 && g0 < r.n_groups) selm[g0] = (uint32_t)bal;
       if (lane == 0 && g0 + 1 < r.n_groups) selm[g0 + 1] = (uint32_t)(bal >> 32);
     }
@@ -940,8 +951,8 @@ __device__ __forceinline__ void row_body(const DecodeArgs& a, const Row& r, cons
     }
     // Gather: wave w takes the 64-group spans w, w + 8, ... and corrects their selected
     // groups as many at a time as a coarse step holds (two; one at D = 256).
-    using KR = KStep<D, MODE_COARSE, true>;
-    using GC = Geo<D, MODE_COARSE>;
+    using KR = KStep<D, MODE_COARSE, true, GS>;
+    using GC = Geo<D, MODE_COARSE, GS>;
     float* wfix = scr;   // [2][64]: refined and coarse weights of the step's selected tokens
     for (int g64 = 64 * w; g64 < r.n_groups; g64 += 64 * kWaves) {
       const int gi = g64 + lane;
@@ -962,26 +973,26 @@ __device__ __forceinline__ void row_body(const DecodeArgs& a, const Row& r, cons
         const int jb = lane / GC::LPB, chunk = lane % GC::LPB;
         const int gv = groups[jb / 2];
         const uint32_t bm = gv >= 0 ? (selm[gv] >> (16 * (jb % 2))) & 0xffffu : 0u;
-        const int ev = chunk * GC::VCH / kGroup;
+        const int ev = chunk * GC::VCH / kUnit / GC::GU;   // meta group of the lane's channels
         uint4 hw4[GC::VCH / 4], lw4[GC::VCH / 4], mv4[4];
         if (bm) {
           const uint8_t* rb = r.rec_ptr(2 * gv + jb % 2);
 #pragma unroll
           for (int i = 0; i < GC::VCH / 4; ++i) {
-            hw4[i] = *reinterpret_cast<const uint4*>(rb + off_v_planes(D) + 4 * (chunk * GC::VCH + 4 * i));
-            lw4[i] = *reinterpret_cast<const uint4*>(rb + off_vlo(D) + 4 * (chunk * GC::VCH + 4 * i));
+            hw4[i] = *reinterpret_cast<const uint4*>(rb + off_v_planes(D, GS) + 4 * (chunk * GC::VCH + 4 * i));
+            lw4[i] = *reinterpret_cast<const uint4*>(rb + off_vlo(D, GS) + 4 * (chunk * GC::VCH + 4 * i));
           }
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            mv4[i] = *reinterpret_cast<const uint4*>(rb + off_vmeta_planes(D) + 4 * (ev * kBlock + 4 * i));
+            mv4[i] = *reinterpret_cast<const uint4*>(rb + off_vmeta_planes(D, GS) + 4 * (ev * kBlock + 4 * i));
         }
         bool own;
         int t_loc;
         const float delta = KR::compute(sm.qperm, klimb, lane, kb, own, t_loc);
-        const int ti = t_loc % kGroup;
-        const int g = groups[t_loc / kGroup];
+        const int ti = t_loc % kUnit;
+        const int g = groups[t_loc / kUnit];
         const bool sel = own && g >= 0 && ((selm[g < 0 ? 0 : g] >> ti) & 1u);
-        const int t = g * kGroup + ti;
+        const int t = g * kUnit + ti;
         const float s_hat = sel ? scores[t] : 0.f;
         const float s_ref = s_hat + delta;
         if (sel) scores[t] = s_ref;
@@ -1053,11 +1064,11 @@ __device__ __forceinline__ void row_body(const DecodeArgs& a, const Row& r, cons
       st.zero();
       st.m = Ms;
       st.lsum = ls;
-      exact_v_pass<D>(r, scores, selm, lane, w, st.acc);
+      exact_v_pass<D, GS>(r, scores, selm, lane, w, st.acc);
 #pragma unroll
       for (int i = 0; i < D / 64; ++i) tacc[i] = 0.f;
       for (int t = r.n_q + w; t < r.N; t += kWaves) {
-        const uint16_t* vt = r.tail + (size_t)(kGroup + t % kGroup) * D;
+        const uint16_t* vt = r.tail + (size_t)(GS + t % GS) * D;
 #pragma unroll
         for (int i = 0; i < D / 64; ++i) tacc[i] = fmaf(scores[t], bf16f(vt[lane + 64 * i]), tacc[i]);
       }
@@ -1111,7 +1122,7 @@ __device__ __forceinline__ void row_body(const DecodeArgs& a, const Row& r, cons
     float o = 0.f;
 #pragma unroll
     for (int ww = 0; ww < kWaves; ++ww) {
-      o += misc[32 + ww * NE + d / kGroup] * fws[ww];
+      o += misc[32 + ww * NE + d / kUnit] * fws[ww];
 #pragma unroll
       for (int vb = 0; vb < G::BPS; ++vb) o += red[(ww * 64 + vb * G::LPB + chunk) * VCH + c];
       o += tred[ww * D + d];
@@ -1167,7 +1178,7 @@ __host__ __device__ inline size_t decode_lds_floats(int max_len, int D) {
 // run the 2-bit path inside every planes variant.
 enum : int { VAR_KIVI = 0, VAR_DENSE = 1, VAR_COARSE = 2, VAR_SPARSE = 3, VAR_SKIP = 4 };
 
-template <int D, int VAR, int PH>
+template <int D, int GS, int VAR, int PH>
 __global__ void __launch_bounds__(kThreads, kWavesPerSimd) k_decode(DecodeArgs a) {
   extern __shared__ float smem[];
   // Rows are (cell, sequence, query head). PH_PART: workgroup (row, split), the splits of a
@@ -1220,15 +1231,15 @@ __global__ void __launch_bounds__(kThreads, kWavesPerSimd) k_decode(DecodeArgs a
   r.pool = a.ws + cell.pool_off;
   r.boff = sm.boff;
   const int slot = a.seq_slots ? a.seq_slots[b] : b;
-  r.tail = reinterpret_cast<const uint16_t*>(a.ws + cell.tail_off) + ((size_t)slot * a.n_kv_heads + kh) * tail_elems(D);
+  r.tail = reinterpret_cast<const uint16_t*>(a.ws + cell.tail_off) + ((size_t)slot * a.n_kv_heads + kh) * tail_elems(D, GS);
   r.N = N;
-  r.n_q = (N / kGroup) * kGroup;
-  r.n_groups = N / kGroup;
+  r.n_q = (N / GS) * GS;
+  r.n_groups = r.n_q / kUnit;   // 32-token units of the quantized prefix
 
   // block table row and sigma * q into LDS
   const int32_t* bt = a.block_table + (size_t)b * a.bt_stride;
   const int nbq = r.n_q / kBlock;
-  const uint32_t rec256 = (uint32_t)(record_bytes(cell.kind, D) / 256);
+  const uint32_t rec256 = (uint32_t)(record_bytes(cell.kind, D, GS) / 256);
   for (int j = tid; j < nbq; j += kThreads)
     sm.boff[j] = (record_slot(bt, j, a.bt_shift) * (uint32_t)a.n_kv_heads + (uint32_t)kh) * rec256;
   for (int d = tid; d < D; d += kThreads) {
@@ -1239,27 +1250,27 @@ __global__ void __launch_bounds__(kThreads, kWavesPerSimd) k_decode(DecodeArgs a
   __syncthreads();
 
   if constexpr (VAR == VAR_KIVI) {
-    row_body<D, MODE_KIVI, false, PH>(a, r, sm, orow, split);
+    row_body<D, GS, MODE_KIVI, false, PH>(a, r, sm, orow, split);
   } else {
-    if (cell.kind == KIND_Q2) row_body<D, MODE_Q2, false, PH>(a, r, sm, orow, split);
-    else if (VAR == VAR_DENSE) row_body<D, MODE_DENSE, false, PH>(a, r, sm, orow, split);
-    else if (VAR == VAR_COARSE) row_body<D, MODE_COARSE, false, PH>(a, r, sm, orow, split);
-    else if (VAR == VAR_SKIP) row_body<D, MODE_COARSE, true, PH, true>(a, r, sm, orow, split);
-    else row_body<D, MODE_COARSE, true, PH>(a, r, sm, orow, split);
+    if (cell.kind == KIND_Q2) row_body<D, GS, MODE_Q2, false, PH>(a, r, sm, orow, split);
+    else if (VAR == VAR_DENSE) row_body<D, GS, MODE_DENSE, false, PH>(a, r, sm, orow, split);
+    else if (VAR == VAR_COARSE) row_body<D, GS, MODE_COARSE, false, PH>(a, r, sm, orow, split);
+    else if (VAR == VAR_SKIP) row_body<D, GS, MODE_COARSE, true, PH, true>(a, r, sm, orow, split);
+    else row_body<D, GS, MODE_COARSE, true, PH>(a, r, sm, orow, split);
   }
 }
 
 size_t decode_lds_bytes(int max_len, int head_dim) { return decode_lds_floats(max_len, head_dim) * 4; }
 
-template <int D, int VAR, int PH>
+template <int D, int GS, int VAR, int PH>
 static void launch_phase(const DecodeArgs& a, size_t grid, size_t lds, hipStream_t stream) {
   static bool attr_set = false;
   if (!attr_set) {
-    (void)hipFuncSetAttribute((const void*)k_decode<D, VAR, PH>, hipFuncAttributeMaxDynamicSharedMemorySize,
+    (void)hipFuncSetAttribute((const void*)k_decode<D, GS, VAR, PH>, hipFuncAttributeMaxDynamicSharedMemorySize,
                               160 * 1024);
     attr_set = true;
   }
-  hipLaunchKernelGGL((k_decode<D, VAR, PH>), dim3((unsigned)grid), dim3(kThreads), lds, stream, a);
+  hipLaunchKernelGGL((k_decode<D, GS, VAR, PH>), dim3((unsigned)grid), dim3(kThreads), lds, stream, a);
 }
 
 // Grid of a one-workgroup-per-row launch: with grouped queries the rows of 8 KV heads form
@@ -1271,25 +1282,31 @@ static size_t row_grid(const DecodeArgs& a, size_t rows) {
   return (groups + 7) / 8 * 8 * (size_t)G;
 }
 
-template <int D, int VAR>
+template <int D, int GS, int VAR>
 static void launch_variant(const DecodeArgs& a, size_t rows, size_t lds, hipStream_t stream) {
   if constexpr (VAR == VAR_SKIP) {   // one workgroup per row only (the host refuses a split)
-    launch_phase<D, VAR, PH_ROW>(a, row_grid(a, rows), lds, stream);
+    launch_phase<D, GS, VAR, PH_ROW>(a, row_grid(a, rows), lds, stream);
   } else if (a.n_split < 1) {
-    launch_phase<D, VAR, PH_ROW>(a, row_grid(a, rows), lds, stream);
+    launch_phase<D, GS, VAR, PH_ROW>(a, row_grid(a, rows), lds, stream);
   } else {   // stream order: every partial is written before the finishing launch reads it
-    launch_phase<D, VAR, PH_PART>(a, rows * (size_t)a.n_split, lds, stream);
-    launch_phase<D, VAR, PH_FINISH>(a, rows, lds, stream);
+    launch_phase<D, GS, VAR, PH_PART>(a, rows * (size_t)a.n_split, lds, stream);
+    launch_phase<D, GS, VAR, PH_FINISH>(a, rows, lds, stream);
   }
+}
+
+template <int D, int GS>
+static void launch_dg(const DecodeArgs& a, size_t rows, size_t lds, hipStream_t stream) {
+  if (a.cells[0].kind == KIND_KIVI4) launch_variant<D, GS, VAR_KIVI>(a, rows, lds, stream);
+  else if (a.tau <= 0.f) launch_variant<D, GS, VAR_DENSE>(a, rows, lds, stream);   // everything kept
+  else if (a.skip) launch_variant<D, GS, VAR_SKIP>(a, rows, lds, stream);
+  else if (a.tau > 1.f) launch_variant<D, GS, VAR_COARSE>(a, rows, lds, stream);
+  else launch_variant<D, GS, VAR_SPARSE>(a, rows, lds, stream);
 }
 
 template <int D>
 static void launch_d(const DecodeArgs& a, size_t rows, size_t lds, hipStream_t stream) {
-  if (a.cells[0].kind == KIND_KIVI4) launch_variant<D, VAR_KIVI>(a, rows, lds, stream);
-  else if (a.tau <= 0.f) launch_variant<D, VAR_DENSE>(a, rows, lds, stream);   // everything kept
-  else if (a.skip) launch_variant<D, VAR_SKIP>(a, rows, lds, stream);
-  else if (a.tau > 1.f) launch_variant<D, VAR_COARSE>(a, rows, lds, stream);
-  else launch_variant<D, VAR_SPARSE>(a, rows, lds, stream);
+  if (a.group == 64) launch_dg<D, 64>(a, rows, lds, stream);
+  else launch_dg<D, 32>(a, rows, lds, stream);
 }
 
 hipError_t launch_decode(const DecodeArgs& a, int head_dim, hipStream_t stream) {

@@ -10,7 +10,8 @@
 
 namespace lkv {
 
-constexpr int kGroup = 32;      // tokens per K group / channels per V group
+constexpr int kGroup = 32;      // default quantization group: tokens per K group / channels per V group
+constexpr int kUnit = 32;       // tokens per decode unit and per selection-mask word
 constexpr int kBlock = 16;      // tokens per record (a page of the block table holds 1 or 2)
 constexpr int kMaxCells = 128;
 constexpr int kMaxLen = 32768;
@@ -18,22 +19,27 @@ constexpr int kMaxLen = 32768;
 // Kinds as the kernels see them (the storage a row reads).
 enum : int32_t { KIND_Q4 = 0, KIND_Q2 = 1, KIND_SHARE = 2, KIND_KIVI4 = 3 };
 
-// Byte offsets inside one record, for head dim D.
+// Byte offsets inside one record, for head dim D and quantization group GS (32 or 64).
+// K meta and V meta take 64 D / GS bytes each: a group's D K-meta words are split over its
+// GS / 16 records, and V meta is [D / GS][16 tokens].
+__host__ __device__ constexpr int meta_bytes(int D, int GS) { return 64 * D / GS; }
 __host__ __device__ constexpr int off_k(int) { return 0; }
 __host__ __device__ constexpr int off_kmeta_planes(int D) { return 4 * D; }
-__host__ __device__ constexpr int off_v_planes(int D) { return 6 * D; }
-__host__ __device__ constexpr int off_vmeta_planes(int D) { return 10 * D; }
-__host__ __device__ constexpr int off_klo(int D) { return 12 * D; }
-__host__ __device__ constexpr int off_vlo(int D) { return 16 * D; }
+__host__ __device__ constexpr int off_v_planes(int D, int GS) { return 4 * D + meta_bytes(D, GS); }
+__host__ __device__ constexpr int off_vmeta_planes(int D, int GS) { return 8 * D + meta_bytes(D, GS); }
+__host__ __device__ constexpr int off_klo(int D, int GS) { return 8 * D + 2 * meta_bytes(D, GS); }
+__host__ __device__ constexpr int off_vlo(int D, int GS) { return 12 * D + 2 * meta_bytes(D, GS); }
 __host__ __device__ constexpr int off_kmeta_kivi(int D) { return 8 * D; }
-__host__ __device__ constexpr int off_v_kivi(int D) { return 10 * D; }
-__host__ __device__ constexpr int off_vmeta_kivi(int D) { return 18 * D; }
+__host__ __device__ constexpr int off_v_kivi(int D, int GS) { return 8 * D + meta_bytes(D, GS); }
+__host__ __device__ constexpr int off_vmeta_kivi(int D, int GS) { return 16 * D + meta_bytes(D, GS); }
 
-__host__ __device__ constexpr int record_bytes(int kind, int D) {
-  return kind == KIND_Q2 ? 12 * D : 20 * D;
+// Record of one 16-token block and one KV head, padded to a multiple of 256 bytes (only
+// D = 64 with groups of 64 pads: 1152 -> 1280, 640 -> 768).
+__host__ __device__ constexpr int record_bytes(int kind, int D, int GS) {
+  return ((kind == KIND_Q2 ? 8 * D : 16 * D) + 2 * meta_bytes(D, GS) + 255) / 256 * 256;
 }
-// Tail of one (cell, slot, head): [2 (K, V)][32][D] bf16.
-__host__ __device__ constexpr int tail_elems(int D) { return 2 * kGroup * D; }
+// Tail of one (cell, slot, head): [2 (K, V)][GS][D] bf16.
+__host__ __device__ constexpr int tail_elems(int D, int GS) { return 2 * GS * D; }
 // Pool index of 16-token record j of a sequence whose block-table row is bt: pages of
 // 2^shift records are consecutive record slots, so record j sits in slot
 // (bt[j >> shift] << shift) + (j mod 2^shift).
@@ -59,6 +65,7 @@ struct AppendArgs {
   int32_t kv_bf16;
   int32_t n_seqs, n_new, n_heads, bt_stride, n_cells;
   int32_t bt_shift;     // log2(records per page): 16-token record j lives in page j >> bt_shift
+  int32_t group;        // quantization group: 32 or 64
   AppendCell cells[kMaxCells];
 };
 
@@ -82,6 +89,7 @@ struct DecodeArgs {
   int32_t n_seqs, n_heads, bt_stride, max_len, sel_words, n_cells;
   int32_t n_kv_heads;   // divides n_heads; query head h reads KV head h / (n_heads / n_kv_heads)
   int32_t bt_shift;     // log2(records per page): 16-token record j lives in page j >> bt_shift
+  int32_t group;        // quantization group: 32 or 64
   float tau, sm_scale;
   // Split of each row's tokens over n_split workgroups (n_split 0: one workgroup per row).
   // part: [rows][n_split][2 + D] floats (m, l, unnormalized o relative to m);

@@ -105,14 +105,15 @@ loopkv_status loopkv_create(const loopkv_config* cfg, loopkv_ctx** out) {
   const int kvh = cfg->n_kv_heads ? cfg->n_kv_heads : cfg->n_heads;
   if (cfg->head_dim != 64 && cfg->head_dim != 128 && cfg->head_dim != 256)
     return fail(LOOPKV_ERR_UNSUPPORTED, "head_dim %d not supported (64, 128 or 256)", cfg->head_dim);
-  if (cfg->group_size != lkv::kGroup) return fail(LOOPKV_ERR_UNSUPPORTED, "group_size must be 32");
+  if (cfg->group_size != 32 && cfg->group_size != 64)
+    return fail(LOOPKV_ERR_UNSUPPORTED, "group_size %d not supported (32 or 64)", cfg->group_size);
   if (cfg->block_tokens != 16 && cfg->block_tokens != 32)
     return fail(LOOPKV_ERR_UNSUPPORTED, "block_tokens %d not supported (16 or 32)", cfg->block_tokens);
   const uint64_t recs = (uint64_t)cfg->num_blocks * (uint64_t)(cfg->block_tokens / lkv::kBlock);
-  if (recs * (uint64_t)kvh * lkv::record_bytes(lkv::KIND_Q4, cfg->head_dim) > 0xFFFFFFFFull)
+  if (recs * (uint64_t)kvh * lkv::record_bytes(lkv::KIND_Q4, cfg->head_dim, cfg->group_size) > 0xFFFFFFFFull)
     return fail(LOOPKV_ERR_UNSUPPORTED,
                 "a cell's pool (num_blocks x block_tokens/16 x KV heads x %d-byte records) must stay below 4 GiB",
-                lkv::record_bytes(lkv::KIND_Q4, cfg->head_dim));
+                lkv::record_bytes(lkv::KIND_Q4, cfg->head_dim, cfg->group_size));
   if ((long long)cfg->n_loops * cfg->n_layers > lkv::kMaxCells)
     return fail(LOOPKV_ERR_UNSUPPORTED, "at most %d cells", lkv::kMaxCells);
   if (cfg->layout != LOOPKV_LAYOUT_PLANES && cfg->layout != LOOPKV_LAYOUT_KIVI4)
@@ -148,12 +149,12 @@ loopkv_status loopkv_plan(loopkv_ctx* c, const uint8_t* kinds) {
     if (kinds[i] == LOOPKV_CELL_SHARE) continue;
     c->pool_off[i] = off;
     off = align256(off + (size_t)c->cfg.num_blocks * (c->cfg.block_tokens / lkv::kBlock) * H *
-                             lkv::record_bytes(device_kind(c, i), D));
+                             lkv::record_bytes(device_kind(c, i), D, c->cfg.group_size));
   }
   for (int i = 0; i < n; ++i) {
     if (kinds[i] == LOOPKV_CELL_SHARE) continue;
     c->tail_off[i] = off;
-    off = align256(off + (size_t)c->cfg.max_seqs * H * lkv::tail_elems(D) * 2);
+    off = align256(off + (size_t)c->cfg.max_seqs * H * lkv::tail_elems(D, c->cfg.group_size) * 2);
   }
   for (int i = 0; i < n; ++i) {
     if (kinds[i] != LOOPKV_CELL_SHARE) continue;
@@ -196,7 +197,7 @@ loopkv_status loopkv_cell_storage(const loopkv_ctx* c, int32_t loop, int32_t lay
   const int st = c->storage[first];
   if (pool_offset) *pool_offset = c->pool_off[st];
   if (tail_offset) *tail_offset = c->tail_off[st];
-  if (record_bytes) *record_bytes = lkv::record_bytes(device_kind(c, st), c->cfg.head_dim);
+  if (record_bytes) *record_bytes = lkv::record_bytes(device_kind(c, st), c->cfg.head_dim, c->cfg.group_size);
   if (storage_cell) *storage_cell = st;
   return ok();
 }
@@ -231,6 +232,7 @@ loopkv_status loopkv_append(loopkv_ctx* c, hipStream_t stream, int32_t loop, int
   a.n_heads = c->kvh;   // the append's inputs hold the KV heads
   a.bt_stride = bt_stride;
   a.bt_shift = c->cfg.block_tokens == 32 ? 1 : 0;
+  a.group = c->cfg.group_size;
   int nc = 0;
   for (int i = first; i < first + count; ++i) {
     if (c->kinds[i] == LOOPKV_CELL_SHARE) continue;
@@ -305,6 +307,7 @@ loopkv_status decode_common(loopkv_ctx* c, hipStream_t stream, int32_t loop, int
   a.n_kv_heads = c->kvh;
   a.bt_stride = bt_stride;
   a.bt_shift = c->cfg.block_tokens == 32 ? 1 : 0;
+  a.group = c->cfg.group_size;
   a.max_len = max_len;
   a.sel_words = (max_len + 31) / 32;
   a.n_cells = count;

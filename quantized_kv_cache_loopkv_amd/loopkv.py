@@ -141,12 +141,14 @@ class Context:
     """One LoopKV cache: config, plan, caller-owned workspace."""
 
     def __init__(self, n_loops: int, n_layers: int, n_heads: int, head_dim: int, num_blocks: int,
-                 max_seqs: int, layout: int = LAYOUT_PLANES, n_kv_heads: int = 0, block_tokens: int = 16):
+                 max_seqs: int, layout: int = LAYOUT_PLANES, n_kv_heads: int = 0, block_tokens: int = 16,
+                 group_size: int = 32):
         """n_kv_heads: KV heads (0: one per query head); query head h reads KV head
         h // (n_heads // n_kv_heads). block_tokens: tokens per page of the block table (16 or
-        32); num_blocks counts pages."""
-        self.cfg = _Config(n_loops, n_layers, n_heads, head_dim, 32, block_tokens, num_blocks, max_seqs, layout,
-                           n_kv_heads)
+        32); num_blocks counts pages. group_size: quantization group (32 or 64 tokens per K
+        group and channels per V group)."""
+        self.cfg = _Config(n_loops, n_layers, n_heads, head_dim, group_size, block_tokens, num_blocks, max_seqs,
+                           layout, n_kv_heads)
         h = ctypes.c_void_p()
         _check(lib().loopkv_create(ctypes.byref(self.cfg), ctypes.byref(h)))
         self._h = h

@@ -49,6 +49,7 @@ class Config:
     plan: Optional[np.ndarray] = field(default=None, repr=False)
     n_kv_heads: int = 0           # 0: one KV head per query head
     block_tokens: int = 16        # tokens per page of the block table (16 or 32)
+    group: int = 32               # quantization group (32 or 64)
 
     @property
     def kv_heads(self) -> int:
@@ -127,12 +128,12 @@ def small_config(name: str, n_loops: int, n_layers: int, n_heads: int, head_dim:
                  lengths: List[int], taus: List[float], plan=None, seed: int = 0,
                  outlier_count: int = 0, outlier_mult: float = 1.0, cell_scales: bool = False,
                  shuffled: bool = False, q_fp32: bool = False, append_steps: int = 0,
-                 n_kv_heads: int = 0, block_tokens: int = 16) -> Config:
+                 n_kv_heads: int = 0, block_tokens: int = 16, group: int = 32) -> Config:
     """A reduced configuration with the same generators, for tests that the oracle finishes quickly."""
     cfg = Config(name, n_loops, n_layers, n_heads, head_dim, len(lengths), list(lengths), list(taus),
                  q_fp32=q_fp32, outlier_count=outlier_count, outlier_mult=outlier_mult,
                  cell_scales=cell_scales, shuffled=shuffled, append_steps=append_steps, seed=seed,
-                 n_kv_heads=n_kv_heads, block_tokens=block_tokens)
+                 n_kv_heads=n_kv_heads, block_tokens=block_tokens, group=group)
     if plan is None:
         plan = np.zeros((n_loops, n_layers), dtype=np.uint8) if n_loops * n_layers == 1 \
             else random_plan(n_loops, n_layers, seed)

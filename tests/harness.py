@@ -38,7 +38,7 @@ class Workload:
         self.plan = plan
         self.nb = R.num_blocks(cfg)
         self.ctx = lkv.Context(cfg.n_loops, cfg.n_layers, cfg.n_heads, cfg.head_dim, self.nb, cfg.batch, layout,
-                               n_kv_heads=cfg.n_kv_heads, block_tokens=cfg.block_tokens)
+                               n_kv_heads=cfg.n_kv_heads, block_tokens=cfg.block_tokens, group_size=cfg.group)
         self.ctx.plan(plan.tolist())
         self.ws = torch.empty(self.ctx.workspace_bytes(), dtype=torch.uint8, device=device)
         self.ctx.bind(self.ws)
@@ -215,13 +215,13 @@ class Workload:
         return self.ws[off:off + rb].cpu().numpy()
 
     def tail(self, cell: int, b: int, h: int) -> np.ndarray:
-        """bf16 bits [2][32][D] of the tail of (cell, slot b, head h)."""
+        """bf16 bits [2][group][D] of the tail of (cell, slot b, head h)."""
         loop, layer = self.cell_ll(cell)
         st = self.ctx.cell_storage(loop, layer)
-        D = self.cfg.head_dim
-        n = 2 * 32 * D * 2
+        D, G = self.cfg.head_dim, self.cfg.group
+        n = 2 * G * D * 2
         off = st["tail_offset"] + (b * self.cfg.kv_heads + h) * n
-        return self.ws[off:off + n].cpu().numpy().view(np.uint16).reshape(2, 32, D)
+        return self.ws[off:off + n].cpu().numpy().view(np.uint16).reshape(2, G, D)
 
 
 def kv_head(cfg: R.Config, h: int) -> int:

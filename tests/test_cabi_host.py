@@ -58,7 +58,8 @@ def _create(**kw):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(head_dim=96), B.ERR_UNSUPPORTED), (dict(head_dim=512), B.ERR_UNSUPPORTED),
-    (dict(group_size=64), B.ERR_UNSUPPORTED), (dict(block_tokens=8), B.ERR_UNSUPPORTED),
+    (dict(group_size=48), B.ERR_UNSUPPORTED), (dict(group_size=128), B.ERR_UNSUPPORTED),
+    (dict(group_size=16), B.ERR_UNSUPPORTED), (dict(block_tokens=8), B.ERR_UNSUPPORTED),
     (dict(block_tokens=64), B.ERR_UNSUPPORTED), (dict(block_tokens=0), B.ERR_UNSUPPORTED),
     # 32-token pages: 52429 x 2 x 16 x 2560 B > 2^32 - 1
     (dict(block_tokens=32, num_blocks=52429), B.ERR_UNSUPPORTED),
@@ -83,6 +84,30 @@ def test_create_accepts_pool_just_under_4gib():
     s, h = _create(num_blocks=52428, block_tokens=32)   # 52428 x 2 x 16 x 2560 B = 2^32 - 65536
     assert s == B.OK and h.value
     lkv.lib().loopkv_destroy(h)
+
+
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_groups_of_64_sizes(D):
+    """Groups of 64: records of 16 D + 2 (64 D / 64) bytes (4-bit) and 8 D + 2 D (2-bit),
+    padded to 256; tails of 64 tokens; the oracle's record sizes agree."""
+    from oracle import loopkv_oracle as O
+    plan = [0, 1, 2, 0, 0, 1]
+    a = lkv.Context(2, 3, 4, D, 10, 3, group_size=64)
+    a.plan(plan)
+    pad = lambda n: (n + 255) // 256 * 256
+    want = {0: pad(18 * D), 1: pad(10 * D)}
+    pools = 0
+    for i, k in enumerate(plan):
+        st = a.cell_storage(i // 3, i % 3)
+        kind = plan[st["storage_cell"]]
+        assert st["record_bytes"] == want[kind] == O.record_bytes(D, kind, O.LAYOUT_PLANES, 64)
+        if k != 2:
+            pools += pad(10 * 4 * want[kind])
+    tails = sum(k != 2 for k in plan) * pad(3 * 4 * 2 * 64 * D * 2)   # [max_seqs][H][K, V][64][D] bf16
+    assert a.workspace_bytes() == pools + tails
+    k = lkv.Context(2, 3, 4, D, 10, 3, layout=lkv.LAYOUT_KIVI4, group_size=64)
+    k.plan([0] * 6)
+    assert k.cell_storage(0, 0)["record_bytes"] == pad(18 * D) == O.record_bytes(D, 0, O.LAYOUT_KIVI4, 64)
 
 
 def test_pages_of_32_tokens_hold_two_records():

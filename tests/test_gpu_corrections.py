@@ -40,12 +40,12 @@ def _bf16(x):
     return torch.tensor(np.asarray(x, dtype=np.float32)).to(torch.bfloat16)
 
 
-def _decode_one(K, V, q, tau, n_split=0):
+def _decode_one(K, V, q, tau, n_split=0, group=32):
     """Append K, V ([N][D] bf16 tensors, one head) to a fresh one-cell 4-bit cache and decode q
     (n_split > 0: the split decode)."""
     N, D = K.shape
     nb = N // 16 + 2
-    ctx = lkv.Context(1, 1, 1, D, nb, 1)
+    ctx = lkv.Context(1, 1, 1, D, nb, 1, group_size=group)
     ctx.plan([lkv.CELL_Q4])
     ws = torch.zeros(ctx.workspace_bytes(), dtype=torch.uint8, device="cuda")
     ctx.bind(ws)
@@ -60,19 +60,20 @@ def _decode_one(K, V, q, tau, n_split=0):
     return out.view(D).cpu().numpy(), sm.view(-1).cpu().numpy()
 
 
-def _check(K, V, q, tau, label, n_split=0):
+def _check(K, V, q, tau, label, n_split=0, group=32):
     N, D = K.shape
-    o_gpu, sm = _decode_one(K, V, q, tau, n_split)
+    o_gpu, sm = _decode_one(K, V, q, tau, n_split, group)
     Kd, Vd = K.float().numpy().astype(np.float64), V.float().numpy().astype(np.float64)
     sig = float(np.float32(1.0 / math.sqrt(D)))
-    o_ref, sel_ref, phat = O.decode_row(np.asarray(q, np.float64), Kd, Vd, O.KIND_Q4, tau, sig)
-    n_q = 32 * (N // 32)
+    o_ref, sel_ref, phat = O.decode_row(np.asarray(q, np.float64), Kd, Vd, O.KIND_Q4, tau, sig, group=group)
+    n_q = group * (N // group)
     sel_gpu = sel_bits_from_mask(sm, n_q)
     excused = np.abs(phat[:n_q] - tau) <= TIE
     bad = (sel_gpu != sel_ref) & ~excused
     assert not bad.any(), f"{label}: selection differs at {np.flatnonzero(bad)[:10]}"
     if (sel_gpu != sel_ref).any():
-        o_ref, _, _ = O.decode_row(np.asarray(q, np.float64), Kd, Vd, O.KIND_Q4, tau, sig, sel_override=sel_gpu)
+        o_ref, _, _ = O.decode_row(np.asarray(q, np.float64), Kd, Vd, O.KIND_Q4, tau, sig, sel_override=sel_gpu,
+                                   group=group)
     err = rel_err(o_gpu, o_ref)
     assert err <= TOL, f"{label}: rel err {err:.3e}"
     return err, int(sel_ref.sum())

@@ -39,8 +39,9 @@ def check_row(wl: Workload, out, sm, q, cell, b, h, tau, n_tokens, label=""):
     _, _, K, V = oracle_row_inputs(cfg, st, b, kv_head(cfg, h), n_tokens, wl.factors)
     qv = q[cell, b, h].float().cpu().numpy().astype(np.float64)
     sig = np.float32(1.0 / math.sqrt(cfg.head_dim))
-    o_ref, sel_ref, phat = O.decode_row(qv, K, V, kind, tau, float(sig))
-    n_q = 32 * (n_tokens // 32)
+    G = cfg.group
+    o_ref, sel_ref, phat = O.decode_row(qv, K, V, kind, tau, float(sig), group=G)
+    n_q = G * (n_tokens // G)
     o_gpu = out[cell, b, h].float().cpu().numpy()
     sel_gpu = sel_bits_from_mask(sm[cell, b, h].cpu().numpy(), n_q)
     if kind == "kivi4" or (kind == O.KIND_Q4 and tau == 0.0):
@@ -52,7 +53,7 @@ def check_row(wl: Workload, out, sm, q, cell, b, h, tau, n_tokens, label=""):
         bad = (sel_gpu != sel_ref) & ~excused
         assert not bad.any(), f"{label}: selection differs at {np.flatnonzero(bad)[:10]}"
         if (sel_gpu != sel_ref).any():
-            o_ref, _, _ = O.decode_row(qv, K, V, kind, tau, float(sig), sel_override=sel_gpu)
+            o_ref, _, _ = O.decode_row(qv, K, V, kind, tau, float(sig), sel_override=sel_gpu, group=G)
     err = rel_err(o_gpu, o_ref)
     assert err <= TOL, f"{label}: rel err {err:.3e}"
     return err

@@ -1,5 +1,6 @@
 """Seeded randomized parity sweep: combinations of plan, head dim, grouped queries, lengths,
-tau, split, skip and output dtype, every row against the fp64 oracle.
+tau, split, skip, output dtype, quantization group and page size, every row against the fp64
+oracle.
 
 The targeted tests cover each feature; this sweep covers their interactions (a constant-term
 exchange that only broke at head dim 256 is the kind of mistake it is for). Each case is small
@@ -16,7 +17,7 @@ from tests.test_gpu_parity import check_row
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 24
+N_CASES = 32
 
 
 def _need_gpu():
@@ -37,8 +38,10 @@ def _case(seed):
     tau = float(rng.choice([0.0, 1e-3, 0.01, 0.05, 1.5]))
     n_split = int(rng.choice([0, 0, 2, 5]))
     bf16_out = bool(rng.integers(0, 2))
+    outliers, q_gain = int(rng.choice([0, 3])), float(rng.choice([1.0, 2.5]))
+    group, pages = int(rng.choice([32, 64])), int(rng.choice([16, 32]))
     return dict(D=D, H=H, Hkv=Hkv, plan=plan, lengths=lengths, tau=tau, n_split=n_split, bf16_out=bf16_out,
-                outliers=int(rng.choice([0, 3])), q_gain=float(rng.choice([1.0, 2.5])))
+                outliers=outliers, q_gain=q_gain, group=group, pages=pages)
 
 
 @pytest.mark.parametrize("seed", range(N_CASES))
@@ -48,7 +51,7 @@ def test_gpu_random_case(seed):
     L, NL = c["plan"].shape
     cfg = R.small_config(f"rnd{seed}", L, NL, c["H"], c["D"], c["lengths"], [c["tau"]], plan=c["plan"],
                          outlier_count=c["outliers"], outlier_mult=10.0, cell_scales=True, shuffled=bool(seed % 2),
-                         n_kv_heads=c["Hkv"], seed=seed)
+                         n_kv_heads=c["Hkv"], seed=seed, group=c["group"], block_tokens=c["pages"])
     print(f"case {seed}: {dict((k, v) for k, v in c.items() if k != 'plan')} plan={c['plan'].tolist()}", flush=True)
     wl = Workload(cfg, gpu_synth=False)
     wl.fill()

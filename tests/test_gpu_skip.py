@@ -39,8 +39,9 @@ def _check_skip_row(wl, out, sm, q, cell, b, h, tau, n_tokens, label):
     qv = q[cell, b, h].float().cpu().numpy().astype(np.float64)
     sig = float(np.float32(1.0 / math.sqrt(cfg.head_dim)))
     skip = kind == O.KIND_Q4
-    o_ref, sel_ref, phat = O.decode_row(qv, K, V, kind, tau, sig, skip=skip)
-    n_q = 32 * (n_tokens // 32)
+    G = cfg.group
+    o_ref, sel_ref, phat = O.decode_row(qv, K, V, kind, tau, sig, skip=skip, group=G)
+    n_q = G * (n_tokens // G)
     o_gpu = out[cell, b, h].float().cpu().numpy()
     sel_gpu = sel_bits_from_mask(sm[cell, b, h].cpu().numpy(), n_q)
     if kind == O.KIND_Q4 and tau > 0:
@@ -48,7 +49,7 @@ def _check_skip_row(wl, out, sm, q, cell, b, h, tau, n_tokens, label):
         bad = (sel_gpu != sel_ref) & ~excused
         assert not bad.any(), f"{label}: selection differs at {np.flatnonzero(bad)[:10]}"
         if (sel_gpu != sel_ref).any():
-            o_ref, _, _ = O.decode_row(qv, K, V, kind, tau, sig, sel_override=sel_gpu, skip=True)
+            o_ref, _, _ = O.decode_row(qv, K, V, kind, tau, sig, sel_override=sel_gpu, skip=True, group=G)
     if not np.any(o_ref):
         assert not np.any(o_gpu), f"{label}: nothing kept, output must be 0"
         return 0.0

@@ -207,7 +207,8 @@ def cpu_baseline(cfg, plan, tau, rows, log, min_seconds=10.0, max_evals=400):
 
 def serving_graph(wl, q, tau, first_step, n_rep, n_split, log, warm=2):
     """Per-(loop, layer) serving order (each cell: append the new token, decode the cell) captured
-    once in a graph and replayed; returns the mean and per-replay ms. Appends n_rep + warm tokens."""
+    once in a HIP graph by the library (loopkv_step_graph_create) and launched once per step;
+    returns the mean and per-launch ms. Appends n_rep + warm tokens."""
     import torch
     cfg = wl.cfg
     C, B, H, D = cfg.n_cells, cfg.batch, cfg.n_heads, cfg.head_dim
@@ -222,12 +223,7 @@ def serving_graph(wl, q, tau, first_step, n_rep, n_split, log, warm=2):
     if n_split:
         scratch = torch.empty(wl.ctx.split_scratch_bytes(B, max_len, n_split, cell=(0, 0)), dtype=torch.uint8,
                               device="cuda")
-    # one read-only decode first: one-time launch attributes are set outside the capture
-    wl.ctx.decode(q[0], wl.bt, la, max_len, tau, cell=(0, 0), out=out[0], n_split=n_split, scratch=scratch)
-    torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        wl.serving_step(sK, sV, q, lb, la, max_len, tau, out, n_split=n_split, scratch=scratch)
+    g = wl.ctx.step_graph(sK, sV, q, wl.bt, lb, la, max_len, tau, out, n_split=n_split, scratch=scratch)
     torch.cuda.synchronize()
     ms = []
     for k in range(warm + n_rep):
@@ -237,12 +233,12 @@ def serving_graph(wl, q, tau, first_step, n_rep, n_split, log, warm=2):
             sV.copy_(V)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        g.replay()
+        g.launch()
         e1.record(stream)
         torch.cuda.synchronize()
         if k >= warm:
             ms.append(e0.elapsed_time(e1))
-    del g
+    g.close()
     return float(sum(ms) / len(ms)), ms
 
 
@@ -399,7 +395,7 @@ def main():
             "batch": B, "context": f"{args.ctx}..{args.ctx + GS}", "ms_per_step": round(ms, 4),
             "whole_plan_ms_per_step": round(float(np.mean(step_ms)), 4),
             "ratio_to_whole_plan": round(ms / float(np.mean(step_ms)), 4),
-            "launches_per_step": 2 * n_storing + C + 2}
+            "launches_per_step": n_storing + C + 1}   # appends, decodes, the length update
         log(f"per-cell graph, batch {B}: {ms:.3f} ms per step vs whole plan {np.mean(step_ms):.3f} ms")
         # one sequence: the per-cell launches hold 16 rows each, so the split decode fills the GPU
         scfg = R.make_config("C4")

@@ -242,6 +242,41 @@ loopkv_status loopkv_plan_search(int32_t n_loops, int32_t n_layers, const loopkv
                                  uint8_t* kinds_out, double* damage_out, double* reads_out,
                                  int64_t* storage_out);
 
+/* One serving decode step in the order a looped model runs it, captured once into a HIP
+ * graph and replayed (the pages serve their fused kernel under a graph: Abstract, serving
+ * sentence). For every cell (loop, layer) in row-major order: the append of the step's token
+ * (storing cells) and the decode of that cell with its query. A reuse cell decodes over
+ * seq_lens_before (its final-loop cell runs later in the step, so that cache does not hold
+ * the step's token yet), every other cell over seq_lens_after; the step ends by adding 1 to
+ * both length arrays, so consecutive launches are consecutive decode steps.
+ *   k, v: device [cells][n_seqs][1][KV heads][D] of kv_dtype (reuse entries ignored);
+ *   q: device [cells][n_seqs][H][D] of q_dtype; out: device [cells][n_seqs][H][D] of
+ *   out_dtype; sel_mask: NULL or device [cells][n_seqs][H][ceil(max_len/32)] u32;
+ *   seq_lens_before, seq_lens_after: device [n_seqs], distinct, advanced in place;
+ *   max_len: bound on seq_lens_after over every launch the graph will make.
+ *   n_split 0: one workgroup per row; 1..LOOPKV_MAX_SPLIT: the split decode, scratch of at
+ *   least loopkv_split_scratch_bytes(ctx, 0, 0, n_seqs, max_len, n_split) bytes, shared by
+ *   the cells one after another (the graph orders them).
+ * Every pointer is fixed at creation and read at each launch: the caller refills k, v and q
+ * between launches. Capture runs on a private stream and enqueues nothing; the graph keeps
+ * the context's workspace and plan as they are at creation (rebinding the workspace or
+ * reloading the plan needs a new graph). Records no memset node. Errors: argument errors
+ * as loopkv_append / loopkv_decode_attn_split (checked before capture), LOOPKV_ERR_HIP if
+ * capture or instantiation fails; *graph is NULL on error. */
+typedef struct loopkv_step_graph loopkv_step_graph;
+loopkv_status loopkv_step_graph_create(loopkv_ctx* ctx, const void* k, const void* v, int32_t kv_dtype,
+                                       const void* q, int32_t q_dtype, int32_t n_seqs,
+                                       const int32_t* seq_slots, const int32_t* block_table,
+                                       int32_t bt_stride, int32_t* seq_lens_before,
+                                       int32_t* seq_lens_after, int32_t max_len, float tau,
+                                       float sm_scale, void* out, int32_t out_dtype,
+                                       uint32_t* sel_mask, int32_t n_split, void* scratch,
+                                       size_t scratch_bytes, loopkv_step_graph** graph);
+/* Replay the step on a stream (asynchronous, like every other call). */
+loopkv_status loopkv_step_graph_launch(loopkv_step_graph* graph, hipStream_t stream);
+/* Release a step graph (NULL is a no-op). Work already enqueued is not affected. */
+void loopkv_step_graph_destroy(loopkv_step_graph* graph);
+
 /* Thread-local description of the last error on this thread ("" after success). */
 const char* loopkv_last_error(void);
 

@@ -278,6 +278,21 @@ static void launch_d(const AppendArgs& a, hipStream_t stream) {
   else launch_dg<D, 32>(a, stream);
 }
 
+// End of a serving step: every sequence's lengths before and after the step's token advance
+// by one (the arrays are distinct).
+__global__ void __launch_bounds__(256) k_advance_lens(int32_t* before, int32_t* after, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) {
+    before[i] += 1;
+    after[i] += 1;
+  }
+}
+
+hipError_t launch_advance_lens(int32_t* before, int32_t* after, int n, hipStream_t stream) {
+  hipLaunchKernelGGL(k_advance_lens, dim3((n + 255) / 256), dim3(256), 0, stream, before, after, n);
+  return hipGetLastError();
+}
+
 // Host launcher: quantize completed groups, then update tails (same stream).
 hipError_t launch_append(const AppendArgs& a, int head_dim, hipStream_t stream) {
   if (a.n_cells == 0 || a.n_seqs == 0 || a.n_new == 0) return hipSuccess;

@@ -1263,14 +1263,50 @@ __global__ void __launch_bounds__(kThreads, kWavesPerSimd) k_decode(DecodeArgs a
 size_t decode_lds_bytes(int max_len, int head_dim) { return decode_lds_floats(max_len, head_dim) * 4; }
 
 template <int D, int GS, int VAR, int PH>
-static void launch_phase(const DecodeArgs& a, size_t grid, size_t lds, hipStream_t stream) {
+static void set_lds_attr() {
   static bool attr_set = false;
   if (!attr_set) {
     (void)hipFuncSetAttribute((const void*)k_decode<D, GS, VAR, PH>, hipFuncAttributeMaxDynamicSharedMemorySize,
                               160 * 1024);
     attr_set = true;
   }
+}
+
+template <int D, int GS, int VAR, int PH>
+static void launch_phase(const DecodeArgs& a, size_t grid, size_t lds, hipStream_t stream) {
+  set_lds_attr<D, GS, VAR, PH>();
   hipLaunchKernelGGL((k_decode<D, GS, VAR, PH>), dim3((unsigned)grid), dim3(kThreads), lds, stream, a);
+}
+
+// Sets the LDS attribute of every decode kernel of a shape, so that a graph capture that
+// follows makes no attribute call.
+template <int D, int GS>
+static void prepare_dg() {
+  set_lds_attr<D, GS, VAR_SKIP, PH_ROW>();
+  set_lds_attr<D, GS, VAR_KIVI, PH_ROW>();
+  set_lds_attr<D, GS, VAR_KIVI, PH_PART>();
+  set_lds_attr<D, GS, VAR_KIVI, PH_FINISH>();
+  set_lds_attr<D, GS, VAR_DENSE, PH_ROW>();
+  set_lds_attr<D, GS, VAR_DENSE, PH_PART>();
+  set_lds_attr<D, GS, VAR_DENSE, PH_FINISH>();
+  set_lds_attr<D, GS, VAR_COARSE, PH_ROW>();
+  set_lds_attr<D, GS, VAR_COARSE, PH_PART>();
+  set_lds_attr<D, GS, VAR_COARSE, PH_FINISH>();
+  set_lds_attr<D, GS, VAR_SPARSE, PH_ROW>();
+  set_lds_attr<D, GS, VAR_SPARSE, PH_PART>();
+  set_lds_attr<D, GS, VAR_SPARSE, PH_FINISH>();
+}
+
+template <int D>
+static void prepare_d(int group) {
+  if (group == 64) prepare_dg<D, 64>();
+  else prepare_dg<D, 32>();
+}
+
+void prepare_decode(int head_dim, int group) {
+  if (head_dim == 128) prepare_d<128>(group);
+  else if (head_dim == 256) prepare_d<256>(group);
+  else prepare_d<64>(group);
 }
 
 // Grid of a one-workgroup-per-row launch: with grouped queries the rows of 8 KV heads form

@@ -1,7 +1,8 @@
 // Host runtime of the C ABI declared in include/loopkv.h: plan validation,
-// workspace carving, argument checks and kernel launches. Nothing here touches
-// the GPU except the launches themselves, so every validation path runs (and is
-// tested) on a machine without a GPU.
+// workspace carving, argument checks, kernel launches and the capture of a serving
+// step into a HIP graph. Nothing here touches the GPU except the launches and the
+// capture, and every argument check comes first, so every validation path runs (and
+// is tested) on a machine without a GPU.
 //
 // Plan semantics follow "LoopKV: Loop-Aware KV Cache Compression for Serving
 // Looped Transformers" (arXiv:2611.04137), Abstract: a cell is 4-bit, 2-bit or
@@ -20,6 +21,8 @@
 namespace lkv {
 hipError_t launch_append(const AppendArgs& a, int head_dim, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int head_dim, hipStream_t stream);
+hipError_t launch_advance_lens(int32_t* before, int32_t* after, int n, hipStream_t stream);
+void prepare_decode(int head_dim, int group);
 size_t decode_lds_bytes(int max_len, int head_dim);
 }  // namespace lkv
 
@@ -378,6 +381,132 @@ loopkv_status loopkv_decode_attn_split(loopkv_ctx* c, hipStream_t stream, int32_
   if (n_split == 0) return fail(LOOPKV_ERR_INVALID_ARG, "n_split %d outside [1, %d]", n_split, LOOPKV_MAX_SPLIT);
   return decode_common(c, stream, loop, layer, q, q_dtype, n_seqs, seq_slots, block_table, bt_stride, seq_lens,
                        max_len, tau, sm_scale, out, out_dtype, sel_mask, n_split, scratch, scratch_bytes, false);
+}
+
+}  // extern "C"
+
+// ----------------------------------------------------------------------------- step graph
+struct loopkv_step_graph {
+  hipGraphExec_t exec = nullptr;
+};
+
+namespace {
+size_t dtype_bytes(int32_t dt) { return dt == LOOPKV_BF16 ? 2 : 4; }
+
+// Enqueue one serving step on a stream (the body of the captured graph).
+loopkv_status enqueue_step(loopkv_ctx* c, hipStream_t s, const uint8_t* k, const uint8_t* v, int32_t kv_dtype,
+                           const uint8_t* q, int32_t q_dtype, int32_t n_seqs, const int32_t* seq_slots,
+                           const int32_t* block_table, int32_t bt_stride, int32_t* before, int32_t* after,
+                           int32_t max_len, float tau, float sm_scale, uint8_t* out, int32_t out_dtype,
+                           uint32_t* sel_mask, int32_t n_split, void* scratch, size_t scratch_bytes) {
+  const int D = c->cfg.head_dim, H = c->cfg.n_heads, L = c->cfg.n_loops, NL = c->cfg.n_layers;
+  const size_t kv_cell = (size_t)n_seqs * c->kvh * D * dtype_bytes(kv_dtype);
+  const size_t q_cell = (size_t)n_seqs * H * D * dtype_bytes(q_dtype);
+  const size_t o_cell = (size_t)n_seqs * H * D * dtype_bytes(out_dtype);
+  const size_t m_cell = (size_t)n_seqs * H * ((max_len + 31) / 32);
+  for (int i = 0; i < L * NL; ++i) {
+    const int loop = i / NL, layer = i % NL;
+    const bool share = c->kinds[i] == LOOPKV_CELL_SHARE;
+    loopkv_status st;
+    if (!share) {
+      st = loopkv_append(c, s, loop, layer, k + i * kv_cell, v + i * kv_cell, kv_dtype, n_seqs, 1, seq_slots,
+                         block_table, bt_stride, before);
+      if (st != LOOPKV_OK) return st;
+    }
+    st = decode_common(c, s, loop, layer, q + i * q_cell, q_dtype, n_seqs, seq_slots, block_table, bt_stride,
+                       share ? before : after, max_len, tau, sm_scale, out + i * o_cell, out_dtype,
+                       sel_mask ? sel_mask + i * m_cell : nullptr, n_split, scratch, scratch_bytes, false);
+    if (st != LOOPKV_OK) return st;
+  }
+  hipError_t e = lkv::launch_advance_lens(before, after, n_seqs, s);
+  if (e != hipSuccess) return fail(LOOPKV_ERR_HIP, "length update launch: %s", hipGetErrorString(e));
+  return ok();
+}
+}  // namespace
+
+extern "C" {
+
+loopkv_status loopkv_step_graph_create(loopkv_ctx* c, const void* k, const void* v, int32_t kv_dtype, const void* q,
+                                       int32_t q_dtype, int32_t n_seqs, const int32_t* seq_slots,
+                                       const int32_t* block_table, int32_t bt_stride, int32_t* seq_lens_before,
+                                       int32_t* seq_lens_after, int32_t max_len, float tau, float sm_scale,
+                                       void* out, int32_t out_dtype, uint32_t* sel_mask, int32_t n_split,
+                                       void* scratch, size_t scratch_bytes, loopkv_step_graph** graph) {
+  if (!graph) return fail(LOOPKV_ERR_INVALID_ARG, "null graph pointer");
+  *graph = nullptr;
+  loopkv_status s = check_ready(c);
+  if (s != LOOPKV_OK) return s;
+  if (n_seqs < 1) return fail(LOOPKV_ERR_INVALID_ARG, "a step graph needs n_seqs >= 1");
+  if (!k || !v || !q || !out || !block_table || !seq_lens_before || !seq_lens_after)
+    return fail(LOOPKV_ERR_INVALID_ARG, "null device pointer");
+  if (seq_lens_before == seq_lens_after)
+    return fail(LOOPKV_ERR_INVALID_ARG, "seq_lens_before and seq_lens_after must be distinct arrays");
+  if (kv_dtype != LOOPKV_F32 && kv_dtype != LOOPKV_BF16) return fail(LOOPKV_ERR_INVALID_ARG, "bad kv dtype %d", kv_dtype);
+  if (q_dtype != LOOPKV_F32 && q_dtype != LOOPKV_BF16) return fail(LOOPKV_ERR_INVALID_ARG, "bad q dtype %d", q_dtype);
+  if (out_dtype != LOOPKV_F32 && out_dtype != LOOPKV_BF16)
+    return fail(LOOPKV_ERR_INVALID_ARG, "bad out dtype %d", out_dtype);
+  if (!seq_slots && n_seqs > c->cfg.max_seqs)
+    return fail(LOOPKV_ERR_CAPACITY, "n_seqs %d > max_seqs %d with identity slots", n_seqs, c->cfg.max_seqs);
+  if (max_len < 1 || max_len > LOOPKV_MAX_LEN)
+    return fail(LOOPKV_ERR_CAPACITY, "max_len %d outside [1, %d]", max_len, LOOPKV_MAX_LEN);
+  if (bt_stride < 1 || (long long)bt_stride * c->cfg.block_tokens < max_len)
+    return fail(LOOPKV_ERR_CAPACITY, "bt_stride %d too small for max_len %d", bt_stride, max_len);
+  if (!(tau >= 0.f)) return fail(LOOPKV_ERR_INVALID_ARG, "tau must be >= 0 (got %g)", (double)tau);
+  if (!(sm_scale > 0.f) || !std::isfinite(sm_scale))
+    return fail(LOOPKV_ERR_INVALID_ARG, "sm_scale must be finite and > 0 (got %g)", (double)sm_scale);
+  if (n_split != 0) {
+    if (n_split < 1 || n_split > LOOPKV_MAX_SPLIT)
+      return fail(LOOPKV_ERR_INVALID_ARG, "n_split %d outside [1, %d]", n_split, LOOPKV_MAX_SPLIT);
+    const size_t need = lkv::split_scratch_floats((size_t)n_seqs * c->cfg.n_heads, n_split, max_len,
+                                                  c->cfg.head_dim) * sizeof(float);
+    if (!scratch || ((uintptr_t)scratch & 15u) != 0 || scratch_bytes < need)
+      return fail(LOOPKV_ERR_WORKSPACE, "split scratch null, unaligned or below %zu bytes", need);
+  }
+
+  // every check passed: capture on a private stream (default priority)
+  lkv::prepare_decode(c->cfg.head_dim, c->cfg.group_size);
+  hipStream_t cap = nullptr;
+  hipError_t e = hipStreamCreateWithFlags(&cap, hipStreamNonBlocking);
+  if (e != hipSuccess) return fail(LOOPKV_ERR_HIP, "capture stream: %s", hipGetErrorString(e));
+  e = hipStreamBeginCapture(cap, hipStreamCaptureModeThreadLocal);
+  if (e != hipSuccess) {
+    (void)hipStreamDestroy(cap);
+    return fail(LOOPKV_ERR_HIP, "begin capture: %s", hipGetErrorString(e));
+  }
+  s = enqueue_step(c, cap, static_cast<const uint8_t*>(k), static_cast<const uint8_t*>(v), kv_dtype,
+                   static_cast<const uint8_t*>(q), q_dtype, n_seqs, seq_slots, block_table, bt_stride,
+                   seq_lens_before, seq_lens_after, max_len, tau, sm_scale, static_cast<uint8_t*>(out), out_dtype,
+                   sel_mask, n_split, scratch, scratch_bytes);
+  const std::string err = g_err;
+  hipGraph_t g = nullptr;
+  e = hipStreamEndCapture(cap, &g);
+  (void)hipStreamDestroy(cap);
+  if (s != LOOPKV_OK || e != hipSuccess || !g) {
+    if (g) (void)hipGraphDestroy(g);
+    if (s != LOOPKV_OK) return fail(s, "%s", err.c_str());
+    return fail(LOOPKV_ERR_HIP, "end capture: %s", hipGetErrorString(e));
+  }
+  hipGraphExec_t exec = nullptr;
+  e = hipGraphInstantiate(&exec, g, nullptr, nullptr, 0);
+  (void)hipGraphDestroy(g);
+  if (e != hipSuccess) return fail(LOOPKV_ERR_HIP, "graph instantiation: %s", hipGetErrorString(e));
+  loopkv_step_graph* out_g = new loopkv_step_graph();
+  out_g->exec = exec;
+  *graph = out_g;
+  return ok();
+}
+
+loopkv_status loopkv_step_graph_launch(loopkv_step_graph* graph, hipStream_t stream) {
+  if (!graph || !graph->exec) return fail(LOOPKV_ERR_INVALID_ARG, "null step graph");
+  hipError_t e = hipGraphLaunch(graph->exec, stream);
+  if (e != hipSuccess) return fail(LOOPKV_ERR_HIP, "graph launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+void loopkv_step_graph_destroy(loopkv_step_graph* graph) {
+  if (!graph) return;
+  if (graph->exec) (void)hipGraphExecDestroy(graph->exec);
+  delete graph;
 }
 
 }  // extern "C"

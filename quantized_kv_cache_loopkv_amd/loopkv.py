@@ -28,7 +28,7 @@ MAX_SPLIT = 64
 EXPORTED = ["loopkv_create", "loopkv_destroy", "loopkv_plan", "loopkv_workspace_bytes",
             "loopkv_bind_workspace", "loopkv_cell_storage", "loopkv_append", "loopkv_decode_attn",
             "loopkv_split_scratch_bytes", "loopkv_decode_attn_split", "loopkv_decode_attn_skip", "loopkv_plan_search",
-            "loopkv_last_error"]
+            "loopkv_step_graph_create", "loopkv_step_graph_launch", "loopkv_step_graph_destroy", "loopkv_last_error"]
 
 
 class LoopKVError(RuntimeError):
@@ -77,11 +77,17 @@ def lib():
     L.loopkv_plan_search.argtypes = [i32, i32, ctypes.POINTER(_CellCost), ctypes.c_double, ctypes.c_int64,
                                      ctypes.POINTER(ctypes.c_uint8), ctypes.POINTER(ctypes.c_double),
                                      ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
+    L.loopkv_step_graph_create.argtypes = [vp, vp, vp, i32, vp, i32, i32, vp, vp, i32, vp, vp, i32, f32, f32, vp, i32,
+                                           vp, i32, vp, ctypes.c_size_t, ctypes.POINTER(vp)]
+    L.loopkv_step_graph_launch.argtypes = [vp, vp]
+    L.loopkv_step_graph_destroy.argtypes = [vp]
+    L.loopkv_step_graph_destroy.restype = None
     L.loopkv_last_error.restype = ctypes.c_char_p
     L.loopkv_last_error.argtypes = []
     for name in ["loopkv_create", "loopkv_plan", "loopkv_workspace_bytes", "loopkv_bind_workspace",
                  "loopkv_cell_storage", "loopkv_append", "loopkv_decode_attn", "loopkv_split_scratch_bytes",
-                 "loopkv_decode_attn_split", "loopkv_decode_attn_skip", "loopkv_plan_search"]:
+                 "loopkv_decode_attn_split", "loopkv_decode_attn_skip", "loopkv_plan_search",
+                 "loopkv_step_graph_create", "loopkv_step_graph_launch"]:
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -230,6 +236,13 @@ class Context:
                                                 ctypes.byref(n)))
         return n.value
 
+    def step_graph(self, k, v, q, block_table, lens_before, lens_after, max_len: int, tau: float, out,
+                   sel_mask=None, n_split: int = 0, scratch=None, sm_scale=None, seq_slots=None) -> "StepGraph":
+        """Capture one serving step of every cell (loopkv_step_graph_create): k, v [cells][B][1][KV
+        heads][D]; q, out [cells][B][H][D]; lens_before / lens_after advance by one per launch."""
+        return StepGraph(self, k, v, q, block_table, lens_before, lens_after, max_len, tau, out, sel_mask, n_split,
+                         scratch, sm_scale, seq_slots)
+
     def decode(self, q: torch.Tensor, block_table: torch.Tensor, seq_lens: torch.Tensor, max_len: int,
                tau: float, sm_scale: Optional[float] = None, cell=None, out_dtype=torch.float32,
                out: Optional[torch.Tensor] = None, sel_mask=False, seq_slots: Optional[torch.Tensor] = None,
@@ -286,3 +299,48 @@ class Context:
         if sm is not None:
             return out, sm
         return out
+
+
+class StepGraph:
+    """One serving step (every cell in order: append the token, decode the cell; then both
+    length arrays advance by one) captured into a HIP graph by loopkv_step_graph_create.
+    Holds the tensors it was built on; refill k, v and q between launches."""
+
+    def __init__(self, ctx: "Context", k, v, q, block_table, lens_before, lens_after, max_len: int, tau: float,
+                 out, sel_mask=None, n_split: int = 0, scratch=None, sm_scale=None, seq_slots=None):
+        n_seqs = q.shape[1]
+        if sm_scale is None:
+            sm_scale = 1.0 / math.sqrt(ctx.cfg.head_dim)
+        for name, t in (("k", k), ("v", v), ("q", q), ("out", out)):
+            if not t.is_cuda or not t.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous CUDA tensor")
+        if n_split and scratch is None:
+            scratch = torch.empty(ctx.split_scratch_bytes(n_seqs, max_len, n_split, (0, 0)), dtype=torch.uint8,
+                                  device=q.device)
+        bt = _dev_i32(block_table, "block_table", n_seqs)
+        _dev_i32(lens_before, "lens_before", n_seqs)
+        _dev_i32(lens_after, "lens_after", n_seqs)
+        _dev_i32(seq_slots, "seq_slots", n_seqs)
+        self._keep = (ctx, k, v, q, bt, lens_before, lens_after, out, sel_mask, scratch, seq_slots)
+        h = ctypes.c_void_p()
+        nbytes = 0 if scratch is None else scratch.numel() * scratch.element_size()
+        _check(lib().loopkv_step_graph_create(ctx._h, _ptr(k), _ptr(v), _dtype_code(k), _ptr(q), _dtype_code(q),
+                                              n_seqs, _ptr(seq_slots), _ptr(bt),
+                                              bt.shape[-1] if bt.dim() == 2 else bt.numel(), _ptr(lens_before),
+                                              _ptr(lens_after), int(max_len), float(tau), float(sm_scale), _ptr(out),
+                                              _dtype_code(out), _ptr(sel_mask), int(n_split), _ptr(scratch), nbytes,
+                                              ctypes.byref(h)))
+        self._h = h
+
+    def launch(self):
+        _check(lib().loopkv_step_graph_launch(self._h, _stream()))
+
+    def close(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value and _lib is not None:
+            _lib.loopkv_step_graph_destroy(h)
+        self._h = None
+
+    def __del__(self):
+        self.close()
+

@@ -341,3 +341,49 @@ def test_grouped_query_workspace_and_shapes():
     lkv.lib().loopkv_destroy(h)
     s, h = _create(num_blocks=104857 * 4)                 # the same blocks with 16 KV heads do not
     assert s == B.ERR_UNSUPPORTED
+
+
+def _step_graph(ctx, **kw):
+    a = dict(k=FAKE_DEV, v=FAKE_DEV, kv_dt=1, q=FAKE_DEV, q_dt=1, n_seqs=2, slots=None, bt=FAKE_DEV, bt_stride=4,
+             before=FAKE_DEV, after=FAKE_DEV + 256, max_len=64, tau=0.01, sm=0.125, out=FAKE_DEV, out_dt=0,
+             mask=None, n_split=0, scratch=None, scratch_bytes=0, graph=True)
+    a.update(kw)
+    vp = ctypes.c_void_p
+    g = vp()
+    st = lkv.lib().loopkv_step_graph_create(
+        ctx._h if ctx is not None else None, vp(a["k"]), vp(a["v"]), a["kv_dt"], vp(a["q"]), a["q_dt"], a["n_seqs"],
+        vp(a["slots"]), vp(a["bt"]), a["bt_stride"], vp(a["before"]), vp(a["after"]), a["max_len"],
+        ctypes.c_float(a["tau"]), ctypes.c_float(a["sm"]), vp(a["out"]), a["out_dt"], vp(a["mask"]), a["n_split"],
+        vp(a["scratch"]), a["scratch_bytes"], ctypes.byref(g) if a["graph"] else None)
+    return st, g
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(graph=False), B.ERR_INVALID_ARG), (dict(n_seqs=0), B.ERR_INVALID_ARG), (dict(k=0), B.ERR_INVALID_ARG),
+    (dict(q=0), B.ERR_INVALID_ARG), (dict(out=0), B.ERR_INVALID_ARG), (dict(bt=0), B.ERR_INVALID_ARG),
+    (dict(before=0), B.ERR_INVALID_ARG), (dict(after=FAKE_DEV), B.ERR_INVALID_ARG),   # before == after
+    (dict(kv_dt=2), B.ERR_INVALID_ARG), (dict(q_dt=7), B.ERR_INVALID_ARG), (dict(out_dt=-1), B.ERR_INVALID_ARG),
+    (dict(n_seqs=3), B.ERR_CAPACITY), (dict(max_len=0), B.ERR_CAPACITY), (dict(max_len=65), B.ERR_CAPACITY),
+    (dict(tau=-1.0), B.ERR_INVALID_ARG), (dict(sm=0.0), B.ERR_INVALID_ARG), (dict(n_split=65), B.ERR_INVALID_ARG),
+    (dict(n_split=2), B.ERR_WORKSPACE), (dict(n_split=2, scratch=FAKE_DEV, scratch_bytes=16), B.ERR_WORKSPACE),
+    (dict(n_split=2, scratch=FAKE_DEV + 8, scratch_bytes=1 << 30), B.ERR_WORKSPACE),
+])
+def test_step_graph_validation(kw, status):
+    """Every argument check of the step graph runs before any capture (no GPU needed)."""
+    st, g = _step_graph(_ready_ctx(), **kw)
+    assert st == status and not g.value
+    assert lkv.lib().loopkv_last_error().decode()
+
+
+def test_step_graph_unready_and_null_handles():
+    L = lkv.lib()
+    st, g = _step_graph(None)
+    assert st == B.ERR_INVALID_ARG and not g.value
+    ctx = lkv.Context(2, 3, 2, 64, 16, 2)
+    st, g = _step_graph(ctx)
+    assert st == B.ERR_PLAN and not g.value
+    ctx.plan([0, 1, 2, 0, 0, 1])
+    st, g = _step_graph(ctx)
+    assert st == B.ERR_WORKSPACE and not g.value
+    assert L.loopkv_step_graph_launch(None, None) == B.ERR_INVALID_ARG
+    L.loopkv_step_graph_destroy(None)

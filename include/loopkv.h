@@ -56,6 +56,10 @@
  * (tokens block_tokens*p .. block_tokens*(p+1)-1) of sequence b; the same id addresses
  * every cell's pool. A page of 16 tokens is one record slot; a page of 32 tokens is the
  * two consecutive slots 2*id and 2*id+1, holding its first and second 16 tokens.
+ * The kernels check page ids against the pool: a decode row whose quantized prefix maps a
+ * page outside [0, num_blocks) (an unmapped -1 included) gets NaN output and an empty
+ * selection instead of reading it; an append does not write a record whose page is out of
+ * range or lies beyond the row's bt_stride entries.
  *
  * Ownership: the caller owns every device buffer (workspace, q, k, v, out,
  * tables, masks). The library never allocates device memory and never

@@ -191,7 +191,10 @@ __global__ void __launch_bounds__(256) k_quantize_groups(AppendArgs a) {
   const int rec = record_bytes(cell.kind, D, GS);
   for (int part = 0; part < P; ++part) {
     const int j = P * g + part;
-    const uint32_t phys = record_slot(a.block_table + (size_t)b * a.bt_stride, j, a.bt_shift);
+    const int32_t* bt = a.block_table + (size_t)b * a.bt_stride;
+    if ((j >> a.bt_shift) >= a.bt_stride || (uint32_t)bt[j >> a.bt_shift] >= (uint32_t)a.num_pages)
+      continue;   // page not mapped (uniform over the workgroup): the record is not written
+    const uint32_t phys = record_slot(bt, j, a.bt_shift);
     uint32_t* r = reinterpret_cast<uint32_t*>(a.ws + cell.pool_off + ((size_t)phys * a.n_heads + h) * rec);
     const int t0 = part * kBlock;
     if (cell.kind == KIND_KIVI4) {

@@ -1215,15 +1215,20 @@ __global__ void __launch_bounds__(kThreads, kWavesPerSimd) k_decode(DecodeArgs a
   sm.wscr = sm.qperm + D;
   sm.misc = sm.wscr + kWaves * kWaveScratch;
 
-  if (N <= 0 || N > a.max_len) {
+  // rows that read nothing: empty (output 0) or invalid (NaN; length above max_len, or a
+  // page of the quantized prefix outside the pool)
+  auto empty_row = [&](bool zero) {
     if (PH == PH_PART) return;   // the finishing launch writes the row
-    const float v = N == 0 ? 0.f : __builtin_nanf("");
+    const float v = zero ? 0.f : __builtin_nanf("");
     for (int d = tid; d < D; d += kThreads) {
-      if (a.out_bf16) reinterpret_cast<uint16_t*>(a.out)[orow * D + d] = N == 0 ? 0 : 0x7fc0;
+      if (a.out_bf16) reinterpret_cast<uint16_t*>(a.out)[orow * D + d] = zero ? 0 : 0x7fc0;
       else reinterpret_cast<float*>(a.out)[orow * D + d] = v;
     }
     if (a.sel_mask)
       for (int g = tid; g < a.sel_words; g += kThreads) a.sel_mask[orow * (size_t)a.sel_words + g] = 0u;
+  };
+  if (N <= 0 || N > a.max_len) {
+    empty_row(N == 0);
     return;
   }
 
@@ -1240,14 +1245,28 @@ __global__ void __launch_bounds__(kThreads, kWavesPerSimd) k_decode(DecodeArgs a
   const int32_t* bt = a.block_table + (size_t)b * a.bt_stride;
   const int nbq = r.n_q / kBlock;
   const uint32_t rec256 = (uint32_t)(record_bytes(cell.kind, D, GS) / 256);
-  for (int j = tid; j < nbq; j += kThreads)
+  int bad_page = 0;
+  for (int j = tid; j < nbq; j += kThreads) {
+    bad_page |= (uint32_t)bt[j >> a.bt_shift] >= (uint32_t)a.num_pages;   // -1 (unmapped) included
     sm.boff[j] = (record_slot(bt, j, a.bt_shift) * (uint32_t)a.n_kv_heads + (uint32_t)kh) * rec256;
+  }
   for (int d = tid; d < D; d += kThreads) {
     const size_t qi = orow * D + d;
     const float qv = a.q_bf16 ? bf16f(reinterpret_cast<const uint16_t*>(a.q)[qi]) : reinterpret_cast<const float*>(a.q)[qi];
     sm.qs[d] = a.sm_scale * qv;
   }
+  // OR of the page check over the workgroup: one flag per wave in the exchange words (written
+  // again only after the row body's first barrier)
+  const bool wave_bad = __any(bad_page);   // every lane of the wave votes
+  if ((tid & 63) == 0) sm.misc[tid >> 6] = wave_bad ? 1.f : 0.f;
   __syncthreads();
+  bool any_bad = false;
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) any_bad |= sm.misc[i] != 0.f;
+  if (any_bad) {   // no record of this row is read
+    empty_row(false);
+    return;
+  }
 
   if constexpr (VAR == VAR_KIVI) {
     row_body<D, GS, MODE_KIVI, false, PH>(a, r, sm, orow, split);

@@ -66,6 +66,8 @@ struct AppendArgs {
   int32_t n_seqs, n_new, n_heads, bt_stride, n_cells;
   int32_t bt_shift;     // log2(records per page): 16-token record j lives in page j >> bt_shift
   int32_t group;        // quantization group: 32 or 64
+  int32_t num_pages;    // pages per pool: records whose page lies outside [0, num_pages), or
+                        // beyond the bt_stride entries of the row, are not written
   AppendCell cells[kMaxCells];
 };
 
@@ -90,6 +92,7 @@ struct DecodeArgs {
   int32_t n_kv_heads;   // divides n_heads; query head h reads KV head h / (n_heads / n_kv_heads)
   int32_t bt_shift;     // log2(records per page): 16-token record j lives in page j >> bt_shift
   int32_t group;        // quantization group: 32 or 64
+  int32_t num_pages;    // pages per pool: a row reading a page outside [0, num_pages) gets NaN
   float tau, sm_scale;
   // Split of each row's tokens over n_split workgroups (n_split 0: one workgroup per row).
   // part: [rows][n_split][2 + D] floats (m, l, unnormalized o relative to m);

@@ -101,3 +101,54 @@ def test_gpu_pages_of_32_serving_appends():
         torch.cuda.synchronize()
         assert torch.equal(res[0][0], res[1][0]) and torch.equal(res[0][1], res[1][1]), f"step {s}"
     _same_storage(w16, w32, [n + STEPS for n in LENGTHS])
+
+
+def test_gpu_out_of_range_pages():
+    """Page ids outside the pool: a row whose quantized prefix maps one gets NaN output and an
+    empty selection (no record read), rows whose prefix is mapped are untouched, and an append
+    skips the records of unmapped pages while writing the rest."""
+    _need_gpu()
+    import math
+    from oracle import loopkv_oracle as O
+    from tests.harness import oracle_row_inputs
+    lengths = [300, 500, 40]
+    cfg = R.small_config("badpages", 1, 1, 2, 128, lengths, [0.01], outlier_count=2, outlier_mult=8.0, shuffled=True)
+    wl = Workload(cfg, gpu_synth=False)
+    wl.fill()
+    q = wl.q_all()
+    bad = wl.bt.clone()
+    bad[0, 3] = -1          # inside sequence 0's quantized prefix (pages 0..17)
+    bad[1, 5] = wl.nb       # one past the pool, inside sequence 1's prefix
+    bad[2, 5] = -1          # past sequence 2's prefix (pages 0..1): never read
+    for n_split, skip in ((0, False), (3, False), (0, True)):
+        good = wl.ctx.decode(q, wl.bt, wl.seq_lens, wl.max_len(), 0.01, sel_mask=True, n_split=n_split, skip=skip)
+        got = wl.ctx.decode(q, bad, wl.seq_lens, wl.max_len(), 0.01, sel_mask=True, n_split=n_split, skip=skip)
+        torch.cuda.synchronize()
+        label = f"split={n_split} skip={skip}"
+        assert torch.isnan(got[0][0, :2]).all(), label
+        assert not got[1][0, :2].any(), label
+        assert torch.equal(got[0][0, 2], good[0][0, 2]) and torch.equal(got[1][0, 2], good[1][0, 2]), label
+        assert not torch.isnan(good[0]).any(), label
+
+    # append through a table whose page for tokens 32..47 of sequence 1 is unmapped
+    ctx = wl.ctx.__class__(1, 1, 2, 128, wl.nb, 3)
+    ctx.plan([0])
+    ws = torch.zeros(ctx.workspace_bytes(), dtype=torch.uint8, device="cuda")
+    ctx.bind(ws)
+    holes = wl.bt.clone()
+    holes[1, 2] = -1
+    holes[1, 3] = 1 << 30
+    K, V = wl.kv_chunk(0, 0, 64, seqs=[1])
+    lens = torch.zeros(1, dtype=torch.int32, device="cuda")
+    slots = torch.tensor([1], dtype=torch.int32, device="cuda")
+    ctx.append(K[:, :64].contiguous(), V[:, :64].contiguous(), holes[1:2].contiguous(), lens, cell=(0, 0),
+               seq_slots=slots)
+    torch.cuda.synchronize()
+    st = ctx.cell_storage(0, 0)
+    _, _, Kd, Vd = oracle_row_inputs(cfg, 0, 1, 0, 64, wl.factors)
+    qh = O.quantize_history(Kd, Vd, 4)
+    for j in (0, 1):   # the mapped pages hold group 0
+        slot = int(holes[1, j])
+        off = st["pool_offset"] + slot * 2 * st["record_bytes"]
+        assert np.array_equal(ws[off:off + st["record_bytes"]].cpu().numpy(), O.pack_block(qh, j))
+    assert math.isfinite(float(ws.float().sum()))

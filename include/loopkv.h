@@ -59,7 +59,9 @@
  * The kernels check page ids against the pool: a decode row whose quantized prefix maps a
  * page outside [0, num_blocks) (an unmapped -1 included) gets NaN output and an empty
  * selection instead of reading it; an append does not write a record whose page is out of
- * range or lies beyond the row's bt_stride entries.
+ * range or lies beyond the row's bt_stride entries. Likewise a seq_slots entry outside
+ * [0, max_seqs) gives a decode row NaN and makes an append skip that sequence, as does a
+ * negative length in an append.
  *
  * Ownership: the caller owns every device buffer (workspace, q, k, v, out,
  * tables, masks). The library never allocates device memory and never

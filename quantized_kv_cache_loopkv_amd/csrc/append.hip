@@ -106,6 +106,7 @@ __device__ void write_tail_tokens(const AppendArgs& a, const AppendCell& cell, i
   const int cnt = end - first;
   if (cnt <= 0) return;
   const int slot = a.seq_slots ? a.seq_slots[b] : b;
+  if (L0 < 0 || (uint32_t)slot >= (uint32_t)a.max_seqs) return;   // invalid sequence: nothing written
   uint16_t* tail = reinterpret_cast<uint16_t*>(a.ws + cell.tail_off) + ((size_t)slot * a.n_heads + h) * tail_elems(D, GS);
   for (int idx = threadIdx.x; idx < cnt * D; idx += blockDim.x) {
     const int i = idx / D, d = idx % D;
@@ -136,6 +137,7 @@ __global__ void __launch_bounds__(256) k_quantize_groups(AppendArgs a) {
   const bool complete = (g + 1) * GS <= L0 + a.n_new;   // uniform over the workgroup
   if (!WITH_TAIL && !complete) return;
   const int slot = a.seq_slots ? a.seq_slots[b] : b;
+  if (L0 < 0 || (uint32_t)slot >= (uint32_t)a.max_seqs) return;   // invalid sequence (uniform): nothing written
   const int tid = threadIdx.x;
   constexpr int P = GS / kBlock;   // records per group
 

@@ -1236,6 +1236,10 @@ __global__ void __launch_bounds__(kThreads, kWavesPerSimd) k_decode(DecodeArgs a
   r.pool = a.ws + cell.pool_off;
   r.boff = sm.boff;
   const int slot = a.seq_slots ? a.seq_slots[b] : b;
+  if ((uint32_t)slot >= (uint32_t)a.max_seqs) {   // no tail of this row exists
+    empty_row(false);
+    return;
+  }
   r.tail = reinterpret_cast<const uint16_t*>(a.ws + cell.tail_off) + ((size_t)slot * a.n_kv_heads + kh) * tail_elems(D, GS);
   r.N = N;
   r.n_q = (N / GS) * GS;

@@ -68,6 +68,8 @@ struct AppendArgs {
   int32_t group;        // quantization group: 32 or 64
   int32_t num_pages;    // pages per pool: records whose page lies outside [0, num_pages), or
                         // beyond the bt_stride entries of the row, are not written
+  int32_t max_seqs;     // tail slots: a sequence whose slot lies outside [0, max_seqs), or whose
+                        // length is negative, is not appended to
   AppendCell cells[kMaxCells];
 };
 
@@ -93,6 +95,7 @@ struct DecodeArgs {
   int32_t bt_shift;     // log2(records per page): 16-token record j lives in page j >> bt_shift
   int32_t group;        // quantization group: 32 or 64
   int32_t num_pages;    // pages per pool: a row reading a page outside [0, num_pages) gets NaN
+  int32_t max_seqs;     // tail slots: a row whose slot lies outside [0, max_seqs) gets NaN
   float tau, sm_scale;
   // Split of each row's tokens over n_split workgroups (n_split 0: one workgroup per row).
   // part: [rows][n_split][2 + D] floats (m, l, unnormalized o relative to m);

@@ -237,6 +237,7 @@ loopkv_status loopkv_append(loopkv_ctx* c, hipStream_t stream, int32_t loop, int
   a.bt_shift = c->cfg.block_tokens == 32 ? 1 : 0;
   a.group = c->cfg.group_size;
   a.num_pages = c->cfg.num_blocks;
+  a.max_seqs = c->cfg.max_seqs;
   int nc = 0;
   for (int i = first; i < first + count; ++i) {
     if (c->kinds[i] == LOOPKV_CELL_SHARE) continue;
@@ -313,6 +314,7 @@ loopkv_status decode_common(loopkv_ctx* c, hipStream_t stream, int32_t loop, int
   a.bt_shift = c->cfg.block_tokens == 32 ? 1 : 0;
   a.group = c->cfg.group_size;
   a.num_pages = c->cfg.num_blocks;
+  a.max_seqs = c->cfg.max_seqs;
   a.max_len = max_len;
   a.sel_words = (max_len + 31) / 32;
   a.n_cells = count;

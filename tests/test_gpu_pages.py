@@ -152,3 +152,36 @@ def test_gpu_out_of_range_pages():
         off = st["pool_offset"] + slot * 2 * st["record_bytes"]
         assert np.array_equal(ws[off:off + st["record_bytes"]].cpu().numpy(), O.pack_block(qh, j))
     assert math.isfinite(float(ws.float().sum()))
+
+
+def test_gpu_out_of_range_slots_and_lengths():
+    """A seq_slots entry outside [0, max_seqs) gives its decode rows NaN (other rows untouched)
+    and makes an append skip that sequence, as does a negative length in an append."""
+    _need_gpu()
+    import quantized_kv_cache_loopkv_amd as lkv
+    lengths = [300, 77, 40]
+    cfg = R.small_config("badslots", 1, 1, 2, 64, lengths, [0.01], shuffled=True)
+    wl = Workload(cfg, gpu_synth=False)
+    wl.fill()
+    q = wl.q_all()
+    slots = torch.tensor([0, 99, 2], dtype=torch.int32, device="cuda")
+    good = wl.ctx.decode(q, wl.bt, wl.seq_lens, wl.max_len(), 0.01, sel_mask=True)
+    got = wl.ctx.decode(q, wl.bt, wl.seq_lens, wl.max_len(), 0.01, sel_mask=True, seq_slots=slots)
+    torch.cuda.synchronize()
+    assert torch.isnan(got[0][0, 1]).all() and not got[1][0, 1].any()
+    for b in (0, 2):
+        assert torch.equal(got[0][0, b], good[0][0, b]) and torch.equal(got[1][0, b], good[1][0, b])
+
+    ctx = lkv.Context(1, 1, 2, 64, wl.nb, 3)
+    ctx.plan([0])
+    ws = torch.zeros(ctx.workspace_bytes(), dtype=torch.uint8, device="cuda")
+    ctx.bind(ws)
+    K, V = wl.kv_chunk(0, 0, 40, seqs=[0])
+    for n in (1, 40):   # the one-kernel append and the prefill path
+        ctx.append(K[:, :n].contiguous(), V[:, :n].contiguous(), wl.bt[0:1].contiguous(),
+                   torch.zeros(1, dtype=torch.int32, device="cuda"), cell=(0, 0),
+                   seq_slots=torch.tensor([3], dtype=torch.int32, device="cuda"))
+        ctx.append(K[:, :n].contiguous(), V[:, :n].contiguous(), wl.bt[0:1].contiguous(),
+                   torch.full((1,), -5, dtype=torch.int32, device="cuda"), cell=(0, 0))
+    torch.cuda.synchronize()
+    assert not ws.any(), "an invalid sequence must not be written"

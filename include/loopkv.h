@@ -89,7 +89,8 @@ typedef enum {
   LOOPKV_ERR_PLAN = 2,        /* no plan loaded, kind > 2, reuse cell in the final loop, bad cell index */
   LOOPKV_ERR_WORKSPACE = 3,   /* workspace not bound, too small, or not 256-byte aligned */
   LOOPKV_ERR_CAPACITY = 4,    /* bt_stride * block_tokens < max_len, max_len above the supported maximum */
-  LOOPKV_ERR_UNSUPPORTED = 5, /* head_dim not 64/128/256, group not 32/64, block not 16/32, too many cells */
+  LOOPKV_ERR_UNSUPPORTED = 5, /* head_dim not 64/128/256, group not 32/64, block not 16/32, too many
+                                 cells; at the first launch on a device: the device is not gfx950 */
   LOOPKV_ERR_HIP = 6          /* HIP runtime / launch failure */
 } loopkv_status;
 

@@ -8,6 +8,7 @@
 // Looped Transformers" (arXiv:2611.04137), Abstract: a cell is 4-bit, 2-bit or
 // a reuse of the final loop's KV of its layer.
 #include <hip/hip_runtime.h>
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -78,6 +79,24 @@ loopkv_status resolve_cells(const loopkv_ctx* c, int loop, int layer, int* first
                 c->cfg.n_loops, c->cfg.n_layers);
   *first = loop * c->cfg.n_layers + layer;
   *count = 1;
+  return LOOPKV_OK;
+}
+
+// The kernels are built for gfx950 only: the current device is checked once (per device id)
+// before the first launch on it.
+loopkv_status check_device() {
+  static std::atomic<int> state[64];   // 0 unknown, 1 gfx950, -1 another device
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(LOOPKV_ERR_HIP, "no current HIP device: %s", hipGetErrorString(e));
+  if (dev >= 0 && dev < 64 && state[dev].load(std::memory_order_relaxed) == 1) return LOOPKV_OK;
+  hipDeviceProp_t prop;
+  e = hipGetDeviceProperties(&prop, dev);
+  if (e != hipSuccess) return fail(LOOPKV_ERR_HIP, "device properties: %s", hipGetErrorString(e));
+  const bool ok950 = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev >= 0 && dev < 64) state[dev].store(ok950 ? 1 : -1, std::memory_order_relaxed);
+  if (!ok950) return fail(LOOPKV_ERR_UNSUPPORTED, "device %d is %s; the kernels are built for gfx950", dev,
+                          prop.gcnArchName);
   return LOOPKV_OK;
 }
 
@@ -249,6 +268,8 @@ loopkv_status loopkv_append(loopkv_ctx* c, hipStream_t stream, int32_t loop, int
   }
   a.n_cells = nc;
   if (nc == 0) return ok();
+  s = check_device();
+  if (s != LOOPKV_OK) return s;
   hipError_t e = lkv::launch_append(a, c->cfg.head_dim, stream);
   if (e != hipSuccess) return fail(LOOPKV_ERR_HIP, "append launch: %s", hipGetErrorString(e));
   return ok();
@@ -334,6 +355,8 @@ loopkv_status decode_common(loopkv_ctx* c, hipStream_t stream, int32_t loop, int
     a.cells[i].tail_off = c->tail_off[st];
     a.cells[i].kind = device_kind(c, st);
   }
+  s = check_device();
+  if (s != LOOPKV_OK) return s;
   hipError_t e = lkv::launch_decode(a, c->cfg.head_dim, stream);
   if (e != hipSuccess) return fail(LOOPKV_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
   return ok();
@@ -468,6 +491,8 @@ loopkv_status loopkv_step_graph_create(loopkv_ctx* c, const void* k, const void*
   }
 
   // every check passed: capture on a private stream (default priority)
+  s = check_device();   // before the capture: no property query inside it
+  if (s != LOOPKV_OK) return s;
   lkv::prepare_decode(c->cfg.head_dim, c->cfg.group_size);
   hipStream_t cap = nullptr;
   hipError_t e = hipStreamCreateWithFlags(&cap, hipStreamNonBlocking);

@@ -387,3 +387,13 @@ def test_step_graph_unready_and_null_handles():
     assert st == B.ERR_WORKSPACE and not g.value
     assert L.loopkv_step_graph_launch(None, None) == B.ERR_INVALID_ARG
     L.loopkv_step_graph_destroy(None)
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    """Without the built library the binding raises; there is no fallback path."""
+    monkeypatch.setattr(B, "_lib", None)
+    monkeypatch.setattr(B, "LIB_PATH", B.LIB_PATH + ".absent")
+    with pytest.raises(RuntimeError, match="not built"):
+        B.lib()
+    with pytest.raises(RuntimeError, match="not built"):
+        lkv.Context(1, 1, 2, 64, 16, 2)

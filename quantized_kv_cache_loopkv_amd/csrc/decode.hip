@@ -949,14 +949,27 @@ __device__ __forceinline__ void row_body(const DecodeArgs& a, const Row& r, cons
       uint32_t* smo = a.sel_mask + orow * (size_t)a.sel_words;
       for (int g = tid; g < a.sel_words; g += kThreads) smo[g] = g < r.n_groups ? selm[g] : 0u;
     }
-    // Gather: wave w takes the 64-group spans w, w + 8, ... and corrects their selected
-    // groups as many at a time as a coarse step holds (two; one at D = 256).
+    // Gather: the selected units are dealt round-robin over the waves in unit order (the
+    // unit of rank k goes to wave k mod 8), and a wave corrects its units as many at a time as
+    // a coarse step holds (two; one at D = 256), so the dependent loads of the corrections
+    // spread over all waves however the selected units cluster.
     using KR = KStep<D, MODE_COARSE, true, GS>;
     using GC = Geo<D, MODE_COARSE, GS>;
     float* wfix = scr;   // [2][64]: refined and coarse weights of the step's selected tokens
-    for (int g64 = 64 * w; g64 < r.n_groups; g64 += 64 * kWaves) {
+    int rank0 = 0;       // selected units in the spans before this one (the same in every wave)
+    for (int g64 = 0; g64 < r.n_groups; g64 += 64) {
       const int gi = g64 + lane;
-      unsigned long long pend = __ballot(gi < r.n_groups && selm[gi < r.n_groups ? gi : 0] != 0u);
+      const unsigned long long all = __ballot(gi < r.n_groups && selm[gi < r.n_groups ? gi : 0] != 0u);
+      unsigned long long pend = 0;   // this wave's share of the span
+      {
+        unsigned long long rest = all;
+        for (int k = rank0; rest; ++k) {
+          const unsigned long long bit = rest & (~rest + 1ull);
+          rest &= rest - 1;
+          if (k % kWaves == w) pend |= bit;
+        }
+      }
+      rank0 += __builtin_popcountll(all);
       while (pend) {
         int groups[2] = {-1, -1};
         groups[0] = g64 + __builtin_ctzll(pend);

@@ -729,6 +729,27 @@ __device__ void exact_v_pass(const Row& r, const float* weights, const uint32_t*
   }
 }
 
+// ----------------------------------------------------------------------------- LDS sizes
+__host__ __device__ inline size_t pad4(size_t n) { return (n + 3) / 4 * 4; }   // keep 16-byte alignment
+__host__ __device__ inline size_t lds_lpad(int max_len) { return ((size_t)max_len + 63) / 64 * 64; }
+__host__ __device__ inline size_t lds_region_a(int max_len, int D) {
+  const size_t need = (size_t)kThreads * (D / 16) + (size_t)kWaves * D;
+  const size_t lp = lds_lpad(max_len);
+  return pad4(lp > need ? lp : need);
+}
+__host__ __device__ inline size_t decode_lds_floats(int max_len, int D) {
+  const size_t lp = lds_lpad(max_len);
+  return lds_region_a(max_len, D) + pad4(lp / 32) + pad4(lp / 16 + 16) + 2 * D + (size_t)kWaves * kWaveScratch + 96;
+}
+// A finishing launch also stages the row's n_split partial value vectors in LDS, right after
+// the row's regions (the exchange words are last), when they fit in the 160 KB.
+__host__ __device__ inline bool finish_parts_in_lds(int max_len, int D, int n_split) {
+  return decode_lds_floats(max_len, D) + (size_t)n_split * D <= (size_t)160 * 1024 / 4;
+}
+__host__ __device__ inline size_t finish_lds_floats(int max_len, int D, int n_split) {
+  return decode_lds_floats(max_len, D) + (finish_parts_in_lds(max_len, D, n_split) ? (size_t)n_split * D : 0);
+}
+
 struct Smem {
   float* scores;    // [lpad]; at the end: [kThreads][VCH] partials, then [kWaves][D] tail partials
   uint32_t* selm;   // [lpad / 32]
@@ -783,6 +804,37 @@ __device__ __forceinline__ void row_body(const DecodeArgs& a, const Row& r, cons
   if (PH == PH_FINISH && lane < a.n_split) {
     part_m = parts[(size_t)lane * (2 + D)];
     part_l = parts[(size_t)lane * (2 + D) + 1];
+  }
+  // PH_FINISH requests everything else it reads from the split scratch here as well, so the
+  // launch waits for memory once: the partials' values into LDS after the row's regions
+  // (when they fit; else the merge loads them), and (selecting rows) the coarse score line.
+  float* pre_parts = PH == PH_FINISH && finish_parts_in_lds(a.max_len, D, a.n_split)
+                         ? sm.misc + 96 : nullptr;
+  if (pre_parts) {
+    for (int idx = tid; idx < a.n_split * D; idx += kThreads)
+      pre_parts[idx] = parts[(size_t)(idx / D) * (2 + D) + 2 + idx % D];
+  }
+  if constexpr (SPARSE && PH == PH_FINISH) {
+    // the row's coarse scores (tail included) from its scratch line into LDS: eight
+    // independent 16-byte loads per thread in flight at once
+    const float4* g4 = reinterpret_cast<const float4*>(a.part_scores + orow * (size_t)a.split_row_stride);
+    float4* l4 = reinterpret_cast<float4*>(scores);
+    const int n4 = (r.N + 3) / 4;   // within the line: its stride is a multiple of 64 floats
+    for (int base = tid; base < n4; base += 8 * kThreads) {
+      // eight named registers (an array here can end up in scratch memory); N >= 1
+      const float4 v0 = g4[min(base + 0 * kThreads, n4 - 1)], v1 = g4[min(base + 1 * kThreads, n4 - 1)];
+      const float4 v2 = g4[min(base + 2 * kThreads, n4 - 1)], v3 = g4[min(base + 3 * kThreads, n4 - 1)];
+      const float4 v4 = g4[min(base + 4 * kThreads, n4 - 1)], v5 = g4[min(base + 5 * kThreads, n4 - 1)];
+      const float4 v6 = g4[min(base + 6 * kThreads, n4 - 1)], v7 = g4[min(base + 7 * kThreads, n4 - 1)];
+      if (base + 0 * kThreads < n4) l4[base + 0 * kThreads] = v0;
+      if (base + 1 * kThreads < n4) l4[base + 1 * kThreads] = v1;
+      if (base + 2 * kThreads < n4) l4[base + 2 * kThreads] = v2;
+      if (base + 3 * kThreads < n4) l4[base + 3 * kThreads] = v3;
+      if (base + 4 * kThreads < n4) l4[base + 4 * kThreads] = v4;
+      if (base + 5 * kThreads < n4) l4[base + 5 * kThreads] = v5;
+      if (base + 6 * kThreads < n4) l4[base + 6 * kThreads] = v6;
+      if (base + 7 * kThreads < n4) l4[base + 7 * kThreads] = v7;
+    }
   }
   __syncthreads();
 
@@ -889,29 +941,8 @@ __device__ __forceinline__ void row_body(const DecodeArgs& a, const Row& r, cons
   if constexpr (SPARSE && PH != PH_PART) {
     float M = -INFINITY, L = 0.f;   // the row's coarse maximum and weight
     if constexpr (PH == PH_FINISH) {
-      // the row's coarse scores (tail included) from its scratch line into LDS: eight
-      // independent 16-byte loads per thread in flight at once
-      const float4* g4 = reinterpret_cast<const float4*>(a.part_scores + orow * (size_t)a.split_row_stride);
-      float4* l4 = reinterpret_cast<float4*>(scores);
-      const int n4 = (r.N + 3) / 4;   // within the line: its stride is a multiple of 64 floats
-      for (int base = tid; base < n4; base += 8 * kThreads) {
-        // eight named registers (an array here can end up in scratch memory); N >= 1
-        const float4 v0 = g4[min(base + 0 * kThreads, n4 - 1)], v1 = g4[min(base + 1 * kThreads, n4 - 1)];
-        const float4 v2 = g4[min(base + 2 * kThreads, n4 - 1)], v3 = g4[min(base + 3 * kThreads, n4 - 1)];
-        const float4 v4 = g4[min(base + 4 * kThreads, n4 - 1)], v5 = g4[min(base + 5 * kThreads, n4 - 1)];
-        const float4 v6 = g4[min(base + 6 * kThreads, n4 - 1)], v7 = g4[min(base + 7 * kThreads, n4 - 1)];
-        if (base + 0 * kThreads < n4) l4[base + 0 * kThreads] = v0;
-        if (base + 1 * kThreads < n4) l4[base + 1 * kThreads] = v1;
-        if (base + 2 * kThreads < n4) l4[base + 2 * kThreads] = v2;
-        if (base + 3 * kThreads < n4) l4[base + 3 * kThreads] = v3;
-        if (base + 4 * kThreads < n4) l4[base + 4 * kThreads] = v4;
-        if (base + 5 * kThreads < n4) l4[base + 5 * kThreads] = v5;
-        if (base + 6 * kThreads < n4) l4[base + 6 * kThreads] = v6;
-        if (base + 7 * kThreads < n4) l4[base + 7 * kThreads] = v7;
-      }
-      M = wave_max(part_m);
+      M = wave_max(part_m);   // the scores reached LDS at the row's start
       L = wave_sum(part_m > -INFINITY ? part_l * __expf(part_m - M) : 0.f);
-      __syncthreads();   // the scores are in LDS
     } else {
       const float lw = wave_sum(st.lsum);
       if (lane == 0) {
@@ -1140,7 +1171,18 @@ __device__ __forceinline__ void row_body(const DecodeArgs& a, const Row& r, cons
       for (int vb = 0; vb < G::BPS; ++vb) o += red[(ww * 64 + vb * G::LPB + chunk) * VCH + c];
       o += tred[ww * D + d];
     }
-    if (with_parts) {   // the partials' values, all loads in flight together
+    if (with_parts && pre_parts) {   // the partials' values, from LDS
+      float ps[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      for (int i0 = 0; i0 < a.n_split; i0 += 8) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int i = i0 + k;
+          const float fi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(part_f), i & 63));
+          if (i < a.n_split) ps[k] = fmaf(pre_parts[i * D + d], fi, ps[k]);
+        }
+      }
+      o += ((ps[0] + ps[1]) + (ps[2] + ps[3])) + ((ps[4] + ps[5]) + (ps[6] + ps[7]));
+    } else if (with_parts) {   // the partials' values, all loads in flight together
       const float* pv = parts + 2 + d;
       float ps[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
       for (int i0 = 0; i0 < a.n_split; i0 += 8) {
@@ -1172,18 +1214,6 @@ __device__ __forceinline__ void row_body(const DecodeArgs& a, const Row& r, cons
       reinterpret_cast<float*>(a.out)[orow * D + d] = o;
     }
   }
-}
-
-__host__ __device__ inline size_t pad4(size_t n) { return (n + 3) / 4 * 4; }   // keep 16-byte alignment
-__host__ __device__ inline size_t lds_lpad(int max_len) { return ((size_t)max_len + 63) / 64 * 64; }
-__host__ __device__ inline size_t lds_region_a(int max_len, int D) {
-  const size_t need = (size_t)kThreads * (D / 16) + (size_t)kWaves * D;
-  const size_t lp = lds_lpad(max_len);
-  return pad4(lp > need ? lp : need);
-}
-__host__ __device__ inline size_t decode_lds_floats(int max_len, int D) {
-  const size_t lp = lds_lpad(max_len);
-  return lds_region_a(max_len, D) + pad4(lp / 32) + pad4(lp / 16 + 16) + 2 * D + (size_t)kWaves * kWaveScratch + 96;
 }
 
 // One kernel per selection regime of the launch (tau = 0, tau > 1, 0 < tau <= 1, or the
@@ -1362,7 +1392,7 @@ static void launch_variant(const DecodeArgs& a, size_t rows, size_t lds, hipStre
     launch_phase<D, GS, VAR, PH_ROW>(a, row_grid(a, rows), lds, stream);
   } else {   // stream order: every partial is written before the finishing launch reads it
     launch_phase<D, GS, VAR, PH_PART>(a, rows * (size_t)a.n_split, lds, stream);
-    launch_phase<D, GS, VAR, PH_FINISH>(a, rows, lds, stream);
+    launch_phase<D, GS, VAR, PH_FINISH>(a, rows, finish_lds_floats(a.max_len, D, a.n_split) * 4, stream);
   }
 }
 

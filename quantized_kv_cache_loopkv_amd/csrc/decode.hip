@@ -1221,8 +1221,15 @@ __device__ __forceinline__ void row_body(const DecodeArgs& a, const Row& r, cons
 // run the 2-bit path inside every planes variant.
 enum : int { VAR_KIVI = 0, VAR_DENSE = 1, VAR_COARSE = 2, VAR_SPARSE = 3, VAR_SKIP = 4 };
 
+// Head dim 256 with both planes (tau = 0) or the KIVI-4 layout needs ~156 VGPRs: those kernels
+// run one workgroup per CU rather than spill (about a third faster than spilling at two).
+template <int D, int VAR>
+constexpr int decode_waves_per_simd() {
+  return (D == 256 && (VAR == VAR_DENSE || VAR == VAR_KIVI)) ? 2 : kWavesPerSimd;
+}
+
 template <int D, int GS, int VAR, int PH>
-__global__ void __launch_bounds__(kThreads, kWavesPerSimd) k_decode(DecodeArgs a) {
+__global__ void __launch_bounds__(kThreads, (decode_waves_per_simd<D, VAR>())) k_decode(DecodeArgs a) {
   extern __shared__ float smem[];
   // Rows are (cell, sequence, query head). PH_PART: workgroup (row, split), the splits of a
   // row adjacent. PH_ROW with grouped queries (G query heads per KV head): workgroups are

@@ -10,11 +10,9 @@
 
 namespace lkv {
 
-constexpr int kGroup = 32;      // default quantization group: tokens per K group / channels per V group
 constexpr int kUnit = 32;       // tokens per decode unit and per selection-mask word
 constexpr int kBlock = 16;      // tokens per record (a page of the block table holds 1 or 2)
 constexpr int kMaxCells = 128;
-constexpr int kMaxLen = 32768;
 
 // Kinds as the kernels see them (the storage a row reads).
 enum : int32_t { KIND_Q4 = 0, KIND_Q2 = 1, KIND_SHARE = 2, KIND_KIVI4 = 3 };
@@ -23,7 +21,6 @@ enum : int32_t { KIND_Q4 = 0, KIND_Q2 = 1, KIND_SHARE = 2, KIND_KIVI4 = 3 };
 // K meta and V meta take 64 D / GS bytes each: a group's D K-meta words are split over its
 // GS / 16 records, and V meta is [D / GS][16 tokens].
 __host__ __device__ constexpr int meta_bytes(int D, int GS) { return 64 * D / GS; }
-__host__ __device__ constexpr int off_k(int) { return 0; }
 __host__ __device__ constexpr int off_kmeta_planes(int D) { return 4 * D; }
 __host__ __device__ constexpr int off_v_planes(int D, int GS) { return 4 * D + meta_bytes(D, GS); }
 __host__ __device__ constexpr int off_vmeta_planes(int D, int GS) { return 8 * D + meta_bytes(D, GS); }

@@ -11,8 +11,8 @@ the last step decodes exactly 16384 tokens.
 Prints one JSON line. ``value`` is the algorithmic HBM rate of the step (bytes
 the method must move / step time); ``roofline`` is the decode kernel's
 algorithmic bytes per launch over its mean duration (HIP events on the launch
-stream) against the 8 TB/s HBM peak; ``cpu_baseline`` times the fp64 oracle on a
-few sampled rows of the same workload on the host.
+stream) against the 8 TB/s HBM peak; ``cpu_baseline`` times the fp64 oracle's decode on a
+row subset of the same workload (every cell x 2 sequences x every head) on the host's cores.
 
 Extra fields: the tau sweep, the token-skipping ablation (unselected tokens dropped instead of
 read at 2 bits), the KIVI-4 layout on the same kernel, a read-ceiling probe, and
@@ -73,30 +73,24 @@ def algorithmic_bytes(plan, lengths, H, D, sel_counts=None, layout_kivi=False, o
       quantized prefix: D/2 + 8D/G B/token (D=128, G=32: K_hi 32 + K_meta 16 + V_hi 32 +
       V_meta 16 = 96; G=64: 80), plus D/2 B (K_lo + V_lo) per selected token on a 4-bit
       target; KIVI-4 reads D + 8D/G B/token (160 at D=128, G=32);
-      tail: 4*D B/token (bf16 K and V); query and output: D * dtype bytes each;
-      block table: 4 B per 16-token block; length: 4 B.
+      tail: 4*D B/token (bf16 K and V); query and output: D * dtype bytes each.
+    Per (cell, sequence): the block table, 4 B per 16-token block (the heads of a sequence
+    share its row).
     sel_counts[c][b][h] is the number of selected tokens (4-bit targets only).
     """
     import numpy as np
     plan = np.asarray(plan).reshape(-1)
-    n_loops_layers = plan.size
     per_tok_base = D // 2 + 8 * D // group
     per_tok_lo = D // 2
     per_tok_kivi = D + 8 * D // group
     total = 0
-    n_layers = None
-    for c in range(n_loops_layers):
-        kind = plan[c]
+    for c in range(plan.size):
         for b, N in enumerate(lengths):
             n_q = group * (N // group)
-            row = (N - n_q) * 4 * D + D * q_bytes + D * out_bytes + 4 * ((N + 15) // 16) + 4
-            if layout_kivi:
-                row += n_q * per_tok_kivi
-                total += H * row
-                continue
-            row += n_q * per_tok_base
-            total += H * row
-            if sel_counts is not None:
+            row = (N - n_q) * 4 * D + D * q_bytes + D * out_bytes
+            row += n_q * (per_tok_kivi if layout_kivi else per_tok_base)
+            total += H * row + 4 * ((N + 15) // 16)
+            if sel_counts is not None and not layout_kivi:
                 total += per_tok_lo * int(sel_counts[c, b].sum())
     return total
 
@@ -112,12 +106,28 @@ def algorithmic_bytes_skip(tk, lengths, H, D, sel_counts, out_bytes=2, q_bytes=2
     for c in range(tk.size):
         for b, N in enumerate(lengths):
             n_q = group * (N // group)
-            row = (N - n_q) * 4 * D + D * q_bytes + D * out_bytes + 4 * ((N + 15) // 16) + 4
+            row = (N - n_q) * 4 * D + D * q_bytes + D * out_bytes
             row += n_q * ((D // 4 + 4 * D // group) if tk[c] == 0 else (D // 2 + 8 * D // group))
-            total += H * row
+            total += H * row + 4 * ((N + 15) // 16)
             if tk[c] == 0:
                 total += (3 * D // 4 + 4 * D // group) * int(sel_counts[c, b].sum())
     return total
+
+
+def gathered_bytes(sm, tk, D, group=32):
+    """Bytes the corrections load for the selected tokens, as the kernel reads them: per 32-token
+    unit holding a selected token its K low plane (8 D) and its group's K meta (4 D: one word
+    per channel), per 16-token block holding one its V high and low planes and V meta
+    (8 D + 64 D / G). The algorithmic count charges D/2 per selected token instead; the
+    difference is the gather's re-read granularity."""
+    import torch
+    w = sm.to(torch.int64) & 0xFFFFFFFF                       # [cells][B][H][units]
+    rows_q4 = torch.as_tensor(tk == 0, device=sm.device).view(-1, 1, 1, 1)
+    units = ((w != 0) & rows_q4).sum().item()
+    blocks = ((((w & 0xFFFF) != 0).to(torch.int64) + (((w >> 16) & 0xFFFF) != 0).to(torch.int64))
+              * rows_q4).sum().item()
+    meta = 64 * D // group
+    return int(units * (8 * D + 4 * D) + blocks * (8 * D + meta))
 
 
 def target_kinds(plan, n_loops, n_layers):
@@ -148,47 +158,129 @@ def sel_counts_from_mask(sm, n_q):
     return bits.sum(axis=-1)
 
 
-def cpu_baseline(cfg, plan, tau, rows, log, min_seconds=10.0, max_evals=400):
-    """Time the fp64 oracle (quantize + loop-aware decode of one row) on sampled rows.
+CPU_SEQS = 2    # sequences of the oracle's row subset: every cell and head of each
+CPU_REPS = 3    # timed repetitions of every row (the subset's time is the median pass)
 
-    The distinct rows' inputs are drawn first (untimed); the oracle then evaluates the
-    rows round-robin until about ``min_seconds`` of CPU time has accumulated."""
+
+def cpu_workers():
+    """Worker processes for the oracle: the host's CPU share for this process, at most 16."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def _cpu_worker_init():
+    """One BLAS thread per worker process: the rows run in parallel across processes."""
+    for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+        os.environ[k] = "1"
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(1)
+    except Exception:
+        pass
+
+
+def cpu_rows_task(kpath, vpath, rows, tau, sig, group, bits, reps):
+    """The oracle's decode of every row reading one storage chunk (one cell and sequence, bf16
+    K and V bits [N][KV heads][D] in two .npy files, removed once read). Per KV head the history
+    is converted and quantized once (untimed); each row (head, query, kind) is then decoded
+    ``reps`` times, each timed. Returns [(head, [seconds per repetition], selected count)]."""
     import numpy as np
     from oracle import loopkv_oracle as O
-    from synth import recipes as R
     from synth.philox import bf16_bits_to_f32
+    kb = np.load(kpath)
+    vb = np.load(vpath)
+    os.remove(kpath)
+    os.remove(vpath)
+    out = []
+    cur, K, V, qh = None, None, None, None
+    for h, q, kind in sorted(rows, key=lambda r: r[0]):
+        if h != cur:
+            K = bf16_bits_to_f32(np.ascontiguousarray(kb[:, h])).astype(np.float64)
+            V = bf16_bits_to_f32(np.ascontiguousarray(vb[:, h])).astype(np.float64)
+            qh = O.quantize_history(K, V, bits, group)
+            cur = h
+        ts = []
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            _, sel, _ = O.decode_row(q, K, V, kind, tau, sig, qh=qh, group=group)
+            ts.append(time.perf_counter() - t0)
+        out.append((h, ts, int(sel.sum())))
+    return out
+
+
+def _spool_dir(need_bytes):
+    import shutil
+    import tempfile
+    for d in ("/dev/shm", tempfile.gettempdir()):
+        try:
+            if os.access(d, os.W_OK) and shutil.disk_usage(d).free > 2 * need_bytes:
+                return tempfile.mkdtemp(prefix="loopkv_cpu_", dir=d)
+        except OSError:
+            continue
+    return tempfile.mkdtemp(prefix="loopkv_cpu_")
+
+
+def cpu_baseline(pool, workers, wl, q, plan, tau, lengths, seqs, log):
+    """The fp64 oracle's decode on a row subset of the timed workload: every cell x the given
+    sequences x every head, on the same inputs (the seeded generator's draws of each row's
+    history, the queries of the timed decode). Generation and quantization are excluded; each row
+    is decoded CPU_REPS times in one of ``workers`` single-threaded processes. The subset's time
+    is the median over the repetitions of the rows' summed time, divided over the workers (rows
+    are independent); the per-step figure scales it by all rows / subset rows."""
+    import numpy as np
+    import torch
+    from oracle import loopkv_oracle as O
+    cfg = wl.cfg
+    C, B, H, D, G = cfg.n_cells, cfg.batch, cfg.n_heads, cfg.head_dim, cfg.group
+    P = plan.reshape(cfg.n_loops, cfg.n_layers)
+    sig = float(np.float32(1.0 / math.sqrt(D)))
+    qh_ = q.float().cpu().numpy().astype(np.float64)
+    chunks = {}
+    for c in range(C):
+        st, kind = O.storage_cell(P, c), O.target_kind(P, c)
+        for b in seqs:
+            for h in range(H):
+                chunks.setdefault((st, b), []).append((h, qh_[c, b, h], kind))
+    n_rows = sum(len(r) for r in chunks.values())
+    chunk_bytes = 2 * max(lengths) * cfg.kv_heads * D * 2
+    spool = _spool_dir(2 * workers * chunk_bytes)
+    t_wall = time.perf_counter()
+    results, pending = [], []
     try:
-        from threadpoolctl import threadpool_info
-        cores = max([1] + [i.get("num_threads", 1) for i in threadpool_info()])
-    except Exception:
-        cores = 1
-    factors = R.factor_table(cfg)
-    sig = float(np.float32(1.0 / math.sqrt(cfg.head_dim)))
-    inputs = []
-    for (c, b, h) in rows:
-        st = O.storage_cell(plan.reshape(cfg.n_loops, cfg.n_layers), c)
-        kind = O.target_kind(plan.reshape(cfg.n_loops, cfg.n_layers), c)
-        N = cfg.lengths[b]
-        kb, vb = R.kv_row_bits(cfg, st, b, h, 0, N, factors)
-        K = bf16_bits_to_f32(kb).astype(np.float64)
-        V = bf16_bits_to_f32(vb).astype(np.float64)
-        q = R.q_values(cfg, c, 0, b, h).astype(np.float64)
-        inputs.append((q, K, V, kind, N))
-    t_total = 0.0
-    bytes_total = 0
-    evals = 0
-    while evals < max_evals and (t_total < min_seconds or evals < len(inputs)):
-        q, K, V, kind, N = inputs[evals % len(inputs)]
-        t0 = time.perf_counter()
-        o, sel, _ = O.decode_row(q, K, V, kind, tau, sig, group=cfg.group)
-        t_total += time.perf_counter() - t0
-        D, G = cfg.head_dim, cfg.group
+        for i, ((st, b), rows) in enumerate(chunks.items()):
+            N = lengths[b]
+            K, V = wl.kv_seq_gpu(st, b, 0, N)
+            kp, vp = os.path.join(spool, f"k{i}.npy"), os.path.join(spool, f"v{i}.npy")
+            np.save(kp, K[0].view(torch.int16).cpu().numpy().view(np.uint16))
+            np.save(vp, V[0].view(torch.int16).cpu().numpy().view(np.uint16))
+            del K, V
+            bits = 2 if int(plan[st]) == 1 else 4
+            pending.append((N, st, pool.apply_async(cpu_rows_task, (kp, vp, rows, tau, sig, G, bits, CPU_REPS))))
+            while len(pending) >= 2 * workers:   # bound the spooled chunks
+                N0, st0, r0 = pending.pop(0)
+                results.append((N0, st0, r0.get()))
+        for N, st, r in pending:
+            results.append((N, st, r.get()))
+    finally:
+        import shutil
+        shutil.rmtree(spool, ignore_errors=True)
+    t_wall = time.perf_counter() - t_wall
+    pass_s = np.zeros(CPU_REPS)
+    sub_bytes = 0
+    for N, st, res in results:
         n_q = G * (N // G)
-        bytes_total += n_q * (D // 2 + 8 * D // G) + (N - n_q) * 4 * D + 4 * D + 4 * ((N + 15) // 16) + 4
-        if kind == 0:
-            bytes_total += D // 2 * int(sel.sum())
-        evals += 1
-    log(f"cpu oracle: {evals} row evaluations ({len(inputs)} distinct rows) in {t_total:.2f}s")
+        for h, ts, n_sel in res:
+            pass_s += np.asarray(ts)
+            sub_bytes += n_q * (D // 2 + 8 * D // G) + (N - n_q) * 4 * D + 4 * D + (D // 2) * n_sel
+    sub_bytes += sum(4 * ((lengths[b] + 15) // 16) for b in seqs) * C   # block table per (cell, sequence)
+    cpu_s = float(np.median(pass_s))
+    sub_s = cpu_s / workers
+    scale = (C * B * H) / n_rows
+    log(f"cpu oracle: {n_rows} rows x {CPU_REPS} on {workers} workers, {t_wall:.1f} s wall "
+        f"(drawing and quantization included); rows' decode time {cpu_s:.1f} cpu-s per pass (median)")
     cpu_model = "unknown"
     try:
         for line in open("/proc/cpuinfo"):
@@ -197,12 +289,18 @@ def cpu_baseline(cfg, plan, tau, rows, log, min_seconds=10.0, max_evals=400):
                 break
     except OSError:
         pass
-    return {"value": bytes_total / t_total / 1e9, "unit": "GB/s", "cores": int(cores), "kind": "oracle",
+    return {"value": sub_bytes / sub_s / 1e9, "unit": "GB/s", "cores": workers, "kind": "oracle",
+            "subset_rows": n_rows, "subset_cpu_seconds_median": round(cpu_s, 3),
+            "subset_seconds_on_cores": round(sub_s, 3),
+            "us_per_step_extrapolated": round(sub_s * scale * 1e6, 1),
             "host_cpus": os.cpu_count(), "cpu_model": cpu_model,
-            "sample": f"{len(inputs)} distinct (cell, seq, head) rows of the 16K-context plan (4-bit, 2-bit and "
-                      f"reuse cells), evaluated round-robin {evals} times: fp64 quantize + loop-aware decode "
-                      f"per row, {t_total:.2f} s measured, input generation excluded; value = the rows' "
-                      f"algorithmic bytes / oracle time"}
+            "sample": f"fp64 oracle decode (numpy) of {n_rows} rows of the timed workload: all {C} cells x "
+                      f"{len(seqs)} sequences x {H} heads at {max(lengths)} tokens, tau {tau}, the same seeded "
+                      f"inputs and queries; quantization and input generation excluded; each row decoded "
+                      f"{CPU_REPS} times, the subset time is the median pass ({cpu_s:.1f} cpu-s) over "
+                      f"{workers} single-threaded worker processes ({sub_s:.2f} s); value = the subset's "
+                      f"algorithmic bytes / that time; us_per_step_extrapolated scales it by "
+                      f"{C * B * H} / {n_rows} rows"}
 
 
 def serving_graph(wl, q, tau, first_step, n_rep, n_split, log, warm=2):
@@ -255,7 +353,6 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-serving", action="store_true",
                     help="skip the per-(loop, layer) graph legs (batch 32 and batch 1)")
-    ap.add_argument("--cpu-rows", type=int, default=6)
     ap.add_argument("--group", type=int, choices=[32, 64], default=32,
                     help="quantization group (tokens per K group, channels per V group); the pages' is 32")
     ap.add_argument("--table", choices=["shuffled", "identity"], default="shuffled",
@@ -277,6 +374,13 @@ def main():
         print(f"bench.py measures one GPU: the library has no multi-GPU path (asked for --gpus {args.gpus}). "
               "Rows of the decode are independent; see the sharding notes for how it would split.", file=sys.stderr)
         sys.exit(2)
+
+    # the oracle's worker processes start before anything touches the GPU
+    pool, workers = None, 0
+    if not args.no_cpu:
+        import multiprocessing as mp
+        workers = cpu_workers()
+        pool = mp.get_context("spawn").Pool(workers, initializer=_cpu_worker_init)
 
     import numpy as np
     import torch
@@ -367,6 +471,10 @@ def main():
             ms = e_a.elapsed_time(e_b) / 3
             sweep[str(tau)] = {"decode_ms": round(ms, 4), "algorithmic_GB": round(bts / 1e9, 3),
                                "GBps": round(bts / (ms * 1e-3) / 1e9, 1), "selected": int(ct.sum())}
+            if 0.0 < tau <= 1.0:   # what the corrections load for the selected tokens, as read
+                gb = gathered_bytes(smt, tk, D, GQ)
+                sweep[str(tau)]["gathered_GB"] = round(gb / 1e9, 4)
+                sweep[str(tau)]["algorithmic_selected_GB"] = round((D // 2) * int(ct.sum()) / 1e9, 4)
             log(f"tau={tau}: {ms:.3f} ms, {bts / 1e9:.2f} GB, {bts / (ms * 1e-3) / 1e9:.0f} GB/s")
         extra["tau_sweep"] = sweep
         # the ablation the pages reject: drop the unselected tokens instead of reading them at 2 bits
@@ -451,22 +559,11 @@ def main():
         log(f"read ceiling probe failed: {e}")
 
     cpu = None
-    if not args.no_cpu:
-        rows = []
-        kinds_seen = {}
-        for c in range(C):
-            k = int(plan[c])
-            if kinds_seen.get(k, 0) < max(1, args.cpu_rows // 3):
-                rows.append((c, (7 * c) % B, (3 * c) % H))
-                kinds_seen[k] = kinds_seen.get(k, 0) + 1
-            if len(rows) >= args.cpu_rows:
-                break
-        ccfg = R.make_config("C4")
-        ccfg.batch = B
-        ccfg.lengths = [args.ctx - S] * B     # the initial histories of the timed workload
-        ccfg.append_steps = S + GS
-        ccfg.group = GQ
-        cpu = cpu_baseline(ccfg, plan, args.tau, rows, log)
+    if pool is not None:
+        seqs = sorted({0, B // 2})[:CPU_SEQS]
+        cpu = cpu_baseline(pool, workers, wl, q, plan, args.tau, final_lens, seqs, log)
+        pool.close()
+        pool.join()
 
     line = {
         "metric": "achieved HBM GB/s (% of peak) + us per decode step, 4x24 plan, 16K ctx",

@@ -115,13 +115,42 @@ def _dtype_code(t: torch.Tensor) -> int:
 
 
 def _dev_i32(t: Optional[torch.Tensor], name: str, numel: Optional[int] = None):
+    """A contiguous int32 tensor of at least ``numel`` elements (its device is checked by
+    _on_device)."""
     if t is None:
         return None
-    if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous():
-        raise ValueError(f"{name} must be a contiguous int32 CUDA tensor")
+    if t.dtype != torch.int32 or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous int32 tensor")
     if numel is not None and t.numel() < numel:
         raise ValueError(f"{name} has {t.numel()} elements, needs {numel}")
     return t
+
+
+def _block_table(bt: torch.Tensor, n_seqs: int):
+    """The kernels read n_seqs rows of bt_stride entries: a 2-D table needs at least n_seqs rows;
+    a 1-D table is one row, so it serves one sequence only. Returns (table, bt_stride)."""
+    _dev_i32(bt, "block_table")
+    if bt.dim() == 2:
+        if bt.shape[0] < n_seqs or bt.shape[1] < 1:
+            raise ValueError(f"block_table of shape {tuple(bt.shape)} has fewer than {n_seqs} rows")
+        return bt, int(bt.shape[1])
+    if bt.dim() == 1:
+        if n_seqs > 1 or bt.numel() < 1:
+            raise ValueError("a 1-D block_table is one sequence's row; pass [n_seqs][bt_stride] for more")
+        return bt, int(bt.numel())
+    raise ValueError("block_table must be [n_seqs][bt_stride] (or one row)")
+
+
+def _on_device(device, **tensors):
+    """Every given tensor must live on the GPU the context's workspace is on (any GPU before a
+    workspace is bound): the library passes their addresses to kernels unchecked."""
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a CUDA tensor")
+        if device is not None and t.device != device:
+            raise ValueError(f"{name} is on {t.device}, the workspace on {device}")
 
 
 def plan_search(n_loops: int, n_layers: int, damage, reads, storage, damage_budget: float, storage_budget: int):
@@ -201,6 +230,9 @@ class Context:
                                          ctypes.byref(s)))
         return {"pool_offset": p.value, "tail_offset": t.value, "record_bytes": r.value, "storage_cell": s.value}
 
+    def _device(self):
+        return None if self.workspace is None else self.workspace.device
+
     def _cell(self, cell):
         if cell is None:
             return -1, -1
@@ -222,10 +254,10 @@ class Context:
             n_seqs, n_new = k.shape[0], k.shape[1]
         if k.shape[-2:] != (self.kv_heads, self.cfg.head_dim):
             raise ValueError("k trailing dims must be [KV heads][D]")
-        bt = _dev_i32(block_table, "block_table", n_seqs)
+        bt, bt_stride = _block_table(block_table, n_seqs)
         _dev_i32(seq_lens, "seq_lens", n_seqs)
         _dev_i32(seq_slots, "seq_slots", n_seqs)
-        bt_stride = bt.shape[-1] if bt.dim() == 2 else bt.numel()
+        _on_device(self._device(), k=k, v=v, block_table=bt, seq_lens=seq_lens, seq_slots=seq_slots)
         _check(lib().loopkv_append(self._h, _stream(), loop, layer, _ptr(k), _ptr(v), _dtype_code(k), n_seqs, n_new,
                                    _ptr(seq_slots), _ptr(bt), bt_stride, _ptr(seq_lens)))
 
@@ -266,15 +298,24 @@ class Context:
             out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
         if out.shape != q.shape or not out.is_contiguous():
             raise ValueError("out must be contiguous with q's shape")
+        _dtype_code(q)
+        _dtype_code(out)
+        words = (int(max_len) + 31) // 32
         sm = None
         if sel_mask is True:
-            sm = torch.zeros((*q.shape[:-1], (max_len + 31) // 32), dtype=torch.int32, device=q.device)
+            sm = torch.zeros((*q.shape[:-1], words), dtype=torch.int32, device=q.device)
         elif isinstance(sel_mask, torch.Tensor):
-            sm = sel_mask
-        bt = _dev_i32(block_table, "block_table", n_seqs)
+            # the kernels write rows x ceil(max_len / 32) words
+            sm = _dev_i32(sel_mask, "sel_mask", q.numel() // D * words)
+        elif sel_mask not in (False, None):
+            raise ValueError("sel_mask must be True, False/None or an int32 tensor")
+        bt, bt_stride = _block_table(block_table, n_seqs)
         _dev_i32(seq_lens, "seq_lens", n_seqs)
         _dev_i32(seq_slots, "seq_slots", n_seqs)
-        bt_stride = bt.shape[-1] if bt.dim() == 2 else bt.numel()
+        if scratch is not None and not scratch.is_contiguous():
+            raise ValueError("scratch must be a contiguous CUDA tensor")
+        _on_device(self._device(), q=q, out=out, sel_mask=sm, block_table=bt, seq_lens=seq_lens,
+                   seq_slots=seq_slots, scratch=scratch)
         if skip:
             if n_split:
                 raise ValueError("the token-skipping ablation runs one workgroup per row (n_split=0)")
@@ -285,8 +326,6 @@ class Context:
             if scratch is None:
                 scratch = torch.empty(self.split_scratch_bytes(n_seqs, max_len, n_split, cell), dtype=torch.uint8,
                                       device=q.device)
-            if not scratch.is_cuda or not scratch.is_contiguous():
-                raise ValueError("scratch must be a contiguous CUDA tensor")
             _check(lib().loopkv_decode_attn_split(self._h, _stream(), loop, layer, _ptr(q), _dtype_code(q), n_seqs,
                                                   _ptr(seq_slots), _ptr(bt), bt_stride, _ptr(seq_lens), int(max_len),
                                                   float(tau), float(sm_scale), _ptr(out), _dtype_code(out), _ptr(sm),
@@ -308,25 +347,42 @@ class StepGraph:
 
     def __init__(self, ctx: "Context", k, v, q, block_table, lens_before, lens_after, max_len: int, tau: float,
                  out, sel_mask=None, n_split: int = 0, scratch=None, sm_scale=None, seq_slots=None):
+        C, H, D, KVH = ctx.n_cells, ctx.cfg.n_heads, ctx.cfg.head_dim, ctx.kv_heads
+        if q.dim() != 4:
+            raise ValueError("q must be [cells][n_seqs][H][D]")
         n_seqs = q.shape[1]
         if sm_scale is None:
-            sm_scale = 1.0 / math.sqrt(ctx.cfg.head_dim)
+            sm_scale = 1.0 / math.sqrt(D)
+        # the captured launches stride k, v over every cell (a reuse cell's slice is unread) and q,
+        # out, sel_mask over every cell
+        if tuple(k.shape) != (C, n_seqs, 1, KVH, D) or tuple(v.shape) != tuple(k.shape):
+            raise ValueError(f"k and v must be [{C} cells][{n_seqs}][1][{KVH}][{D}]")
+        if tuple(q.shape) != (C, n_seqs, H, D) or tuple(out.shape) != tuple(q.shape):
+            raise ValueError(f"q and out must be [{C} cells][n_seqs][{H}][{D}]")
+        if k.dtype != v.dtype:
+            raise ValueError("k and v must share a dtype")
         for name, t in (("k", k), ("v", v), ("q", q), ("out", out)):
-            if not t.is_cuda or not t.is_contiguous():
-                raise ValueError(f"{name} must be a contiguous CUDA tensor")
-        if n_split and scratch is None:
-            scratch = torch.empty(ctx.split_scratch_bytes(n_seqs, max_len, n_split, (0, 0)), dtype=torch.uint8,
-                                  device=q.device)
-        bt = _dev_i32(block_table, "block_table", n_seqs)
+            _dtype_code(t)
+            if not t.is_contiguous():
+                raise ValueError(f"{name} must be contiguous")
+        if sel_mask is not None:
+            _dev_i32(sel_mask, "sel_mask", C * n_seqs * H * ((int(max_len) + 31) // 32))
+        bt, bt_stride = _block_table(block_table, n_seqs)
         _dev_i32(lens_before, "lens_before", n_seqs)
         _dev_i32(lens_after, "lens_after", n_seqs)
         _dev_i32(seq_slots, "seq_slots", n_seqs)
+        if scratch is not None and not scratch.is_contiguous():
+            raise ValueError("scratch must be a contiguous CUDA tensor")
+        _on_device(ctx._device(), k=k, v=v, q=q, out=out, sel_mask=sel_mask, block_table=bt,
+                   lens_before=lens_before, lens_after=lens_after, seq_slots=seq_slots, scratch=scratch)
+        if n_split and scratch is None:
+            scratch = torch.empty(ctx.split_scratch_bytes(n_seqs, max_len, n_split, (0, 0)), dtype=torch.uint8,
+                                  device=q.device)
         self._keep = (ctx, k, v, q, bt, lens_before, lens_after, out, sel_mask, scratch, seq_slots)
         h = ctypes.c_void_p()
         nbytes = 0 if scratch is None else scratch.numel() * scratch.element_size()
         _check(lib().loopkv_step_graph_create(ctx._h, _ptr(k), _ptr(v), _dtype_code(k), _ptr(q), _dtype_code(q),
-                                              n_seqs, _ptr(seq_slots), _ptr(bt),
-                                              bt.shape[-1] if bt.dim() == 2 else bt.numel(), _ptr(lens_before),
+                                              n_seqs, _ptr(seq_slots), _ptr(bt), bt_stride, _ptr(lens_before),
                                               _ptr(lens_after), int(max_len), float(tau), float(sm_scale), _ptr(out),
                                               _dtype_code(out), _ptr(sel_mask), int(n_split), _ptr(scratch), nbytes,
                                               ctypes.byref(h)))

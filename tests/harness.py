@@ -202,6 +202,28 @@ class Workload:
         lens_before.add_(1)
         lens_after.add_(1)
 
+    # ------------------------------------------------------------------ oracle inputs
+    def oracle_inputs(self, cell_store: int, b: int, kvh: int, n_tokens: int):
+        """float64 K, V [n_tokens][D] of one (storage cell, sequence, KV head), drawn by the seeded
+        generator for the oracle. Workloads that draw on the GPU draw here on the GPU too (the same
+        bits as the host draw; every head of the sequence at once, the last two kept); the library
+        plays no part."""
+        if not self.gpu_synth:
+            _, _, K, V = oracle_row_inputs(self.cfg, cell_store, b, kvh, n_tokens, self.factors)
+            return K, V
+        cache = self.__dict__.setdefault("_row_cache", {})
+        key = (cell_store, b, n_tokens)
+        if key not in cache:
+            K, V = self.kv_seq_gpu(cell_store, b, 0, n_tokens)
+            kb = K[0].view(torch.int16).cpu().numpy().view(np.uint16)
+            vb = V[0].view(torch.int16).cpu().numpy().view(np.uint16)
+            while len(cache) >= 2:
+                cache.pop(next(iter(cache)))
+            cache[key] = (kb, vb)
+        kb, vb = cache[key]
+        return (bf16_bits_to_f32(np.ascontiguousarray(kb[:, kvh])).astype(np.float64),
+                bf16_bits_to_f32(np.ascontiguousarray(vb[:, kvh])).astype(np.float64))
+
     # ------------------------------------------------------------------ inspection
     def record(self, cell: int, b: int, h: int, j: int) -> np.ndarray:
         """Bytes of the record of 16-token block j of (cell, sequence b, KV head h): pages of
@@ -242,6 +264,16 @@ def rel_err(o, ref):
     ref = np.asarray(ref, np.float64)
     den = np.abs(ref).max()
     return float(np.abs(o - ref).max() / (den if den > 0 else 1.0))
+
+
+def selected_counts(sm: torch.Tensor) -> torch.Tensor:
+    """Selected tokens per row of a mask tensor [..][words] (int32 words, on the device)."""
+    x = sm.to(torch.int64) & 0xFFFFFFFF
+    x = x - ((x >> 1) & 0x55555555)
+    x = (x & 0x33333333) + ((x >> 2) & 0x33333333)
+    x = (x + (x >> 4)) & 0x0F0F0F0F
+    x = ((x * 0x01010101) & 0xFFFFFFFF) >> 24
+    return x.sum(-1)
 
 
 def sel_bits_from_mask(mask_words: np.ndarray, n_q: int) -> np.ndarray:

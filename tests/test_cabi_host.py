@@ -397,3 +397,84 @@ def test_missing_library_fails_loudly(monkeypatch):
         B.lib()
     with pytest.raises(RuntimeError, match="not built"):
         lkv.Context(1, 1, 2, 64, 16, 2)
+
+
+# --------------------------------------------------------------------------- binding argument checks
+# The binding checks shapes, dtypes and sizes before anything reaches the library, and device
+# placement last; on a host without a GPU every tensor is a CPU tensor, so a call whose shapes
+# are right stops at the device check ("CUDA"), and one whose shapes are wrong stops earlier.
+def _binding_ctx(H=2, D=64, n_seqs=2):
+    import torch
+    ctx = lkv.Context(1, 2, H, D, 64, 4)
+    ctx.plan([0, 1])
+    q = torch.zeros((2, n_seqs, H, D), dtype=torch.float32)
+    bt = torch.zeros((n_seqs, 8), dtype=torch.int32)
+    lens = torch.zeros(n_seqs, dtype=torch.int32)
+    return ctx, q, bt, lens
+
+
+def test_binding_block_table_rows():
+    import torch
+    ctx, q, bt, lens = _binding_ctx()
+    with pytest.raises(ValueError, match="fewer than 2 rows"):
+        ctx.decode(q, bt[:1].contiguous(), lens, 100, 0.01)
+    with pytest.raises(ValueError, match="1-D block_table"):
+        ctx.decode(q, bt.reshape(-1).contiguous(), lens, 100, 0.01)
+    with pytest.raises(ValueError, match="int32"):
+        ctx.decode(q, bt.to(torch.int64), lens, 100, 0.01)
+    k = torch.zeros((2, 2, 1, 2, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="fewer than 2 rows"):
+        ctx.append(k, k.clone(), bt[:1].contiguous(), lens)
+    with pytest.raises(ValueError, match="1-D block_table"):
+        ctx.append(k, k.clone(), bt.reshape(-1).contiguous(), lens)
+    # one sequence may pass its row as a 1-D table
+    with pytest.raises(ValueError, match="CUDA"):
+        ctx.decode(q[:, :1].contiguous(), bt[0].contiguous(), lens[:1], 100, 0.01)
+    with pytest.raises(ValueError, match="CUDA"):
+        ctx.decode(q, bt, lens, 100, 0.01)
+    with pytest.raises(ValueError, match="CUDA"):
+        ctx.append(k, k.clone(), bt, lens)
+
+
+def test_binding_sel_mask_and_lengths():
+    import torch
+    ctx, q, bt, lens = _binding_ctx()
+    words = (100 + 31) // 32
+    need = 2 * 2 * 2 * words
+    with pytest.raises(ValueError, match="sel_mask has"):
+        ctx.decode(q, bt, lens, 100, 0.01, sel_mask=torch.zeros(need - 1, dtype=torch.int32))
+    with pytest.raises(ValueError, match="int32"):
+        ctx.decode(q, bt, lens, 100, 0.01, sel_mask=torch.zeros(need, dtype=torch.float32))
+    with pytest.raises(ValueError, match="sel_mask must be"):
+        ctx.decode(q, bt, lens, 100, 0.01, sel_mask="yes")
+    with pytest.raises(ValueError, match="seq_lens has"):
+        ctx.decode(q, bt, lens[:1], 100, 0.01)
+    with pytest.raises(ValueError, match="CUDA"):
+        ctx.decode(q, bt, lens, 100, 0.01, sel_mask=torch.zeros(need, dtype=torch.int32))
+    with pytest.raises(ValueError, match="out must be"):
+        ctx.decode(q, bt, lens, 100, 0.01, out=torch.zeros((2, 2, 2, 32)))
+    with pytest.raises(ValueError, match="unsupported dtype"):
+        ctx.decode(q.to(torch.float16), bt, lens, 100, 0.01)
+
+
+def test_binding_step_graph_shapes():
+    """A captured step strides k, v, q, out and sel_mask over every cell of the plan."""
+    import torch
+    ctx, q, bt, lens = _binding_ctx()
+    C, B_, H, D = 2, 2, 2, 64
+    k = torch.zeros((C, B_, 1, H, D), dtype=torch.bfloat16)
+    out = torch.zeros_like(q)
+    la = lens + 1
+    with pytest.raises(ValueError, match="k and v must be"):
+        ctx.step_graph(k[:1].contiguous(), k[:1].contiguous(), q, bt, lens, la, 100, 0.01, out)
+    with pytest.raises(ValueError, match="k and v must be"):
+        ctx.step_graph(k, k[:, :, :, :1].contiguous(), q, bt, lens, la, 100, 0.01, out)
+    with pytest.raises(ValueError, match="q and out must be"):
+        ctx.step_graph(k, k.clone(), q, bt, lens, la, 100, 0.01, out[:1].contiguous())
+    with pytest.raises(ValueError, match="sel_mask has"):
+        ctx.step_graph(k, k.clone(), q, bt, lens, la, 100, 0.01, out,
+                       sel_mask=torch.zeros(C * B_ * H * 4 - 1, dtype=torch.int32))
+    with pytest.raises(ValueError, match="fewer than 2 rows"):
+        ctx.step_graph(k, k.clone(), q, bt[:1].contiguous(), lens, la, 100, 0.01, out)
+    with pytest.raises(ValueError, match="CUDA"):
+        ctx.step_graph(k, k.clone(), q, bt, lens, la, 100, 0.01, out)

@@ -160,3 +160,30 @@ def test_gpu_peaked_rows(row, n_split):
     err, n_sel = _check(_bf16(K), _bf16(V), q, tau, f"peaked {row} split={n_split}", n_split=n_split)
     print(f"peaked {row} split={n_split}: removed/kept {ratio:.0f}, rel err {err:.2e}, selected {n_sel}",
           flush=True)
+
+
+# Generator rows (found by a search with the oracle alone) whose removed / kept coarse weight
+# lies in [4, 8): just under the ratio at which the kernel recomputes a row's values, so the
+# corrected values sum keeps the selected winner's block rounding, amplified by up to 8x.
+_NEAR_GUARD = [(0, 128, 1, 0, 5.0, 0.05), (2, 128, 0, 2, 3.0, 0.05), (2, 128, 1, 2, 5.0, 0.05),
+               (3, 128, 0, 3, 5.0, 0.05), (2, 256, 1, 0, 5.0, 0.05), (6, 256, 1, 3, 5.0, 0.05),
+               (0, 256, 1, 0, 5.0, 0.05), (3, 64, 1, 3, 3.0, 0.05), (6, 64, 1, 2, 3.0, 0.05),
+               (0, 64, 0, 3, 3.0, 0.05)]
+
+
+@pytest.mark.parametrize("n_split", [0, 4])
+@pytest.mark.parametrize("row", _NEAR_GUARD)
+def test_gpu_rows_under_the_recompute_ratio(row, n_split):
+    _need_gpu()
+    from synth import recipes as R
+    from tests.harness import oracle_row_inputs
+    seed, D, b, h, gain, tau = row
+    cfg = R.small_config("peak", 1, 1, 4, D, [700, 1300], [tau], outlier_count=3, outlier_mult=10.0, seed=seed)
+    N = cfg.lengths[b]
+    _, _, K, V = oracle_row_inputs(cfg, 0, b, h, N, R.factor_table(cfg))
+    q = (R.q_values(cfg, 0, 0, b, h) * gain).astype(np.float32)
+    ratio = _removed_over_kept(q.astype(np.float64), K, V, tau, float(np.float32(1.0 / math.sqrt(D))))
+    assert 4.0 <= ratio < 8.0, ratio
+    err, n_sel = _check(_bf16(K), _bf16(V), q, tau, f"near-guard {row} split={n_split}", n_split=n_split)
+    print(f"near-guard {row} split={n_split}: removed/kept {ratio:.2f}, rel err {err:.2e}, selected {n_sel}",
+          flush=True)

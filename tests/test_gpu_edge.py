@@ -1,0 +1,262 @@
+"""GPU parity on the quantizer's and the decode's edge regimes, against the fp64 oracle.
+
+The generator's Irwin-Hall draws are light-tailed and zero-mean, so the general parity tests
+never reach these regimes; here K and V are built directly (rounded to bf16 once, the same
+bf16 values feeding both sides):
+
+* constant groups: K channels constant over a quantization group and V token slices constant
+  over a channel group give scale 0 and code 0 (the value is the zero point), down to a whole
+  K group whose every coefficient is 0 and a V history that is one constant vector, where the
+  attention output is that vector (oracle pin P7);
+* power-of-two scaling (pin P8): V x 2^k must give exactly 2^k times the output, and K x 2^k
+  with sigma x 2^-k exactly the same selection and output. The kernel's fixed-point folding
+  takes its scales from the data's binary exponents, so these hold bit for bit on the GPU too;
+* zero points far from zero (|z| >> s): the scores' constant terms and the value sums'
+  zero-point terms dominate;
+* magnitudes up to the 3e4 bound the fp16 scale and zero point allow, and heavy-tailed
+  (Student-t) values, whose groups hold one far outlier each.
+
+Every row is compared with the oracle: selection bit-exact outside the 1e-5 tie band, output
+within 2e-3 (max |o - ref| / max |ref|), for 4-bit targets at tau 0, 0.01 and 1.1, 2-bit
+targets and the KIVI-4 layout, groups of 32 and 64.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import quantized_kv_cache_loopkv_amd as lkv
+from oracle import loopkv_oracle as O
+from tests.harness import rel_err, sel_bits_from_mask
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-3
+TIE = 1e-5
+LENGTHS = [700, 333, 64]   # several tiles, a ragged tail, an exact group multiple
+
+
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _bf16_np(x):
+    """float64 values of the bf16 rounding of x (nearest even, through torch)."""
+    return torch.tensor(np.asarray(x, dtype=np.float32)).to(torch.bfloat16).float().numpy().astype(np.float64)
+
+
+class Cell:
+    """One-cell cache ([B] sequences of explicit K, V [N_b][H][D], bf16) of a given kind."""
+
+    def __init__(self, Ks, Vs, kind, layout=lkv.LAYOUT_PLANES, group=32):
+        self.B = len(Ks)
+        self.H, self.D = Ks[0].shape[1], Ks[0].shape[2]
+        self.lengths = [k.shape[0] for k in Ks]
+        self.kind, self.layout, self.group = kind, layout, group
+        self.Ks = [_bf16_np(k) for k in Ks]
+        self.Vs = [_bf16_np(v) for v in Vs]
+        per = max(self.lengths) // 16 + 2
+        self.ctx = lkv.Context(1, 1, self.H, self.D, self.B * per, self.B, layout, group_size=group)
+        self.ctx.plan([kind])
+        self.ws = torch.zeros(self.ctx.workspace_bytes(), dtype=torch.uint8, device="cuda")
+        self.ctx.bind(self.ws)
+        self.bt = torch.arange(self.B * per, dtype=torch.int32, device="cuda").view(self.B, per)
+        for b in range(self.B):
+            N = self.lengths[b]
+            k = torch.tensor(self.Ks[b], dtype=torch.float32).to(torch.bfloat16).view(1, N, self.H, self.D)
+            v = torch.tensor(self.Vs[b], dtype=torch.float32).to(torch.bfloat16).view(1, N, self.H, self.D)
+            lens = torch.zeros(1, dtype=torch.int32, device="cuda")
+            slots = torch.tensor([b], dtype=torch.int32, device="cuda")
+            self.ctx.append(k.cuda().contiguous(), v.cuda().contiguous(), self.bt[b:b + 1].contiguous(), lens,
+                            cell=(0, 0), seq_slots=slots)
+        self.lens = torch.tensor(self.lengths, dtype=torch.int32, device="cuda")
+        torch.cuda.synchronize()
+
+    def decode(self, q, tau, sm_scale=None, n_split=0):
+        """q: float32 [B][H][D] numpy. Returns (out fp32 [B][H][D], mask words [B][H][W]) on the host."""
+        qd = torch.tensor(np.asarray(q, dtype=np.float32)).cuda().contiguous()
+        out, sm = self.ctx.decode(qd, self.bt, self.lens, max(self.lengths), tau, sm_scale=sm_scale, cell=(0, 0),
+                                  sel_mask=True, n_split=n_split)
+        torch.cuda.synchronize()
+        return out.cpu().numpy(), sm.cpu().numpy()
+
+    def check(self, q, tau, label, sm_scale=None, n_split=0):
+        """Every row against the oracle; returns (GPU outputs, masks, max rel err, selected count)."""
+        sig = float(np.float32(1.0 / math.sqrt(self.D))) if sm_scale is None else float(np.float32(sm_scale))
+        out, sm = self.decode(q, tau, sm_scale=sig, n_split=n_split)
+        kind = "kivi4" if self.layout == lkv.LAYOUT_KIVI4 else self.kind
+        worst, n_sel = 0.0, 0
+        for b in range(self.B):
+            N = self.lengths[b]
+            n_q = self.group * (N // self.group)
+            for h in range(self.H):
+                qv = np.asarray(q[b, h], np.float64)
+                K, V = self.Ks[b][:, h], self.Vs[b][:, h]
+                o_ref, sel_ref, phat = O.decode_row(qv, K, V, kind, tau, sig, group=self.group)
+                sel = sel_bits_from_mask(sm[b, h], n_q)
+                tag = f"{label} b={b} h={h} tau={tau}"
+                if kind == "kivi4" or (kind == O.KIND_Q4 and tau == 0.0):
+                    assert sel.all(), tag
+                elif kind == O.KIND_Q2 or tau > 1.0:
+                    assert not sel.any(), tag
+                else:
+                    excused = np.abs(phat[:n_q] - tau) <= TIE
+                    bad = (sel != sel_ref) & ~excused
+                    assert not bad.any(), f"{tag}: selection differs at {np.flatnonzero(bad)[:10]}"
+                    if (sel != sel_ref).any():
+                        o_ref, _, _ = O.decode_row(qv, K, V, kind, tau, sig, sel_override=sel, group=self.group)
+                    n_sel += int(sel.sum())
+                err = rel_err(out[b, h], o_ref)
+                assert np.isfinite(out[b, h]).all(), f"{tag}: non-finite output"
+                assert err <= TOL, f"{tag}: rel err {err:.3e}"
+                worst = max(worst, err)
+        return out, sm, worst, n_sel
+
+
+REGIMES = [(lkv.CELL_Q4, lkv.LAYOUT_PLANES, 0.0), (lkv.CELL_Q4, lkv.LAYOUT_PLANES, 0.01),
+           (lkv.CELL_Q4, lkv.LAYOUT_PLANES, 1.1), (lkv.CELL_Q2, lkv.LAYOUT_PLANES, 0.01),
+           (lkv.CELL_Q4, lkv.LAYOUT_KIVI4, 0.01)]
+
+
+def _sweep(Ks, Vs, q, label, group=32, splits=(0,)):
+    for kind, layout, tau in REGIMES:
+        cell = Cell(Ks, Vs, kind, layout, group)
+        for ns in splits:
+            _, _, err, n_sel = cell.check(q, tau, f"{label} kind={kind} layout={layout} split={ns}", n_split=ns)
+            print(f"{label} kind={kind} layout={layout} tau={tau} split={ns}: max rel err {err:.2e}, "
+                  f"selected {n_sel}", flush=True)
+        del cell
+
+
+# --------------------------------------------------------------------------- constant groups
+def _constant_inputs(D, H, group, seed):
+    """K, V per sequence with constant structure at the quantization group's granularity:
+    channels d % 7 == 3 of K are constant inside every group of tokens, tokens 1..2 groups of K
+    are constant per channel (every K coefficient of that group is 0), V slices of tokens
+    t % 5 == 1 are constant, tokens of the third group are one constant per token, and head 1
+    of every sequence has one constant V vector for every token."""
+    rng = np.random.default_rng(seed)
+    Ks, Vs = [], []
+    for N in LENGTHS:
+        K = rng.standard_normal((N, H, D)) * 1.5
+        V = rng.standard_normal((N, H, D))
+        for g0 in range(0, N - N % group, group):
+            K[g0:g0 + group, :, 3::7] = rng.standard_normal((1, H, len(range(3, D, 7)))) * 2.0
+        if N >= 2 * group:
+            K[group:2 * group] = rng.standard_normal((1, H, D))
+        for t in range(1, N, 5):
+            for e in range(D // group):
+                V[t, :, e * group:(e + 1) * group] = rng.standard_normal((H, 1))
+        if N >= 3 * group:
+            V[2 * group:3 * group] = rng.standard_normal((group, H, 1))
+        V[:, 1, :] = rng.standard_normal(D)[None, :] * 3.0
+        Ks.append(K)
+        Vs.append(V)
+    q = rng.standard_normal((len(LENGTHS), H, D)) * 2.0
+    return Ks, Vs, q.astype(np.float32)
+
+
+@pytest.mark.parametrize("group", [32, 64])
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_gpu_constant_groups(D, group):
+    _need_gpu()
+    Ks, Vs, q = _constant_inputs(D, 2, group, seed=100 + D + group)
+    _sweep(Ks, Vs, q, f"const D={D} G={group}", group=group, splits=(0, 3))
+    # P7: head 1 reads one constant V vector, so every output of it is that vector
+    cell = Cell(Ks, Vs, lkv.CELL_Q4, group=group)
+    out, _ = cell.decode(q, 0.01)
+    for b in range(len(LENGTHS)):
+        v0 = cell.Vs[b][0, 1]
+        assert rel_err(out[b, 1], v0) <= 1e-6, f"constant V b={b}"
+
+
+# --------------------------------------------------------------------------- power-of-two scaling
+@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("k", [-3, 4])
+def test_gpu_power_of_two_scaling(D, k):
+    """P8 on the GPU: bitwise 2^k scaling of the output with V, bitwise invariance of selection
+    and output under (K x 2^k, sigma x 2^-k), each case also against the oracle."""
+    _need_gpu()
+    rng = np.random.default_rng(7 + D)
+    H = 2
+    Ks = [rng.standard_normal((N, H, D)) for N in LENGTHS]
+    Vs = [rng.standard_normal((N, H, D)) for N in LENGTHS]
+    q = (rng.standard_normal((len(LENGTHS), H, D)) * 1.5).astype(np.float32)
+    sig = float(np.float32(1.0 / math.sqrt(D)))
+    for kind, layout, tau in REGIMES:
+        base = Cell(Ks, Vs, kind, layout)
+        o0, m0, _, _ = base.check(q, tau, f"pow2 base D={D}")
+        del base
+        vs = Cell(Ks, [v * 2.0 ** k for v in Vs], kind, layout)
+        o1, m1, _, _ = vs.check(q, tau, f"pow2 V x 2^{k} D={D}")
+        del vs
+        assert np.array_equal(m1, m0), "V scaling changed the selection"
+        assert np.array_equal(o1, (o0.astype(np.float64) * 2.0 ** k).astype(np.float32)), \
+            f"V x 2^{k}: output not scaled exactly (kind={kind} layout={layout} tau={tau})"
+        ks = Cell([x * 2.0 ** k for x in Ks], Vs, kind, layout)
+        o2, m2, _, _ = ks.check(q, tau, f"pow2 K x 2^{k} D={D}", sm_scale=sig * 2.0 ** -k)
+        del ks
+        assert np.array_equal(m2, m0), f"K x 2^{k}, sigma x 2^-{k}: selection changed"
+        assert np.array_equal(o2, o0), f"K x 2^{k}, sigma x 2^-{k}: output changed (kind={kind} tau={tau})"
+    print(f"pow2 D={D} k={k}: bitwise", flush=True)
+
+
+# --------------------------------------------------------------------------- large zero points
+@pytest.mark.parametrize("group", [32, 64])
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_gpu_large_zero_points(D, group):
+    """K channels around +100 and -250 and V slices around -300 or +1000, spread about 1:
+    zero points hundreds of times the scale."""
+    _need_gpu()
+    rng = np.random.default_rng(31 + D)
+    H = 2
+    Ks, Vs = [], []
+    for N in LENGTHS:
+        K = rng.standard_normal((N, H, D))
+        K[:, :, 1::9] += 100.0
+        K[:, :, 4::13] -= 250.0
+        V = rng.standard_normal((N, H, D))
+        V[:, 0, :group] -= 300.0
+        V[:, 1, D - group:] += 1000.0
+        Ks.append(K)
+        Vs.append(V)
+    q = (rng.standard_normal((len(LENGTHS), H, D)) * 2.0).astype(np.float32)
+    _sweep(Ks, Vs, q, f"zero-point D={D} G={group}", group=group, splits=(0, 2))
+
+
+# --------------------------------------------------------------------------- range bound and heavy tails
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_gpu_values_near_range_bound(D):
+    """Values up to |x| = 3e4: V channels uniform in [-3e4, 3e4]; K channels of magnitude
+    2e4-3e4 met by query components near 1e-4 (scores of order one); and a head whose scores
+    are large, so the softmax is nearly one-hot."""
+    _need_gpu()
+    rng = np.random.default_rng(77 + D)
+    H = 2
+    Ks, Vs = [], []
+    for N in LENGTHS:
+        K = rng.standard_normal((N, H, D))
+        K[:, 0, ::8] = rng.uniform(2e4, 3e4, size=(N, len(range(0, D, 8)))) * rng.choice([-1, 1], size=(1, len(range(0, D, 8))))
+        K[:, 1] *= 40.0
+        V = rng.standard_normal((N, H, D)) * 50.0
+        V[:, :, ::4] = rng.uniform(-3e4, 3e4, size=(N, H, len(range(0, D, 4))))
+        Ks.append(K)
+        Vs.append(V)
+    q = rng.standard_normal((len(LENGTHS), H, D))
+    q[:, 0, ::8] = rng.standard_normal((len(LENGTHS), len(range(0, D, 8)))) * 1e-4
+    _sweep(Ks, Vs, q.astype(np.float32), f"range D={D}", splits=(0, 3))
+
+
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_gpu_heavy_tails(D):
+    """Student-t (2 degrees of freedom) K and V clipped to the 3e4 bound: groups whose range is
+    set by one far value, with most codes at 0 or 1."""
+    _need_gpu()
+    rng = np.random.default_rng(191 + D)
+    H = 2
+    Ks = [np.clip(rng.standard_t(2.0, size=(N, H, D)), -3e4, 3e4) for N in LENGTHS]
+    Vs = [np.clip(rng.standard_t(2.0, size=(N, H, D)), -3e4, 3e4) for N in LENGTHS]
+    q = (rng.standard_normal((len(LENGTHS), H, D)) * 2.0).astype(np.float32)
+    _sweep(Ks, Vs, q, f"t2 D={D}", splits=(0, 2))

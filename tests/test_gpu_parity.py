@@ -29,18 +29,24 @@ def _need_gpu():
         pytest.skip("no GPU")
 
 
-def check_row(wl: Workload, out, sm, q, cell, b, h, tau, n_tokens, label=""):
-    """Compare one row of a decode call with the oracle. Returns the relative error."""
+def check_row(wl: Workload, out, sm, q, cell, b, h, tau, n_tokens, label="", inputs=None):
+    """Compare one row of a decode call with the oracle. Returns the relative error.
+    inputs: optional (K, V, qh) of the row's storage (qh: the oracle's quantized history, or
+    None), so that one row can be checked at several tau without drawing it again."""
     cfg = wl.cfg
     st = O.storage_cell(wl.plan.reshape(cfg.n_loops, cfg.n_layers), cell)
     kind = O.target_kind(wl.plan.reshape(cfg.n_loops, cfg.n_layers), cell)
     if wl.layout == lkv.LAYOUT_KIVI4:
         kind = "kivi4"
-    _, _, K, V = oracle_row_inputs(cfg, st, b, kv_head(cfg, h), n_tokens, wl.factors)
+    if inputs is None:
+        _, _, K, V = oracle_row_inputs(cfg, st, b, kv_head(cfg, h), n_tokens, wl.factors)
+        qh = None
+    else:
+        K, V, qh = inputs
     qv = q[cell, b, h].float().cpu().numpy().astype(np.float64)
     sig = np.float32(1.0 / math.sqrt(cfg.head_dim))
     G = cfg.group
-    o_ref, sel_ref, phat = O.decode_row(qv, K, V, kind, tau, float(sig), group=G)
+    o_ref, sel_ref, phat = O.decode_row(qv, K, V, kind, tau, float(sig), qh=qh, group=G)
     n_q = G * (n_tokens // G)
     o_gpu = out[cell, b, h].float().cpu().numpy()
     sel_gpu = sel_bits_from_mask(sm[cell, b, h].cpu().numpy(), n_q)
@@ -53,7 +59,7 @@ def check_row(wl: Workload, out, sm, q, cell, b, h, tau, n_tokens, label=""):
         bad = (sel_gpu != sel_ref) & ~excused
         assert not bad.any(), f"{label}: selection differs at {np.flatnonzero(bad)[:10]}"
         if (sel_gpu != sel_ref).any():
-            o_ref, _, _ = O.decode_row(qv, K, V, kind, tau, float(sig), sel_override=sel_gpu, group=G)
+            o_ref, _, _ = O.decode_row(qv, K, V, kind, tau, float(sig), qh=qh, sel_override=sel_gpu, group=G)
     err = rel_err(o_gpu, o_ref)
     assert err <= TOL, f"{label}: rel err {err:.3e}"
     return err

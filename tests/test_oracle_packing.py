@@ -102,3 +102,39 @@ def test_pack_roundtrip(D, layout, bits, group):
         vs, vz = _meta(vm)
         assert np.array_equal(vs.reshape(D // group, 16).T, qh["vs"][t0:t0 + 16])
         assert np.array_equal(vz.reshape(D // group, 16).T, qh["vz"][t0:t0 + 16])
+
+
+def _pending_by_appends(K_bits, V_bits, group):
+    """Token-by-token append model: each token enters the pending buffer at slot t mod group; when
+    a group's last token arrives the group leaves for the quantizer and the buffer empties.
+    Returns (position of the first pending token, pending K, pending V) after all N tokens."""
+    pend_k, pend_v, first = [], [], 0
+    for t in range(K_bits.shape[0]):
+        assert len(pend_k) == t % group          # the slot a token takes is its position mod group
+        pend_k.append(K_bits[t])
+        pend_v.append(V_bits[t])
+        if len(pend_k) == group:
+            pend_k, pend_v, first = [], [], t + 1
+    D = K_bits.shape[1]
+    mk = lambda rows: np.array(rows, dtype=K_bits.dtype).reshape(len(rows), D)
+    return first, mk(pend_k), mk(pend_v)
+
+
+@pytest.mark.parametrize("group", [32, 64])
+def test_tail_tokens_match_token_by_token_appends(group):
+    """The tail (exact bf16 tokens not yet quantized) equals what a token-by-token append leaves
+    pending, for lengths around group boundaries; it is shorter than a group, empty exactly at
+    multiples of it, and together with the quantized prefix covers the history."""
+    rng = np.random.default_rng(3)
+    D = group
+    for N in [0, 1, group - 1, group, group + 1, 2 * group - 1, 2 * group, 5 * group + 7]:
+        kb = rng.integers(0, 1 << 16, size=(N, D), dtype=np.uint64).astype(np.uint16)
+        vb = rng.integers(0, 1 << 16, size=(N, D), dtype=np.uint64).astype(np.uint16)
+        first, tk, tv = O.tail_tokens(kb, vb, group)
+        want_first, want_k, want_v = _pending_by_appends(kb, vb, group)
+        assert first == want_first
+        assert np.array_equal(tk, want_k) and np.array_equal(tv, want_v)
+        assert len(tk) < group and (len(tk) == 0) == (N % group == 0)
+        if N:
+            qh = O.quantize_history(kb.astype(np.float64), vb.astype(np.float64), 4, group)
+            assert qh["n_q"] == first and qh["n_q"] + len(tk) == N

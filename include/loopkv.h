@@ -112,7 +112,8 @@ typedef struct {
   int32_t group_size;        /* quantization group G: 32 (the default reading) or 64 */
   int32_t block_tokens;      /* tokens per page of the block table: 16 or 32 */
   int32_t num_blocks;        /* physical pages in each storing cell's pool; a pool (num_blocks x
-                                block_tokens/16 x KV heads x 20*head_dim bytes) stays below 4 GiB */
+                                block_tokens/16 x KV heads x 20*head_dim bytes) stays below 1 TiB
+                                (pools of 4 GiB or more are read with 64-bit record offsets) */
   int32_t max_seqs;          /* sequence slots (tail buffers) */
   int32_t layout;            /* loopkv_layout; KIVI4 requires an all-4-bit plan */
   int32_t n_kv_heads;        /* KV heads (0: = n_heads, MHA); divides n_heads. Query head h

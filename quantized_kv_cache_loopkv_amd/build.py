@@ -45,15 +45,22 @@ def _run(cmd, verbose):
 
 
 def build_loopkv(verbose: bool = False) -> str:
+    """Compile the units in parallel (decode.hip twice: 32-bit and 64-bit record offsets), link."""
+    from concurrent.futures import ThreadPoolExecutor
     os.makedirs(BUILD, exist_ok=True)
     hipcc = _hipcc()
-    objs = []
-    units = [("runtime.cpp", []), ("planner.cpp", []), ("append.hip", ["-ffp-contract=off"]), ("decode.hip", [])]
-    for src, extra in units:
-        obj = os.path.join(BUILD, src.replace(".", "_") + ".o")
-        lang = ["-x", "hip"]
-        _run([hipcc, *COMMON, *extra, *lang, "-c", os.path.join(CSRC, src), "-o", obj], verbose)
+    units = [("runtime.cpp", [], "runtime"), ("planner.cpp", [], "planner"),
+             ("append.hip", ["-ffp-contract=off"], "append"), ("decode.hip", [], "decode"),
+             ("decode.hip", ["-DLKV_DECODE_BIG=1"], "decode_big")]
+    cmds, objs = [], []
+    for src, extra, name in units:
+        obj = os.path.join(BUILD, name + ".o")
+        cmds.append([hipcc, *COMMON, *extra, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
+    jobs = max(1, min(len(cmds), int(os.environ.get("MAX_JOBS", "0")) or (os.cpu_count() or 1)))
+    with ThreadPoolExecutor(jobs) as ex:
+        for f in [ex.submit(_run, c, verbose) for c in cmds]:
+            f.result()
     out = os.path.join(PKG, "libloopkv.so")
     tmp = out + ".tmp"
     _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs], verbose)

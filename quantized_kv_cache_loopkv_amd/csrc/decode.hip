@@ -226,14 +226,20 @@ __device__ inline uint32_t fixed16_lo(float a, float scl) {
   return __float_as_uint(fmaf(a, scl, 8388608.0f));
 }
 
-struct Row {
+// BIG: the pool may exceed 4 GiB. Otherwise a record's byte offset fits 32 bits and a load
+// takes the uniform pool base plus a 32-bit lane offset (the scalar-base form, no 64-bit
+// address arithmetic); with BIG each lane forms a 64-bit address.
+template <bool BIG>
+struct RowT {
   const uint8_t* pool;     // pool base of the storage cell
   const uint32_t* boff;    // per logical block: record offset in 256-byte units (in LDS)
   const uint16_t* tail;    // tail of (slot, head): [2][32][D] bf16
   int N, n_q, n_groups;
-  // Byte `off` of logical block j's record: the pool is under 4 GiB (checked at create), so
-  // the offset is 32-bit and the load takes the uniform pool base plus a 32-bit lane offset.
-  __device__ inline const uint8_t* at(int j, uint32_t off) const { return pool + ((boff[j] << 8) + off); }
+  // Byte `off` of logical block j's record.
+  __device__ inline const uint8_t* at(int j, uint32_t off) const {
+    if constexpr (BIG) return pool + (((size_t)boff[j] << 8) + off);
+    else return pool + ((boff[j] << 8) + off);
+  }
   __device__ inline const uint8_t* rec_ptr(int j) const { return at(j, 0u); }
 };
 
@@ -330,7 +336,8 @@ struct KStep {
 
   // groups: the group read by each of the step's GPS slots (an empty slot repeats a valid
   // group of the step, so every load is in bounds and the kernel needs no per-lane branch).
-  __device__ static inline void load(const Row& r, const int* groups, int lane, Buf& b) {
+  template <class RW>
+  __device__ static inline void load(const RW& r, const int* groups, int lane, Buf& b) {
     int gsub, blk, quad, cp;
     role(lane, gsub, blk, quad, cp);
     const int g = groups[gsub];
@@ -562,7 +569,8 @@ struct VStep {
   };
 
   // Blocks past the row's end repeat the step's first block (in bounds; their weights are 0).
-  __device__ static inline void load(const Row& r, int jbase, int nb, int lane, Buf& b) {
+  template <class RW>
+  __device__ static inline void load(const RW& r, int jbase, int nb, int lane, Buf& b) {
     int jm = jbase + lane / (4 * G::NE);
     const int p = (lane / G::NE) % 4, e = lane % G::NE;
     jm = jm < nb ? jm : jbase;
@@ -698,8 +706,8 @@ struct VStep {
 // bits, the rest at the bucket midpoint) in the value-lane layout of the coarse step
 // (4 blocks per 64 lanes, D/16 channels per lane), constants included. Runs only when a
 // correction would cancel most of the row's weight.
-template <int D, int GS>
-__device__ void exact_v_pass(const Row& r, const float* weights, const uint32_t* selm, int lane, int w,
+template <int D, int GS, class RW>
+__device__ void exact_v_pass(const RW& r, const float* weights, const uint32_t* selm, int lane, int w,
                              float* acc) {
   using GC = Geo<D, MODE_COARSE, GS>;
   constexpr int VCH = GC::VCH;
@@ -778,8 +786,8 @@ __device__ inline void split_range(int n_chunks, int n_split, int split, int& cb
 // SKIP (with SPARSE, PH_ROW): the token-skipping ablation. The same coarse pass and
 // selection, but the values are not streamed and the unselected quantized tokens leave the
 // attention: the softmax runs over the selected tokens (at 4 bits) and the tail only.
-template <int D, int GS, int MODE, bool SPARSE, int PH, bool SKIP = false>
-__device__ __forceinline__ void row_body(const DecodeArgs& a, const Row& r, const Smem& sm, size_t orow, int split) {
+template <int D, int GS, int MODE, bool SPARSE, int PH, bool SKIP = false, class RW>
+__device__ __forceinline__ void row_body(const DecodeArgs& a, const RW& r, const Smem& sm, size_t orow, int split) {
   using G = Geo<D, MODE, GS>;
   using KS = KStep<D, MODE, false, GS>;
   using VS = VStep<D, MODE, GS>;
@@ -1228,7 +1236,7 @@ constexpr int decode_waves_per_simd() {
   return (D == 256 && (VAR == VAR_DENSE || VAR == VAR_KIVI)) ? 2 : kWavesPerSimd;
 }
 
-template <int D, int GS, int VAR, int PH>
+template <int D, int GS, int VAR, int PH, bool BIG>
 __global__ void __launch_bounds__(kThreads, (decode_waves_per_simd<D, VAR>())) k_decode(DecodeArgs a) {
   extern __shared__ float smem[];
   // Rows are (cell, sequence, query head). PH_PART: workgroup (row, split), the splits of a
@@ -1282,7 +1290,7 @@ __global__ void __launch_bounds__(kThreads, (decode_waves_per_simd<D, VAR>())) k
     return;
   }
 
-  Row r;
+  RowT<BIG> r;
   r.pool = a.ws + cell.pool_off;
   r.boff = sm.boff;
   const int slot = a.seq_slots ? a.seq_slots[b] : b;
@@ -1333,14 +1341,23 @@ __global__ void __launch_bounds__(kThreads, (decode_waves_per_simd<D, VAR>())) k
   }
 }
 
+// Two objects are built from this file: records addressed with 32-bit offsets (pools below
+// 4 GiB) and with 64-bit ones (LKV_DECODE_BIG=1); the host picks one per context.
+#ifndef LKV_DECODE_BIG
+#define LKV_DECODE_BIG 0
+#endif
+constexpr bool kBig = LKV_DECODE_BIG != 0;
+
+#if !LKV_DECODE_BIG
 size_t decode_lds_bytes(int max_len, int head_dim) { return decode_lds_floats(max_len, head_dim) * 4; }
+#endif
 
 template <int D, int GS, int VAR, int PH>
 static void set_lds_attr() {
   static bool attr_set = false;
   if (!attr_set) {
-    (void)hipFuncSetAttribute((const void*)k_decode<D, GS, VAR, PH>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                              160 * 1024);
+    (void)hipFuncSetAttribute((const void*)k_decode<D, GS, VAR, PH, kBig>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     attr_set = true;
   }
 }
@@ -1348,7 +1365,7 @@ static void set_lds_attr() {
 template <int D, int GS, int VAR, int PH>
 static void launch_phase(const DecodeArgs& a, size_t grid, size_t lds, hipStream_t stream) {
   set_lds_attr<D, GS, VAR, PH>();
-  hipLaunchKernelGGL((k_decode<D, GS, VAR, PH>), dim3((unsigned)grid), dim3(kThreads), lds, stream, a);
+  hipLaunchKernelGGL((k_decode<D, GS, VAR, PH, kBig>), dim3((unsigned)grid), dim3(kThreads), lds, stream, a);
 }
 
 // Sets the LDS attribute of every decode kernel of a shape, so that a graph capture that
@@ -1376,7 +1393,11 @@ static void prepare_d(int group) {
   else prepare_dg<D, 32>();
 }
 
-void prepare_decode(int head_dim, int group) {
+#if LKV_DECODE_BIG
+void prepare_decode_big(int head_dim, int group) {
+#else
+void prepare_decode_small(int head_dim, int group) {
+#endif
   if (head_dim == 128) prepare_d<128>(group);
   else if (head_dim == 256) prepare_d<256>(group);
   else prepare_d<64>(group);
@@ -1418,10 +1439,14 @@ static void launch_d(const DecodeArgs& a, size_t rows, size_t lds, hipStream_t s
   else launch_dg<D, 32>(a, rows, lds, stream);
 }
 
-hipError_t launch_decode(const DecodeArgs& a, int head_dim, hipStream_t stream) {
+#if LKV_DECODE_BIG
+hipError_t launch_decode_big(const DecodeArgs& a, int head_dim, hipStream_t stream) {
+#else
+hipError_t launch_decode_small(const DecodeArgs& a, int head_dim, hipStream_t stream) {
+#endif
   const size_t rows = (size_t)a.n_cells * a.n_seqs * a.n_heads;
   if (rows == 0) return hipSuccess;
-  const size_t lds = decode_lds_bytes(a.max_len, head_dim);
+  const size_t lds = decode_lds_floats(a.max_len, head_dim) * 4;
   if (head_dim == 128) launch_d<128>(a, rows, lds, stream);
   else if (head_dim == 256) launch_d<256>(a, rows, lds, stream);
   else launch_d<64>(a, rows, lds, stream);

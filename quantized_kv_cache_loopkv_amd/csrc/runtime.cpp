@@ -21,15 +21,20 @@
 
 namespace lkv {
 hipError_t launch_append(const AppendArgs& a, int head_dim, hipStream_t stream);
-hipError_t launch_decode(const DecodeArgs& a, int head_dim, hipStream_t stream);
+// decode.hip is built twice: records addressed by 32-bit offsets (every pool below 4 GiB) and
+// by 64-bit ones
+hipError_t launch_decode_small(const DecodeArgs& a, int head_dim, hipStream_t stream);
+hipError_t launch_decode_big(const DecodeArgs& a, int head_dim, hipStream_t stream);
+void prepare_decode_small(int head_dim, int group);
+void prepare_decode_big(int head_dim, int group);
 hipError_t launch_advance_lens(int32_t* before, int32_t* after, int n, hipStream_t stream);
-void prepare_decode(int head_dim, int group);
 size_t decode_lds_bytes(int max_len, int head_dim);
 }  // namespace lkv
 
 struct loopkv_ctx {
   loopkv_config cfg;
   int kvh = 0;                    // KV heads (cfg.n_kv_heads, or n_heads when 0)
+  bool big = false;               // a pool reaches 4 GiB: the decode addresses records in 64 bits
   bool has_plan = false;
   std::vector<uint8_t> kinds;     // per cell, loopkv_cell_kind
   std::vector<int> storage;       // per cell: cell whose cache it reads
@@ -132,10 +137,10 @@ loopkv_status loopkv_create(const loopkv_config* cfg, loopkv_ctx** out) {
   if (cfg->block_tokens != 16 && cfg->block_tokens != 32)
     return fail(LOOPKV_ERR_UNSUPPORTED, "block_tokens %d not supported (16 or 32)", cfg->block_tokens);
   const uint64_t recs = (uint64_t)cfg->num_blocks * (uint64_t)(cfg->block_tokens / lkv::kBlock);
-  if (recs * (uint64_t)kvh * lkv::record_bytes(lkv::KIND_Q4, cfg->head_dim, cfg->group_size) > 0xFFFFFFFFull)
-    return fail(LOOPKV_ERR_UNSUPPORTED,
-                "a cell's pool (num_blocks x block_tokens/16 x KV heads x %d-byte records) must stay below 4 GiB",
-                lkv::record_bytes(lkv::KIND_Q4, cfg->head_dim, cfg->group_size));
+  const uint64_t pool_bytes = recs * (uint64_t)kvh * lkv::record_bytes(lkv::KIND_Q4, cfg->head_dim, cfg->group_size);
+  if (pool_bytes >= (1ull << 40))   // record offsets are 32-bit counts of 256-byte units
+    return fail(LOOPKV_ERR_UNSUPPORTED, "a cell's pool of %llu bytes reaches 1 TiB",
+                (unsigned long long)pool_bytes);
   if ((long long)cfg->n_loops * cfg->n_layers > lkv::kMaxCells)
     return fail(LOOPKV_ERR_UNSUPPORTED, "at most %d cells", lkv::kMaxCells);
   if (cfg->layout != LOOPKV_LAYOUT_PLANES && cfg->layout != LOOPKV_LAYOUT_KIVI4)
@@ -143,6 +148,7 @@ loopkv_status loopkv_create(const loopkv_config* cfg, loopkv_ctx** out) {
   loopkv_ctx* c = new loopkv_ctx();
   c->cfg = *cfg;
   c->kvh = kvh;
+  c->big = pool_bytes > 0xFFFFFFFFull;
   *out = c;
   return ok();
 }
@@ -343,12 +349,6 @@ loopkv_status decode_common(loopkv_ctx* c, hipStream_t stream, int32_t loop, int
   a.sm_scale = sm_scale;
   a.n_split = n_split;
   a.skip = skip ? 1 : 0;
-  if (n_split > 0) {
-    const size_t rows = (size_t)count * n_seqs * c->cfg.n_heads;
-    a.split_row_stride = (int32_t)lkv::split_row_stride(max_len);
-    a.part = static_cast<float*>(scratch);
-    a.part_scores = a.part + lkv::split_part_floats(rows, n_split, c->cfg.head_dim);
-  }
   for (int i = 0; i < count; ++i) {
     const int st = c->storage[first + i];
     a.cells[i].pool_off = c->pool_off[st];
@@ -357,7 +357,14 @@ loopkv_status decode_common(loopkv_ctx* c, hipStream_t stream, int32_t loop, int
   }
   s = check_device();
   if (s != LOOPKV_OK) return s;
-  hipError_t e = lkv::launch_decode(a, c->cfg.head_dim, stream);
+  if (n_split > 0) {
+    const size_t rows = (size_t)count * n_seqs * c->cfg.n_heads;
+    a.split_row_stride = (int32_t)lkv::split_row_stride(max_len);
+    a.part = static_cast<float*>(scratch);
+    a.part_scores = a.part + lkv::split_part_floats(rows, n_split, c->cfg.head_dim);
+  }
+  hipError_t e = c->big ? lkv::launch_decode_big(a, c->cfg.head_dim, stream)
+                         : lkv::launch_decode_small(a, c->cfg.head_dim, stream);
   if (e != hipSuccess) return fail(LOOPKV_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
   return ok();
 }
@@ -493,7 +500,8 @@ loopkv_status loopkv_step_graph_create(loopkv_ctx* c, const void* k, const void*
   // every check passed: capture on a private stream (default priority)
   s = check_device();   // before the capture: no property query inside it
   if (s != LOOPKV_OK) return s;
-  lkv::prepare_decode(c->cfg.head_dim, c->cfg.group_size);
+  if (c->big) lkv::prepare_decode_big(c->cfg.head_dim, c->cfg.group_size);
+  else lkv::prepare_decode_small(c->cfg.head_dim, c->cfg.group_size);
   hipStream_t cap = nullptr;
   hipError_t e = hipStreamCreateWithFlags(&cap, hipStreamNonBlocking);
   if (e != hipSuccess) return fail(LOOPKV_ERR_HIP, "capture stream: %s", hipGetErrorString(e));

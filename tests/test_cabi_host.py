@@ -61,13 +61,14 @@ def _create(**kw):
     (dict(group_size=48), B.ERR_UNSUPPORTED), (dict(group_size=128), B.ERR_UNSUPPORTED),
     (dict(group_size=16), B.ERR_UNSUPPORTED), (dict(block_tokens=8), B.ERR_UNSUPPORTED),
     (dict(block_tokens=64), B.ERR_UNSUPPORTED), (dict(block_tokens=0), B.ERR_UNSUPPORTED),
-    # 32-token pages: 52429 x 2 x 16 x 2560 B > 2^32 - 1
-    (dict(block_tokens=32, num_blocks=52429), B.ERR_UNSUPPORTED),
+    # 32-token pages: 13421773 x 2 x 16 x 2560 B reaches 1 TiB
+    (dict(block_tokens=32, num_blocks=13421773), B.ERR_UNSUPPORTED),
     (dict(n_loops=0), B.ERR_INVALID_ARG), (dict(n_heads=0), B.ERR_INVALID_ARG),
     (dict(num_blocks=0), B.ERR_INVALID_ARG), (dict(max_seqs=0), B.ERR_INVALID_ARG),
     (dict(n_loops=6, n_layers=24), B.ERR_UNSUPPORTED), (dict(layout=5), B.ERR_INVALID_ARG),
-    # a cell's pool must stay below 4 GiB: 104858 x 16 x 2560 B > 2^32 - 1
-    (dict(num_blocks=104858), B.ERR_UNSUPPORTED),
+    # a cell's pool must stay below 1 TiB (record offsets count 256-byte units in 32 bits):
+    # 26843546 x 16 x 2560 B >= 2^40
+    (dict(num_blocks=26843546), B.ERR_UNSUPPORTED),
     (dict(n_kv_heads=3), B.ERR_INVALID_ARG), (dict(n_kv_heads=-1), B.ERR_INVALID_ARG),
     (dict(n_kv_heads=32), B.ERR_INVALID_ARG),
 ])
@@ -77,13 +78,14 @@ def test_create_rejects(kw, status):
     assert lkv.lib().loopkv_last_error().decode()
 
 
-def test_create_accepts_pool_just_under_4gib():
-    s, h = _create(num_blocks=104857)   # 104857 x 16 x 2560 B = 2^32 - 2560
-    assert s == B.OK and h.value
-    lkv.lib().loopkv_destroy(h)
-    s, h = _create(num_blocks=52428, block_tokens=32)   # 52428 x 2 x 16 x 2560 B = 2^32 - 65536
-    assert s == B.OK and h.value
-    lkv.lib().loopkv_destroy(h)
+def test_create_accepts_pools_above_4gib():
+    """Pools of 4 GiB and more are addressed with 64-bit offsets; 1 TiB is the limit."""
+    for kw in (dict(num_blocks=104857), dict(num_blocks=104858), dict(num_blocks=131072),
+               dict(num_blocks=52429, block_tokens=32), dict(num_blocks=26843545),
+               dict(num_blocks=13421772, block_tokens=32)):
+        s, h = _create(**kw)
+        assert s == B.OK and h.value, kw
+        lkv.lib().loopkv_destroy(h)
 
 
 @pytest.mark.parametrize("D", [64, 128, 256])
@@ -336,10 +338,10 @@ def test_grouped_query_workspace_and_shapes():
     assert mha.workspace_bytes() == 16 * per_head
     assert gqa.workspace_bytes() == 4 * per_head
     assert gqa.kv_heads == 4 and mha.kv_heads == 16
-    s, h = _create(num_blocks=104857 * 4, n_kv_heads=4)   # 4 KV heads: the pool stays under 4 GiB
+    s, h = _create(num_blocks=26843545 * 4, n_kv_heads=4)   # 4 KV heads: the pool stays under 1 TiB
     assert s == B.OK
     lkv.lib().loopkv_destroy(h)
-    s, h = _create(num_blocks=104857 * 4)                 # the same blocks with 16 KV heads do not
+    s, h = _create(num_blocks=26843545 * 4)                 # the same blocks with 16 KV heads do not
     assert s == B.ERR_UNSUPPORTED
 
 

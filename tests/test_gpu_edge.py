@@ -136,7 +136,8 @@ def _constant_inputs(D, H, group, seed):
     channels d % 7 == 3 of K are constant inside every group of tokens, tokens 1..2 groups of K
     are constant per channel (every K coefficient of that group is 0), V slices of tokens
     t % 5 == 1 are constant, tokens of the third group are one constant per token, and head 1
-    of every sequence has one constant V vector for every token."""
+    of every sequence has the same V for every token, constant inside each channel group (so
+    its groups have scale 0 and every value is its zero point exactly)."""
     rng = np.random.default_rng(seed)
     Ks, Vs = [], []
     for N in LENGTHS:
@@ -151,7 +152,7 @@ def _constant_inputs(D, H, group, seed):
                 V[t, :, e * group:(e + 1) * group] = rng.standard_normal((H, 1))
         if N >= 3 * group:
             V[2 * group:3 * group] = rng.standard_normal((group, H, 1))
-        V[:, 1, :] = rng.standard_normal(D)[None, :] * 3.0
+        V[:, 1, :] = np.repeat(rng.standard_normal(D // group) * 3.0, group)[None, :]
         Ks.append(K)
         Vs.append(V)
     q = rng.standard_normal((len(LENGTHS), H, D)) * 2.0
@@ -164,7 +165,8 @@ def test_gpu_constant_groups(D, group):
     _need_gpu()
     Ks, Vs, q = _constant_inputs(D, 2, group, seed=100 + D + group)
     _sweep(Ks, Vs, q, f"const D={D} G={group}", group=group, splits=(0, 3))
-    # P7: head 1 reads one constant V vector, so every output of it is that vector
+    # P7: head 1's values are their zero points (scale 0), the same for every token, so its
+    # output is that vector (up to the fp32 division of equal sums)
     cell = Cell(Ks, Vs, lkv.CELL_Q4, group=group)
     out, _ = cell.decode(q, 0.01)
     for b in range(len(LENGTHS)):

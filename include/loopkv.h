@@ -208,6 +208,28 @@ loopkv_status loopkv_decode_attn_split(loopkv_ctx* ctx, hipStream_t stream, int3
                                        uint32_t* sel_mask, int32_t n_split, void* scratch,
                                        size_t scratch_bytes);
 
+/* Bytes of the fixed device array behind loopkv_decode_attn_split_noalloc (one per GPU). */
+#define LOOPKV_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): loopkv_decode_attn_split with the scratch taken
+ * from a file-scope device array of LOOPKV_NOALLOC_SCRATCH_BYTES bytes inside the library
+ * instead of a caller buffer. Same arguments (without scratch), same kernels, same results.
+ * The library allocates nothing here; each GPU the call runs on holds its own copy of the
+ * array until the process ends (its address is resolved on the first call on a device, which
+ * callers that capture should make once before capturing). Every call on one GPU shares that
+ * GPU's array and overwrites it (no initialization needed): calls that overlap on one GPU
+ * (different streams, or contexts used from several threads) race and must be ordered by the
+ * caller. Errors as loopkv_decode_attn_split, and LOOPKV_ERR_WORKSPACE when the call needs
+ * more than LOOPKV_NOALLOC_SCRATCH_BYTES of scratch (loopkv_split_scratch_bytes tells). */
+loopkv_status loopkv_decode_attn_split_noalloc(loopkv_ctx* ctx, hipStream_t stream, int32_t loop,
+                                               int32_t layer, const void* q, int32_t q_dtype,
+                                               int32_t n_seqs, const int32_t* seq_slots,
+                                               const int32_t* block_table, int32_t bt_stride,
+                                               const int32_t* seq_lens, int32_t max_len, float tau,
+                                               float sm_scale, void* out, int32_t out_dtype,
+                                               uint32_t* sel_mask, int32_t n_split);
+
 /* The token-skipping ablation (the alternative the Abstract's sentence on skipping rejects;
  * not the method): arguments, selection and sel_mask as loopkv_decode_attn, but a 4-bit
  * target's unselected quantized tokens are dropped instead of read at 2 bits: their values

@@ -9,6 +9,7 @@
 // a reuse of the final loop's KV of its layer.
 #include <hip/hip_runtime.h>
 #include <atomic>
+#include <mutex>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -283,13 +284,41 @@ loopkv_status loopkv_append(loopkv_ctx* c, hipStream_t stream, int32_t loop, int
 
 }  // extern "C"
 
+// The split-decode scratch of loopkv_decode_attn_split_noalloc: a fixed array in device
+// memory, one copy per GPU for the life of the process. Host code never uses the name
+// itself (on the host it is a stand-in, not a device address): the device address is
+// resolved once per device and passed to the kernels as the split decode's scratch.
+static __device__ __align__(256) unsigned char scratch[LOOPKV_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch_dev[64] = {};   // device address of `scratch`, per device id
+
+loopkv_status noalloc_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(LOOPKV_ERR_HIP, "no current HIP device: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= 64) return fail(LOOPKV_ERR_UNSUPPORTED, "device id %d above 63", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(LOOPKV_ERR_HIP, "device address of the fixed scratch: %s", hipGetErrorString(e));
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return LOOPKV_OK;
+}
+}  // namespace
+
 namespace {
 // Shared by the one-workgroup-per-row decode (n_split 0) and the split decode.
 loopkv_status decode_common(loopkv_ctx* c, hipStream_t stream, int32_t loop, int32_t layer, const void* q,
                             int32_t q_dtype, int32_t n_seqs, const int32_t* seq_slots, const int32_t* block_table,
                             int32_t bt_stride, const int32_t* seq_lens, int32_t max_len, float tau, float sm_scale,
                             void* out, int32_t out_dtype, uint32_t* sel_mask, int32_t n_split, void* scratch,
-                            size_t scratch_bytes, bool skip) {
+                            size_t scratch_bytes, bool skip, bool fixed_scratch = false) {
   loopkv_status s = check_ready(c);
   if (s != LOOPKV_OK) return s;
   int first, count;
@@ -314,7 +343,7 @@ loopkv_status decode_common(loopkv_ctx* c, hipStream_t stream, int32_t loop, int
   if (n_split != 0) {
     if (n_split < 1 || n_split > LOOPKV_MAX_SPLIT)
       return fail(LOOPKV_ERR_INVALID_ARG, "n_split %d outside [1, %d]", n_split, LOOPKV_MAX_SPLIT);
-    if (n_seqs > 0 && (!scratch || ((uintptr_t)scratch & 15u) != 0))
+    if (n_seqs > 0 && !fixed_scratch && (!scratch || ((uintptr_t)scratch & 15u) != 0))
       return fail(LOOPKV_ERR_WORKSPACE, "split scratch is null or not 16-byte aligned");
     const size_t need = lkv::split_scratch_floats((size_t)count * n_seqs * c->cfg.n_heads, n_split, max_len,
                                                   c->cfg.head_dim) * sizeof(float);
@@ -357,6 +386,10 @@ loopkv_status decode_common(loopkv_ctx* c, hipStream_t stream, int32_t loop, int
   }
   s = check_device();
   if (s != LOOPKV_OK) return s;
+  if (n_split > 0 && fixed_scratch) {   // every host check has passed: now the device address
+    s = noalloc_scratch(&scratch);
+    if (s != LOOPKV_OK) return s;
+  }
   if (n_split > 0) {
     const size_t rows = (size_t)count * n_seqs * c->cfg.n_heads;
     a.split_row_stride = (int32_t)lkv::split_row_stride(max_len);
@@ -415,6 +448,27 @@ loopkv_status loopkv_decode_attn_split(loopkv_ctx* c, hipStream_t stream, int32_
   if (n_split == 0) return fail(LOOPKV_ERR_INVALID_ARG, "n_split %d outside [1, %d]", n_split, LOOPKV_MAX_SPLIT);
   return decode_common(c, stream, loop, layer, q, q_dtype, n_seqs, seq_slots, block_table, bt_stride, seq_lens,
                        max_len, tau, sm_scale, out, out_dtype, sel_mask, n_split, scratch, scratch_bytes, false);
+}
+
+loopkv_status loopkv_decode_attn_split_noalloc(loopkv_ctx* c, hipStream_t stream, int32_t loop, int32_t layer,
+                                               const void* q, int32_t q_dtype, int32_t n_seqs,
+                                               const int32_t* seq_slots, const int32_t* block_table,
+                                               int32_t bt_stride, const int32_t* seq_lens, int32_t max_len,
+                                               float tau, float sm_scale, void* out, int32_t out_dtype,
+                                               uint32_t* sel_mask, int32_t n_split) {
+  if (n_split == 0) return fail(LOOPKV_ERR_INVALID_ARG, "n_split %d outside [1, %d]", n_split, LOOPKV_MAX_SPLIT);
+  size_t need = 0;
+  loopkv_status s = loopkv_split_scratch_bytes(c, loop, layer, n_seqs, max_len, n_split, &need);
+  if (s != LOOPKV_OK) return s;
+  if (need > LOOPKV_NOALLOC_SCRATCH_BYTES)
+    return fail(LOOPKV_ERR_WORKSPACE,
+                "this call needs %zu bytes of split scratch, above the %u-byte fixed array of the "
+                "no-allocation decode (fewer sequences, cells, splits or a shorter max_len fit)",
+                need, (unsigned)LOOPKV_NOALLOC_SCRATCH_BYTES);
+  // the array's device address is resolved inside, after every host check
+  return decode_common(c, stream, loop, layer, q, q_dtype, n_seqs, seq_slots, block_table, bt_stride, seq_lens,
+                       max_len, tau, sm_scale, out, out_dtype, sel_mask, n_split, nullptr,
+                       LOOPKV_NOALLOC_SCRATCH_BYTES, false, true);
 }
 
 }  // extern "C"

@@ -24,10 +24,12 @@ LAYOUT_PLANES, LAYOUT_KIVI4 = 0, 1
 MAX_LEN = 32768
 MAX_CELLS = 128
 MAX_SPLIT = 64
+NOALLOC_SCRATCH_BYTES = 16 << 20
 
 EXPORTED = ["loopkv_create", "loopkv_destroy", "loopkv_plan", "loopkv_workspace_bytes",
             "loopkv_bind_workspace", "loopkv_cell_storage", "loopkv_append", "loopkv_decode_attn",
-            "loopkv_split_scratch_bytes", "loopkv_decode_attn_split", "loopkv_decode_attn_skip", "loopkv_plan_search",
+            "loopkv_split_scratch_bytes", "loopkv_decode_attn_split", "loopkv_decode_attn_split_noalloc",
+            "loopkv_decode_attn_skip", "loopkv_plan_search",
             "loopkv_step_graph_create", "loopkv_step_graph_launch", "loopkv_step_graph_destroy", "loopkv_last_error"]
 
 
@@ -74,6 +76,8 @@ def lib():
     L.loopkv_split_scratch_bytes.argtypes = [vp, i32, i32, i32, i32, i32, ctypes.POINTER(ctypes.c_size_t)]
     L.loopkv_decode_attn_split.argtypes = [vp, vp, i32, i32, vp, i32, i32, vp, vp, i32, vp, i32, f32, f32, vp, i32,
                                            vp, i32, vp, ctypes.c_size_t]
+    L.loopkv_decode_attn_split_noalloc.argtypes = [vp, vp, i32, i32, vp, i32, i32, vp, vp, i32, vp, i32, f32, f32,
+                                                   vp, i32, vp, i32]
     L.loopkv_plan_search.argtypes = [i32, i32, ctypes.POINTER(_CellCost), ctypes.c_double, ctypes.c_int64,
                                      ctypes.POINTER(ctypes.c_uint8), ctypes.POINTER(ctypes.c_double),
                                      ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
@@ -86,7 +90,8 @@ def lib():
     L.loopkv_last_error.argtypes = []
     for name in ["loopkv_create", "loopkv_plan", "loopkv_workspace_bytes", "loopkv_bind_workspace",
                  "loopkv_cell_storage", "loopkv_append", "loopkv_decode_attn", "loopkv_split_scratch_bytes",
-                 "loopkv_decode_attn_split", "loopkv_decode_attn_skip", "loopkv_plan_search",
+                 "loopkv_decode_attn_split", "loopkv_decode_attn_split_noalloc", "loopkv_decode_attn_skip",
+                 "loopkv_plan_search",
                  "loopkv_step_graph_create", "loopkv_step_graph_launch"]:
         getattr(L, name).restype = ctypes.c_int
     _lib = L
@@ -278,11 +283,14 @@ class Context:
     def decode(self, q: torch.Tensor, block_table: torch.Tensor, seq_lens: torch.Tensor, max_len: int,
                tau: float, sm_scale: Optional[float] = None, cell=None, out_dtype=torch.float32,
                out: Optional[torch.Tensor] = None, sel_mask=False, seq_slots: Optional[torch.Tensor] = None,
-               n_split: int = 0, scratch: Optional[torch.Tensor] = None, skip: bool = False):
+               n_split: int = 0, scratch: Optional[torch.Tensor] = None, skip: bool = False,
+               no_alloc: bool = False):
         """q: [cells][n_seqs][H][D] (cell=None) or [n_seqs][H][D]. Returns out (and sel_mask if asked).
         n_split > 0 splits each row over that many workgroups (loopkv_decode_attn_split); scratch is
         then a CUDA tensor of at least split_scratch_bytes() bytes (allocated here if None).
-        skip=True runs the token-skipping ablation (loopkv_decode_attn_skip), not the method."""
+        skip=True runs the token-skipping ablation (loopkv_decode_attn_skip), not the method.
+        no_alloc=True (with n_split > 0) runs loopkv_decode_attn_split_noalloc: the split scratch is
+        the library's fixed device array (NOALLOC_SCRATCH_BYTES), nothing is allocated."""
         loop, layer = self._cell(cell)
         if not q.is_contiguous():
             raise ValueError("q must be contiguous")
@@ -316,12 +324,21 @@ class Context:
             raise ValueError("scratch must be a contiguous CUDA tensor")
         _on_device(self._device(), q=q, out=out, sel_mask=sm, block_table=bt, seq_lens=seq_lens,
                    seq_slots=seq_slots, scratch=scratch)
+        if no_alloc and (skip or not n_split):
+            raise ValueError("no_alloc is the split decode's variant: give n_split > 0")
         if skip:
             if n_split:
                 raise ValueError("the token-skipping ablation runs one workgroup per row (n_split=0)")
             _check(lib().loopkv_decode_attn_skip(self._h, _stream(), loop, layer, _ptr(q), _dtype_code(q), n_seqs,
                                                  _ptr(seq_slots), _ptr(bt), bt_stride, _ptr(seq_lens), int(max_len),
                                                  float(tau), float(sm_scale), _ptr(out), _dtype_code(out), _ptr(sm)))
+        elif n_split and no_alloc:
+            if scratch is not None:
+                raise ValueError("no_alloc takes no scratch")
+            _check(lib().loopkv_decode_attn_split_noalloc(self._h, _stream(), loop, layer, _ptr(q), _dtype_code(q),
+                                                          n_seqs, _ptr(seq_slots), _ptr(bt), bt_stride,
+                                                          _ptr(seq_lens), int(max_len), float(tau), float(sm_scale),
+                                                          _ptr(out), _dtype_code(out), _ptr(sm), int(n_split)))
         elif n_split:
             if scratch is None:
                 scratch = torch.empty(self.split_scratch_bytes(n_seqs, max_len, n_split, cell), dtype=torch.uint8,

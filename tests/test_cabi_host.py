@@ -480,3 +480,37 @@ def test_binding_step_graph_shapes():
         ctx.step_graph(k, k.clone(), q, bt[:1].contiguous(), lens, la, 100, 0.01, out)
     with pytest.raises(ValueError, match="CUDA"):
         ctx.step_graph(k, k.clone(), q, bt, lens, la, 100, 0.01, out)
+
+
+def _decode_noalloc(ctx, **kw):
+    a = dict(loop=-1, layer=-1, q=FAKE_DEV, q_dtype=1, n_seqs=2, slots=None, bt=FAKE_DEV, bt_stride=4,
+             lens=FAKE_DEV, max_len=64, tau=0.01, sm=0.125, out=FAKE_DEV, out_dtype=0, mask=None, n_split=4)
+    a.update(kw)
+    vp = ctypes.c_void_p
+    return lkv.lib().loopkv_decode_attn_split_noalloc(
+        None if ctx is None else ctx._h, None, a["loop"], a["layer"], vp(a["q"]), a["q_dtype"], a["n_seqs"],
+        vp(a["slots"]), vp(a["bt"]), a["bt_stride"], vp(a["lens"]), a["max_len"], a["tau"], a["sm"],
+        vp(a["out"]), a["out_dtype"], vp(a["mask"]), a["n_split"])
+
+
+def test_noalloc_split_decode_validation():
+    """The no-allocation split decode checks every argument on the host, including that the call's
+    scratch fits the fixed array, before it touches the device (its address included)."""
+    assert B.NOALLOC_SCRATCH_BYTES == 16 << 20
+    ctx = _ready_ctx()
+    assert _decode_noalloc(None) == B.ERR_INVALID_ARG
+    assert _decode_noalloc(ctx, n_split=0) == B.ERR_INVALID_ARG
+    assert _decode_noalloc(ctx, n_split=65) == B.ERR_INVALID_ARG
+    assert _decode_noalloc(ctx, max_len=40000) == B.ERR_CAPACITY
+    # 6 cells x 100 sequences x 2 heads x 32768 scores: far above the fixed array
+    assert _decode_noalloc(ctx, n_seqs=100, max_len=32768, bt_stride=2048) == B.ERR_WORKSPACE
+    assert "fixed array" in lkv.lib().loopkv_last_error().decode()
+    need = ctx.split_scratch_bytes(2, 64, 4)
+    assert need <= B.NOALLOC_SCRATCH_BYTES
+    assert _decode_noalloc(ctx, q=0) == B.ERR_INVALID_ARG          # host checks still run
+    assert _decode_noalloc(ctx, bt_stride=3) == B.ERR_CAPACITY
+    assert _decode_noalloc(ctx, tau=-1.0) == B.ERR_INVALID_ARG
+    assert _decode_noalloc(ctx, n_seqs=0) == B.OK                  # nothing to do, nothing touched
+    unready = lkv.Context(2, 3, 2, 64, 16, 2)
+    unready.plan([0, 1, 2, 0, 0, 1])
+    assert _decode_noalloc(unready) == B.ERR_WORKSPACE

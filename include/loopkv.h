@@ -41,10 +41,14 @@
  *   K plane (2-bit): D/16 columns x 16 tokens of u32; word (w, t) holds channels
  *     16w..16w+15 of token t, channel 16w+4k+p at bit 8k+2p.
  *   K plane (4-bit): D/8 columns x 16 tokens; channel 8w+2k+n at bit 8k+4n.
- *   V plane (2-bit): D words; word d holds channel d of the 16 tokens, token t at
+ *   V plane (2-bit): D words; logical word d holds channel d of the 16 tokens, token t at
  *     bit 8*(t%4) + 2*(t/4).
- *   V plane (4-bit): D x 2 words; word (d, j) holds tokens 8j..8j+7, token
- *     t' = t-8j at bit 8*(t'%4) + 4*(t'/4).
+ *   V plane (4-bit): D x 2 words; logical word 2d+j holds tokens 8j..8j+7 of channel d,
+ *     token t' = t-8j at bit 8*(t'%4) + 4*(t'/4).
+ *   V planes are stored as 16-byte quads of four logical words, transposed: logical quad
+ *     q = r*a + i of a plane of Q quads sits at quad position i*(Q/r) + a, with r = 2 for
+ *     the 2-bit planes and r = 2 (head_dim <= 128) or 4 (head_dim 256) for the 4-bit plane
+ *     (a value lane's r quads are then r contiguous spans read by r load instructions).
  *   Meta word: f16 scale in bits 0-15, f16 zero in bits 16-31.
  *   K_meta of group g: one word per channel, permuted inside each K column so that a
  *     column's words follow its bit layout — 2-bit: position 16w+4p+k holds channel

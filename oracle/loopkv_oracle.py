@@ -269,13 +269,21 @@ def _pack_2bit_k(c):
     return words.T.reshape(-1).astype("<u4").view(np.uint8)
 
 
+def _transpose_quads(words, r):
+    """A V plane's 16-byte quads (runs of 4 words) stored transposed: logical quad q = r a + i
+    goes to position i (nq / r) + a."""
+    nq = words.size // 4
+    return words.reshape(nq // r, r, 4).transpose(1, 0, 2).reshape(-1)
+
+
 def _pack_2bit_channel_major(c):
-    """[16][D] codes -> D little-endian u32; token t of channel d at bit 8*(t%4) + 2*(t//4)."""
+    """[16][D] codes -> D little-endian u32, word d (logical order) holding channel d with
+    token t at bit 8*(t%4) + 2*(t//4); the plane's quads are stored transposed with r = 2."""
     T, D = c.shape
     words = np.zeros(D, dtype=np.uint64)
     for t in range(T):
         words |= c[t].astype(np.uint64) << np.uint64(8 * (t % 4) + 2 * (t // 4))
-    return words.astype("<u4").view(np.uint8)
+    return _transpose_quads(words, 2).astype("<u4").view(np.uint8)
 
 
 def _pack_4bit_k(c):
@@ -289,14 +297,15 @@ def _pack_4bit_k(c):
 
 
 def _pack_4bit_channel_major(c):
-    """[16][D] codes -> D*2 u32 (channel-major, word w covers tokens 8w..8w+7);
-    token t' = t - 8w at bit 8*(t'%4) + 4*(t'//4)."""
+    """[16][D] codes -> D*2 u32 (channel-major: logical word 2d + w covers tokens 8w..8w+7 of
+    channel d, token t' = t - 8w at bit 8*(t'%4) + 4*(t'//4)); the plane's quads are stored
+    transposed with r = 2 (D <= 128) or 4 (D = 256)."""
     T, D = c.shape
     words = np.zeros((D, 2), dtype=np.uint64)
     for t in range(T):
         w, tp = divmod(t, 8)
         words[:, w] |= c[t].astype(np.uint64) << np.uint64(8 * (tp % 4) + 4 * (tp // 4))
-    return words.reshape(-1).astype("<u4").view(np.uint8)
+    return _transpose_quads(words.reshape(-1), 4 if D == 256 else 2).astype("<u4").view(np.uint8)
 
 
 def _meta_words(s, z):
@@ -337,7 +346,7 @@ def pack_block(qh, j, layout=LAYOUT_PLANES):
     2-bit:                [K2   | K_meta | V2   | V_meta]
     4-bit, KIVI-4 layout: [K4   | K_meta | V4   | V_meta]
     K planes are column-major (16-channel columns of the 16 tokens), V planes
-    channel-major (see the helpers above).
+    channel-major with their 16-byte quads stored transposed (see the helpers above).
     K_meta of group g = j // P (P = group / 16 blocks per group) holds one word per
     channel in the order of k_meta_order (a permutation inside each K column),
     split over the group's P blocks: block P g + i holds positions i D/P ..

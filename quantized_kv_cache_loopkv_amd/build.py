@@ -68,6 +68,47 @@ def build_loopkv(verbose: bool = False) -> str:
     return out
 
 
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer", "-g"]
+
+
+def asan_runtime() -> str:
+    """Path of the clang AddressSanitizer runtime that a process loading the sanitized library
+    must preload (the Python interpreter itself is not instrumented)."""
+    clang = os.path.join(os.path.dirname(os.path.realpath(_hipcc())), "..", "lib", "llvm", "bin", "clang++")
+    for c in (clang, "/opt/rocm/llvm/bin/clang++"):
+        if os.path.exists(c):
+            r = subprocess.run([c, "--print-file-name=libclang_rt.asan-x86_64.so"], stdout=subprocess.PIPE, text=True)
+            path = r.stdout.strip()
+            if os.path.exists(path):
+                return path
+    raise RuntimeError("clang's AddressSanitizer runtime not found")
+
+
+def build_sanitized(verbose: bool = False) -> str:
+    """A host-sanitized copy of the library for CPU-only checks of the host code: runtime.cpp
+    and planner.cpp built with AddressSanitizer and UndefinedBehaviorSanitizer on the host side
+    only (device code unchanged), linked with the regular kernel objects into
+    _build/libloopkv_san.so. Load it with LOOPKV_LIB pointing at it and the ASan runtime
+    preloaded (asan_runtime())."""
+    from concurrent.futures import ThreadPoolExecutor
+    build_loopkv(verbose)   # the kernel objects
+    hipcc = _hipcc()
+    cmds, objs = [], []
+    for src, name in (("runtime.cpp", "runtime_san"), ("planner.cpp", "planner_san")):
+        obj = os.path.join(BUILD, name + ".o")
+        cmds.append([hipcc, *COMMON, *SAN_FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj])
+        objs.append(obj)
+    with ThreadPoolExecutor(2) as ex:
+        for f in [ex.submit(_run, c, verbose) for c in cmds]:
+            f.result()
+    objs += [os.path.join(BUILD, n + ".o") for n in ("append", "decode", "decode_big")]
+    out = os.path.join(BUILD, "libloopkv_san.so")
+    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Xarch_host", "-fsanitize=address",
+          "-Xarch_host", "-fsanitize=undefined", "-shared-libsan", "-o", out, *objs], verbose)
+    return out
+
+
 def build_synth(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     hipcc = _hipcc()
@@ -84,5 +125,9 @@ def build_all(verbose: bool = False):
 
 
 if __name__ == "__main__":
-    for p in build_all(verbose="-v" in sys.argv):
-        print(p)
+    if "--sanitize" in sys.argv:
+        print(build_sanitized(verbose="-v" in sys.argv))
+        print(asan_runtime())
+    else:
+        for p in build_all(verbose="-v" in sys.argv):
+            print(p)

@@ -211,7 +211,7 @@ __global__ void __launch_bounds__(256) k_quantize_groups(AppendArgs a) {
         const int d = idx / 2, jj = idx % 2;
         uint32_t word = 0;
         for (int tp = 0; tp < 8; ++tp) word |= (uint32_t)vc[t0 + 8 * jj + tp][d] << (8 * (tp % 4) + 4 * (tp / 4));
-        r[off_v_kivi(D, GS) / 4 + idx] = word;
+        r[off_v_kivi(D, GS) / 4 + vword_pos(idx, true, D)] = word;
       }
       for (int c = tid; c < D / P; c += blockDim.x) r[off_kmeta_kivi(D) / 4 + c] = kmeta[kmeta_channel4(part * (D / P) + c)];
       for (int idx = tid; idx < kBlock * (D / GS); idx += blockDim.x)
@@ -247,8 +247,9 @@ __global__ void __launch_bounds__(256) k_quantize_groups(AppendArgs a) {
             hi |= code << sh;
           }
         }
-        r[off_v_planes(D, GS) / 4 + d] = hi;
-        if (q4) r[off_vlo(D, GS) / 4 + d] = lo;
+        const int wp = vword_pos(d, false, D);   // the planes' quads are stored transposed
+        r[off_v_planes(D, GS) / 4 + wp] = hi;
+        if (q4) r[off_vlo(D, GS) / 4 + wp] = lo;
       }
       for (int c = tid; c < D / P; c += blockDim.x) r[off_kmeta_planes(D) / 4 + c] = kmeta[kmeta_channel2(part * (D / P) + c)];
       for (int idx = tid; idx < kBlock * (D / GS); idx += blockDim.x)

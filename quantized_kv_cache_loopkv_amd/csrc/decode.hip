@@ -297,6 +297,9 @@ struct Geo {
   static constexpr int COOP = BPS * 4 * NE;
   static constexpr int VW = KIVI ? 2 * VCH : VCH;   // code words per lane (high plane or KIVI-4)
   static constexpr int NV4 = VW / 4;
+  static constexpr int NQ = KIVI ? D / 2 : D / 4;    // 16-byte quads of a V plane
+  static constexpr int VR = vquad_r(KIVI, D);        // their stored transposition (layout.h)
+  static_assert(KIVI ? NV4 == VR : (NV4 == 1 || NV4 == VR), "value lanes read whole transposed quads");
   static constexpr int VOFF = KIVI ? off_v_kivi(D, GS) : off_v_planes(D, GS);
   static constexpr int VMETA = KIVI ? off_vmeta_kivi(D, GS) : off_vmeta_planes(D, GS);
   // Token t_loc of a step is owned by lane t_loc and a weight lane's four tokens are its own
@@ -347,12 +350,14 @@ struct KStep {
       b.meta = ld_words<G::CPL>(r.at(2 * g + (pos0 >= D / 2), G::KMETA + 4 * (pos0 % (D / 2))));
     else
       b.meta = ld_words<G::CPL>(r.at(G::GP * (g / G::GU) + pos0 / (D / G::GP), G::KMETA + 4 * (pos0 % (D / G::GP))));
-    const uint8_t* kp = r.at(2 * g + blk, CODE_OFF + ((cp * G::NC) * kBlock + 4 * quad) * 4);
+    // lane cp reads columns cp, cp + CPG, ...: each load instruction covers CPG whole
+    // consecutive columns (CPG x 64 contiguous bytes) of each of its records
+    const uint8_t* kp = r.at(2 * g + blk, CODE_OFF + (cp * kBlock + 4 * quad) * 4);
 #pragma unroll
-    for (int i = 0; i < G::NC; ++i) b.c[i] = ld_stream4(kp + i * kBlock * 4);
+    for (int i = 0; i < G::NC; ++i) b.c[i] = ld_stream4(kp + i * G::CPG * kBlock * 4);
     if (G::DENSE) {
 #pragma unroll
-      for (int i = 0; i < G::NC; ++i) b.l[i] = ld_stream4(kp + off_klo(D, GS) + i * kBlock * 4);
+      for (int i = 0; i < G::NC; ++i) b.l[i] = ld_stream4(kp + off_klo(D, GS) + i * G::CPG * kBlock * 4);
     }
   }
 
@@ -481,16 +486,14 @@ struct KStep {
     }
     wave_sync_lds();
     // Limbs of this lane's NC columns (SPC sets x 3 words each); the four tokens' chains run
-    // interleaved, limb 2 first. With registers to spare (2 waves per SIMD) one chain per
-    // token covers all columns; otherwise one column at a time, each recombined exactly.
-    constexpr bool ONE_CHAIN = kWavesPerSimd <= 2;
-    constexpr int NCC = ONE_CHAIN ? G::NC : 1;   // columns per chain
+    // interleaved, limb 2 first, one column at a time, each recombined exactly.
+    constexpr int NCC = 1;   // columns per chain
     constexpr int CW = NCC * G::SPC * 3;
     int acc4[4] = {0, 0, 0, 0};
 #pragma unroll
     for (int i0 = 0; i0 < G::NC; i0 += NCC) {
       uint32_t L[CW];
-      const uint32_t* src = klimb + (gsub * (D / 4) + (cp * G::NC + i0) * G::SPC) * 3;
+      const uint32_t* src = klimb + (gsub * (D / 4) + (cp + i0 * G::CPG) * G::SPC) * 3;   // column cp + i0 CPG
       if constexpr (CW % 4 == 0) {
 #pragma unroll
         for (int u4 = 0; u4 < CW / 4; ++u4) {
@@ -578,13 +581,13 @@ struct VStep {
     int j = jbase + lane / G::LPB;
     j = j < nb ? j : jbase;
     const int chunk = lane % G::LPB;
-    const uint8_t* rb = r.at(j, G::VOFF + chunk * G::VW * 4);
+    // the lane's NV4 logical quads chunk NV4 + i, stored transposed (see vquad_pos)
 #pragma unroll
-    for (int i = 0; i < G::NV4; ++i) b.c[i] = ld_stream4(rb + 16 * i);
+    for (int i = 0; i < G::NV4; ++i) b.c[i] = ld_stream4(r.at(j, G::VOFF + 16 * vquad_pos(chunk * G::NV4 + i, G::NQ, G::VR)));
     if (G::DENSE) {
-      const uint8_t* rl = r.at(j, off_vlo(D, GS) + chunk * G::VCH * 4);
 #pragma unroll
-      for (int i = 0; i < G::NV4; ++i) b.l[i] = ld_stream4(rl + 16 * i);
+      for (int i = 0; i < G::NV4; ++i)
+        b.l[i] = ld_stream4(r.at(j, off_vlo(D, GS) + 16 * vquad_pos(chunk * G::NV4 + i, G::NQ, G::VR)));
     }
   }
 
@@ -718,8 +721,9 @@ __device__ void exact_v_pass(const RW& r, const float* weights, const uint32_t* 
     uint32_t hw[VCH], lw[VCH];
 #pragma unroll
     for (int c = 0; c < VCH; ++c) {
-      hw[c] = reinterpret_cast<const uint32_t*>(rb + off_v_planes(D, GS))[chunk * VCH + c];
-      lw[c] = reinterpret_cast<const uint32_t*>(rb + off_vlo(D, GS))[chunk * VCH + c];
+      const int wp = vword_pos(chunk * VCH + c, false, D);
+      hw[c] = reinterpret_cast<const uint32_t*>(rb + off_v_planes(D, GS))[wp];
+      lw[c] = reinterpret_cast<const uint32_t*>(rb + off_vlo(D, GS))[wp];
     }
     const uint32_t bm = (selm[j >> 1] >> (16 * (j & 1))) & 0xffffu;
     for (int tt = 0; tt < kBlock; ++tt) {
@@ -1031,8 +1035,9 @@ __device__ __forceinline__ void row_body(const DecodeArgs& a, const RW& r, const
           const uint8_t* rb = r.rec_ptr(2 * gv + jb % 2);
 #pragma unroll
           for (int i = 0; i < GC::VCH / 4; ++i) {
-            hw4[i] = *reinterpret_cast<const uint4*>(rb + off_v_planes(D, GS) + 4 * (chunk * GC::VCH + 4 * i));
-            lw4[i] = *reinterpret_cast<const uint4*>(rb + off_vlo(D, GS) + 4 * (chunk * GC::VCH + 4 * i));
+            const int qp = 16 * vquad_pos(chunk * GC::NV4 + i, GC::NQ, GC::VR);
+            hw4[i] = *reinterpret_cast<const uint4*>(rb + off_v_planes(D, GS) + qp);
+            lw4[i] = *reinterpret_cast<const uint4*>(rb + off_vlo(D, GS) + qp);
           }
 #pragma unroll
           for (int i = 0; i < 4; ++i)

@@ -30,6 +30,18 @@ __host__ __device__ constexpr int off_kmeta_kivi(int D) { return 8 * D; }
 __host__ __device__ constexpr int off_v_kivi(int D, int GS) { return 8 * D + meta_bytes(D, GS); }
 __host__ __device__ constexpr int off_vmeta_kivi(int D, int GS) { return 16 * D + meta_bytes(D, GS); }
 
+// V planes store their 16-byte quads (four channel words; KIVI-4: two channels) transposed, so
+// that the decode's value lanes, each reading R consecutive logical quads, read R contiguous
+// spans with R load instructions: logical quad q of a plane of NQ quads sits at position
+// (q mod R) * (NQ / R) + q / R. R = 2 for the 2-bit planes (NQ = D / 4); for the KIVI-4 V plane
+// (NQ = D / 2) R = 2 at D <= 128 and 4 at D = 256.
+__host__ __device__ constexpr int vquad_r(bool kivi, int D) { return kivi && D == 256 ? 4 : 2; }
+__host__ __device__ constexpr int vquad_pos(int q, int nq, int r) { return (q % r) * (nq / r) + q / r; }
+// Word position of logical word w of a V plane.
+__host__ __device__ constexpr int vword_pos(int w, bool kivi, int D) {
+  return vquad_pos(w / 4, kivi ? D / 2 : D / 4, vquad_r(kivi, D)) * 4 + w % 4;
+}
+
 // Record of one 16-token block and one KV head, padded to a multiple of 256 bytes (only
 // D = 64 with groups of 64 pads: 1152 -> 1280, 640 -> 768).
 __host__ __device__ constexpr int record_bytes(int kind, int D, int GS) {

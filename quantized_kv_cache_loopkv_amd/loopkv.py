@@ -15,7 +15,8 @@ from typing import Optional, Sequence
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libloopkv.so")
+# LOOPKV_LIB selects another build of the same library (the host-sanitized one, for CPU checks)
+LIB_PATH = os.environ.get("LOOPKV_LIB") or os.path.join(_HERE, "libloopkv.so")
 
 OK, ERR_INVALID_ARG, ERR_PLAN, ERR_WORKSPACE, ERR_CAPACITY, ERR_UNSUPPORTED, ERR_HIP = range(7)
 CELL_Q4, CELL_Q2, CELL_SHARE = 0, 1, 2

@@ -29,19 +29,40 @@ def _unpack_k(buf, D, width):
     return out
 
 
+def _stored_word(logical, n_words, r):
+    """Where logical word n of a V plane is stored: quads of four words are transposed, so the
+    quad q = r a + i of a plane of Q quads sits at quad position i (Q / r) + a."""
+    q, k = divmod(logical, 4)
+    a, i = divmod(q, r)
+    return 4 * (i * (n_words // 4 // r) + a) + k
+
+
 def _unpack_channel_major_2bit(buf, D):
     bits = _bits(buf)
-    return np.array([[_field(bits, 32 * d + 8 * (t % 4) + 2 * (t // 4), 2) for d in range(D)] for t in range(16)])
+    return np.array([[_field(bits, 32 * _stored_word(d, D, 2) + 8 * (t % 4) + 2 * (t // 4), 2) for d in range(D)]
+                     for t in range(16)])
 
 
 def _unpack_channel_major_4bit(buf, D):
     bits = _bits(buf)
+    r = 4 if D == 256 else 2
     out = np.zeros((16, D), dtype=np.int64)
     for t in range(16):
         w, tp = divmod(t, 8)
         for d in range(D):
-            out[t, d] = _field(bits, 64 * d + 32 * w + 8 * (tp % 4) + 4 * (tp // 4), 4)
+            out[t, d] = _field(bits, 32 * _stored_word(2 * d + w, 2 * D, r) + 8 * (tp % 4) + 4 * (tp // 4), 4)
     return out
+
+
+def test_v_quads_transposed_positions():
+    """The transposition on a small plane, written out: with 8 quads and r = 2 the stored order
+    is quads 0, 2, 4, 6, 1, 3, 5, 7; with r = 4, quads 0, 4, 1, 5, 2, 6, 3, 7."""
+    pos2 = [_stored_word(4 * q, 32, 2) // 4 for q in range(8)]
+    assert [pos2.index(p) for p in range(8)] == [0, 2, 4, 6, 1, 3, 5, 7]
+    pos4 = [_stored_word(4 * q, 32, 4) // 4 for q in range(8)]
+    assert [pos4.index(p) for p in range(8)] == [0, 4, 1, 5, 2, 6, 3, 7]
+    words = np.arange(32, dtype=np.uint64)
+    assert O._transpose_quads(words, 2).reshape(8, 4)[:, 0].tolist() == [0, 8, 16, 24, 4, 12, 20, 28]
 
 
 def _meta(buf):
@@ -52,7 +73,7 @@ def _meta(buf):
 
 
 @pytest.mark.parametrize("group", [32, 64])
-@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("D", [64, 128, 256])
 @pytest.mark.parametrize("layout,bits", [(O.LAYOUT_PLANES, 4), (O.LAYOUT_PLANES, 2), (O.LAYOUT_KIVI4, 4)])
 def test_pack_roundtrip(D, layout, bits, group):
     rng = np.random.default_rng(D + bits + layout + group)

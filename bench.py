@@ -37,7 +37,8 @@ PEAK_HBM_GBS = 8000.0
 SERVING_WARM, SERVING_REPS = 2, 5     # graph replays of the per-(loop, layer) legs
 SERVING_SPLITS = (0, 8, 16, 32)       # workgroups per row tried at batch 1
 COUNTERS = os.path.join(ROOT, "profiles", "k_decode_c4_tau0.01_counters.json")
-KERNEL_SOURCES = ["quantized_kv_cache_loopkv_amd/csrc/decode.hip", "quantized_kv_cache_loopkv_amd/csrc/layout.h"]
+KERNEL_SOURCES = ["quantized_kv_cache_loopkv_amd/csrc/decode.hip", "quantized_kv_cache_loopkv_amd/csrc/layout.h",
+                  "quantized_kv_cache_loopkv_amd/csrc/quantize.h"]
 
 
 def kernel_source_hash():
@@ -340,6 +341,20 @@ def serving_graph(wl, q, tau, first_step, n_rep, n_split, log, warm=2):
     return float(sum(ms) / len(ms)), ms
 
 
+def workload_name(wk, cfg, args, group):
+    import numpy as np
+    p = cfg.plan.reshape(-1)
+    kinds = f"{int((p == 0).sum())} q4 / {int((p == 1).sum())} q2 / {int((p == 2).sum())} reuse"
+    if wk == "c5":
+        ctx = f"lengths uniform in [1024, 16384] (mean {int(np.mean(cfg.lengths)) + cfg.append_steps})"
+    else:
+        ctx = f"context {args.ctx} (last step)"
+    table = "shuffled" if cfg.shuffled else "identity"
+    return (f"{cfg.n_loops} loops x {cfg.n_layers} layers, {kinds}, {cfg.n_heads} heads x {cfg.head_dim}, "
+            f"batch {cfg.batch}, {ctx}, 16-token blocks {table}, tau {args.tau}, "
+            "1-token append + whole-plan decode per step" + ("" if group == 32 else f", quantization groups of {group}"))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -357,6 +372,10 @@ def main():
                     help="quantization group (tokens per K group, channels per V group); the pages' is 32")
     ap.add_argument("--table", choices=["shuffled", "identity"], default="shuffled",
                     help="block table of the workload (the configuration uses a shuffled one)")
+    ap.add_argument("--workload", choices=["c4", "c3", "c5", "c5-16k-half"], default="c4",
+                    help="c4: the headline (4x24 plan, batch 32, 16K, shuffled table); c3: 8K context, identity "
+                         "table; c5: batch 128, lengths uniform in [1024, 16384]; c5-16k-half: batch 128 at 16K "
+                         "on the plan's last two loops (48 cells; pools above 4 GiB)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a device-to-device copy of 4 GiB three times (counter calibration)")
     args = ap.parse_args()
@@ -391,10 +410,26 @@ def main():
     torch.cuda.set_device(0)
     lkv.lib()
     S = args.warmup + args.steps
+    wk = args.workload
+    if wk == "c3":
+        args.ctx, args.table = 8192, "identity"
+    if wk in ("c5", "c5-16k-half"):
+        args.batch = 128
+        args.no_kivi = True      # the KIVI-4 cache of these batches does not fit beside the LoopKV one
+        args.no_serving = True   # the per-cell serving legs are measured on the headline workload
     GS = 0 if args.no_serving else SERVING_WARM + SERVING_REPS   # tokens the serving leg appends
-    cfg = R.make_config("C4")
+    if wk == "c5":
+        cfg = R.make_config("C5")   # lengths uniform in [1024, 16384]: the first step's
+        cfg.lengths = [n - S for n in cfg.lengths]
+        args.ctx = max(cfg.lengths) + S
+    else:
+        cfg = R.make_config("C4")
+        cfg.batch = args.batch
+        cfg.lengths = [args.ctx - S] * args.batch
+        if wk == "c5-16k-half":   # loops 2 and 3: reuse cells of loop 2 read loop 3
+            cfg.n_loops = 2
+            cfg.plan = cfg.plan[2:4].copy()
     cfg.batch = args.batch
-    cfg.lengths = [args.ctx - S] * args.batch
     cfg.append_steps = S + GS
     cfg.shuffled = args.table == "shuffled"
     cfg.group = GQ = args.group
@@ -448,7 +483,7 @@ def main():
     value = float(np.mean(step_bytes)) / (ms_per_step * 1e-3) / 1e9
     dec_mean_ms = float(np.mean(dec_ms))
     achieved = dec_bytes / (dec_mean_ms * 1e-3) / 1e9
-    sel_frac = float(counts.sum()) / max(1, sum(int(H * B * (GQ * (final_lens[0] // GQ))) for c in range(C) if tk[c] == 0))
+    sel_frac = float(counts.sum()) / max(1, sum(H * GQ * (n // GQ) for n in final_lens) * int((tk == 0).sum()))
     log(f"step {ms_per_step:.3f} ms (events {np.mean(step_ms):.3f}), decode {dec_mean_ms:.3f} ms, "
         f"append {np.mean(app_ms):.3f} ms; decode {achieved:.0f} GB/s algorithmic; selected fraction {sel_frac:.2e}")
 
@@ -580,10 +615,7 @@ def main():
         "vs_baseline": None,
         "dtype": "i8 dot products into i32, f32 softmax and accumulators (bf16 q/K/V in, bf16 out)",
         "data": "synthetic (seeded Philox normal draws, shapes of the pages' Ouro-1.4B 16K serving workload)",
-        "config": {"workload": "4 loops x 24 layers, 48 q4 / 29 q2 / 19 reuse, 16 heads x 128, batch 32, "
-                               f"context {args.ctx} (last step), 16-token blocks shuffled, tau {args.tau}, "
-                               "1-token append + whole-plan decode per step"
-                               + ("" if GQ == 32 else f", quantization groups of {GQ}"),
+        "config": {"workload": workload_name(wk, cfg, args, GQ),
                    "global_batch": B, "seq_len": args.ctx, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4),

@@ -29,73 +29,9 @@
 #include <hip/hip_fp16.h>
 #include <stdint.h>
 #include "layout.h"
+#include "quantize.h"
 
 namespace lkv {
-
-// float64 -> float16 bits, round to nearest even, one rounding.
-__device__ inline uint32_t f64_to_f16_bits(double x) {
-  uint64_t b = (uint64_t)__double_as_longlong(x);
-  uint32_t sign = (uint32_t)(b >> 48) & 0x8000u;
-  int ex = (int)((b >> 52) & 0x7ff);
-  uint64_t man = b & 0xFFFFFFFFFFFFFull;
-  if (ex == 0x7ff) return sign | 0x7c00u | (man ? 0x200u : 0u);
-  if (ex == 0) return sign;                       // below 2^-1022: rounds to zero
-  int e = ex - 1023;
-  if (e > 15) return sign | 0x7c00u;
-  uint64_t m = man | (1ull << 52);
-  int s = (e >= -14) ? 42 : (28 - e);             // bits dropped to reach the f16 ulp
-  if (s > 60) return sign;
-  uint64_t q = m >> s;
-  uint64_t rem = m & ((1ull << s) - 1);
-  uint64_t half = 1ull << (s - 1);
-  if (rem > half || (rem == half && (q & 1))) q++;
-  uint32_t bits = (e >= -14) ? (uint32_t)(((e + 15) << 10) + (int)q - 1024) : (uint32_t)q;
-  if (bits >= 0x7c00u) bits = 0x7c00u;
-  return sign | bits;
-}
-
-__device__ inline double f16_bits_to_f64(uint32_t h) {
-  return (double)__half2float(__ushort_as_half((unsigned short)h));
-}
-
-__device__ inline float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
-
-__device__ inline uint16_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);   // NaN stays NaN
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
-
-// Quantize n values read through get(i) with M = 2^bits - 1 levels.
-template <typename Get>
-__device__ inline void quantize_group(Get get, int n, int M, uint8_t* codes, int stride, uint32_t* meta) {
-  double mn = get(0), mx = mn;
-  for (int i = 1; i < n; ++i) {
-    double x = get(i);
-    mn = fmin(mn, x);
-    mx = fmax(mx, x);
-  }
-  uint32_t zb = f64_to_f16_bits(mn);
-  uint32_t sb = f64_to_f16_bits((mx - mn) / (double)M);
-  double z = f16_bits_to_f64(zb);
-  double s = f16_bits_to_f64(sb);
-  for (int i = 0; i < n; ++i) {
-    int c = 0;
-    if (s != 0.0) {
-      double r = rint((get(i) - z) / s);
-      r = fmin(fmax(r, 0.0), (double)M);
-      c = (int)r;
-    }
-    codes[i * stride] = (uint8_t)c;
-  }
-  *meta = sb | (zb << 16);
-}
-
-// Channel stored at K-meta position i: the words of a K column follow the column's
-// bit layout (2-bit: byte k, bit pair p; 4-bit: byte k, nibble n).
-__device__ inline int kmeta_channel2(int i) { return (i & ~15) + 4 * (i & 3) + ((i >> 2) & 3); }
-__device__ inline int kmeta_channel4(int i) { return (i & ~7) + 2 * (i & 3) + ((i >> 2) & 1); }
 
 // The new tokens of (cell ci, sequence b, head h) that stay in the tail (those after the
 // last group the append completes), rounded from f32 if needed.
@@ -177,15 +113,11 @@ __global__ void __launch_bounds__(256) k_quantize_groups(AppendArgs a) {
   }
 
   const int M = (cell.kind == KIND_Q2) ? 3 : 15;
-  // K: one group per channel over the GS tokens.
-  for (int d = tid; d < D; d += blockDim.x)
-    quantize_group([&](int i) { return (double)bf16_to_f32(kx[i][d]); }, GS, M, &kc[0][d], D, &kmeta[d]);
-  // V: one group per token over each run of GS channels.
-  for (int task = tid; task < GS * (D / GS); task += blockDim.x) {
-    const int i = task / (D / GS), e = task % (D / GS);
-    quantize_group([&](int j) { return (double)bf16_to_f32(vx[i][e * GS + j]); }, GS, M, &vc[i][e * GS], 1,
-                   &vmeta[i][e]);
-  }
+  // K: one group per channel over the GS tokens; V: one group per token over each run of GS
+  // channels.
+  quantize_group_codes<D, GS>([&](int i, int d) { return (double)bf16_bits_to_f32(kx[i][d]); },
+                              [&](int i, int d) { return (double)bf16_bits_to_f32(vx[i][d]); }, M, kc, vc, kmeta,
+                              vmeta, tid, (int)blockDim.x);
   __syncthreads();
 
   // The group's P records: record P g + part holds tokens 16 part .. 16 part + 15 and the
@@ -198,63 +130,7 @@ __global__ void __launch_bounds__(256) k_quantize_groups(AppendArgs a) {
       continue;   // page not mapped (uniform over the workgroup): the record is not written
     const uint32_t phys = record_slot(bt, j, a.bt_shift);
     uint32_t* r = reinterpret_cast<uint32_t*>(a.ws + cell.pool_off + ((size_t)phys * a.n_heads + h) * rec);
-    const int t0 = part * kBlock;
-    if (cell.kind == KIND_KIVI4) {
-      // K4: D/8 columns x 16 tokens; V4: D channels x 2 words.
-      for (int idx = tid; idx < (D / 8) * kBlock; idx += blockDim.x) {
-        const int w = idx / kBlock, t = idx % kBlock;
-        uint32_t word = 0;
-        for (int c = 0; c < 8; ++c) word |= (uint32_t)kc[t0 + t][8 * w + c] << (4 * c);
-        r[idx] = word;
-      }
-      for (int idx = tid; idx < D * 2; idx += blockDim.x) {
-        const int d = idx / 2, jj = idx % 2;
-        uint32_t word = 0;
-        for (int tp = 0; tp < 8; ++tp) word |= (uint32_t)vc[t0 + 8 * jj + tp][d] << (8 * (tp % 4) + 4 * (tp / 4));
-        r[off_v_kivi(D, GS) / 4 + vword_pos(idx, true, D)] = word;
-      }
-      for (int c = tid; c < D / P; c += blockDim.x) r[off_kmeta_kivi(D) / 4 + c] = kmeta[kmeta_channel4(part * (D / P) + c)];
-      for (int idx = tid; idx < kBlock * (D / GS); idx += blockDim.x)
-        r[off_vmeta_kivi(D, GS) / 4 + idx] = vmeta[t0 + idx % kBlock][idx / kBlock];
-    } else {
-      const bool q4 = cell.kind == KIND_Q4;
-      // K planes: D/16 columns x 16 tokens.
-      for (int idx = tid; idx < (D / 16) * kBlock; idx += blockDim.x) {
-        const int w = idx / kBlock, t = idx % kBlock;
-        uint32_t hi = 0, lo = 0;
-        for (int c = 0; c < 16; ++c) {
-          const uint32_t code = kc[t0 + t][16 * w + c];
-          if (q4) {
-            hi |= (code >> 2) << (2 * c);
-            lo |= (code & 3u) << (2 * c);
-          } else {
-            hi |= code << (2 * c);
-          }
-        }
-        r[idx] = hi;
-        if (q4) r[off_klo(D, GS) / 4 + idx] = lo;
-      }
-      // V planes: one word per channel, token t at bit 8*(t%4) + 2*(t/4).
-      for (int d = tid; d < D; d += blockDim.x) {
-        uint32_t hi = 0, lo = 0;
-        for (int t = 0; t < kBlock; ++t) {
-          const uint32_t code = vc[t0 + t][d];
-          const int sh = 8 * (t % 4) + 2 * (t / 4);
-          if (q4) {
-            hi |= (code >> 2) << sh;
-            lo |= (code & 3u) << sh;
-          } else {
-            hi |= code << sh;
-          }
-        }
-        const int wp = vword_pos(d, false, D);   // the planes' quads are stored transposed
-        r[off_v_planes(D, GS) / 4 + wp] = hi;
-        if (q4) r[off_vlo(D, GS) / 4 + wp] = lo;
-      }
-      for (int c = tid; c < D / P; c += blockDim.x) r[off_kmeta_planes(D) / 4 + c] = kmeta[kmeta_channel2(part * (D / P) + c)];
-      for (int idx = tid; idx < kBlock * (D / GS); idx += blockDim.x)
-        r[off_vmeta_planes(D, GS) / 4 + idx] = vmeta[t0 + idx % kBlock][idx / kBlock];
-    }
+    pack_record<D, GS>(r, cell.kind, part, kc, vc, kmeta, vmeta, tid, (int)blockDim.x);
   }
 }
 

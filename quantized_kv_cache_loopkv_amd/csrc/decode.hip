@@ -44,6 +44,7 @@
 #include <stdint.h>
 #include <math.h>
 #include "layout.h"
+#include "quantize.h"
 
 namespace lkv {
 
@@ -780,11 +781,71 @@ struct Smem {
 enum : int { PH_ROW = 0, PH_PART = 1, PH_FINISH = 2 };
 
 // Chunk range [cb, ce) of split `split` over a row of n_chunks chunks: equal shares rounded
-// up to a multiple of the waves of a workgroup, so every wave gets the same step count.
+// up to a multiple of the waves of a workgroup, so every wave gets the same step count, taken
+// from the row's end: the last split always holds the last chunks (with the tail), so in a
+// serving step the workgroup that appends the step's token is the only one reading the group
+// that token completes; splits left without chunks are the first ones.
 __device__ inline void split_range(int n_chunks, int n_split, int split, int& cb, int& ce) {
   const int per = ((n_chunks + n_split - 1) / n_split + kWaves - 1) / kWaves * kWaves;
-  cb = min(n_chunks, split * per);
-  ce = min(n_chunks, cb + per);
+  ce = max(0, n_chunks - (n_split - 1 - split) * per);
+  cb = max(0, ce - per);
+}
+
+// The in-launch append of a serving step (DecodeArgs::app_k): the token of (sequence b, KV
+// head kh) at position L0 = app_lens[b]. It stays in the tail (slot L0 mod GS) unless it
+// completes group g = L0 / GS; then the group's GS tokens (GS - 1 from the tail, the new one)
+// are quantized and its GS / 16 records written through the block table, exactly as the
+// append kernels do (same quantizer, same packer). Unmapped pages and invalid sequences are
+// skipped as there. The caller synchronizes the workgroup afterwards.
+template <int D, int GS>
+__device__ void fused_append(const DecodeArgs& a, const DecodeCell& cell, int b, int kh, unsigned char* lds) {
+  const int tid = threadIdx.x;
+  const int L0 = a.app_lens[b];
+  const int slot = a.seq_slots ? a.seq_slots[b] : b;
+  if (L0 < 0 || (uint32_t)slot >= (uint32_t)a.max_seqs) return;   // uniform: nothing written
+  uint16_t* tail = reinterpret_cast<uint16_t*>(const_cast<uint8_t*>(a.ws) + cell.tail_off) +
+                   ((size_t)slot * a.n_kv_heads + kh) * tail_elems(D, GS);
+  const size_t e0 = ((size_t)b * a.n_kv_heads + kh) * D;
+  auto new_bits = [&](const void* src, int d) -> uint16_t {
+    return a.app_bf16 ? reinterpret_cast<const uint16_t*>(src)[e0 + d]
+                      : f32_to_bf16_rne(reinterpret_cast<const float*>(src)[e0 + d]);
+  };
+  const int pos = L0 % GS;
+  if (pos != GS - 1) {   // the token stays in the tail
+    for (int d = tid; d < D; d += kThreads) {
+      tail[(size_t)pos * D + d] = new_bits(a.app_k, d);
+      tail[(size_t)(GS + pos) * D + d] = new_bits(a.app_v, d);
+    }
+    return;
+  }
+  auto kx = reinterpret_cast<uint16_t(*)[D]>(lds);                        // [GS][D]
+  auto vx = reinterpret_cast<uint16_t(*)[D]>(lds + 2 * GS * D);
+  auto kc = reinterpret_cast<uint8_t(*)[D]>(lds + 4 * GS * D);
+  auto vc = reinterpret_cast<uint8_t(*)[D]>(lds + 5 * GS * D);
+  uint32_t* kmeta = reinterpret_cast<uint32_t*>(lds + 6 * GS * D);
+  auto vmeta = reinterpret_cast<uint32_t(*)[D / GS]>(lds + 6 * GS * D + 4 * D);
+  for (int idx = tid; idx < GS * D; idx += kThreads) {
+    const int i = idx / D, d = idx % D;
+    const bool old = i < GS - 1;   // positions g GS .. L0 - 1 sit in tail slots 0 .. GS - 2
+    kx[i][d] = old ? tail[(size_t)i * D + d] : new_bits(a.app_k, d);
+    vx[i][d] = old ? tail[(size_t)(GS + i) * D + d] : new_bits(a.app_v, d);
+  }
+  __syncthreads();
+  const int M = cell.kind == KIND_Q2 ? 3 : 15;
+  quantize_group_codes<D, GS>([&](int i, int d) { return (double)bf16_bits_to_f32(kx[i][d]); },
+                              [&](int i, int d) { return (double)bf16_bits_to_f32(vx[i][d]); }, M, kc, vc, kmeta,
+                              vmeta, tid, kThreads);
+  __syncthreads();
+  const int g = L0 / GS;
+  const int rec = record_bytes(cell.kind, D, GS);
+  const int32_t* bt = a.block_table + (size_t)b * a.bt_stride;
+  for (int part = 0; part < GS / kBlock; ++part) {
+    const int j = (GS / kBlock) * g + part;
+    if ((j >> a.bt_shift) >= a.bt_stride || (uint32_t)bt[j >> a.bt_shift] >= (uint32_t)a.num_pages) continue;
+    uint32_t* r = reinterpret_cast<uint32_t*>(const_cast<uint8_t*>(a.ws) + cell.pool_off +
+                                              ((size_t)record_slot(bt, j, a.bt_shift) * a.n_kv_heads + kh) * rec);
+    pack_record<D, GS>(r, cell.kind, part, kc, vc, kmeta, vmeta, tid, kThreads);
+  }
 }
 
 // SKIP (with SPARSE, PH_ROW): the token-skipping ablation. The same coarse pass and
@@ -1266,6 +1327,11 @@ __global__ void __launch_bounds__(kThreads, (decode_waves_per_simd<D, VAR>())) k
   const DecodeCell cell = a.cells[ci];
   const int tid = threadIdx.x;
   const size_t orow = ((size_t)ci * a.n_seqs + b) * a.n_heads + h;
+  if (a.app_k && (PH == PH_ROW || (PH == PH_PART && split == a.n_split - 1))) {
+    static_assert(fused_append_lds_bytes(D, GS) <= 160 * 1024, "in-launch append LDS");
+    fused_append<D, GS>(a, cell, b, kh, reinterpret_cast<unsigned char*>(smem));
+    __syncthreads();   // the appended token and records are written before the row reads them
+  }
   const int N = a.seq_lens[b];
 
   const size_t lp = lds_lpad(a.max_len);
@@ -1451,7 +1517,8 @@ hipError_t launch_decode_small(const DecodeArgs& a, int head_dim, hipStream_t st
 #endif
   const size_t rows = (size_t)a.n_cells * a.n_seqs * a.n_heads;
   if (rows == 0) return hipSuccess;
-  const size_t lds = decode_lds_floats(a.max_len, head_dim) * 4;
+  size_t lds = decode_lds_floats(a.max_len, head_dim) * 4;
+  if (a.app_k) lds = lds > fused_append_lds_bytes(head_dim, a.group) ? lds : fused_append_lds_bytes(head_dim, a.group);
   if (head_dim == 128) launch_d<128>(a, rows, lds, stream);
   else if (head_dim == 256) launch_d<256>(a, rows, lds, stream);
   else launch_d<64>(a, rows, lds, stream);

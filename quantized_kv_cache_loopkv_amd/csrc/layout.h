@@ -113,8 +113,22 @@ struct DecodeArgs {
   int32_t skip;   // token-skipping ablation: unselected quantized tokens leave the attention
   float* part;
   float* part_scores;
+  // In-launch append of a serving step (one cell, every KV head read by one row): the token of
+  // (sequence b, KV head h) is app_k / app_v [n_seqs][1][n_kv_heads][D] (bf16 when app_bf16,
+  // else f32 rounded to bf16), appended at position app_lens[b] by the workgroup that decodes
+  // the row (the last split's, in a split decode) before it reads anything. Null: no append.
+  const void* app_k;
+  const void* app_v;
+  const int32_t* app_lens;
+  int32_t app_bf16;
   DecodeCell cells[kMaxCells];
 };
+
+// LDS of the in-launch append, in bytes: the group's bf16 K and V, their codes, K meta (one
+// word per channel) and V meta (one word per token and channel group).
+__host__ __device__ constexpr size_t fused_append_lds_bytes(int D, int GS) {
+  return (size_t)6 * GS * D + (size_t)8 * D;
+}
 
 // Scratch of a split decode, in floats: partials (padded to 64 floats), then one score line
 // per decoded row (lines of a multiple of 64 floats, so every line is 256-byte aligned

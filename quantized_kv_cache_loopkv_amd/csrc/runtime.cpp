@@ -318,7 +318,9 @@ loopkv_status decode_common(loopkv_ctx* c, hipStream_t stream, int32_t loop, int
                             int32_t q_dtype, int32_t n_seqs, const int32_t* seq_slots, const int32_t* block_table,
                             int32_t bt_stride, const int32_t* seq_lens, int32_t max_len, float tau, float sm_scale,
                             void* out, int32_t out_dtype, uint32_t* sel_mask, int32_t n_split, void* scratch,
-                            size_t scratch_bytes, bool skip, bool fixed_scratch = false) {
+                            size_t scratch_bytes, bool skip, bool fixed_scratch = false,
+                            const void* app_k = nullptr, const void* app_v = nullptr, int32_t app_dtype = LOOPKV_BF16,
+                            const int32_t* app_lens = nullptr) {
   loopkv_status s = check_ready(c);
   if (s != LOOPKV_OK) return s;
   int first, count;
@@ -378,6 +380,12 @@ loopkv_status decode_common(loopkv_ctx* c, hipStream_t stream, int32_t loop, int
   a.sm_scale = sm_scale;
   a.n_split = n_split;
   a.skip = skip ? 1 : 0;
+  if (app_k) {   // serving step: the row's workgroup appends the step's token first
+    a.app_k = app_k;
+    a.app_v = app_v;
+    a.app_lens = app_lens;
+    a.app_bf16 = app_dtype == LOOPKV_BF16;
+  }
   for (int i = 0; i < count; ++i) {
     const int st = c->storage[first + i];
     a.cells[i].pool_off = c->pool_off[st];
@@ -492,18 +500,26 @@ loopkv_status enqueue_step(loopkv_ctx* c, hipStream_t s, const uint8_t* k, const
   const size_t q_cell = (size_t)n_seqs * H * D * dtype_bytes(q_dtype);
   const size_t o_cell = (size_t)n_seqs * H * D * dtype_bytes(out_dtype);
   const size_t m_cell = (size_t)n_seqs * H * ((max_len + 31) / 32);
+  // With one query head per KV head, a storing cell's append runs inside its decode launch:
+  // the workgroup of each (sequence, KV head) appends the token and then decodes the row (in a
+  // split decode, the last split's workgroup, which alone reads the appended token's group).
+  // With grouped queries several rows read one KV head, so the append is its own launch.
+  const bool fuse = c->kvh == H;
   for (int i = 0; i < L * NL; ++i) {
     const int loop = i / NL, layer = i % NL;
     const bool share = c->kinds[i] == LOOPKV_CELL_SHARE;
     loopkv_status st;
-    if (!share) {
+    if (!share && !fuse) {
       st = loopkv_append(c, s, loop, layer, k + i * kv_cell, v + i * kv_cell, kv_dtype, n_seqs, 1, seq_slots,
                          block_table, bt_stride, before);
       if (st != LOOPKV_OK) return st;
     }
+    const bool app = !share && fuse;
     st = decode_common(c, s, loop, layer, q + i * q_cell, q_dtype, n_seqs, seq_slots, block_table, bt_stride,
                        share ? before : after, max_len, tau, sm_scale, out + i * o_cell, out_dtype,
-                       sel_mask ? sel_mask + i * m_cell : nullptr, n_split, scratch, scratch_bytes, false);
+                       sel_mask ? sel_mask + i * m_cell : nullptr, n_split, scratch, scratch_bytes, false, false,
+                       app ? k + i * kv_cell : nullptr, app ? v + i * kv_cell : nullptr, kv_dtype,
+                       app ? before : nullptr);
     if (st != LOOPKV_OK) return st;
   }
   hipError_t e = lkv::launch_advance_lens(before, after, n_seqs, s);

@@ -8,8 +8,10 @@ append, every decode, the length update) into a HIP graph once; each launch repl
 
 Checks: every launch equals the same step run call by call on an identical cache, bit for
 bit, with eager work and synchronizations between launches; one-workgroup and split decodes,
-grouped queries and groups of 64; rows of the final state against the fp64 oracle (a reuse
-cell over the final loop's history without the step's token).
+grouped queries and groups of 64; the records and tails the graph's appends wrote (inside the
+decode launches when every KV head has one query head) equal those of the append calls; rows of
+the final state against the fp64 oracle (a reuse cell over the final loop's history without the
+step's token).
 """
 import numpy as np
 import pytest
@@ -93,6 +95,18 @@ def test_gpu_step_graph_launches_equal_eager(n_split, Hkv, group):
     assert torch.equal(slb.cpu(), torch.tensor([n + STEPS for n in cfg.lengths], dtype=torch.int32))
     assert torch.equal(sla.cpu(), torch.tensor([n + STEPS + 1 for n in cfg.lengths], dtype=torch.int32))
     g.close()
+    # the graph's appends (inside the decode launches with one query head per KV head) wrote the
+    # same records and tails as the append calls
+    G = cfg.group
+    for c in ea.storing_cells():
+        for b, n0 in enumerate(cfg.lengths):
+            n = n0 + STEPS
+            for h in range(cfg.kv_heads):
+                for j in range(G * (n // G) // 16):
+                    assert np.array_equal(ea.record(c, b, h, j), gb.record(c, b, h, j)), f"record c={c} b={b} h={h} j={j}"
+                ta, tb = ea.tail(c, b, h), gb.tail(c, b, h)
+                for t in range(G * (n // G), n):
+                    assert np.array_equal(ta[:, t % G], tb[:, t % G]), f"tail c={c} b={b} h={h} t={t}"
 
     q = qs[-1]
     o_last, s_last = ref[-1]

@@ -5,11 +5,11 @@
  * Transformers" (arXiv:2611.04137), Abstract. A looped transformer keeps a KV
  * cache per (loop, layer) cell; each cell is stored as 4-bit, as 2-bit, or as
  * a reuse of the final loop's KV of the same layer (abstract: the sentence on
- * the one-time offline profile). While decoding, each loop reads the high 2
- * bits of every 4-bit value and fetches the low bits only where its own
- * attention weights require 4-bit precision (abstract: the sentence on
- * decoding); values with low attention are read at 2 bits, never skipped
- * (abstract: the sentence on skipping). KIVI-4, uniform 4-bit quantization,
+ * the one-time offline profile). A decoding loop scores every key from the
+ * upper half of its 4-bit code and loads the lower half only for the tokens
+ * whose weight in that loop is large enough to need the full code (abstract:
+ * the sentence on decoding); tokens of small weight still count, read at 2
+ * bits, and are never dropped (abstract: the sentence on skipping). KIVI-4, uniform 4-bit quantization,
  * is the baseline run on the same kernel (abstract: the serving sentence).
  *
  * The abstract gives no formula; this library fixes:

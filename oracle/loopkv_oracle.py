@@ -11,9 +11,9 @@ shape:
 * every (loop, layer) cell picks 4-bit storage, 2-bit storage, or reuse of the
   final loop's KV of that layer (abstract, the sentence on the one-time
   offline profile);
-* while decoding, each loop reads the high 2 bits of every 4-bit value and
-  fetches the low bits only where its own attention weights call for 4-bit
-  precision (abstract, the sentence on decoding);
+* a decoding loop scores every key from the upper half of its 4-bit code and
+  loads the lower half only for tokens whose weight in that loop is large enough
+  to need the full code (abstract, the sentence on decoding);
 * low-attention values are not skipped, since skipping compounds errors across
   loops (abstract, the sentence on skipping);
 * KIVI-4, uniform 4-bit quantization, is the baseline (abstract, the serving

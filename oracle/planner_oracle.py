@@ -6,9 +6,9 @@ may use it. It shares no code with the library's planner.
 Source: "LoopKV: Loop-Aware KV Cache Compression for Serving Looped Transformers"
 (arXiv:2611.04137), Abstract: every (loop, layer) cell is stored at 4 bits, at 2 bits,
 or reuses the final loop's KV of its layer (sentence on the one-time offline profile);
-the damages of single cells add up to approximately the damage of the whole model
-(sentence on the measurements on Ouro); the planner minimizes reads under budgets for
-predicted damage and storage (sentence on the planner).
+damages measured one cell at a time roughly add up to the whole model's (sentence on
+the measurements on Ouro); the chosen plan reads as little as possible while its
+predicted damage and its storage stay within their budgets (sentence on the planner).
 
 Readings taken where the abstract is silent:
 

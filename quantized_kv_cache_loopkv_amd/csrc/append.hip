@@ -2,9 +2,9 @@
 //
 // Source: "LoopKV: Loop-Aware KV Cache Compression for Serving Looped
 // Transformers" (arXiv:2611.04137), Abstract — every cell is stored as 4-bit
-// (KIVI-4 style) or 2-bit, and decoding reads the high 2 bits of each 4-bit
-// value apart from its low bits, so 4-bit codes are split into a high and a
-// low 2-bit plane here.
+// (KIVI-4 style) or 2-bit, and a decoding loop can read the upper half of a 4-bit
+// code without its lower half, so 4-bit codes are split into a high and a low
+// 2-bit plane here.
 //
 // Quantizer (KIVI-style asymmetric groups of GS = 32, or 64): K per channel over GS
 // consecutive tokens, V per token over GS consecutive channels;

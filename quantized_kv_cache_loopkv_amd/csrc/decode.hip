@@ -1,11 +1,12 @@
 // Loop-aware decode attention over the per-(loop, layer) mixed-precision KV cache (gfx950).
 //
 // Source: "LoopKV: Loop-Aware KV Cache Compression for Serving Looped
-// Transformers" (arXiv:2611.04137), Abstract: during decoding each loop reads
-// the high 2 bits of every 4-bit value and fetches the low bits only where its
-// own attention weights require 4-bit precision; low-attention values are read
-// at low precision rather than skipped; a reuse cell reads the final loop's KV;
-// KIVI-4 (uniform 4-bit) runs on the same kernel as the baseline.
+// Transformers" (arXiv:2611.04137), Abstract (sentences on decoding, on skipping,
+// on the three storage choices and the serving sentence): a loop scores every key
+// from the upper half of its 4-bit code and loads the lower half only for tokens
+// whose weight in that loop is large enough to need the full code; tokens of small
+// weight still count, read coarsely; a reuse cell reads the final loop's cache; the
+// uniform 4-bit KIVI-4 layout goes through the same kernel as the baseline.
 //
 // One workgroup (8 wave64s) owns one row (cell, sequence, head); a whole plan is
 // one launch of cells x sequences x heads workgroups. The path is HBM-bound with
@@ -152,6 +153,25 @@ __device__ inline float mul_f16lo(float a, uint32_t w) {
   return r;
 }
 __device__ inline float bf16f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// TC consecutive bf16 values of a tail row, read with one 2-, 4- or 8-byte load.
+template <int TC>
+struct TailRow {
+  uint32_t w[(TC + 1) / 2];
+  __device__ inline void load(const uint16_t* p) {
+    if constexpr (TC == 1) w[0] = *p;
+    else if constexpr (TC == 2) w[0] = *reinterpret_cast<const uint32_t*>(p);
+    else {
+      const uint2 v = *reinterpret_cast<const uint2*>(p);
+      w[0] = v.x;
+      w[1] = v.y;
+    }
+  }
+  __device__ inline float f(int i) const {
+    const uint32_t x = w[i / 2];
+    return __uint_as_float(i % 2 ? (x & 0xffff0000u) : (x << 16));
+  }
+};
 __device__ inline uint32_t w4(const uint4& v, int i) { return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w; }
 
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
@@ -887,7 +907,14 @@ __device__ __forceinline__ void row_body(const DecodeArgs& a, const RW& r, const
     for (int idx = tid; idx < a.n_split * D; idx += kThreads)
       pre_parts[idx] = parts[(size_t)(idx / D) * (2 + D) + 2 + idx % D];
   }
+  // The row's coarse (M, L) from the partials: with tau L > 1 no token is selected (see the
+  // selection below) and the score line is not needed.
+  bool stage_scores = SPARSE && PH == PH_FINISH;
   if constexpr (SPARSE && PH == PH_FINISH) {
+    const float Mf = wave_max(part_m);
+    stage_scores = !(a.tau * wave_sum(part_m > -INFINITY ? part_l * __expf(part_m - Mf) : 0.f) > 1.f);
+  }
+  if (stage_scores) {
     // the row's coarse scores (tail included) from its scratch line into LDS: eight
     // independent 16-byte loads per thread in flight at once
     const float4* g4 = reinterpret_cast<const float4*>(a.part_scores + orow * (size_t)a.split_row_stride);
@@ -981,32 +1008,49 @@ __device__ __forceinline__ void row_body(const DecodeArgs& a, const RW& r, const
     if (s + 2 < steps) issue_v(s + 2, vb0);
     step_v(s + 1, vb1, wgt);
   }
-  // ---- tail (exact bf16): tokens n_q + w, n_q + w + 8, ...; tacc: channels lane + 64 i
-  float tacc[D / 64];
+  // ---- tail (exact bf16): tokens n_q + w, n_q + w + 8, ...; a lane holds the TC contiguous
+  // channels lane TC .. lane TC + TC - 1 (tacc), read with one load per row. A wave requests the
+  // K and V rows of TB of its tail tokens at once, then works through them, so the tail costs
+  // one memory round trip per TB tokens instead of one per token.
+  constexpr int TC = D / 64;
+  constexpr int TB = 2;
+  float tacc[TC];
 #pragma unroll
-  for (int i = 0; i < D / 64; ++i) tacc[i] = 0.f;
+  for (int i = 0; i < TC; ++i) tacc[i] = 0.f;
   const bool has_tail = PH == PH_ROW || (PH == PH_PART && split == a.n_split - 1);
   float tl = 0.f;   // SKIP: the tail's weight (lane 0)
-  for (int t = r.n_q + w; has_tail && t < r.N; t += kWaves) {
-    const uint16_t* kt = r.tail + (size_t)(t % GS) * D;
-    float p = 0.f;
+  for (int t0 = r.n_q + w; has_tail && t0 < r.N; t0 += TB * kWaves) {
+    TailRow<TC> kr[TB], vr[TB];
 #pragma unroll
-    for (int i = 0; i < D / 64; ++i) p = fmaf(sm.qs[lane + 64 * i], bf16f(kt[lane + 64 * i]), p);
-    p = uniform(wave_sum(p));
-    if (lane == 0) scores[t] = p;
-    if (p > st.m) {
-      const float f = st.raise(p);
-#pragma unroll
-      for (int i = 0; i < D / 64; ++i) tacc[i] *= f;
-      if constexpr (SKIP) tl *= f;
+    for (int k = 0; k < TB; ++k) {
+      const int t = t0 + k * kWaves;
+      if (t < r.N) {
+        kr[k].load(r.tail + (size_t)(t % GS) * D + lane * TC);
+        vr[k].load(r.tail + (size_t)(GS + t % GS) * D + lane * TC);
+      }
     }
-    const float wgt = __expf(p - st.m);
-    if (lane == 0) st.lsum += wgt;
-    if constexpr (SKIP)
-      if (lane == 0) tl += wgt;
-    const uint16_t* vt = r.tail + (size_t)(GS + t % GS) * D;
 #pragma unroll
-    for (int i = 0; i < D / 64; ++i) tacc[i] = fmaf(wgt, bf16f(vt[lane + 64 * i]), tacc[i]);
+    for (int k = 0; k < TB; ++k) {
+      const int t = t0 + k * kWaves;
+      if (t >= r.N) break;   // uniform over the wave
+      float p = 0.f;
+#pragma unroll
+      for (int i = 0; i < TC; ++i) p = fmaf(sm.qs[lane * TC + i], kr[k].f(i), p);
+      p = uniform(wave_sum(p));
+      if (lane == 0) scores[t] = p;
+      if (p > st.m) {
+        const float f = st.raise(p);
+#pragma unroll
+        for (int i = 0; i < TC; ++i) tacc[i] *= f;
+        if constexpr (SKIP) tl *= f;
+      }
+      const float wgt = __expf(p - st.m);
+      if (lane == 0) st.lsum += wgt;
+      if constexpr (SKIP)
+        if (lane == 0) tl += wgt;
+#pragma unroll
+      for (int i = 0; i < TC; ++i) tacc[i] = fmaf(wgt, vr[k].f(i), tacc[i]);
+    }
   }
 
   // ---- selection (4-bit target, 0 < tau <= 1) and corrections
@@ -1031,15 +1075,19 @@ __device__ __forceinline__ void row_body(const DecodeArgs& a, const RW& r, const
     if (st.m > -INFINITY) {
       const float f = st.raise(M);
 #pragma unroll
-      for (int i = 0; i < D / 64; ++i) tacc[i] *= f;
+      for (int i = 0; i < TC; ++i) tacc[i] *= f;
       if constexpr (SKIP) tl *= f;
     }
     st.m = M;   // every wave now shares the reference M
     if constexpr (SKIP) st.lsum = tl;   // the quantized tokens' coarse weights served the selection only
     float removed = 0.f;   // coarse weight taken out by the corrections
-    // exp(s - M) / L >= tau  <=>  s >= M + ln(tau L): one compare per token
+    // exp(s - M) / L >= tau  <=>  s >= M + ln(tau L): one compare per token. With tau L > 1 the
+    // threshold lies above the maximum M, so no token is selected: the row skips the scan and
+    // the gather (the same outcome as running them).
     const float thr = M + logf(a.tau * L);
-    for (int base = 0; base < r.n_q; base += kThreads) {
+    const bool none = a.tau * L > 1.f;
+    const int n_scan = none ? 0 : r.n_q, n_units = none ? 0 : r.n_groups;
+    for (int base = 0; base < n_scan; base += kThreads) {
       const int t = base + tid;
       bool pred = false;
       if (t < r.n_q) pred = scores[t] >= thr;
@@ -1051,7 +1099,7 @@ __device__ __forceinline__ void row_body(const DecodeArgs& a, const RW& r, const
     __syncthreads();
     if (a.sel_mask) {
       uint32_t* smo = a.sel_mask + orow * (size_t)a.sel_words;
-      for (int g = tid; g < a.sel_words; g += kThreads) smo[g] = g < r.n_groups ? selm[g] : 0u;
+      for (int g = tid; g < a.sel_words; g += kThreads) smo[g] = g < n_units ? selm[g] : 0u;
     }
     // Gather: the selected units are dealt round-robin over the waves in unit order (the
     // unit of rank k goes to wave k mod 8), and a wave corrects its units as many at a time as
@@ -1061,7 +1109,7 @@ __device__ __forceinline__ void row_body(const DecodeArgs& a, const RW& r, const
     using GC = Geo<D, MODE_COARSE, GS>;
     float* wfix = scr;   // [2][64]: refined and coarse weights of the step's selected tokens
     int rank0 = 0;       // selected units in the spans before this one (the same in every wave)
-    for (int g64 = 0; g64 < r.n_groups; g64 += 64) {
+    for (int g64 = 0; g64 < n_units; g64 += 64) {
       const int gi = g64 + lane;
       const unsigned long long all = __ballot(gi < r.n_groups && selm[gi < r.n_groups ? gi : 0] != 0u);
       unsigned long long pend = 0;   // this wave's share of the span
@@ -1119,7 +1167,7 @@ __device__ __forceinline__ void row_body(const DecodeArgs& a, const RW& r, const
           const float f = st.raise(wave_max(sref));
           removed *= f;
 #pragma unroll
-          for (int i = 0; i < D / 64; ++i) tacc[i] *= f;
+          for (int i = 0; i < TC; ++i) tacc[i] *= f;
         }
         const float wf = sel ? __expf(s_ref - st.m) : 0.f;
         const float wc = (sel && !SKIP) ? __expf(s_hat - st.m) : 0.f;   // SKIP: nothing to take out
@@ -1184,11 +1232,11 @@ __device__ __forceinline__ void row_body(const DecodeArgs& a, const RW& r, const
       st.lsum = ls;
       exact_v_pass<D, GS>(r, scores, selm, lane, w, st.acc);
 #pragma unroll
-      for (int i = 0; i < D / 64; ++i) tacc[i] = 0.f;
+      for (int i = 0; i < TC; ++i) tacc[i] = 0.f;
       for (int t = r.n_q + w; t < r.N; t += kWaves) {
         const uint16_t* vt = r.tail + (size_t)(GS + t % GS) * D;
 #pragma unroll
-        for (int i = 0; i < D / 64; ++i) tacc[i] = fmaf(scores[t], bf16f(vt[lane + 64 * i]), tacc[i]);
+        for (int i = 0; i < TC; ++i) tacc[i] = fmaf(scores[t], bf16f(vt[lane * TC + i]), tacc[i]);
       }
     }
   } else if constexpr (PH != PH_PART) {
@@ -1225,7 +1273,7 @@ __device__ __forceinline__ void row_body(const DecodeArgs& a, const RW& r, const
 #pragma unroll
   for (int c = 0; c < VCH; ++c) red[tid * VCH + c] = st.acc[c] * fw;
 #pragma unroll
-  for (int i = 0; i < D / 64; ++i) tred[w * D + lane + 64 * i] = tacc[i] * fw;
+  for (int i = 0; i < TC; ++i) tred[w * D + lane * TC + i] = tacc[i] * fw;
   __syncthreads();
   float fws[kWaves];
   float Lt = 0.f;

@@ -2,8 +2,10 @@
 //
 // "LoopKV: Loop-Aware KV Cache Compression for Serving Looped Transformers"
 // (arXiv:2611.04137), Abstract: each cell is stored at 4 bits, at 2 bits or reuses the
-// final loop's KV of its layer; single-cell damages add up to approximately the model's
-// damage; the planner minimizes reads under budgets for predicted damage and storage.
+// final loop's KV of its layer; the damages measured cell by cell roughly add up to the
+// model's (sentence on the measurements on Ouro); the plan reads as little as possible
+// while its predicted damage and its storage stay within their budgets (sentence on the
+// planner).
 // With additive damage, reads and storage this is a multiple-choice knapsack with two
 // budgets; it is solved exactly here.
 //

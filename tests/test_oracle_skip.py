@@ -2,8 +2,9 @@
 skipping low-attention values; CPU only).
 
 "LoopKV: Loop-Aware KV Cache Compression for Serving Looped Transformers" (arXiv:2611.04137),
-Abstract: skipping low-attention values to save reads makes errors compound across loops,
-which is why the method reads unselected tokens at 2 bits instead. The skip mode keeps the
+Abstract (sentence on skipping): dropping the values of small attention weight to save
+reads lets errors grow from loop to loop, which is why the method reads unselected tokens
+at 2 bits instead. The skip mode keeps the
 same coarse pass and selection and drops the unselected quantized tokens.
 
 * S1  tau = 0 keeps every token: equals full 4-bit attention (closed form);

@@ -1,8 +1,9 @@
 """The library's planner (loopkv_plan_search, host code) against the brute-force oracle (CPU).
 
 "LoopKV: Loop-Aware KV Cache Compression for Serving Looped Transformers" (arXiv:2611.04137),
-Abstract: the planner minimizes reads under budgets for predicted (additive) damage and
-storage, choosing 4-bit, 2-bit or final-loop reuse per (loop, layer) cell.
+Abstract (sentence on the planner): per (loop, layer) cell the planner picks 4-bit, 2-bit or
+final-loop reuse so that reads are least while predicted (additive) damage and storage stay
+within budget.
 
 Costs are dyadic rationals (multiples of 2^-10), so every sum is exact in float64 and both
 sides decide feasibility identically. Several plans can share the least reads: the total

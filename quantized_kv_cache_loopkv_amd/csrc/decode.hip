@@ -762,11 +762,18 @@ __device__ void exact_v_pass(const RW& r, const float* weights, const uint32_t* 
   }
 }
 
+// Bit m of an 8-bit value to bit 4m (m = 0..7).
+__device__ inline uint32_t spread4(uint32_t x) {
+  x = (x | (x << 12)) & 0x000F000Fu;
+  x = (x | (x << 6)) & 0x03030303u;
+  return (x | (x << 3)) & 0x11111111u;
+}
+
 // ----------------------------------------------------------------------------- LDS sizes
 __host__ __device__ inline size_t pad4(size_t n) { return (n + 3) / 4 * 4; }   // keep 16-byte alignment
 __host__ __device__ inline size_t lds_lpad(int max_len) { return ((size_t)max_len + 63) / 64 * 64; }
 __host__ __device__ inline size_t lds_region_a(int max_len, int D) {
-  const size_t need = (size_t)kThreads * (D / 16) + (size_t)kWaves * D;
+  const size_t need = (size_t)kWaves * D;   // the merge's wave vectors
   const size_t lp = lds_lpad(max_len);
   return pad4(lp > need ? lp : need);
 }
@@ -784,13 +791,13 @@ __host__ __device__ inline size_t finish_lds_floats(int max_len, int D, int n_sp
 }
 
 struct Smem {
-  float* scores;    // [lpad]; at the end: [kThreads][VCH] partials, then [kWaves][D] tail partials
+  float* scores;    // [lpad]; at the end: [kWaves][D] the waves' value vectors
   uint32_t* selm;   // [lpad / 32]
   uint32_t* boff;   // [lpad / 16] record offset of each logical block, 256-byte units
   float* qs;        // [D]
   float* qperm;     // [D] sigma q in K-meta position order
   float* wscr;      // [kWaves][kWaveScratch]
-  float* misc;      // [96]: per wave m, l, removed weight (0..23), constant terms [kWaves][NE] (32..)
+  float* misc;      // [96]: per wave m, l, removed weight (0..23); the partials' factors (32..95)
 };
 
 // ----------------------------------------------------------------------------- row body
@@ -871,8 +878,18 @@ __device__ void fused_append(const DecodeArgs& a, const DecodeCell& cell, int b,
 // SKIP (with SPARSE, PH_ROW): the token-skipping ablation. The same coarse pass and
 // selection, but the values are not streamed and the unselected quantized tokens leave the
 // attention: the softmax runs over the selected tokens (at 4 bits) and the tail only.
+// What a finishing launch reads of its row's partials, requested at the launch's start: lane
+// i of every wave holds partial i's (m, l) (n_split <= 64); the partials' value vectors are
+// staged in LDS after the row's regions when they fit (pre), else the merge loads them.
+struct FinishIn {
+  const float* parts = nullptr;
+  float* pre = nullptr;
+  float m = -INFINITY, l = 0.f;
+};
+
 template <int D, int GS, int MODE, bool SPARSE, int PH, bool SKIP = false, class RW>
-__device__ __forceinline__ void row_body(const DecodeArgs& a, const RW& r, const Smem& sm, size_t orow, int split) {
+__device__ __forceinline__ void row_body(const DecodeArgs& a, const RW& r, const Smem& sm, size_t orow, int split,
+                                         const FinishIn& fin) {
   using G = Geo<D, MODE, GS>;
   using KS = KStep<D, MODE, false, GS>;
   using VS = VStep<D, MODE, GS>;
@@ -886,27 +903,13 @@ __device__ __forceinline__ void row_body(const DecodeArgs& a, const RW& r, const
   float* misc = sm.misc;
   constexpr int NE = G::NE;
   constexpr int VCH = G::VCH;
-  static_assert(32 + kWaves * NE <= 96, "constant terms of every wave fit the exchange words");
 
   Acc<VCH> st;
   st.zero();
   KS::fill_qperm(sm.qs, sm.qperm);
-  // PH_FINISH: lane i of every wave holds partial i's (m, l) (n_split <= 64)
-  const float* parts = PH == PH_FINISH ? a.part + orow * (size_t)a.n_split * (2 + D) : nullptr;
-  float part_m = -INFINITY, part_l = 0.f;
-  if (PH == PH_FINISH && lane < a.n_split) {
-    part_m = parts[(size_t)lane * (2 + D)];
-    part_l = parts[(size_t)lane * (2 + D) + 1];
-  }
-  // PH_FINISH requests everything else it reads from the split scratch here as well, so the
-  // launch waits for memory once: the partials' values into LDS after the row's regions
-  // (when they fit; else the merge loads them), and (selecting rows) the coarse score line.
-  float* pre_parts = PH == PH_FINISH && finish_parts_in_lds(a.max_len, D, a.n_split)
-                         ? sm.misc + 96 : nullptr;
-  if (pre_parts) {
-    for (int idx = tid; idx < a.n_split * D; idx += kThreads)
-      pre_parts[idx] = parts[(size_t)(idx / D) * (2 + D) + 2 + idx % D];
-  }
+  const float* parts = fin.parts;
+  const float part_m = fin.m, part_l = fin.l;
+  float* pre_parts = fin.pre;
   // The row's coarse (M, L) from the partials: with tau L > 1 no token is selected (see the
   // selection below) and the score line is not needed.
   bool stage_scores = SPARSE && PH == PH_FINISH;
@@ -997,17 +1000,26 @@ __device__ __forceinline__ void row_body(const DecodeArgs& a, const RW& r, const
     issue_k(0, kb0);
     issue_v(0, vb0);
   }
+  // Waves w and w + 4 share a SIMD, where the older wave wins issue ties; left alone, waves
+  // 4..7 finish their steps well after waves 0..3 and the merge waits for them. The two take
+  // turns at the higher priority instead: one step each per loop round.
+  const bool hi_half = w >= 4;
   for (int s = 0; s < steps; s += 2) {
+    if (hi_half) __builtin_amdgcn_s_setprio(1);
+    else __builtin_amdgcn_s_setprio(0);
     if (s + 1 < steps) issue_k(s + 1, kb1);
     float wgt = step_k(s, kb0);
     if (s + 1 < steps) issue_v(s + 1, vb1);
     step_v(s, vb0, wgt);
     if (s + 1 >= steps) break;
+    if (hi_half) __builtin_amdgcn_s_setprio(0);
+    else __builtin_amdgcn_s_setprio(1);
     if (s + 2 < steps) issue_k(s + 2, kb0);
     wgt = step_k(s + 1, kb1);
     if (s + 2 < steps) issue_v(s + 2, vb0);
     step_v(s + 1, vb1, wgt);
   }
+  __builtin_amdgcn_s_setprio(0);
   // ---- tail (exact bf16): tokens n_q + w, n_q + w + 8, ...; a lane holds the TC contiguous
   // channels lane TC .. lane TC + TC - 1 (tacc), read with one load per row. A wave requests the
   // K and V rows of TB of its tail tokens at once, then works through them, so the tail costs
@@ -1085,18 +1097,33 @@ __device__ __forceinline__ void row_body(const DecodeArgs& a, const RW& r, const
     // threshold lies above the maximum M, so no token is selected: the row skips the scan and
     // the gather (the same outcome as running them).
     const float thr = M + logf(a.tau * L);
-    const bool none = a.tau * L > 1.f;
-    const int n_scan = none ? 0 : r.n_q, n_units = none ? 0 : r.n_groups;
-    for (int base = 0; base < n_scan; base += kThreads) {
-      const int t = base + tid;
-      bool pred = false;
-      if (t < r.n_q) pred = scores[t] >= thr;
-      const unsigned long long bal = __ballot(pred);
-      const int g0 = (base + 64 * w) / kUnit;
-      if (lane == 0 && g0 < r.n_groups) selm[g0] = (uint32_t)bal;
-      if (lane == 0 && g0 + 1 < r.n_groups) selm[g0 + 1] = (uint32_t)(bal >> 32);
+    const bool none = a.tau * L > 1.f;   // the same in every wave
+    const int n_units = none ? 0 : r.n_groups;
+    if (!none) {
+      // Selection words: wave w scans 256 tokens per round, lane l the four tokens 4l .. 4l + 3
+      // with one LDS read; ballot k holds bit k of every lane's four, and the word of unit u
+      // (lanes 8u .. 8u + 7, token 4m + k of the unit at bit 4m + k) interleaves byte u of
+      // the four ballots.
+      for (int base = 256 * w; base < r.n_q; base += 256 * kWaves) {
+        const int t0 = base + 4 * lane;   // n_q is a multiple of 32: all four or none valid
+        bool p0 = false, p1 = false, p2 = false, p3 = false;
+        if (t0 < r.n_q) {
+          const float4 v = *reinterpret_cast<const float4*>(scores + t0);
+          p0 = v.x >= thr;
+          p1 = v.y >= thr;
+          p2 = v.z >= thr;
+          p3 = v.w >= thr;
+        }
+        const unsigned long long b0 = __ballot(p0), b1 = __ballot(p1), b2 = __ballot(p2), b3 = __ballot(p3);
+        const int g = base / kUnit + lane;
+        if (lane < 8 && g < r.n_groups) {
+          const int sh = 8 * lane;
+          selm[g] = spread4((uint32_t)(b0 >> sh) & 0xffu) | (spread4((uint32_t)(b1 >> sh) & 0xffu) << 1) |
+                    (spread4((uint32_t)(b2 >> sh) & 0xffu) << 2) | (spread4((uint32_t)(b3 >> sh) & 0xffu) << 3);
+        }
+      }
+      __syncthreads();
     }
-    __syncthreads();
     if (a.sel_mask) {
       uint32_t* smo = a.sel_mask + orow * (size_t)a.sel_words;
       for (int g = tid; g < a.sel_words; g += kThreads) smo[g] = g < n_units ? selm[g] : 0u;
@@ -1199,44 +1226,46 @@ __device__ __forceinline__ void row_body(const DecodeArgs& a, const RW& r, const
         wave_sync_lds();
       }
     }
-    // Cancellation check over the row.
-    const float lw2 = wave_sum(st.lsum), rw = wave_sum(removed);
-    __syncthreads();
-    if (lane == 0) {
-      misc[w] = st.m;
-      misc[8 + w] = lw2;
-      misc[16 + w] = rw;
-    }
-    __syncthreads();
-    float Ms = misc[0];
-    for (int i = 1; i < kWaves; ++i) Ms = fmaxf(Ms, misc[i]);
-    float Lp = 0.f, Rm = 0.f;
-    for (int i = 0; i < kWaves; ++i) {
-      const float f = __expf(misc[i] - Ms);
-      Lp += misc[8 + i] * f;
-      Rm += misc[16 + i] * f;
-    }
-    if (PH == PH_FINISH) Lp += L * __expf(M - Ms);   // the streamed part's coarse weight
-    if (Rm > 8.f * Lp) {   // recompute the row's V from the final scores
-      use_parts = false;
+    // Cancellation check over the row (nothing removed when nothing was selected).
+    if (!none) {
+      const float lw2 = wave_sum(st.lsum), rw = wave_sum(removed);
       __syncthreads();
-      float ls = 0.f;
-      for (int t = tid; t < r.N; t += kThreads) {
-        const float wgt = __expf(scores[t] - Ms);
-        scores[t] = wgt;
-        ls += wgt;
+      if (lane == 0) {
+        misc[w] = st.m;
+        misc[8 + w] = lw2;
+        misc[16 + w] = rw;
       }
       __syncthreads();
-      st.zero();
-      st.m = Ms;
-      st.lsum = ls;
-      exact_v_pass<D, GS>(r, scores, selm, lane, w, st.acc);
+      float Ms = misc[0];
+      for (int i = 1; i < kWaves; ++i) Ms = fmaxf(Ms, misc[i]);
+      float Lp = 0.f, Rm = 0.f;
+      for (int i = 0; i < kWaves; ++i) {
+        const float f = __expf(misc[i] - Ms);
+        Lp += misc[8 + i] * f;
+        Rm += misc[16 + i] * f;
+      }
+      if (PH == PH_FINISH) Lp += L * __expf(M - Ms);   // the streamed part's coarse weight
+      if (Rm > 8.f * Lp) {   // recompute the row's V from the final scores
+        use_parts = false;
+        __syncthreads();
+        float ls = 0.f;
+        for (int t = tid; t < r.N; t += kThreads) {
+          const float wgt = __expf(scores[t] - Ms);
+          scores[t] = wgt;
+          ls += wgt;
+        }
+        __syncthreads();
+        st.zero();
+        st.m = Ms;
+        st.lsum = ls;
+        exact_v_pass<D, GS>(r, scores, selm, lane, w, st.acc);
 #pragma unroll
-      for (int i = 0; i < TC; ++i) tacc[i] = 0.f;
-      for (int t = r.n_q + w; t < r.N; t += kWaves) {
-        const uint16_t* vt = r.tail + (size_t)(GS + t % GS) * D;
+        for (int i = 0; i < TC; ++i) tacc[i] = 0.f;
+        for (int t = r.n_q + w; t < r.N; t += kWaves) {
+          const uint16_t* vt = r.tail + (size_t)(GS + t % GS) * D;
 #pragma unroll
-        for (int i = 0; i < TC; ++i) tacc[i] = fmaf(scores[t], bf16f(vt[lane * TC + i]), tacc[i]);
+          for (int i = 0; i < TC; ++i) tacc[i] = fmaf(scores[t], bf16f(vt[lane * TC + i]), tacc[i]);
+        }
       }
     }
   } else if constexpr (PH != PH_PART) {
@@ -1248,17 +1277,18 @@ __device__ __forceinline__ void row_body(const DecodeArgs& a, const RW& r, const
   }
 
   // ---- merge the waves (the exact pass writes in the value-lane layout of the coarse
-  // step, which is this mode's layout whenever it runs)
+  // step, which is this mode's layout whenever it runs). Each wave folds its value lanes over
+  // the step's blocks with cross-row swaps, adds its constant terms and its tail channels,
+  // scales by exp(m_w - M) and leaves one D-vector in LDS; four lanes per channel then add
+  // the waves (and, finishing a split row, the partials) in a fixed order.
   const float lsum = wave_sum(st.lsum);
   float zs[NE];
 #pragma unroll
   for (int e = 0; e < NE; ++e) zs[e] = wave_sum((lane % NE) == e && lane < G::COOP ? st.accz : 0.f);
-  __syncthreads();   // scores are dead from here on: reuse them for partials
+  __syncthreads();   // scores are dead from here on: reuse them for the wave vectors
   if (lane == 0) {
     misc[w] = st.m;
     misc[8 + w] = lsum;
-#pragma unroll
-    for (int e = 0; e < NE; ++e) misc[32 + w * NE + e] = zs[e];   // NE <= 8: within the 96 words
   }
   __syncthreads();
   float M = misc[0];
@@ -1268,55 +1298,50 @@ __device__ __forceinline__ void row_body(const DecodeArgs& a, const RW& r, const
   if (with_parts) M = fmaxf(M, wave_max(part_m));
   const float part_f = with_parts && part_m > -INFINITY ? __expf(part_m - M) : 0.f;   // lane i: partial i
   const float fw = st.m > -INFINITY ? __expf(st.m - M) : 0.f;
-  float* red = sm.scores;                      // [kThreads][VCH]
-  float* tred = sm.scores + kThreads * VCH;    // [kWaves][D]
+  float* wv = sm.scores;   // [kWaves][D]
+  float* pf = misc + 32;   // [n_split] the partials' factors (n_split <= 64)
+  {
+    float v[VCH];
 #pragma unroll
-  for (int c = 0; c < VCH; ++c) red[tid * VCH + c] = st.acc[c] * fw;
+    for (int c = 0; c < VCH; ++c) {
+      float x = st.acc[c];
+      if constexpr (G::BPS == 4) x = add_halves(add_rows2(x));   // lanes chunk + 16 vb
+      else x = add_halves(x);                                    // lanes chunk + 32 vb
+      v[c] = x;
+    }
+    const int chunk = lane % G::LPB;
+    if (lane < G::LPB) {
 #pragma unroll
-  for (int i = 0; i < TC; ++i) tred[w * D + lane * TC + i] = tacc[i] * fw;
+      for (int c = 0; c < VCH; ++c) {
+        const int e = (chunk * VCH + c) / kUnit;   // the channel's 32-channel slice
+        float z = zs[0];
+#pragma unroll
+        for (int k = 1; k < NE; ++k) z = e == k ? zs[k] : z;
+        wv[w * D + chunk * VCH + c] = (v[c] + z) * fw;
+      }
+    }
+  }
+  wave_sync_lds();   // the wave's value lanes wrote its vector; its tail lanes add theirs
+#pragma unroll
+  for (int i = 0; i < TC; ++i) wv[w * D + lane * TC + i] += tacc[i] * fw;
+  if (with_parts && w == 0 && lane < a.n_split) pf[lane] = part_f;
   __syncthreads();
-  float fws[kWaves];
   float Lt = 0.f;
 #pragma unroll
-  for (int i = 0; i < kWaves; ++i) {
-    fws[i] = misc[i] > -INFINITY ? __expf(misc[i] - M) : 0.f;
-    Lt += misc[8 + i] * fws[i];
-  }
+  for (int i = 0; i < kWaves; ++i) Lt += misc[8 + i] * (misc[i] > -INFINITY ? __expf(misc[i] - M) : 0.f);
   if (with_parts) Lt += wave_sum(part_l * part_f);
-  for (int d = tid; d < D; d += kThreads) {
-    const int chunk = d / VCH, c = d % VCH;
-    float o = 0.f;
-#pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww) {
-      o += misc[32 + ww * NE + d / kUnit] * fws[ww];
-#pragma unroll
-      for (int vb = 0; vb < G::BPS; ++vb) o += red[(ww * 64 + vb * G::LPB + chunk) * VCH + c];
-      o += tred[ww * D + d];
-    }
-    if (with_parts && pre_parts) {   // the partials' values, from LDS
-      float ps[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-      for (int i0 = 0; i0 < a.n_split; i0 += 8) {
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const int i = i0 + k;
-          const float fi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(part_f), i & 63));
-          if (i < a.n_split) ps[k] = fmaf(pre_parts[i * D + d], fi, ps[k]);
-        }
+  const int j = tid & 3;
+  for (int d = tid >> 2; d < D; d += kThreads / 4) {   // four lanes per channel (quad-uniform)
+    float o = wv[j * D + d] + wv[(j + 4) * D + d];
+    if (with_parts) {
+      for (int i = j; i < a.n_split; i += 4) {
+        const float pv = pre_parts ? pre_parts[i * D + d] : parts[(size_t)i * (2 + D) + 2 + d];
+        o = fmaf(pv, pf[i], o);
       }
-      o += ((ps[0] + ps[1]) + (ps[2] + ps[3])) + ((ps[4] + ps[5]) + (ps[6] + ps[7]));
-    } else if (with_parts) {   // the partials' values, all loads in flight together
-      const float* pv = parts + 2 + d;
-      float ps[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-      for (int i0 = 0; i0 < a.n_split; i0 += 8) {
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const int i = i0 + k;
-          const float fi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(part_f), i & 63));
-          if (i < a.n_split) ps[k] = fmaf(pv[(size_t)i * (2 + D)], fi, ps[k]);
-        }
-      }
-      o += ((ps[0] + ps[1]) + (ps[2] + ps[3])) + ((ps[4] + ps[5]) + (ps[6] + ps[7]));
     }
+    o += dpp<0xB1>(o);   // quad_perm [1,0,3,2]
+    o += dpp<0x4E>(o);   // quad_perm [2,3,0,1]
+    if (j != 0) continue;
     if constexpr (PH == PH_PART) {   // unnormalized, relative to M
       float* pp = a.part + (orow * (size_t)a.n_split + split) * (2 + D);
       if (d == 0) {
@@ -1350,6 +1375,44 @@ constexpr int decode_waves_per_simd() {
   return (D == 256 && (VAR == VAR_DENSE || VAR == VAR_KIVI)) ? 2 : kWavesPerSimd;
 }
 
+// Finishing launch of a split row that selects nothing (every row of a launch whose target
+// is not 4-bit, or with tau L > 1): the output is the partials' merge alone, read by four
+// lanes per channel in the same order as the general merge (whose wave vectors are zero
+// here), so the result is the same bit for bit. The partials' factors reach the lanes by
+// lane shuffles; no workgroup barrier is needed past the staging of the value vectors.
+template <int D>
+__device__ void finish_from_partials(const DecodeArgs& a, const FinishIn& fin, size_t orow, int n_groups,
+                                     uint32_t fill) {
+  const int tid = threadIdx.x;
+  if (fin.pre) __syncthreads();   // the staged value vectors
+  const float M = wave_max(fin.m);   // lanes >= n_split hold -inf
+  const float f = fin.m > -INFINITY ? __expf(fin.m - M) : 0.f;
+  const float Lt = wave_sum(fin.l * f);
+  const int j = tid & 3;
+  for (int d = tid >> 2; d < D; d += kThreads / 4) {   // quad-uniform
+    float o = 0.f;
+    for (int i = j; i < a.n_split; i += 4) {
+      const float pv = fin.pre ? fin.pre[i * D + d] : fin.parts[(size_t)i * (2 + D) + 2 + d];
+      o = fmaf(pv, __shfl(f, i), o);
+    }
+    o += dpp<0xB1>(o);   // quad_perm [1,0,3,2]
+    o += dpp<0x4E>(o);   // quad_perm [2,3,0,1]
+    if (j != 0) continue;
+    o = o / Lt;
+    if (a.out_bf16) {
+      uint32_t u = __float_as_uint(o);
+      u += 0x7fffu + ((u >> 16) & 1u);
+      reinterpret_cast<uint16_t*>(a.out)[orow * D + d] = (uint16_t)(u >> 16);
+    } else {
+      reinterpret_cast<float*>(a.out)[orow * D + d] = o;
+    }
+  }
+  if (a.sel_mask) {
+    uint32_t* smo = a.sel_mask + orow * (size_t)a.sel_words;
+    for (int g = tid; g < a.sel_words; g += kThreads) smo[g] = g < n_groups ? fill : 0u;
+  }
+}
+
 template <int D, int GS, int VAR, int PH, bool BIG>
 __global__ void __launch_bounds__(kThreads, (decode_waves_per_simd<D, VAR>())) k_decode(DecodeArgs a) {
   extern __shared__ float smem[];
@@ -1380,8 +1443,6 @@ __global__ void __launch_bounds__(kThreads, (decode_waves_per_simd<D, VAR>())) k
     fused_append<D, GS>(a, cell, b, kh, reinterpret_cast<unsigned char*>(smem));
     __syncthreads();   // the appended token and records are written before the row reads them
   }
-  const int N = a.seq_lens[b];
-
   const size_t lp = lds_lpad(a.max_len);
   Smem sm;
   sm.scores = smem;
@@ -1391,6 +1452,24 @@ __global__ void __launch_bounds__(kThreads, (decode_waves_per_simd<D, VAR>())) k
   sm.qperm = sm.qs + D;
   sm.wscr = sm.qperm + D;
   sm.misc = sm.wscr + kWaves * kWaveScratch;
+
+  // PH_FINISH: the row's partials depend on nothing the prologue reads, so they are
+  // requested first and their latency overlaps the prologue's
+  FinishIn fin;
+  if constexpr (PH == PH_FINISH) {
+    fin.parts = a.part + orow * (size_t)a.n_split * (2 + D);
+    const int lane = tid & 63;
+    if (lane < a.n_split) {
+      fin.m = fin.parts[(size_t)lane * (2 + D)];
+      fin.l = fin.parts[(size_t)lane * (2 + D) + 1];
+    }
+    if (finish_parts_in_lds(a.max_len, D, a.n_split)) {
+      fin.pre = sm.misc + 96;
+      for (int idx = tid; idx < a.n_split * D; idx += kThreads)
+        fin.pre[idx] = fin.parts[(size_t)(idx / D) * (2 + D) + 2 + idx % D];
+    }
+  }
+  const int N = a.seq_lens[b];
 
   // rows that read nothing: empty (output 0) or invalid (NaN; length above max_len, or a
   // page of the quantized prefix outside the pool)
@@ -1422,6 +1501,31 @@ __global__ void __launch_bounds__(kThreads, (decode_waves_per_simd<D, VAR>())) k
   r.n_q = (N / GS) * GS;
   r.n_groups = r.n_q / kUnit;   // 32-token units of the quantized prefix
 
+  if constexpr (PH == PH_FINISH) {
+    // A row whose prefix maps a page outside the pool has NaN partials (its partial launch
+    // checked the pages and read no record).
+    const int lane = tid & 63;
+    if (__any(lane < a.n_split && fin.m != fin.m)) {
+      empty_row(false);
+      return;
+    }
+    // Rows that select nothing need neither the block table nor the query: the partials
+    // are the row.
+    bool selects = false;
+    if constexpr (VAR == VAR_SPARSE || VAR == VAR_SKIP) {
+      selects = VAR == VAR_SKIP || cell.kind != KIND_Q2;
+      if (VAR == VAR_SPARSE && selects) {
+        const float Mf = wave_max(fin.m);
+        selects = !(a.tau * wave_sum(fin.m > -INFINITY ? fin.l * __expf(fin.m - Mf) : 0.f) > 1.f);
+      }
+    }
+    if (!selects) {
+      const bool full = VAR == VAR_KIVI || (VAR == VAR_DENSE && cell.kind != KIND_Q2);   // every token at 4 bits
+      finish_from_partials<D>(a, fin, orow, r.n_groups, full ? 0xffffffffu : 0u);
+      return;
+    }
+  }
+
   // block table row and sigma * q into LDS
   const int32_t* bt = a.block_table + (size_t)b * a.bt_stride;
   const int nbq = r.n_q / kBlock;
@@ -1445,18 +1549,19 @@ __global__ void __launch_bounds__(kThreads, (decode_waves_per_simd<D, VAR>())) k
 #pragma unroll
   for (int i = 0; i < kWaves; ++i) any_bad |= sm.misc[i] != 0.f;
   if (any_bad) {   // no record of this row is read
+    if (PH == PH_PART && tid == 0) a.part[(orow * (size_t)a.n_split + split) * (2 + D)] = __builtin_nanf("");
     empty_row(false);
     return;
   }
 
   if constexpr (VAR == VAR_KIVI) {
-    row_body<D, GS, MODE_KIVI, false, PH>(a, r, sm, orow, split);
+    row_body<D, GS, MODE_KIVI, false, PH>(a, r, sm, orow, split, fin);
   } else {
-    if (cell.kind == KIND_Q2) row_body<D, GS, MODE_Q2, false, PH>(a, r, sm, orow, split);
-    else if (VAR == VAR_DENSE) row_body<D, GS, MODE_DENSE, false, PH>(a, r, sm, orow, split);
-    else if (VAR == VAR_COARSE) row_body<D, GS, MODE_COARSE, false, PH>(a, r, sm, orow, split);
-    else if (VAR == VAR_SKIP) row_body<D, GS, MODE_COARSE, true, PH, true>(a, r, sm, orow, split);
-    else row_body<D, GS, MODE_COARSE, true, PH>(a, r, sm, orow, split);
+    if (cell.kind == KIND_Q2) row_body<D, GS, MODE_Q2, false, PH>(a, r, sm, orow, split, fin);
+    else if (VAR == VAR_DENSE) row_body<D, GS, MODE_DENSE, false, PH>(a, r, sm, orow, split, fin);
+    else if (VAR == VAR_COARSE) row_body<D, GS, MODE_COARSE, false, PH>(a, r, sm, orow, split, fin);
+    else if (VAR == VAR_SKIP) row_body<D, GS, MODE_COARSE, true, PH, true>(a, r, sm, orow, split, fin);
+    else row_body<D, GS, MODE_COARSE, true, PH>(a, r, sm, orow, split, fin);
   }
 }
 

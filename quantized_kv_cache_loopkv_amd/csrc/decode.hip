@@ -44,6 +44,7 @@
 #include <hip/hip_fp16.h>
 #include <stdint.h>
 #include <math.h>
+#include "loopkv.h"
 #include "layout.h"
 #include "quantize.h"
 
@@ -1282,9 +1283,17 @@ __device__ __forceinline__ void row_body(const DecodeArgs& a, const RW& r, const
   // scales by exp(m_w - M) and leaves one D-vector in LDS; four lanes per channel then add
   // the waves (and, finishing a split row, the partials) in a fixed order.
   const float lsum = wave_sum(st.lsum);
+  // constant terms of each 32-channel slice e: the lanes l = e (mod NE) summed by row
+  // rotates and cross-row swaps; lane e then holds slice e's
+  float zl = lane < G::COOP ? st.accz : 0.f;
+  static_assert(NE == 2 || NE == 4 || NE == 8, "slices per row");
+  zl += dpp<0x128>(zl);                           // row_ror:8
+  if constexpr (NE <= 4) zl += dpp<0x124>(zl);    // row_ror:4
+  if constexpr (NE <= 2) zl += dpp<0x122>(zl);    // row_ror:2
+  zl = add_halves(add_rows2(zl));
   float zs[NE];
 #pragma unroll
-  for (int e = 0; e < NE; ++e) zs[e] = wave_sum((lane % NE) == e && lane < G::COOP ? st.accz : 0.f);
+  for (int e = 0; e < NE; ++e) zs[e] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(zl), e));
   __syncthreads();   // scores are dead from here on: reuse them for the wave vectors
   if (lane == 0) {
     misc[w] = st.m;
@@ -1469,6 +1478,20 @@ __global__ void __launch_bounds__(kThreads, (decode_waves_per_simd<D, VAR>())) k
         fin.pre[idx] = fin.parts[(size_t)(idx / D) * (2 + D) + 2 + idx % D];
     }
   }
+  // PH_PART: the row's block-table entries (every block a row of max_len tokens can have
+  // quantized) are requested together with its length, so the first record loads wait for
+  // one memory round trip less; the entries past the row are never used.
+  constexpr int kBtPer = (LOOPKV_MAX_LEN / kBlock + kThreads - 1) / kThreads;
+  int32_t btv[kBtPer];
+  if constexpr (PH == PH_PART) {
+    const int32_t* bt0 = a.block_table + (size_t)b * a.bt_stride;
+    const int nb_max = a.max_len / kBlock;   // bt_stride pages cover max_len tokens
+#pragma unroll
+    for (int k = 0; k < kBtPer; ++k) {
+      const int j = tid + k * kThreads;
+      btv[k] = j < nb_max ? bt0[j >> a.bt_shift] : 0;
+    }
+  }
   const int N = a.seq_lens[b];
 
   // rows that read nothing: empty (output 0) or invalid (NaN; length above max_len, or a
@@ -1531,9 +1554,21 @@ __global__ void __launch_bounds__(kThreads, (decode_waves_per_simd<D, VAR>())) k
   const int nbq = r.n_q / kBlock;
   const uint32_t rec256 = (uint32_t)(record_bytes(cell.kind, D, GS) / 256);
   int bad_page = 0;
-  for (int j = tid; j < nbq; j += kThreads) {
-    bad_page |= (uint32_t)bt[j >> a.bt_shift] >= (uint32_t)a.num_pages;   // -1 (unmapped) included
-    sm.boff[j] = (record_slot(bt, j, a.bt_shift) * (uint32_t)a.n_kv_heads + (uint32_t)kh) * rec256;
+  if constexpr (PH == PH_PART) {
+#pragma unroll
+    for (int k = 0; k < kBtPer; ++k) {
+      const int j = tid + k * kThreads;
+      if (j < nbq) {
+        bad_page |= (uint32_t)btv[k] >= (uint32_t)a.num_pages;   // -1 (unmapped) included
+        const uint32_t slot_j = ((uint32_t)btv[k] << a.bt_shift) + (uint32_t)(j & ((1 << a.bt_shift) - 1));
+        sm.boff[j] = (slot_j * (uint32_t)a.n_kv_heads + (uint32_t)kh) * rec256;
+      }
+    }
+  } else {
+    for (int j = tid; j < nbq; j += kThreads) {
+      bad_page |= (uint32_t)bt[j >> a.bt_shift] >= (uint32_t)a.num_pages;   // -1 (unmapped) included
+      sm.boff[j] = (record_slot(bt, j, a.bt_shift) * (uint32_t)a.n_kv_heads + (uint32_t)kh) * rec256;
+    }
   }
   for (int d = tid; d < D; d += kThreads) {
     const size_t qi = orow * D + d;

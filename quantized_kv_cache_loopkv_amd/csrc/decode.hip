@@ -176,6 +176,7 @@ struct TailRow {
 __device__ inline uint32_t w4(const uint4& v, int i) { return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w; }
 
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 // Streaming loads (the cache bytes are read once per decode).
 __device__ inline uint4 ld_stream4(const void* p) {
@@ -346,6 +347,14 @@ template <int D, int MODE, bool REFINE, int GS>
 struct KStep {
   using G = Geo<D, MODE, GS>;
   static constexpr int CODE_OFF = REFINE ? off_klo(D, GS) : 0;
+  // Matrix-core path (2-bit codes, 64-token steps of two units): v_mfma_i32_16x16x64_i8 with
+  // the codes as B (column j of tile T = token 4j + T of the step; lane group cg = one code
+  // column of 16 channels, its four bit-pair words) and the coefficient limbs as A (rows
+  // 0..2: limbs 0..2 of the step's first unit, rows 4..6: of its second, other rows zero).
+  // Each token's three limb sums come out exact in 32-bit integers and combine exactly.
+  static constexpr bool MF = !REFINE && !G::KIVI && !G::DENSE && G::TPS == 64 && G::GPS == 2 && (D == 64 || D == 128);
+  static constexpr int NCH = G::COLS / 4;   // 64-channel chunks (MFMA depth)
+  static_assert(!MF || NCH == G::NC, "one 16-byte code load per chunk");
 
   struct Buf {
     uint4 meta, c[G::NC], l[G::DENSE ? G::NC : 1];
@@ -372,6 +381,15 @@ struct KStep {
       b.meta = ld_words<G::CPL>(r.at(2 * g + (pos0 >= D / 2), G::KMETA + 4 * (pos0 % (D / 2))));
     else
       b.meta = ld_words<G::CPL>(r.at(G::GP * (g / G::GU) + pos0 / (D / G::GP), G::KMETA + 4 * (pos0 % (D / G::GP))));
+    if constexpr (MF) {
+      // lane (token quad j, column group cg): tokens 4j .. 4j + 3 of column 4C + cg; the 16
+      // lanes of a quad-of-quads cover four whole consecutive columns of a record
+      const int j = lane % 16, cg = lane / 16;
+      const uint8_t* kq = r.at(2 * groups[j / 8] + (j % 8) / 4, CODE_OFF + (cg * kBlock + 4 * (j % 4)) * 4);
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) b.c[i] = ld_stream4(kq + i * 4 * kBlock * 4);
+      return;
+    }
     // lane cp reads columns cp, cp + CPG, ...: each load instruction covers CPG whole
     // consecutive columns (CPG x 64 contiguous bytes) of each of its records
     const uint8_t* kp = r.at(2 * g + blk, CODE_OFF + (cp * kBlock + 4 * quad) * 4);
@@ -501,12 +519,61 @@ struct KStep {
     if ((lane % (4 / G::CPL)) == 0) {
       uint32_t limb[3];
       transpose3(u, limb);
-      uint32_t* dst = klimb + (gsub * (D / 4) + pos0 / 4) * 3;
+      if constexpr (MF) {
+        // [unit][column][limb][bit pair]: an A row reads its column's four pair words at once
+        const int st = pos0 / 4;   // limb set: column st / 4, bit pair st % 4
+        uint32_t* dst = klimb + (gsub * G::COLS + st / 4) * 12 + st % 4;
+        dst[0] = limb[0] ^ 0x80808080u;   // biased byte -> signed digit
+        dst[4] = limb[1] ^ 0x80808080u;
+        dst[8] = limb[2];
+      } else {
+        uint32_t* dst = klimb + (gsub * (D / 4) + pos0 / 4) * 3;
 #pragma unroll
-      for (int j = 0; j < 2; ++j) dst[j] = limb[j] ^ 0x80808080u;   // biased byte -> signed digit
-      dst[2] = limb[2];
+        for (int j = 0; j < 2; ++j) dst[j] = limb[j] ^ 0x80808080u;   // biased byte -> signed digit
+        dst[2] = limb[2];
+      }
     }
     wave_sync_lds();
+    if constexpr (MF) {
+      const int m = lane % 16, cg = lane / 16;
+      const bool arow = m < 8 && (m & 3) < 3;
+      i32x4_t A[NCH];
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        const uint4 t = *reinterpret_cast<const uint4*>(klimb + ((m / 4) % 2 * G::COLS + 4 * c + cg) * 12 + (m & 3) % 3 * 4);
+        A[c] = arow ? i32x4_t{(int)t.x, (int)t.y, (int)t.z, (int)t.w} : i32x4_t{0, 0, 0, 0};
+      }
+      // the two units' inverse scales and constants (uniform over each unit's 32 lanes)
+      const float inv0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(inv), 0));
+      const float inv1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(inv), 32));
+      const float cst0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cst), 0));
+      const float cst1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cst), 32));
+      float sc[4];
+#pragma unroll
+      for (int T = 0; T < 4; ++T) {
+        i32x4_t acc = {0, 0, 0, 0};
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+          uint32_t mw[4];
+          masked(w4(b.c[c], T), 0u, mw);
+          const i32x4_t bv = {(int)mw[0], (int)mw[1], (int)mw[2], (int)mw[3]};
+          acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[c], bv, acc, 0, 0, 0);
+        }
+        // lanes 0..7: rows 0..3 (unit 0) of columns 0..7; lanes 24..31: rows 4..7 (unit 1)
+        // of columns 8..15; the limb sums recombine exactly (mod 2^32, the true sum fits)
+        const uint32_t v = (uint32_t)acc[0] + ((uint32_t)acc[1] << 8) + ((uint32_t)acc[2] << 16);
+        sc[T] = fmaf(lane >= 16 ? inv1 : inv0, (float)(int)v, lane >= 16 ? cst1 : cst0);
+      }
+      // to one token per lane: token 4j + T of column j sits in lane j (j < 8) or 16 + j
+      wave_sync_lds();   // every lane's A words are read before the scores reuse them
+      float* tr = reinterpret_cast<float*>(klimb);
+      if (lane < 8 || (lane >= 24 && lane < 32))
+        *reinterpret_cast<float4*>(tr + 4 * (lane % 16)) = make_float4(sc[0], sc[1], sc[2], sc[3]);
+      wave_sync_lds();
+      own = true;
+      t_loc = lane;
+      return tr[lane];
+    }
     // Limbs of this lane's NC columns (SPC sets x 3 words each); the four tokens' chains run
     // interleaved, limb 2 first, one column at a time, each recombined exactly.
     constexpr int NCC = 1;   // columns per chain

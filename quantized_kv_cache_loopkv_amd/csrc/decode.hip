@@ -56,7 +56,7 @@ namespace lkv {
 constexpr int kWaves = LKV_WAVES;           // waves per workgroup (one row)
 constexpr int kThreads = 64 * kWaves;
 constexpr int kWavesPerSimd = kWaves / 2;   // two workgroups per CU (LDS-bound)
-constexpr int kWaveScratch = 256;   // words of per-wave LDS scratch
+constexpr int kWaveScratch = 272;   // words of per-wave LDS scratch
 
 enum : int { MODE_COARSE = 0, MODE_DENSE = 1, MODE_Q2 = 2, MODE_KIVI = 3 };
 
@@ -293,12 +293,16 @@ struct Acc {
 
 // ----------------------------------------------------------------------------- step geometry
 // A step covers TPS tokens: 64, or 32 for 4-bit codes at D = 128 and for D = 256, so that
-// every lane reads 32 bytes of K codes and 32 bytes of V codes (16 for 2-bit codes at D = 64).
-template <int D, int MODE, int GS>
+// every lane reads 32 bytes of K codes and 32 bytes of V codes. WIDE: the streaming pass of
+// 2-bit codes at D = 64 takes 128-token steps (four units), so a lane still reads 32 bytes of
+// each and the per-step work that does not scale with D is spread over twice the tokens;
+// the corrections, the exact pass and the merge keep the 64-token geometry (WIDE false).
+template <int D, int MODE, int GS, bool WIDE = true>
 struct Geo {
   static constexpr bool KIVI = MODE == MODE_KIVI;
   static constexpr bool DENSE = MODE == MODE_DENSE;
-  static constexpr int TPS = (D == 256 || ((KIVI || DENSE) && D == 128)) ? 32 : 64;
+  static constexpr bool W128 = WIDE && D == 64 && !KIVI && !DENSE;
+  static constexpr int TPS = W128 ? 128 : (D == 256 || ((KIVI || DENSE) && D == 128)) ? 32 : 64;
   static constexpr int GPS = TPS / kUnit;       // 32-token units per step
   static constexpr int GU = GS / kUnit;         // units per quantization group (1 or 2)
   static constexpr int GP = GS / kBlock;        // records per quantization group (2 or 4)
@@ -329,8 +333,8 @@ struct Geo {
   // quad: the weights reach the weight lanes by quad broadcasts (D = 128, 2-bit codes).
   static constexpr bool QUAD_W = CPG == 4 && LPG == 32 && NE == 4;
   // per-wave scratch (words): K limbs at 0; step weights at 0 once the K limbs are
-  // consumed; V limbs and their inverse scales from 64.
-  static constexpr int S_W = 0, S_VL = 64, S_VI = 64 + BPS * NE * 8;
+  // consumed; V limbs and their inverse scales from max(64, TPS).
+  static constexpr int S_W = 0, S_VL = TPS > 64 ? TPS : 64, S_VI = S_VL + BPS * NE * 8;
   static_assert(NC >= 1 && VW % 4 == 0 && COOP <= 64, "geometry");
   static_assert(GPS * (D / 4) * 3 <= kWaveScratch && S_VI + BPS * NE <= kWaveScratch && TPS <= S_VL, "scratch");
 };
@@ -345,7 +349,7 @@ struct Geo {
 // sigma q s and the constant -3/2 sigma q . s (from the bucket midpoint to lo).
 template <int D, int MODE, bool REFINE, int GS>
 struct KStep {
-  using G = Geo<D, MODE, GS>;
+  using G = Geo<D, MODE, GS, !REFINE>;
   static constexpr int CODE_OFF = REFINE ? off_klo(D, GS) : 0;
   // Matrix-core path (2-bit codes, 64-token steps of two units): v_mfma_i32_16x16x64_i8 with
   // the codes as B (column j of tile T = token 4j + T of the step; lane group cg = one code
@@ -355,6 +359,11 @@ struct KStep {
   static constexpr bool MF = !REFINE && !G::KIVI && !G::DENSE && G::TPS == 64 && G::GPS == 2 && (D == 64 || D == 128);
   static constexpr int NCH = G::COLS / 4;   // 64-channel chunks (MFMA depth)
   static_assert(!MF || NCH == G::NC, "one 16-byte code load per chunk");
+  // The same on 128-token steps of four units (D = 64, one chunk): column j of tile T is
+  // token 8j + T (a lane loads eight consecutive tokens of its column), A row 4u + r holds
+  // limb r of unit u, and the valid outputs of column j are those of lane group j / 4.
+  static constexpr bool MF128 = !REFINE && G::W128;
+  static_assert(!MF128 || (G::GPS == 4 && G::COLS == 4 && G::NC == 2 && G::CPL == 4), "wide key geometry");
 
   struct Buf {
     uint4 meta, c[G::NC], l[G::DENSE ? G::NC : 1];
@@ -381,6 +390,15 @@ struct KStep {
       b.meta = ld_words<G::CPL>(r.at(2 * g + (pos0 >= D / 2), G::KMETA + 4 * (pos0 % (D / 2))));
     else
       b.meta = ld_words<G::CPL>(r.at(G::GP * (g / G::GU) + pos0 / (D / G::GP), G::KMETA + 4 * (pos0 % (D / G::GP))));
+    if constexpr (MF128) {
+      // lane (token octet j, column cg): tokens 8j .. 8j + 7 of column cg (unit j / 4); the
+      // eight lanes of two octets cover the record's four columns (256 contiguous bytes)
+      const int j = lane % 16, cg = lane / 16;
+      const uint8_t* kq = r.at(2 * groups[j / 4] + (j % 4) / 2, CODE_OFF + (cg * kBlock + 8 * (j % 2)) * 4);
+      b.c[0] = ld_stream4(kq);
+      b.c[1] = ld_stream4(kq + 16);
+      return;
+    }
     if constexpr (MF) {
       // lane (token quad j, column group cg): tokens 4j .. 4j + 3 of column 4C + cg; the 16
       // lanes of a quad-of-quads cover four whole consecutive columns of a record
@@ -437,8 +455,9 @@ struct KStep {
 
   // The step's scores. Every token t_loc of the step has one owner lane (own), which
   // receives sigma q . k_t (REFINE: the correction to it).
+  // MF128: every lane owns two tokens, t_loc and t_loc + 64 (the second score in *second).
   __device__ static inline float compute(const float* qperm, uint32_t* klimb, int lane, const Buf& b, bool& own,
-                                         int& t_loc) {
+                                         int& t_loc, float* second = nullptr) {
     int gsub, blk, quad, cp;
     role(lane, gsub, blk, quad, cp);
     const int pos0 = (lane % G::LPG) * G::CPL;
@@ -477,15 +496,17 @@ struct KStep {
       cst += dpp<0x141>(cst);
       v = max(v, dpp_u<0x140>(v));
       cst += dpp<0x140>(cst);
-      v = max_rows2(v);
-      cst = add_rows2(cst);
+      if (G::LPG >= 32) {
+        v = max_rows2(v);
+        cst = add_rows2(cst);
+      }
       if (G::LPG == 64) {
         v = max_halves(v);
         cst = add_halves(cst);
       }
       fm = __uint_as_float(v);
     }
-    static_assert(G::LPG >= 32, "group lanes");
+    static_assert(G::LPG >= (MF128 ? 16 : 32), "group lanes");
     const int ex = set_exponent(fm);
     // 2-bit planes (see masked): positions of bit pairs 0 and 2 get 4x coefficients (below
     // 2^22), those of pairs 1 and 3 scale 1 (below 2^20), every product then holds 4 v c;
@@ -519,7 +540,7 @@ struct KStep {
     if ((lane % (4 / G::CPL)) == 0) {
       uint32_t limb[3];
       transpose3(u, limb);
-      if constexpr (MF) {
+      if constexpr (MF || MF128) {
         // [unit][column][limb][bit pair]: an A row reads its column's four pair words at once
         const int st = pos0 / 4;   // limb set: column st / 4, bit pair st % 4
         uint32_t* dst = klimb + (gsub * G::COLS + st / 4) * 12 + st % 4;
@@ -534,6 +555,30 @@ struct KStep {
       }
     }
     wave_sync_lds();
+    if constexpr (MF128) {
+      const int m = lane % 16, cg = lane / 16;
+      const uint4 t = *reinterpret_cast<const uint4*>(klimb + ((m / 4) * G::COLS + cg) * 12 + (m & 3) % 3 * 4);
+      const i32x4_t A = (m & 3) < 3 ? i32x4_t{(int)t.x, (int)t.y, (int)t.z, (int)t.w} : i32x4_t{0, 0, 0, 0};
+      wave_sync_lds();   // every lane's A words are read before the scores reuse them
+      float* tr = reinterpret_cast<float*>(klimb);
+      const int j = lane % 16;
+      const bool mine = j / 4 == cg;   // lane group q holds rows 4q .. 4q + 3: unit q's limbs,
+                                       // whose scale and constant this lane built
+#pragma unroll
+      for (int T = 0; T < 8; ++T) {
+        uint32_t mw[4];
+        masked(w4(b.c[T / 4], T % 4), 0u, mw);
+        const i32x4_t bv = {(int)mw[0], (int)mw[1], (int)mw[2], (int)mw[3]};
+        const i32x4_t acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, bv, i32x4_t{0, 0, 0, 0}, 0, 0, 0);
+        const uint32_t v = (uint32_t)acc[0] + ((uint32_t)acc[1] << 8) + ((uint32_t)acc[2] << 16);
+        if (mine) tr[8 * j + T] = fmaf(inv, (float)(int)v, cst);
+      }
+      wave_sync_lds();
+      own = true;
+      t_loc = lane;
+      *second = tr[64 + lane];
+      return tr[lane];
+    }
     if constexpr (MF) {
       const int m = lane % 16, cg = lane / 16;
       const bool arow = m < 8 && (m & 3) < 3;
@@ -801,7 +846,7 @@ struct VStep {
 template <int D, int GS, class RW>
 __device__ void exact_v_pass(const RW& r, const float* weights, const uint32_t* selm, int lane, int w,
                              float* acc) {
-  using GC = Geo<D, MODE_COARSE, GS>;
+  using GC = Geo<D, MODE_COARSE, GS, false>;
   constexpr int VCH = GC::VCH;
   const int nb = r.n_q / kBlock;
   const int jb = lane / GC::LPB, chunk = lane % GC::LPB, e = chunk * VCH / kUnit / GC::GU;   // meta group
@@ -959,6 +1004,7 @@ template <int D, int GS, int MODE, bool SPARSE, int PH, bool SKIP = false, class
 __device__ __forceinline__ void row_body(const DecodeArgs& a, const RW& r, const Smem& sm, size_t orow, int split,
                                          const FinishIn& fin) {
   using G = Geo<D, MODE, GS>;
+  using GN = Geo<D, MODE, GS, false>;   // value-lane layout after the pass (corrections, merge)
   using KS = KStep<D, MODE, false, GS>;
   using VS = VStep<D, MODE, GS>;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -1024,9 +1070,9 @@ __device__ __forceinline__ void row_body(const DecodeArgs& a, const RW& r, const
   auto issue_k = [&](int s, typename KS::Buf& kb) {
     const int c = cb + s * kWaves + w;
     if (c >= n_chunks) return;   // no chunk for this wave (uniform)
-    int groups[2];
+    int groups[4];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < 4; ++i) {
       const int g = c * G::GPS + i;
       groups[i] = (i < G::GPS && g < r.n_groups) ? g : c * G::GPS;
     }
@@ -1043,6 +1089,23 @@ __device__ __forceinline__ void row_body(const DecodeArgs& a, const RW& r, const
     if (c >= n_chunks) return 0.f;
     bool own;
     int t_loc;
+    if constexpr (G::TPS == 128) {   // two tokens per lane: lane and lane + 64
+      float sc1;
+      const float sc0 = KS::compute(sm.qperm, klimb, lane, kb, own, t_loc, &sc1);
+      const bool v0 = c * G::GPS + lane / kUnit < r.n_groups, v1 = c * G::GPS + (64 + lane) / kUnit < r.n_groups;
+      const float s0 = v0 ? sc0 : -INFINITY, s1 = v1 ? sc1 : -INFINITY;
+      if (v0) scores[c * G::TPS + lane] = s0;
+      if (v1) scores[c * G::TPS + 64 + lane] = s1;
+      const float smax = fmaxf(s0, s1);
+      if (__any(smax > st.m)) st.raise(wave_max(smax));
+      const float w0 = v0 ? __expf(s0 - st.m) : 0.f, w1 = v1 ? __expf(s1 - st.m) : 0.f;
+      st.lsum += w0 + w1;
+      wave_sync_lds();   // the transposed scores are read before the weights overwrite them
+      scr[G::S_W + lane] = w0;
+      scr[G::S_W + 64 + lane] = w1;
+      wave_sync_lds();
+      return 0.f;
+    }
     const float sc0 = KS::compute(sm.qperm, klimb, lane, kb, own, t_loc);
     const bool valid = own && c * G::GPS + t_loc / kUnit < r.n_groups;
     const float sc = valid ? sc0 : -INFINITY;
@@ -1088,6 +1151,23 @@ __device__ __forceinline__ void row_body(const DecodeArgs& a, const RW& r, const
     step_v(s + 1, vb1, wgt);
   }
   __builtin_amdgcn_s_setprio(0);
+  if constexpr (G::W128 && !SKIP) {
+    // 128-token steps leave lane (block jb = lane / 8, chunk) with channels 8 chunk .. of
+    // block jb: sum the eight blocks (lane bits 3, 4, 5) and hand the channel totals to the
+    // 64-token value-lane layout the rest of the row uses (lanes 0..15, 4 channels each)
+    float x[VCH];
+#pragma unroll
+    for (int c = 0; c < VCH; ++c) x[c] = add_halves(add_rows2(st.acc[c] + dpp<0x128>(st.acc[c])));   // row_ror:8
+    wave_sync_lds();
+    if (lane < 8) {
+#pragma unroll
+      for (int c = 0; c < VCH; ++c) scr[VCH * lane + c] = x[c];
+    }
+    wave_sync_lds();
+#pragma unroll
+    for (int c = 0; c < VCH; ++c) st.acc[c] = lane < 16 && c < GN::VCH ? scr[GN::VCH * lane + c % GN::VCH] : 0.f;
+    wave_sync_lds();
+  }
   // ---- tail (exact bf16): tokens n_q + w, n_q + w + 8, ...; a lane holds the TC contiguous
   // channels lane TC .. lane TC + TC - 1 (tacc), read with one load per row. A wave requests the
   // K and V rows of TB of its tail tokens at once, then works through them, so the tail costs
@@ -1201,7 +1281,7 @@ __device__ __forceinline__ void row_body(const DecodeArgs& a, const RW& r, const
     // a coarse step holds (two; one at D = 256), so the dependent loads of the corrections
     // spread over all waves however the selected units cluster.
     using KR = KStep<D, MODE_COARSE, true, GS>;
-    using GC = Geo<D, MODE_COARSE, GS>;
+    using GC = Geo<D, MODE_COARSE, GS, false>;
     float* wfix = scr;   // [2][64]: refined and coarse weights of the step's selected tokens
     int rank0 = 0;       // selected units in the spans before this one (the same in every wave)
     for (int g64 = 0; g64 < n_units; g64 += 64) {
@@ -1377,23 +1457,24 @@ __device__ __forceinline__ void row_body(const DecodeArgs& a, const RW& r, const
   float* wv = sm.scores;   // [kWaves][D]
   float* pf = misc + 32;   // [n_split] the partials' factors (n_split <= 64)
   {
-    float v[VCH];
+    constexpr int VN = GN::VCH;
+    float v[VN];
 #pragma unroll
-    for (int c = 0; c < VCH; ++c) {
+    for (int c = 0; c < VN; ++c) {
       float x = st.acc[c];
-      if constexpr (G::BPS == 4) x = add_halves(add_rows2(x));   // lanes chunk + 16 vb
-      else x = add_halves(x);                                    // lanes chunk + 32 vb
+      if constexpr (GN::BPS == 4) x = add_halves(add_rows2(x));   // lanes chunk + 16 vb
+      else x = add_halves(x);                                     // lanes chunk + 32 vb
       v[c] = x;
     }
-    const int chunk = lane % G::LPB;
-    if (lane < G::LPB) {
+    const int chunk = lane % GN::LPB;
+    if (lane < GN::LPB) {
 #pragma unroll
-      for (int c = 0; c < VCH; ++c) {
-        const int e = (chunk * VCH + c) / kUnit;   // the channel's 32-channel slice
+      for (int c = 0; c < VN; ++c) {
+        const int e = (chunk * VN + c) / kUnit;   // the channel's 32-channel slice
         float z = zs[0];
 #pragma unroll
         for (int k = 1; k < NE; ++k) z = e == k ? zs[k] : z;
-        wv[w * D + chunk * VCH + c] = (v[c] + z) * fw;
+        wv[w * D + chunk * VN + c] = (v[c] + z) * fw;
       }
     }
   }

@@ -364,6 +364,11 @@ struct KStep {
   // limb r of unit u, and the valid outputs of column j are those of lane group j / 4.
   static constexpr bool MF128 = !REFINE && G::W128;
   static_assert(!MF128 || (G::GPS == 4 && G::COLS == 4 && G::NC == 2 && G::CPL == 4), "wide key geometry");
+  // And on 32-token steps of one unit (D = 256, four chunks): column j of tile T is token
+  // 2j + T (a lane loads two consecutive tokens of each of its four columns), A rows 0..2
+  // hold the unit's limbs, and lanes 0..15 receive the 32 tokens' sums.
+  static constexpr bool MF32 = !REFINE && !G::KIVI && !G::DENSE && D == 256 && G::TPS == 32;
+  static_assert(!MF32 || (G::GPS == 1 && G::COLS == 16 && G::NC == 2 && G::CPL == 4), "key geometry, D = 256");
 
   struct Buf {
     uint4 meta, c[G::NC], l[G::DENSE ? G::NC : 1];
@@ -390,6 +395,18 @@ struct KStep {
       b.meta = ld_words<G::CPL>(r.at(2 * g + (pos0 >= D / 2), G::KMETA + 4 * (pos0 % (D / 2))));
     else
       b.meta = ld_words<G::CPL>(r.at(G::GP * (g / G::GU) + pos0 / (D / G::GP), G::KMETA + 4 * (pos0 % (D / G::GP))));
+    if constexpr (MF32) {
+      // lane (token pair j, column group cg): tokens 2j, 2j + 1 of columns 4C + cg (record
+      // j / 8); per chunk the 16 lanes of a record cover its four columns (256 bytes)
+      const int j = lane % 16, cg = lane / 16;
+      const uint8_t* kq = r.at(2 * groups[0] + j / 8, CODE_OFF + (cg * kBlock + 2 * (j % 8)) * 4);
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const uint4 lo = ld_stream2(kq + (2 * c) * 4 * kBlock * 4), hi = ld_stream2(kq + (2 * c + 1) * 4 * kBlock * 4);
+        b.c[c] = make_uint4(lo.x, lo.y, hi.x, hi.y);   // chunk 2c: words 0, 1; chunk 2c + 1: words 2, 3
+      }
+      return;
+    }
     if constexpr (MF128) {
       // lane (token octet j, column cg): tokens 8j .. 8j + 7 of column cg (unit j / 4); the
       // eight lanes of two octets cover the record's four columns (256 contiguous bytes)
@@ -540,7 +557,7 @@ struct KStep {
     if ((lane % (4 / G::CPL)) == 0) {
       uint32_t limb[3];
       transpose3(u, limb);
-      if constexpr (MF || MF128) {
+      if constexpr (MF || MF128 || MF32) {
         // [unit][column][limb][bit pair]: an A row reads its column's four pair words at once
         const int st = pos0 / 4;   // limb set: column st / 4, bit pair st % 4
         uint32_t* dst = klimb + (gsub * G::COLS + st / 4) * 12 + st % 4;
@@ -555,6 +572,36 @@ struct KStep {
       }
     }
     wave_sync_lds();
+    if constexpr (MF32) {
+      const int m = lane % 16, cg = lane / 16;
+      i32x4_t acc[2] = {i32x4_t{0, 0, 0, 0}, i32x4_t{0, 0, 0, 0}};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const uint4 t = *reinterpret_cast<const uint4*>(klimb + (4 * c + cg) * 12 + (m < 3 ? m : 0) * 4);
+        const i32x4_t A = m < 3 ? i32x4_t{(int)t.x, (int)t.y, (int)t.z, (int)t.w} : i32x4_t{0, 0, 0, 0};
+#pragma unroll
+        for (int T = 0; T < 2; ++T) {
+          uint32_t mw[4];
+          masked(w4(b.c[c / 2], 2 * (c % 2) + T), 0u, mw);
+          const i32x4_t bv = {(int)mw[0], (int)mw[1], (int)mw[2], (int)mw[3]};
+          acc[T] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, bv, acc[T], 0, 0, 0);
+        }
+      }
+      wave_sync_lds();   // every lane's A words are read before the scores reuse them
+      float* tr = reinterpret_cast<float*>(klimb);
+      if (lane < 16) {
+        float2 sc;
+        const uint32_t v0 = (uint32_t)acc[0][0] + ((uint32_t)acc[0][1] << 8) + ((uint32_t)acc[0][2] << 16);
+        const uint32_t v1 = (uint32_t)acc[1][0] + ((uint32_t)acc[1][1] << 8) + ((uint32_t)acc[1][2] << 16);
+        sc.x = fmaf(inv, (float)(int)v0, cst);
+        sc.y = fmaf(inv, (float)(int)v1, cst);
+        *reinterpret_cast<float2*>(tr + 2 * lane) = sc;
+      }
+      wave_sync_lds();
+      own = lane < 32;
+      t_loc = lane % 32;
+      return tr[lane % 32];
+    }
     if constexpr (MF128) {
       const int m = lane % 16, cg = lane / 16;
       const uint4 t = *reinterpret_cast<const uint4*>(klimb + ((m / 4) * G::COLS + cg) * 12 + (m & 3) % 3 * 4);

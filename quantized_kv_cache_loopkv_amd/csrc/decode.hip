@@ -1673,12 +1673,12 @@ __global__ void __launch_bounds__(kThreads, (decode_waves_per_simd<D, VAR>())) k
         fin.pre[idx] = fin.parts[(size_t)(idx / D) * (2 + D) + 2 + idx % D];
     }
   }
-  // PH_PART: the row's block-table entries (every block a row of max_len tokens can have
-  // quantized) are requested together with its length, so the first record loads wait for
-  // one memory round trip less; the entries past the row are never used.
+  // PH_ROW / PH_PART: the row's block-table entries (every block a row of max_len tokens can
+  // have quantized) are requested together with its length, so the first record loads wait
+  // for one memory round trip less; the entries past the row are never used.
   constexpr int kBtPer = (LOOPKV_MAX_LEN / kBlock + kThreads - 1) / kThreads;
   int32_t btv[kBtPer];
-  if constexpr (PH == PH_PART) {
+  if constexpr (PH != PH_FINISH) {
     const int32_t* bt0 = a.block_table + (size_t)b * a.bt_stride;
     const int nb_max = a.max_len / kBlock;   // bt_stride pages cover max_len tokens
 #pragma unroll
@@ -1749,7 +1749,7 @@ __global__ void __launch_bounds__(kThreads, (decode_waves_per_simd<D, VAR>())) k
   const int nbq = r.n_q / kBlock;
   const uint32_t rec256 = (uint32_t)(record_bytes(cell.kind, D, GS) / 256);
   int bad_page = 0;
-  if constexpr (PH == PH_PART) {
+  if constexpr (PH != PH_FINISH) {
 #pragma unroll
     for (int k = 0; k < kBtPer; ++k) {
       const int j = tid + k * kThreads;

@@ -56,7 +56,10 @@ namespace lkv {
 constexpr int kWaves = LKV_WAVES;           // waves per workgroup (one row)
 constexpr int kThreads = 64 * kWaves;
 constexpr int kWavesPerSimd = kWaves / 2;   // two workgroups per CU (LDS-bound)
-constexpr int kWaveScratch = 272;   // words of per-wave LDS scratch
+// Words of per-wave LDS scratch: 256, or 272 for head dim 64, whose 128-token steps keep 128
+// weights below the value limbs. (At 16K tokens a workgroup's LDS sits just under half of
+// the CU's 160 KB, so two workgroups share a CU; the larger scratch would break that.)
+__host__ __device__ constexpr int wave_scratch(int D) { return D == 64 ? 272 : 256; }
 
 enum : int { MODE_COARSE = 0, MODE_DENSE = 1, MODE_Q2 = 2, MODE_KIVI = 3 };
 
@@ -336,7 +339,7 @@ struct Geo {
   // consumed; V limbs and their inverse scales from max(64, TPS).
   static constexpr int S_W = 0, S_VL = TPS > 64 ? TPS : 64, S_VI = S_VL + BPS * NE * 8;
   static_assert(NC >= 1 && VW % 4 == 0 && COOP <= 64, "geometry");
-  static_assert(GPS * (D / 4) * 3 <= kWaveScratch && S_VI + BPS * NE <= kWaveScratch && TPS <= S_VL, "scratch");
+  static_assert(GPS * (D / 4) * 3 <= wave_scratch(D) && S_VI + BPS * NE <= wave_scratch(D) && TPS <= S_VL, "scratch");
 };
 
 // ----------------------------------------------------------------------------- K step
@@ -939,7 +942,7 @@ __host__ __device__ inline size_t lds_region_a(int max_len, int D) {
 }
 __host__ __device__ inline size_t decode_lds_floats(int max_len, int D) {
   const size_t lp = lds_lpad(max_len);
-  return lds_region_a(max_len, D) + pad4(lp / 32) + pad4(lp / 16 + 16) + 2 * D + (size_t)kWaves * kWaveScratch + 96;
+  return lds_region_a(max_len, D) + pad4(lp / 32) + pad4(lp / 16 + 16) + 2 * D + (size_t)kWaves * wave_scratch(D) + 96;
 }
 // A finishing launch also stages the row's n_split partial value vectors in LDS, right after
 // the row's regions (the exchange words are last), when they fit in the 160 KB.
@@ -956,7 +959,7 @@ struct Smem {
   uint32_t* boff;   // [lpad / 16] record offset of each logical block, 256-byte units
   float* qs;        // [D]
   float* qperm;     // [D] sigma q in K-meta position order
-  float* wscr;      // [kWaves][kWaveScratch]
+  float* wscr;      // [kWaves][wave_scratch(D)]
   float* misc;      // [96]: per wave m, l, removed weight (0..23); the partials' factors (32..95)
 };
 
@@ -1055,7 +1058,7 @@ __device__ __forceinline__ void row_body(const DecodeArgs& a, const RW& r, const
   using KS = KStep<D, MODE, false, GS>;
   using VS = VStep<D, MODE, GS>;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  float* scr = sm.wscr + w * kWaveScratch;
+  float* scr = sm.wscr + w * wave_scratch(D);
   uint32_t* klimb = reinterpret_cast<uint32_t*>(scr);
   // coarse scores: LDS, except the partial launches of a split row, which leave them in the
   // row's scratch line for the finishing launch to copy back into LDS
@@ -1655,7 +1658,7 @@ __global__ void __launch_bounds__(kThreads, (decode_waves_per_simd<D, VAR>())) k
   sm.qs = reinterpret_cast<float*>(sm.boff + pad4(lp / 16 + 16));
   sm.qperm = sm.qs + D;
   sm.wscr = sm.qperm + D;
-  sm.misc = sm.wscr + kWaves * kWaveScratch;
+  sm.misc = sm.wscr + kWaves * wave_scratch(D);
 
   // PH_FINISH: the row's partials depend on nothing the prologue reads, so they are
   // requested first and their latency overlaps the prologue's

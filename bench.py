@@ -600,6 +600,8 @@ def main():
         pool.close()
         pool.join()
 
+    default_workload = (wk == "c4" and GQ == 32 and B == 32 and args.ctx == 16384 and args.tau == 0.01
+                        and cfg.shuffled)
     line = {
         "metric": "achieved HBM GB/s (% of peak) + us per decode step, 4x24 plan, 16K ctx",
         "value": round(value, 1),
@@ -619,7 +621,8 @@ def main():
                    "global_batch": B, "seq_len": args.ctx, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4),
-                     "traffic": counter_traffic() if GQ == 32 else None,   # the counters cover groups of 32
+                     # the counters were taken on the default workload (C4, groups of 32, tau 0.01)
+                     "traffic": counter_traffic() if default_workload else None,
                      "kernel": f"k_decode<128, {GQ}, tau regime, PH_ROW>", "bytes_per_launch": dec_bytes,
                      "mean_launch_ms": round(dec_mean_ms, 4)},
         "cpu_baseline": cpu,

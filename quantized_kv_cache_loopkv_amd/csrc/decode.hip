@@ -367,11 +367,12 @@ struct KStep {
   // limb r of unit u, and the valid outputs of column j are those of lane group j / 4.
   static constexpr bool MF128 = !REFINE && G::W128;
   static_assert(!MF128 || (G::GPS == 4 && G::COLS == 4 && G::NC == 2 && G::CPL == 4), "wide key geometry");
-  // And on 32-token steps of one unit (D = 256, four chunks): column j of tile T is token
-  // 2j + T (a lane loads two consecutive tokens of each of its four columns), A rows 0..2
+  // And on 32-token steps of one unit (D = 256, and both planes at D = 128: 4-bit codes
+  // 4 hi + lo, one byte each): column j of tile T is token 2j + T (a lane loads two
+  // consecutive tokens of each of its columns, of both planes for 4-bit codes), A rows 0..2
   // hold the unit's limbs, and lanes 0..15 receive the 32 tokens' sums.
-  static constexpr bool MF32 = !REFINE && !G::KIVI && !G::DENSE && D == 256 && G::TPS == 32;
-  static_assert(!MF32 || (G::GPS == 1 && G::COLS == 16 && G::NC == 2 && G::CPL == 4), "key geometry, D = 256");
+  static constexpr bool MF32 = !REFINE && !G::KIVI && G::TPS == 32 && (D == 256 || (D == 128 && G::DENSE));
+  static_assert(!MF32 || (G::GPS == 1 && G::COLS == 8 * G::NC), "32-token key geometry");
 
   struct Buf {
     uint4 meta, c[G::NC], l[G::DENSE ? G::NC : 1];
@@ -404,9 +405,14 @@ struct KStep {
       const int j = lane % 16, cg = lane / 16;
       const uint8_t* kq = r.at(2 * groups[0] + j / 8, CODE_OFF + (cg * kBlock + 2 * (j % 8)) * 4);
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const uint4 lo = ld_stream2(kq + (2 * c) * 4 * kBlock * 4), hi = ld_stream2(kq + (2 * c + 1) * 4 * kBlock * 4);
-        b.c[c] = make_uint4(lo.x, lo.y, hi.x, hi.y);   // chunk 2c: words 0, 1; chunk 2c + 1: words 2, 3
+      for (int c = 0; c < G::NC; ++c) {   // chunk 2c: words 0, 1; chunk 2c + 1: words 2, 3
+        const uint4 a0 = ld_stream2(kq + (2 * c) * 4 * kBlock * 4), a1 = ld_stream2(kq + (2 * c + 1) * 4 * kBlock * 4);
+        b.c[c] = make_uint4(a0.x, a0.y, a1.x, a1.y);
+        if constexpr (G::DENSE) {
+          const uint4 b0 = ld_stream2(kq + off_klo(D, GS) + (2 * c) * 4 * kBlock * 4);
+          const uint4 b1 = ld_stream2(kq + off_klo(D, GS) + (2 * c + 1) * 4 * kBlock * 4);
+          b.l[c] = make_uint4(b0.x, b0.y, b1.x, b1.y);
+        }
       }
       return;
     }
@@ -579,13 +585,13 @@ struct KStep {
       const int m = lane % 16, cg = lane / 16;
       i32x4_t acc[2] = {i32x4_t{0, 0, 0, 0}, i32x4_t{0, 0, 0, 0}};
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
+      for (int c = 0; c < NCH; ++c) {
         const uint4 t = *reinterpret_cast<const uint4*>(klimb + (4 * c + cg) * 12 + (m < 3 ? m : 0) * 4);
         const i32x4_t A = m < 3 ? i32x4_t{(int)t.x, (int)t.y, (int)t.z, (int)t.w} : i32x4_t{0, 0, 0, 0};
 #pragma unroll
         for (int T = 0; T < 2; ++T) {
           uint32_t mw[4];
-          masked(w4(b.c[c / 2], 2 * (c % 2) + T), 0u, mw);
+          masked(w4(b.c[c / 2], 2 * (c % 2) + T), G::DENSE ? w4(b.l[c / 2], 2 * (c % 2) + T) : 0u, mw);
           const i32x4_t bv = {(int)mw[0], (int)mw[1], (int)mw[2], (int)mw[3]};
           acc[T] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, bv, acc[T], 0, 0, 0);
         }

@@ -359,7 +359,8 @@ struct KStep {
   // column of 16 channels, its four bit-pair words) and the coefficient limbs as A (rows
   // 0..2: limbs 0..2 of the step's first unit, rows 4..6: of its second, other rows zero).
   // Each token's three limb sums come out exact in 32-bit integers and combine exactly.
-  static constexpr bool MF = !REFINE && !G::KIVI && !G::DENSE && G::TPS == 64 && G::GPS == 2 && (D == 64 || D == 128);
+  // (also the corrections' low-plane refinement, REFINE: the same 2-bit geometry)
+  static constexpr bool MF = !G::KIVI && !G::DENSE && G::TPS == 64 && G::GPS == 2 && (D == 64 || D == 128);
   static constexpr int NCH = G::COLS / 4;   // 64-channel chunks (MFMA depth)
   static_assert(!MF || NCH == G::NC, "one 16-byte code load per chunk");
   // The same on 128-token steps of four units (D = 64, one chunk): column j of tile T is
@@ -371,7 +372,7 @@ struct KStep {
   // 4 hi + lo, one byte each): column j of tile T is token 2j + T (a lane loads two
   // consecutive tokens of each of its columns, of both planes for 4-bit codes), A rows 0..2
   // hold the unit's limbs, and lanes 0..15 receive the 32 tokens' sums.
-  static constexpr bool MF32 = !REFINE && !G::KIVI && G::TPS == 32 && (D == 256 || (D == 128 && G::DENSE));
+  static constexpr bool MF32 = !G::KIVI && G::TPS == 32 && (D == 256 || (D == 128 && G::DENSE));
   static_assert(!MF32 || (G::GPS == 1 && G::COLS == 8 * G::NC), "32-token key geometry");
 
   struct Buf {

@@ -361,19 +361,20 @@ struct KStep {
   // Each token's three limb sums come out exact in 32-bit integers and combine exactly.
   // (also the corrections' low-plane refinement, REFINE: the same 2-bit geometry)
   static constexpr bool MF = !G::KIVI && !G::DENSE && G::TPS == 64 && G::GPS == 2 && (D == 64 || D == 128);
-  static constexpr int NCH = G::COLS / 4;   // 64-channel chunks (MFMA depth)
+  static constexpr int NCH = D / 64;   // 64-channel chunks (MFMA depth)
   static_assert(!MF || NCH == G::NC, "one 16-byte code load per chunk");
   // The same on 128-token steps of four units (D = 64, one chunk): column j of tile T is
   // token 8j + T (a lane loads eight consecutive tokens of its column), A row 4u + r holds
   // limb r of unit u, and the valid outputs of column j are those of lane group j / 4.
   static constexpr bool MF128 = !REFINE && G::W128;
   static_assert(!MF128 || (G::GPS == 4 && G::COLS == 4 && G::NC == 2 && G::CPL == 4), "wide key geometry");
-  // And on 32-token steps of one unit (D = 256, and both planes at D = 128: 4-bit codes
-  // 4 hi + lo, one byte each): column j of tile T is token 2j + T (a lane loads two
-  // consecutive tokens of each of its columns, of both planes for 4-bit codes), A rows 0..2
-  // hold the unit's limbs, and lanes 0..15 receive the 32 tokens' sums.
-  static constexpr bool MF32 = !G::KIVI && G::TPS == 32 && (D == 256 || (D == 128 && G::DENSE));
-  static_assert(!MF32 || (G::GPS == 1 && G::COLS == 8 * G::NC), "32-token key geometry");
+  // And on 32-token steps of one unit (D = 256, both planes at D = 128 and the KIVI-4 layout:
+  // 4-bit codes, one byte each): column j of tile T is token 2j + T (a lane loads two
+  // consecutive tokens of each of its columns), A rows 0..2 hold the unit's limbs, and lanes
+  // 0..15 receive the 32 tokens' sums. A lane group covers 16 channels: one 2-bit column
+  // (four bit-pair words) or two KIVI-4 columns (two nibble words each).
+  static constexpr bool MF32 = G::TPS == 32 && (D == 256 || (D == 128 && (G::DENSE || G::KIVI)));
+  static_assert(!MF32 || (G::GPS == 1 && G::COLS == 8 * G::NC && NCH == (G::KIVI ? 1 : 2) * G::NC), "32-token key geometry");
 
   struct Buf {
     uint4 meta, c[G::NC], l[G::DENSE ? G::NC : 1];
@@ -400,6 +401,18 @@ struct KStep {
       b.meta = ld_words<G::CPL>(r.at(2 * g + (pos0 >= D / 2), G::KMETA + 4 * (pos0 % (D / 2))));
     else
       b.meta = ld_words<G::CPL>(r.at(G::GP * (g / G::GU) + pos0 / (D / G::GP), G::KMETA + 4 * (pos0 % (D / G::GP))));
+    if constexpr (MF32 && G::KIVI) {
+      // lane (token pair j, column group cg): tokens 2j, 2j + 1 of columns 8C + 2cg and
+      // 8C + 2cg + 1 (record j / 8); b.c[C] = {first column: t, t + 1; second: t, t + 1}
+      const int j = lane % 16, cg = lane / 16;
+      const uint8_t* kq = r.at(2 * groups[0] + j / 8, CODE_OFF + (2 * cg * kBlock + 2 * (j % 8)) * 4);
+#pragma unroll
+      for (int c = 0; c < G::NC; ++c) {
+        const uint4 a0 = ld_stream2(kq + 8 * c * kBlock * 4), a1 = ld_stream2(kq + (8 * c + 1) * kBlock * 4);
+        b.c[c] = make_uint4(a0.x, a0.y, a1.x, a1.y);
+      }
+      return;
+    }
     if constexpr (MF32) {
       // lane (token pair j, column group cg): tokens 2j, 2j + 1 of columns 4C + cg (record
       // j / 8); per chunk the 16 lanes of a record cover its four columns (256 bytes)
@@ -568,12 +581,12 @@ struct KStep {
       uint32_t limb[3];
       transpose3(u, limb);
       if constexpr (MF || MF128 || MF32) {
-        // [unit][column][limb][bit pair]: an A row reads its column's four pair words at once
-        const int st = pos0 / 4;   // limb set: column st / 4, bit pair st % 4
-        uint32_t* dst = klimb + (gsub * G::COLS + st / 4) * 12 + st % 4;
+        // [unit][column][limb][bit pair or nibble]: an A row reads its column's limb words at once
+        const int st = pos0 / 4;   // limb set: column st / SPC, bit pair (or nibble) st % SPC
+        uint32_t* dst = klimb + (gsub * G::COLS + st / G::SPC) * (3 * G::SPC) + st % G::SPC;
         dst[0] = limb[0] ^ 0x80808080u;   // biased byte -> signed digit
-        dst[4] = limb[1] ^ 0x80808080u;
-        dst[8] = limb[2];
+        dst[G::SPC] = limb[1] ^ 0x80808080u;
+        dst[2 * G::SPC] = limb[2];
       } else {
         uint32_t* dst = klimb + (gsub * (D / 4) + pos0 / 4) * 3;
 #pragma unroll
@@ -587,12 +600,24 @@ struct KStep {
       i32x4_t acc[2] = {i32x4_t{0, 0, 0, 0}, i32x4_t{0, 0, 0, 0}};
 #pragma unroll
       for (int c = 0; c < NCH; ++c) {
-        const uint4 t = *reinterpret_cast<const uint4*>(klimb + (4 * c + cg) * 12 + (m < 3 ? m : 0) * 4);
-        const i32x4_t A = m < 3 ? i32x4_t{(int)t.x, (int)t.y, (int)t.z, (int)t.w} : i32x4_t{0, 0, 0, 0};
+        i32x4_t A;
+        if constexpr (G::KIVI) {   // columns 8c + 2cg and 8c + 2cg + 1: two nibble words each
+          const uint2 t0 = *reinterpret_cast<const uint2*>(klimb + (8 * c + 2 * cg) * 6 + (m < 3 ? m : 0) * 2);
+          const uint2 t1 = *reinterpret_cast<const uint2*>(klimb + (8 * c + 2 * cg + 1) * 6 + (m < 3 ? m : 0) * 2);
+          A = m < 3 ? i32x4_t{(int)t0.x, (int)t0.y, (int)t1.x, (int)t1.y} : i32x4_t{0, 0, 0, 0};
+        } else {
+          const uint4 t = *reinterpret_cast<const uint4*>(klimb + (4 * c + cg) * 12 + (m < 3 ? m : 0) * 4);
+          A = m < 3 ? i32x4_t{(int)t.x, (int)t.y, (int)t.z, (int)t.w} : i32x4_t{0, 0, 0, 0};
+        }
 #pragma unroll
         for (int T = 0; T < 2; ++T) {
           uint32_t mw[4];
-          masked(w4(b.c[c / 2], 2 * (c % 2) + T), G::DENSE ? w4(b.l[c / 2], 2 * (c % 2) + T) : 0u, mw);
+          if constexpr (G::KIVI) {
+            masked(w4(b.c[c], T), 0u, mw);
+            masked(w4(b.c[c], 2 + T), 0u, mw + 2);
+          } else {
+            masked(w4(b.c[c / 2], 2 * (c % 2) + T), G::DENSE ? w4(b.l[c / 2], 2 * (c % 2) + T) : 0u, mw);
+          }
           const i32x4_t bv = {(int)mw[0], (int)mw[1], (int)mw[2], (int)mw[3]};
           acc[T] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, bv, acc[T], 0, 0, 0);
         }

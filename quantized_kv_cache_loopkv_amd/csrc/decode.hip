@@ -9,12 +9,14 @@
 // uniform 4-bit KIVI-4 layout goes through the same kernel as the baseline.
 //
 // One workgroup (8 wave64s) owns one row (cell, sequence, head); a whole plan is
-// one launch of cells x sequences x heads workgroups. The path is HBM-bound with
-// a VALU co-limit, so no MFMA: codes are widened with byte masks and multiplied by
-// fixed-point coefficients with v_dot4 integer dot products.
+// one launch of cells x sequences x heads workgroups. The path is HBM-bound with a
+// VALU co-limit: codes are widened with byte masks and multiplied by fixed-point
+// coefficients in exact integer arithmetic; the key scores' dot products run on the
+// matrix cores (v_mfma_i32_16x16x64_i8, most rows of A zero: it takes integer work off the
+// VALU, not a GEMM), the value sums on v_dot4.
 //
 // Single streaming pass (split-K online softmax): each wave walks its share of the
-// row in steps of 32 or 64 tokens. A step reads, for every 16-token block it covers,
+// row in steps of 32, 64 or 128 tokens. A step reads, for every 16-token block it covers,
 // the K and V parts of the record that every token needs (one contiguous span of the
 // record), and computes
 //   K   scores s_t = sigma q . (z + s c) from the codes it read (4-bit target: high
@@ -1187,20 +1189,21 @@ __device__ __forceinline__ void row_body(const DecodeArgs& a, const RW& r, const
       scr[G::S_W + 64 + lane] = w1;
       wave_sync_lds();
       return 0.f;
+    } else {
+      const float sc0 = KS::compute(sm.qperm, klimb, lane, kb, own, t_loc);
+      const bool valid = own && c * G::GPS + t_loc / kUnit < r.n_groups;
+      const float sc = valid ? sc0 : -INFINITY;
+      if (valid) scores[c * G::TPS + t_loc] = sc;
+      if (__any(sc > st.m)) st.raise(wave_max(sc));   // a new running maximum (rare once warm)
+      const float wgt = valid ? __expf(sc - st.m) : 0.f;
+      st.lsum += wgt;
+      if constexpr (!G::QUAD_W) {
+        wave_sync_lds();   // the K limbs are read before the weights overwrite them
+        if (own) scr[G::S_W + t_loc] = wgt;
+      }
+      wave_sync_lds();
+      return wgt;
     }
-    const float sc0 = KS::compute(sm.qperm, klimb, lane, kb, own, t_loc);
-    const bool valid = own && c * G::GPS + t_loc / kUnit < r.n_groups;
-    const float sc = valid ? sc0 : -INFINITY;
-    if (valid) scores[c * G::TPS + t_loc] = sc;
-    if (__any(sc > st.m)) st.raise(wave_max(sc));   // a new running maximum (rare once warm)
-    const float wgt = valid ? __expf(sc - st.m) : 0.f;
-    st.lsum += wgt;
-    if constexpr (!G::QUAD_W) {
-      wave_sync_lds();   // the K limbs are read before the weights overwrite them
-      if (own) scr[G::S_W + t_loc] = wgt;
-    }
-    wave_sync_lds();
-    return wgt;
   };
   auto step_v = [&](int s, const typename VS::Buf& vb, float wgt) {
     if constexpr (SKIP) return;

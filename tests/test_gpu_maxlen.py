@@ -41,7 +41,7 @@ def _workload(D):
     return _cache[D]
 
 
-@pytest.mark.parametrize("D,tau", [(128, 0.0), (128, 0.01), (128, 1.1), (256, 0.01)])
+@pytest.mark.parametrize("D,tau", [(128, 0.0), (128, 0.01), (128, 1.1), (256, 0.01), (64, 0.01), (64, 0.0)])
 def test_gpu_max_len_rows(D, tau):
     _need_gpu()
     wl = _workload(D)

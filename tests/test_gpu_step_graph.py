@@ -31,21 +31,24 @@ def _need_gpu():
         pytest.skip("no GPU")
 
 
-def _workload(Hkv, group):
+def _workload(Hkv, group, D=128):
     plan = np.array([[0, 2, 1], [2, 1, 0], [0, 1, 0]], dtype=np.uint8)
     lengths = [95, 517] if group == 32 else [62, 517]   # the first sequence completes a group
-    cfg = R.small_config("stepgraph", 3, 3, 2, 128, lengths, [0.01], plan=plan, cell_scales=True, shuffled=True,
+    cfg = R.small_config("stepgraph", 3, 3, 2, D, lengths, [0.01], plan=plan, cell_scales=True, shuffled=True,
                          append_steps=STEPS, n_kv_heads=Hkv, group=group)
     wl = Workload(cfg, gpu_synth=False)
     wl.fill()
     return wl
 
 
-@pytest.mark.parametrize("n_split,Hkv,group", [(0, 0, 32), (3, 0, 32), (0, 1, 64), (2, 1, 64)])
-def test_gpu_step_graph_launches_equal_eager(n_split, Hkv, group):
+@pytest.mark.parametrize("n_split,Hkv,group,D", [(0, 0, 32, 128), (3, 0, 32, 128), (0, 1, 64, 128), (2, 1, 64, 128),
+                                                 (0, 0, 32, 64), (3, 0, 64, 64), (0, 0, 32, 256), (2, 0, 64, 256)])
+def test_gpu_step_graph_launches_equal_eager(n_split, Hkv, group, D):
+    """Head dims 64 and 256 run their own step geometries (128- and 32-token steps) and their own
+    in-launch appends."""
     _need_gpu()
     tau = 0.01
-    ea, gb = _workload(Hkv, group), _workload(Hkv, group)
+    ea, gb = _workload(Hkv, group, D), _workload(Hkv, group, D)
     cfg = ea.cfg
     C, B, H, D = cfg.n_cells, cfg.batch, cfg.n_heads, cfg.head_dim
     max_len = max(cfg.lengths) + STEPS
@@ -89,7 +92,7 @@ def test_gpu_step_graph_launches_equal_eager(n_split, Hkv, group):
         out.fill_(float("nan"))   # eager work between launches
         g.launch()
         torch.cuda.synchronize()
-        print(f"n_split={n_split} Hkv={Hkv} group={group} launch {s}", flush=True)
+        print(f"n_split={n_split} Hkv={Hkv} group={group} D={D} launch {s}", flush=True)
         assert torch.equal(out, ref[s][0]), f"launch {s}: outputs differ"
         assert torch.equal(sm, ref[s][1]), f"launch {s}: selections differ"
     assert torch.equal(slb.cpu(), torch.tensor([n + STEPS for n in cfg.lengths], dtype=torch.int32))
@@ -99,11 +102,15 @@ def test_gpu_step_graph_launches_equal_eager(n_split, Hkv, group):
     # same records and tails as the append calls
     G = cfg.group
     for c in ea.storing_cells():
+        # the record's data (planes and meta); the bytes after it pad the record to a 256-byte
+        # multiple (D = 64 with groups of 64) and are never written
+        used = (8 * D if ea.plan[c] == R.Q2 else 16 * D) + 2 * (64 * D // G)
         for b, n0 in enumerate(cfg.lengths):
             n = n0 + STEPS
             for h in range(cfg.kv_heads):
                 for j in range(G * (n // G) // 16):
-                    assert np.array_equal(ea.record(c, b, h, j), gb.record(c, b, h, j)), f"record c={c} b={b} h={h} j={j}"
+                    assert np.array_equal(ea.record(c, b, h, j)[:used], gb.record(c, b, h, j)[:used]), \
+                        f"record c={c} b={b} h={h} j={j}"
                 ta, tb = ea.tail(c, b, h), gb.tail(c, b, h)
                 for t in range(G * (n // G), n):
                     assert np.array_equal(ta[:, t % G], tb[:, t % G]), f"tail c={c} b={b} h={h} t={t}"

@@ -538,7 +538,11 @@ def main():
             "batch": B, "context": f"{args.ctx}..{args.ctx + GS}", "ms_per_step": round(ms, 4),
             "whole_plan_ms_per_step": round(float(np.mean(step_ms)), 4),
             "ratio_to_whole_plan": round(ms / float(np.mean(step_ms)), 4),
-            "launches_per_step": n_storing + C + 1}   # appends, decodes, the length update
+            "launches_per_step": n_storing + C + 1,   # appends, decodes, the length update
+            # the whole-plan decode's algorithmic bytes (the serving steps run up to GS tokens
+            # longer, a few 1e-4 more bytes; the appends' few KB are not counted)
+            "algorithmic_GBps": round(dec_bytes / (ms * 1e-3) / 1e9, 1),
+            "frac_of_peak": round(dec_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
         log(f"per-cell graph, batch {B}: {ms:.3f} ms per step vs whole plan {np.mean(step_ms):.3f} ms")
         # one sequence: the per-cell launches hold 16 rows each, so the split decode fills the GPU
         scfg = R.make_config("C4")
@@ -549,12 +553,16 @@ def main():
         sw = Workload(scfg, gpu_synth=True, log=log)
         sw.fill()
         sq = sw.q_all()
-        small = {"batch": 1, "context": args.ctx}
+        # algorithmic bytes of one batch-1 step (selected tokens' low planes, ~1e-4 of the
+        # bytes at tau 0.01, not counted)
+        b1 = algorithmic_bytes(plan, [args.ctx], H, D, group=GQ)
+        small = {"batch": 1, "context": args.ctx, "algorithmic_GB": round(b1 / 1e9, 4)}
         first = 0
         for ns in SERVING_SPLITS:
             ms1, _ = serving_graph(sw, sq, args.tau, first, SERVING_REPS, ns, log, warm=SERVING_WARM)
             first += SERVING_WARM + SERVING_REPS
             small[f"ms_per_step_split{ns}"] = round(ms1, 4)
+            small[f"GBps_split{ns}"] = round(b1 / (ms1 * 1e-3) / 1e9, 1)
             log(f"per-cell graph, batch 1, n_split {ns}: {ms1:.3f} ms per step")
         extra["per_cell_graph_batch1"] = small
         del sw

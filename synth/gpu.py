@@ -61,7 +61,8 @@ def normal(seed: int, stream: int, offset: int, out: torch.Tensor):
 
 
 def read_ceiling(n_bytes: int = 16 << 30, record_bytes: int = 2560, chunk_bytes: int = 768, reps: int = 3) -> dict:
-    """Practical HBM read rates on this device: a plain streaming read of ``n_bytes``, and
+    """Practical HBM read rates on this device: a streaming read of ``n_bytes`` (contiguous
+    spans per workgroup, nontemporal loads), and
     ``chunk_bytes`` reads at the starts of ``record_bytes`` records in a seeded random order
     (the shape of the decode's per-block reads). Returns GB/s for both."""
     buf = torch.empty(n_bytes, dtype=torch.uint8, device="cuda")
@@ -70,10 +71,12 @@ def read_ceiling(n_bytes: int = 16 << 30, record_bytes: int = 2560, chunk_bytes:
     out = torch.empty(blocks * 256, dtype=torch.int32, device="cuda")
     L = lib()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    L.synth_stream_read(_s(), ctypes.c_void_p(buf.data_ptr()), n_bytes // 16, blocks, ctypes.c_void_p(out.data_ptr()))
+    sblocks = 4096   # contiguous spans of 4 MB per workgroup at 16 GiB
+    L.synth_stream_read(_s(), ctypes.c_void_p(buf.data_ptr()), n_bytes // 16, sblocks, ctypes.c_void_p(out.data_ptr()))
     ev0.record()
     for _ in range(reps):
-        L.synth_stream_read(_s(), ctypes.c_void_p(buf.data_ptr()), n_bytes // 16, blocks, ctypes.c_void_p(out.data_ptr()))
+        L.synth_stream_read(_s(), ctypes.c_void_p(buf.data_ptr()), n_bytes // 16, sblocks,
+                            ctypes.c_void_p(out.data_ptr()))
     ev1.record()
     torch.cuda.synchronize()
     stream_gbs = reps * n_bytes / (ev0.elapsed_time(ev1) * 1e-3) / 1e9

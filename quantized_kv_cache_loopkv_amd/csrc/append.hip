@@ -13,7 +13,11 @@
 // All of it in float64 with one round-to-nearest-even to f16, so codes and
 // meta are reproducible bit for bit. Built with -ffp-contract=off.
 //
-// Appends of fewer than GS tokens per sequence (decode time) take one kernel:
+// The one-token append of a decode step takes one kernel:
+//   k_append_token<D, GS>  one workgroup per (cell, sequence) for every head: the token goes
+//                      to its tail slot unless it completes a group, whose GS / 16 records
+//                      the workgroup then quantizes and writes head by head.
+// Other appends of fewer than GS tokens per sequence take one kernel:
 //   k_quantize_groups<D, GS, true>  one workgroup per (head, cell x sequence): reads the
 //                      old tail of the group this append completes (if any) into LDS,
 //                      writes the new tokens that stay in the tail once every read of
@@ -32,6 +36,55 @@
 #include "quantize.h"
 
 namespace lkv {
+
+constexpr int kAppendThreads = 256;   // workgroup size of every append kernel
+
+// Fills kx / vx (bf16 bits [GS][D] in LDS) with the GS tokens of a group: element (i, d) from
+// value(i, d, is_k). Each thread takes the elements tid, tid + 256, ... and requests 16 of them
+// (K and V) before it stores any, so the group costs one or a few memory round trips instead
+// of one per element (the loads would otherwise wait on each other through the LDS stores).
+template <int D, int GS, class Val>
+__device__ inline void gather_group(uint16_t (*kx)[D], uint16_t (*vx)[D], int tid, Val value) {
+  constexpr int PER = GS * D / kAppendThreads;   // 8 .. 64
+  constexpr int CH = PER < 16 ? PER : 16;
+  static_assert(PER % CH == 0, "gather batches");
+#pragma unroll 1
+  for (int k0 = 0; k0 < PER; k0 += CH) {
+    uint16_t kv[CH], vv[CH];
+#pragma unroll
+    for (int k = 0; k < CH; ++k) {
+      const int idx = (k0 + k) * kAppendThreads + tid;
+      kv[k] = value(idx / D, idx % D, true);
+      vv[k] = value(idx / D, idx % D, false);
+    }
+#pragma unroll
+    for (int k = 0; k < CH; ++k) {
+      const int idx = (k0 + k) * kAppendThreads + tid;
+      kx[idx / D][idx % D] = kv[k];
+      vx[idx / D][idx % D] = vv[k];
+    }
+  }
+}
+
+// Codes and meta of the group in kx / vx: the D K groups (one per channel, over the GS tokens)
+// and the GS * D / GS V groups (one per token and run of GS channels) form one task list over
+// the workgroup's threads, so the K and V groups run side by side (the quantizer's loops are
+// latency-bound). Each group is quantize_group's, exactly as in quantize_group_codes.
+template <int D, int GS>
+__device__ inline void quantize_tasks(const uint16_t (*kx)[D], const uint16_t (*vx)[D], int M, uint8_t (*kc)[D],
+                                      uint8_t (*vc)[D], uint32_t* kmeta, uint32_t (*vmeta)[D / GS], int tid) {
+  constexpr int NV = GS * (D / GS);
+  for (int task = tid; task < D + NV; task += kAppendThreads) {
+    if (task < D) {
+      const int d = task;
+      quantize_group([&](int i) { return (double)bf16_bits_to_f32(kx[i][d]); }, GS, M, &kc[0][d], D, &kmeta[d]);
+    } else {
+      const int i = (task - D) / (D / GS), e = (task - D) % (D / GS);
+      quantize_group([&](int j) { return (double)bf16_bits_to_f32(vx[i][e * GS + j]); }, GS, M, &vc[i][e * GS], 1,
+                     &vmeta[i][e]);
+    }
+  }
+}
 
 // The new tokens of (cell ci, sequence b, head h) that stay in the tail (those after the
 // last group the append completes), rounded from f32 if needed.
@@ -63,7 +116,7 @@ __device__ void write_tail_tokens(const AppendArgs& a, const AppendCell& cell, i
 
 // WITH_TAIL: the one-kernel append of fewer than GS tokens (grid x = 1).
 template <int D, int GS, bool WITH_TAIL>
-__global__ void __launch_bounds__(256) k_quantize_groups(AppendArgs a) {
+__global__ void __launch_bounds__(kAppendThreads) k_quantize_groups(AppendArgs a) {
   const int b = blockIdx.z % a.n_seqs;
   const int ci = blockIdx.z / a.n_seqs;
   const int h = blockIdx.y;
@@ -86,25 +139,15 @@ __global__ void __launch_bounds__(256) k_quantize_groups(AppendArgs a) {
 
   const uint16_t* tail = reinterpret_cast<const uint16_t*>(a.ws + cell.tail_off) +
                          ((size_t)slot * a.n_heads + h) * tail_elems(D, GS);
-  for (int idx = tid; complete && idx < GS * D; idx += blockDim.x) {
-    const int i = idx / D, d = idx % D;
-    const int p = g * GS + i;
-    uint16_t kb, vb;
-    if (p < L0) {
-      kb = tail[(0 * GS + (p % GS)) * D + d];
-      vb = tail[(1 * GS + (p % GS)) * D + d];
-    } else {
+  if (complete) {
+    gather_group<D, GS>(kx, vx, tid, [&](int i, int d, bool is_k) -> uint16_t {
+      const int p = g * GS + i;
+      if (p < L0) return tail[((is_k ? 0 : GS) + (p % GS)) * D + d];
       const size_t e = ((((size_t)cell.in_cell * a.n_seqs + b) * a.n_new + (p - L0)) * a.n_heads + h) * D + d;
-      if (a.kv_bf16) {
-        kb = reinterpret_cast<const uint16_t*>(a.k)[e];
-        vb = reinterpret_cast<const uint16_t*>(a.v)[e];
-      } else {
-        kb = f32_to_bf16_rne(reinterpret_cast<const float*>(a.k)[e]);
-        vb = f32_to_bf16_rne(reinterpret_cast<const float*>(a.v)[e]);
-      }
-    }
-    kx[i][d] = kb;
-    vx[i][d] = vb;
+      const void* src = is_k ? a.k : a.v;
+      return a.kv_bf16 ? reinterpret_cast<const uint16_t*>(src)[e]
+                       : f32_to_bf16_rne(reinterpret_cast<const float*>(src)[e]);
+    });
   }
   __syncthreads();
   if constexpr (WITH_TAIL) {   // every read of the old tail is done (barrier above)
@@ -115,9 +158,7 @@ __global__ void __launch_bounds__(256) k_quantize_groups(AppendArgs a) {
   const int M = (cell.kind == KIND_Q2) ? 3 : 15;
   // K: one group per channel over the GS tokens; V: one group per token over each run of GS
   // channels.
-  quantize_group_codes<D, GS>([&](int i, int d) { return (double)bf16_bits_to_f32(kx[i][d]); },
-                              [&](int i, int d) { return (double)bf16_bits_to_f32(vx[i][d]); }, M, kc, vc, kmeta,
-                              vmeta, tid, (int)blockDim.x);
+  quantize_tasks<D, GS>(kx, vx, M, kc, vc, kmeta, vmeta, tid);
   __syncthreads();
 
   // The group's P records: record P g + part holds tokens 16 part .. 16 part + 15 and the
@@ -134,8 +175,85 @@ __global__ void __launch_bounds__(256) k_quantize_groups(AppendArgs a) {
   }
 }
 
+// The one-token append (n_new = 1) of (cell ci, sequence b) for all a.n_heads heads. The
+// token's K and V are requested together with the sequence's length (their addresses do not
+// depend on it), so a step that completes no group costs one memory round trip; the token
+// goes to tail slot L0 mod GS. When it completes group g = L0 / GS it stays out of the tail,
+// and the group of each head in turn (GS - 1 tokens from the tail, the new one from the
+// input) is quantized and packed exactly as in k_quantize_groups. Records, tails and the
+// skipped cases (invalid sequence, unmapped page) are those of k_quantize_groups<D, GS, true>.
 template <int D, int GS>
-__global__ void __launch_bounds__(256) k_write_tail(AppendArgs a) {
+__global__ void __launch_bounds__(kAppendThreads) k_append_token(AppendArgs a) {
+  const int b = blockIdx.x % a.n_seqs;
+  const int ci = blockIdx.x / a.n_seqs;
+  const AppendCell cell = a.cells[ci];
+  const int tid = threadIdx.x;
+  const int HD = a.n_heads * D;
+  const size_t e0 = ((size_t)cell.in_cell * a.n_seqs + b) * HD;   // [cells][n_seqs][1][heads][D]
+  auto new_bits = [&](const void* src, size_t e) -> uint16_t {
+    return a.kv_bf16 ? reinterpret_cast<const uint16_t*>(src)[e]
+                     : f32_to_bf16_rne(reinterpret_cast<const float*>(src)[e]);
+  };
+  const int L0 = a.seq_lens[b];
+  const int slot = a.seq_slots ? a.seq_slots[b] : b;
+  const bool valid = L0 >= 0 && (uint32_t)slot < (uint32_t)a.max_seqs;   // uniform
+  const bool complete = valid && (L0 + 1) % GS == 0;
+  uint16_t* tail0 = reinterpret_cast<uint16_t*>(a.ws + cell.tail_off) + (size_t)(valid ? slot : 0) * a.n_heads * tail_elems(D, GS);
+  const int pos = valid ? L0 % GS : 0;
+  for (int base = 0; base < HD; base += 8 * kAppendThreads) {
+    uint16_t kb[8], vb[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int idx = base + u * kAppendThreads + tid;
+      kb[u] = idx < HD ? new_bits(a.k, e0 + idx) : 0;
+      vb[u] = idx < HD ? new_bits(a.v, e0 + idx) : 0;
+    }
+    if (!valid || complete) break;   // uniform: nothing, or the records below
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int idx = base + u * kAppendThreads + tid;
+      if (idx >= HD) continue;
+      uint16_t* th = tail0 + (size_t)(idx / D) * tail_elems(D, GS);
+      th[(0 * GS + pos) * D + idx % D] = kb[u];
+      th[(1 * GS + pos) * D + idx % D] = vb[u];
+    }
+  }
+  if (!complete) return;
+
+  constexpr int P = GS / kBlock;   // records per group
+  __shared__ uint16_t kx[GS][D];
+  __shared__ uint16_t vx[GS][D];
+  __shared__ uint8_t kc[GS][D];
+  __shared__ uint8_t vc[GS][D];
+  __shared__ uint32_t kmeta[D];
+  __shared__ uint32_t vmeta[GS][D / GS];
+  const int g = L0 / GS;
+  const int M = (cell.kind == KIND_Q2) ? 3 : 15;
+  const int rec = record_bytes(cell.kind, D, GS);
+  const int32_t* bt = a.block_table + (size_t)b * a.bt_stride;
+  for (int h = 0; h < a.n_heads; ++h) {
+    const uint16_t* th = tail0 + (size_t)h * tail_elems(D, GS);
+    // positions g GS .. L0 - 1 sit in tail slots 0 .. GS - 2; the new token is the input's
+    gather_group<D, GS>(kx, vx, tid, [&](int i, int d, bool is_k) -> uint16_t {
+      return i < GS - 1 ? th[((is_k ? 0 : GS) + i) * D + d] : new_bits(is_k ? a.k : a.v, e0 + (size_t)h * D + d);
+    });
+    __syncthreads();
+    quantize_tasks<D, GS>(kx, vx, M, kc, vc, kmeta, vmeta, tid);
+    __syncthreads();
+    for (int part = 0; part < P; ++part) {
+      const int j = P * g + part;
+      if ((j >> a.bt_shift) >= a.bt_stride || (uint32_t)bt[j >> a.bt_shift] >= (uint32_t)a.num_pages)
+        continue;   // page not mapped (uniform over the workgroup): the record is not written
+      const uint32_t phys = record_slot(bt, j, a.bt_shift);
+      uint32_t* r = reinterpret_cast<uint32_t*>(a.ws + cell.pool_off + ((size_t)phys * a.n_heads + h) * rec);
+      pack_record<D, GS>(r, cell.kind, part, kc, vc, kmeta, vmeta, tid, kAppendThreads);
+    }
+    __syncthreads();   // the group's LDS is reused for the next head
+  }
+}
+
+template <int D, int GS>
+__global__ void __launch_bounds__(kAppendThreads) k_write_tail(AppendArgs a) {
   const int b = blockIdx.z % a.n_seqs;
   const int ci = blockIdx.z / a.n_seqs;
   write_tail_tokens<D, GS>(a, a.cells[ci], b, blockIdx.y, a.seq_lens[b]);
@@ -143,15 +261,19 @@ __global__ void __launch_bounds__(256) k_write_tail(AppendArgs a) {
 
 template <int D, int GS>
 static void launch_dg(const AppendArgs& a, hipStream_t stream) {
+  if (a.n_new == 1) {   // a decode step's token: one workgroup per (cell, sequence)
+    hipLaunchKernelGGL((k_append_token<D, GS>), dim3(a.n_cells * a.n_seqs), dim3(kAppendThreads), 0, stream, a);
+    return;
+  }
   if (a.n_new < GS) {   // at most one group per (sequence, head) completes: one kernel
-    hipLaunchKernelGGL((k_quantize_groups<D, GS, true>), dim3(1, a.n_heads, a.n_cells * a.n_seqs), dim3(256), 0,
+    hipLaunchKernelGGL((k_quantize_groups<D, GS, true>), dim3(1, a.n_heads, a.n_cells * a.n_seqs), dim3(kAppendThreads), 0,
                        stream, a);
     return;
   }
   const int slots = a.n_new / GS + 1;   // groups one append can complete
-  hipLaunchKernelGGL((k_quantize_groups<D, GS, false>), dim3(slots, a.n_heads, a.n_cells * a.n_seqs), dim3(256), 0,
+  hipLaunchKernelGGL((k_quantize_groups<D, GS, false>), dim3(slots, a.n_heads, a.n_cells * a.n_seqs), dim3(kAppendThreads), 0,
                      stream, a);
-  hipLaunchKernelGGL((k_write_tail<D, GS>), dim3(1, a.n_heads, a.n_cells * a.n_seqs), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((k_write_tail<D, GS>), dim3(1, a.n_heads, a.n_cells * a.n_seqs), dim3(kAppendThreads), 0, stream, a);
 }
 
 template <int D>

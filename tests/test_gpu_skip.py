@@ -1,8 +1,9 @@
 """The token-skipping ablation (loopkv_decode_attn_skip) on the GPU.
 
 "LoopKV: Loop-Aware KV Cache Compression for Serving Looped Transformers" (arXiv:2611.04137),
-Abstract: skipping low-attention values to save reads produces errors that compound across
-loops, so the method reads the unselected tokens at 2 bits instead of skipping them.
+Abstract, sentence on skipping: leaving out the values of weakly attended tokens saves reads
+but its error grows from loop to loop, so the method reads the unselected tokens at 2 bits
+instead of leaving them out.
 
 * rows of the skip kernel match the oracle's skip mode (selection bit-exact outside the 1e-5
   tie band, output within 2e-3), over tau regimes, head dims, ragged lengths and a mixed plan;

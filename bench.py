@@ -141,14 +141,36 @@ def target_kinds(plan, n_loops, n_layers):
     return out
 
 
-def append_bytes(n_storing, B, H, D, lengths_before, group=32):
+def append_bytes(n_storing, B, H, D, lengths_before, group=32, n_q2=0):
     """Bytes of a one-token append: bf16 K and V in, one tail slot out; a completed group
-    also reads its G - 1 tail tokens and writes its G / 16 4-bit records (G D + 8 D bytes)."""
-    import numpy as np
+    also reads its G - 1 tail tokens and writes its G / 16 records: G D + 8 D bytes at 4 bits,
+    G D / 2 + 8 D bytes for the n_q2 storing cells kept at 2 bits."""
     tok = 2 * H * D * 2
     total = n_storing * B * (tok + tok)
     done = sum(1 for n in lengths_before if n % group == group - 1)
-    return total + n_storing * done * H * ((group - 1) * 2 * D * 2 + group * D + 8 * D)
+    tail_read = (group - 1) * 2 * D * 2
+    flush = (n_storing - n_q2) * (tail_read + group * D + 8 * D) + n_q2 * (tail_read + group * D // 2 + 8 * D)
+    return total + done * H * flush
+
+
+def append_figures(app_ms, lengths_before, n_storing, B, H, D, group=32, n_q2=0):
+    """The timed steps' one-token appends, split into steps that only write the token to the tail
+    and steps whose token completes a group of every sequence (each then quantizes and writes the
+    group's records): mean ms, algorithmic bytes (append_bytes) and GB/s of each kind. The append
+    is latency-bound (a few KB per workgroup); the fraction of the 8 TB/s peak is given anyway."""
+    import numpy as np
+    out = {}
+    for kind, pick in (("token_only", lambda L: all(n % group != group - 1 for n in L)),
+                       ("group_completing", lambda L: any(n % group == group - 1 for n in L))):
+        idx = [i for i, L in enumerate(lengths_before) if pick(L)]
+        if not idx:
+            continue
+        ms = float(np.mean([app_ms[i] for i in idx]))
+        by = float(np.mean([append_bytes(n_storing, B, H, D, lengths_before[i], group, n_q2) for i in idx]))
+        gbs = by / (ms * 1e-3) / 1e9
+        out[kind] = {"steps": len(idx), "ms": round(ms, 4), "algorithmic_GB": round(by / 1e9, 4),
+                     "GBps": round(gbs, 1), "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4)}
+    return out
 
 
 def sel_counts_from_mask(sm, n_q):
@@ -478,14 +500,18 @@ def main():
     counts[tk != 0] = 0
     dec_bytes = algorithmic_bytes(plan, final_lens, H, D, counts, group=GQ)
     n_storing = len(wl.storing_cells())
+    n_q2 = int((plan == 1).sum())   # storing cells kept at 2 bits
     step_bytes = [algorithmic_bytes(plan, wl.current_lengths(s + 1), H, D, counts, group=GQ) +
-                  append_bytes(n_storing, B, H, D, lengths_before[s], group=GQ) for s in range(args.warmup, S)]
+                  append_bytes(n_storing, B, H, D, lengths_before[s], group=GQ, n_q2=n_q2) for s in range(args.warmup, S)]
     value = float(np.mean(step_bytes)) / (ms_per_step * 1e-3) / 1e9
     dec_mean_ms = float(np.mean(dec_ms))
     achieved = dec_bytes / (dec_mean_ms * 1e-3) / 1e9
     sel_frac = float(counts.sum()) / max(1, sum(H * GQ * (n // GQ) for n in final_lens) * int((tk == 0).sum()))
     log(f"step {ms_per_step:.3f} ms (events {np.mean(step_ms):.3f}), decode {dec_mean_ms:.3f} ms, "
         f"append {np.mean(app_ms):.3f} ms; decode {achieved:.0f} GB/s algorithmic; selected fraction {sel_frac:.2e}")
+    append_fig = append_figures(app_ms, [lengths_before[s] for s in range(args.warmup, S)], n_storing, B,
+                                cfg.kv_heads, D, GQ, n_q2)
+    log(f"append: {append_fig}")
 
     extra = {}
     if not args.no_sweep:
@@ -636,6 +662,7 @@ def main():
         "cpu_baseline": cpu,
         "selected_fraction_q4_targets": sel_frac,
         "append_ms": round(float(np.mean(app_ms)), 4),
+        "append": append_fig,
     }
     line.update(extra)
     print(json.dumps(line), flush=True)

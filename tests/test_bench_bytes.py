@@ -76,6 +76,20 @@ def test_append_bytes(G):
     got = bench.append_bytes(4, B, H, D, before, group=G)
     flush = H * ((G - 1) * 4 * D + (G // 16) * (16 * D + 2 * (64 * D // G)))
     assert got == 4 * B * 2 * tok + 4 * 2 * flush
+    # one of the four storing cells at 2 bits: its records hold one K and one V plane (8 D per block)
+    flush2 = H * ((G - 1) * 4 * D + (G // 16) * (8 * D + 2 * (64 * D // G)))
+    assert bench.append_bytes(4, B, H, D, before, group=G, n_q2=1) == 4 * B * 2 * tok + 3 * 2 * flush + 2 * flush2
+
+
+def test_append_figures_split_step_kinds():
+    """Token-only steps and group-completing steps are reported apart, each with its own bytes."""
+    D, H, B, G = 128, 2, 2, 32
+    lens = [[5, 7], [G - 1, 2 * G - 1], [6, 8]]
+    fig = bench.append_figures([0.01, 0.5, 0.03], lens, 3, B, H, D, G, n_q2=1)
+    assert fig["token_only"]["steps"] == 2 and fig["group_completing"]["steps"] == 1
+    assert abs(fig["token_only"]["ms"] - 0.02) < 1e-9 and fig["group_completing"]["ms"] == 0.5
+    by = bench.append_bytes(3, B, H, D, lens[1], G, 1)
+    assert abs(fig["group_completing"]["algorithmic_GB"] - round(by / 1e9, 4)) < 1e-12
 
 
 def test_gathered_bytes_counts_units_and_blocks():

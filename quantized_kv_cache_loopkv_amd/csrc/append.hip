@@ -38,6 +38,7 @@
 namespace lkv {
 
 constexpr int kAppendThreads = 256;   // workgroup size of every append kernel
+constexpr int kQuantStep = 4;         // elements per quantizer loop step (their latencies overlap)
 
 // Fills kx / vx (bf16 bits [GS][D] in LDS) with the GS tokens of a group: element (i, d) from
 // value(i, d, is_k). Each thread takes the elements tid, tid + 256, ... and requests 16 of them
@@ -77,11 +78,12 @@ __device__ inline void quantize_tasks(const uint16_t (*kx)[D], const uint16_t (*
   for (int task = tid; task < D + NV; task += kAppendThreads) {
     if (task < D) {
       const int d = task;
-      quantize_group([&](int i) { return (double)bf16_bits_to_f32(kx[i][d]); }, GS, M, &kc[0][d], D, &kmeta[d]);
+      quantize_group<kQuantStep>([&](int i) { return (double)bf16_bits_to_f32(kx[i][d]); }, GS, M, &kc[0][d], D,
+                                 &kmeta[d]);
     } else {
       const int i = (task - D) / (D / GS), e = (task - D) % (D / GS);
-      quantize_group([&](int j) { return (double)bf16_bits_to_f32(vx[i][e * GS + j]); }, GS, M, &vc[i][e * GS], 1,
-                     &vmeta[i][e]);
+      quantize_group<kQuantStep>([&](int j) { return (double)bf16_bits_to_f32(vx[i][e * GS + j]); }, GS, M,
+                                 &vc[i][e * GS], 1, &vmeta[i][e], vgroup_rot<GS>(task - D));
     }
   }
 }
@@ -132,7 +134,7 @@ __global__ void __launch_bounds__(kAppendThreads) k_quantize_groups(AppendArgs a
 
   __shared__ uint16_t kx[GS][D];   // bf16 bits of the group's GS tokens (exact values)
   __shared__ uint16_t vx[GS][D];
-  __shared__ uint8_t kc[GS][D];
+  __shared__ __align__(16) uint8_t kc[GS][D];   // rows read as 32-bit words by the packer
   __shared__ uint8_t vc[GS][D];
   __shared__ uint32_t kmeta[D];
   __shared__ uint32_t vmeta[GS][D / GS];
@@ -182,8 +184,17 @@ __global__ void __launch_bounds__(kAppendThreads) k_quantize_groups(AppendArgs a
 // and the group of each head in turn (GS - 1 tokens from the tail, the new one from the
 // input) is quantized and packed exactly as in k_quantize_groups. Records, tails and the
 // skipped cases (invalid sequence, unmapped page) are those of k_quantize_groups<D, GS, true>.
+// Waves per SIMD the one-token append asks the register allocator for: its workgroups' LDS
+// (the group staging of k_append_token) allows floor(160 KB / LDS) of them per CU, each one wave
+// per SIMD; at most four.
+constexpr int append_token_waves(int D, int GS) {
+  const int lds = GS * D * 2 * 2 + GS * D * 2 + 4 * D + 4 * GS * (D / GS);
+  const int per_cu = 160 * 1024 / lds;
+  return per_cu < 1 ? 1 : per_cu > 4 ? 4 : per_cu;
+}
+
 template <int D, int GS>
-__global__ void __launch_bounds__(kAppendThreads) k_append_token(AppendArgs a) {
+__global__ void __launch_bounds__(kAppendThreads, append_token_waves(D, GS)) k_append_token(AppendArgs a) {
   const int b = blockIdx.x % a.n_seqs;
   const int ci = blockIdx.x / a.n_seqs;
   const AppendCell cell = a.cells[ci];
@@ -223,7 +234,7 @@ __global__ void __launch_bounds__(kAppendThreads) k_append_token(AppendArgs a) {
   constexpr int P = GS / kBlock;   // records per group
   __shared__ uint16_t kx[GS][D];
   __shared__ uint16_t vx[GS][D];
-  __shared__ uint8_t kc[GS][D];
+  __shared__ __align__(16) uint8_t kc[GS][D];   // rows read as 32-bit words by the packer
   __shared__ uint8_t vc[GS][D];
   __shared__ uint32_t kmeta[D];
   __shared__ uint32_t vmeta[GS][D / GS];

@@ -54,34 +54,87 @@ __device__ inline uint16_t f32_to_bf16_rne(float f) {
   return (uint16_t)(u >> 16);
 }
 
-// Quantize n values read through get(i) with M = 2^bits - 1 levels. The loops stay rolled: a
-// caller inside the decode kernel has few registers to spare.
-template <typename Get>
-__device__ inline void quantize_group(Get get, int n, int M, uint8_t* codes, int stride, uint32_t* meta) {
+// Quantize n values (n a power of two) read through get(i) with M = 2^bits - 1 levels. Step k
+// takes element (k + rot) mod n: the minimum, the maximum and each element's code do not depend
+// on the order, and callers whose lanes read elements at a stride that maps them to the same
+// LDS bank give each lane its own rotation. U elements are taken per loop step (U divides n),
+// their loads and divisions independent of each other; U = 1 keeps the loops rolled for a
+// caller inside the decode kernel, which has few registers to spare.
+template <int U = 1, typename Get>
+__device__ inline void quantize_group(Get get, int n, int M, uint8_t* codes, int stride, uint32_t* meta, int rot = 0) {
 #pragma clang fp contract(off)
-  double mn = get(0), mx = mn;
+  static_assert(U == 1 || U == 2 || U == 4 || U == 8, "elements per step");
+  const int mask = n - 1;
+  double mn = get(rot & mask), mx = mn;
+  if constexpr (U == 1) {
 #pragma unroll 1
-  for (int i = 1; i < n; ++i) {
-    double x = get(i);
-    mn = fmin(mn, x);
-    mx = fmax(mx, x);
+    for (int k = 1; k < n; ++k) {
+      double x = get((k + rot) & mask);
+      mn = fmin(mn, x);
+      mx = fmax(mx, x);
+    }
+  } else {
+#pragma unroll 1
+    for (int k0 = 0; k0 < n; k0 += U) {
+      double x[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) x[u] = get((k0 + u + rot) & mask);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        mn = fmin(mn, x[u]);
+        mx = fmax(mx, x[u]);
+      }
+    }
   }
   uint32_t zb = f64_to_f16_bits(mn);
   uint32_t sb = f64_to_f16_bits((mx - mn) / (double)M);
   double z = f16_bits_to_f64(zb);
   double s = f16_bits_to_f64(sb);
+  // The code is rint of the correctly rounded quotient q = (x - z) / s. The product y = (x - z) *
+  // fl(1 / s) is within |q| 2^-51 of q, below 2^-46 for the quotients that matter here (|q| <= 16;
+  // larger ones clamp to M either way), so rint(y) = rint(q) unless a rounding tie k + 1/2 lies
+  // within 2^-46 of y: there (|y - floor(y) - 1/2| <= 2^-40) the division itself decides.
+  // Infinities and NaNs reach the same codes on both routes.
+  // The division runs behind a wave-uniform test, only in waves where some lane needs it.
+  const double rs = 1.0 / s;
 #pragma unroll 1
-  for (int i = 0; i < n; ++i) {
-    int c = 0;
-    if (s != 0.0) {
-      double r = rint((get(i) - z) / s);
-      r = fmin(fmax(r, 0.0), (double)M);
-      c = (int)r;
+  for (int k0 = 0; k0 < n; k0 += U) {
+    double d[U], y[U];
+    bool tie[U];
+    bool any_tie = false;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      d[u] = get((k0 + u + rot) & mask) - z;
+      y[u] = d[u] * rs;
+      tie[u] = fabs(y[u] - floor(y[u]) - 0.5) <= 0x1p-40;
+      any_tie |= tie[u];
     }
-    codes[i * stride] = (uint8_t)c;
+    if (__any(any_tie)) {
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (tie[u]) y[u] = d[u] / s;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = (k0 + u + rot) & mask;
+      int c = 0;
+      if (s != 0.0) {   // s = 0: every code is 0 (y is not used)
+        double r = rint(y[u]);
+        r = fmin(fmax(r, 0.0), (double)M);
+        c = (int)r;
+      }
+      codes[i * stride] = (uint8_t)c;
+    }
   }
   *meta = sb | (zb << 16);
 }
+
+// Rotation of V group `task` (token task / (D / GS), channels GS (task mod (D / GS)) + ...): the
+// groups of consecutive tasks sit GS * 2 bytes apart in the bf16 staging rows and GS bytes apart
+// in the code rows, so without it the lanes of a wave hit a few LDS banks at every step; task
+// times GS / 32 spreads them over all banks.
+template <int GS>
+__device__ inline int vgroup_rot(int task) { return task * (GS / 32); }
 
 // Channel stored at K-meta position i: the words of a K column follow the column's
 // bit layout (2-bit: byte k, bit pair p; 4-bit: byte k, nibble n).
@@ -98,7 +151,8 @@ __device__ inline void quantize_group_codes(GetK getk, GetV getv, int M, uint8_t
   for (int d = tid; d < D; d += nthr) quantize_group([&](int i) { return getk(i, d); }, GS, M, &kc[0][d], D, &kmeta[d]);
   for (int task = tid; task < GS * (D / GS); task += nthr) {
     const int i = task / (D / GS), e = task % (D / GS);
-    quantize_group([&](int j) { return getv(i, e * GS + j); }, GS, M, &vc[i][e * GS], 1, &vmeta[i][e]);
+    quantize_group([&](int j) { return getv(i, e * GS + j); }, GS, M, &vc[i][e * GS], 1, &vmeta[i][e],
+                   vgroup_rot<GS>(task));
   }
 }
 
@@ -128,12 +182,23 @@ __device__ inline void pack_record(uint32_t* r, int kind, int part, const uint8_
       r[off_vmeta_kivi(D, GS) / 4 + idx] = vmeta[t0 + idx % kBlock][idx / kBlock];
   } else {
     const bool q4 = kind == KIND_Q4;
-    // K planes: D/16 columns x 16 tokens.
+    // K planes: D/16 columns x 16 tokens. The lanes of a column read code rows D bytes apart,
+    // so each takes its row's four code words in its own rotated order (fewer lanes on one LDS
+    // bank at a time) and puts them back in order with selects; kc rows are 16-byte aligned.
     for (int idx = tid; idx < (D / 16) * kBlock; idx += nthr) {
       const int w = idx / kBlock, t = idx % kBlock;
+      const uint32_t* row = reinterpret_cast<const uint32_t*>(&kc[t0 + t][16 * w]);
+      const int rr = t & 3;
+      const uint32_t a0 = row[rr], a1 = row[(rr + 1) & 3], a2 = row[(rr + 2) & 3], a3 = row[(rr + 3) & 3];
+      // code word k = a[(k - rr) mod 4]
+      const uint32_t cw[4] = {rr == 0 ? a0 : rr == 1 ? a3 : rr == 2 ? a2 : a1,
+                              rr == 0 ? a1 : rr == 1 ? a0 : rr == 2 ? a3 : a2,
+                              rr == 0 ? a2 : rr == 1 ? a1 : rr == 2 ? a0 : a3,
+                              rr == 0 ? a3 : rr == 1 ? a2 : rr == 2 ? a1 : a0};
       uint32_t hi = 0, lo = 0;
+#pragma unroll
       for (int c = 0; c < 16; ++c) {
-        const uint32_t code = kc[t0 + t][16 * w + c];
+        const uint32_t code = (cw[c >> 2] >> (8 * (c & 3))) & 0xffu;
         if (q4) {
           hi |= (code >> 2) << (2 * c);
           lo |= (code & 3u) << (2 * c);

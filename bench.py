@@ -153,6 +153,23 @@ def append_bytes(n_storing, B, H, D, lengths_before, group=32, n_q2=0):
     return total + done * H * flush
 
 
+def prefill_bytes(plan, lengths, H, D, group=32):
+    """Bytes of the bulk appends that build the cache: for every storing cell and sequence of N
+    tokens, bf16 K and V in (4 D B per token-head), the records of its N // G complete groups out
+    (G D + 8 D B per group-head at 4 bits, G D / 2 + 8 D at 2 bits) and its last N mod G tokens
+    into the tail (4 D B per token-head)."""
+    import numpy as np
+    plan = np.asarray(plan).reshape(-1)
+    total = 0
+    for kind in plan:
+        if kind == 2:   # reuse: nothing stored
+            continue
+        flush = group * D + 8 * D if kind == 0 else group * D // 2 + 8 * D
+        for N in lengths:
+            total += H * (N * 4 * D + (N // group) * flush + (N % group) * 4 * D)
+    return total
+
+
 def append_figures(app_ms, lengths_before, n_storing, B, H, D, group=32, n_q2=0):
     """The timed steps' one-token appends, split into steps that only write the token to the tail
     and steps whose token completes a group of every sequence (each then quantizes and writes the
@@ -461,8 +478,16 @@ def main():
     t0 = time.time()
     wl = Workload(cfg, gpu_synth=True, log=log)
     log(f"workspace {wl.ws.numel() / 1e9:.2f} GB; filling {len(wl.storing_cells())} storing cells")
-    wl.fill()
+    fill_ev = []
+    wl.fill(events=fill_ev)
     log(f"filled in {time.time() - t0:.1f}s")
+    fill_ms = sum(e0.elapsed_time(e1) for e0, e1, _ in fill_ev)
+    pre_by = prefill_bytes(plan, cfg.lengths, cfg.kv_heads, D, GQ)
+    prefill = {"tokens_per_sequence": int(max(cfg.lengths)), "append_calls": len(fill_ev),
+               "ms": round(fill_ms, 3), "algorithmic_GB": round(pre_by / 1e9, 3),
+               "GBps": round(pre_by / (fill_ms * 1e-3) / 1e9, 1),
+               "frac_of_peak": round(pre_by / (fill_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    log(f"prefill appends: {prefill}")
     q = wl.q_all()
     out = torch.empty((C, B, H, D), dtype=torch.bfloat16, device="cuda")
     stream = torch.cuda.current_stream()
@@ -663,6 +688,7 @@ def main():
         "selected_fraction_q4_targets": sel_frac,
         "append_ms": round(float(np.mean(app_ms)), 4),
         "append": append_fig,
+        "prefill": prefill,
     }
     line.update(extra)
     print(json.dumps(line), flush=True)

@@ -90,9 +90,23 @@ class Workload:
                   self.factors_dev[cell, 1].contiguous(), V, t0s=t0s + b * cfg.token_stride)
         return K, V
 
-    def fill(self, chunk_tokens: Optional[int] = None):
-        """Append every sequence's initial history to every storing cell (bulk appends)."""
+    def fill(self, chunk_tokens: Optional[int] = None, events: Optional[list] = None):
+        """Append every sequence's initial history to every storing cell (bulk appends). With
+        ``events`` (a list), each append call is bracketed by a pair of timing events on the
+        current stream, appended as (start, end, cell)."""
         cfg = self.cfg
+        stream = torch.cuda.current_stream() if events is not None else None
+
+        def timed_append(*args, **kw):
+            if events is None:
+                self.ctx.append(*args, **kw)
+                return
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            self.ctx.append(*args, **kw)
+            e1.record(stream)
+            events.append((e0, e1, c))
+
         equal = len(set(cfg.lengths)) == 1
         t_start = time.time()
         for i, c in enumerate(self.storing_cells()):
@@ -104,7 +118,7 @@ class Workload:
                     n = min(step, N - t0)
                     K, V = self.kv_chunk(c, t0, n)
                     lens = torch.full((cfg.batch,), t0, dtype=torch.int32, device=self.device)
-                    self.ctx.append(K, V, self.bt, lens, cell=(loop, layer))
+                    timed_append(K, V, self.bt, lens, cell=(loop, layer))
                     del K, V
             else:
                 for b in range(cfg.batch):
@@ -116,7 +130,7 @@ class Workload:
                         K, V = K[:, :N].contiguous(), V[:, :N].contiguous()
                     lens = torch.zeros(1, dtype=torch.int32, device=self.device)
                     slots = torch.tensor([b], dtype=torch.int32, device=self.device)
-                    self.ctx.append(K, V, self.bt[b:b + 1].contiguous(), lens, cell=(loop, layer), seq_slots=slots)
+                    timed_append(K, V, self.bt[b:b + 1].contiguous(), lens, cell=(loop, layer), seq_slots=slots)
             if (i + 1) % 8 == 0:
                 torch.cuda.synchronize()
                 self.log(f"  filled {i + 1}/{len(self.storing_cells())} cells ({time.time() - t_start:.1f}s)")

@@ -126,3 +126,29 @@ def test_cpu_rows_task(tmp_path):
         V = bf16_bits_to_f32(np.ascontiguousarray(vb[:, h])).astype(np.float64)
         _, sel, _ = O.decode_row(q[h], K, V, 0, 0.01, sig)
         assert n_sel == int(sel.sum())
+
+
+@pytest.mark.parametrize("G", [32, 64])
+def test_prefill_bytes(G):
+    """Bulk appends: K and V in, the complete groups' records out, the rest into the tail; reuse
+    cells store nothing."""
+    D, H = 128, 2
+    lengths = [3 * G + 5, G]
+    got = bench.prefill_bytes(np.array([0, 1, 2]), lengths, H, D, group=G)
+    rec4, rec2 = (G // 16) * record_size(0, D, G), (G // 16) * record_size(1, D, G)
+    want = 0
+    for rec in (rec4, rec2):
+        for N in lengths:
+            want += H * (N * 4 * D + (N // G) * rec + (N % G) * 4 * D)
+    assert got == want
+    assert record_size(0, D, 32) == 20 * D and record_size(1, D, 32) == 12 * D   # the layout's 20D / 12D
+    assert record_size(0, D, 64) == 18 * D and record_size(1, D, 64) == 10 * D
+
+
+def record_size(kind, D, G):
+    """Bytes of one 16-token record, from the record layout: the K and V high planes (4 D each),
+    the K meta and the V meta (64 D / G each: 2 D at G = 32), and at 4 bits the K and V low
+    planes (4 D each)."""
+    meta = 2 * (64 * D // G)
+    planes = 2 * 4 * D + (2 * 4 * D if kind == 0 else 0)
+    return planes + meta

@@ -67,6 +67,41 @@ __device__ inline void gather_group(uint16_t (*kx)[D], uint16_t (*vx)[D], int ti
   }
 }
 
+// Rows r0 .. r0 + n - 1 of kx / vx (bf16, D channels) from K rows at ksrc + r stride and V rows
+// at vsrc + r stride (r = 0 .. n - 1; every row and both sources 16-byte aligned): 16-byte loads,
+// two K and two V per thread requested before any is stored (named registers: an array here
+// ends up in scratch memory).
+template <int D, int GS>
+__device__ inline void copy_rows16(uint16_t (*kx)[D], uint16_t (*vx)[D], int r0, int n, const uint16_t* ksrc,
+                                   const uint16_t* vsrc, size_t stride, int tid) {
+  constexpr int C8 = D / 8;   // 16-byte chunks per row
+  const int total = n * C8;
+  auto src = [&](int c) { return (size_t)(c / C8) * stride + 8 * (c % C8); };
+#pragma unroll 1
+  for (int c0 = tid; c0 < total; c0 += 2 * kAppendThreads) {
+    const int c1 = c0 + kAppendThreads;
+    const uint4 k0 = *reinterpret_cast<const uint4*>(ksrc + src(c0));
+    const uint4 v0 = *reinterpret_cast<const uint4*>(vsrc + src(c0));
+    uint4 k1 = k0, v1 = v0;
+    if (c1 < total) {
+      k1 = *reinterpret_cast<const uint4*>(ksrc + src(c1));
+      v1 = *reinterpret_cast<const uint4*>(vsrc + src(c1));
+    }
+    *reinterpret_cast<uint4*>(&kx[r0 + c0 / C8][8 * (c0 % C8)]) = k0;
+    *reinterpret_cast<uint4*>(&vx[r0 + c0 / C8][8 * (c0 % C8)]) = v0;
+    if (c1 < total) {
+      *reinterpret_cast<uint4*>(&kx[r0 + c1 / C8][8 * (c1 % C8)]) = k1;
+      *reinterpret_cast<uint4*>(&vx[r0 + c1 / C8][8 * (c1 % C8)]) = v1;
+    }
+  }
+}
+
+// bf16 inputs whose K and V tensors start on 16-byte boundaries (rows of D channels then are
+// too) take the 16-byte gathers; others the element-wise ones.
+__device__ inline bool rows16_ok(const AppendArgs& a) {
+  return a.kv_bf16 && ((reinterpret_cast<uintptr_t>(a.k) | reinterpret_cast<uintptr_t>(a.v)) & 15u) == 0;
+}
+
 // Codes and meta of the group in kx / vx: the D K groups (one per channel, over the GS tokens)
 // and the GS * D / GS V groups (one per token and run of GS channels) form one task list over
 // the workgroup's threads, so the K and V groups run side by side (the quantizer's loops are
@@ -132,8 +167,8 @@ __global__ void __launch_bounds__(kAppendThreads) k_quantize_groups(AppendArgs a
   const int tid = threadIdx.x;
   constexpr int P = GS / kBlock;   // records per group
 
-  __shared__ uint16_t kx[GS][D];   // bf16 bits of the group's GS tokens (exact values)
-  __shared__ uint16_t vx[GS][D];
+  __shared__ __align__(16) uint16_t kx[GS][D];   // bf16 bits of the group's GS tokens (exact values)
+  __shared__ __align__(16) uint16_t vx[GS][D];
   __shared__ __align__(16) uint8_t kc[GS][D];   // rows read as 32-bit words by the packer
   __shared__ uint8_t vc[GS][D];
   __shared__ uint32_t kmeta[D];
@@ -141,7 +176,11 @@ __global__ void __launch_bounds__(kAppendThreads) k_quantize_groups(AppendArgs a
 
   const uint16_t* tail = reinterpret_cast<const uint16_t*>(a.ws + cell.tail_off) +
                          ((size_t)slot * a.n_heads + h) * tail_elems(D, GS);
-  if (complete) {
+  if (complete && g * GS >= L0 && rows16_ok(a)) {   // the whole group comes from the input
+    const size_t row0 = (((size_t)cell.in_cell * a.n_seqs + b) * a.n_new + (size_t)(g * GS - L0)) * a.n_heads + h;
+    copy_rows16<D, GS>(kx, vx, 0, GS, reinterpret_cast<const uint16_t*>(a.k) + row0 * D,
+                       reinterpret_cast<const uint16_t*>(a.v) + row0 * D, (size_t)a.n_heads * D, tid);
+  } else if (complete) {
     gather_group<D, GS>(kx, vx, tid, [&](int i, int d, bool is_k) -> uint16_t {
       const int p = g * GS + i;
       if (p < L0) return tail[((is_k ? 0 : GS) + (p % GS)) * D + d];
@@ -186,11 +225,12 @@ __global__ void __launch_bounds__(kAppendThreads) k_quantize_groups(AppendArgs a
 // skipped cases (invalid sequence, unmapped page) are those of k_quantize_groups<D, GS, true>.
 // Waves per SIMD the one-token append asks the register allocator for: its workgroups' LDS
 // (the group staging of k_append_token) allows floor(160 KB / LDS) of them per CU, each one wave
-// per SIMD; at most four.
+// per SIMD; at most four, three for groups of 64 (their gathers need more registers).
 constexpr int append_token_waves(int D, int GS) {
   const int lds = GS * D * 2 * 2 + GS * D * 2 + 4 * D + 4 * GS * (D / GS);
   const int per_cu = 160 * 1024 / lds;
-  return per_cu < 1 ? 1 : per_cu > 4 ? 4 : per_cu;
+  const int cap = GS == 64 ? 3 : 4;
+  return per_cu < 1 ? 1 : per_cu > cap ? cap : per_cu;
 }
 
 template <int D, int GS>
@@ -232,8 +272,8 @@ __global__ void __launch_bounds__(kAppendThreads, append_token_waves(D, GS)) k_a
   if (!complete) return;
 
   constexpr int P = GS / kBlock;   // records per group
-  __shared__ uint16_t kx[GS][D];
-  __shared__ uint16_t vx[GS][D];
+  __shared__ __align__(16) uint16_t kx[GS][D];
+  __shared__ __align__(16) uint16_t vx[GS][D];
   __shared__ __align__(16) uint8_t kc[GS][D];   // rows read as 32-bit words by the packer
   __shared__ uint8_t vc[GS][D];
   __shared__ uint32_t kmeta[D];
@@ -245,9 +285,15 @@ __global__ void __launch_bounds__(kAppendThreads, append_token_waves(D, GS)) k_a
   for (int h = 0; h < a.n_heads; ++h) {
     const uint16_t* th = tail0 + (size_t)h * tail_elems(D, GS);
     // positions g GS .. L0 - 1 sit in tail slots 0 .. GS - 2; the new token is the input's
-    gather_group<D, GS>(kx, vx, tid, [&](int i, int d, bool is_k) -> uint16_t {
-      return i < GS - 1 ? th[((is_k ? 0 : GS) + i) * D + d] : new_bits(is_k ? a.k : a.v, e0 + (size_t)h * D + d);
-    });
+    if (rows16_ok(a)) {   // tail rows and the input row with 16-byte loads (tails are 16-byte aligned)
+      copy_rows16<D, GS>(kx, vx, 0, GS - 1, th, th + (size_t)GS * D, D, tid);
+      copy_rows16<D, GS>(kx, vx, GS - 1, 1, reinterpret_cast<const uint16_t*>(a.k) + e0 + (size_t)h * D,
+                         reinterpret_cast<const uint16_t*>(a.v) + e0 + (size_t)h * D, D, tid);
+    } else {
+      gather_group<D, GS>(kx, vx, tid, [&](int i, int d, bool is_k) -> uint16_t {
+        return i < GS - 1 ? th[((is_k ? 0 : GS) + i) * D + d] : new_bits(is_k ? a.k : a.v, e0 + (size_t)h * D + d);
+      });
+    }
     __syncthreads();
     quantize_tasks<D, GS>(kx, vx, M, kc, vc, kmeta, vmeta, tid);
     __syncthreads();

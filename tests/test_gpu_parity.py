@@ -154,6 +154,38 @@ def test_gpu_f32_input_rounds_to_bf16():
             assert np.array_equal(a.record(0, 0, h, j), b_.record(0, 0, h, j))
 
 
+@pytest.mark.gpu
+def test_gpu_append_unaligned_input_same_records():
+    """K and V whose data start 2 bytes past a 16-byte boundary take the element-wise gathers of
+    the append kernels (aligned bf16 inputs take 16-byte loads): the same records and tails, for a
+    bulk append and for one-token appends that complete a group."""
+    _need_gpu()
+    cfg = R.small_config("unal", 1, 1, 2, 128, [70], [0.01])
+    a = Workload(cfg, gpu_synth=False)
+    a.fill()
+    b_ = Workload(cfg, gpu_synth=False)
+    K, V = b_.kv_chunk(0, 0, 70)
+
+    def shifted(x):
+        buf = torch.empty(x.numel() + 8, dtype=x.dtype, device=x.device)
+        y = buf[1:1 + x.numel()].view(x.shape)
+        y.copy_(x)
+        assert y.data_ptr() % 16 == 2 and y.is_contiguous()
+        return y
+
+    lens = torch.zeros(1, dtype=torch.int32, device="cuda")
+    b_.ctx.append(shifted(K[:, :63].contiguous()), shifted(V[:, :63].contiguous()), b_.bt, lens, cell=(0, 0))
+    for t in range(63, 70):   # token 63 completes group 1 through the one-token kernel
+        lens = torch.full((1,), t, dtype=torch.int32, device="cuda")
+        b_.ctx.append(shifted(K[:, t:t + 1].contiguous()), shifted(V[:, t:t + 1].contiguous()), b_.bt, lens,
+                      cell=(0, 0))
+    torch.cuda.synchronize()
+    for h in range(2):
+        for j in range(4):
+            assert np.array_equal(a.record(0, 0, h, j), b_.record(0, 0, h, j)), f"record h={h} j={j}"
+        assert np.array_equal(a.tail(0, 0, h)[:, :6], b_.tail(0, 0, h)[:, :6])
+
+
 # --------------------------------------------------------------------------- decode
 def test_gpu_decode_c1():
     _need_gpu()

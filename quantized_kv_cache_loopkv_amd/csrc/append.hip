@@ -104,8 +104,9 @@ __device__ inline bool rows16_ok(const AppendArgs& a) {
 
 // Codes and meta of the group in kx / vx: the D K groups (one per channel, over the GS tokens)
 // and the GS * D / GS V groups (one per token and run of GS channels) form one task list over
-// the workgroup's threads, so the K and V groups run side by side (the quantizer's loops are
-// latency-bound). Each group is quantize_group's, exactly as in quantize_group_codes.
+// the workgroup's threads, so the K and V groups run side by side; kQuantStep elements per
+// loop step and V groups at rotated starting elements (vgroup_rot). Each group is
+// quantize_group's, as in quantize_group_codes.
 template <int D, int GS>
 __device__ inline void quantize_tasks(const uint16_t (*kx)[D], const uint16_t (*vx)[D], int M, uint8_t (*kc)[D],
                                       uint8_t (*vc)[D], uint32_t* kmeta, uint32_t (*vmeta)[D / GS], int tid) {
@@ -216,13 +217,6 @@ __global__ void __launch_bounds__(kAppendThreads) k_quantize_groups(AppendArgs a
   }
 }
 
-// The one-token append (n_new = 1) of (cell ci, sequence b) for all a.n_heads heads. The
-// token's K and V are requested together with the sequence's length (their addresses do not
-// depend on it), so a step that completes no group costs one memory round trip; the token
-// goes to tail slot L0 mod GS. When it completes group g = L0 / GS it stays out of the tail,
-// and the group of each head in turn (GS - 1 tokens from the tail, the new one from the
-// input) is quantized and packed exactly as in k_quantize_groups. Records, tails and the
-// skipped cases (invalid sequence, unmapped page) are those of k_quantize_groups<D, GS, true>.
 // Waves per SIMD the one-token append asks the register allocator for: its workgroups' LDS
 // (the group staging of k_append_token) allows floor(160 KB / LDS) of them per CU, each one wave
 // per SIMD; at most four, three for groups of 64 (their gathers need more registers).
@@ -233,6 +227,13 @@ constexpr int append_token_waves(int D, int GS) {
   return per_cu < 1 ? 1 : per_cu > cap ? cap : per_cu;
 }
 
+// The one-token append (n_new = 1) of (cell ci, sequence b) for all a.n_heads heads. The
+// token's K and V are requested together with the sequence's length (their addresses do not
+// depend on it), so a step that completes no group costs one memory round trip; the token
+// goes to tail slot L0 mod GS. When it completes group g = L0 / GS it stays out of the tail,
+// and the group of each head in turn (GS - 1 tokens from the tail, the new one from the
+// input) is quantized and packed exactly as in k_quantize_groups. Records, tails and the
+// skipped cases (invalid sequence, unmapped page) are those of k_quantize_groups<D, GS, true>.
 template <int D, int GS>
 __global__ void __launch_bounds__(kAppendThreads, append_token_waves(D, GS)) k_append_token(AppendArgs a) {
   const int b = blockIdx.x % a.n_seqs;

@@ -252,22 +252,37 @@ __global__ void __launch_bounds__(kAppendThreads, append_token_waves(D, GS)) k_a
   const bool complete = valid && (L0 + 1) % GS == 0;
   uint16_t* tail0 = reinterpret_cast<uint16_t*>(a.ws + cell.tail_off) + (size_t)(valid ? slot : 0) * a.n_heads * tail_elems(D, GS);
   const int pos = valid ? L0 % GS : 0;
-  for (int base = 0; base < HD; base += 8 * kAppendThreads) {
-    uint16_t kb[8], vb[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int idx = base + u * kAppendThreads + tid;
-      kb[u] = idx < HD ? new_bits(a.k, e0 + idx) : 0;
-      vb[u] = idx < HD ? new_bits(a.v, e0 + idx) : 0;
+  if (rows16_ok(a)) {   // 16-byte chunks of the token (8 channels of one head; tails are 16-byte aligned)
+    constexpr int C8 = D / 8;
+    const uint16_t* k16 = reinterpret_cast<const uint16_t*>(a.k) + e0;
+    const uint16_t* v16 = reinterpret_cast<const uint16_t*>(a.v) + e0;
+#pragma unroll 1
+    for (int c = tid; c < HD / 8; c += kAppendThreads) {
+      const uint4 kq = *reinterpret_cast<const uint4*>(k16 + 8 * c);
+      const uint4 vq = *reinterpret_cast<const uint4*>(v16 + 8 * c);
+      if (!valid || complete) break;   // uniform: nothing, or the records below
+      uint16_t* th = tail0 + (size_t)(c / C8) * tail_elems(D, GS) + 8 * (c % C8);
+      *reinterpret_cast<uint4*>(th + (size_t)pos * D) = kq;
+      *reinterpret_cast<uint4*>(th + (size_t)(GS + pos) * D) = vq;
     }
-    if (!valid || complete) break;   // uniform: nothing, or the records below
+  } else {
+    for (int base = 0; base < HD; base += 8 * kAppendThreads) {
+      uint16_t kb[8], vb[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int idx = base + u * kAppendThreads + tid;
-      if (idx >= HD) continue;
-      uint16_t* th = tail0 + (size_t)(idx / D) * tail_elems(D, GS);
-      th[(0 * GS + pos) * D + idx % D] = kb[u];
-      th[(1 * GS + pos) * D + idx % D] = vb[u];
+      for (int u = 0; u < 8; ++u) {
+        const int idx = base + u * kAppendThreads + tid;
+        kb[u] = idx < HD ? new_bits(a.k, e0 + idx) : 0;
+        vb[u] = idx < HD ? new_bits(a.v, e0 + idx) : 0;
+      }
+      if (!valid || complete) break;   // uniform: nothing, or the records below
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int idx = base + u * kAppendThreads + tid;
+        if (idx >= HD) continue;
+        uint16_t* th = tail0 + (size_t)(idx / D) * tail_elems(D, GS);
+        th[(0 * GS + pos) * D + idx % D] = kb[u];
+        th[(1 * GS + pos) * D + idx % D] = vb[u];
+      }
     }
   }
   if (!complete) return;

@@ -14,7 +14,7 @@
 // meta are reproducible bit for bit. Built with -ffp-contract=off.
 //
 // The one-token append of a decode step takes one kernel:
-//   k_append_token<D, GS>  one workgroup per (cell, sequence) for every head: the token goes
+//   k_append_token<D, GS>  one workgroup per (cell, sequence, four KV heads): the token goes
 //                      to its tail slot unless it completes a group, whose GS / 16 records
 //                      the workgroup then quantizes and writes head by head.
 // Other appends of fewer than GS tokens per sequence take one kernel:
@@ -39,6 +39,7 @@ namespace lkv {
 
 constexpr int kAppendThreads = 256;   // workgroup size of every append kernel
 constexpr int kQuantStep = 4;         // elements per quantizer loop step (their latencies overlap)
+constexpr int kTokenHeads = 4;        // KV heads per workgroup of the one-token append
 
 // Fills kx / vx (bf16 bits [GS][D] in LDS) with the GS tokens of a group: element (i, d) from
 // value(i, d, is_k). Each thread takes the elements tid, tid + 256, ... and requests 16 of them
@@ -227,7 +228,9 @@ constexpr int append_token_waves(int D, int GS) {
   return per_cu < 1 ? 1 : per_cu > cap ? cap : per_cu;
 }
 
-// The one-token append (n_new = 1) of (cell ci, sequence b) for all a.n_heads heads. The
+// The one-token append (n_new = 1) of (cell ci, sequence b) for kTokenHeads of its heads (the
+// heads of a sequence whose token completes a group are quantized in turn, so with fewer heads
+// per workgroup a step where only some sequences complete a group ends sooner). The
 // token's K and V are requested together with the sequence's length (their addresses do not
 // depend on it), so a step that completes no group costs one memory round trip; the token
 // goes to tail slot L0 mod GS. When it completes group g = L0 / GS it stays out of the tail,
@@ -236,12 +239,16 @@ constexpr int append_token_waves(int D, int GS) {
 // skipped cases (invalid sequence, unmapped page) are those of k_quantize_groups<D, GS, true>.
 template <int D, int GS>
 __global__ void __launch_bounds__(kAppendThreads, append_token_waves(D, GS)) k_append_token(AppendArgs a) {
-  const int b = blockIdx.x % a.n_seqs;
-  const int ci = blockIdx.x / a.n_seqs;
+  const int n_hs = (a.n_heads + kTokenHeads - 1) / kTokenHeads;   // head slices per sequence
+  const int hs = blockIdx.x % n_hs;
+  const int b = (blockIdx.x / n_hs) % a.n_seqs;
+  const int ci = blockIdx.x / n_hs / a.n_seqs;
   const AppendCell cell = a.cells[ci];
   const int tid = threadIdx.x;
-  const int HD = a.n_heads * D;
-  const size_t e0 = ((size_t)cell.in_cell * a.n_seqs + b) * HD;   // [cells][n_seqs][1][heads][D]
+  const int h0 = hs * kTokenHeads, h1 = min(a.n_heads, h0 + kTokenHeads);   // this workgroup's heads
+  const int HD = (h1 - h0) * D;
+  // [cells][n_seqs][1][heads][D], from head h0
+  const size_t e0 = ((size_t)cell.in_cell * a.n_seqs + b) * a.n_heads * D + (size_t)h0 * D;
   auto new_bits = [&](const void* src, size_t e) -> uint16_t {
     return a.kv_bf16 ? reinterpret_cast<const uint16_t*>(src)[e]
                      : f32_to_bf16_rne(reinterpret_cast<const float*>(src)[e]);
@@ -250,7 +257,8 @@ __global__ void __launch_bounds__(kAppendThreads, append_token_waves(D, GS)) k_a
   const int slot = a.seq_slots ? a.seq_slots[b] : b;
   const bool valid = L0 >= 0 && (uint32_t)slot < (uint32_t)a.max_seqs;   // uniform
   const bool complete = valid && (L0 + 1) % GS == 0;
-  uint16_t* tail0 = reinterpret_cast<uint16_t*>(a.ws + cell.tail_off) + (size_t)(valid ? slot : 0) * a.n_heads * tail_elems(D, GS);
+  uint16_t* tail0 = reinterpret_cast<uint16_t*>(a.ws + cell.tail_off) +
+                   ((size_t)(valid ? slot : 0) * a.n_heads + h0) * tail_elems(D, GS);   // head h0's tail
   const int pos = valid ? L0 % GS : 0;
   if (rows16_ok(a)) {   // 16-byte chunks of the token (8 channels of one head; tails are 16-byte aligned)
     constexpr int C8 = D / 8;
@@ -298,16 +306,16 @@ __global__ void __launch_bounds__(kAppendThreads, append_token_waves(D, GS)) k_a
   const int M = (cell.kind == KIND_Q2) ? 3 : 15;
   const int rec = record_bytes(cell.kind, D, GS);
   const int32_t* bt = a.block_table + (size_t)b * a.bt_stride;
-  for (int h = 0; h < a.n_heads; ++h) {
-    const uint16_t* th = tail0 + (size_t)h * tail_elems(D, GS);
+  for (int h = h0; h < h1; ++h) {
+    const uint16_t* th = tail0 + (size_t)(h - h0) * tail_elems(D, GS);
     // positions g GS .. L0 - 1 sit in tail slots 0 .. GS - 2; the new token is the input's
     if (rows16_ok(a)) {   // tail rows and the input row with 16-byte loads (tails are 16-byte aligned)
       copy_rows16<D, GS>(kx, vx, 0, GS - 1, th, th + (size_t)GS * D, D, tid);
-      copy_rows16<D, GS>(kx, vx, GS - 1, 1, reinterpret_cast<const uint16_t*>(a.k) + e0 + (size_t)h * D,
-                         reinterpret_cast<const uint16_t*>(a.v) + e0 + (size_t)h * D, D, tid);
+      copy_rows16<D, GS>(kx, vx, GS - 1, 1, reinterpret_cast<const uint16_t*>(a.k) + e0 + (size_t)(h - h0) * D,
+                         reinterpret_cast<const uint16_t*>(a.v) + e0 + (size_t)(h - h0) * D, D, tid);
     } else {
       gather_group<D, GS>(kx, vx, tid, [&](int i, int d, bool is_k) -> uint16_t {
-        return i < GS - 1 ? th[((is_k ? 0 : GS) + i) * D + d] : new_bits(is_k ? a.k : a.v, e0 + (size_t)h * D + d);
+        return i < GS - 1 ? th[((is_k ? 0 : GS) + i) * D + d] : new_bits(is_k ? a.k : a.v, e0 + (size_t)(h - h0) * D + d);
       });
     }
     __syncthreads();
@@ -334,8 +342,10 @@ __global__ void __launch_bounds__(kAppendThreads) k_write_tail(AppendArgs a) {
 
 template <int D, int GS>
 static void launch_dg(const AppendArgs& a, hipStream_t stream) {
-  if (a.n_new == 1) {   // a decode step's token: one workgroup per (cell, sequence)
-    hipLaunchKernelGGL((k_append_token<D, GS>), dim3(a.n_cells * a.n_seqs), dim3(kAppendThreads), 0, stream, a);
+  if (a.n_new == 1) {   // a decode step's token: one workgroup per (cell, sequence, kTokenHeads heads)
+    const int n_hs = (a.n_heads + kTokenHeads - 1) / kTokenHeads;
+    hipLaunchKernelGGL((k_append_token<D, GS>), dim3(a.n_cells * a.n_seqs * n_hs), dim3(kAppendThreads), 0, stream,
+                       a);
     return;
   }
   if (a.n_new < GS) {   // at most one group per (sequence, head) completes: one kernel
